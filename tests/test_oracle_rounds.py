@@ -1,0 +1,66 @@
+"""Droplessness pins: the oracle's round executor (fixed E x C buffer, one
+round at a time, token-slot collect buffer poisoned with NaN) must give the
+same bits as the plain per-token loop for every capacity. CPU only."""
+import numpy as np
+import pytest
+
+import oracle
+from round_dropless_expert_amd import configs, synth
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    w = configs.TINY_F32
+    inp = synth.generate(w)
+    idx, wt = oracle.route(inp.logits, w.k)
+    y = oracle.forward_tokens(np.arange(w.T), idx, wt, inp.x, inp.Wg, inp.Wu,
+                              inp.Wd)
+    return w, inp, idx, wt, y
+
+
+def test_every_capacity_is_bit_identical_tiny(tiny):
+    w, inp, idx, wt, y = tiny
+    rounds = []
+    for C in range(1, w.T + 1):
+        p = oracle.plan(idx, w.E, C)
+        Z, y2 = oracle.round_executor(idx, wt, p, C, inp.x, inp.Wg, inp.Wu,
+                                      inp.Wd)
+        assert not np.isnan(Z).any()
+        assert np.array_equal(y, y2), f"C={C}"
+        rounds.append(p.R)
+    # capacity trades rounds for memory: R is non-increasing in C, R = 1 once
+    # C covers the busiest expert
+    assert all(a >= b for a, b in zip(rounds, rounds[1:]))
+    nmax = int(np.bincount(idx.reshape(-1), minlength=w.E).max())
+    assert rounds[nmax - 1] == 1 and rounds[nmax - 2] == 2
+    assert rounds[w.C - 1] == 3
+
+
+def test_capacities_on_balanced_shapes_slice():
+    w = configs.BALANCED_BF16.with_T(256)
+    inp = synth.generate(w)
+    idx, wt = oracle.route(inp.logits, w.k)
+    y = oracle.forward_tokens(np.arange(w.T), idx, wt, inp.x, inp.Wg, inp.Wu,
+                              inp.Wd)
+    for C in (1, 7, -(-w.T * w.k // w.E), w.T):
+        p = oracle.plan(idx, w.E, C)
+        Z, y2 = oracle.round_executor(idx, wt, p, C, inp.x, inp.Wg, inp.Wu,
+                                      inp.Wd)
+        assert np.array_equal(y, y2), f"C={C}"
+
+
+def test_executor_rejects_a_dropped_or_moved_slot(tiny):
+    """Plant a mistake in the plan handed to the executor: a slot that points
+    at the wrong assignment, and a round count one short. Both must fail."""
+    w, inp, idx, wt, _ = tiny
+    p = oracle.plan(idx, w.E, w.C)
+    bad = oracle.Plan(**{**p.__dict__})
+    bad.perm = p.perm.copy()
+    bad.perm[[3, 4]] = bad.perm[[4, 3]]  # swap two slots of expert 0
+    with pytest.raises(oracle.OracleError):
+        oracle.round_executor(idx, wt, bad, w.C, inp.x, inp.Wg, inp.Wu, inp.Wd)
+    short = oracle.Plan(**{**p.__dict__})
+    short.R = p.R - 1  # the last round never runs: its slots stay unfilled
+    with pytest.raises(oracle.OracleError):
+        oracle.round_executor(idx, wt, short, w.C, inp.x, inp.Wg, inp.Wu,
+                              inp.Wd)
