@@ -1,0 +1,176 @@
+/*
+ * moe_rounds.h -- C ABI of the multi-round dropless mixture-of-experts layer
+ * forward on one AMD Instinct MI355X (gfx950).
+ *
+ * The method (sources: "Frontier Pre-training at Microsoft AI (MAI-Base-2)",
+ * section "Key claims", item on multi-round dropless MoE; "Microsoft AI's
+ * MAI-Base-2 trained on 16K GPUs with Muon", section "Expert groups keep
+ * memory fixed when tokens pile up"; "MAI-Base-2: Microsoft details its new
+ * training infrastructure", section "Optimizations to prevent memory loss"):
+ * a router sends each token to a few experts; experts then run one or more
+ * dispatch -> compute -> collect rounds, each with a fixed per-expert token
+ * capacity C. Assignments beyond an expert's capacity wait for a later round,
+ * so no token is dropped, and the device memory the layer needs depends only
+ * on the shapes and C, never on how skewed the routing is.
+ *
+ * Notation: T tokens, E experts, top-k routing, d = d_model, f = d_ff,
+ * assignment id a = t*k + j (j-th choice of token t), n_e = assignments of
+ * expert e, C' = min(C, T) (a capacity above T acts as T),
+ * m(r,e) = clamp(n_e - r*C', 0, C') rows of expert e in round r,
+ * R = max_e ceil(n_e / C') rounds.
+ *
+ * Layouts (row-major, contiguous, no padding):
+ *   logits  float32 [T][E]            (always fp32)
+ *   x, y    elem    [T][d]
+ *   w_gate  elem    [E][f][d]         (out-features x in-features)
+ *   w_up    elem    [E][f][d]
+ *   w_down  elem    [E][d][f]
+ * where elem is float32 (MOE_F32) or bfloat16 (MOE_BF16). With bf16 the
+ * products run on the matrix cores with fp32 accumulation; the SwiGLU
+ * activation is rounded to bf16 once (to nearest even), each expert output
+ * row once, and y once after an fp32 weighted sum.
+ *
+ * Ownership: the caller allocates every buffer, including the workspace of
+ * moe_workspace_size() bytes. The library allocates no device memory and
+ * keeps no mutable global state; all work is enqueued on the caller's HIP
+ * stream (`stream` is a hipStream_t; NULL means the null stream). Calls on
+ * one workspace must not overlap in time. Device pointers must be 16-byte
+ * aligned.
+ *
+ * Errors: every call returns a moe_status_t and validates its arguments
+ * before touching the GPU, so an argument error enqueues nothing. A failed
+ * HIP call returns MOE_ERR_HIP and moe_last_error() gives its text (thread
+ * local). Device data are not validated: NaN or infinite logits give an
+ * unspecified (but in-bounds) routing.
+ *
+ * Limits of this version: 1 <= E <= 64, 1 <= k <= E, T >= 1, T*k < 2^31,
+ * C >= 1, d and f positive multiples of 64, E*C'*max(d, f) < 2^40.
+ */
+#ifndef MOE_ROUNDS_H
+#define MOE_ROUNDS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARGUMENT = 1,
+  MOE_ERR_UNSUPPORTED = 2,
+  MOE_ERR_WORKSPACE_TOO_SMALL = 3,
+  MOE_ERR_HIP = 4
+} moe_status_t;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
+
+typedef struct {
+  int64_t T;       /* tokens */
+  int32_t E;       /* experts */
+  int32_t k;       /* experts per token */
+  int32_t d_model; /* d */
+  int32_t d_ff;    /* f */
+  int64_t C;       /* per-expert capacity of one round */
+  int32_t dtype;   /* moe_dtype_t of x, weights and y */
+} moe_config_t;
+
+/* Byte offsets of the internal buffers inside the workspace. Every offset is
+ * a multiple of 256. Contents (all produced by the calls below):
+ *   idx      int32 [T][k]    expert of assignment a (top-k, ties to the lower
+ *                            index, ordered by descending logit)
+ *   weight   float [T][k]    routing weight: softmax of the k chosen logits
+ *   counts   int32 [E]       n_e
+ *   offsets  int32 [E+1]     exclusive prefix sum of counts
+ *   n_rounds int32 [1]       R
+ *   perm     int32 [T*k]     assignment ids sorted by (expert, a) -- stable
+ *   pos      int32 [T*k]     inverse of perm
+ *   round_of int32 [T*k]     round of assignment a: i / C'
+ *   row_of   int32 [T*k]     round-buffer row of a: e*C' + i % C'
+ *                            (i = pos[a] - offsets[e])
+ *   xr       elem [E*C'][d]  round buffer of gathered token rows
+ *   h        elem [E*C'][f]  SwiGLU activations of the round
+ *   z        elem [T*k][d]   unweighted expert output of every assignment,
+ *                            in token-slot order
+ *   scratch  int32 [...]     plan-internal partial counts
+ * The layout, and so the size, is a pure function of the config.
+ */
+typedef struct {
+  size_t idx, weight, counts, offsets, n_rounds, perm, pos, round_of, row_of,
+      scratch, xr, h, z;
+  size_t total;
+} moe_workspace_layout_t;
+
+/* Human-readable name of a status code (static storage). */
+const char *moe_status_string(moe_status_t status);
+
+/* Text of the last MOE_ERR_HIP / validation failure on this thread. */
+const char *moe_last_error(void);
+
+/* HIP runtime version the library runs against (hipRuntimeGetVersion), or a
+ * negative value if the query fails. Makes no other HIP call. */
+int32_t moe_hip_runtime_version(void);
+
+/* Validate a config (no pointers). Pure host function. */
+moe_status_t moe_check_config(const moe_config_t *cfg);
+
+/* Workspace bytes for a config: a pure host function, no HIP call. The size
+ * depends on (T, E, k, d, f, C, dtype) only, never on routing -- the fixed
+ * memory of the method ("Expert groups keep memory fixed when tokens pile
+ * up"). */
+moe_status_t moe_workspace_size(const moe_config_t *cfg, size_t *bytes);
+
+/* Offsets of every internal buffer (pure host function). */
+moe_status_t moe_workspace_layout(const moe_config_t *cfg,
+                                  moe_workspace_layout_t *out);
+
+/* Route and plan ("a router sends each token to a few experts"; "fixed token
+ * capacity per expert ... overflow tokens go into extra rounds").
+ * Reads logits [T][E]; writes idx, weight, counts, offsets, perm, pos,
+ * round_of, row_of and n_rounds in the workspace. If n_rounds_host is not
+ * NULL the call waits for the stream and stores R there; otherwise it is
+ * asynchronous. */
+moe_status_t moe_plan(const moe_config_t *cfg, const float *logits, void *ws,
+                      size_t ws_bytes, int32_t *n_rounds_host, void *stream);
+
+/* Dispatch of round r ("dispatch -> compute -> collect rounds"): for every
+ * expert e and slot c < m(r,e), copies x[perm[offsets[e] + r*C' + c] / k]
+ * into round-buffer row e*C' + c. Rows c >= m(r,e) are left untouched.
+ * 0 <= round < ceil(T / C'); a round >= R moves nothing. Asynchronous. */
+moe_status_t moe_dispatch(const moe_config_t *cfg, int32_t round,
+                          const void *x, void *ws, size_t ws_bytes,
+                          void *stream);
+
+/* Expert compute and collect of round r: for every expert e with
+ * m(r,e) > 0, h = silu(xr_e . w_gate[e]^T) * (xr_e . w_up[e]^T) on the
+ * first m(r,e) rows of expert e's region, then o = h . w_down[e]^T, and
+ * row c of o is stored at z[perm[offsets[e] + r*C' + c]] (collect into the
+ * token-slot buffer). Grouped GEMMs over all active experts in one launch
+ * each ("grouped GEMM" per expert group, section "Reducing per-expert
+ * overhead" as quoted in "Key claims"). Asynchronous. */
+moe_status_t moe_expert_ffn(const moe_config_t *cfg, int32_t round,
+                            const void *w_gate, const void *w_up,
+                            const void *w_down, void *ws, size_t ws_bytes,
+                            void *stream);
+
+/* Weighted combine after the last round: y[t] = sum_{j<k} weight[t][j] *
+ * z[t*k + j], summed in fp32 over ascending j and rounded once to elem.
+ * Reads only the workspace. Asynchronous. */
+moe_status_t moe_combine(const moe_config_t *cfg, const void *ws,
+                         size_t ws_bytes, void *y, void *stream);
+
+/* The whole layer: plan, one wait to learn R, then R rounds of dispatch and
+ * expert compute + collect, then the weighted combine. y is written in full.
+ * Returns after enqueueing the combine (the plan's wait is the only host
+ * synchronisation). The result does not depend on C. */
+moe_status_t moe_forward(const moe_config_t *cfg, const float *logits,
+                         const void *x, const void *w_gate, const void *w_up,
+                         const void *w_down, void *y, void *ws,
+                         size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_ROUNDS_H */

@@ -1,0 +1,213 @@
+"""ctypes binding of libmoe_rounds.so (the C ABI in include/moe_rounds.h).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels. Device buffers are torch tensors (or raw device addresses); torch
+provides device memory and the current stream, nothing else. If the library
+has not been built this module raises at load time: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # loads the HIP runtime the library must share
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "lib", "libmoe_rounds.so")
+
+MOE_OK = 0
+MOE_ERR_INVALID_ARGUMENT = 1
+MOE_ERR_UNSUPPORTED = 2
+MOE_ERR_WORKSPACE_TOO_SMALL = 3
+MOE_ERR_HIP = 4
+
+MOE_F32 = 0
+MOE_BF16 = 1
+
+EXPORTS = ("moe_status_string", "moe_last_error", "moe_hip_runtime_version",
+           "moe_check_config", "moe_workspace_size", "moe_workspace_layout",
+           "moe_plan", "moe_dispatch", "moe_expert_ffn", "moe_combine",
+           "moe_forward")
+
+
+class MoeConfig(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("E", ctypes.c_int32),
+                ("k", ctypes.c_int32), ("d_model", ctypes.c_int32),
+                ("d_ff", ctypes.c_int32), ("C", ctypes.c_int64),
+                ("dtype", ctypes.c_int32)]
+
+
+LAYOUT_FIELDS = ("idx", "weight", "counts", "offsets", "n_rounds", "perm",
+                 "pos", "round_of", "row_of", "scratch", "xr", "h", "z")
+
+
+class MoeLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in LAYOUT_FIELDS] + \
+        [("total", ctypes.c_size_t)]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load the HIP library (raises if it is missing: no fallback path)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with "
+            "`python -c 'import __graft_entry__ as g; g.build()'` "
+            "or `python round_dropless_expert_amd/csrc/build.py`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, sz, i32, i32p = (ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32,
+                         ctypes.POINTER(ctypes.c_int32))
+    cfgp = ctypes.POINTER(MoeConfig)
+    L.moe_status_string.argtypes = [ctypes.c_int]
+    L.moe_status_string.restype = ctypes.c_char_p
+    L.moe_last_error.argtypes = []
+    L.moe_last_error.restype = ctypes.c_char_p
+    L.moe_hip_runtime_version.argtypes = []
+    L.moe_hip_runtime_version.restype = ctypes.c_int32
+    L.moe_check_config.argtypes = [cfgp]
+    L.moe_workspace_size.argtypes = [cfgp, ctypes.POINTER(ctypes.c_size_t)]
+    L.moe_workspace_layout.argtypes = [cfgp, ctypes.POINTER(MoeLayout)]
+    L.moe_plan.argtypes = [cfgp, vp, vp, sz, i32p, vp]
+    L.moe_dispatch.argtypes = [cfgp, i32, vp, vp, sz, vp]
+    L.moe_expert_ffn.argtypes = [cfgp, i32, vp, vp, vp, vp, sz, vp]
+    L.moe_combine.argtypes = [cfgp, vp, sz, vp, vp]
+    L.moe_forward.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    for n in ("moe_check_config", "moe_workspace_size", "moe_workspace_layout",
+              "moe_plan", "moe_dispatch", "moe_expert_ffn", "moe_combine",
+              "moe_forward"):
+        getattr(L, n).restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def check_runtime() -> None:
+    """The library must run on the same HIP runtime instance as torch."""
+    v = load().moe_hip_runtime_version()
+    want = torch.version.hip
+    if want is None:
+        raise RuntimeError("torch was built without HIP")
+    major, minor = (int(x) for x in want.split(".")[:2])
+    if v < 0 or v // 10_000_000 != major or (v // 100_000) % 100 != minor:
+        raise RuntimeError(f"libmoe_rounds sees HIP runtime {v}, torch uses {want}")
+
+
+def _check(status: int) -> None:
+    if status != MOE_OK:
+        L = load()
+        raise MoeError(status, f"{L.moe_status_string(status).decode()}: "
+                               f"{L.moe_last_error().decode()}")
+
+
+def config(T, E, k, d_model, d_ff, C, dtype) -> MoeConfig:
+    if isinstance(dtype, str):
+        dtype = {"f32": MOE_F32, "bf16": MOE_BF16}[dtype]
+    elif isinstance(dtype, torch.dtype):
+        dtype = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16}[dtype]
+    return MoeConfig(int(T), int(E), int(k), int(d_model), int(d_ff), int(C),
+                     int(dtype))
+
+
+def check_config(cfg: MoeConfig) -> int:
+    return load().moe_check_config(ctypes.byref(cfg))
+
+
+def workspace_size(cfg: MoeConfig) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().moe_workspace_size(ctypes.byref(cfg), ctypes.byref(n)))
+    return n.value
+
+
+def workspace_layout(cfg: MoeConfig) -> dict:
+    L = MoeLayout()
+    _check(load().moe_workspace_layout(ctypes.byref(cfg), ctypes.byref(L)))
+    return {n: getattr(L, n) for n in LAYOUT_FIELDS + ("total",)}
+
+
+def _ptr(t) -> int:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _nbytes(ws) -> int:
+    return ws.numel() * ws.element_size()
+
+
+def moe_plan(cfg, logits, ws, read_rounds=True, stream=None):
+    """Route + plan. Returns R when read_rounds (waits for the stream)."""
+    R = ctypes.c_int32(0)
+    _check(load().moe_plan(ctypes.byref(cfg), _ptr(logits), _ptr(ws),
+                           _nbytes(ws), ctypes.byref(R) if read_rounds else None,
+                           _stream(stream)))
+    return R.value if read_rounds else None
+
+
+def moe_dispatch(cfg, round_, x, ws, stream=None):
+    _check(load().moe_dispatch(ctypes.byref(cfg), int(round_), _ptr(x),
+                               _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def moe_expert_ffn(cfg, round_, w_gate, w_up, w_down, ws, stream=None):
+    _check(load().moe_expert_ffn(ctypes.byref(cfg), int(round_), _ptr(w_gate),
+                                 _ptr(w_up), _ptr(w_down), _ptr(ws),
+                                 _nbytes(ws), _stream(stream)))
+
+
+def moe_combine(cfg, ws, y, stream=None):
+    _check(load().moe_combine(ctypes.byref(cfg), _ptr(ws), _nbytes(ws),
+                              _ptr(y), _stream(stream)))
+
+
+def moe_forward(cfg, logits, x, w_gate, w_up, w_down, y, ws, stream=None):
+    _check(load().moe_forward(ctypes.byref(cfg), _ptr(logits), _ptr(x),
+                              _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(y),
+                              _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def workspace_views(cfg: MoeConfig, ws: torch.Tensor) -> dict:
+    """torch views of the internal buffers of a uint8 workspace tensor."""
+    L = workspace_layout(cfg)
+    T, E, k = cfg.T, cfg.E, cfg.k
+    ce = min(cfg.C, cfg.T)
+    el = torch.bfloat16 if cfg.dtype == MOE_BF16 else torch.float32
+    es = 2 if cfg.dtype == MOE_BF16 else 4
+
+    def view(name, n, dt, size):
+        return ws[L[name]:L[name] + n * size].view(dt)
+
+    i32 = torch.int32
+    return {
+        "idx": view("idx", T * k, i32, 4).view(T, k),
+        "weight": view("weight", T * k, torch.float32, 4).view(T, k),
+        "counts": view("counts", E, i32, 4),
+        "offsets": view("offsets", E + 1, i32, 4),
+        "n_rounds": view("n_rounds", 1, i32, 4),
+        "perm": view("perm", T * k, i32, 4),
+        "pos": view("pos", T * k, i32, 4),
+        "round_of": view("round_of", T * k, i32, 4),
+        "row_of": view("row_of", T * k, i32, 4),
+        "xr": view("xr", E * ce * cfg.d_model, el, es).view(E * ce, cfg.d_model),
+        "h": view("h", E * ce * cfg.d_ff, el, es).view(E * ce, cfg.d_ff),
+        "z": view("z", T * k * cfg.d_model, el, es).view(T * k, cfg.d_model),
+    }

@@ -1,0 +1,327 @@
+// C ABI of the multi-round dropless MoE layer forward: argument validation,
+// the workspace layout (a pure function of the config), and the round loop.
+//
+// The round loop follows "Frontier Pre-training at Microsoft AI
+// (MAI-Base-2)", section "Key claims" (one or more dispatch -> compute ->
+// collect rounds with a fixed per-expert capacity; memory static regardless
+// of token imbalance) and "Microsoft AI's MAI-Base-2 trained on 16K GPUs with
+// Muon", section "Expert groups keep memory fixed when tokens pile up"
+// (overflow tokens go into extra rounds). The plan stays on the device; the
+// host reads back only the round count R.
+#include <atomic>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/moe_rounds.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+moe_status_t fail(moe_status_t s, const char* msg, const char* name = nullptr) {
+  if (name)
+    std::snprintf(g_err, sizeof g_err, "%s: %s", name, msg);
+  else
+    std::snprintf(g_err, sizeof g_err, "%s", msg);
+  return s;
+}
+
+moe_status_t hip_fail(hipError_t e, const char* where) {
+  std::snprintf(g_err, sizeof g_err, "%s: %s (%d)", where, hipGetErrorString(e),
+                (int)e);
+  return MOE_ERR_HIP;
+}
+
+size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
+
+int64_t eff_capacity(const moe_config_t* c) { return c->C < c->T ? c->C : c->T; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+moe_status_t check_cfg(const moe_config_t* c) {
+  if (!c) return fail(MOE_ERR_INVALID_ARGUMENT, "config is NULL");
+  if (c->T < 1) return fail(MOE_ERR_INVALID_ARGUMENT, "T must be >= 1");
+  if (c->E < 1) return fail(MOE_ERR_INVALID_ARGUMENT, "E must be >= 1");
+  if (c->k < 1 || c->k > c->E)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "k must satisfy 1 <= k <= E");
+  if (c->C < 1) return fail(MOE_ERR_INVALID_ARGUMENT, "C must be >= 1");
+  if (c->d_model < 1 || c->d_ff < 1)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "d_model and d_ff must be >= 1");
+  if (c->dtype != MOE_F32 && c->dtype != MOE_BF16)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "unknown dtype");
+  if (c->E > 64) return fail(MOE_ERR_UNSUPPORTED, "E > 64 is not supported");
+  if (c->d_model % 64 || c->d_ff % 64)
+    return fail(MOE_ERR_UNSUPPORTED, "d_model and d_ff must be multiples of 64");
+  const int64_t TK = c->T * (int64_t)c->k;
+  if (c->T >= (int64_t(1) << 31) || TK >= (int64_t(1) << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "T*k must be < 2^31");
+  const int64_t ce = eff_capacity(c);
+  const int64_t dm = c->d_model > c->d_ff ? c->d_model : c->d_ff;
+  if ((int64_t)c->E * ce >= (int64_t(1) << 31) || ce * dm >= (int64_t(1) << 31) ||
+      (int64_t)c->d_model * c->d_ff >= (int64_t(1) << 31))
+    return fail(MOE_ERR_UNSUPPORTED,
+                "E*C', C'*max(d,f) and d*f must be < 2^31");
+  return MOE_OK;
+}
+
+void layout_of(const moe_config_t* c, moe_workspace_layout_t* L) {
+  const size_t TK = (size_t)c->T * c->k;
+  const size_t E = (size_t)c->E;
+  const size_t ce = (size_t)eff_capacity(c);
+  const size_t es = c->dtype == MOE_BF16 ? 2 : 4;
+  moe::Shape s{c->T, c->E, c->k, c->d_model, c->d_ff, (int)ce, c->dtype == MOE_BF16};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  L->idx = take(TK * 4);
+  L->weight = take(TK * 4);
+  L->counts = take(E * 4);
+  L->offsets = take((E + 1) * 4);
+  L->n_rounds = take(4);
+  L->perm = take(TK * 4);
+  L->pos = take(TK * 4);
+  L->round_of = take(TK * 4);
+  L->row_of = take(TK * 4);
+  L->scratch = take((size_t)moe::plan_blocks(s) * E * 4);
+  L->xr = take(E * ce * (size_t)c->d_model * es);
+  L->h = take(E * ce * (size_t)c->d_ff * es);
+  L->z = take(TK * (size_t)c->d_model * es);
+  L->total = off;
+}
+
+struct Bound {
+  moe::Shape s;
+  moe_workspace_layout_t L;
+  char* ws;
+  moe::PlanBuffers pb;
+};
+
+moe_status_t bind(const moe_config_t* c, void* ws, size_t ws_bytes, Bound* b) {
+  moe_status_t st = check_cfg(c);
+  if (st != MOE_OK) return st;
+  if (!ws) return fail(MOE_ERR_INVALID_ARGUMENT, "workspace is NULL");
+  if (!aligned16(ws))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+  layout_of(c, &b->L);
+  if (ws_bytes < b->L.total)
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace too small");
+  b->s = moe::Shape{c->T, c->E, c->k, c->d_model, c->d_ff, (int)eff_capacity(c),
+                    c->dtype == MOE_BF16};
+  b->ws = static_cast<char*>(ws);
+  char* w = b->ws;
+  const moe_workspace_layout_t& L = b->L;
+  b->pb = moe::PlanBuffers{
+      reinterpret_cast<int32_t*>(w + L.idx),      reinterpret_cast<float*>(w + L.weight),
+      reinterpret_cast<int32_t*>(w + L.counts),   reinterpret_cast<int32_t*>(w + L.offsets),
+      reinterpret_cast<int32_t*>(w + L.n_rounds), reinterpret_cast<int32_t*>(w + L.perm),
+      reinterpret_cast<int32_t*>(w + L.pos),      reinterpret_cast<int32_t*>(w + L.round_of),
+      reinterpret_cast<int32_t*>(w + L.row_of),   reinterpret_cast<int32_t*>(w + L.scratch)};
+  return MOE_OK;
+}
+
+moe_status_t check_ptr(const void* p, const char* name) {
+  if (!p) return fail(MOE_ERR_INVALID_ARGUMENT, "is NULL", name);
+  if (!aligned16(p))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "must be 16-byte aligned", name);
+  return MOE_OK;
+}
+
+moe_status_t check_round(const Bound& b, int32_t round) {
+  const int64_t max_rounds = (b.s.T + b.s.ce - 1) / b.s.ce;
+  if (round < 0 || round >= max_rounds)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "round out of range [0, ceil(T/C'))");
+  return MOE_OK;
+}
+
+// Compute units of the current device, cached per device id.
+std::atomic<int> g_cus[64];
+
+moe_status_t num_cus(int* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev >= 0 && dev < 64) {
+    const int v = g_cus[dev].load(std::memory_order_relaxed);
+    if (v > 0) {
+      *out = v;
+      return MOE_OK;
+    }
+  }
+  int n = 0;
+  e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+  if (n < 1) n = 1;
+  if (dev >= 0 && dev < 64) g_cus[dev].store(n, std::memory_order_relaxed);
+  *out = n;
+  return MOE_OK;
+}
+
+#define MOE_HIP(call, where)                         \
+  do {                                               \
+    hipError_t _e = (call);                          \
+    if (_e != hipSuccess) return hip_fail(_e, where); \
+  } while (0)
+
+moe_status_t run_plan(const Bound& b, const float* logits, hipStream_t st) {
+  MOE_HIP(moe::launch_route(b.s, logits, b.pb, st), "route launch");
+  MOE_HIP(moe::launch_plan(b.s, b.pb, st), "plan launch");
+  return MOE_OK;
+}
+
+moe_status_t run_ffn(const Bound& b, int r, const void* wg, const void* wu,
+                     const void* wd, int cus, hipStream_t st) {
+  MOE_HIP(moe::launch_gate_up(b.s, r, b.ws + b.L.xr, wg, wu, b.pb.counts,
+                              b.ws + b.L.h, cus, st),
+          "gate/up launch");
+  MOE_HIP(moe::launch_down(b.s, r, b.ws + b.L.h, wd, b.pb, b.ws + b.L.z, cus, st),
+          "down launch");
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status_t s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARGUMENT: return "MOE_ERR_INVALID_ARGUMENT";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+  }
+  return "MOE_ERR_UNKNOWN";
+}
+
+const char* moe_last_error(void) { return g_err; }
+
+int32_t moe_hip_runtime_version(void) {
+  int v = 0;
+  if (hipRuntimeGetVersion(&v) != hipSuccess) return -1;
+  return v;
+}
+
+moe_status_t moe_check_config(const moe_config_t* cfg) { return check_cfg(cfg); }
+
+moe_status_t moe_workspace_size(const moe_config_t* cfg, size_t* bytes) {
+  moe_status_t st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if (!bytes) return fail(MOE_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  moe_workspace_layout_t L;
+  layout_of(cfg, &L);
+  *bytes = L.total;
+  return MOE_OK;
+}
+
+moe_status_t moe_workspace_layout(const moe_config_t* cfg,
+                                  moe_workspace_layout_t* out) {
+  moe_status_t st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if (!out) return fail(MOE_ERR_INVALID_ARGUMENT, "out is NULL");
+  layout_of(cfg, out);
+  return MOE_OK;
+}
+
+moe_status_t moe_plan(const moe_config_t* cfg, const float* logits, void* ws,
+                      size_t ws_bytes, int32_t* n_rounds_host, void* stream) {
+  Bound b;
+  moe_status_t st = bind(cfg, ws, ws_bytes, &b);
+  if (st != MOE_OK) return st;
+  if ((st = check_ptr(logits, "logits")) != MOE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = run_plan(b, logits, s)) != MOE_OK) return st;
+  if (n_rounds_host) {
+    MOE_HIP(hipMemcpyAsync(n_rounds_host, b.pb.n_rounds, sizeof(int32_t),
+                           hipMemcpyDeviceToHost, s),
+            "read of R");
+    MOE_HIP(hipStreamSynchronize(s), "stream sync");
+  }
+  return MOE_OK;
+}
+
+moe_status_t moe_dispatch(const moe_config_t* cfg, int32_t round, const void* x,
+                          void* ws, size_t ws_bytes, void* stream) {
+  Bound b;
+  moe_status_t st = bind(cfg, ws, ws_bytes, &b);
+  if (st != MOE_OK) return st;
+  if ((st = check_ptr(x, "x")) != MOE_OK) return st;
+  if ((st = check_round(b, round)) != MOE_OK) return st;
+  int cus = 0;
+  if ((st = num_cus(&cus)) != MOE_OK) return st;
+  MOE_HIP(moe::launch_dispatch(b.s, round, x, b.pb, b.ws + b.L.xr, cus,
+                               static_cast<hipStream_t>(stream)),
+          "dispatch launch");
+  return MOE_OK;
+}
+
+moe_status_t moe_expert_ffn(const moe_config_t* cfg, int32_t round,
+                            const void* w_gate, const void* w_up,
+                            const void* w_down, void* ws, size_t ws_bytes,
+                            void* stream) {
+  Bound b;
+  moe_status_t st = bind(cfg, ws, ws_bytes, &b);
+  if (st != MOE_OK) return st;
+  if ((st = check_ptr(w_gate, "w_gate")) != MOE_OK) return st;
+  if ((st = check_ptr(w_up, "w_up")) != MOE_OK) return st;
+  if ((st = check_ptr(w_down, "w_down")) != MOE_OK) return st;
+  if ((st = check_round(b, round)) != MOE_OK) return st;
+  int cus = 0;
+  if ((st = num_cus(&cus)) != MOE_OK) return st;
+  return run_ffn(b, round, w_gate, w_up, w_down, cus,
+                 static_cast<hipStream_t>(stream));
+}
+
+moe_status_t moe_combine(const moe_config_t* cfg, const void* ws,
+                         size_t ws_bytes, void* y, void* stream) {
+  Bound b;
+  moe_status_t st = bind(cfg, const_cast<void*>(ws), ws_bytes, &b);
+  if (st != MOE_OK) return st;
+  if ((st = check_ptr(y, "y")) != MOE_OK) return st;
+  int cus = 0;
+  if ((st = num_cus(&cus)) != MOE_OK) return st;
+  MOE_HIP(moe::launch_combine(b.s, b.ws + b.L.z, b.pb.weight, y, cus,
+                              static_cast<hipStream_t>(stream)),
+          "combine launch");
+  return MOE_OK;
+}
+
+moe_status_t moe_forward(const moe_config_t* cfg, const float* logits,
+                         const void* x, const void* w_gate, const void* w_up,
+                         const void* w_down, void* y, void* ws, size_t ws_bytes,
+                         void* stream) {
+  Bound b;
+  moe_status_t st = bind(cfg, ws, ws_bytes, &b);
+  if (st != MOE_OK) return st;
+  if ((st = check_ptr(logits, "logits")) != MOE_OK) return st;
+  if ((st = check_ptr(x, "x")) != MOE_OK) return st;
+  if ((st = check_ptr(w_gate, "w_gate")) != MOE_OK) return st;
+  if ((st = check_ptr(w_up, "w_up")) != MOE_OK) return st;
+  if ((st = check_ptr(w_down, "w_down")) != MOE_OK) return st;
+  if ((st = check_ptr(y, "y")) != MOE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int cus = 0;
+  if ((st = num_cus(&cus)) != MOE_OK) return st;
+  if ((st = run_plan(b, logits, s)) != MOE_OK) return st;
+  int32_t R = 0;
+  MOE_HIP(hipMemcpyAsync(&R, b.pb.n_rounds, sizeof(int32_t),
+                         hipMemcpyDeviceToHost, s),
+          "read of R");
+  MOE_HIP(hipStreamSynchronize(s), "stream sync");
+  const int64_t max_rounds = (b.s.T + b.s.ce - 1) / b.s.ce;
+  if (R < 1 || R > max_rounds)
+    return fail(MOE_ERR_HIP, "device plan reported an impossible round count");
+  for (int r = 0; r < R; ++r) {
+    MOE_HIP(moe::launch_dispatch(b.s, r, x, b.pb, b.ws + b.L.xr, cus, s),
+            "dispatch launch");
+    if ((st = run_ffn(b, r, w_gate, w_up, w_down, cus, s)) != MOE_OK) return st;
+  }
+  MOE_HIP(moe::launch_combine(b.s, b.ws + b.L.z, b.pb.weight, y, cus, s),
+          "combine launch");
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,53 @@
+// Host-side launchers of the MoE layer kernels (internal interface between
+// the C ABI and the kernel translation units). All launchers enqueue on the
+// given stream and return the HIP error of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+struct Shape {
+  int64_t T;
+  int E, k, d, f;
+  int ce;       // min(C, T)
+  bool bf16;    // element type of x, weights, y and the round buffers
+};
+
+// Plan-internal chunk of assignments handled by one workgroup.
+constexpr int kPlanChunk = 1024;
+
+inline int64_t plan_blocks(const Shape& s) {
+  return (s.T * s.k + kPlanChunk - 1) / kPlanChunk;
+}
+
+struct PlanBuffers {
+  int32_t* idx;
+  float* weight;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* n_rounds;
+  int32_t* perm;
+  int32_t* pos;
+  int32_t* round_of;
+  int32_t* row_of;
+  int32_t* scratch;  // [plan_blocks][E]
+};
+
+hipError_t launch_route(const Shape& s, const float* logits, PlanBuffers b,
+                        hipStream_t st);
+hipError_t launch_plan(const Shape& s, PlanBuffers b, hipStream_t st);
+hipError_t launch_dispatch(const Shape& s, int r, const void* x,
+                           const PlanBuffers& b, void* xr, int num_cus,
+                           hipStream_t st);
+hipError_t launch_gate_up(const Shape& s, int r, const void* xr,
+                          const void* wg, const void* wu, const int32_t* counts,
+                          void* h, int num_cus, hipStream_t st);
+hipError_t launch_down(const Shape& s, int r, const void* h, const void* wd,
+                       const PlanBuffers& b, void* z, int num_cus,
+                       hipStream_t st);
+hipError_t launch_combine(const Shape& s, const void* z, const float* weight,
+                          void* y, int num_cus, hipStream_t st);
+
+}  // namespace moe

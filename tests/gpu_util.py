@@ -1,0 +1,107 @@
+"""Helpers for the GPU parity tests: upload seeded inputs, run the C ABI,
+and compare with the oracle. Imported by GPU tests only."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+from round_dropless_expert_amd import binding as B
+from round_dropless_expert_amd import synth
+from round_dropless_expert_amd.configs import Workload
+
+# max |err| <= TOL * max |ref| over the compared elements
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def note(msg: str) -> None:
+    """Name the case before a GPU step (flushed, so a fault still shows it)."""
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def el_dtype(w: Workload):
+    return torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+
+class Case:
+    """One workload's inputs on the host (float32, dtype-exact) and device."""
+
+    def __init__(self, w: Workload, dev="cuda:0"):
+        self.w = w
+        self.dev = dev
+        note(f"generate {w.name} T={w.T} d={w.d_model} f={w.d_ff} E={w.E} "
+             f"k={w.k} C={w.C} skew={w.skew}")
+        self.inp = synth.generate(w)
+        dt = el_dtype(w)
+        up = lambda a: torch.from_numpy(a).to(dev).to(dt).contiguous()
+        self.logits = torch.from_numpy(self.inp.logits).to(dev)
+        self.x = up(self.inp.x)
+        self.wg = up(self.inp.Wg)
+        self.wu = up(self.inp.Wu)
+        self.wd = up(self.inp.Wd)
+        self.idx, self.wt = oracle.route(self.inp.logits, w.k)
+
+    def cfg(self, C=None):
+        w = self.w
+        return B.config(w.T, w.E, w.k, w.d_model, w.d_ff,
+                        w.C if C is None else C, w.dtype)
+
+    def workspace(self, cfg, poison=True):
+        n = B.workspace_size(cfg)
+        ws = torch.empty(n, dtype=torch.uint8, device=self.dev)
+        if poison:
+            ws.fill_(0xFF)  # NaN in bf16 and fp32: unwritten slots show
+        return ws
+
+    def new_y(self):
+        return torch.full((self.w.T, self.w.d_model), float("nan"),
+                          dtype=el_dtype(self.w), device=self.dev)
+
+    def oracle_y(self, tokens):
+        return oracle.forward_tokens(tokens, self.idx, self.wt, self.inp.x,
+                                     self.inp.Wg, self.inp.Wu, self.inp.Wd)
+
+
+def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape
+    assert np.all(np.isfinite(got)), "non-finite values in GPU output"
+    scale = np.max(np.abs(ref))
+    return float(np.max(np.abs(got - ref)) / (scale if scale > 0 else 1.0))
+
+
+def assert_close(got, ref, dtype: str, what: str) -> float:
+    e = rel_err(got, ref)
+    assert e <= TOL[dtype], f"{what}: max|err|/max|ref| = {e:.3e} > {TOL[dtype]}"
+    return e
+
+
+def to_np(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy() if t.dtype == torch.bfloat16 \
+        else t.detach().cpu().numpy()
+
+
+def assert_plan_equal(views: dict, p: oracle.Plan, idx: np.ndarray):
+    np.testing.assert_array_equal(views["idx"].cpu().numpy(), idx)
+    np.testing.assert_array_equal(views["counts"].cpu().numpy(), p.counts)
+    np.testing.assert_array_equal(views["offsets"].cpu().numpy(), p.offsets)
+    np.testing.assert_array_equal(views["perm"].cpu().numpy(), p.perm)
+    np.testing.assert_array_equal(views["pos"].cpu().numpy(), p.pos)
+    np.testing.assert_array_equal(views["round_of"].cpu().numpy(), p.round_of)
+    np.testing.assert_array_equal(views["row_of"].cpu().numpy(), p.row_of)
+    assert int(views["n_rounds"].item()) == p.R
+
+
+def sample_tokens(T: int, p: oracle.Plan, k: int, n: int, seed: int = 1):
+    """Tokens 0 and T-1, every token with an assignment in the last round
+    (up to n), and a seeded random sample."""
+    rng = np.random.default_rng(seed)
+    last = np.unique(np.nonzero(p.round_of == p.R - 1)[0] // k)
+    if last.size > n // 2:
+        last = rng.choice(last, n // 2, replace=False)
+    rand = rng.choice(T, min(T, n), replace=False)
+    return np.unique(np.concatenate([[0, T - 1], last, rand])).astype(np.int64)

@@ -1,0 +1,142 @@
+"""The C ABI on the CPU: the library loads, exports every function the header
+declares, computes the workspace layout as a pure function of the config, and
+rejects bad arguments with exact status codes before any HIP call."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_rounds.h")
+
+
+@pytest.fixture(scope="module")
+def B():
+    from round_dropless_expert_amd import binding
+    if not os.path.exists(binding.LIB_PATH):
+        from round_dropless_expert_amd.csrc import build
+        build.build()
+    binding.load()
+    return binding
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\S[^\n;]*?\b(moe_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("moe_plan", "moe_dispatch", "moe_expert_ffn", "moe_combine",
+              "moe_forward", "moe_workspace_size"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(B):
+    L = B.load()
+    names = declared_functions()
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (moe_\w+)$", out, re.M))
+    assert set(names) <= exported
+    assert set(B.EXPORTS) == set(names)
+
+
+def ceil_div(a, b):
+    return -(-a // b)
+
+
+def expected_total(T, E, k, d, f, C, es):
+    al = lambda v: (v + 255) // 256 * 256
+    ce = min(C, T)
+    TK = T * k
+    nb = ceil_div(TK, 1024)
+    parts = [TK * 4, TK * 4, E * 4, (E + 1) * 4, 4, TK * 4, TK * 4, TK * 4,
+             TK * 4, nb * E * 4, E * ce * d * es, E * ce * f * es, TK * d * es]
+    return sum(al(p) for p in parts)
+
+
+def test_workspace_is_a_function_of_the_config_only(B):
+    from round_dropless_expert_amd import configs
+    sizes = {}
+    for name, w in configs.WORKLOADS.items():
+        cfg = B.config(w.T, w.E, w.k, w.d_model, w.d_ff, w.C, w.dtype)
+        es = 2 if w.dtype == "bf16" else 4
+        n = B.workspace_size(cfg)
+        assert n == expected_total(w.T, w.E, w.k, w.d_model, w.d_ff, w.C, es)
+        lay = B.workspace_layout(cfg)
+        offs = [lay[f] for f in B.LAYOUT_FIELDS]
+        assert all(o % 256 == 0 for o in offs)
+        assert offs == sorted(offs) and lay["total"] == n
+        sizes[name] = n
+    # skewed routing needs exactly the balanced workload's memory
+    assert sizes["skewed_bf16"] == sizes["balanced_bf16"]
+    assert 336_000_000 < sizes["balanced_bf16"] < 337_000_000
+    # capacity costs memory; above T it acts as T
+    w = configs.HOT_EXPERT_BF16
+    prev = 0
+    for C in w.sweep_C:
+        n = B.workspace_size(B.config(w.T, w.E, w.k, w.d_model, w.d_ff, C, "bf16"))
+        assert n > prev
+        prev = n
+    big = B.workspace_size(B.config(w.T, w.E, w.k, w.d_model, w.d_ff, 10 * w.T, "bf16"))
+    assert big == prev
+
+
+BAD_CONFIGS = [
+    (dict(T=0), 1), (dict(E=0), 1), (dict(k=0), 1), (dict(k=9), 1),
+    (dict(C=0), 1), (dict(d_model=0), 1), (dict(dtype=7), 1),
+    (dict(E=65, k=2), 2), (dict(d_model=96), 2), (dict(d_ff=100), 2),
+    (dict(T=1 << 29, k=4), 2),
+]
+
+
+@pytest.mark.parametrize("change,status", BAD_CONFIGS)
+def test_config_validation(B, change, status):
+    base = dict(T=512, E=8, k=2, d_model=64, d_ff=128, C=64, dtype=0)
+    base.update(change)
+    cfg = B.config(**base)
+    assert B.check_config(cfg) == status
+    L = B.load()
+    n = ctypes.c_size_t(0)
+    assert L.moe_workspace_size(ctypes.byref(cfg), ctypes.byref(n)) == status
+    assert B.load().moe_last_error().decode()
+
+
+def test_null_config(B):
+    L = B.load()
+    n = ctypes.c_size_t(0)
+    assert L.moe_workspace_size(None, ctypes.byref(n)) == B.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_forward(None, 16, 16, 16, 16, 16, 16, 16, 1 << 40, None) == \
+        B.MOE_ERR_INVALID_ARGUMENT
+
+
+def test_pointer_and_workspace_checks_before_any_hip_call(B):
+    """These calls fail validation, so they never reach the HIP runtime (this
+    machine has no GPU: a HIP call would report an error of its own)."""
+    L = B.load()
+    cfg = B.config(512, 8, 2, 64, 128, 64, "f32")
+    need = B.workspace_size(cfg)
+    p = 1 << 20  # aligned fake device address, never dereferenced
+    c = ctypes.byref(cfg)
+    assert L.moe_forward(c, p, p, p, p, p, p, p, need - 1, None) == \
+        B.MOE_ERR_WORKSPACE_TOO_SMALL
+    assert L.moe_forward(c, p, p, p, p, p, p, None, need, None) == \
+        B.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_forward(c, p + 4, p, p, p, p, p, p, need, None) == \
+        B.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_forward(c, p, p, p, p, None, p, p, need, None) == \
+        B.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_plan(c, None, p, need, None, None) == B.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_plan(c, p, p + 8, need, None, None) == B.MOE_ERR_INVALID_ARGUMENT
+    # round range: ceil(T / C') rounds at most
+    assert L.moe_dispatch(c, -1, p, p, need, None) == B.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_dispatch(c, 8, p, p, need, None) == B.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_expert_ffn(c, 8, p, p, p, p, need, None) == \
+        B.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_combine(c, p, need, None, None) == B.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_status_string(3) == b"MOE_ERR_WORKSPACE_TOO_SMALL"
