@@ -1,0 +1,232 @@
+#!/usr/bin/env python3
+"""Throughput of the multi-round dropless MoE layer forward on one MI355X.
+
+A step is one moe_forward over the balanced bf16 workload (T=8192 tokens,
+d_model=2048, d_ff=1024, E=32 experts, top-4, C=ceil(T*k/E)=1024): routing,
+plan, the read of the round count, every round's dispatch + grouped
+gate/up + grouped down/collect, and the weighted combine. Inputs are seeded
+synthetic data already resident in HBM when timing starts.
+
+Prints one JSON line with the whole-step throughput (tokens/s), the roofline
+of the dominant kernel (the grouped gate/up GEMM, timed with HIP events on
+the stream it runs on), per-kernel figures, and the CPU oracle timed on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/sec on 1 MI355X; grouped-GEMM MFMA util %; dispatch GB/s"
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}  # dense MFMA, MI355X
+PEAK_HBM_GBPS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None,
+                    help="workload name (default: the balanced bf16 layer)")
+    ap.add_argument("--kernel-steps", type=int, default=20,
+                    help="steps of the per-kernel timing pass")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="approximate wall time of the CPU oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def cpu_baseline(w, inp, seconds: float) -> dict:
+    """The fp64 oracle as it stands, on the host cores: route + plan over all
+    T tokens, then the per-token expert loop over seeded token batches until
+    about `seconds` of wall time."""
+    import numpy as np
+
+    import oracle
+    t0 = time.perf_counter()
+    idx, wt = oracle.route(inp.logits, w.k)
+    oracle.plan(idx, w.E, w.C)
+    t_plan = time.perf_counter() - t0
+    rng = np.random.default_rng(1234)
+    order = rng.permutation(w.T)
+    done, t_ffn, batch = 0, 0.0, 64
+    while done < w.T and t_ffn < seconds:
+        toks = order[done:done + batch].astype(np.int64)
+        t1 = time.perf_counter()
+        oracle.forward_tokens(toks, idx, wt, inp.x, inp.Wg, inp.Wu, inp.Wd)
+        dt = time.perf_counter() - t1
+        t_ffn += dt
+        done += toks.size
+        if dt < seconds / 8:
+            batch *= 2
+    per_token = t_ffn / done + t_plan / w.T
+    return {"value": 1.0 / per_token, "unit": "tokens/s",
+            "cores": oracle.max_threads(), "kind": "oracle",
+            "sample": f"{done} of {w.T} tokens of {w.name} (seeded order) "
+                      f"through the per-token fp64 expert loop in "
+                      f"{t_ffn:.1f} s, plus route+plan over all {w.T} tokens "
+                      f"in {t_plan:.2f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this layer runs on one GPU; --gpus {args.gpus} is not "
+              "supported (multi-GPU expert parallelism is not built)",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from round_dropless_expert_amd import binding as B
+    from round_dropless_expert_amd import configs, synth
+
+    w = configs.WORKLOADS[args.workload] if args.workload else configs.BENCH_WORKLOAD
+    B.load()
+    B.check_runtime()
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    print(f"[bench] generating {w.name}", file=sys.stderr, flush=True)
+    inp = synth.generate(w)
+    el = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    up = lambda a: torch.from_numpy(a).to(dev).to(el).contiguous()
+    logits = torch.from_numpy(inp.logits).to(dev)
+    x, wg, wu, wd = up(inp.x), up(inp.Wg), up(inp.Wu), up(inp.Wd)
+    cfg = B.config(w.T, w.E, w.k, w.d_model, w.d_ff, w.C, w.dtype)
+    ws_bytes = B.workspace_size(cfg)
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    base_alloc = torch.cuda.memory_allocated()
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    y = torch.empty(w.T, w.d_model, dtype=el, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        B.moe_forward(cfg, logits, x, wg, wu, wd, y, ws, stream)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    tokens_per_s = w.T * args.steps / wall
+    peak_bytes = torch.cuda.max_memory_allocated() - base_alloc
+    print(f"[bench] timed {args.steps} steps: {ms_per_step:.4f} ms/step",
+          file=sys.stderr, flush=True)
+
+    # plan figures for the algorithmic bytes
+    views = B.workspace_views(cfg, ws)
+    R = int(views["n_rounds"].item())
+    round_of = views["round_of"].cpu().numpy()
+    A = np.bincount(round_of, minlength=R)[:R].astype(np.int64)
+    U = np.array([np.unique(np.nonzero(round_of == r)[0] // w.k).size
+                  for r in range(R)], dtype=np.int64)
+    es = 2 if w.dtype == "bf16" else 4
+    TK = w.T * w.k
+
+    # per-kernel pass: HIP events on the same stream around each stage
+    names = ("plan", "dispatch", "gate_up", "down", "combine")
+    tot = {n: 0.0 for n in names}
+    for it in range(args.kernel_steps + 2):
+        ev = []
+
+        def mark():
+            e = torch.cuda.Event(enable_timing=True)
+            e.record(stream)
+            ev.append(e)
+            return e
+
+        rec = []
+        a0 = mark()
+        B.moe_plan(cfg, logits, ws, read_rounds=False, stream=stream)
+        a1 = mark()
+        rec.append(("plan", a0, a1))
+        for r in range(R):
+            b0 = mark()
+            B.moe_dispatch(cfg, r, x, ws, stream)
+            b1 = mark()
+            B.moe_expert_gate_up(cfg, r, wg, wu, ws, stream)
+            b2 = mark()
+            B.moe_expert_down(cfg, r, wd, ws, stream)
+            b3 = mark()
+            rec += [("dispatch", b0, b1), ("gate_up", b1, b2), ("down", b2, b3)]
+        c0 = mark()
+        B.moe_combine(cfg, ws, y, stream)
+        c1 = mark()
+        rec.append(("combine", c0, c1))
+        torch.cuda.synchronize()
+        if it >= 2:  # two untimed passes
+            for n, e0, e1 in rec:
+                tot[n] += e0.elapsed_time(e1) * 1e-3
+    ks = args.kernel_steps
+    sec = {n: tot[n] / ks for n in names}  # seconds per step, per stage
+
+    flops_gu = 4.0 * TK * w.d_model * w.d_ff
+    flops_dn = 2.0 * TK * w.d_model * w.d_ff
+    peak_tf = PEAK_TFLOPS[w.dtype]
+    disp_bytes = float(np.sum(U * w.d_model * es + A * w.d_model * es + 4 * A))
+    comb_bytes = float(TK * w.d_model * es + w.T * w.d_model * es + 4 * TK)
+    kernels = {
+        "plan": {"us_per_step": sec["plan"] * 1e6, "launches_per_step": 4},
+        "dispatch": {"us_per_step": sec["dispatch"] * 1e6, "launches_per_step": R,
+                     "GB/s": disp_bytes / sec["dispatch"] / 1e9,
+                     "frac_hbm": disp_bytes / sec["dispatch"] / 1e9 / PEAK_HBM_GBPS,
+                     "algorithmic_bytes": disp_bytes},
+        "gate_up": {"us_per_step": sec["gate_up"] * 1e6, "launches_per_step": R,
+                    "TFLOP/s": flops_gu / sec["gate_up"] / 1e12,
+                    "frac_mfma": flops_gu / sec["gate_up"] / 1e12 / peak_tf},
+        "down": {"us_per_step": sec["down"] * 1e6, "launches_per_step": R,
+                 "TFLOP/s": flops_dn / sec["down"] / 1e12,
+                 "frac_mfma": flops_dn / sec["down"] / 1e12 / peak_tf},
+        "combine": {"us_per_step": sec["combine"] * 1e6, "launches_per_step": 1,
+                    "GB/s": comb_bytes / sec["combine"] / 1e9,
+                    "frac_hbm": comb_bytes / sec["combine"] / 1e9 / PEAK_HBM_GBPS,
+                    "algorithmic_bytes": comb_bytes},
+    }
+    gemm_util = (flops_gu + flops_dn) / (sec["gate_up"] + sec["down"]) / 1e12 / peak_tf
+    achieved = flops_gu / sec["gate_up"] / 1e12
+    roofline = {"bound": "mfma", "kernel": "grouped gate/up GEMM + SwiGLU",
+                "achieved": achieved, "peak": peak_tf, "unit": "TFLOP/s",
+                "frac": achieved / peak_tf, "traffic": None,
+                "flops_per_launch": flops_gu / R,
+                "avg_launch_us": sec["gate_up"] / R * 1e6}
+
+    out = {
+        "metric": METRIC, "value": tokens_per_s, "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_per_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded numpy PCG64; N(0,1) logits and tokens, "
+                "N(0,1/fan_in) weights)",
+        "config": {"workload": w.name, "T": w.T, "d_model": w.d_model,
+                   "d_ff": w.d_ff, "E": w.E, "k": w.k, "C": w.C,
+                   "skew": list(w.skew), "rounds": R,
+                   "rows_per_round": A.tolist()},
+        "grouped_gemm_mfma_util_pct": 100.0 * gemm_util,
+        "dispatch_GBps": kernels["dispatch"]["GB/s"],
+        "combine_GBps": kernels["combine"]["GB/s"],
+        "workspace_bytes": ws_bytes, "peak_allocated_bytes": peak_bytes,
+        "roofline": roofline, "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

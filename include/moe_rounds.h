@@ -7,11 +7,12 @@
  * MAI-Base-2 trained on 16K GPUs with Muon", section "Expert groups keep
  * memory fixed when tokens pile up"; "MAI-Base-2: Microsoft details its new
  * training infrastructure", section "Optimizations to prevent memory loss"):
- * a router sends each token to a few experts; experts then run one or more
- * dispatch -> compute -> collect rounds, each with a fixed per-expert token
- * capacity C. Assignments beyond an expert's capacity wait for a later round,
- * so no token is dropped, and the device memory the layer needs depends only
- * on the shapes and C, never on how skewed the routing is.
+ * routing assigns every token to a small number of experts; the experts then
+ * work in one or more rounds of dispatch, compute and collect, and a round
+ * holds at most C tokens per expert. Assignments beyond an expert's capacity
+ * are deferred to a later round, so none is lost, and the device memory the
+ * layer needs depends only on the shapes and C, never on how skewed the
+ * routing is.
  *
  * Notation: T tokens, E experts, top-k routing, d = d_model, f = d_ff,
  * assignment id a = t*k + j (j-th choice of token t), n_e = assignments of
@@ -44,7 +45,8 @@
  * unspecified (but in-bounds) routing.
  *
  * Limits of this version: 1 <= E <= 64, 1 <= k <= E, T >= 1, T*k < 2^31,
- * C >= 1, d and f positive multiples of 64, E*C'*max(d, f) < 2^40.
+ * C >= 1, d and f positive multiples of 64, and E*C', C'*max(d, f) and d*f
+ * each below 2^31 (MOE_ERR_UNSUPPORTED otherwise).
  */
 #ifndef MOE_ROUNDS_H
 #define MOE_ROUNDS_H
@@ -125,8 +127,9 @@ moe_status_t moe_workspace_size(const moe_config_t *cfg, size_t *bytes);
 moe_status_t moe_workspace_layout(const moe_config_t *cfg,
                                   moe_workspace_layout_t *out);
 
-/* Route and plan ("a router sends each token to a few experts"; "fixed token
- * capacity per expert ... overflow tokens go into extra rounds").
+/* Route and plan: every token picks its top-k experts; each expert's
+ * assignments are then split into rounds of at most C' (the per-expert
+ * capacity is fixed, and what does not fit waits for a later round).
  * Reads logits [T][E]; writes idx, weight, counts, offsets, perm, pos,
  * round_of, row_of and n_rounds in the workspace. If n_rounds_host is not
  * NULL the call waits for the stream and stores R there; otherwise it is
@@ -153,6 +156,17 @@ moe_status_t moe_expert_ffn(const moe_config_t *cfg, int32_t round,
                             const void *w_gate, const void *w_up,
                             const void *w_down, void *ws, size_t ws_bytes,
                             void *stream);
+
+/* The two halves of moe_expert_ffn, for callers that time or schedule them
+ * separately: gate/up writes h for round r (first m(r,e) rows of each
+ * expert's region), down reads h and writes the round's rows of z. Same
+ * arguments, layouts and asynchrony as moe_expert_ffn. */
+moe_status_t moe_expert_gate_up(const moe_config_t *cfg, int32_t round,
+                                const void *w_gate, const void *w_up, void *ws,
+                                size_t ws_bytes, void *stream);
+moe_status_t moe_expert_down(const moe_config_t *cfg, int32_t round,
+                             const void *w_down, void *ws, size_t ws_bytes,
+                             void *stream);
 
 /* Weighted combine after the last round: y[t] = sum_{j<k} weight[t][j] *
  * z[t*k + j], summed in fp32 over ascending j and rounded once to elem.

@@ -19,10 +19,11 @@
  *   [P2] "MAI-Base-2: Microsoft's 2.8T Model is a BREAKTHROUGH", video
  *        transcript at 03:11.
  *
- * The pages give the method only in outline: a router sends each token to a
- * few experts; each expert group runs dispatch -> compute -> collect rounds
- * with a fixed per-expert capacity; overflow waits for an extra round and
- * nothing is dropped. Where they are silent this file takes these readings:
+ * The pages give the method only in outline: routing assigns every token to
+ * a small number of experts; the experts of a group then work in rounds of
+ * dispatch, compute and collect, each round holding at most a fixed number
+ * of tokens per expert; assignments that do not fit are deferred to a later
+ * round, so none is lost. Where they are silent this file takes these readings:
  *   - routing is top-k over the raw logits with ties to the lower expert
  *     index, and the k weights are the softmax over all E logits
  *     renormalised over the k chosen experts;
@@ -69,8 +70,8 @@ void oracle_set_threads(int n) {
 #endif
 }
 
-/* Router [P4 "Expert groups keep memory fixed..."]: each token goes to a few
- * experts. Top-k by raw fp32 logit, order (logit descending, expert index
+/* Router [P4 "Expert groups keep memory fixed..."]: every token is routed to
+ * a small number of experts. Top-k by raw fp32 logit, order (logit descending, expert index
  * ascending); -0 and +0 compare equal. Then the softmax over all E logits,
  * renormalised over the k chosen experts. idx is [T][k] int32, w is [T][k]
  * fp64. Returns OR_ERR_NONFINITE if any logit is NaN or infinite. */

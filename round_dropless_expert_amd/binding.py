@@ -26,8 +26,8 @@ MOE_BF16 = 1
 
 EXPORTS = ("moe_status_string", "moe_last_error", "moe_hip_runtime_version",
            "moe_check_config", "moe_workspace_size", "moe_workspace_layout",
-           "moe_plan", "moe_dispatch", "moe_expert_ffn", "moe_combine",
-           "moe_forward")
+           "moe_plan", "moe_dispatch", "moe_expert_ffn", "moe_expert_gate_up",
+           "moe_expert_down", "moe_combine", "moe_forward")
 
 
 class MoeConfig(ctypes.Structure):
@@ -81,10 +81,13 @@ def load() -> ctypes.CDLL:
     L.moe_plan.argtypes = [cfgp, vp, vp, sz, i32p, vp]
     L.moe_dispatch.argtypes = [cfgp, i32, vp, vp, sz, vp]
     L.moe_expert_ffn.argtypes = [cfgp, i32, vp, vp, vp, vp, sz, vp]
+    L.moe_expert_gate_up.argtypes = [cfgp, i32, vp, vp, vp, sz, vp]
+    L.moe_expert_down.argtypes = [cfgp, i32, vp, vp, sz, vp]
     L.moe_combine.argtypes = [cfgp, vp, sz, vp, vp]
     L.moe_forward.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     for n in ("moe_check_config", "moe_workspace_size", "moe_workspace_layout",
-              "moe_plan", "moe_dispatch", "moe_expert_ffn", "moe_combine",
+              "moe_plan", "moe_dispatch", "moe_expert_ffn",
+              "moe_expert_gate_up", "moe_expert_down", "moe_combine",
               "moe_forward"):
         getattr(L, n).restype = ctypes.c_int
     _lib = L
@@ -172,6 +175,18 @@ def moe_expert_ffn(cfg, round_, w_gate, w_up, w_down, ws, stream=None):
     _check(load().moe_expert_ffn(ctypes.byref(cfg), int(round_), _ptr(w_gate),
                                  _ptr(w_up), _ptr(w_down), _ptr(ws),
                                  _nbytes(ws), _stream(stream)))
+
+
+def moe_expert_gate_up(cfg, round_, w_gate, w_up, ws, stream=None):
+    _check(load().moe_expert_gate_up(ctypes.byref(cfg), int(round_),
+                                     _ptr(w_gate), _ptr(w_up), _ptr(ws),
+                                     _nbytes(ws), _stream(stream)))
+
+
+def moe_expert_down(cfg, round_, w_down, ws, stream=None):
+    _check(load().moe_expert_down(ctypes.byref(cfg), int(round_),
+                                  _ptr(w_down), _ptr(ws), _nbytes(ws),
+                                  _stream(stream)))
 
 
 def moe_combine(cfg, ws, y, stream=None):

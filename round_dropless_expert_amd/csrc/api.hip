@@ -275,6 +275,40 @@ moe_status_t moe_expert_ffn(const moe_config_t* cfg, int32_t round,
                  static_cast<hipStream_t>(stream));
 }
 
+moe_status_t moe_expert_gate_up(const moe_config_t* cfg, int32_t round,
+                                const void* w_gate, const void* w_up, void* ws,
+                                size_t ws_bytes, void* stream) {
+  Bound b;
+  moe_status_t st = bind(cfg, ws, ws_bytes, &b);
+  if (st != MOE_OK) return st;
+  if ((st = check_ptr(w_gate, "w_gate")) != MOE_OK) return st;
+  if ((st = check_ptr(w_up, "w_up")) != MOE_OK) return st;
+  if ((st = check_round(b, round)) != MOE_OK) return st;
+  int cus = 0;
+  if ((st = num_cus(&cus)) != MOE_OK) return st;
+  MOE_HIP(moe::launch_gate_up(b.s, round, b.ws + b.L.xr, w_gate, w_up,
+                              b.pb.counts, b.ws + b.L.h, cus,
+                              static_cast<hipStream_t>(stream)),
+          "gate/up launch");
+  return MOE_OK;
+}
+
+moe_status_t moe_expert_down(const moe_config_t* cfg, int32_t round,
+                             const void* w_down, void* ws, size_t ws_bytes,
+                             void* stream) {
+  Bound b;
+  moe_status_t st = bind(cfg, ws, ws_bytes, &b);
+  if (st != MOE_OK) return st;
+  if ((st = check_ptr(w_down, "w_down")) != MOE_OK) return st;
+  if ((st = check_round(b, round)) != MOE_OK) return st;
+  int cus = 0;
+  if ((st = num_cus(&cus)) != MOE_OK) return st;
+  MOE_HIP(moe::launch_down(b.s, round, b.ws + b.L.h, w_down, b.pb, b.ws + b.L.z,
+                           cus, static_cast<hipStream_t>(stream)),
+          "down launch");
+  return MOE_OK;
+}
+
 moe_status_t moe_combine(const moe_config_t* cfg, const void* ws,
                          size_t ws_bytes, void* y, void* stream) {
   Bound b;

@@ -1,8 +1,8 @@
 // Router and round plan of the multi-round dropless MoE layer (gfx950).
 //
 // Router ("Microsoft AI's MAI-Base-2 trained on 16K GPUs with Muon", section
-// "Expert groups keep memory fixed when tokens pile up": a router sends each
-// token to a few experts): top-k over the raw fp32 logits, ties to the lower
+// "Expert groups keep memory fixed when tokens pile up": routing assigns every
+// token to a small number of experts): top-k over the raw fp32 logits, ties to the lower
 // expert index, ordered by descending logit; weights are the softmax of the
 // k chosen logits (equal to the full softmax renormalised over them).
 //
