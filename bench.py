@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate wall time of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--weights", choices=("tiled", "row_major"), default="tiled",
+                    help="expert weight layout the layer reads (tiled = packed "
+                         "once by moe_pack_weights before timing)")
     return ap.parse_args()
 
 
@@ -100,8 +103,16 @@ def main():
     el = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     up = lambda a: torch.from_numpy(a).to(dev).to(el).contiguous()
     logits = torch.from_numpy(inp.logits).to(dev)
-    x, wg, wu, wd = up(inp.x), up(inp.Wg), up(inp.Wu), up(inp.Wd)
-    cfg = B.config(w.T, w.E, w.k, w.d_model, w.d_ff, w.C, w.dtype)
+    x, wg_rm, wu_rm, wd_rm = up(inp.x), up(inp.Wg), up(inp.Wu), up(inp.Wd)
+    layout = args.weights
+    cfg = B.config(w.T, w.E, w.k, w.d_model, w.d_ff, w.C, w.dtype, layout)
+    if layout == "tiled":
+        # one-time repack at load time, outside the timed region
+        wg, wu, wd = (torch.empty_like(t) for t in (wg_rm, wu_rm, wd_rm))
+        B.moe_pack_weights(cfg, wg_rm, wu_rm, wd_rm, wg, wu, wd)
+        del wg_rm, wu_rm, wd_rm
+    else:
+        wg, wu, wd = wg_rm, wu_rm, wd_rm
     ws_bytes = B.workspace_size(cfg)
     torch.cuda.synchronize()
     torch.cuda.reset_peak_memory_stats()
@@ -214,6 +225,7 @@ def main():
                 "N(0,1/fan_in) weights)",
         "config": {"workload": w.name, "T": w.T, "d_model": w.d_model,
                    "d_ff": w.d_ff, "E": w.E, "k": w.k, "C": w.C,
+                   "weight_layout": layout,
                    "skew": list(w.skew), "rounds": R,
                    "rows_per_round": A.tolist()},
         "grouped_gemm_mfma_util_pct": 100.0 * gemm_util,

@@ -68,15 +68,35 @@ typedef enum {
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
 
+/* Layout of w_gate, w_up and w_down as the calls below read them:
+ *   MOE_WEIGHTS_ROW_MAJOR  [E][out][in] row-major, as documented above;
+ *   MOE_WEIGHTS_TILED      the tiled layout written by moe_pack_weights:
+ *                          each expert's [out][in] matrix stored as 4 KiB
+ *                          blocks of 64 rows x 64 bytes (see "Tiled layout").
+ * The arithmetic and the results are identical; the tiled layout lets every
+ * 64-row band of a K stage be fetched as one contiguous 4 KiB read. */
+typedef enum { MOE_WEIGHTS_ROW_MAJOR = 0, MOE_WEIGHTS_TILED = 1 } moe_weight_layout_t;
+
 typedef struct {
-  int64_t T;       /* tokens */
-  int32_t E;       /* experts */
-  int32_t k;       /* experts per token */
-  int32_t d_model; /* d */
-  int32_t d_ff;    /* f */
-  int64_t C;       /* per-expert capacity of one round */
-  int32_t dtype;   /* moe_dtype_t of x, weights and y */
+  int64_t T;             /* tokens */
+  int32_t E;             /* experts */
+  int32_t k;             /* experts per token */
+  int32_t d_model;       /* d */
+  int32_t d_ff;          /* f */
+  int64_t C;             /* per-expert capacity of one round */
+  int32_t dtype;         /* moe_dtype_t of x, weights and y */
+  int32_t weight_layout; /* moe_weight_layout_t of the expert weights */
 } moe_config_t;
+
+/* Tiled layout. A matrix with R rows (R padded up to a multiple of 64) and
+ * Kb = K * sizeof(elem) bytes per row (a multiple of 64) is a sequence of
+ * 4096-byte blocks. Block b = (row / 64) * (Kb / 64) + byte / 64 holds rows
+ * row - row % 64 .. +63 and bytes byte - byte % 64 .. +63 of each; inside it,
+ * row r = row % 64 occupies bytes [64 r, 64 r + 64), and the 16-byte chunk
+ * c = (byte % 64) / 16 of that row sits at position c ^ ((r / 4) % 4):
+ *   offset(row, byte) = 4096 * b + 64 * r + 16 * (c ^ ((r >> 2) & 3))
+ *                       + byte % 16.
+ * Weights: expert e's matrix starts at element e * out * in of its array. */
 
 /* Byte offsets of the internal buffers inside the workspace. Every offset is
  * a multiple of 256. Contents (all produced by the calls below):
@@ -91,8 +111,11 @@ typedef struct {
  *   round_of int32 [T*k]     round of assignment a: i / C'
  *   row_of   int32 [T*k]     round-buffer row of a: e*C' + i % C'
  *                            (i = pos[a] - offsets[e])
- *   xr       elem [E*C'][d]  round buffer of gathered token rows
- *   h        elem [E*C'][f]  SwiGLU activations of the round
+ *   xr       elem [E][P][d]  round buffer of gathered token rows, P =
+ *                            C' rounded up to a multiple of 64; expert e's
+ *                            P x d matrix in the tiled layout (slot c is row
+ *                            c; rows at or beyond m(r,e) hold stale data)
+ *   h        elem [E][P][f]  SwiGLU activations of the round, same layout
  *   z        elem [T*k][d]   unweighted expert output of every assignment,
  *                            in token-slot order
  *   scratch  int32 [...]     plan-internal partial counts
@@ -139,7 +162,8 @@ moe_status_t moe_plan(const moe_config_t *cfg, const float *logits, void *ws,
 
 /* Dispatch of round r ("dispatch -> compute -> collect rounds"): for every
  * expert e and slot c < m(r,e), copies x[perm[offsets[e] + r*C' + c] / k]
- * into round-buffer row e*C' + c. Rows c >= m(r,e) are left untouched.
+ * into row c of expert e's round buffer (tiled layout). Rows c >= m(r,e)
+ * are left untouched.
  * 0 <= round < ceil(T / C'); a round >= R moves nothing. Asynchronous. */
 moe_status_t moe_dispatch(const moe_config_t *cfg, int32_t round,
                           const void *x, void *ws, size_t ws_bytes,
@@ -167,6 +191,15 @@ moe_status_t moe_expert_gate_up(const moe_config_t *cfg, int32_t round,
 moe_status_t moe_expert_down(const moe_config_t *cfg, int32_t round,
                              const void *w_down, void *ws, size_t ws_bytes,
                              void *stream);
+
+/* Repack expert weights from the row-major layout into the tiled layout
+ * (MOE_WEIGHTS_TILED): gate and up are [E][f][d], down is [E][d][f]; each
+ * output array has the size of its input. cfg->weight_layout is ignored.
+ * Meant to run once, when the weights are loaded. Asynchronous. */
+moe_status_t moe_pack_weights(const moe_config_t *cfg, const void *w_gate,
+                              const void *w_up, const void *w_down,
+                              void *out_gate, void *out_up, void *out_down,
+                              void *stream);
 
 /* Weighted combine after the last round: y[t] = sum_{j<k} weight[t][j] *
  * z[t*k + j], summed in fp32 over ascending j and rounded once to elem.

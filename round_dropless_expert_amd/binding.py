@@ -24,17 +24,20 @@ MOE_ERR_HIP = 4
 MOE_F32 = 0
 MOE_BF16 = 1
 
+MOE_WEIGHTS_ROW_MAJOR = 0
+MOE_WEIGHTS_TILED = 1
+
 EXPORTS = ("moe_status_string", "moe_last_error", "moe_hip_runtime_version",
            "moe_check_config", "moe_workspace_size", "moe_workspace_layout",
            "moe_plan", "moe_dispatch", "moe_expert_ffn", "moe_expert_gate_up",
-           "moe_expert_down", "moe_combine", "moe_forward")
+           "moe_expert_down", "moe_pack_weights", "moe_combine", "moe_forward")
 
 
 class MoeConfig(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("E", ctypes.c_int32),
                 ("k", ctypes.c_int32), ("d_model", ctypes.c_int32),
                 ("d_ff", ctypes.c_int32), ("C", ctypes.c_int64),
-                ("dtype", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("weight_layout", ctypes.c_int32)]
 
 
 LAYOUT_FIELDS = ("idx", "weight", "counts", "offsets", "n_rounds", "perm",
@@ -83,12 +86,13 @@ def load() -> ctypes.CDLL:
     L.moe_expert_ffn.argtypes = [cfgp, i32, vp, vp, vp, vp, sz, vp]
     L.moe_expert_gate_up.argtypes = [cfgp, i32, vp, vp, vp, sz, vp]
     L.moe_expert_down.argtypes = [cfgp, i32, vp, vp, sz, vp]
+    L.moe_pack_weights.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp]
     L.moe_combine.argtypes = [cfgp, vp, sz, vp, vp]
     L.moe_forward.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     for n in ("moe_check_config", "moe_workspace_size", "moe_workspace_layout",
               "moe_plan", "moe_dispatch", "moe_expert_ffn",
-              "moe_expert_gate_up", "moe_expert_down", "moe_combine",
-              "moe_forward"):
+              "moe_expert_gate_up", "moe_expert_down", "moe_pack_weights",
+              "moe_combine", "moe_forward"):
         getattr(L, n).restype = ctypes.c_int
     _lib = L
     return L
@@ -112,13 +116,17 @@ def _check(status: int) -> None:
                                f"{L.moe_last_error().decode()}")
 
 
-def config(T, E, k, d_model, d_ff, C, dtype) -> MoeConfig:
+def config(T, E, k, d_model, d_ff, C, dtype,
+           weight_layout=MOE_WEIGHTS_ROW_MAJOR) -> MoeConfig:
     if isinstance(dtype, str):
         dtype = {"f32": MOE_F32, "bf16": MOE_BF16}[dtype]
     elif isinstance(dtype, torch.dtype):
         dtype = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16}[dtype]
+    if isinstance(weight_layout, str):
+        weight_layout = {"row_major": MOE_WEIGHTS_ROW_MAJOR,
+                         "tiled": MOE_WEIGHTS_TILED}[weight_layout]
     return MoeConfig(int(T), int(E), int(k), int(d_model), int(d_ff), int(C),
-                     int(dtype))
+                     int(dtype), int(weight_layout))
 
 
 def check_config(cfg: MoeConfig) -> int:
@@ -189,6 +197,14 @@ def moe_expert_down(cfg, round_, w_down, ws, stream=None):
                                   _stream(stream)))
 
 
+def moe_pack_weights(cfg, w_gate, w_up, w_down, out_gate, out_up, out_down,
+                     stream=None):
+    """Row-major expert weights -> the tiled layout (MOE_WEIGHTS_TILED)."""
+    _check(load().moe_pack_weights(ctypes.byref(cfg), _ptr(w_gate), _ptr(w_up),
+                                   _ptr(w_down), _ptr(out_gate), _ptr(out_up),
+                                   _ptr(out_down), _stream(stream)))
+
+
 def moe_combine(cfg, ws, y, stream=None):
     _check(load().moe_combine(ctypes.byref(cfg), _ptr(ws), _nbytes(ws),
                               _ptr(y), _stream(stream)))
@@ -201,10 +217,13 @@ def moe_forward(cfg, logits, x, w_gate, w_up, w_down, y, ws, stream=None):
 
 
 def workspace_views(cfg: MoeConfig, ws: torch.Tensor) -> dict:
-    """torch views of the internal buffers of a uint8 workspace tensor."""
+    """torch views of the internal buffers of a uint8 workspace tensor.
+    xr and h are returned as raw bytes per expert ([E, P * row bytes], P =
+    min(C, T) rounded up to 64) since they are stored in the tiled layout."""
     L = workspace_layout(cfg)
     T, E, k = cfg.T, cfg.E, cfg.k
     ce = min(cfg.C, cfg.T)
+    pad = (ce + 63) // 64 * 64
     el = torch.bfloat16 if cfg.dtype == MOE_BF16 else torch.float32
     es = 2 if cfg.dtype == MOE_BF16 else 4
 
@@ -222,7 +241,7 @@ def workspace_views(cfg: MoeConfig, ws: torch.Tensor) -> dict:
         "pos": view("pos", T * k, i32, 4),
         "round_of": view("round_of", T * k, i32, 4),
         "row_of": view("row_of", T * k, i32, 4),
-        "xr": view("xr", E * ce * cfg.d_model, el, es).view(E * ce, cfg.d_model),
-        "h": view("h", E * ce * cfg.d_ff, el, es).view(E * ce, cfg.d_ff),
+        "xr": view("xr", E * pad * cfg.d_model * es, torch.uint8, 1).view(E, -1),
+        "h": view("h", E * pad * cfg.d_ff * es, torch.uint8, 1).view(E, -1),
         "z": view("z", T * k * cfg.d_model, el, es).view(T * k, cfg.d_model),
     }

@@ -50,18 +50,23 @@ moe_status_t check_cfg(const moe_config_t* c) {
     return fail(MOE_ERR_INVALID_ARGUMENT, "d_model and d_ff must be >= 1");
   if (c->dtype != MOE_F32 && c->dtype != MOE_BF16)
     return fail(MOE_ERR_INVALID_ARGUMENT, "unknown dtype");
+  if (c->weight_layout != MOE_WEIGHTS_ROW_MAJOR && c->weight_layout != MOE_WEIGHTS_TILED)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "unknown weight layout");
   if (c->E > 64) return fail(MOE_ERR_UNSUPPORTED, "E > 64 is not supported");
   if (c->d_model % 64 || c->d_ff % 64)
     return fail(MOE_ERR_UNSUPPORTED, "d_model and d_ff must be multiples of 64");
   const int64_t TK = c->T * (int64_t)c->k;
   if (c->T >= (int64_t(1) << 31) || TK >= (int64_t(1) << 31))
     return fail(MOE_ERR_UNSUPPORTED, "T*k must be < 2^31");
-  const int64_t ce = eff_capacity(c);
+  // per-expert matrices are addressed with 32-bit byte offsets
+  const int64_t ce_pad = (eff_capacity(c) + 63) / 64 * 64;
   const int64_t dm = c->d_model > c->d_ff ? c->d_model : c->d_ff;
-  if ((int64_t)c->E * ce >= (int64_t(1) << 31) || ce * dm >= (int64_t(1) << 31) ||
-      (int64_t)c->d_model * c->d_ff >= (int64_t(1) << 31))
+  const int64_t es = c->dtype == MOE_BF16 ? 2 : 4;
+  if ((int64_t)c->E * ce_pad >= (int64_t(1) << 31) ||
+      ce_pad * dm * es >= (int64_t(1) << 31) ||
+      (int64_t)c->d_model * c->d_ff * es >= (int64_t(1) << 31))
     return fail(MOE_ERR_UNSUPPORTED,
-                "E*C', C'*max(d,f) and d*f must be < 2^31");
+                "E*C', C'*max(d,f)*elem and d*f*elem must be < 2^31");
   return MOE_OK;
 }
 
@@ -70,7 +75,9 @@ void layout_of(const moe_config_t* c, moe_workspace_layout_t* L) {
   const size_t E = (size_t)c->E;
   const size_t ce = (size_t)eff_capacity(c);
   const size_t es = c->dtype == MOE_BF16 ? 2 : 4;
-  moe::Shape s{c->T, c->E, c->k, c->d_model, c->d_ff, (int)ce, c->dtype == MOE_BF16};
+  moe::Shape s{c->T, c->E, c->k, c->d_model, c->d_ff, (int)ce, c->dtype == MOE_BF16,
+               c->weight_layout == MOE_WEIGHTS_TILED};
+  const size_t ce_pad = (size_t)s.ce_pad();
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -87,8 +94,8 @@ void layout_of(const moe_config_t* c, moe_workspace_layout_t* L) {
   L->round_of = take(TK * 4);
   L->row_of = take(TK * 4);
   L->scratch = take((size_t)moe::plan_blocks(s) * E * 4);
-  L->xr = take(E * ce * (size_t)c->d_model * es);
-  L->h = take(E * ce * (size_t)c->d_ff * es);
+  L->xr = take(E * ce_pad * (size_t)c->d_model * es);
+  L->h = take(E * ce_pad * (size_t)c->d_ff * es);
   L->z = take(TK * (size_t)c->d_model * es);
   L->total = off;
 }
@@ -110,7 +117,7 @@ moe_status_t bind(const moe_config_t* c, void* ws, size_t ws_bytes, Bound* b) {
   if (ws_bytes < b->L.total)
     return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace too small");
   b->s = moe::Shape{c->T, c->E, c->k, c->d_model, c->d_ff, (int)eff_capacity(c),
-                    c->dtype == MOE_BF16};
+                    c->dtype == MOE_BF16, c->weight_layout == MOE_WEIGHTS_TILED};
   b->ws = static_cast<char*>(ws);
   char* w = b->ws;
   const moe_workspace_layout_t& L = b->L;
@@ -306,6 +313,36 @@ moe_status_t moe_expert_down(const moe_config_t* cfg, int32_t round,
   MOE_HIP(moe::launch_down(b.s, round, b.ws + b.L.h, w_down, b.pb, b.ws + b.L.z,
                            cus, static_cast<hipStream_t>(stream)),
           "down launch");
+  return MOE_OK;
+}
+
+moe_status_t moe_pack_weights(const moe_config_t* cfg, const void* w_gate,
+                              const void* w_up, const void* w_down,
+                              void* out_gate, void* out_up, void* out_down,
+                              void* stream) {
+  if (!cfg) return fail(MOE_ERR_INVALID_ARGUMENT, "config is NULL");
+  moe_config_t c = *cfg;
+  c.weight_layout = MOE_WEIGHTS_ROW_MAJOR;
+  moe_status_t st = check_cfg(&c);
+  if (st != MOE_OK) return st;
+  const void* in[3] = {w_gate, w_up, w_down};
+  void* out[3] = {out_gate, out_up, out_down};
+  const char* names[6] = {"w_gate", "w_up", "w_down", "out_gate", "out_up", "out_down"};
+  for (int i = 0; i < 3; ++i) {
+    if ((st = check_ptr(in[i], names[i])) != MOE_OK) return st;
+    if ((st = check_ptr(out[i], names[3 + i])) != MOE_OK) return st;
+  }
+  int cus = 0;
+  if ((st = num_cus(&cus)) != MOE_OK) return st;
+  moe::Shape s{c.T, c.E, c.k, c.d_model, c.d_ff, (int)eff_capacity(&c),
+               c.dtype == MOE_BF16, false};
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  MOE_HIP(moe::launch_pack_weights(s, w_gate, out_gate, c.d_ff, c.d_model, cus, hs),
+          "pack launch");
+  MOE_HIP(moe::launch_pack_weights(s, w_up, out_up, c.d_ff, c.d_model, cus, hs),
+          "pack launch");
+  MOE_HIP(moe::launch_pack_weights(s, w_down, out_down, c.d_model, c.d_ff, cus, hs),
+          "pack launch");
   return MOE_OK;
 }
 

@@ -55,6 +55,14 @@ def build(verbose: bool = False) -> str:
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
+    # a kernel whose host-side launch stub was not emitted leaves an
+    # undefined symbol that only shows when the library is loaded
+    und = subprocess.run(["nm", "-D", "--undefined-only", tmp],
+                         capture_output=True, text=True, check=True).stdout
+    missing = [ln.split()[-1] for ln in und.splitlines()
+               if "device_stub" in ln or "_ZN3moe" in ln]
+    if missing:
+        raise RuntimeError(f"{tmp}: undefined kernel symbols {missing}")
     os.replace(tmp, LIB)
     return LIB
 

@@ -65,3 +65,29 @@ __device__ __forceinline__ int rows_in_round(int n_e, int r, int ce) {
 }
 
 }  // namespace moe
+
+namespace moe {
+
+// Tiled matrix layout used for the round buffers and for packed weights.
+// A matrix of R rows (R a multiple of 64 after padding) and Kb bytes per
+// row (a multiple of 64) is stored as 4 KiB blocks of 64 rows x 64 bytes,
+// block (row / 64, byte / 64) at index (row / 64) * (Kb / 64) + byte / 64.
+// Inside a block, row r holds its four 16-byte chunks in the order
+// c ^ ((r >> 2) & 3) -- the bank swizzle the GEMM's LDS stages use -- so a
+// block can be copied into LDS verbatim, and one K stage of a 64-row band
+// is one contiguous 4 KiB read.
+constexpr int kTileRows = 64;
+constexpr int kTileRowBytes = 64;
+constexpr int kTileBytes = kTileRows * kTileRowBytes;
+
+__host__ __device__ __forceinline__ int64_t tiled_offset(int64_t row,
+                                                         int64_t byte,
+                                                         int64_t row_bytes) {
+  const int64_t blk = (row >> 6) * (row_bytes >> 6) + (byte >> 6);
+  const int r = (int)(row & 63);
+  const int b = (int)(byte & 63);
+  return blk * kTileBytes + r * kTileRowBytes + (((b >> 4) ^ ((r >> 2) & 3)) << 4) +
+         (b & 15);
+}
+
+}  // namespace moe

@@ -11,29 +11,40 @@
 
 namespace moe {
 
-// Row copy by one wavefront: n16 16-byte vectors, 4 loads in flight per
-// lane before the stores.
-__device__ __forceinline__ void wave_copy_row(const u32x4* __restrict__ src,
-                                              u32x4* __restrict__ dst, int n16,
-                                              int lane) {
+// Copy of one row into a tiled matrix by one wavefront: 16-byte chunk q of
+// the source row goes to tiled_offset(row, 16 q) of the destination; four
+// loads in flight per lane before the stores.
+__device__ __forceinline__ void wave_copy_row_tiled(const u32x4* __restrict__ src,
+                                                    char* __restrict__ dst_mat,
+                                                    int64_t row, int64_t row_bytes,
+                                                    int lane) {
+  const int n16 = (int)(row_bytes / 16);
+  const int64_t band = (row >> 6) * (row_bytes >> 6) * kTileBytes;
+  const int r = (int)(row & 63);
+  const int sw = (r >> 2) & 3;
+  auto dst = [&](int q) -> u32x4* {
+    return reinterpret_cast<u32x4*>(dst_mat + band + (int64_t)(q >> 2) * kTileBytes +
+                                    r * kTileRowBytes + (((q & 3) ^ sw) << 4));
+  };
   int v = lane;
   for (; v + 3 * kWave < n16; v += 4 * kWave) {
     const u32x4 a0 = src[v], a1 = src[v + kWave], a2 = src[v + 2 * kWave],
                 a3 = src[v + 3 * kWave];
-    dst[v] = a0;
-    dst[v + kWave] = a1;
-    dst[v + 2 * kWave] = a2;
-    dst[v + 3 * kWave] = a3;
+    *dst(v) = a0;
+    *dst(v + kWave) = a1;
+    *dst(v + 2 * kWave) = a2;
+    *dst(v + 3 * kWave) = a3;
   }
-  for (; v < n16; v += kWave) dst[v] = src[v];
+  for (; v < n16; v += kWave) *dst(v) = src[v];
 }
 
 // Round r: the round's rows are numbered expert by expert; row i belongs to
 // expert e with pre[e] <= i < pre[e+1] (pre = prefix of m(r, e)) and is slot
 // c = i - pre[e]. Its source token is perm[offsets[e] + r*C' + c] / k and its
-// destination is round-buffer row e*C' + c.
+// destination is row c of expert e's tiled round-buffer matrix.
 __global__ __launch_bounds__(256) void dispatch_kernel(
-    const char* __restrict__ x, int64_t row_bytes, int E, int k, int ce, int r,
+    const char* __restrict__ x, int64_t row_bytes, int E, int k, int ce,
+    int ce_pad, int r,
     const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ perm, char* __restrict__ xr) {
   __shared__ int pre[kWave + 1];
@@ -49,15 +60,13 @@ __global__ __launch_bounds__(256) void dispatch_kernel(
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kWave;
   const int64_t nwaves = (int64_t)gridDim.x * blockDim.x / kWave;
-  const int n16 = (int)(row_bytes / 16);
   for (int64_t i = wave; i < rows; i += nwaves) {
     const int e = segment_of(pre, E + 1, (int)i);
     const int c = (int)i - pre[e];
     const int a = perm[offsets[e] + (int64_t)r * ce + c];
     const int64_t t = a / k;
-    wave_copy_row(reinterpret_cast<const u32x4*>(x + t * row_bytes),
-                  reinterpret_cast<u32x4*>(xr + ((int64_t)e * ce + c) * row_bytes),
-                  n16, lane);
+    wave_copy_row_tiled(reinterpret_cast<const u32x4*>(x + t * row_bytes),
+                        xr + (int64_t)e * ce_pad * row_bytes, c, row_bytes, lane);
   }
 }
 
@@ -73,8 +82,41 @@ hipError_t launch_dispatch(const Shape& s, int r, const void* x,
   if (blocks > cap) blocks = cap;
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL(dispatch_kernel, dim3((unsigned)blocks), dim3(256), 0, st,
-                     static_cast<const char*>(x), row_bytes, s.E, s.k, s.ce, r,
+                     static_cast<const char*>(x), row_bytes, s.E, s.k, s.ce,
+                     s.ce_pad(), r,
                      b.counts, b.offsets, b.perm, static_cast<char*>(xr));
+  return hipGetLastError();
+}
+
+// Row-major [E][rows][cols] -> tiled per expert (moe_pack_weights): one
+// thread per 16-byte chunk, reads coalesced.
+__global__ __launch_bounds__(256) void pack_tiled_kernel(
+    const char* __restrict__ src, char* __restrict__ dst, int64_t chunks,
+    int rows, int64_t row_bytes) {
+  const int64_t cpr = row_bytes / 16;
+  const int64_t per_mat = (int64_t)rows * cpr;
+  for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < chunks;
+       g += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t e = g / per_mat;
+    const int64_t w = g - e * per_mat;
+    const int64_t row = w / cpr;
+    const int64_t q = w - row * cpr;
+    const int64_t base = e * per_mat * 16;
+    *reinterpret_cast<u32x4*>(dst + base + tiled_offset(row, q * 16, row_bytes)) =
+        *reinterpret_cast<const u32x4*>(src + g * 16);
+  }
+}
+
+hipError_t launch_pack_weights(const Shape& s, const void* src, void* dst,
+                               int rows, int cols, int num_cus, hipStream_t st) {
+  const int64_t row_bytes = (int64_t)cols * (s.bf16 ? 2 : 4);
+  const int64_t chunks = (int64_t)s.E * rows * (row_bytes / 16);
+  int64_t blocks = (chunks + 255) / 256;
+  const int64_t cap = (int64_t)num_cus * 16;
+  if (blocks > cap) blocks = cap;
+  hipLaunchKernelGGL(pack_tiled_kernel, dim3((unsigned)blocks), dim3(256), 0, st,
+                     static_cast<const char*>(src), static_cast<char*>(dst), chunks,
+                     rows, row_bytes);
   return hipGetLastError();
 }
 

@@ -20,11 +20,10 @@
 // stores in the epilogue.
 //
 // Tiles: 256 threads = 2 x 2 wavefronts; wavefront (wm, wn) owns WJ 32-token
-// blocks and WI 32-weight-row blocks. K advances 128 bytes per stage
-// (64 bf16 or 32 fp32), double-buffered in LDS with one barrier per stage.
-// LDS rows are 128 bytes; the 16-byte chunk c of row q is stored at chunk
-// c ^ (q & 7), so the eight rows read together by a fragment load fall in
-// distinct banks.
+// blocks and WI 32-weight-row blocks. K advances 64 bytes per stage (32 bf16
+// or 16 fp32) through a ring of LDS stages filled by LDS-direct buffer loads,
+// with up to three stages in flight and one barrier per stage. Fragment
+// reads run one MFMA step ahead of the MFMAs that use them.
 //
 // Determinism: every output element is one fixed sequence of MFMA steps
 // over K in ascending order, whatever the round, the slot or the tile it
@@ -37,32 +36,43 @@ namespace moe {
 template <typename Elem>
 struct MmaOp;
 
+// LDS stage layout: every tile row (weight rows first, then token rows)
+// holds 64 bytes of K per stage, as four 16-byte chunks; logical chunk c of
+// row q sits at physical chunk c ^ ((q >> 2) & 3). The 16 rows that one
+// ds_read_b128 touches per LDS cycle then cover all 64 banks once.
+constexpr int kRowBytes = 64;
+
+__device__ __forceinline__ int lds_swizzle(int row, int chunk) {
+  return (chunk ^ ((row >> 2) & 3)) * 16;
+}
+
 // v_mfma_f32_32x32x16_bf16: lane l supplies row (l % 32) and k-run
-// [8*(l/32), 8*(l/32)+8) of its operand.
+// [8*(l/32), 8*(l/32)+8) of its operand; one stage holds 2 such steps.
 template <>
 struct MmaOp<bf16> {
-  static constexpr int kSteps = 4;  // instructions per 128-byte k stage
+  static constexpr int kSteps = 2;
   typedef bf16x8 frag_t;
-  __device__ static __forceinline__ frag_t load(const char* row, int step,
-                                                int half, int swz) {
-    const int chunk = (2 * step + half) ^ swz;
-    return *reinterpret_cast<const frag_t*>(row + chunk * 16);
+  __device__ static __forceinline__ frag_t load(const char* stage, int row,
+                                                int step, int half) {
+    return *reinterpret_cast<const frag_t*>(stage + row * kRowBytes +
+                                            lds_swizzle(row, 2 * step + half));
   }
   __device__ static __forceinline__ void mma(f32x16& acc, frag_t a, frag_t b) {
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
   }
 };
 
-// v_mfma_f32_32x32x2f32: lane l supplies row (l % 32) and k = l / 32.
+// v_mfma_f32_32x32x2f32: lane l supplies row (l % 32) and k = l / 32; one
+// stage (16 floats) holds 8 steps.
 template <>
 struct MmaOp<float> {
-  static constexpr int kSteps = 16;
+  static constexpr int kSteps = 8;
   typedef float frag_t;
-  __device__ static __forceinline__ frag_t load(const char* row, int step,
-                                                int half, int swz) {
+  __device__ static __forceinline__ frag_t load(const char* stage, int row,
+                                                int step, int half) {
     const int byte = (2 * step + half) * 4;
-    const int chunk = (byte >> 4) ^ swz;
-    return *reinterpret_cast<const float*>(row + chunk * 16 + (byte & 15));
+    return *reinterpret_cast<const float*>(stage + row * kRowBytes +
+                                           lds_swizzle(row, byte >> 4) + (byte & 15));
   }
   __device__ static __forceinline__ void mma(f32x16& acc, frag_t a, frag_t b) {
     acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
@@ -79,37 +89,157 @@ struct GemmParams {
   const int32_t* offsets;
   const int32_t* perm;
   int E, ce, r, K, N;  // N = output features: f (gate/up) or d (down)
+  int ce_pad;          // round-buffer rows per expert (multiple of 64)
+  int tiled_w;         // weights in the tiled layout (else row-major)
 };
 
 __device__ __forceinline__ float silu_mul(float g, float u) {
   return g / (1.0f + expf(-g)) * u;
 }
 
+// Buffer resource word 3 for gfx9-family raw (untyped) buffer access.
+constexpr int kRsrcWord3 = 0x00020000;
+
+typedef __attribute__((address_space(3))) char lds_char;
+typedef int int32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor (scalar registers) over `bytes` bytes at `base`.
+__device__ __forceinline__ int32x4 buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  int32x4 r;
+  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r.y = __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xFFFFu));
+  r.z = __builtin_amdgcn_readfirstlane((int)bytes);
+  r.w = kRsrcWord3;
+  return r;
+}
+
+// LDS-direct 16-byte load: lane i of the wavefront reads
+// base + voff + soff and writes LDS bytes [dst + 16*i, dst + 16*i + 16).
+// Issued from asm so that the compiler does not order later LDS reads of
+// other ring slots behind it; the kernel waits for it with explicit vmcnt
+// counts. It has no register results. M0 (which holds the LDS address) is
+// set inside the same statement; the compiler keeps nothing in M0 here.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_dma16(int32x4 rsrc, uint32_t voff,
+                                          uint32_t soff, lds_char* dst) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               ::"s"(m0), "v"(voff), "s"(rsrc), "s"(soff)
+               : "m0");
+}
+#pragma clang diagnostic pop
+
+// Wait until at most N of this wavefront's vector-memory operations are
+// outstanding (the LDS-direct loads of later stages), then join the
+// workgroup barrier. A bare s_barrier: __syncthreads() would also drain
+// every in-flight stage.
+template <int N>
+__device__ __forceinline__ void wait_vmem_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(N) : "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <typename Elem, int WI, int WJ>
+struct Frags {
+  typename MmaOp<Elem>::frag_t a[WI], b[WJ];
+};
+
+// Fragments of MFMA step s: weight rows (A operand) and token rows (B).
+template <typename Elem, int WI, int WJ>
+__device__ __forceinline__ void load_frags(Frags<Elem, WI, WJ>& f,
+                                           const char* stage, int wrow,
+                                           int trow, int s, int half) {
+#pragma unroll
+  for (int ib = 0; ib < WI; ++ib)
+    f.a[ib] = MmaOp<Elem>::load(stage, wrow + 32 * ib, s, half);
+#pragma unroll
+  for (int jb = 0; jb < WJ; ++jb)
+    f.b[jb] = MmaOp<Elem>::load(stage, trow + 32 * jb, s, half);
+}
+
+template <typename Elem, int WI, int WJ>
+__device__ __forceinline__ void mma_step(f32x16 (&acc)[WI][WJ],
+                                         const Frags<Elem, WI, WJ>& f) {
+#pragma unroll
+  for (int ib = 0; ib < WI; ++ib)
+#pragma unroll
+    for (int jb = 0; jb < WJ; ++jb) MmaOp<Elem>::mma(acc[ib][jb], f.a[ib], f.b[jb]);
+}
+
+// Scheduling pins for one MFMA step: one LDS fragment read after each of
+// the first MFMAs, then (when a stage is being fetched) one LDS-direct
+// buffer load after each of the following MFMAs, then the remaining MFMAs.
+template <int kMfma, int kReads, int kLoads>
+__device__ __forceinline__ void pin_step() {
+  constexpr int nl = kReads < kMfma ? kReads : kMfma;
+#pragma unroll
+  for (int g = 0; g < nl; ++g) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+  }
+  if constexpr (kReads > nl) __builtin_amdgcn_sched_group_barrier(0x100, kReads - nl, 0);
+  constexpr int room = kMfma - nl;
+  constexpr int nv = kLoads < room ? kLoads : room;
+#pragma unroll
+  for (int g = 0; g < nv; ++g) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+  }
+  if constexpr (kLoads > nv) __builtin_amdgcn_sched_group_barrier(0x020, kLoads - nv, 0);
+  if constexpr (room - nv > 0) __builtin_amdgcn_sched_group_barrier(0x008, room - nv, 0);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// K pipeline: a ring of kSlots LDS stages. Each stage has one barrier,
+// placed before its last MFMA step; by then the stage's last fragments are
+// in registers, so its slot is free and the barrier issues the LDS-direct
+// fetch of stage kt + kSlots into it. The barrier first waits for stage
+// kt + 1, so up to kSlots - 1 later stages stay in flight, and the next
+// stage's first fragments load while the last step's MFMAs run.
+constexpr int kSlots = 4;  // the stage loop below names four slots
+
 template <typename Elem, int WI, int WJ, bool kGateUp>
 __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
     GemmParams<Elem> p) {
-  typedef MmaOp<Elem> Op;
-  constexpr int kVec = 16 / sizeof(Elem);        // elements per 16 B chunk
-  constexpr int kStageK = 128 / sizeof(Elem);    // k elements per stage
+  typedef Frags<Elem, WI, WJ> frags_t;
+  constexpr int kEs = sizeof(Elem);
+  constexpr int kStageK = kRowBytes / kEs;       // k elements per stage
   constexpr int BN = 64 * WI;                    // weight rows per tile
   constexpr int BM = 64 * WJ;                    // token rows per tile
   constexpr int NF = kGateUp ? BN / 2 : BN;      // output features per tile
-  constexpr int kWPasses = BN / 32;              // 32 rows per load pass
-  constexpr int kTPasses = BM / 32;
-  constexpr int kStageBytes = (BN + BM) * 128;
+  constexpr int kWPasses = BN / 64;              // 64 rows per load pass
+  constexpr int kTPasses = BM / 64;
+  constexpr int kPasses = kWPasses + kTPasses;
+  constexpr int kStageBytes = (BN + BM) * kRowBytes;
+  constexpr int kSteps = MmaOp<Elem>::kSteps;
+  constexpr int kMfmaPerStep = WI * WJ;
+  constexpr int kReadsPerStep = WI + WJ;
+  static_assert(kSteps % 2 == 0, "fragment sets alternate by step");
+  static_assert(!kGateUp || WI % 4 == 0,
+                "each gate/up load pass must stay inside one matrix");
+  static_assert(kPasses * (kSlots - 1) <= 63, "vmcnt budget");
 
-  __shared__ __attribute__((aligned(16))) char smem[2 * kStageBytes];
+  // the ring: kSlots stages as separate LDS objects, so the compiler can
+  // tell a fragment read of one slot from a pending LDS-direct fill of
+  // another and needs no conservative wait between them
+  __shared__ __attribute__((aligned(1024))) char slot0[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char slot1[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char slot2[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char slot3[kStageBytes];
   __shared__ int tile_pre[kWave + 1];
   __shared__ int rows_m[kWave];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave_id = tid / kWave;
+  const int wave_id = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wn = wave_id & 1;   // weight-row half of the tile
   const int wm = wave_id >> 1;  // token half of the tile
   const int half = lane / 32;
   const int l32 = lane & 31;
-  const int swz = lane & 7;
 
   const int nt = (p.N + NF - 1) / NF;
   if (tid < kWave) {
@@ -122,51 +252,71 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
     if (e == 0) tile_pre[0] = 0;
   }
   __syncthreads();
-  const int total = tile_pre[p.E];
+  const int total = __builtin_amdgcn_readfirstlane(tile_pre[p.E]);
 
   // XCD-contiguous walk: workgroup b runs on XCD b % 8.
   const int G = gridDim.x;
   const int slot = (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8);
 
-  // load-pass geometry: thread covers chunk ch of rows r0 + 32*i
-  const int r0 = tid >> 3;
-  const int ch = tid & 7;
+  // Load passes: pass i fills stage rows 64*i .. 64*i+63; lane tid writes
+  // bytes [16*tid, 16*tid+16) of the pass: row r0 = tid / 4, physical
+  // chunk tid % 4, i.e. logical chunk (tid % 4) ^ ((r0 >> 2) & 3).
+  const int r0 = tid >> 2;
+  const int chunk = (tid & 3) ^ ((r0 >> 2) & 3);
+  // fragment rows of this lane inside a stage
+  const int wrow = wn * (BN / 2) + l32;
+  const int trow = BN + wm * (BM / 2) + l32;
 
   for (int tile = slot; tile < total; tile += G) {
-    const int e = segment_of(tile_pre, p.E + 1, tile);
-    const int m = rows_m[e];
+    const int e = __builtin_amdgcn_readfirstlane(segment_of(tile_pre, p.E + 1, tile));
+    const int m = __builtin_amdgcn_readfirstlane(rows_m[e]);
     const int mt = (m + BM - 1) / BM;
-    const int local = tile - tile_pre[e];
+    const int local = tile - __builtin_amdgcn_readfirstlane(tile_pre[e]);
     const int n0 = (local / mt) * NF;
     const int m0 = (local % mt) * BM;
 
-    const Elem* wbase0 = p.w0 + (int64_t)e * p.N * p.K;
-    const Elem* wbase1 = kGateUp ? p.w1 + (int64_t)e * p.N * p.K : nullptr;
-    const Elem* abase = p.act + (int64_t)e * p.ce * p.K;
+    const uint32_t wbytes = (uint32_t)p.N * p.K * kEs;
+    const uint32_t kbytes = (uint32_t)p.K * kEs;    // bytes of one row
+    const uint32_t band_bytes = kbytes * kTileRows;  // one 64-row band, tiled
+    const __amdgpu_buffer_rsrc_t rw0 = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.w0 + (int64_t)e * p.N * p.K), 0, (int)wbytes, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rw1 = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(kGateUp ? p.w1 + (int64_t)e * p.N * p.K : p.w0), 0, (int)wbytes,
+        kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.act + (int64_t)e * p.ce_pad * p.K), 0,
+        (int)((uint32_t)p.ce_pad * kbytes), kRsrcWord3);
 
-    // per-pass source rows as 32-bit element offsets inside the expert's
-    // matrices (the layer's limits keep N*K and C'*K below 2^31). For gate/up
-    // the first half of each wavefront's weight rows are gate rows and the
-    // second half up rows of the same features; which one a pass loads is
-    // fixed by the pass index alone.
-    int32_t off[kWPasses + kTPasses];
+    // Byte offsets (k = 0) of what this lane fetches in each pass. A pass
+    // covers one 64-row band: tiled operands give one contiguous 4 KiB
+    // block per stage (the lane's 16 bytes at 16 * tid); row-major weights
+    // give this lane's row r0 of the band, logical chunk `chunk`. For
+    // gate/up, the first half of each wavefront's weight rows are gate rows
+    // and the second half up rows of the same features; a 64-row band lies
+    // inside one of them, so its matrix follows from the pass index.
+    uint32_t voff[kPasses];
 #pragma unroll
     for (int i = 0; i < kWPasses; ++i) {
-      int feat;
-      if (kGateUp)
-        feat = n0 + (i / WI) * (BN / 4) + 32 * ((i % WI) % (WI / 2)) + r0;
-      else
-        feat = n0 + 32 * i + r0;
-      feat = feat < p.N ? feat : p.N - 1;
-      off[i] = feat * p.K + ch * kVec;
+      int feat0;
+      if (kGateUp) {
+        const int rho = 64 * i;  // first row of the pass
+        feat0 = n0 + (rho / (BN / 2)) * (BN / 4) + (rho % (BN / 2)) % (BN / 4);
+      } else {
+        feat0 = n0 + 64 * i;
+      }
+      if (p.tiled_w) {
+        const int band = feat0 < p.N ? feat0 / 64 : p.N / 64 - 1;
+        voff[i] = (uint32_t)band * band_bytes + tid * 16;
+      } else {
+        int feat = feat0 + r0;
+        feat = feat < p.N ? feat : p.N - 1;
+        voff[i] = (uint32_t)feat * kbytes + chunk * 16;
+      }
     }
 #pragma unroll
-    for (int j = 0; j < kTPasses; ++j) {
-      int c = m0 + r0 + 32 * j;
-      c = c < m ? c : m - 1;
-      off[kWPasses + j] = c * p.K + ch * kVec;
-    }
-    const int lds_w = (r0 * 128) + ((ch ^ (r0 & 7)) * 16);
+    for (int j = 0; j < kTPasses; ++j)  // bands past ce_pad read as zeros
+      voff[kWPasses + j] = (uint32_t)(m0 / 64 + j) * band_bytes + tid * 16;
+    const uint32_t wstride = p.tiled_w ? (uint32_t)kTileBytes : (uint32_t)kRowBytes;
 
     f32x16 acc[WI][WJ];
 #pragma unroll
@@ -176,56 +326,76 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[ib][jb][v] = 0.f;
 
-    auto src = [&](int i) -> const Elem* {
-      if (i >= kWPasses) return abase + off[i];
-      if (kGateUp && (i % WI) >= WI / 2) return wbase1 + off[i];
-      return wbase0 + off[i];
-    };
-    u32x4 stage[kWPasses + kTPasses];
     const int KT = p.K / kStageK;
 
-    // prologue: stage 0
+    // Fetch stage ks into `slot` with LDS-direct buffer loads (lane i of a
+    // wavefront writes bytes [16 i, 16 i + 16) of its 1 KiB share of each
+    // 4 KiB pass). A stage at or past the end of K is fetched with an
+    // offset beyond the buffer: the hardware returns zeros without touching
+    // memory, so such a stage adds exact zeros to the accumulators. K is
+    // walked in groups of kSlots stages, the last group padded this way.
+    auto fetch = [&](char* slot, int ks) {
+      lds_char* dst = (lds_char*)slot + wave_id * 1024;
+      const bool live = ks < KT;
+      const uint32_t soff_w = live ? (uint32_t)ks * wstride : 0x80000000u;
+      const uint32_t soff_t = live ? (uint32_t)ks * kTileBytes : 0x80000000u;
 #pragma unroll
-    for (int i = 0; i < kWPasses + kTPasses; ++i)
-      stage[i] = *reinterpret_cast<const u32x4*>(src(i));
-#pragma unroll
-    for (int i = 0; i < kWPasses + kTPasses; ++i)
-      *reinterpret_cast<u32x4*>(smem + lds_w + i * 32 * 128) = stage[i];
-    __syncthreads();
+      for (int i = 0; i < kPasses; ++i) {
+        const __amdgpu_buffer_rsrc_t rs =
+            i >= kWPasses ? ra
+                          : ((kGateUp && ((64 * i) % (BN / 2)) >= BN / 4) ? rw1 : rw0);
+        // (scalar copy: clang's host pass drops the launch stub when an
+        // array element is passed to this builtin directly)
+        const uint32_t vo = voff[i];
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (void __attribute__((address_space(3)))*)(dst + i * 4096), 16, vo,
+            i >= kWPasses ? soff_t : soff_w, 0, 0);
+      }
+    };
 
-    for (int kt = 0; kt < KT; ++kt) {
-      const char* buf = smem + (kt & 1) * kStageBytes;
-      const bool more = kt + 1 < KT;
-      if (more) {
-        const int koff = (kt + 1) * kStageK;
-#pragma unroll
-        for (int i = 0; i < kWPasses + kTPasses; ++i)
-          stage[i] = *reinterpret_cast<const u32x4*>(src(i) + koff);
-      }
-      const char* wrow = buf + (wn * (BN / 2) + l32) * 128;
-      const char* trow = buf + BN * 128 + (wm * (BM / 2) + l32) * 128;
-#pragma unroll
-      for (int s = 0; s < Op::kSteps; ++s) {
-        typename Op::frag_t a[WI], b[WJ];
-#pragma unroll
-        for (int ib = 0; ib < WI; ++ib) a[ib] = Op::load(wrow + ib * 32 * 128, s, half, swz);
-#pragma unroll
-        for (int jb = 0; jb < WJ; ++jb) b[jb] = Op::load(trow + jb * 32 * 128, s, half, swz);
-#pragma unroll
-        for (int ib = 0; ib < WI; ++ib)
-#pragma unroll
-          for (int jb = 0; jb < WJ; ++jb) Op::mma(acc[ib][jb], a[ib], b[jb]);
-      }
-      if (more) {
-        char* nbuf = smem + ((kt + 1) & 1) * kStageBytes;
-#pragma unroll
-        for (int i = 0; i < kWPasses + kTPasses; ++i)
-          *reinterpret_cast<u32x4*>(nbuf + lds_w + i * 32 * 128) = stage[i];
-      }
-      __syncthreads();
+    // One stage: its first MFMA step also issues the fetch of stage kt + 3
+    // into the slot freed at the previous barrier, one load between
+    // consecutive MFMAs; the barrier before the last step waits for stage
+    // kt + 1 (stages kt + 2 and kt + 3 stay in flight), after which the
+    // next stage's first fragments load while the last step's MFMAs run.
+#define MOE_STAGE(CUR, NXT, FSLOT, KT_)                                          \
+    _Pragma("unroll") for (int s = 0; s < kSteps; s += 2) {                     \
+      load_frags<Elem, WI, WJ>(f1, CUR, wrow, trow, s + 1, half);               \
+      if (s == 0) fetch(FSLOT, (KT_) + kSlots - 1);                             \
+      mma_step<Elem, WI, WJ>(acc, f0);                                          \
+      if (s == 0)                                                               \
+        pin_step<kMfmaPerStep, kReadsPerStep, kPasses>();                       \
+      else                                                                      \
+        pin_step<kMfmaPerStep, kReadsPerStep, 0>();                             \
+      if (s + 2 < kSteps) {                                                     \
+        load_frags<Elem, WI, WJ>(f0, CUR, wrow, trow, s + 2, half);             \
+      } else {                                                                  \
+        wait_vmem_barrier<(kSlots - 2) * kPasses>();                            \
+        load_frags<Elem, WI, WJ>(f0, NXT, wrow, trow, 0, half);                 \
+      }                                                                         \
+      mma_step<Elem, WI, WJ>(acc, f1);                                          \
+      pin_step<kMfmaPerStep, kReadsPerStep, 0>();                               \
     }
 
-    // epilogue
+    // prologue: stages 0 .. kSlots-2 in flight; wait for stage 0
+    fetch(slot0, 0);
+    fetch(slot1, 1);
+    fetch(slot2, 2);
+    wait_vmem_barrier<(kSlots - 2) * kPasses>();
+
+    frags_t f0, f1;
+    load_frags<Elem, WI, WJ>(f0, slot0, wrow, trow, 0, half);
+    const int KT4 = (KT + kSlots - 1) / kSlots * kSlots;
+    for (int kt = 0; kt < KT4; kt += kSlots) {
+      MOE_STAGE(slot0, slot1, slot3, kt)
+      MOE_STAGE(slot1, slot2, slot0, kt + 1)
+      MOE_STAGE(slot2, slot3, slot1, kt + 2)
+      MOE_STAGE(slot3, slot0, slot2, kt + 3)
+    }
+#undef MOE_STAGE
+
+    // epilogue: lane holds, for token j = l32 of each 32-token block, four
+    // runs of four consecutive output features
     typedef Elem vec4_t __attribute__((ext_vector_type(4)));
 #pragma unroll
     for (int jb = 0; jb < WJ; ++jb) {
@@ -233,12 +403,14 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
       if (c >= m) continue;
       Elem* orow;
       if (kGateUp) {
-        orow = p.out + ((int64_t)e * p.ce + c) * p.N;
+        // h: row c of expert e's tiled matrix
+        orow = p.out + (int64_t)e * p.ce_pad * p.N;
       } else {
         const int a = p.perm[p.offsets[e] + (int64_t)p.r * p.ce + c];
         orow = p.out + (int64_t)a * p.N;
       }
       if (kGateUp) {
+        char* hmat = reinterpret_cast<char*>(orow);
 #pragma unroll
         for (int ib = 0; ib < WI / 2; ++ib) {
 #pragma unroll
@@ -250,7 +422,8 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
             for (int q = 0; q < 4; ++q)
               o[q] = from_f32<Elem>(silu_mul(acc[ib][jb][4 * g4 + q],
                                              acc[ib + WI / 2][jb][4 * g4 + q]));
-            *reinterpret_cast<vec4_t*>(orow + feat) = o;
+            *reinterpret_cast<vec4_t*>(
+                hmat + tiled_offset(c, (int64_t)feat * kEs, (int64_t)p.N * kEs)) = o;
           }
         }
       } else {
@@ -268,11 +441,14 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
         }
       }
     }
+    // the next tile's prologue refills the ring: every wavefront must be
+    // done with its last fragment reads
+    __syncthreads();
   }
 }
 
 // Tile shapes: bf16 uses 256 x 256 tiles (4 x 4 MFMA blocks per wavefront);
-// fp32 uses 128 x 128.
+// fp32 uses 256 weight rows x 128 tokens.
 template <typename Elem>
 struct TileCfg;
 template <>
@@ -281,7 +457,7 @@ struct TileCfg<bf16> {
 };
 template <>
 struct TileCfg<float> {
-  static constexpr int WI = 2, WJ = 2;
+  static constexpr int WI = 4, WJ = 2;
 };
 
 template <typename Elem, bool kGateUp>
@@ -301,12 +477,14 @@ hipError_t launch_gate_up(const Shape& s, int r, const void* xr,
   if (s.bf16) {
     GemmParams<bf16> p{static_cast<const bf16*>(xr), static_cast<const bf16*>(wg),
                        static_cast<const bf16*>(wu), static_cast<bf16*>(h),
-                       counts, nullptr, nullptr, s.E, s.ce, r, s.d, s.f};
+                       counts, nullptr, nullptr, s.E, s.ce, r, s.d, s.f,
+                       s.ce_pad(), s.tiled_w};
     return launch_gemm<bf16, true>(p, num_cus, st);
   }
   GemmParams<float> p{static_cast<const float*>(xr), static_cast<const float*>(wg),
                       static_cast<const float*>(wu), static_cast<float*>(h),
-                      counts, nullptr, nullptr, s.E, s.ce, r, s.d, s.f};
+                      counts, nullptr, nullptr, s.E, s.ce, r, s.d, s.f,
+                      s.ce_pad(), s.tiled_w};
   return launch_gemm<float, true>(p, num_cus, st);
 }
 
@@ -316,12 +494,12 @@ hipError_t launch_down(const Shape& s, int r, const void* h, const void* wd,
   if (s.bf16) {
     GemmParams<bf16> p{static_cast<const bf16*>(h), static_cast<const bf16*>(wd),
                        nullptr, static_cast<bf16*>(z), b.counts, b.offsets,
-                       b.perm, s.E, s.ce, r, s.f, s.d};
+                       b.perm, s.E, s.ce, r, s.f, s.d, s.ce_pad(), s.tiled_w};
     return launch_gemm<bf16, false>(p, num_cus, st);
   }
   GemmParams<float> p{static_cast<const float*>(h), static_cast<const float*>(wd),
                       nullptr, static_cast<float*>(z), b.counts, b.offsets,
-                      b.perm, s.E, s.ce, r, s.f, s.d};
+                      b.perm, s.E, s.ce, r, s.f, s.d, s.ce_pad(), s.tiled_w};
   return launch_gemm<float, false>(p, num_cus, st);
 }
 

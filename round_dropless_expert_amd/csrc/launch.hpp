@@ -11,8 +11,10 @@ namespace moe {
 struct Shape {
   int64_t T;
   int E, k, d, f;
-  int ce;       // min(C, T)
-  bool bf16;    // element type of x, weights, y and the round buffers
+  int ce;        // min(C, T)
+  bool bf16;     // element type of x, weights, y and the round buffers
+  bool tiled_w;  // weights in the tiled layout of moe_pack_weights
+  int ce_pad() const { return (ce + 63) / 64 * 64; }  // round-buffer rows per expert
 };
 
 // Plan-internal chunk of assignments handled by one workgroup.
@@ -47,6 +49,8 @@ hipError_t launch_gate_up(const Shape& s, int r, const void* xr,
 hipError_t launch_down(const Shape& s, int r, const void* h, const void* wd,
                        const PlanBuffers& b, void* z, int num_cus,
                        hipStream_t st);
+hipError_t launch_pack_weights(const Shape& s, const void* src, void* dst,
+                               int rows, int cols, int num_cus, hipStream_t st);
 hipError_t launch_combine(const Shape& s, const void* z, const float* weight,
                           void* y, int num_cus, hipStream_t st);
 

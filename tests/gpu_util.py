@@ -44,10 +44,22 @@ class Case:
         self.wd = up(self.inp.Wd)
         self.idx, self.wt = oracle.route(self.inp.logits, w.k)
 
-    def cfg(self, C=None):
+    def cfg(self, C=None, weight_layout="tiled"):
         w = self.w
         return B.config(w.T, w.E, w.k, w.d_model, w.d_ff,
-                        w.C if C is None else C, w.dtype)
+                        w.C if C is None else C, w.dtype, weight_layout)
+
+    def weights(self, layout="tiled"):
+        """(w_gate, w_up, w_down) on the device in the given layout."""
+        if layout == "row_major":
+            return self.wg, self.wu, self.wd
+        if not hasattr(self, "_packed"):
+            out = [torch.empty_like(t) for t in (self.wg, self.wu, self.wd)]
+            note(f"{self.w.name}: moe_pack_weights")
+            B.moe_pack_weights(self.cfg(), self.wg, self.wu, self.wd, *out)
+            torch.cuda.synchronize()
+            self._packed = tuple(out)
+        return self._packed
 
     def workspace(self, cfg, poison=True):
         n = B.workspace_size(cfg)
@@ -105,3 +117,22 @@ def sample_tokens(T: int, p: oracle.Plan, k: int, n: int, seed: int = 1):
         last = rng.choice(last, n // 2, replace=False)
     rand = rng.choice(T, min(T, n), replace=False)
     return np.unique(np.concatenate([[0, T - 1], last, rand])).astype(np.int64)
+
+
+def tiled_index(rows: int, row_bytes: int) -> np.ndarray:
+    """Byte offset, in the tiled layout (64-row x 64-byte blocks, chunk c of
+    row r stored at c ^ ((r >> 2) & 3)), of every byte of a rows x row_bytes
+    row-major matrix. rows must be a multiple of 64."""
+    r = np.arange(rows, dtype=np.int64)[:, None]
+    b = np.arange(row_bytes, dtype=np.int64)[None, :]
+    blk = (r >> 6) * (row_bytes >> 6) + (b >> 6)
+    rr = r & 63
+    bb = b & 63
+    return blk * 4096 + rr * 64 + (((bb >> 4) ^ ((rr >> 2) & 3)) << 4) + (bb & 15)
+
+
+def untile(mat_bytes: torch.Tensor, rows: int, cols: int, dtype) -> torch.Tensor:
+    """Row-major [rows, cols] tensor of `dtype` from one tiled matrix."""
+    es = torch.empty(0, dtype=dtype).element_size()
+    idx = torch.from_numpy(tiled_index(rows, cols * es)).to(mat_bytes.device)
+    return mat_bytes[idx.reshape(-1)].view(rows, cols * es).view(dtype)

@@ -53,10 +53,11 @@ def ceil_div(a, b):
 def expected_total(T, E, k, d, f, C, es):
     al = lambda v: (v + 255) // 256 * 256
     ce = min(C, T)
+    pad = ceil_div(ce, 64) * 64  # round-buffer rows per expert, tiled
     TK = T * k
     nb = ceil_div(TK, 1024)
     parts = [TK * 4, TK * 4, E * 4, (E + 1) * 4, 4, TK * 4, TK * 4, TK * 4,
-             TK * 4, nb * E * 4, E * ce * d * es, E * ce * f * es, TK * d * es]
+             TK * 4, nb * E * 4, E * pad * d * es, E * pad * f * es, TK * d * es]
     return sum(al(p) for p in parts)
 
 
@@ -90,6 +91,7 @@ def test_workspace_is_a_function_of_the_config_only(B):
 BAD_CONFIGS = [
     (dict(T=0), 1), (dict(E=0), 1), (dict(k=0), 1), (dict(k=9), 1),
     (dict(C=0), 1), (dict(d_model=0), 1), (dict(dtype=7), 1),
+    (dict(weight_layout=2), 1),
     (dict(E=65, k=2), 2), (dict(d_model=96), 2), (dict(d_ff=100), 2),
     (dict(T=1 << 29, k=4), 2),
 ]
@@ -97,7 +99,8 @@ BAD_CONFIGS = [
 
 @pytest.mark.parametrize("change,status", BAD_CONFIGS)
 def test_config_validation(B, change, status):
-    base = dict(T=512, E=8, k=2, d_model=64, d_ff=128, C=64, dtype=0)
+    base = dict(T=512, E=8, k=2, d_model=64, d_ff=128, C=64, dtype=0,
+                weight_layout=0)
     base.update(change)
     cfg = B.config(**base)
     assert B.check_config(cfg) == status
@@ -139,4 +142,6 @@ def test_pointer_and_workspace_checks_before_any_hip_call(B):
     assert L.moe_expert_ffn(c, 8, p, p, p, p, need, None) == \
         B.MOE_ERR_INVALID_ARGUMENT
     assert L.moe_combine(c, p, need, None, None) == B.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_pack_weights(c, p, p, None, p, p, p, None) == \
+        B.MOE_ERR_INVALID_ARGUMENT
     assert L.moe_status_string(3) == b"MOE_ERR_WORKSPACE_TOO_SMALL"

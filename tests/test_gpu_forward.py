@@ -23,12 +23,13 @@ def get_case(name):
     return _cache[name]
 
 
-def forward(case, C=None, poison=True):
-    cfg = case.cfg(C)
+def forward(case, C=None, poison=True, layout="tiled"):
+    cfg = case.cfg(C, weight_layout=layout)
+    wg, wu, wd = case.weights(layout)
     ws = case.workspace(cfg, poison=poison)
     y = case.new_y()
-    note(f"{case.w.name}: moe_forward C={cfg.C}")
-    B.moe_forward(cfg, case.logits, case.x, case.wg, case.wu, case.wd, y, ws)
+    note(f"{case.w.name}: moe_forward C={cfg.C} weights={layout}")
+    B.moe_forward(cfg, case.logits, case.x, wg, wu, wd, y, ws)
     torch.cuda.synchronize()
     return cfg, ws, y
 
@@ -54,10 +55,12 @@ def test_forward_matches_oracle(name):
     assert torch.isfinite(y.float()).all(), "unwritten rows in y"
     # z holds every assignment's output: nothing left at the NaN poison
     assert torch.isfinite(views["z"].float()).all(), "unwritten slots in z"
-    # run to run: bitwise identical
+    # run to run, and row-major weights against tiled: bitwise identical
+    ib = torch.int16 if w.dtype == "bf16" else torch.int32
     _, _, y2 = forward(case, poison=False)
-    assert torch.equal(y.view(torch.int16 if w.dtype == "bf16" else torch.int32),
-                       y2.view(torch.int16 if w.dtype == "bf16" else torch.int32))
+    assert torch.equal(y.view(ib), y2.view(ib))
+    _, _, y3 = forward(case, poison=False, layout="row_major")
+    assert torch.equal(y.view(ib), y3.view(ib)), "weight layouts disagree"
 
 
 def test_hot_expert_capacity_sweep_is_bit_identical():

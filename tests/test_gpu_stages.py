@@ -10,7 +10,8 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import (Case, assert_close, assert_plan_equal, note, to_np)
+from gpu_util import (Case, assert_close, assert_plan_equal, el_dtype, note,
+                      tiled_index, to_np, untile)
 from round_dropless_expert_amd import binding as B
 from round_dropless_expert_amd import configs
 
@@ -39,13 +40,15 @@ STAGE_CASES = [
 ]
 
 
+@pytest.mark.parametrize("layout", ["tiled", "row_major"])
 @pytest.mark.parametrize("w", STAGE_CASES, ids=lambda w: w.name)
-def test_stages_match_oracle(w):
+def test_stages_match_oracle(w, layout):
     torch.cuda.synchronize()
     case = Case(w)
-    cfg = case.cfg()
+    cfg = case.cfg(weight_layout=layout)
+    wg, wu, wd = case.weights(layout)
     ws = case.workspace(cfg)
-    note(f"{w.name}: moe_plan")
+    note(f"{w.name}/{layout}: moe_plan")
     R = B.moe_plan(cfg, case.logits, ws)
     views = B.workspace_views(cfg, ws)
     p = oracle.plan(case.idx, w.E, w.C)
@@ -55,34 +58,61 @@ def test_stages_match_oracle(w):
     assert np.all(np.abs(wt - case.wt) <= 1e-6 * case.wt), "routing weights"
 
     ce = p.C_eff
-    xr_bits = views["xr"].view(torch.int16 if w.dtype == "bf16" else torch.int32)
-    x_bits = case.x.view(torch.int16 if w.dtype == "bf16" else torch.int32)
+    pad = (ce + 63) // 64 * 64
+    dt = el_dtype(w)
+    ibits = torch.int16 if w.dtype == "bf16" else torch.int32
     for r in range(R):
-        note(f"{w.name}: moe_dispatch round {r}")
+        note(f"{w.name}/{layout}: moe_dispatch round {r}")
         B.moe_dispatch(cfg, r, case.x, ws)
         torch.cuda.synchronize()
         m = p.rows_in_round(r)
-        rows, assigns = [], []
-        for e in range(w.E):
-            for c in range(int(m[e])):
-                rows.append(e * ce + c)
-                assigns.append(int(p.perm[p.offsets[e] + r * ce + c]))
-        rows_t = torch.tensor(rows, device=case.dev, dtype=torch.long)
+        experts = [e for e in range(w.E) if m[e] > 0]
+        assigns = [int(p.perm[p.offsets[e] + r * ce + c])
+                   for e in experts for c in range(int(m[e]))]
         a_t = torch.tensor(assigns, device=case.dev, dtype=torch.long)
-        assert torch.equal(xr_bits[rows_t], x_bits[a_t // w.k]), f"xr round {r}"
+        xr = torch.cat([untile(views["xr"][e], pad, w.d_model, dt)[:int(m[e])]
+                        for e in experts])
+        assert torch.equal(xr.view(ibits), case.x[a_t // w.k].view(ibits)), \
+            f"xr round {r}"
 
-        note(f"{w.name}: moe_expert_ffn round {r}")
-        B.moe_expert_ffn(cfg, r, case.wg, case.wu, case.wd, ws)
+        note(f"{w.name}/{layout}: moe_expert_ffn round {r}")
+        B.moe_expert_ffn(cfg, r, wg, wu, wd, ws)
         torch.cuda.synchronize()
         h_ref, o_ref = oracle.assignment_outputs(
             np.array(assigns), case.idx, case.inp.x, case.inp.Wg, case.inp.Wu,
             case.inp.Wd, want_h=True)
-        assert_close(to_np(views["h"][rows_t]), h_ref, w.dtype, f"h round {r}")
+        h = torch.cat([untile(views["h"][e], pad, w.d_ff, dt)[:int(m[e])]
+                       for e in experts])
+        assert_close(to_np(h), h_ref, w.dtype, f"h round {r}")
         assert_close(to_np(views["z"][a_t]), o_ref, w.dtype, f"z round {r}")
 
-    note(f"{w.name}: moe_combine")
+    note(f"{w.name}/{layout}: moe_combine")
     y = case.new_y()
     B.moe_combine(cfg, ws, y)
     torch.cuda.synchronize()
     y_ref = case.oracle_y(np.arange(w.T))
     assert_close(to_np(y), y_ref, w.dtype, "y")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_pack_weights_is_the_tiled_permutation(dtype):
+    """moe_pack_weights moves every byte to the documented tiled offset."""
+    E, f, d = 3, 192, 128
+    cfg = B.config(64, E, 1, d, f, 64, dtype)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    gen = torch.Generator().manual_seed(5)
+    src = [torch.randn(E, f, d, generator=gen).to(tdt).cuda(),
+           torch.randn(E, f, d, generator=gen).to(tdt).cuda(),
+           torch.randn(E, d, f, generator=gen).to(tdt).cuda()]
+    out = [torch.full_like(t, float("nan")) for t in src]
+    note(f"moe_pack_weights {dtype}")
+    B.moe_pack_weights(cfg, *src, *out)
+    torch.cuda.synchronize()
+    es = src[0].element_size()
+    for t, o in zip(src, out):
+        rows, cols = t.shape[1], t.shape[2]
+        idx = torch.from_numpy(tiled_index(rows, cols * es).reshape(-1)).cuda()
+        for e in range(E):
+            sb = t[e].contiguous().view(torch.uint8).reshape(-1)
+            ob = o[e].contiguous().view(torch.uint8).reshape(-1)
+            assert torch.equal(ob[idx], sb)
