@@ -99,7 +99,8 @@ typedef struct {
  * Weights: expert e's matrix starts at element e * out * in of its array. */
 
 /* Byte offsets of the internal buffers inside the workspace. Every offset is
- * a multiple of 256. Contents (all produced by the calls below):
+ * a multiple of 256 except n_rounds, which directly follows the E counts
+ * (counts + 4 E) so that one read returns both. Contents (all produced by the calls below):
  *   idx      int32 [T][k]    expert of assignment a (top-k, ties to the lower
  *                            index, ordered by descending logit)
  *   weight   float [T][k]    routing weight: softmax of the k chosen logits

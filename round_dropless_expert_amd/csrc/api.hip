@@ -35,6 +35,8 @@ moe_status_t hip_fail(hipError_t e, const char* where) {
 
 size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
 
+constexpr int kMaxExperts = 64;
+
 int64_t eff_capacity(const moe_config_t* c) { return c->C < c->T ? c->C : c->T; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
@@ -52,7 +54,7 @@ moe_status_t check_cfg(const moe_config_t* c) {
     return fail(MOE_ERR_INVALID_ARGUMENT, "unknown dtype");
   if (c->weight_layout != MOE_WEIGHTS_ROW_MAJOR && c->weight_layout != MOE_WEIGHTS_TILED)
     return fail(MOE_ERR_INVALID_ARGUMENT, "unknown weight layout");
-  if (c->E > 64) return fail(MOE_ERR_UNSUPPORTED, "E > 64 is not supported");
+  if (c->E > kMaxExperts) return fail(MOE_ERR_UNSUPPORTED, "E > 64 is not supported");
   if (c->d_model % 64 || c->d_ff % 64)
     return fail(MOE_ERR_UNSUPPORTED, "d_model and d_ff must be multiples of 64");
   const int64_t TK = c->T * (int64_t)c->k;
@@ -86,9 +88,10 @@ void layout_of(const moe_config_t* c, moe_workspace_layout_t* L) {
   };
   L->idx = take(TK * 4);
   L->weight = take(TK * 4);
-  L->counts = take(E * 4);
+  // R sits right after the E counts, so one read returns both
+  L->counts = take((E + 1) * 4);
+  L->n_rounds = L->counts + E * 4;
   L->offsets = take((E + 1) * 4);
-  L->n_rounds = take(4);
   L->perm = take(TK * 4);
   L->pos = take(TK * 4);
   L->round_of = take(TK * 4);
@@ -180,11 +183,13 @@ moe_status_t run_plan(const Bound& b, const float* logits, hipStream_t st) {
 }
 
 moe_status_t run_ffn(const Bound& b, int r, const void* wg, const void* wu,
-                     const void* wd, int cus, hipStream_t st) {
+                     const void* wd, const int32_t* counts_host, int cus,
+                     hipStream_t st) {
   MOE_HIP(moe::launch_gate_up(b.s, r, b.ws + b.L.xr, wg, wu, b.pb.counts,
-                              b.ws + b.L.h, cus, st),
+                              counts_host, b.ws + b.L.h, cus, st),
           "gate/up launch");
-  MOE_HIP(moe::launch_down(b.s, r, b.ws + b.L.h, wd, b.pb, b.ws + b.L.z, cus, st),
+  MOE_HIP(moe::launch_down(b.s, r, b.ws + b.L.h, wd, b.pb, counts_host,
+                           b.ws + b.L.z, cus, st),
           "down launch");
   return MOE_OK;
 }
@@ -278,7 +283,7 @@ moe_status_t moe_expert_ffn(const moe_config_t* cfg, int32_t round,
   if ((st = check_round(b, round)) != MOE_OK) return st;
   int cus = 0;
   if ((st = num_cus(&cus)) != MOE_OK) return st;
-  return run_ffn(b, round, w_gate, w_up, w_down, cus,
+  return run_ffn(b, round, w_gate, w_up, w_down, nullptr, cus,
                  static_cast<hipStream_t>(stream));
 }
 
@@ -294,7 +299,7 @@ moe_status_t moe_expert_gate_up(const moe_config_t* cfg, int32_t round,
   int cus = 0;
   if ((st = num_cus(&cus)) != MOE_OK) return st;
   MOE_HIP(moe::launch_gate_up(b.s, round, b.ws + b.L.xr, w_gate, w_up,
-                              b.pb.counts, b.ws + b.L.h, cus,
+                              b.pb.counts, nullptr, b.ws + b.L.h, cus,
                               static_cast<hipStream_t>(stream)),
           "gate/up launch");
   return MOE_OK;
@@ -310,8 +315,8 @@ moe_status_t moe_expert_down(const moe_config_t* cfg, int32_t round,
   if ((st = check_round(b, round)) != MOE_OK) return st;
   int cus = 0;
   if ((st = num_cus(&cus)) != MOE_OK) return st;
-  MOE_HIP(moe::launch_down(b.s, round, b.ws + b.L.h, w_down, b.pb, b.ws + b.L.z,
-                           cus, static_cast<hipStream_t>(stream)),
+  MOE_HIP(moe::launch_down(b.s, round, b.ws + b.L.h, w_down, b.pb, nullptr,
+                           b.ws + b.L.z, cus, static_cast<hipStream_t>(stream)),
           "down launch");
   return MOE_OK;
 }
@@ -377,18 +382,21 @@ moe_status_t moe_forward(const moe_config_t* cfg, const float* logits,
   int cus = 0;
   if ((st = num_cus(&cus)) != MOE_OK) return st;
   if ((st = run_plan(b, logits, s)) != MOE_OK) return st;
-  int32_t R = 0;
-  MOE_HIP(hipMemcpyAsync(&R, b.pb.n_rounds, sizeof(int32_t),
+  // one read: the E per-expert counts followed by R
+  int32_t counts_r[kMaxExperts + 1];
+  MOE_HIP(hipMemcpyAsync(counts_r, b.pb.counts, (b.s.E + 1) * sizeof(int32_t),
                          hipMemcpyDeviceToHost, s),
-          "read of R");
+          "read of counts and R");
   MOE_HIP(hipStreamSynchronize(s), "stream sync");
+  const int32_t R = counts_r[b.s.E];
   const int64_t max_rounds = (b.s.T + b.s.ce - 1) / b.s.ce;
   if (R < 1 || R > max_rounds)
     return fail(MOE_ERR_HIP, "device plan reported an impossible round count");
   for (int r = 0; r < R; ++r) {
     MOE_HIP(moe::launch_dispatch(b.s, r, x, b.pb, b.ws + b.L.xr, cus, s),
             "dispatch launch");
-    if ((st = run_ffn(b, r, w_gate, w_up, w_down, cus, s)) != MOE_OK) return st;
+    if ((st = run_ffn(b, r, w_gate, w_up, w_down, counts_r, cus, s)) != MOE_OK)
+      return st;
   }
   MOE_HIP(moe::launch_combine(b.s, b.ws + b.L.z, b.pb.weight, y, cus, s),
           "combine launch");

@@ -21,9 +21,12 @@
 //
 // Tiles: 256 threads = 2 x 2 wavefronts; wavefront (wm, wn) owns WJ 32-token
 // blocks and WI 32-weight-row blocks. K advances 64 bytes per stage (32 bf16
-// or 16 fp32) through a ring of LDS stages filled by LDS-direct buffer loads,
-// with up to three stages in flight and one barrier per stage. Fragment
-// reads run one MFMA step ahead of the MFMAs that use them.
+// or 16 fp32); SPB stages form a slot of a four-slot LDS ring filled by
+// LDS-direct buffer loads, with up to three slots in flight and one barrier
+// per slot. Fragment reads run one MFMA step ahead of the MFMAs that use
+// them. Two tile shapes: 256 weight rows x 256 tokens, and 128 x 64 (three
+// stages per slot) for rounds with too few rows to give every CU a large
+// tile, which mostly stream weights and need many workgroups.
 //
 // Determinism: every output element is one fixed sequence of MFMA steps
 // over K in ascending order, whatever the round, the slot or the tile it
@@ -101,36 +104,6 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
 constexpr int kRsrcWord3 = 0x00020000;
 
 typedef __attribute__((address_space(3))) char lds_char;
-typedef int int32x4 __attribute__((ext_vector_type(4)));
-
-// Raw buffer descriptor (scalar registers) over `bytes` bytes at `base`.
-__device__ __forceinline__ int32x4 buffer_rsrc(const void* base, uint32_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  int32x4 r;
-  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-  r.y = __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xFFFFu));
-  r.z = __builtin_amdgcn_readfirstlane((int)bytes);
-  r.w = kRsrcWord3;
-  return r;
-}
-
-// LDS-direct 16-byte load: lane i of the wavefront reads
-// base + voff + soff and writes LDS bytes [dst + 16*i, dst + 16*i + 16).
-// Issued from asm so that the compiler does not order later LDS reads of
-// other ring slots behind it; the kernel waits for it with explicit vmcnt
-// counts. It has no register results. M0 (which holds the LDS address) is
-// set inside the same statement; the compiler keeps nothing in M0 here.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void lds_dma16(int32x4 rsrc, uint32_t voff,
-                                          uint32_t soff, lds_char* dst) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               ::"s"(m0), "v"(voff), "s"(rsrc), "s"(soff)
-               : "m0");
-}
-#pragma clang diagnostic pop
-
 // Wait until at most N of this wavefront's vector-memory operations are
 // outstanding (the LDS-direct loads of later stages), then join the
 // workgroup barrier. A bare s_barrier: __syncthreads() would also drain
@@ -147,19 +120,6 @@ template <typename Elem, int WI, int WJ>
 struct Frags {
   typename MmaOp<Elem>::frag_t a[WI], b[WJ];
 };
-
-// Fragments of MFMA step s: weight rows (A operand) and token rows (B).
-template <typename Elem, int WI, int WJ>
-__device__ __forceinline__ void load_frags(Frags<Elem, WI, WJ>& f,
-                                           const char* stage, int wrow,
-                                           int trow, int s, int half) {
-#pragma unroll
-  for (int ib = 0; ib < WI; ++ib)
-    f.a[ib] = MmaOp<Elem>::load(stage, wrow + 32 * ib, s, half);
-#pragma unroll
-  for (int jb = 0; jb < WJ; ++jb)
-    f.b[jb] = MmaOp<Elem>::load(stage, trow + 32 * jb, s, half);
-}
 
 template <typename Elem, int WI, int WJ>
 __device__ __forceinline__ void mma_step(f32x16 (&acc)[WI][WJ],
@@ -194,15 +154,28 @@ __device__ __forceinline__ void pin_step() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// K pipeline: a ring of kSlots LDS stages. Each stage has one barrier,
-// placed before its last MFMA step; by then the stage's last fragments are
-// in registers, so its slot is free and the barrier issues the LDS-direct
-// fetch of stage kt + kSlots into it. The barrier first waits for stage
-// kt + 1, so up to kSlots - 1 later stages stay in flight, and the next
-// stage's first fragments load while the last step's MFMAs run.
+// K pipeline: a ring of kSlots LDS slots, each holding SPB consecutive
+// 64-byte K stages (a "super-stage"). Each super-stage has one barrier,
+// placed before its last MFMA step; the barrier waits for super-stage
+// ks + 1 (ks + 2 and ks + 3 stay in flight), after which the next
+// super-stage's first fragments load while the last step's MFMAs run. The
+// first MFMA step of super-stage ks issues the fetch of ks + kSlots - 1 into
+// the slot freed at the previous barrier, one load between MFMAs.
 constexpr int kSlots = 4;  // the stage loop below names four slots
 
-template <typename Elem, int WI, int WJ, bool kGateUp>
+// Tile configurations (WI / WJ: 32-row MFMA blocks per wavefront along
+// weight rows / tokens; the 2 x 2 wavefronts cover 64*WI weight rows and
+// 64*WJ tokens; SPB: 64-byte K stages per slot and barrier).
+struct TileBig {    // rounds with more than 64 rows in some expert
+  static constexpr int WI = 4, WJ = 4, SPB = 1;
+};
+struct TileSmall {  // rounds too small to give every CU a large tile: such
+                    // a round mostly streams expert weights; spread them
+                    // over more workgroups and keep more bytes in flight
+  static constexpr int WI = 2, WJ = 1, SPB = 3;
+};
+
+template <typename Elem, int WI, int WJ, int SPB, bool kGateUp>
 __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
     GemmParams<Elem> p) {
   typedef Frags<Elem, WI, WJ> frags_t;
@@ -215,21 +188,22 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
   constexpr int kTPasses = BM / 64;
   constexpr int kPasses = kWPasses + kTPasses;
   constexpr int kStageBytes = (BN + BM) * kRowBytes;
+  constexpr int kSlotBytes = SPB * kStageBytes;
+  constexpr int kLoads = SPB * kPasses;          // loads per slot and thread
   constexpr int kSteps = MmaOp<Elem>::kSteps;
   constexpr int kMfmaPerStep = WI * WJ;
   constexpr int kReadsPerStep = WI + WJ;
   static_assert(kSteps % 2 == 0, "fragment sets alternate by step");
-  static_assert(!kGateUp || WI % 4 == 0,
-                "each gate/up load pass must stay inside one matrix");
-  static_assert(kPasses * (kSlots - 1) <= 63, "vmcnt budget");
+  static_assert(WI % 2 == 0, "gate/up pairs and the 2 x 2 wavefront grid");
+  static_assert(kLoads * (kSlots - 2) <= 63, "vmcnt budget");
 
-  // the ring: kSlots stages as separate LDS objects, so the compiler can
+  // the ring: kSlots slots as separate LDS objects, so the compiler can
   // tell a fragment read of one slot from a pending LDS-direct fill of
   // another and needs no conservative wait between them
-  __shared__ __attribute__((aligned(1024))) char slot0[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) char slot1[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) char slot2[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) char slot3[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char slot0[kSlotBytes];
+  __shared__ __attribute__((aligned(1024))) char slot1[kSlotBytes];
+  __shared__ __attribute__((aligned(1024))) char slot2[kSlotBytes];
+  __shared__ __attribute__((aligned(1024))) char slot3[kSlotBytes];
   __shared__ int tile_pre[kWave + 1];
   __shared__ int rows_m[kWave];
 
@@ -258,13 +232,20 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
   const int G = gridDim.x;
   const int slot = (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8);
 
+  // Row order inside a stage: weight rows, then token rows. For gate/up the
+  // weight rows are all gate rows (features n0 .. n0+NF-1), then all up
+  // rows of the same features, so every 64-row load pass reads one matrix.
   // Load passes: pass i fills stage rows 64*i .. 64*i+63; lane tid writes
   // bytes [16*tid, 16*tid+16) of the pass: row r0 = tid / 4, physical
   // chunk tid % 4, i.e. logical chunk (tid % 4) ^ ((r0 >> 2) & 3).
   const int r0 = tid >> 2;
   const int chunk = (tid & 3) ^ ((r0 >> 2) & 3);
-  // fragment rows of this lane inside a stage
-  const int wrow = wn * (BN / 2) + l32;
+  // fragment rows of this lane: weight block ib, token block 0
+  auto wrow_of = [&](int ib) {
+    if (kGateUp)
+      return (ib < WI / 2 ? 0 : BN / 2) + wn * (BN / 4) + (ib % (WI / 2)) * 32 + l32;
+    return wn * (BN / 2) + ib * 32 + l32;
+  };
   const int trow = BN + wm * (BM / 2) + l32;
 
   for (int tile = slot; tile < total; tile += G) {
@@ -290,20 +271,12 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
     // Byte offsets (k = 0) of what this lane fetches in each pass. A pass
     // covers one 64-row band: tiled operands give one contiguous 4 KiB
     // block per stage (the lane's 16 bytes at 16 * tid); row-major weights
-    // give this lane's row r0 of the band, logical chunk `chunk`. For
-    // gate/up, the first half of each wavefront's weight rows are gate rows
-    // and the second half up rows of the same features; a 64-row band lies
-    // inside one of them, so its matrix follows from the pass index.
+    // give this lane's row r0 of the band, logical chunk `chunk`.
     uint32_t voff[kPasses];
 #pragma unroll
     for (int i = 0; i < kWPasses; ++i) {
-      int feat0;
-      if (kGateUp) {
-        const int rho = 64 * i;  // first row of the pass
-        feat0 = n0 + (rho / (BN / 2)) * (BN / 4) + (rho % (BN / 2)) % (BN / 4);
-      } else {
-        feat0 = n0 + 64 * i;
-      }
+      int feat0 = n0 + 64 * i;
+      if (kGateUp && 64 * i >= BN / 2) feat0 -= BN / 2;  // an up-row pass
       if (p.tiled_w) {
         const int band = feat0 < p.N ? feat0 / 64 : p.N / 64 - 1;
         voff[i] = (uint32_t)band * band_bytes + tid * 16;
@@ -328,71 +301,90 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
 
     const int KT = p.K / kStageK;
 
-    // Fetch stage ks into `slot` with LDS-direct buffer loads (lane i of a
-    // wavefront writes bytes [16 i, 16 i + 16) of its 1 KiB share of each
-    // 4 KiB pass). A stage at or past the end of K is fetched with an
-    // offset beyond the buffer: the hardware returns zeros without touching
-    // memory, so such a stage adds exact zeros to the accumulators. K is
-    // walked in groups of kSlots stages, the last group padded this way.
-    auto fetch = [&](char* slot, int ks) {
-      lds_char* dst = (lds_char*)slot + wave_id * 1024;
-      const bool live = ks < KT;
-      const uint32_t soff_w = live ? (uint32_t)ks * wstride : 0x80000000u;
-      const uint32_t soff_t = live ? (uint32_t)ks * kTileBytes : 0x80000000u;
+    // Fetch super-stage ks (stages ks*SPB .. ks*SPB+SPB-1) into `slot` with
+    // LDS-direct buffer loads (lane i of a wavefront writes bytes
+    // [16 i, 16 i + 16) of its 1 KiB share of each 4 KiB pass). A stage at
+    // or past the end of K is fetched with an offset beyond the buffer: the
+    // hardware returns zeros without touching memory, so such a stage adds
+    // exact zeros to the accumulators. K is walked in groups of kSlots
+    // super-stages, the last group padded this way.
+    auto fetch = [&](char* slot_mem, int ks) {
 #pragma unroll
-      for (int i = 0; i < kPasses; ++i) {
-        const __amdgpu_buffer_rsrc_t rs =
-            i >= kWPasses ? ra
-                          : ((kGateUp && ((64 * i) % (BN / 2)) >= BN / 4) ? rw1 : rw0);
-        // (scalar copy: clang's host pass drops the launch stub when an
-        // array element is passed to this builtin directly)
-        const uint32_t vo = voff[i];
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rs, (void __attribute__((address_space(3)))*)(dst + i * 4096), 16, vo,
-            i >= kWPasses ? soff_t : soff_w, 0, 0);
+      for (int sub = 0; sub < SPB; ++sub) {
+        const int g = ks * SPB + sub;
+        lds_char* dst = (lds_char*)slot_mem + sub * kStageBytes + wave_id * 1024;
+        const bool live = g < KT;
+        const uint32_t soff_w = live ? (uint32_t)g * wstride : 0x80000000u;
+#pragma unroll
+        for (int i = 0; i < kPasses; ++i) {
+          const __amdgpu_buffer_rsrc_t rs =
+              i >= kWPasses ? ra : ((kGateUp && 64 * i >= BN / 2) ? rw1 : rw0);
+          // token bands at or past the expert's m rows feed only outputs
+          // that are never stored: fetch them as zeros too
+          const bool band_live = i < kWPasses || m0 + 64 * (i - kWPasses) < m;
+          const uint32_t soff = i < kWPasses
+                                    ? soff_w
+                                    : (live && band_live ? (uint32_t)g * kTileBytes
+                                                         : 0x80000000u);
+          // (scalar copy: clang's host pass drops the launch stub when an
+          // array element is passed to this builtin directly)
+          const uint32_t vo = voff[i];
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rs, (void __attribute__((address_space(3)))*)(dst + i * 4096), 16, vo,
+              soff, 0, 0);
+        }
       }
     };
 
-    // One stage: its first MFMA step also issues the fetch of stage kt + 3
-    // into the slot freed at the previous barrier, one load between
-    // consecutive MFMAs; the barrier before the last step waits for stage
-    // kt + 1 (stages kt + 2 and kt + 3 stay in flight), after which the
-    // next stage's first fragments load while the last step's MFMAs run.
-#define MOE_STAGE(CUR, NXT, FSLOT, KT_)                                          \
-    _Pragma("unroll") for (int s = 0; s < kSteps; s += 2) {                     \
-      load_frags<Elem, WI, WJ>(f1, CUR, wrow, trow, s + 1, half);               \
-      if (s == 0) fetch(FSLOT, (KT_) + kSlots - 1);                             \
-      mma_step<Elem, WI, WJ>(acc, f0);                                          \
-      if (s == 0)                                                               \
-        pin_step<kMfmaPerStep, kReadsPerStep, kPasses>();                       \
-      else                                                                      \
+    frags_t f0, f1;
+    // fragments of step s of the stage at `stage`
+    auto frags = [&](frags_t& f, const char* stage, int s) {
+#pragma unroll
+      for (int ib = 0; ib < WI; ++ib)
+        f.a[ib] = MmaOp<Elem>::load(stage, wrow_of(ib), s, half);
+#pragma unroll
+      for (int jb = 0; jb < WJ; ++jb)
+        f.b[jb] = MmaOp<Elem>::load(stage, trow + 32 * jb, s, half);
+    };
+
+#define MOE_SUPER(CUR, NXT, FSLOT, KS_)                                          \
+    _Pragma("unroll") for (int sub = 0; sub < SPB; ++sub) {                     \
+      const char* cs = CUR + sub * kStageBytes;                                 \
+      const char* ns = sub + 1 < SPB ? CUR + (sub + 1) * kStageBytes : NXT;     \
+      _Pragma("unroll") for (int s = 0; s < kSteps; s += 2) {                   \
+        frags(f1, cs, s + 1);                                                   \
+        if (sub == 0 && s == 0) fetch(FSLOT, (KS_) + kSlots - 1);               \
+        mma_step<Elem, WI, WJ>(acc, f0);                                        \
+        if (sub == 0 && s == 0)                                                 \
+          pin_step<kMfmaPerStep, kReadsPerStep, kLoads>();                      \
+        else                                                                    \
+          pin_step<kMfmaPerStep, kReadsPerStep, 0>();                           \
+        if (s + 2 < kSteps) {                                                   \
+          frags(f0, cs, s + 2);                                                 \
+        } else {                                                                \
+          if (sub + 1 == SPB) wait_vmem_barrier<(kSlots - 2) * kLoads>();       \
+          frags(f0, ns, 0);                                                     \
+        }                                                                       \
+        mma_step<Elem, WI, WJ>(acc, f1);                                        \
         pin_step<kMfmaPerStep, kReadsPerStep, 0>();                             \
-      if (s + 2 < kSteps) {                                                     \
-        load_frags<Elem, WI, WJ>(f0, CUR, wrow, trow, s + 2, half);             \
-      } else {                                                                  \
-        wait_vmem_barrier<(kSlots - 2) * kPasses>();                            \
-        load_frags<Elem, WI, WJ>(f0, NXT, wrow, trow, 0, half);                 \
       }                                                                         \
-      mma_step<Elem, WI, WJ>(acc, f1);                                          \
-      pin_step<kMfmaPerStep, kReadsPerStep, 0>();                               \
     }
 
-    // prologue: stages 0 .. kSlots-2 in flight; wait for stage 0
+    // prologue: super-stages 0 .. kSlots-2 in flight; wait for the first
     fetch(slot0, 0);
     fetch(slot1, 1);
     fetch(slot2, 2);
-    wait_vmem_barrier<(kSlots - 2) * kPasses>();
-
-    frags_t f0, f1;
-    load_frags<Elem, WI, WJ>(f0, slot0, wrow, trow, 0, half);
-    const int KT4 = (KT + kSlots - 1) / kSlots * kSlots;
-    for (int kt = 0; kt < KT4; kt += kSlots) {
-      MOE_STAGE(slot0, slot1, slot3, kt)
-      MOE_STAGE(slot1, slot2, slot0, kt + 1)
-      MOE_STAGE(slot2, slot3, slot1, kt + 2)
-      MOE_STAGE(slot3, slot0, slot2, kt + 3)
+    wait_vmem_barrier<(kSlots - 2) * kLoads>();
+    frags(f0, slot0, 0);
+    const int KS = (KT + SPB - 1) / SPB;
+    const int KS4 = (KS + kSlots - 1) / kSlots * kSlots;
+    for (int ks = 0; ks < KS4; ks += kSlots) {
+      MOE_SUPER(slot0, slot1, slot3, ks)
+      MOE_SUPER(slot1, slot2, slot0, ks + 1)
+      MOE_SUPER(slot2, slot3, slot1, ks + 2)
+      MOE_SUPER(slot3, slot0, slot2, ks + 3)
     }
-#undef MOE_STAGE
+#undef MOE_SUPER
 
     // epilogue: lane holds, for token j = l32 of each 32-token block, four
     // runs of four consecutive output features
@@ -401,16 +393,9 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
     for (int jb = 0; jb < WJ; ++jb) {
       const int c = m0 + wm * (BM / 2) + jb * 32 + l32;
       if (c >= m) continue;
-      Elem* orow;
       if (kGateUp) {
         // h: row c of expert e's tiled matrix
-        orow = p.out + (int64_t)e * p.ce_pad * p.N;
-      } else {
-        const int a = p.perm[p.offsets[e] + (int64_t)p.r * p.ce + c];
-        orow = p.out + (int64_t)a * p.N;
-      }
-      if (kGateUp) {
-        char* hmat = reinterpret_cast<char*>(orow);
+        char* hmat = reinterpret_cast<char*>(p.out + (int64_t)e * p.ce_pad * p.N);
 #pragma unroll
         for (int ib = 0; ib < WI / 2; ++ib) {
 #pragma unroll
@@ -427,6 +412,9 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
           }
         }
       } else {
+        // z: the assignment's token slot
+        const int a = p.perm[p.offsets[e] + (int64_t)p.r * p.ce + c];
+        Elem* orow = p.out + (int64_t)a * p.N;
 #pragma unroll
         for (int ib = 0; ib < WI; ++ib) {
 #pragma unroll
@@ -447,60 +435,98 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
   }
 }
 
-// Tile shapes: bf16 uses 256 x 256 tiles (4 x 4 MFMA blocks per wavefront);
-// fp32 uses 256 weight rows x 128 tokens.
-template <typename Elem>
-struct TileCfg;
-template <>
-struct TileCfg<bf16> {
-  static constexpr int WI = 4, WJ = 4;
-};
-template <>
-struct TileCfg<float> {
-  static constexpr int WI = 4, WJ = 2;
-};
+// Tiles one round needs under configuration Cfg (host side, from counts).
+template <typename Cfg>
+static int64_t round_tiles(const Shape& s, const int32_t* counts_host, int r,
+                           int N, bool gate_up) {
+  const int BM = 64 * Cfg::WJ;
+  const int NF = gate_up ? 32 * Cfg::WI : 64 * Cfg::WI;
+  const int64_t nt = (N + NF - 1) / NF;
+  int64_t tiles = 0;
+  for (int e = 0; e < s.E; ++e) {
+    int64_t m = (int64_t)counts_host[e] - (int64_t)r * s.ce;
+    m = m < 0 ? 0 : (m > s.ce ? s.ce : m);
+    tiles += (m + BM - 1) / BM * nt;
+  }
+  return tiles;
+}
 
-template <typename Elem, bool kGateUp>
-static hipError_t launch_gemm(const GemmParams<Elem>& p, int num_cus,
-                              hipStream_t st) {
-  constexpr int WI = TileCfg<Elem>::WI, WJ = TileCfg<Elem>::WJ;
-  int G = num_cus;  // one 256-thread workgroup per CU (LDS-limited)
-  G = (G + 7) / 8 * 8;
-  hipLaunchKernelGGL((grouped_ffn_gemm_kernel<Elem, WI, WJ, kGateUp>), dim3(G),
-                     dim3(256), 0, st, p);
+// Workgroups for a round: one per CU, or fewer when the round has fewer
+// tiles; a multiple of 8 (the XCD-contiguous walk assumes it).
+static int grid_for(int64_t tiles, int num_cus) {
+  int64_t g = tiles < num_cus ? tiles : num_cus;
+  g = (g + 7) / 8 * 8;
+  return (int)(g < 8 ? 8 : g);
+}
+
+template <typename Elem, typename Cfg, bool kGateUp>
+static hipError_t launch_gemm_cfg(const GemmParams<Elem>& p, int grid,
+                                  hipStream_t st) {
+  hipLaunchKernelGGL(
+      (grouped_ffn_gemm_kernel<Elem, Cfg::WI, Cfg::WJ, Cfg::SPB, kGateUp>),
+      dim3(grid), dim3(256), 0, st, p);
   return hipGetLastError();
+}
+
+// counts_host (nullable): per-expert counts on the host. With them the
+// round's tile shape and grid are chosen from its largest expert; without
+// them the large tile and one workgroup per CU are used. Both shapes run the
+// same MFMA sequence over K for every output, so results are identical.
+template <typename Elem, bool kGateUp>
+static hipError_t launch_gemm(const Shape& s, const GemmParams<Elem>& p,
+                              const int32_t* counts_host, int num_cus,
+                              hipStream_t st) {
+  const int N = kGateUp ? s.f : s.d;
+  if (counts_host) {
+    int64_t mmax = 0;
+    for (int e = 0; e < s.E; ++e) {
+      int64_t m = (int64_t)counts_host[e] - (int64_t)p.r * s.ce;
+      m = m < 0 ? 0 : (m > s.ce ? s.ce : m);
+      mmax = m > mmax ? m : mmax;
+    }
+    if (mmax == 0) return hipSuccess;  // nothing in this round
+    // the large tile when it gives every CU at least one tile, else the
+    // small one (rounds of a few rows per expert stream weights)
+    const int64_t tb = round_tiles<TileBig>(s, counts_host, p.r, N, kGateUp);
+    if (tb >= num_cus)
+      return launch_gemm_cfg<Elem, TileBig, kGateUp>(p, grid_for(tb, num_cus), st);
+    const int64_t t = round_tiles<TileSmall>(s, counts_host, p.r, N, kGateUp);
+    return launch_gemm_cfg<Elem, TileSmall, kGateUp>(p, grid_for(t, num_cus), st);
+  }
+  return launch_gemm_cfg<Elem, TileBig, kGateUp>(p, grid_for(num_cus, num_cus), st);
 }
 
 hipError_t launch_gate_up(const Shape& s, int r, const void* xr,
                           const void* wg, const void* wu, const int32_t* counts,
-                          void* h, int num_cus, hipStream_t st) {
+                          const int32_t* counts_host, void* h, int num_cus,
+                          hipStream_t st) {
   if (s.bf16) {
     GemmParams<bf16> p{static_cast<const bf16*>(xr), static_cast<const bf16*>(wg),
                        static_cast<const bf16*>(wu), static_cast<bf16*>(h),
                        counts, nullptr, nullptr, s.E, s.ce, r, s.d, s.f,
                        s.ce_pad(), s.tiled_w};
-    return launch_gemm<bf16, true>(p, num_cus, st);
+    return launch_gemm<bf16, true>(s, p, counts_host, num_cus, st);
   }
   GemmParams<float> p{static_cast<const float*>(xr), static_cast<const float*>(wg),
                       static_cast<const float*>(wu), static_cast<float*>(h),
                       counts, nullptr, nullptr, s.E, s.ce, r, s.d, s.f,
                       s.ce_pad(), s.tiled_w};
-  return launch_gemm<float, true>(p, num_cus, st);
+  return launch_gemm<float, true>(s, p, counts_host, num_cus, st);
 }
 
 hipError_t launch_down(const Shape& s, int r, const void* h, const void* wd,
-                       const PlanBuffers& b, void* z, int num_cus,
-                       hipStream_t st) {
+                       const PlanBuffers& b, const int32_t* counts_host, void* z,
+                       int num_cus, hipStream_t st) {
   if (s.bf16) {
     GemmParams<bf16> p{static_cast<const bf16*>(h), static_cast<const bf16*>(wd),
                        nullptr, static_cast<bf16*>(z), b.counts, b.offsets,
                        b.perm, s.E, s.ce, r, s.f, s.d, s.ce_pad(), s.tiled_w};
-    return launch_gemm<bf16, false>(p, num_cus, st);
+    return launch_gemm<bf16, false>(s, p, counts_host, num_cus, st);
   }
   GemmParams<float> p{static_cast<const float*>(h), static_cast<const float*>(wd),
                       nullptr, static_cast<float*>(z), b.counts, b.offsets,
                       b.perm, s.E, s.ce, r, s.f, s.d, s.ce_pad(), s.tiled_w};
-  return launch_gemm<float, false>(p, num_cus, st);
+  return launch_gemm<float, false>(s, p, counts_host, num_cus, st);
 }
 
 }  // namespace moe

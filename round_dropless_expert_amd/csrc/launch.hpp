@@ -43,12 +43,17 @@ hipError_t launch_plan(const Shape& s, PlanBuffers b, hipStream_t st);
 hipError_t launch_dispatch(const Shape& s, int r, const void* x,
                            const PlanBuffers& b, void* xr, int num_cus,
                            hipStream_t st);
+// counts_host: the plan's per-expert counts read back to the host, or NULL.
+// With them each round gets the tile shape and grid that fit its largest
+// expert (results are identical either way); without them the large tile
+// and one workgroup per CU are used.
 hipError_t launch_gate_up(const Shape& s, int r, const void* xr,
                           const void* wg, const void* wu, const int32_t* counts,
-                          void* h, int num_cus, hipStream_t st);
+                          const int32_t* counts_host, void* h, int num_cus,
+                          hipStream_t st);
 hipError_t launch_down(const Shape& s, int r, const void* h, const void* wd,
-                       const PlanBuffers& b, void* z, int num_cus,
-                       hipStream_t st);
+                       const PlanBuffers& b, const int32_t* counts_host, void* z,
+                       int num_cus, hipStream_t st);
 hipError_t launch_pack_weights(const Shape& s, const void* src, void* dst,
                                int rows, int cols, int num_cus, hipStream_t st);
 hipError_t launch_combine(const Shape& s, const void* z, const float* weight,

@@ -56,7 +56,8 @@ def expected_total(T, E, k, d, f, C, es):
     pad = ceil_div(ce, 64) * 64  # round-buffer rows per expert, tiled
     TK = T * k
     nb = ceil_div(TK, 1024)
-    parts = [TK * 4, TK * 4, E * 4, (E + 1) * 4, 4, TK * 4, TK * 4, TK * 4,
+    # counts and R share one block: [E counts][R]
+    parts = [TK * 4, TK * 4, (E + 1) * 4, (E + 1) * 4, TK * 4, TK * 4, TK * 4,
              TK * 4, nb * E * 4, E * pad * d * es, E * pad * f * es, TK * d * es]
     return sum(al(p) for p in parts)
 
@@ -70,7 +71,8 @@ def test_workspace_is_a_function_of_the_config_only(B):
         n = B.workspace_size(cfg)
         assert n == expected_total(w.T, w.E, w.k, w.d_model, w.d_ff, w.C, es)
         lay = B.workspace_layout(cfg)
-        offs = [lay[f] for f in B.LAYOUT_FIELDS]
+        assert lay["n_rounds"] == lay["counts"] + 4 * w.E
+        offs = [lay[f] for f in B.LAYOUT_FIELDS if f != "n_rounds"]
         assert all(o % 256 == 0 for o in offs)
         assert offs == sorted(offs) and lay["total"] == n
         sizes[name] = n

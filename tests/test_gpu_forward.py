@@ -61,6 +61,27 @@ def test_forward_matches_oracle(name):
     assert torch.equal(y.view(ib), y2.view(ib))
     _, _, y3 = forward(case, poison=False, layout="row_major")
     assert torch.equal(y.view(ib), y3.view(ib)), "weight layouts disagree"
+    # moe_forward picks each round's tile shape from the expert counts; the
+    # stage calls always use the large tile: same bits
+    y4 = stage_path(case)
+    assert torch.equal(y.view(ib), y4.view(ib)), "tile shapes disagree"
+
+
+def stage_path(case):
+    """The layer through the stage calls (plan, then per round dispatch and
+    expert FFN, then combine)."""
+    cfg = case.cfg()
+    wg, wu, wd = case.weights()
+    ws = case.workspace(cfg)
+    note(f"{case.w.name}: stage calls")
+    R = B.moe_plan(cfg, case.logits, ws)
+    for r in range(R):
+        B.moe_dispatch(cfg, r, case.x, ws)
+        B.moe_expert_ffn(cfg, r, wg, wu, wd, ws)
+    y = case.new_y()
+    B.moe_combine(cfg, ws, y)
+    torch.cuda.synchronize()
+    return y
 
 
 def test_hot_expert_capacity_sweep_is_bit_identical():
