@@ -155,11 +155,11 @@ moe_status_t moe_workspace_layout(const moe_config_t *cfg,
  * assignments are then split into rounds of at most C' (the per-expert
  * capacity is fixed, and what does not fit waits for a later round).
  * Reads logits [T][E]; writes idx, weight, counts, offsets, perm, pos,
- * round_of, row_of and n_rounds in the workspace. If n_rounds_host is not
- * NULL the call waits for the stream and stores R there; otherwise it is
- * asynchronous. */
+ * round_of, row_of and n_rounds in the workspace. If plan_host is not NULL
+ * (host memory, E + 1 int32) the call waits for the stream and stores the
+ * E counts n_e followed by R there; otherwise it is asynchronous. */
 moe_status_t moe_plan(const moe_config_t *cfg, const float *logits, void *ws,
-                      size_t ws_bytes, int32_t *n_rounds_host, void *stream);
+                      size_t ws_bytes, int32_t *plan_host, void *stream);
 
 /* Dispatch of round r ("dispatch -> compute -> collect rounds"): for every
  * expert e and slot c < m(r,e), copies x[perm[offsets[e] + r*C' + c] / k]
@@ -176,22 +176,29 @@ moe_status_t moe_dispatch(const moe_config_t *cfg, int32_t round,
  * row c of o is stored at z[perm[offsets[e] + r*C' + c]] (collect into the
  * token-slot buffer). Grouped GEMMs over all active experts in one launch
  * each ("grouped GEMM" per expert group, section "Reducing per-expert
- * overhead" as quoted in "Key claims"). Asynchronous. */
+ * overhead" as quoted in "Key claims").
+ * counts_host: NULL, or a host copy of the E counts n_e (the first E values
+ * moe_plan stores in plan_host). With it the launch shape fits the round:
+ * a 256 x 256 output tile when that gives every CU a tile, else a 128 x 64
+ * tile, and no more workgroups than tiles (what moe_forward does); without
+ * it the 256 x 256 tile and one workgroup per CU are used. The results are
+ * bit-identical either way. Asynchronous. */
 moe_status_t moe_expert_ffn(const moe_config_t *cfg, int32_t round,
                             const void *w_gate, const void *w_up,
-                            const void *w_down, void *ws, size_t ws_bytes,
-                            void *stream);
+                            const void *w_down, const int32_t *counts_host,
+                            void *ws, size_t ws_bytes, void *stream);
 
 /* The two halves of moe_expert_ffn, for callers that time or schedule them
  * separately: gate/up writes h for round r (first m(r,e) rows of each
  * expert's region), down reads h and writes the round's rows of z. Same
  * arguments, layouts and asynchrony as moe_expert_ffn. */
 moe_status_t moe_expert_gate_up(const moe_config_t *cfg, int32_t round,
-                                const void *w_gate, const void *w_up, void *ws,
+                                const void *w_gate, const void *w_up,
+                                const int32_t *counts_host, void *ws,
                                 size_t ws_bytes, void *stream);
 moe_status_t moe_expert_down(const moe_config_t *cfg, int32_t round,
-                             const void *w_down, void *ws, size_t ws_bytes,
-                             void *stream);
+                             const void *w_down, const int32_t *counts_host,
+                             void *ws, size_t ws_bytes, void *stream);
 
 /* Repack expert weights from the row-major layout into the tiled layout
  * (MOE_WEIGHTS_TILED): gate and up are [E][f][d], down is [E][d][f]; each
@@ -208,8 +215,9 @@ moe_status_t moe_pack_weights(const moe_config_t *cfg, const void *w_gate,
 moe_status_t moe_combine(const moe_config_t *cfg, const void *ws,
                          size_t ws_bytes, void *y, void *stream);
 
-/* The whole layer: plan, one wait to learn R, then R rounds of dispatch and
- * expert compute + collect, then the weighted combine. y is written in full.
+/* The whole layer: plan, one wait to learn the counts and R, then R rounds
+ * of dispatch and expert compute + collect (launch shapes fitted to each
+ * round as with counts_host above), then the weighted combine. y is written in full.
  * Returns after enqueueing the combine (the plan's wait is the only host
  * synchronisation). The result does not depend on C. */
 moe_status_t moe_forward(const moe_config_t *cfg, const float *logits,

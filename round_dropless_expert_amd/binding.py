@@ -10,6 +10,8 @@ from __future__ import annotations
 import ctypes
 import os
 
+import numpy as np
+
 import torch  # loads the HIP runtime the library must share
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -83,9 +85,9 @@ def load() -> ctypes.CDLL:
     L.moe_workspace_layout.argtypes = [cfgp, ctypes.POINTER(MoeLayout)]
     L.moe_plan.argtypes = [cfgp, vp, vp, sz, i32p, vp]
     L.moe_dispatch.argtypes = [cfgp, i32, vp, vp, sz, vp]
-    L.moe_expert_ffn.argtypes = [cfgp, i32, vp, vp, vp, vp, sz, vp]
-    L.moe_expert_gate_up.argtypes = [cfgp, i32, vp, vp, vp, sz, vp]
-    L.moe_expert_down.argtypes = [cfgp, i32, vp, vp, sz, vp]
+    L.moe_expert_ffn.argtypes = [cfgp, i32, vp, vp, vp, i32p, vp, sz, vp]
+    L.moe_expert_gate_up.argtypes = [cfgp, i32, vp, vp, i32p, vp, sz, vp]
+    L.moe_expert_down.argtypes = [cfgp, i32, vp, i32p, vp, sz, vp]
     L.moe_pack_weights.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp]
     L.moe_combine.argtypes = [cfgp, vp, sz, vp, vp]
     L.moe_forward.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -165,13 +167,26 @@ def _nbytes(ws) -> int:
     return ws.numel() * ws.element_size()
 
 
-def moe_plan(cfg, logits, ws, read_rounds=True, stream=None):
-    """Route + plan. Returns R when read_rounds (waits for the stream)."""
-    R = ctypes.c_int32(0)
+def moe_plan(cfg, logits, ws, read_rounds=True, stream=None,
+             return_counts=False):
+    """Route + plan. With read_rounds (waits for the stream) returns R, or
+    (R, counts) with return_counts (counts: int32 numpy array of E, the
+    counts_host argument of the expert calls)."""
+    out = (ctypes.c_int32 * (cfg.E + 1))()
     _check(load().moe_plan(ctypes.byref(cfg), _ptr(logits), _ptr(ws),
-                           _nbytes(ws), ctypes.byref(R) if read_rounds else None,
+                           _nbytes(ws), out if read_rounds else None,
                            _stream(stream)))
-    return R.value if read_rounds else None
+    if not read_rounds:
+        return None
+    vals = np.frombuffer(out, dtype=np.int32).copy()
+    return (int(vals[-1]), vals[:-1].copy()) if return_counts else int(vals[-1])
+
+
+def _counts(counts_host):
+    if counts_host is None:
+        return None
+    a = np.ascontiguousarray(counts_host, dtype=np.int32)
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), a
 
 
 def moe_dispatch(cfg, round_, x, ws, stream=None):
@@ -179,22 +194,27 @@ def moe_dispatch(cfg, round_, x, ws, stream=None):
                                _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
-def moe_expert_ffn(cfg, round_, w_gate, w_up, w_down, ws, stream=None):
+def moe_expert_ffn(cfg, round_, w_gate, w_up, w_down, ws, stream=None,
+                   counts_host=None):
+    c = _counts(counts_host)
     _check(load().moe_expert_ffn(ctypes.byref(cfg), int(round_), _ptr(w_gate),
-                                 _ptr(w_up), _ptr(w_down), _ptr(ws),
-                                 _nbytes(ws), _stream(stream)))
+                                 _ptr(w_up), _ptr(w_down), c and c[0],
+                                 _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
-def moe_expert_gate_up(cfg, round_, w_gate, w_up, ws, stream=None):
+def moe_expert_gate_up(cfg, round_, w_gate, w_up, ws, stream=None,
+                       counts_host=None):
+    c = _counts(counts_host)
     _check(load().moe_expert_gate_up(ctypes.byref(cfg), int(round_),
-                                     _ptr(w_gate), _ptr(w_up), _ptr(ws),
-                                     _nbytes(ws), _stream(stream)))
+                                     _ptr(w_gate), _ptr(w_up), c and c[0],
+                                     _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
-def moe_expert_down(cfg, round_, w_down, ws, stream=None):
+def moe_expert_down(cfg, round_, w_down, ws, stream=None, counts_host=None):
+    c = _counts(counts_host)
     _check(load().moe_expert_down(ctypes.byref(cfg), int(round_),
-                                  _ptr(w_down), _ptr(ws), _nbytes(ws),
-                                  _stream(stream)))
+                                  _ptr(w_down), c and c[0], _ptr(ws),
+                                  _nbytes(ws), _stream(stream)))
 
 
 def moe_pack_weights(cfg, w_gate, w_up, w_down, out_gate, out_up, out_down,

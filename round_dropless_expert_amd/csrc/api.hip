@@ -182,6 +182,15 @@ moe_status_t run_plan(const Bound& b, const float* logits, hipStream_t st) {
   return MOE_OK;
 }
 
+// The E counts and R (adjacent in the workspace) to the host; waits.
+moe_status_t read_plan(const Bound& b, int32_t* out, hipStream_t st) {
+  MOE_HIP(hipMemcpyAsync(out, b.pb.counts, (b.s.E + 1) * sizeof(int32_t),
+                         hipMemcpyDeviceToHost, st),
+          "read of counts and R");
+  MOE_HIP(hipStreamSynchronize(st), "stream sync");
+  return MOE_OK;
+}
+
 moe_status_t run_ffn(const Bound& b, int r, const void* wg, const void* wu,
                      const void* wd, const int32_t* counts_host, int cus,
                      hipStream_t st) {
@@ -239,19 +248,14 @@ moe_status_t moe_workspace_layout(const moe_config_t* cfg,
 }
 
 moe_status_t moe_plan(const moe_config_t* cfg, const float* logits, void* ws,
-                      size_t ws_bytes, int32_t* n_rounds_host, void* stream) {
+                      size_t ws_bytes, int32_t* plan_host, void* stream) {
   Bound b;
   moe_status_t st = bind(cfg, ws, ws_bytes, &b);
   if (st != MOE_OK) return st;
   if ((st = check_ptr(logits, "logits")) != MOE_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if ((st = run_plan(b, logits, s)) != MOE_OK) return st;
-  if (n_rounds_host) {
-    MOE_HIP(hipMemcpyAsync(n_rounds_host, b.pb.n_rounds, sizeof(int32_t),
-                           hipMemcpyDeviceToHost, s),
-            "read of R");
-    MOE_HIP(hipStreamSynchronize(s), "stream sync");
-  }
+  if (plan_host) return read_plan(b, plan_host, s);
   return MOE_OK;
 }
 
@@ -272,8 +276,8 @@ moe_status_t moe_dispatch(const moe_config_t* cfg, int32_t round, const void* x,
 
 moe_status_t moe_expert_ffn(const moe_config_t* cfg, int32_t round,
                             const void* w_gate, const void* w_up,
-                            const void* w_down, void* ws, size_t ws_bytes,
-                            void* stream) {
+                            const void* w_down, const int32_t* counts_host,
+                            void* ws, size_t ws_bytes, void* stream) {
   Bound b;
   moe_status_t st = bind(cfg, ws, ws_bytes, &b);
   if (st != MOE_OK) return st;
@@ -283,12 +287,13 @@ moe_status_t moe_expert_ffn(const moe_config_t* cfg, int32_t round,
   if ((st = check_round(b, round)) != MOE_OK) return st;
   int cus = 0;
   if ((st = num_cus(&cus)) != MOE_OK) return st;
-  return run_ffn(b, round, w_gate, w_up, w_down, nullptr, cus,
+  return run_ffn(b, round, w_gate, w_up, w_down, counts_host, cus,
                  static_cast<hipStream_t>(stream));
 }
 
 moe_status_t moe_expert_gate_up(const moe_config_t* cfg, int32_t round,
-                                const void* w_gate, const void* w_up, void* ws,
+                                const void* w_gate, const void* w_up,
+                                const int32_t* counts_host, void* ws,
                                 size_t ws_bytes, void* stream) {
   Bound b;
   moe_status_t st = bind(cfg, ws, ws_bytes, &b);
@@ -299,15 +304,15 @@ moe_status_t moe_expert_gate_up(const moe_config_t* cfg, int32_t round,
   int cus = 0;
   if ((st = num_cus(&cus)) != MOE_OK) return st;
   MOE_HIP(moe::launch_gate_up(b.s, round, b.ws + b.L.xr, w_gate, w_up,
-                              b.pb.counts, nullptr, b.ws + b.L.h, cus,
+                              b.pb.counts, counts_host, b.ws + b.L.h, cus,
                               static_cast<hipStream_t>(stream)),
           "gate/up launch");
   return MOE_OK;
 }
 
 moe_status_t moe_expert_down(const moe_config_t* cfg, int32_t round,
-                             const void* w_down, void* ws, size_t ws_bytes,
-                             void* stream) {
+                             const void* w_down, const int32_t* counts_host,
+                             void* ws, size_t ws_bytes, void* stream) {
   Bound b;
   moe_status_t st = bind(cfg, ws, ws_bytes, &b);
   if (st != MOE_OK) return st;
@@ -315,7 +320,7 @@ moe_status_t moe_expert_down(const moe_config_t* cfg, int32_t round,
   if ((st = check_round(b, round)) != MOE_OK) return st;
   int cus = 0;
   if ((st = num_cus(&cus)) != MOE_OK) return st;
-  MOE_HIP(moe::launch_down(b.s, round, b.ws + b.L.h, w_down, b.pb, nullptr,
+  MOE_HIP(moe::launch_down(b.s, round, b.ws + b.L.h, w_down, b.pb, counts_host,
                            b.ws + b.L.z, cus, static_cast<hipStream_t>(stream)),
           "down launch");
   return MOE_OK;
@@ -384,10 +389,7 @@ moe_status_t moe_forward(const moe_config_t* cfg, const float* logits,
   if ((st = run_plan(b, logits, s)) != MOE_OK) return st;
   // one read: the E per-expert counts followed by R
   int32_t counts_r[kMaxExperts + 1];
-  MOE_HIP(hipMemcpyAsync(counts_r, b.pb.counts, (b.s.E + 1) * sizeof(int32_t),
-                         hipMemcpyDeviceToHost, s),
-          "read of counts and R");
-  MOE_HIP(hipStreamSynchronize(s), "stream sync");
+  if ((st = read_plan(b, counts_r, s)) != MOE_OK) return st;
   const int32_t R = counts_r[b.s.E];
   const int64_t max_rounds = (b.s.T + b.s.ce - 1) / b.s.ce;
   if (R < 1 || R > max_rounds)

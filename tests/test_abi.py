@@ -141,7 +141,11 @@ def test_pointer_and_workspace_checks_before_any_hip_call(B):
     # round range: ceil(T / C') rounds at most
     assert L.moe_dispatch(c, -1, p, p, need, None) == B.MOE_ERR_INVALID_ARGUMENT
     assert L.moe_dispatch(c, 8, p, p, need, None) == B.MOE_ERR_INVALID_ARGUMENT
-    assert L.moe_expert_ffn(c, 8, p, p, p, p, need, None) == \
+    assert L.moe_expert_ffn(c, 8, p, p, p, None, p, need, None) == \
+        B.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_expert_gate_up(c, 0, p, None, None, p, need, None) == \
+        B.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_expert_down(c, -1, p, None, p, need, None) == \
         B.MOE_ERR_INVALID_ARGUMENT
     assert L.moe_combine(c, p, need, None, None) == B.MOE_ERR_INVALID_ARGUMENT
     assert L.moe_pack_weights(c, p, p, None, p, p, p, None) == \

@@ -49,10 +49,14 @@ def test_stages_match_oracle(w, layout):
     wg, wu, wd = case.weights(layout)
     ws = case.workspace(cfg)
     note(f"{w.name}/{layout}: moe_plan")
-    R = B.moe_plan(cfg, case.logits, ws)
+    R, counts = B.moe_plan(cfg, case.logits, ws, return_counts=True)
     views = B.workspace_views(cfg, ws)
     p = oracle.plan(case.idx, w.E, w.C)
     assert R == p.R
+    np.testing.assert_array_equal(counts, p.counts)
+    # tiled weights: launch shapes fitted to each round (as moe_forward);
+    # row-major: the default shape
+    counts_host = counts if layout == "tiled" else None
     assert_plan_equal(views, p, case.idx)
     wt = views["weight"].cpu().numpy().astype(np.float64)
     assert np.all(np.abs(wt - case.wt) <= 1e-6 * case.wt), "routing weights"
@@ -76,7 +80,7 @@ def test_stages_match_oracle(w, layout):
             f"xr round {r}"
 
         note(f"{w.name}/{layout}: moe_expert_ffn round {r}")
-        B.moe_expert_ffn(cfg, r, wg, wu, wd, ws)
+        B.moe_expert_ffn(cfg, r, wg, wu, wd, ws, counts_host=counts_host)
         torch.cuda.synchronize()
         h_ref, o_ref = oracle.assignment_outputs(
             np.array(assigns), case.idx, case.inp.x, case.inp.Wg, case.inp.Wu,
