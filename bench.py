@@ -188,7 +188,7 @@ def main():
     df = float(w.d_model) * w.d_ff
     disp_bytes = [float(U[r] * w.d_model * es + A[r] * w.d_model * es + 4 * A[r])
                   for r in range(R)]
-    comb_bytes = float(TK * w.d_model * es + w.T * w.d_model * es + 4 * TK)
+    comb_bytes = float(TK * w.d_model * es + w.T * w.d_model * es + 8 * TK)
     per_launch = {"plan": {"us": sec["plan"] * 1e6}}
     for r in range(R):
         t_d, t_g, t_n = (sec[f"{n}[{r}]"] for n in ("dispatch", "gate_up", "down"))

@@ -118,7 +118,9 @@ typedef struct {
  *                            c; rows at or beyond m(r,e) hold stale data)
  *   h        elem [E][P][f]  SwiGLU activations of the round, same layout
  *   z        elem [T*k][d]   unweighted expert output of every assignment,
- *                            in token-slot order
+ *                            in expert-sorted order: row i holds the output
+ *                            of assignment perm[i] (so assignment a's row
+ *                            is pos[a])
  *   scratch  int32 [...]     plan-internal partial counts
  * The layout, and so the size, is a pure function of the config.
  */
@@ -173,8 +175,9 @@ moe_status_t moe_dispatch(const moe_config_t *cfg, int32_t round,
 /* Expert compute and collect of round r: for every expert e with
  * m(r,e) > 0, h = silu(xr_e . w_gate[e]^T) * (xr_e . w_up[e]^T) on the
  * first m(r,e) rows of expert e's region, then o = h . w_down[e]^T, and
- * row c of o is stored at z[perm[offsets[e] + r*C' + c]] (collect into the
- * token-slot buffer). Grouped GEMMs over all active experts in one launch
+ * row c of o is stored at z[offsets[e] + r*C' + c], the row of assignment
+ * perm[offsets[e] + r*C' + c] (the combine collects these rows back to
+ * token order). Grouped GEMMs over all active experts in one launch
  * each ("grouped GEMM" per expert group, section "Reducing per-expert
  * overhead" as quoted in "Key claims").
  * counts_host: NULL, or a host copy of the E counts n_e (the first E values
@@ -209,15 +212,17 @@ moe_status_t moe_pack_weights(const moe_config_t *cfg, const void *w_gate,
                               void *out_gate, void *out_up, void *out_down,
                               void *stream);
 
-/* Weighted combine after the last round: y[t] = sum_{j<k} weight[t][j] *
- * z[t*k + j], summed in fp32 over ascending j and rounded once to elem.
- * Reads only the workspace. Asynchronous. */
+/* Collect and weighted combine after the last round: y[t] =
+ * sum_{j<k} weight[t][j] * z[pos[t*k + j]] (gathering every assignment's
+ * expert output back to its token), summed in fp32 over ascending j and
+ * rounded once to elem. Reads only the workspace. Asynchronous. */
 moe_status_t moe_combine(const moe_config_t *cfg, const void *ws,
                          size_t ws_bytes, void *y, void *stream);
 
 /* The whole layer: plan, one wait to learn the counts and R, then R rounds
- * of dispatch and expert compute + collect (launch shapes fitted to each
- * round as with counts_host above), then the weighted combine. y is written in full.
+ * of dispatch and expert compute (launch shapes fitted to each round as
+ * with counts_host above), then the collect and weighted combine. y is
+ * written in full.
  * Returns after enqueueing the combine (the plan's wait is the only host
  * synchronisation). The result does not depend on C. */
 moe_status_t moe_forward(const moe_config_t *cfg, const float *logits,

@@ -364,7 +364,7 @@ moe_status_t moe_combine(const moe_config_t* cfg, const void* ws,
   if ((st = check_ptr(y, "y")) != MOE_OK) return st;
   int cus = 0;
   if ((st = num_cus(&cus)) != MOE_OK) return st;
-  MOE_HIP(moe::launch_combine(b.s, b.ws + b.L.z, b.pb.weight, y, cus,
+  MOE_HIP(moe::launch_combine(b.s, b.ws + b.L.z, b.pb.weight, b.pb.pos, y, cus,
                               static_cast<hipStream_t>(stream)),
           "combine launch");
   return MOE_OK;
@@ -400,7 +400,7 @@ moe_status_t moe_forward(const moe_config_t* cfg, const float* logits,
     if ((st = run_ffn(b, r, w_gate, w_up, w_down, counts_r, cus, s)) != MOE_OK)
       return st;
   }
-  MOE_HIP(moe::launch_combine(b.s, b.ws + b.L.z, b.pb.weight, y, cus, s),
+  MOE_HIP(moe::launch_combine(b.s, b.ws + b.L.z, b.pb.weight, b.pb.pos, y, cus, s),
           "combine launch");
   return MOE_OK;
 }

@@ -120,14 +120,15 @@ hipError_t launch_pack_weights(const Shape& s, const void* src, void* dst,
   return hipGetLastError();
 }
 
-// y[t] = sum_{j<k} weight[t][j] * z[t*k + j], fp32 fused multiply-adds over
-// ascending j starting from zero, rounded once to the element type. A
-// token's k rows of z are contiguous, so one wavefront streams k*d elements
-// and writes d.
+// y[t] = sum_{j<k} weight[t][j] * z[pos[t*k + j]], fp32 fused multiply-adds
+// over ascending j starting from zero, rounded once to the element type. z
+// holds the expert outputs in expert-sorted order (row i = assignment
+// perm[i]), so pos[a] is assignment a's row: the collect is this gather.
+// One wavefront per token streams its k rows (16-byte vectors) and writes d.
 template <typename Elem>
 __global__ __launch_bounds__(256) void combine_kernel(
-    const Elem* __restrict__ z, const float* __restrict__ weight, int64_t T,
-    int k, int d, Elem* __restrict__ y) {
+    const Elem* __restrict__ z, const float* __restrict__ weight,
+    const int32_t* __restrict__ pos, int64_t T, int k, int d, Elem* __restrict__ y) {
   constexpr int kVec = 16 / sizeof(Elem);  // elements per 16-byte vector
   typedef Elem vec_t __attribute__((ext_vector_type(kVec)));
   const int lane = threadIdx.x & (kWave - 1);
@@ -136,7 +137,7 @@ __global__ __launch_bounds__(256) void combine_kernel(
   const int nv = d / kVec;
   for (int64_t t = wave; t < T; t += nwaves) {
     const float wl = lane < k ? weight[t * k + lane] : 0.f;
-    const vec_t* zt = reinterpret_cast<const vec_t*>(z + t * k * (int64_t)d);
+    const int rl = lane < k ? pos[t * k + lane] : 0;
     vec_t* yt = reinterpret_cast<vec_t*>(y + t * (int64_t)d);
     for (int v = lane; v < nv; v += kWave) {
       float acc[kVec];
@@ -144,7 +145,8 @@ __global__ __launch_bounds__(256) void combine_kernel(
       for (int q = 0; q < kVec; ++q) acc[q] = 0.f;
       for (int j = 0; j < k; ++j) {
         const float wj = __shfl(wl, j, kWave);
-        const vec_t zv = zt[(int64_t)j * nv + v];
+        const int64_t row = __shfl(rl, j, kWave);
+        const vec_t zv = reinterpret_cast<const vec_t*>(z + row * d)[v];
 #pragma unroll
         for (int q = 0; q < kVec; ++q) acc[q] = fmaf(wj, to_f32(zv[q]), acc[q]);
       }
@@ -157,17 +159,17 @@ __global__ __launch_bounds__(256) void combine_kernel(
 }
 
 hipError_t launch_combine(const Shape& s, const void* z, const float* weight,
-                          void* y, int num_cus, hipStream_t st) {
+                          const int32_t* pos, void* y, int num_cus, hipStream_t st) {
   int64_t blocks = (s.T + 3) / 4;
   const int64_t cap = (int64_t)num_cus * 8;
   if (blocks > cap) blocks = cap;
   if (s.bf16)
     hipLaunchKernelGGL(combine_kernel<bf16>, dim3((unsigned)blocks), dim3(256),
-                       0, st, static_cast<const bf16*>(z), weight, s.T, s.k,
+                       0, st, static_cast<const bf16*>(z), weight, pos, s.T, s.k,
                        s.d, static_cast<bf16*>(y));
   else
     hipLaunchKernelGGL(combine_kernel<float>, dim3((unsigned)blocks), dim3(256),
-                       0, st, static_cast<const float*>(z), weight, s.T, s.k,
+                       0, st, static_cast<const float*>(z), weight, pos, s.T, s.k,
                        s.d, static_cast<float*>(y));
   return hipGetLastError();
 }

@@ -21,10 +21,10 @@
 //
 // Tiles: 256 threads = 2 x 2 wavefronts; wavefront (wm, wn) owns WJ 32-token
 // blocks and WI 32-weight-row blocks. K advances 64 bytes per stage (32 bf16
-// or 16 fp32); SPB stages form a slot of a four-slot LDS ring filled by
-// LDS-direct buffer loads, with up to three slots in flight and one barrier
+// or 16 fp32); SPB stages form a slot of a five-slot LDS ring filled by
+// LDS-direct buffer loads, with up to four slots in flight and one barrier
 // per slot. Fragment reads run one MFMA step ahead of the MFMAs that use
-// them. Two tile shapes: 256 weight rows x 256 tokens, and 128 x 64 (three
+// them. Two tile shapes: 256 weight rows x 256 tokens, and 128 x 64 (two
 // stages per slot) for rounds with too few rows to give every CU a large
 // tile, which mostly stream weights and need many workgroups.
 //
@@ -96,14 +96,54 @@ struct GemmParams {
   int tiled_w;         // weights in the tiled layout (else row-major)
 };
 
+// silu(g) * u = g * u / (1 + e^-g), with the hardware base-2 exponential
+// (e^-g = 2^(-g log2 e)) and reciprocal (each about 1 ulp): a handful of
+// instructions per element instead of a full-precision exp and divide,
+// since the epilogue runs while the matrix cores idle. Large -g gives
+// 2^+inf = inf and a zero reciprocal (silu -> -0), large g gives 1.
 __device__ __forceinline__ float silu_mul(float g, float u) {
-  return g / (1.0f + expf(-g)) * u;
+  const float e = __builtin_amdgcn_exp2f(g * -1.44269504088896341f);
+  return g * u * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// An accumulator element, read from its AGPR at this point of the program
+// (asm, so that the epilogue moves a few values at a time into VGPRs rather
+// than the compiler copying every accumulator out at once).
+__device__ __forceinline__ float acc_read(float a) {
+  float v;
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
+  return v;
 }
 
 // Buffer resource word 3 for gfx9-family raw (untyped) buffer access.
 constexpr int kRsrcWord3 = 0x00020000;
 
 typedef __attribute__((address_space(3))) char lds_char;
+
+// Buffer-to-LDS loads (LDS-direct): lane i reads `bytes` at voff + soff
+// of the buffer and writes them to LDS at m0 + bytes * i. Written as asm:
+// the compiler then neither tracks them (every wait on them is the kernel's
+// own, explicit and exact, vmcnt count) nor moves them, so they stay
+// exactly where the stage loop interleaves them with the MFMAs. They have
+// no register results. M0 is saved and restored around each one, with the
+// wait state an LDS-direct load needs after an M0 write.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff,
+                                           uint32_t soff, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+      : "m0");
+}
+#pragma clang diagnostic pop
+
 // Wait until at most N of this wavefront's vector-memory operations are
 // outstanding (the LDS-direct loads of later stages), then join the
 // workgroup barrier. A bare s_barrier: __syncthreads() would also drain
@@ -121,37 +161,23 @@ struct Frags {
   typename MmaOp<Elem>::frag_t a[WI], b[WJ];
 };
 
-template <typename Elem, int WI, int WJ>
+// One MFMA step (WI x WJ MFMAs) with kOps other instructions spread over
+// it in a fixed order: op(x) for x = 0 .. kOps-1 (fragment reads of the
+// next step first, then LDS-direct loads), issued after MFMA i for
+// x in [i*kOps/M, (i+1)*kOps/M). Each group is fenced, so the compiler keeps
+// the order; it still inserts the LDS-read waits before the MFMAs of the
+// next step that consume them.
+template <typename Elem, int WI, int WJ, int kOps, typename Op>
 __device__ __forceinline__ void mma_step(f32x16 (&acc)[WI][WJ],
-                                         const Frags<Elem, WI, WJ>& f) {
+                                         const Frags<Elem, WI, WJ>& f, Op op) {
+  constexpr int M = WI * WJ;
 #pragma unroll
-  for (int ib = 0; ib < WI; ++ib)
+  for (int i = 0; i < M; ++i) {
+    MmaOp<Elem>::mma(acc[i / WJ][i % WJ], f.a[i / WJ], f.b[i % WJ]);
 #pragma unroll
-    for (int jb = 0; jb < WJ; ++jb) MmaOp<Elem>::mma(acc[ib][jb], f.a[ib], f.b[jb]);
-}
-
-// Scheduling pins for one MFMA step: one LDS fragment read after each of
-// the first MFMAs, then (when a stage is being fetched) one LDS-direct
-// buffer load after each of the following MFMAs, then the remaining MFMAs.
-template <int kMfma, int kReads, int kLoads>
-__device__ __forceinline__ void pin_step() {
-  constexpr int nl = kReads < kMfma ? kReads : kMfma;
-#pragma unroll
-  for (int g = 0; g < nl; ++g) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+    for (int x = i * kOps / M; x < (i + 1) * kOps / M; ++x) op(x);
+    __builtin_amdgcn_sched_barrier(0);
   }
-  if constexpr (kReads > nl) __builtin_amdgcn_sched_group_barrier(0x100, kReads - nl, 0);
-  constexpr int room = kMfma - nl;
-  constexpr int nv = kLoads < room ? kLoads : room;
-#pragma unroll
-  for (int g = 0; g < nv; ++g) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
-  }
-  if constexpr (kLoads > nv) __builtin_amdgcn_sched_group_barrier(0x020, kLoads - nv, 0);
-  if constexpr (room - nv > 0) __builtin_amdgcn_sched_group_barrier(0x008, room - nv, 0);
-  __builtin_amdgcn_sched_barrier(0);
 }
 
 // K pipeline: a ring of kSlots LDS slots, each holding SPB consecutive
@@ -159,20 +185,37 @@ __device__ __forceinline__ void pin_step() {
 // placed before its last MFMA step; the barrier waits for super-stage
 // ks + 1 (ks + 2 and ks + 3 stay in flight), after which the next
 // super-stage's first fragments load while the last step's MFMAs run. The
-// first MFMA step of super-stage ks issues the fetch of ks + kSlots - 1 into
-// the slot freed at the previous barrier, one load between MFMAs.
+// first MFMA step of super-stage ks issues the fetch of ks + 3 into the slot
+// freed at the previous barrier, one load between MFMAs. The ring runs on
+// across tiles: the last three fetches of a tile bring the first three
+// super-stages of the workgroup's next tile, so a tile's SwiGLU / store
+// epilogue overlaps those loads and the next tile starts with data in LDS.
 constexpr int kSlots = 4;  // the stage loop below names four slots
 
 // Tile configurations (WI / WJ: 32-row MFMA blocks per wavefront along
 // weight rows / tokens; the 2 x 2 wavefronts cover 64*WI weight rows and
 // 64*WJ tokens; SPB: 64-byte K stages per slot and barrier).
-struct TileBig {    // rounds with more than 64 rows in some expert
+struct TileBig {    // rounds that give every CU at least one such tile
   static constexpr int WI = 4, WJ = 4, SPB = 1;
 };
 struct TileSmall {  // rounds too small to give every CU a large tile: such
                     // a round mostly streams expert weights; spread them
                     // over more workgroups and keep more bytes in flight
-  static constexpr int WI = 2, WJ = 1, SPB = 3;
+  static constexpr int WI = 2, WJ = 1, SPB = 2;
+};
+
+// Offset that puts a buffer load out of range: the load returns zeros and
+// touches no memory (every real offset is below 2^31).
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+// Where one tile's operands live: buffer descriptors over the expert's
+// weights and round rows, and the uniform byte offset (k = 0) of each 64-row
+// load pass. Everything is wavefront-uniform (scalar registers).
+template <int kWPasses, int kTPasses>
+struct TileSrc {
+  __amdgpu_buffer_rsrc_t rw0, rw1, ra;
+  uint32_t wbase[kWPasses];  // weight pass offsets
+  uint32_t tbase[kTPasses];  // token pass offsets, kOutOfRange if dead
 };
 
 template <typename Elem, int WI, int WJ, int SPB, bool kGateUp>
@@ -193,9 +236,13 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
   constexpr int kSteps = MmaOp<Elem>::kSteps;
   constexpr int kMfmaPerStep = WI * WJ;
   constexpr int kReadsPerStep = WI + WJ;
+  // A barrier waits for the fetch of super-stage ks + 1; two more fetches
+  // are in flight behind it (see the stage loop)
+  constexpr int kWait = (kSlots - 2) * kLoads;
+  typedef TileSrc<kWPasses, kTPasses> src_t;
   static_assert(kSteps % 2 == 0, "fragment sets alternate by step");
   static_assert(WI % 2 == 0, "gate/up pairs and the 2 x 2 wavefront grid");
-  static_assert(kLoads * (kSlots - 2) <= 63, "vmcnt budget");
+  static_assert(kWait <= 63, "vmcnt budget");
 
   // the ring: kSlots slots as separate LDS objects, so the compiler can
   // tell a fragment read of one slot from a pending LDS-direct fill of
@@ -204,8 +251,6 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
   __shared__ __attribute__((aligned(1024))) char slot1[kSlotBytes];
   __shared__ __attribute__((aligned(1024))) char slot2[kSlotBytes];
   __shared__ __attribute__((aligned(1024))) char slot3[kSlotBytes];
-  __shared__ int tile_pre[kWave + 1];
-  __shared__ int rows_m[kWave];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -215,31 +260,104 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
   const int half = lane / 32;
   const int l32 = lane & 31;
 
+  // Every wavefront keeps the round's tile table in registers: lane e holds
+  // expert e's rows m_e and the inclusive prefix of the tile counts.
   const int nt = (p.N + NF - 1) / NF;
-  if (tid < kWave) {
-    const int e = tid;
-    const int m = e < p.E ? rows_in_round(p.counts[e], p.r, p.ce) : 0;
-    rows_m[e] = m;
-    const int tiles = ((m + BM - 1) / BM) * nt;
-    const int incl = wave_inclusive_scan(tiles);
-    tile_pre[e + 1] = incl;
-    if (e == 0) tile_pre[0] = 0;
-  }
-  __syncthreads();
-  const int total = __builtin_amdgcn_readfirstlane(tile_pre[p.E]);
+  const int lane_m = lane < p.E ? rows_in_round(p.counts[lane], p.r, p.ce) : 0;
+  const int lane_incl = wave_inclusive_scan(((lane_m + BM - 1) / BM) * nt);
+  const int total = __builtin_amdgcn_readlane(lane_incl, kWave - 1);
+  // (down) lane e also holds offsets[e]: the epilogue then needs no load
+  const int lane_off = !kGateUp && lane < p.E ? p.offsets[lane] : 0;
 
   // XCD-contiguous walk: workgroup b runs on XCD b % 8.
   const int G = gridDim.x;
-  const int slot = (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8);
+  int tile = (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8);
+  if (tile >= total) return;
+
+  const uint32_t kbytes = (uint32_t)p.K * kEs;    // bytes of one row
+  const uint32_t band_bytes = kbytes * kTileRows;  // one 64-row band, tiled
+  const uint32_t wbytes = (uint32_t)p.N * kbytes;  // one expert's matrix
+  const uint32_t wstride = p.tiled_w ? (uint32_t)kTileBytes : (uint32_t)kRowBytes;
 
   // Row order inside a stage: weight rows, then token rows. For gate/up the
   // weight rows are all gate rows (features n0 .. n0+NF-1), then all up
   // rows of the same features, so every 64-row load pass reads one matrix.
   // Load passes: pass i fills stage rows 64*i .. 64*i+63; lane tid writes
   // bytes [16*tid, 16*tid+16) of the pass: row r0 = tid / 4, physical
-  // chunk tid % 4, i.e. logical chunk (tid % 4) ^ ((r0 >> 2) & 3).
+  // chunk tid % 4, i.e. logical chunk (tid % 4) ^ ((r0 >> 2) & 3). The
+  // lane's part of the source offset is the same for every pass: a tiled
+  // band is one contiguous 4 KiB block per stage; a row-major band gives
+  // row r0 of the band, logical chunk `chunk`.
   const int r0 = tid >> 2;
   const int chunk = (tid & 3) ^ ((r0 >> 2) & 3);
+  const uint32_t vo_w = p.tiled_w ? (uint32_t)tid * 16 : (uint32_t)r0 * kbytes + chunk * 16;
+  const uint32_t vo_t = (uint32_t)tid * 16;
+
+  // Tile t: expert, feature block and token block, and its operand sources.
+  // Weight rows at or past N and token bands past m or past the round
+  // buffer fall outside the descriptors' ranges or get kOutOfRange, so they
+  // read as zeros; they only feed outputs that are never stored.
+  int e = 0, m = 0, n0 = 0, m0 = 0;
+  auto locate = [&](int t, int& te, int& tm, int& tn0, int& tm0) {
+    // expert of the tile: the number of experts whose tiles all come first
+    te = __builtin_popcountll(__builtin_amdgcn_ballot_w64(lane_incl <= t));
+    tm = __builtin_amdgcn_readlane(lane_m, te);
+    const int mt = (tm + BM - 1) / BM;
+    const int local = t - (te > 0 ? __builtin_amdgcn_readlane(lane_incl, te - 1) : 0);
+    tn0 = (local / mt) * NF;
+    tm0 = (local % mt) * BM;
+  };
+  auto sources = [&](int te, int tm, int tn0, int tm0, bool exists) {
+    src_t S;
+    const uint32_t wb = exists ? wbytes : 0u;  // no next tile: all out of range
+    S.rw0 = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.w0 + (int64_t)te * p.N * p.K), 0, (int)wb, kRsrcWord3);
+    S.rw1 = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(kGateUp ? p.w1 + (int64_t)te * p.N * p.K : p.w0), 0, (int)wb,
+        kRsrcWord3);
+    S.ra = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.act + (int64_t)te * p.ce_pad * p.K), 0,
+        exists ? (int)((uint32_t)p.ce_pad * kbytes) : 0, kRsrcWord3);
+#pragma unroll
+    for (int i = 0; i < kWPasses; ++i) {
+      int feat0 = tn0 + 64 * i;
+      if (kGateUp && 64 * i >= BN / 2) feat0 -= BN / 2;  // an up-row pass
+      S.wbase[i] = p.tiled_w ? (uint32_t)(feat0 / 64) * band_bytes
+                             : (uint32_t)feat0 * kbytes;
+    }
+#pragma unroll
+    for (int j = 0; j < kTPasses; ++j)
+      S.tbase[j] = tm0 + 64 * j < tm ? (uint32_t)(tm0 / 64 + j) * band_bytes
+                                     : kOutOfRange;
+    return S;
+  };
+
+  const int KT = p.K / kStageK;            // 64-byte K stages
+  const int KS = (KT + SPB - 1) / SPB;     // super-stages of one tile
+  const int KS4 = (KS + kSlots - 1) / kSlots * kSlots;
+
+  // Load x of the fetch of super-stage ks of the tile with sources S into
+  // `slot_mem`: stage sub = x / kPasses of the super-stage, pass
+  // i = x % kPasses (64 rows: weight rows, then token rows); lane i of a
+  // wavefront writes bytes [16 i, 16 i + 16) of its 1 KiB share of the
+  // pass's 4 KiB. A stage at or past the end of K reads as zeros and adds
+  // exact zeros.
+  const uint32_t lds_wave = (uint32_t)wave_id * 1024;
+  auto fetch_one = [&](char* slot_mem, int ks, const src_t& S, int x) {
+    const int sub = x / kPasses, i = x % kPasses;
+    const int g = ks * SPB + sub;
+    const bool w = i < kWPasses;
+    const __amdgpu_buffer_rsrc_t rs =
+        !w ? S.ra : ((kGateUp && 64 * i >= BN / 2) ? S.rw1 : S.rw0);
+    const uint32_t base = w ? S.wbase[i] : S.tbase[i - kWPasses];
+    const uint32_t soff =
+        g < KT && base != kOutOfRange
+            ? base + (uint32_t)g * (w ? wstride : (uint32_t)kTileBytes)
+            : kOutOfRange;
+    const uint32_t lds = (uint32_t)(uintptr_t)(lds_char*)slot_mem +
+                         sub * kStageBytes + i * 4096 + lds_wave;
+    lds_load16(rs, w ? vo_w : vo_t, soff, lds);
+  };
   // fragment rows of this lane: weight block ib, token block 0
   auto wrow_of = [&](int ib) {
     if (kGateUp)
@@ -247,51 +365,41 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
     return wn * (BN / 2) + ib * 32 + l32;
   };
   const int trow = BN + wm * (BM / 2) + l32;
+  frags_t f0, f1;
+  // fragment r of step s of the stage at `stage`: weight blocks, then token
+  // blocks
+  auto read_one = [&](frags_t& f, const char* stage, int s, int r) {
+    if (r < WI)
+      f.a[r] = MmaOp<Elem>::load(stage, wrow_of(r), s, half);
+    else
+      f.b[r - WI] = MmaOp<Elem>::load(stage, trow + 32 * (r - WI), s, half);
+  };
 
-  for (int tile = slot; tile < total; tile += G) {
-    const int e = __builtin_amdgcn_readfirstlane(segment_of(tile_pre, p.E + 1, tile));
-    const int m = __builtin_amdgcn_readfirstlane(rows_m[e]);
-    const int mt = (m + BM - 1) / BM;
-    const int local = tile - __builtin_amdgcn_readfirstlane(tile_pre[e]);
-    const int n0 = (local / mt) * NF;
-    const int m0 = (local % mt) * BM;
-
-    const uint32_t wbytes = (uint32_t)p.N * p.K * kEs;
-    const uint32_t kbytes = (uint32_t)p.K * kEs;    // bytes of one row
-    const uint32_t band_bytes = kbytes * kTileRows;  // one 64-row band, tiled
-    const __amdgpu_buffer_rsrc_t rw0 = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(p.w0 + (int64_t)e * p.N * p.K), 0, (int)wbytes, kRsrcWord3);
-    const __amdgpu_buffer_rsrc_t rw1 = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(kGateUp ? p.w1 + (int64_t)e * p.N * p.K : p.w0), 0, (int)wbytes,
-        kRsrcWord3);
-    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(p.act + (int64_t)e * p.ce_pad * p.K), 0,
-        (int)((uint32_t)p.ce_pad * kbytes), kRsrcWord3);
-
-    // Byte offsets (k = 0) of what this lane fetches in each pass. A pass
-    // covers one 64-row band: tiled operands give one contiguous 4 KiB
-    // block per stage (the lane's 16 bytes at 16 * tid); row-major weights
-    // give this lane's row r0 of the band, logical chunk `chunk`.
-    uint32_t voff[kPasses];
+  // prologue of the workgroup's first tile: super-stages 0 .. 2 in flight;
+  // wait for the first
+  locate(tile, e, m, n0, m0);
+  src_t cur = sources(e, m, n0, m0, true);
 #pragma unroll
-    for (int i = 0; i < kWPasses; ++i) {
-      int feat0 = n0 + 64 * i;
-      if (kGateUp && 64 * i >= BN / 2) feat0 -= BN / 2;  // an up-row pass
-      if (p.tiled_w) {
-        const int band = feat0 < p.N ? feat0 / 64 : p.N / 64 - 1;
-        voff[i] = (uint32_t)band * band_bytes + tid * 16;
-      } else {
-        int feat = feat0 + r0;
-        feat = feat < p.N ? feat : p.N - 1;
-        voff[i] = (uint32_t)feat * kbytes + chunk * 16;
-      }
-    }
+  for (int x = 0; x < kLoads; ++x) fetch_one(slot0, 0, cur, x);
 #pragma unroll
-    for (int j = 0; j < kTPasses; ++j)  // bands past ce_pad read as zeros
-      voff[kWPasses + j] = (uint32_t)(m0 / 64 + j) * band_bytes + tid * 16;
-    const uint32_t wstride = p.tiled_w ? (uint32_t)kTileBytes : (uint32_t)kRowBytes;
+  for (int x = 0; x < kLoads; ++x) fetch_one(slot1, 1, cur, x);
+#pragma unroll
+  for (int x = 0; x < kLoads; ++x) fetch_one(slot2, 2, cur, x);
+  wait_vmem_barrier<kWait>();
+#pragma unroll
+  for (int r = 0; r < kReadsPerStep; ++r) read_one(f0, slot0, 0, r);
 
-    f32x16 acc[WI][WJ];
+  typedef Elem vec4_t __attribute__((ext_vector_type(4)));
+  f32x16 acc[WI][WJ];
+  while (true) {
+    // the next tile of this workgroup, whose first super-stages the ring
+    // fetches at the end of this one
+    const int tile_n = tile + G;
+    const bool has_next = tile_n < total;
+    int e_n = 0, m_n = 0, n0_n = 0, m0_n = 0;
+    if (has_next) locate(tile_n, e_n, m_n, n0_n, m0_n);
+    const src_t nxt = sources(e_n, m_n, n0_n, m0_n, has_next);
+
 #pragma unroll
     for (int ib = 0; ib < WI; ++ib)
 #pragma unroll
@@ -299,85 +407,39 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[ib][jb][v] = 0.f;
 
-    const int KT = p.K / kStageK;
-
-    // Fetch super-stage ks (stages ks*SPB .. ks*SPB+SPB-1) into `slot` with
-    // LDS-direct buffer loads (lane i of a wavefront writes bytes
-    // [16 i, 16 i + 16) of its 1 KiB share of each 4 KiB pass). A stage at
-    // or past the end of K is fetched with an offset beyond the buffer: the
-    // hardware returns zeros without touching memory, so such a stage adds
-    // exact zeros to the accumulators. K is walked in groups of kSlots
-    // super-stages, the last group padded this way.
-    auto fetch = [&](char* slot_mem, int ks) {
-#pragma unroll
-      for (int sub = 0; sub < SPB; ++sub) {
-        const int g = ks * SPB + sub;
-        lds_char* dst = (lds_char*)slot_mem + sub * kStageBytes + wave_id * 1024;
-        const bool live = g < KT;
-        const uint32_t soff_w = live ? (uint32_t)g * wstride : 0x80000000u;
-#pragma unroll
-        for (int i = 0; i < kPasses; ++i) {
-          const __amdgpu_buffer_rsrc_t rs =
-              i >= kWPasses ? ra : ((kGateUp && 64 * i >= BN / 2) ? rw1 : rw0);
-          // token bands at or past the expert's m rows feed only outputs
-          // that are never stored: fetch them as zeros too
-          const bool band_live = i < kWPasses || m0 + 64 * (i - kWPasses) < m;
-          const uint32_t soff = i < kWPasses
-                                    ? soff_w
-                                    : (live && band_live ? (uint32_t)g * kTileBytes
-                                                         : 0x80000000u);
-          // (scalar copy: clang's host pass drops the launch stub when an
-          // array element is passed to this builtin directly)
-          const uint32_t vo = voff[i];
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(
-              rs, (void __attribute__((address_space(3)))*)(dst + i * 4096), 16, vo,
-              soff, 0, 0);
-        }
-      }
-    };
-
-    frags_t f0, f1;
-    // fragments of step s of the stage at `stage`
-    auto frags = [&](frags_t& f, const char* stage, int s) {
-#pragma unroll
-      for (int ib = 0; ib < WI; ++ib)
-        f.a[ib] = MmaOp<Elem>::load(stage, wrow_of(ib), s, half);
-#pragma unroll
-      for (int jb = 0; jb < WJ; ++jb)
-        f.b[jb] = MmaOp<Elem>::load(stage, trow + 32 * jb, s, half);
-    };
-
+    // Super-stage ks in slot CUR (NXT holds ks + 1). Its first MFMA step
+    // also fetches ring position ks + 3 into FSLOT (this tile's super-stage
+    // ks + 3 or, past the tile's end KS4, the next tile's); its last step
+    // follows the barrier, which waits for super-stage ks + 1.
 #define MOE_SUPER(CUR, NXT, FSLOT, KS_)                                          \
-    _Pragma("unroll") for (int sub = 0; sub < SPB; ++sub) {                     \
-      const char* cs = CUR + sub * kStageBytes;                                 \
-      const char* ns = sub + 1 < SPB ? CUR + (sub + 1) * kStageBytes : NXT;     \
-      _Pragma("unroll") for (int s = 0; s < kSteps; s += 2) {                   \
-        frags(f1, cs, s + 1);                                                   \
-        if (sub == 0 && s == 0) fetch(FSLOT, (KS_) + kSlots - 1);               \
-        mma_step<Elem, WI, WJ>(acc, f0);                                        \
-        if (sub == 0 && s == 0)                                                 \
-          pin_step<kMfmaPerStep, kReadsPerStep, kLoads>();                      \
-        else                                                                    \
-          pin_step<kMfmaPerStep, kReadsPerStep, 0>();                           \
-        if (s + 2 < kSteps) {                                                   \
-          frags(f0, cs, s + 2);                                                 \
-        } else {                                                                \
-          if (sub + 1 == SPB) wait_vmem_barrier<(kSlots - 2) * kLoads>();       \
-          frags(f0, ns, 0);                                                     \
+    {                                                                           \
+      const int vf = (KS_) + kSlots - 1;                                        \
+      const src_t& SF = vf < KS4 ? cur : nxt;                                   \
+      const int kf = vf < KS4 ? vf : vf - KS4;                                  \
+      _Pragma("unroll") for (int sub = 0; sub < SPB; ++sub) {                   \
+        const char* cs = CUR + sub * kStageBytes;                               \
+        const char* ns = sub + 1 < SPB ? CUR + (sub + 1) * kStageBytes : NXT;   \
+        _Pragma("unroll") for (int s = 0; s < kSteps; s += 2) {                 \
+          const bool last = s + 2 >= kSteps && sub + 1 == SPB;                  \
+          if (sub == 0 && s == 0)                                               \
+            mma_step<Elem, WI, WJ, kReadsPerStep + kLoads>(acc, f0, [&](int x) { \
+              if (x < kReadsPerStep) read_one(f1, cs, s + 1, x);                \
+              else fetch_one(FSLOT, kf, SF, x - kReadsPerStep);                 \
+            });                                                                 \
+          else                                                                  \
+            mma_step<Elem, WI, WJ, kReadsPerStep>(acc, f0, [&](int x) {         \
+              read_one(f1, cs, s + 1, x);                                       \
+            });                                                                 \
+          if (last) wait_vmem_barrier<kWait>();                                 \
+          const char* rs_ = s + 2 < kSteps ? cs : ns;                           \
+          const int rstep = s + 2 < kSteps ? s + 2 : 0;                         \
+          mma_step<Elem, WI, WJ, kReadsPerStep>(acc, f1, [&](int x) {           \
+            read_one(f0, rs_, rstep, x);                                        \
+          });                                                                   \
         }                                                                       \
-        mma_step<Elem, WI, WJ>(acc, f1);                                        \
-        pin_step<kMfmaPerStep, kReadsPerStep, 0>();                             \
       }                                                                         \
     }
 
-    // prologue: super-stages 0 .. kSlots-2 in flight; wait for the first
-    fetch(slot0, 0);
-    fetch(slot1, 1);
-    fetch(slot2, 2);
-    wait_vmem_barrier<(kSlots - 2) * kLoads>();
-    frags(f0, slot0, 0);
-    const int KS = (KT + SPB - 1) / SPB;
-    const int KS4 = (KS + kSlots - 1) / kSlots * kSlots;
     for (int ks = 0; ks < KS4; ks += kSlots) {
       MOE_SUPER(slot0, slot1, slot3, ks)
       MOE_SUPER(slot1, slot2, slot0, ks + 1)
@@ -386,53 +448,91 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
     }
 #undef MOE_SUPER
 
-    // epilogue: lane holds, for token j = l32 of each 32-token block, four
-    // runs of four consecutive output features
-    typedef Elem vec4_t __attribute__((ext_vector_type(4)));
+    // Epilogue: lane holds, for token c (row l32 of each 32-token block),
+    // four runs of four consecutive output features. Straight-line code:
+    // outputs outside the tile's m rows or N features get an out-of-range
+    // offset and the buffer unit drops the store, so there is no divergent
+    // branch and every group of four is finished before the next starts.
+    // (the accumulators are read by asm below: give the last MFMAs the wait
+    // states a VALU read of their results needs, which the compiler cannot
+    // see through the asm)
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    typedef uint32_t st_t __attribute__((ext_vector_type(kEs == 2 ? 2 : 4)));
+    auto store4 = [&](__amdgpu_buffer_rsrc_t rs, uint32_t off, vec4_t o) {
+      if constexpr (kEs == 2)
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(st_t, o), rs, off, 0, 0);
+      else
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(st_t, o), rs, off, 0, 0);
+    };
+    if (kGateUp) {
+      // h: expert e's tiled matrix, row c
+      const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(p.out + (int64_t)e * p.ce_pad * p.N), 0,
+          (int)((uint32_t)p.ce_pad * p.N * kEs), kRsrcWord3);
 #pragma unroll
-    for (int jb = 0; jb < WJ; ++jb) {
-      const int c = m0 + wm * (BM / 2) + jb * 32 + l32;
-      if (c >= m) continue;
-      if (kGateUp) {
-        // h: row c of expert e's tiled matrix
-        char* hmat = reinterpret_cast<char*>(p.out + (int64_t)e * p.ce_pad * p.N);
+      for (int jb = 0; jb < WJ; ++jb) {
+        const int c = m0 + wm * (BM / 2) + jb * 32 + l32;
 #pragma unroll
         for (int ib = 0; ib < WI / 2; ++ib) {
 #pragma unroll
           for (int g4 = 0; g4 < 4; ++g4) {
             const int feat = n0 + wn * (BN / 4) + ib * 32 + 8 * g4 + 4 * half;
-            if (feat >= p.N) continue;
             vec4_t o;
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-              o[q] = from_f32<Elem>(silu_mul(acc[ib][jb][4 * g4 + q],
-                                             acc[ib + WI / 2][jb][4 * g4 + q]));
-            *reinterpret_cast<vec4_t*>(
-                hmat + tiled_offset(c, (int64_t)feat * kEs, (int64_t)p.N * kEs)) = o;
+              o[q] = from_f32<Elem>(silu_mul(acc_read(acc[ib][jb][4 * g4 + q]),
+                                             acc_read(acc[ib + WI / 2][jb][4 * g4 + q])));
+            const uint32_t off =
+                c < m && feat < p.N
+                    ? (uint32_t)tiled_offset(c, (int64_t)feat * kEs, (int64_t)p.N * kEs)
+                    : kOutOfRange;
+            store4(rh, off, o);
+            __builtin_amdgcn_sched_barrier(0);
           }
         }
-      } else {
-        // z: the assignment's token slot
-        const int a = p.perm[p.offsets[e] + (int64_t)p.r * p.ce + c];
-        Elem* orow = p.out + (int64_t)a * p.N;
+      }
+    } else {
+      // z: rows offsets[e] + r*C' + c (c < m) of the expert-sorted order, i.e.
+      // the slot of assignment perm[offsets[e] + r*C' + c]
+      const int64_t i0 = (int64_t)__builtin_amdgcn_readlane(lane_off, e) +
+                         (int64_t)p.r * p.ce;
+      const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(p.out + i0 * p.N), 0, (int)((uint32_t)m * p.N * kEs), kRsrcWord3);
+#pragma unroll
+      for (int jb = 0; jb < WJ; ++jb) {
+        const int c = m0 + wm * (BM / 2) + jb * 32 + l32;
 #pragma unroll
         for (int ib = 0; ib < WI; ++ib) {
 #pragma unroll
           for (int g4 = 0; g4 < 4; ++g4) {
             const int feat = n0 + wn * (BN / 2) + ib * 32 + 8 * g4 + 4 * half;
-            if (feat >= p.N) continue;
             vec4_t o;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) o[q] = from_f32<Elem>(acc[ib][jb][4 * g4 + q]);
-            *reinterpret_cast<vec4_t*>(orow + feat) = o;
+            for (int q = 0; q < 4; ++q) o[q] = from_f32<Elem>(acc_read(acc[ib][jb][4 * g4 + q]));
+            // rows c >= m fall past the descriptor's range
+            const uint32_t off = feat < p.N ? ((uint32_t)c * p.N + feat) * kEs : kOutOfRange;
+            store4(rz, off, o);
+            __builtin_amdgcn_sched_barrier(0);
           }
         }
       }
     }
-    // the next tile's prologue refills the ring: every wavefront must be
-    // done with its last fragment reads
-    __syncthreads();
+    if (!has_next) break;
+    // the next tile's first fragments (its super-stage 0 is in slot0, ring
+    // position KS4): read here rather than in the last MFMA step, so that
+    // they do not occupy registers during the epilogue
+#pragma unroll
+    for (int r = 0; r < kReadsPerStep; ++r) read_one(f0, slot0, 0, r);
+    tile = tile_n;
+    e = e_n;
+    m = m_n;
+    n0 = n0_n;
+    m0 = m0_n;
+    cur = nxt;
   }
+  // the fetches that ran past the last tile read nothing, but they still
+  // write LDS: let them land before the workgroup ends
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 // Tiles one round needs under configuration Cfg (host side, from counts).

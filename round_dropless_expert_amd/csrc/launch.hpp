@@ -57,6 +57,6 @@ hipError_t launch_down(const Shape& s, int r, const void* h, const void* wd,
 hipError_t launch_pack_weights(const Shape& s, const void* src, void* dst,
                                int rows, int cols, int num_cus, hipStream_t st);
 hipError_t launch_combine(const Shape& s, const void* z, const float* weight,
-                          void* y, int num_cus, hipStream_t st);
+                          const int32_t* pos, void* y, int num_cus, hipStream_t st);
 
 }  // namespace moe

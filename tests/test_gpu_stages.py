@@ -88,7 +88,9 @@ def test_stages_match_oracle(w, layout):
         h = torch.cat([untile(views["h"][e], pad, w.d_ff, dt)[:int(m[e])]
                        for e in experts])
         assert_close(to_np(h), h_ref, w.dtype, f"h round {r}")
-        assert_close(to_np(views["z"][a_t]), o_ref, w.dtype, f"z round {r}")
+        # z is in expert-sorted order: assignment a's row is pos[a]
+        rows = torch.from_numpy(p.pos[np.array(assigns)]).to(case.dev).long()
+        assert_close(to_np(views["z"][rows]), o_ref, w.dtype, f"z round {r}")
 
     note(f"{w.name}/{layout}: moe_combine")
     y = case.new_y()
