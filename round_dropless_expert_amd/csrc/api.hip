@@ -170,6 +170,37 @@ moe_status_t num_cus(int* out) {
   return MOE_OK;
 }
 
+// Per thread and device: a small pinned host buffer that receives the
+// plan's counts and R, and an event recorded behind that copy. Pinned memory
+// lets the copy run asynchronously, so moe_forward can queue the first
+// dispatch before it waits for the plan. Created on first use and kept for
+// the life of the thread (a few hundred bytes of host memory per device).
+struct PlanReadback {
+  int32_t* host = nullptr;  // kMaxExperts + 1 int32, hipHostMalloc
+  hipEvent_t done = nullptr;
+};
+thread_local PlanReadback g_readback[64];
+
+moe_status_t plan_readback(PlanReadback** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= 64) return fail(MOE_ERR_UNSUPPORTED, "device id >= 64");
+  PlanReadback& r = g_readback[dev];
+  if (!r.host) {
+    void* h = nullptr;
+    e = hipHostMalloc(&h, (kMaxExperts + 1) * sizeof(int32_t), hipHostMallocDefault);
+    if (e != hipSuccess) return hip_fail(e, "hipHostMalloc of the plan readback");
+    r.host = static_cast<int32_t*>(h);
+  }
+  if (!r.done) {
+    e = hipEventCreateWithFlags(&r.done, hipEventDisableTiming);
+    if (e != hipSuccess) return hip_fail(e, "hipEventCreateWithFlags");
+  }
+  *out = &r;
+  return MOE_OK;
+}
+
 #define MOE_HIP(call, where)                         \
   do {                                               \
     hipError_t _e = (call);                          \
@@ -387,16 +418,28 @@ moe_status_t moe_forward(const moe_config_t* cfg, const float* logits,
   int cus = 0;
   if ((st = num_cus(&cus)) != MOE_OK) return st;
   if ((st = run_plan(b, logits, s)) != MOE_OK) return st;
-  // one read: the E per-expert counts followed by R
+  // One read of the E per-expert counts followed by R into pinned memory.
+  // Round 0 always exists and its dispatch needs nothing from the host, so
+  // it is queued before the wait: the GPU gathers while the host learns R.
+  PlanReadback* rb = nullptr;
+  if ((st = plan_readback(&rb)) != MOE_OK) return st;
+  MOE_HIP(hipMemcpyAsync(rb->host, b.pb.counts, (b.s.E + 1) * sizeof(int32_t),
+                         hipMemcpyDeviceToHost, s),
+          "read of counts and R");
+  MOE_HIP(hipEventRecord(rb->done, s), "hipEventRecord");
+  MOE_HIP(moe::launch_dispatch(b.s, 0, x, b.pb, b.ws + b.L.xr, cus, s),
+          "dispatch launch");
+  MOE_HIP(hipEventSynchronize(rb->done), "wait for the plan");
   int32_t counts_r[kMaxExperts + 1];
-  if ((st = read_plan(b, counts_r, s)) != MOE_OK) return st;
+  std::memcpy(counts_r, rb->host, (b.s.E + 1) * sizeof(int32_t));
   const int32_t R = counts_r[b.s.E];
   const int64_t max_rounds = (b.s.T + b.s.ce - 1) / b.s.ce;
   if (R < 1 || R > max_rounds)
     return fail(MOE_ERR_HIP, "device plan reported an impossible round count");
   for (int r = 0; r < R; ++r) {
-    MOE_HIP(moe::launch_dispatch(b.s, r, x, b.pb, b.ws + b.L.xr, cus, s),
-            "dispatch launch");
+    if (r > 0)
+      MOE_HIP(moe::launch_dispatch(b.s, r, x, b.pb, b.ws + b.L.xr, cus, s),
+              "dispatch launch");
     if ((st = run_ffn(b, r, w_gate, w_up, w_down, counts_r, cus, s)) != MOE_OK)
       return st;
   }

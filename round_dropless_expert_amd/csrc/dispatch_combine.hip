@@ -11,80 +11,76 @@
 
 namespace moe {
 
-// Copy of one row into a tiled matrix by one wavefront: 16-byte chunk q of
-// the source row goes to tiled_offset(row, 16 q) of the destination; four
-// loads in flight per lane before the stores.
-__device__ __forceinline__ void wave_copy_row_tiled(const u32x4* __restrict__ src,
-                                                    char* __restrict__ dst_mat,
-                                                    int64_t row, int64_t row_bytes,
-                                                    int lane) {
-  const int n16 = (int)(row_bytes / 16);
-  const int64_t band = (row >> 6) * (row_bytes >> 6) * kTileBytes;
-  const int r = (int)(row & 63);
-  const int sw = (r >> 2) & 3;
-  auto dst = [&](int q) -> u32x4* {
-    return reinterpret_cast<u32x4*>(dst_mat + band + (int64_t)(q >> 2) * kTileBytes +
-                                    r * kTileRowBytes + (((q & 3) ^ sw) << 4));
-  };
-  int v = lane;
-  for (; v + 3 * kWave < n16; v += 4 * kWave) {
-    const u32x4 a0 = src[v], a1 = src[v + kWave], a2 = src[v + 2 * kWave],
-                a3 = src[v + 3 * kWave];
-    *dst(v) = a0;
-    *dst(v + kWave) = a1;
-    *dst(v + 2 * kWave) = a2;
-    *dst(v + 3 * kWave) = a3;
-  }
-  for (; v < n16; v += kWave) *dst(v) = src[v];
-}
-
-// Round r: the round's rows are numbered expert by expert; row i belongs to
-// expert e with pre[e] <= i < pre[e+1] (pre = prefix of m(r, e)) and is slot
-// c = i - pre[e]. Its source token is perm[offsets[e] + r*C' + c] / k and its
-// destination is row c of expert e's tiled round-buffer matrix.
+// Round r, token-major: one wavefront per token reads the token's row of x
+// once and writes it to every slot the token holds in round r. The token's
+// k assignments a = t*k + j carry their expert idx[a], round round_of[a]
+// and round-buffer row row_of[a] = e*C' + c; assignment j goes to slot c of
+// expert e's tiled round-buffer matrix if round_of[a] == r. Each lane moves
+// 16-byte chunks q = lane + 64 i of the row: chunk q lands in 4 KiB block
+// q / 4 of the row's 64-row band, at row c % 64 and chunk position
+// (q % 4) ^ ((c / 4) % 4) (the tiled layout).
+template <int kChunks>  // 16-byte chunks per lane held in registers
 __global__ __launch_bounds__(256) void dispatch_kernel(
-    const char* __restrict__ x, int64_t row_bytes, int E, int k, int ce,
-    int ce_pad, int r,
-    const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ perm, char* __restrict__ xr) {
-  __shared__ int pre[kWave + 1];
-  if (threadIdx.x < kWave) {
-    const int e = threadIdx.x;
-    const int m = e < E ? rows_in_round(counts[e], r, ce) : 0;
-    const int incl = wave_inclusive_scan(m);
-    pre[e + 1] = incl;
-    if (e == 0) pre[0] = 0;
-  }
-  __syncthreads();
-  const int rows = pre[E];
+    const char* __restrict__ x, int64_t T, int row_bytes, int k, int ce,
+    int ce_pad, int r, const int32_t* __restrict__ idx,
+    const int32_t* __restrict__ round_of, const int32_t* __restrict__ row_of,
+    char* __restrict__ xr) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kWave;
   const int64_t nwaves = (int64_t)gridDim.x * blockDim.x / kWave;
-  for (int64_t i = wave; i < rows; i += nwaves) {
-    const int e = segment_of(pre, E + 1, (int)i);
-    const int c = (int)i - pre[e];
-    const int a = perm[offsets[e] + (int64_t)r * ce + c];
-    const int64_t t = a / k;
-    wave_copy_row_tiled(reinterpret_cast<const u32x4*>(x + t * row_bytes),
-                        xr + (int64_t)e * ce_pad * row_bytes, c, row_bytes, lane);
+  const int n16 = row_bytes / 16;
+  const int64_t mat_bytes = (int64_t)ce_pad * row_bytes;
+  const int64_t band_bytes = (int64_t)row_bytes * kTileRows;
+  for (int64_t t = wave; t < T; t += nwaves) {
+    int e = 0, row = 0;
+    bool mine = false;
+    if (lane < k) {
+      const int64_t a = t * k + lane;
+      mine = round_of[a] == r;
+      e = idx[a];
+      row = row_of[a];
+    }
+    uint64_t todo = __builtin_amdgcn_ballot_w64(mine);
+    if (todo == 0) continue;
+    const u32x4* src = reinterpret_cast<const u32x4*>(x + t * (int64_t)row_bytes);
+    for (int base = 0; base < n16; base += kChunks * kWave) {
+      u32x4 v[kChunks];
+#pragma unroll
+      for (int i = 0; i < kChunks; ++i) {
+        const int q = base + lane + i * kWave;
+        if (q < n16) v[i] = src[q];
+      }
+      for (uint64_t m = todo; m; m &= m - 1) {
+        const int j = __builtin_ctzll(m);
+        const int ej = __shfl(e, j, kWave);
+        const int c = __shfl(row, j, kWave) - ej * ce;
+        char* dst = xr + ej * mat_bytes + (int64_t)(c >> 6) * band_bytes +
+                    (c & 63) * kTileRowBytes;
+        const int sw = (c >> 2) & 3;
+#pragma unroll
+        for (int i = 0; i < kChunks; ++i) {
+          const int q = base + lane + i * kWave;
+          if (q < n16)
+            *reinterpret_cast<u32x4*>(dst + (int64_t)(q >> 2) * kTileBytes +
+                                      (((q & 3) ^ sw) << 4)) = v[i];
+        }
+      }
+    }
   }
 }
 
 hipError_t launch_dispatch(const Shape& s, int r, const void* x,
                            const PlanBuffers& b, void* xr, int num_cus,
                            hipStream_t st) {
-  const int64_t row_bytes = (int64_t)s.d * (s.bf16 ? 2 : 4);
-  // at most min(T*k, E*C') rows in a round; 4 rows per workgroup per pass
-  int64_t max_rows = s.T * s.k;
-  if ((int64_t)s.E * s.ce < max_rows) max_rows = (int64_t)s.E * s.ce;
-  int64_t blocks = (max_rows + 3) / 4;
+  const int row_bytes = s.d * (s.bf16 ? 2 : 4);
+  int64_t blocks = (s.T + 3) / 4;  // 4 tokens per workgroup per pass
   const int64_t cap = (int64_t)num_cus * 8;
   if (blocks > cap) blocks = cap;
   if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL(dispatch_kernel, dim3((unsigned)blocks), dim3(256), 0, st,
-                     static_cast<const char*>(x), row_bytes, s.E, s.k, s.ce,
-                     s.ce_pad(), r,
-                     b.counts, b.offsets, b.perm, static_cast<char*>(xr));
+  hipLaunchKernelGGL(dispatch_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, st,
+                     static_cast<const char*>(x), s.T, row_bytes, s.k, s.ce,
+                     s.ce_pad(), r, b.idx, b.round_of, b.row_of,
+                     static_cast<char*>(xr));
   return hipGetLastError();
 }
 
@@ -124,12 +120,15 @@ hipError_t launch_pack_weights(const Shape& s, const void* src, void* dst,
 // over ascending j starting from zero, rounded once to the element type. z
 // holds the expert outputs in expert-sorted order (row i = assignment
 // perm[i]), so pos[a] is assignment a's row: the collect is this gather.
-// One wavefront per token streams its k rows (16-byte vectors) and writes d.
-template <typename Elem>
+// One wavefront per token; each lane takes kVecs 16-byte vectors of the
+// row and loads them from all k rows before it adds (k * kVecs loads in
+// flight).
+template <typename Elem, int kVecs>
 __global__ __launch_bounds__(256) void combine_kernel(
     const Elem* __restrict__ z, const float* __restrict__ weight,
     const int32_t* __restrict__ pos, int64_t T, int k, int d, Elem* __restrict__ y) {
   constexpr int kVec = 16 / sizeof(Elem);  // elements per 16-byte vector
+  constexpr int kMaxK = 8;                 // rows loaded ahead per vector
   typedef Elem vec_t __attribute__((ext_vector_type(kVec)));
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kWave;
@@ -139,21 +138,48 @@ __global__ __launch_bounds__(256) void combine_kernel(
     const float wl = lane < k ? weight[t * k + lane] : 0.f;
     const int rl = lane < k ? pos[t * k + lane] : 0;
     vec_t* yt = reinterpret_cast<vec_t*>(y + t * (int64_t)d);
-    for (int v = lane; v < nv; v += kWave) {
-      float acc[kVec];
+    for (int base = 0; base < nv; base += kVecs * kWave) {
+      float acc[kVecs][kVec];
 #pragma unroll
-      for (int q = 0; q < kVec; ++q) acc[q] = 0.f;
-      for (int j = 0; j < k; ++j) {
-        const float wj = __shfl(wl, j, kWave);
-        const int64_t row = __shfl(rl, j, kWave);
-        const vec_t zv = reinterpret_cast<const vec_t*>(z + row * d)[v];
+      for (int i = 0; i < kVecs; ++i)
 #pragma unroll
-        for (int q = 0; q < kVec; ++q) acc[q] = fmaf(wj, to_f32(zv[q]), acc[q]);
+        for (int q = 0; q < kVec; ++q) acc[i][q] = 0.f;
+      for (int j0 = 0; j0 < k; j0 += kMaxK) {
+        vec_t zv[kMaxK][kVecs];
+#pragma unroll
+        for (int jj = 0; jj < kMaxK; ++jj) {
+          if (j0 + jj < k) {
+            const int64_t row = __shfl(rl, j0 + jj, kWave);
+            const vec_t* zr = reinterpret_cast<const vec_t*>(z + row * d);
+#pragma unroll
+            for (int i = 0; i < kVecs; ++i) {
+              const int v = base + lane + i * kWave;
+              if (v < nv) zv[jj][i] = zr[v];
+            }
+          }
+        }
+#pragma unroll
+        for (int jj = 0; jj < kMaxK; ++jj) {
+          if (j0 + jj < k) {
+            const float wj = __shfl(wl, j0 + jj, kWave);
+#pragma unroll
+            for (int i = 0; i < kVecs; ++i)
+#pragma unroll
+              for (int q = 0; q < kVec; ++q)
+                acc[i][q] = fmaf(wj, to_f32(zv[jj][i][q]), acc[i][q]);
+          }
+        }
       }
-      vec_t out;
 #pragma unroll
-      for (int q = 0; q < kVec; ++q) out[q] = from_f32<Elem>(acc[q]);
-      yt[v] = out;
+      for (int i = 0; i < kVecs; ++i) {
+        const int v = base + lane + i * kWave;
+        if (v < nv) {
+          vec_t out;
+#pragma unroll
+          for (int q = 0; q < kVec; ++q) out[q] = from_f32<Elem>(acc[i][q]);
+          yt[v] = out;
+        }
+      }
     }
   }
 }
@@ -164,11 +190,11 @@ hipError_t launch_combine(const Shape& s, const void* z, const float* weight,
   const int64_t cap = (int64_t)num_cus * 8;
   if (blocks > cap) blocks = cap;
   if (s.bf16)
-    hipLaunchKernelGGL(combine_kernel<bf16>, dim3((unsigned)blocks), dim3(256),
+    hipLaunchKernelGGL((combine_kernel<bf16, 2>), dim3((unsigned)blocks), dim3(256),
                        0, st, static_cast<const bf16*>(z), weight, pos, s.T, s.k,
                        s.d, static_cast<bf16*>(y));
   else
-    hipLaunchKernelGGL(combine_kernel<float>, dim3((unsigned)blocks), dim3(256),
+    hipLaunchKernelGGL((combine_kernel<float, 2>), dim3((unsigned)blocks), dim3(256),
                        0, st, static_cast<const float*>(z), weight, pos, s.T, s.k,
                        s.d, static_cast<float*>(y));
   return hipGetLastError();
