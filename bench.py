@@ -41,6 +41,10 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate wall time of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run torch's device-to-device copy of a known "
+                         "size (256 MiB, 5 times): the reference kernel for "
+                         "scaling the FETCH_SIZE / WRITE_SIZE counters")
     ap.add_argument("--weights", choices=("tiled", "row_major"), default="tiled",
                     help="expert weight layout the layer reads (tiled = packed "
                          "once by moe_pack_weights before timing)")
@@ -79,8 +83,44 @@ def cpu_baseline(w, inp, seconds: float) -> dict:
                       f"in {t_plan:.2f} s"}
 
 
+COPY_BYTES = 256 << 20  # bytes read and bytes written per calibration copy
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic_gate_up_balanced_bf16.md")
+GEMM_SOURCE = os.path.join(ROOT, "round_dropless_expert_amd", "csrc", "grouped_gemm.hip")
+
+
+def copy_calibration():
+    """torch's copy kernel over COPY_BYTES, five times (for a --pmc run)."""
+    import torch
+    src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": COPY_BYTES, "launches": 5}), flush=True)
+
+
+def measured_traffic():
+    """HBM bytes per launch of the round-0 gate/up kernel from the committed
+    counter summary, or None if the kernel source changed since then."""
+    import hashlib
+    import re
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    m = re.search(r"^source_sha256: ([0-9a-f]{64})$", text, re.M)
+    t = re.search(r"^traffic_bytes_per_launch: ([0-9.e+]+)$", text, re.M)
+    if not m or not t:
+        return None
+    if hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest() != m.group(1):
+        return None
+    return float(t.group(1))
+
+
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(f"bench.py: this layer runs on one GPU; --gpus {args.gpus} is not "
               "supported (multi-GPU expert parallelism is not built)",
@@ -213,7 +253,7 @@ def main():
     achieved = flops_g0 / sec["gate_up[0]"] / 1e12
     roofline = {"bound": "mfma", "kernel": "grouped gate/up GEMM + SwiGLU, round 0",
                 "achieved": achieved, "peak": peak_tf, "unit": "TFLOP/s",
-                "frac": achieved / peak_tf, "traffic": None,
+                "frac": achieved / peak_tf, "traffic": measured_traffic(),
                 "flops_per_launch": flops_g0,
                 "avg_launch_us": sec["gate_up[0]"] * 1e6}
     kernels = per_launch
