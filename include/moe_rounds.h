@@ -226,8 +226,8 @@ moe_status_t moe_combine(const moe_config_t *cfg, const void *ws,
  * Returns after enqueueing the combine (the plan's wait is the only host
  * synchronisation; round 0's dispatch is queued before it). For that read
  * the library keeps, per calling thread and device, a pinned host buffer of
- * 65 int32 and an event, created on first use. The result does not depend
- * on C. */
+ * 65 int32, a side stream of default priority that does the copy, and two
+ * events, created on first use. The result does not depend on C. */
 moe_status_t moe_forward(const moe_config_t *cfg, const float *logits,
                          const void *x, const void *w_gate, const void *w_up,
                          const void *w_down, void *y, void *ws,

@@ -96,7 +96,7 @@ void layout_of(const moe_config_t* c, moe_workspace_layout_t* L) {
   L->pos = take(TK * 4);
   L->round_of = take(TK * 4);
   L->row_of = take(TK * 4);
-  L->scratch = take((size_t)moe::plan_blocks(s) * E * 4);
+  L->scratch = take((size_t)moe::plan_scratch_ints(s) * 4);
   L->xr = take(E * ce_pad * (size_t)c->d_model * es);
   L->h = take(E * ce_pad * (size_t)c->d_ff * es);
   L->z = take(TK * (size_t)c->d_model * es);
@@ -171,12 +171,16 @@ moe_status_t num_cus(int* out) {
 }
 
 // Per thread and device: a small pinned host buffer that receives the
-// plan's counts and R, and an event recorded behind that copy. Pinned memory
-// lets the copy run asynchronously, so moe_forward can queue the first
-// dispatch before it waits for the plan. Created on first use and kept for
-// the life of the thread (a few hundred bytes of host memory per device).
+// plan's counts and R, a side stream (default priority) that copies them,
+// and two events: "planned" on the caller's stream behind the plan, "done"
+// on the side stream behind the copy. moe_forward queues round 0's dispatch
+// on the caller's stream while the side stream copies, so neither the copy
+// nor the host's wake-up delays the GPU. Created on first use and kept for
+// the life of the thread.
 struct PlanReadback {
   int32_t* host = nullptr;  // kMaxExperts + 1 int32, hipHostMalloc
+  hipStream_t side = nullptr;
+  hipEvent_t planned = nullptr;
   hipEvent_t done = nullptr;
 };
 thread_local PlanReadback g_readback[64];
@@ -192,6 +196,14 @@ moe_status_t plan_readback(PlanReadback** out) {
     e = hipHostMalloc(&h, (kMaxExperts + 1) * sizeof(int32_t), hipHostMallocDefault);
     if (e != hipSuccess) return hip_fail(e, "hipHostMalloc of the plan readback");
     r.host = static_cast<int32_t*>(h);
+  }
+  if (!r.side) {
+    e = hipStreamCreateWithFlags(&r.side, hipStreamNonBlocking);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamCreateWithFlags");
+  }
+  if (!r.planned) {
+    e = hipEventCreateWithFlags(&r.planned, hipEventDisableTiming);
+    if (e != hipSuccess) return hip_fail(e, "hipEventCreateWithFlags");
   }
   if (!r.done) {
     e = hipEventCreateWithFlags(&r.done, hipEventDisableTiming);
@@ -418,15 +430,18 @@ moe_status_t moe_forward(const moe_config_t* cfg, const float* logits,
   int cus = 0;
   if ((st = num_cus(&cus)) != MOE_OK) return st;
   if ((st = run_plan(b, logits, s)) != MOE_OK) return st;
-  // One read of the E per-expert counts followed by R into pinned memory.
-  // Round 0 always exists and its dispatch needs nothing from the host, so
-  // it is queued before the wait: the GPU gathers while the host learns R.
+  // One read of the E per-expert counts followed by R into pinned memory,
+  // on the side stream behind the plan. Round 0 always exists and its
+  // dispatch needs nothing from the host, so it is queued on the caller's
+  // stream before the wait: the GPU gathers while the counts travel.
   PlanReadback* rb = nullptr;
   if ((st = plan_readback(&rb)) != MOE_OK) return st;
+  MOE_HIP(hipEventRecord(rb->planned, s), "hipEventRecord");
+  MOE_HIP(hipStreamWaitEvent(rb->side, rb->planned, 0), "hipStreamWaitEvent");
   MOE_HIP(hipMemcpyAsync(rb->host, b.pb.counts, (b.s.E + 1) * sizeof(int32_t),
-                         hipMemcpyDeviceToHost, s),
+                         hipMemcpyDeviceToHost, rb->side),
           "read of counts and R");
-  MOE_HIP(hipEventRecord(rb->done, s), "hipEventRecord");
+  MOE_HIP(hipEventRecord(rb->done, rb->side), "hipEventRecord");
   MOE_HIP(moe::launch_dispatch(b.s, 0, x, b.pb, b.ws + b.L.xr, cus, s),
           "dispatch launch");
   MOE_HIP(hipEventSynchronize(rb->done), "wait for the plan");

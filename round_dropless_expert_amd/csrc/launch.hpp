@@ -17,11 +17,21 @@ struct Shape {
   int ce_pad() const { return (ce + 63) / 64 * 64; }  // round-buffer rows per expert
 };
 
-// Plan-internal chunk of assignments handled by one workgroup.
-constexpr int kPlanChunk = 1024;
+// Plan-internal granularity: the router counts an expert histogram for
+// every 8 consecutive tokens (one workgroup each); a reduction sums them per
+// chunk of 256 tokens, and the ranking kernel takes one chunk per workgroup.
+constexpr int kHistTokens = 8;
+constexpr int kRankTokens = 256;
 
-inline int64_t plan_blocks(const Shape& s) {
-  return (s.T * s.k + kPlanChunk - 1) / kPlanChunk;
+inline int64_t hist_rows(const Shape& s) {
+  return (s.T + kHistTokens - 1) / kHistTokens;
+}
+inline int64_t rank_blocks(const Shape& s) {
+  return (s.T + kRankTokens - 1) / kRankTokens;
+}
+// plan scratch: hist [hist_rows][E], then chunk sums [rank_blocks][E]
+inline int64_t plan_scratch_ints(const Shape& s) {
+  return (hist_rows(s) + rank_blocks(s)) * s.E;
 }
 
 struct PlanBuffers {
@@ -34,7 +44,7 @@ struct PlanBuffers {
   int32_t* pos;
   int32_t* round_of;
   int32_t* row_of;
-  int32_t* scratch;  // [plan_blocks][E]
+  int32_t* scratch;  // hist [hist_rows][E], chunk sums [rank_blocks][E]
 };
 
 hipError_t launch_route(const Shape& s, const float* logits, PlanBuffers b,

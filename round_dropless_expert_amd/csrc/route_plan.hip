@@ -17,24 +17,32 @@
 namespace moe {
 
 // ---------------------------------------------------------------- router
-// One wavefront serves 64/EP rows; lane e of a row segment holds logit e.
-// The k picks are k butterfly arg-max reductions over the segment, keyed by
-// (logit descending, expert ascending), a strict total order since experts
-// are distinct, so every lane of the segment agrees on the winner.
+// Workgroup b routes the tokens [kHistTokens*b, kHistTokens*(b+1)): one
+// wavefront serves 64/EP rows at a time, lane e of a row segment holding
+// logit e. The k picks are k butterfly arg-max reductions over the segment,
+// keyed by (logit descending, expert ascending), a strict total order since
+// experts are distinct, so every lane of the segment agrees on the winner.
+// Their expert histogram (plan phase 1) is counted on the way in LDS: a
+// count does not depend on the order the increments land in.
 template <int EP>
 __global__ __launch_bounds__(256) void topk_softmax_kernel(
     const float* __restrict__ logits, int64_t T, int E, int k,
-    int32_t* __restrict__ idx, float* __restrict__ weight) {
+    int32_t* __restrict__ idx, float* __restrict__ weight,
+    int32_t* __restrict__ hist) {
   constexpr int kRowsPerWave = kWave / EP;
+  constexpr int kRowsPerPass = 4 * kRowsPerWave;
+  __shared__ int h[kWave];
   const int lane = threadIdx.x & (kWave - 1);
+  const int wv = threadIdx.x / kWave;
   const int seg = lane / EP;
   const int e = lane % EP;
-  const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kWave;
-  const int64_t nwaves = (int64_t)gridDim.x * blockDim.x / kWave;
-  for (int64_t row0 = wave * kRowsPerWave; row0 < T;
-       row0 += nwaves * kRowsPerWave) {
+  if (threadIdx.x < kWave) h[threadIdx.x] = 0;
+  __syncthreads();
+  const int64_t first = (int64_t)blockIdx.x * kHistTokens;
+  const int64_t last = first + kHistTokens < T ? first + kHistTokens : T;
+  for (int64_t row0 = first + wv * kRowsPerWave; row0 < last; row0 += kRowsPerPass) {
     const int64_t row = row0 + seg;
-    const bool live = row < T && e < E;
+    const bool live = row < last && e < E;
     float v = live ? logits[row * E + e] : -INFINITY;
     int key = live ? e : kWave + e;  // padding lanes lose every tie
     int sel_e = 0;
@@ -66,21 +74,22 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(
     float sum = ex;
 #pragma unroll
     for (int off = EP / 2; off > 0; off >>= 1) sum += __shfl_xor(sum, off, EP);
-    if (row < T && e < k) {
+    if (row < last && e < k) {
       idx[row * k + e] = sel_e;
       weight[row * k + e] = ex / sum;
+      atomicAdd(&h[sel_e], 1);
     }
   }
+  __syncthreads();
+  if (threadIdx.x < E) hist[(int64_t)blockIdx.x * E + threadIdx.x] = h[threadIdx.x];
 }
 
 template <int EP>
 static hipError_t route_ep(const Shape& s, const float* logits, PlanBuffers b,
                            hipStream_t st) {
-  constexpr int rows_per_block = 4 * (kWave / EP);
-  int64_t blocks = (s.T + rows_per_block - 1) / rows_per_block;
-  if (blocks > 8192) blocks = 8192;
-  hipLaunchKernelGGL(topk_softmax_kernel<EP>, dim3((unsigned)blocks), dim3(256),
-                     0, st, logits, s.T, s.E, s.k, b.idx, b.weight);
+  hipLaunchKernelGGL(topk_softmax_kernel<EP>, dim3((unsigned)hist_rows(s)),
+                     dim3(256), 0, st, logits, s.T, s.E, s.k, b.idx, b.weight,
+                     b.scratch);
   return hipGetLastError();
 }
 
@@ -96,50 +105,90 @@ hipError_t launch_route(const Shape& s, const float* logits, PlanBuffers b,
 }
 
 // ------------------------------------------------------------------ plan
-// Phase 1: per-chunk histogram of experts (LDS counters; a count does not
-// depend on the order the increments land in).
-__global__ __launch_bounds__(256) void plan_hist_kernel(
-    const int32_t* __restrict__ idx, int64_t TK, int E,
-    int32_t* __restrict__ hist) {
-  __shared__ int h[kWave];
-  if (threadIdx.x < kWave) h[threadIdx.x] = 0;
+// Phase 1 is the router's histogram hist[q][e] of the tokens [8 q, 8 q + 8);
+// this kernel sums it per chunk of 256 tokens: sums[b][e] = sum of rows
+// 32 b .. 32 b + 31 (wavefront w adds rows w, w + 4, ...; the order of the
+// terms of a sum does not matter).
+__global__ __launch_bounds__(256) void plan_chunk_sum_kernel(
+    const int32_t* __restrict__ hist, int64_t nrows, int E,
+    int32_t* __restrict__ sums) {
+  constexpr int kRows = kRankTokens / kHistTokens;
+  __shared__ int part[4][kWave];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = threadIdx.x / kWave;
+  const int64_t q0 = (int64_t)blockIdx.x * kRows;
+  int n = 0;
+  if (lane < E)
+#pragma unroll
+    for (int i = wv; i < kRows; i += 4)
+      if (q0 + i < nrows) n += hist[(q0 + i) * E + lane];
+  part[wv][lane] = n;
   __syncthreads();
-  const int64_t base = (int64_t)blockIdx.x * kPlanChunk;
-  const int64_t end = base + kPlanChunk < TK ? base + kPlanChunk : TK;
-  for (int64_t a = base + threadIdx.x; a < end; a += blockDim.x)
-    atomicAdd(&h[idx[a]], 1);
-  __syncthreads();
-  if (threadIdx.x < E) hist[(int64_t)blockIdx.x * E + threadIdx.x] = h[threadIdx.x];
+  if (threadIdx.x < E)
+    sums[(int64_t)blockIdx.x * E + threadIdx.x] =
+        part[0][threadIdx.x] + part[1][threadIdx.x] + part[2][threadIdx.x] +
+        part[3][threadIdx.x];
 }
 
-// Phase 2 (one wavefront): counts, exclusive offsets, R, and for every
-// chunk b the first position of expert e's entries from that chunk:
-// offsets[e] + sum_{b' < b} hist[b'][e] (written over hist).
-__global__ __launch_bounds__(64) void plan_scan_kernel(
-    int32_t* __restrict__ hist, int64_t nblocks, int E, int ce,
+// Phase 2, the prefix sums over chunks: counts n_e = sum_b sums[b][e],
+// exclusive offsets over e, R = max_e ceil(n_e / C'), and for every chunk b
+// the first position of expert e's entries from it, offsets[e] +
+// sum_{b' < b} sums[b'][e]. With up to kSelfScanMaxChunks chunks every
+// ranking workgroup sums the columns it needs itself (kSelfScan);
+// otherwise one workgroup does it here and leaves the chunk starts in place
+// of the sums.
+__global__ __launch_bounds__(1024) void plan_scan_kernel(
+    int32_t* __restrict__ hist, int64_t nrows, int E, int ce,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ n_rounds) {
-  const int e = threadIdx.x;
+  constexpr int kWaves = 16;
+  __shared__ int part[kWaves][kWave];
+  __shared__ int base[kWave];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = threadIdx.x / kWave;
+  const bool on = lane < E;
+  // column sums: wavefront w takes chunks w, w + 16, ...
   int n = 0;
-  if (e < E)
-    for (int64_t b = 0; b < nblocks; ++b) n += hist[b * E + e];
-  const int incl = wave_inclusive_scan(n);
-  const int excl = incl - n;
-  if (e < E) {
-    counts[e] = n;
-    offsets[e] = excl;
-  }
-  if (e == E - 1) offsets[E] = incl;
-  const int r = (e < E) ? (int)(((int64_t)n + ce - 1) / ce) : 0;
-  const int rmax = wave_max(r);
-  if (e == 0) *n_rounds = rmax;
-  if (e < E) {
-    int run = excl;
-    for (int64_t b = 0; b < nblocks; ++b) {
-      const int c = hist[b * E + e];
-      hist[b * E + e] = run;
-      run += c;
+  if (on)
+    for (int64_t b = wv; b < nrows; b += kWaves) n += hist[b * E + lane];
+  part[wv][lane] = n;
+  __syncthreads();
+  if (wv == 0) {
+    int tot = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) tot += part[w][lane];
+    if (!on) tot = 0;
+    const int incl = wave_inclusive_scan(tot);
+    const int excl = incl - tot;
+    if (on) {
+      counts[lane] = tot;
+      offsets[lane] = excl;
     }
+    if (lane == E - 1) offsets[E] = incl;
+    const int r = on ? (int)(((int64_t)tot + ce - 1) / ce) : 0;
+    const int rmax = wave_max(r);
+    if (lane == 0) *n_rounds = rmax;
+    base[lane] = excl;
+  }
+  __syncthreads();
+  // chunk starts, 16 consecutive chunks at a time: wavefront w takes chunk
+  // 16 t + w, and the starts follow from an exclusive scan over the group
+  for (int64_t b0 = 0; b0 < nrows; b0 += kWaves) {
+    const int64_t b = b0 + wv;
+    const int c = on && b < nrows ? hist[b * E + lane] : 0;
+    part[wv][lane] = c;
+    __syncthreads();
+    int pre = base[lane];
+    for (int w = 0; w < wv; ++w) pre += part[w][lane];
+    if (on && b < nrows) hist[b * E + lane] = pre;
+    __syncthreads();
+    if (wv == 0) {
+      int add = 0;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) add += part[w][lane];
+      base[lane] += add;
+    }
+    __syncthreads();
   }
 }
 
@@ -148,21 +197,78 @@ __global__ __launch_bounds__(64) void plan_scan_kernel(
 // expert are found with six ballots (one per bit of the expert index), the
 // rank is the number of such lanes below, and per-wave totals are combined
 // in wave order through LDS. Then the position, its inverse and the round
-// split are written.
+// split are written. Workgroup b ranks the assignments of tokens
+// [256 b, 256 b + 256). With kSelfScan the workgroup first derives its
+// starts (and, in workgroup 0, counts, offsets and R) from the chunk sums.
+template <bool kSelfScan>
 __global__ __launch_bounds__(256) void plan_rank_kernel(
-    const int32_t* __restrict__ idx, int64_t TK, int E, int ce,
-    const int32_t* __restrict__ chunk_base, const int32_t* __restrict__ offsets,
-    int32_t* __restrict__ perm, int32_t* __restrict__ pos,
-    int32_t* __restrict__ round_of, int32_t* __restrict__ row_of) {
+    const int32_t* __restrict__ idx, int64_t TK, int E, int k, int ce,
+    int64_t nrows, const int32_t* __restrict__ hist,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets_out,
+    int32_t* __restrict__ n_rounds, int32_t* __restrict__ perm,
+    int32_t* __restrict__ pos, int32_t* __restrict__ round_of,
+    int32_t* __restrict__ row_of) {
   __shared__ int running[kWave];
+  __shared__ int offs[kWave];
   __shared__ int cnt[4][kWave];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wv = tid / kWave;
-  if (tid < kWave)
-    running[tid] = (tid < E) ? chunk_base[(int64_t)blockIdx.x * E + tid] : 0;
-  const int64_t start = (int64_t)blockIdx.x * kPlanChunk;
-  const int64_t end = start + kPlanChunk < TK ? start + kPlanChunk : TK;
+  const int64_t blk = blockIdx.x;
+  if (kSelfScan) {
+    // column totals and the prefix over the chunks before this one:
+    // wavefront w takes chunks w, w + 4, ... (a sum does not depend on the
+    // order of its terms)
+    const int64_t row0 = blk;
+    int tot = 0, pre = 0;
+    if (lane < E) {
+      int64_t q = wv;
+      for (; q + 12 < nrows; q += 16) {  // four loads in flight
+        const int v0 = hist[q * E + lane], v1 = hist[(q + 4) * E + lane];
+        const int v2 = hist[(q + 8) * E + lane], v3 = hist[(q + 12) * E + lane];
+        tot += v0 + v1 + v2 + v3;
+        pre += (q < row0 ? v0 : 0) + (q + 4 < row0 ? v1 : 0) +
+               (q + 8 < row0 ? v2 : 0) + (q + 12 < row0 ? v3 : 0);
+      }
+      for (; q < nrows; q += 4) {
+        const int v = hist[q * E + lane];
+        tot += v;
+        if (q < row0) pre += v;
+      }
+    }
+    cnt[wv][lane] = tot;
+    running[lane] = 0;
+    __syncthreads();
+    if (wv == 0) {
+      int n = cnt[0][lane] + cnt[1][lane] + cnt[2][lane] + cnt[3][lane];
+      if (lane >= E) n = 0;
+      const int incl = wave_inclusive_scan(n);
+      offs[lane] = incl - n;
+      if (blk == 0) {
+        if (lane < E) {
+          counts[lane] = n;
+          offsets_out[lane] = incl - n;
+        }
+        if (lane == E - 1) offsets_out[E] = incl;
+        const int r = lane < E ? (int)(((int64_t)n + ce - 1) / ce) : 0;
+        const int rmax = wave_max(r);
+        if (lane == 0) *n_rounds = rmax;
+      }
+    }
+    __syncthreads();
+    cnt[wv][lane] = pre;
+    __syncthreads();
+    if (tid < kWave)
+      running[tid] = offs[tid] + cnt[0][tid] + cnt[1][tid] + cnt[2][tid] + cnt[3][tid];
+  } else {
+    if (tid < kWave) {
+      running[tid] = tid < E ? hist[blk * E + tid] : 0;
+      offs[tid] = tid < E ? offsets_out[tid] : 0;
+    }
+  }
+  const int64_t start = blk * kRankTokens * k;
+  const int64_t end = start + (int64_t)kRankTokens * k < TK
+                          ? start + (int64_t)kRankTokens * k : TK;
   const uint64_t below = lane == 0 ? 0ull : (~0ull >> (kWave - lane));
   __syncthreads();
   for (int64_t s = start; s < end; s += blockDim.x) {
@@ -193,27 +299,39 @@ __global__ __launch_bounds__(256) void plan_rank_kernel(
     if (live) {
       perm[p] = (int32_t)a;
       pos[a] = p;
-      const int i = p - offsets[e];
+      const int i = p - offs[e];
       round_of[a] = i / ce;
       row_of[a] = e * ce + i % ce;
     }
   }
 }
 
+// Chunks up to which every ranking workgroup sums the columns itself
+// (chunks * E reads per workgroup, from L2).
+constexpr int64_t kSelfScanMaxChunks = 1024;
+
 hipError_t launch_plan(const Shape& s, PlanBuffers b, hipStream_t st) {
   const int64_t TK = s.T * s.k;
-  const int64_t nb = plan_blocks(s);
-  hipLaunchKernelGGL(plan_hist_kernel, dim3((unsigned)nb), dim3(256), 0, st,
-                     b.idx, TK, s.E, b.scratch);
+  const int64_t nrows = hist_rows(s);
+  const int64_t nb = rank_blocks(s);
+  int32_t* sums = b.scratch + nrows * s.E;
+  hipLaunchKernelGGL(plan_chunk_sum_kernel, dim3((unsigned)nb), dim3(256), 0, st,
+                     b.scratch, nrows, s.E, sums);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(plan_scan_kernel, dim3(1), dim3(64), 0, st, b.scratch, nb,
-                     s.E, s.ce, b.counts, b.offsets, b.n_rounds);
+  if (nb <= kSelfScanMaxChunks) {
+    hipLaunchKernelGGL(plan_rank_kernel<true>, dim3((unsigned)nb), dim3(256), 0,
+                       st, b.idx, TK, s.E, s.k, s.ce, nb, sums, b.counts,
+                       b.offsets, b.n_rounds, b.perm, b.pos, b.round_of, b.row_of);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(plan_scan_kernel, dim3(1), dim3(1024), 0, st, sums, nb, s.E,
+                     s.ce, b.counts, b.offsets, b.n_rounds);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(plan_rank_kernel, dim3((unsigned)nb), dim3(256), 0, st,
-                     b.idx, TK, s.E, s.ce, b.scratch, b.offsets, b.perm, b.pos,
-                     b.round_of, b.row_of);
+  hipLaunchKernelGGL(plan_rank_kernel<false>, dim3((unsigned)nb), dim3(256), 0, st,
+                     b.idx, TK, s.E, s.k, s.ce, nb, sums, b.counts, b.offsets,
+                     b.n_rounds, b.perm, b.pos, b.round_of, b.row_of);
   return hipGetLastError();
 }
 

@@ -55,7 +55,7 @@ def expected_total(T, E, k, d, f, C, es):
     ce = min(C, T)
     pad = ceil_div(ce, 64) * 64  # round-buffer rows per expert, tiled
     TK = T * k
-    nb = ceil_div(TK, 1024)
+    nb = ceil_div(T, 8) + ceil_div(T, 256)  # plan histogram rows, chunk sums
     # counts and R share one block: [E counts][R]
     parts = [TK * 4, TK * 4, (E + 1) * 4, (E + 1) * 4, TK * 4, TK * 4, TK * 4,
              TK * 4, nb * E * 4, E * pad * d * es, E * pad * f * es, TK * d * es]

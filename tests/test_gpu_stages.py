@@ -122,3 +122,24 @@ def test_pack_weights_is_the_tiled_permutation(dtype):
             sb = t[e].contiguous().view(torch.uint8).reshape(-1)
             ob = o[e].contiguous().view(torch.uint8).reshape(-1)
             assert torch.equal(ob[idx], sb)
+
+
+def test_plan_with_more_chunks_than_the_self_scan_limit():
+    """Above 1024 plan chunks (256 tokens each) the prefix sums run in a
+    separate scan kernel: the plan stays bit-exact."""
+    w = W("many_chunks", T=1100 * 256 + 77, d_model=64, d_ff=64, E=16, k=3,
+          C=5000, dtype="f32", skew=("zipf", 0.7))
+    from round_dropless_expert_amd import synth
+    note(f"{w.name}: logits")
+    logits = synth.generate_activations(w).logits
+    idx, _ = oracle.route(logits, w.k)
+    p = oracle.plan(idx, w.E, w.C)
+    cfg = B.config(w.T, w.E, w.k, w.d_model, w.d_ff, w.C, w.dtype)
+    ws = torch.empty(B.workspace_size(cfg), dtype=torch.uint8, device="cuda:0")
+    ws.fill_(0xFF)
+    note(f"{w.name}: moe_plan T={w.T}")
+    R, counts = B.moe_plan(cfg, torch.from_numpy(logits).cuda(), ws,
+                           return_counts=True)
+    assert R == p.R
+    np.testing.assert_array_equal(counts, p.counts)
+    assert_plan_equal(B.workspace_views(cfg, ws), p, idx)
