@@ -24,9 +24,9 @@
 // or 16 fp32); SPB stages form a slot of a five-slot LDS ring filled by
 // LDS-direct buffer loads, with up to four slots in flight and one barrier
 // per slot. Fragment reads run one MFMA step ahead of the MFMAs that use
-// them. Two tile shapes: 256 weight rows x 256 tokens, and 128 x 64 (two
-// stages per slot) for rounds with too few rows to give every CU a large
-// tile, which mostly stream weights and need many workgroups.
+// them. Three tile shapes, chosen per round: 256 weight rows x 256 tokens,
+// 256 x 128, and 128 x 64 (two stages per slot) for rounds of a few rows
+// per expert, which mostly stream weights and need many workgroups.
 //
 // Determinism: every output element is one fixed sequence of MFMA steps
 // over K in ascending order, whatever the round, the slot or the tile it
@@ -195,13 +195,23 @@ constexpr int kSlots = 4;  // the stage loop below names four slots
 // Tile configurations (WI / WJ: 32-row MFMA blocks per wavefront along
 // weight rows / tokens; the 2 x 2 wavefronts cover 64*WI weight rows and
 // 64*WJ tokens; SPB: 64-byte K stages per slot and barrier).
-struct TileBig {    // rounds that give every CU at least one such tile
+// The host picks, per round, the shape with the least estimated time
+// (waves of tiles over the CUs x tile area / relative MFMA efficiency).
+struct TileBig {     // 256 weight rows x 256 tokens: 128 FLOP per byte
   static constexpr int WI = 4, WJ = 4, SPB = 1;
+  static constexpr float kEff = 1.0f;
 };
-struct TileSmall {  // rounds too small to give every CU a large tile: such
-                    // a round mostly streams expert weights; spread them
-                    // over more workgroups and keep more bytes in flight
+struct TileMedium {  // 256 x 128: rounds of one or a few experts with
+                     // thousands of rows, which 256 x 256 tiles leave
+                     // mostly idle
+  static constexpr int WI = 4, WJ = 2, SPB = 1;
+  static constexpr float kEff = 0.85f;
+};
+struct TileSmall {   // 128 x 64, two K stages per slot: rounds of a few
+                     // rows per expert, which mostly stream weights and
+                     // need many workgroups
   static constexpr int WI = 2, WJ = 1, SPB = 2;
+  static constexpr float kEff = 0.45f;
 };
 
 // Offset that puts a buffer load out of range: the load returns zeros and
@@ -551,6 +561,14 @@ static int64_t round_tiles(const Shape& s, const int32_t* counts_host, int r,
   return tiles;
 }
 
+// Estimated time of a round in a tile shape: waves of tiles over the CUs
+// times the tile's area over its relative MFMA efficiency.
+template <typename Cfg>
+static float est_cost(int64_t tiles, int num_cus) {
+  const int64_t waves = (tiles + num_cus - 1) / num_cus;
+  return (float)waves * (64.0f * Cfg::WI) * (64.0f * Cfg::WJ) / Cfg::kEff;
+}
+
 // Workgroups for a round: one per CU, or fewer when the round has fewer
 // tiles; a multiple of 8 (the XCD-contiguous walk assumes it).
 static int grid_for(int64_t tiles, int num_cus) {
@@ -569,8 +587,8 @@ static hipError_t launch_gemm_cfg(const GemmParams<Elem>& p, int grid,
 }
 
 // counts_host (nullable): per-expert counts on the host. With them the
-// round's tile shape and grid are chosen from its largest expert; without
-// them the large tile and one workgroup per CU are used. Both shapes run the
+// round's tile shape and grid are chosen from its tile counts; without them
+// the large tile and one workgroup per CU are used. Every shape runs the
 // same MFMA sequence over K for every output, so results are identical.
 template <typename Elem, bool kGateUp>
 static hipError_t launch_gemm(const Shape& s, const GemmParams<Elem>& p,
@@ -585,13 +603,17 @@ static hipError_t launch_gemm(const Shape& s, const GemmParams<Elem>& p,
       mmax = m > mmax ? m : mmax;
     }
     if (mmax == 0) return hipSuccess;  // nothing in this round
-    // the large tile when it gives every CU at least one tile, else the
-    // small one (rounds of a few rows per expert stream weights)
     const int64_t tb = round_tiles<TileBig>(s, counts_host, p.r, N, kGateUp);
-    if (tb >= num_cus)
+    const int64_t tm = round_tiles<TileMedium>(s, counts_host, p.r, N, kGateUp);
+    const int64_t ts = round_tiles<TileSmall>(s, counts_host, p.r, N, kGateUp);
+    const float cb = est_cost<TileBig>(tb, num_cus);
+    const float cm = est_cost<TileMedium>(tm, num_cus);
+    const float cs = est_cost<TileSmall>(ts, num_cus);
+    if (cb <= cm && cb <= cs)
       return launch_gemm_cfg<Elem, TileBig, kGateUp>(p, grid_for(tb, num_cus), st);
-    const int64_t t = round_tiles<TileSmall>(s, counts_host, p.r, N, kGateUp);
-    return launch_gemm_cfg<Elem, TileSmall, kGateUp>(p, grid_for(t, num_cus), st);
+    if (cm <= cs)
+      return launch_gemm_cfg<Elem, TileMedium, kGateUp>(p, grid_for(tm, num_cus), st);
+    return launch_gemm_cfg<Elem, TileSmall, kGateUp>(p, grid_for(ts, num_cus), st);
   }
   return launch_gemm_cfg<Elem, TileBig, kGateUp>(p, grid_for(num_cus, num_cus), st);
 }
