@@ -248,6 +248,22 @@ def main():
     gemm_util = 6.0 * TK * df / t_gemm / 1e12 / peak_tf
     t_disp = stage_sum("dispatch")
 
+    # practical HBM ceiling for the copy-like kernels: a device-to-device
+    # copy of 256 MiB (read + write bytes over its time)
+    csrc = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
+    cdst = torch.empty_like(csrc)
+    for _ in range(2):
+        cdst.copy_(csrc)
+    c0 = torch.cuda.Event(enable_timing=True)
+    c1 = torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(10):
+        cdst.copy_(csrc)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 2 * COPY_BYTES * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del csrc, cdst
+
     # dominant kernel: the round-0 grouped gate/up launch (the largest round)
     flops_g0 = 4.0 * float(A[0]) * df
     achieved = flops_g0 / sec["gate_up[0]"] / 1e12
@@ -273,6 +289,7 @@ def main():
         "grouped_gemm_mfma_util_pct": 100.0 * gemm_util,
         "dispatch_GBps": sum(disp_bytes) / t_disp / 1e9,
         "combine_GBps": kernels["combine"]["GB/s"],
+        "device_copy_GBps": copy_gbps,
         "workspace_bytes": ws_bytes, "peak_allocated_bytes": peak_bytes,
         "roofline": roofline, "kernels": kernels,
     }

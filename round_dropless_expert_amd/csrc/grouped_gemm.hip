@@ -246,9 +246,19 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
   constexpr int kSteps = MmaOp<Elem>::kSteps;
   constexpr int kMfmaPerStep = WI * WJ;
   constexpr int kReadsPerStep = WI + WJ;
-  // A barrier waits for the fetch of super-stage ks + 1; two more fetches
-  // are in flight behind it (see the stage loop)
-  constexpr int kWait = (kSlots - 2) * kLoads;
+  // The fetch of a super-stage is spread over all its MFMA steps (at most
+  // kLoadsPerStep loads after the fragment reads of each step), so that the
+  // address unit is never handed more loads than it retires while the
+  // MFMAs run: a burst of LDS-direct loads stalls the issuing wavefront,
+  // and with it the matrix core.
+  constexpr int kStepsPerSuper = SPB * kSteps;
+  constexpr int kLoadsPerStep = (kLoads + kStepsPerSuper - 1) / kStepsPerSuper;
+  constexpr int kLoadsLast =  // loads in the last step (after the barrier)
+      kLoads - (kStepsPerSuper - 1) * kLoadsPerStep > 0
+          ? kLoads - (kStepsPerSuper - 1) * kLoadsPerStep : 0;
+  // A barrier waits for the fetch of super-stage ks + 1; behind it in issue
+  // order: the fetch of ks + 2 and the part of ks + 3 issued before it
+  constexpr int kWait = kLoads + (kLoads - kLoadsLast);
   typedef TileSrc<kWPasses, kTPasses> src_t;
   static_assert(kSteps % 2 == 0, "fragment sets alternate by step");
   static_assert(WI % 2 == 0, "gate/up pairs and the 2 x 2 wavefront grid");
@@ -417,10 +427,10 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[ib][jb][v] = 0.f;
 
-    // Super-stage ks in slot CUR (NXT holds ks + 1). Its first MFMA step
-    // also fetches ring position ks + 3 into FSLOT (this tile's super-stage
-    // ks + 3 or, past the tile's end KS4, the next tile's); its last step
-    // follows the barrier, which waits for super-stage ks + 1.
+    // Super-stage ks in slot CUR (NXT holds ks + 1). Its MFMA steps also
+    // fetch ring position ks + 3 into FSLOT (this tile's super-stage ks + 3
+    // or, past the tile's end KS4, the next tile's), kLoadsPerStep loads a
+    // step; the last step follows the barrier, which waits for ks + 1.
 #define MOE_SUPER(CUR, NXT, FSLOT, KS_)                                          \
     {                                                                           \
       const int vf = (KS_) + kSlots - 1;                                        \
@@ -430,21 +440,26 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
         const char* cs = CUR + sub * kStageBytes;                               \
         const char* ns = sub + 1 < SPB ? CUR + (sub + 1) * kStageBytes : NXT;   \
         _Pragma("unroll") for (int s = 0; s < kSteps; s += 2) {                 \
+          const int ja = sub * kSteps + s; /* step index in the super-stage */  \
           const bool last = s + 2 >= kSteps && sub + 1 == SPB;                  \
-          if (sub == 0 && s == 0)                                               \
-            mma_step<Elem, WI, WJ, kReadsPerStep + kLoads>(acc, f0, [&](int x) { \
-              if (x < kReadsPerStep) read_one(f1, cs, s + 1, x);                \
-              else fetch_one(FSLOT, kf, SF, x - kReadsPerStep);                 \
-            });                                                                 \
-          else                                                                  \
-            mma_step<Elem, WI, WJ, kReadsPerStep>(acc, f0, [&](int x) {         \
+          mma_step<Elem, WI, WJ, kReadsPerStep + kLoadsPerStep>(acc, f0, [&](int x) { \
+            if (x < kReadsPerStep) {                                            \
               read_one(f1, cs, s + 1, x);                                       \
-            });                                                                 \
+            } else {                                                            \
+              const int li = ja * kLoadsPerStep + x - kReadsPerStep;            \
+              if (li < kLoads) fetch_one(FSLOT, kf, SF, li);                    \
+            }                                                                   \
+          });                                                                   \
           if (last) wait_vmem_barrier<kWait>();                                 \
           const char* rs_ = s + 2 < kSteps ? cs : ns;                           \
           const int rstep = s + 2 < kSteps ? s + 2 : 0;                         \
-          mma_step<Elem, WI, WJ, kReadsPerStep>(acc, f1, [&](int x) {           \
-            read_one(f0, rs_, rstep, x);                                        \
+          mma_step<Elem, WI, WJ, kReadsPerStep + kLoadsPerStep>(acc, f1, [&](int x) { \
+            if (x < kReadsPerStep) {                                            \
+              read_one(f0, rs_, rstep, x);                                      \
+            } else {                                                            \
+              const int li = (ja + 1) * kLoadsPerStep + x - kReadsPerStep;      \
+              if (li < kLoads) fetch_one(FSLOT, kf, SF, li);                    \
+            }                                                                   \
           });                                                                   \
         }                                                                       \
       }                                                                         \
