@@ -48,8 +48,16 @@ def lib():
             _i64, _i32, _i32, _i32, _i32, _i64, _i32p, _f64p, _i32p, _i32p,
             _i32p, _i32p, _i32p, _i32, _f32p, _f32p, _f32p, _f32p, _f64p,
             _f64p]
+        L.oracle_plan_groups.argtypes = [
+            _i64, _i32, _i32, _i64, _i32, _i32p, _i32p, _i32p, _i32p, _i32p,
+            _i32p, _i32p, _i32p, _i32p, _i64]
+        L.oracle_round_executor_groups.argtypes = [
+            _i64, _i32, _i32, _i32, _i32, _i64, _i32, _i32p, _f64p, _i32p,
+            _i32p, _i32p, _i32p, _i32p, _i32, _i32p, _f32p, _f32p, _f32p,
+            _f32p, _f64p, _f64p]
         for name in ("oracle_route", "oracle_plan", "oracle_assignment_outputs",
                      "oracle_forward_tokens", "oracle_round_executor",
+                     "oracle_plan_groups", "oracle_round_executor_groups",
                      "oracle_max_threads"):
             getattr(L, name).restype = ctypes.c_int
         L.oracle_set_threads.argtypes = [ctypes.c_int]
@@ -95,11 +103,21 @@ class Plan:
     row_of: np.ndarray    # int32 [T*k]
     R: int
     C_eff: int
+    G: int = 1                 # experts per capacity group
+    alloc: np.ndarray = None   # int32 [R, E] rows per round (groups only)
 
     def rows_in_round(self, r: int) -> np.ndarray:
         """m_{r,e} for every expert (int64 [E])."""
+        if self.alloc is not None:
+            return self.alloc[r].astype(np.int64)
         m = self.counts.astype(np.int64) - r * self.C_eff
         return np.clip(m, 0, self.C_eff)
+
+    def first_in_round(self, r: int) -> np.ndarray:
+        """Index, in each expert's stable list, of its first round-r entry."""
+        if self.alloc is not None:
+            return self.alloc[:r].astype(np.int64).sum(axis=0)
+        return np.minimum(self.counts.astype(np.int64), r * self.C_eff)
 
 
 def plan(idx: np.ndarray, E: int, C: int) -> Plan:
@@ -117,6 +135,48 @@ def plan(idx: np.ndarray, E: int, C: int) -> Plan:
                              perm, pos, round_of, row_of, R), "oracle_plan")
     return Plan(counts, offsets, perm, pos, round_of, row_of, int(R[0]),
                 min(int(C), int(T)))
+
+
+def plan_groups(idx: np.ndarray, E: int, C: int, G: int) -> Plan:
+    """Plan with the capacity of each group of G experts shared among them
+    (oracle_plan_groups); G = 1 is the strict per-expert capacity."""
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    T, k = idx.shape
+    TK = T * k
+    Ce = min(int(C), int(T))
+    counts = np.empty(E, dtype=np.int32)
+    offsets = np.empty(E + 1, dtype=np.int32)
+    perm = np.empty(TK, dtype=np.int32)
+    pos = np.empty(TK, dtype=np.int32)
+    round_of = np.empty(TK, dtype=np.int32)
+    row_of = np.empty(TK, dtype=np.int32)
+    R = np.zeros(1, dtype=np.int32)
+    rows = -(-T // Ce)  # at most ceil(T / C') rounds
+    alloc = np.zeros(rows * E, dtype=np.int32)
+    _check(lib().oracle_plan_groups(T, E, k, C, G, idx.reshape(-1), counts,
+                                    offsets, perm, pos, round_of, row_of, R,
+                                    alloc, rows), "oracle_plan_groups")
+    R = int(R[0])
+    return Plan(counts, offsets, perm, pos, round_of, row_of, R, Ce, int(G),
+                alloc.reshape(rows, E)[:R].copy())
+
+
+def round_executor_groups(idx, w, p: Plan, C: int, x, Wg, Wu, Wd):
+    """round_executor for a plan_groups plan."""
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    w = np.ascontiguousarray(w, dtype=np.float64)
+    T, k = idx.shape
+    E, f, d = Wg.shape
+    Z = np.empty((T * k, d), dtype=np.float64)
+    y = np.empty((T, d), dtype=np.float64)
+    alloc = np.ascontiguousarray(p.alloc, dtype=np.int32).reshape(-1)
+    if alloc.size == 0:
+        alloc = np.zeros(1, dtype=np.int32)
+    _check(lib().oracle_round_executor_groups(
+        T, E, k, d, f, C, p.G, idx.reshape(-1), w.reshape(-1), p.counts,
+        p.offsets, p.perm, p.round_of, p.row_of, p.R, alloc, _f32(x),
+        _f32(Wg), _f32(Wu), _f32(Wd), Z, y), "oracle_round_executor_groups")
+    return Z, y
 
 
 def assignment_outputs(a_list, idx, x, Wg, Wu, Wd, want_h=False):

@@ -32,11 +32,16 @@
  *   - round-buffer row of the c-th slot of expert e is e*C + c, where a
  *     capacity above T acts as T (an expert never holds more than T tokens);
  *   - the expert FFN is SwiGLU with no biases: h = silu(x.Wg^T) * (x.Wu^T),
- *     o = h.Wd^T; the layer output is y_t = sum_j w_tj * o_tj, j ascending.
+ *     o = h.Wd^T; the layer output is y_t = sum_j w_tj * o_tj, j ascending;
+ *   - with capacity shared in groups of G experts (oracle_plan_groups), an
+ *     expert first fills its own C slots, then the group's unused slots go
+ *     to its overloaded experts in ascending expert order.
  *
  * Parity pins for every function live in the test suite (brute-force top-k,
- * library sort/histogram, closed forms, a library SwiGLU for E = k = 1, and
- * bit-identity of the round executor with the per-token loop for every C).
+ * library sort/histogram, closed forms, a library SwiGLU for E = k = 1,
+ * bit-identity of the round executors with the per-token loop for every C
+ * and group size, a Python simulation of the group fill rule, and
+ * hand-worked fixtures).
  */
 #include <math.h>
 #include <stdint.h>
@@ -174,6 +179,106 @@ int oracle_plan(int64_t T, int32_t E, int32_t k, int64_t C, const int32_t *idx,
  * SwiGLU with no biases]. xr is the token row in fp64; Wg_e, Wu_e are
  * [f][d], Wd_e is [d][f]. h (length f) receives silu(g)*u, o (length d)
  * receives h.Wd^T. Sums run over ascending index, no intermediate rounding. */
+/*
+ * Plan with capacity shared inside expert groups ("Frontier Pre-training at
+ * Microsoft AI (MAI-Base-2)", section "Key claims", and "Microsoft AI's
+ * MAI-Base-2 trained on 16K GPUs with Muon", section "Expert groups keep
+ * memory fixed when tokens pile up": an overloaded expert first uses the
+ * unused capacity of the other experts of its group, and only what still
+ * does not fit waits for another round).
+ *
+ * Reading taken here (the pages give no procedure): experts e are grouped
+ * by e / G (G consecutive experts, G divides E). In every round a group
+ * owns G * C' slots. Each expert first takes min(remaining, C') of its
+ * remaining assignments (its own capacity); the slots its group leaves
+ * unused then go to the group's overloaded experts in ascending expert
+ * order, each taking as many of its remaining assignments as the spare
+ * slots allow. An expert's assignments keep their stable order and each
+ * round takes the next m(r, e) of them. Inside a round the group's slots
+ * are filled expert by expert: row_of = g * G * C' + (rows of the group's
+ * lower experts in that round) + c. G = 1 is the strict per-expert
+ * capacity of oracle_plan.
+ *
+ * alloc receives m(r, e) for r < *R (alloc_rows * E int32 provided).
+ */
+int oracle_plan_groups(int64_t T, int32_t E, int32_t k, int64_t C, int32_t G,
+                       const int32_t *idx, int32_t *counts, int32_t *offsets,
+                       int32_t *perm, int32_t *pos, int32_t *round_of,
+                       int32_t *row_of, int32_t *R, int32_t *alloc,
+                       int64_t alloc_rows) {
+  if (T < 1 || E < 1 || k < 1 || k > E || C < 1 || G < 1 || E % G != 0 ||
+      !idx || !counts || !offsets || !perm || !pos || !round_of || !row_of ||
+      !R || !alloc || alloc_rows < 1)
+    return OR_ERR_ARG;
+  const int64_t TK = T * k;
+  const int64_t Ce = min_i64(C, T);
+  for (int32_t e = 0; e < E; ++e) counts[e] = 0;
+  for (int64_t a = 0; a < TK; ++a) {
+    if (idx[a] < 0 || idx[a] >= E) return OR_ERR_ARG;
+    counts[idx[a]] += 1;
+  }
+  offsets[0] = 0;
+  for (int32_t e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
+  int32_t *cursor = (int32_t *)malloc(sizeof(int32_t) * (size_t)E);
+  int64_t *rem = (int64_t *)malloc(sizeof(int64_t) * (size_t)E);
+  if (!cursor || !rem) {
+    free(cursor);
+    free(rem);
+    return OR_ERR_NOMEM;
+  }
+  for (int32_t e = 0; e < E; ++e) cursor[e] = offsets[e];
+  for (int64_t a = 0; a < TK; ++a) perm[cursor[idx[a]]++] = (int32_t)a;
+  for (int64_t p = 0; p < TK; ++p) pos[perm[p]] = (int32_t)p;
+
+  /* rounds: allocation table m(r, e) */
+  for (int32_t e = 0; e < E; ++e) rem[e] = counts[e];
+  int64_t r = 0;
+  int err = OR_OK;
+  for (;;) {
+    int64_t left = 0;
+    for (int32_t e = 0; e < E; ++e) left += rem[e];
+    if (left == 0) break;
+    if (r >= alloc_rows) {
+      err = OR_ERR_ARG;
+      break;
+    }
+    int32_t *m = alloc + r * E;
+    for (int32_t g0 = 0; g0 < E; g0 += G) {
+      int64_t spare = (int64_t)G * Ce;
+      for (int32_t e = g0; e < g0 + G; ++e) {
+        m[e] = (int32_t)min_i64(rem[e], Ce);
+        spare -= m[e];
+      }
+      for (int32_t e = g0; e < g0 + G; ++e) {
+        const int64_t more = min_i64(rem[e] - m[e], spare);
+        m[e] += (int32_t)more;
+        spare -= more;
+      }
+      for (int32_t e = g0; e < g0 + G; ++e) rem[e] -= m[e];
+    }
+    ++r;
+  }
+  *R = (int32_t)r;
+  /* each assignment's round and row */
+  for (int64_t a = 0; a < TK && err == OR_OK; ++a) {
+    const int32_t e = idx[a];
+    const int32_t g0 = e - e % G;
+    int64_t i = (int64_t)pos[a] - offsets[e]; /* index in expert e's list */
+    int64_t rr = 0;
+    while (i >= alloc[rr * E + e]) {
+      i -= alloc[rr * E + e];
+      ++rr;
+    }
+    int64_t before = 0; /* rows of the group's lower experts in round rr */
+    for (int32_t e2 = g0; e2 < e; ++e2) before += alloc[rr * E + e2];
+    round_of[a] = (int32_t)rr;
+    row_of[a] = (int32_t)((int64_t)g0 * Ce + before + i);
+  }
+  free(cursor);
+  free(rem);
+  return err;
+}
+
 static void expert_ffn_row(int32_t d, int32_t f, const double *xr,
                            const float *Wg_e, const float *Wu_e,
                            const float *Wd_e, double *h, double *o) {
@@ -380,5 +485,118 @@ int oracle_round_executor(int64_t T, int32_t E, int32_t k, int32_t d,
   free(filled);
   free(Xr);
   free(slot_a);
+  return err;
+}
+
+/*
+ * Round executor for a plan with shared group capacity (oracle_plan_groups):
+ * round by round, the assignments the allocation table gives every expert
+ * are gathered into the E * C' slot buffer at their rows, each slot's
+ * expert output goes to Z[a] (NaN until written), then the per-token
+ * combine. Every row is checked against the table: expert e's m(r, e)
+ * slots of round r are the next m(r, e) entries of its list, at rows
+ * g * G * C' + (rows of lower experts of its group) + c.
+ */
+int oracle_round_executor_groups(int64_t T, int32_t E, int32_t k, int32_t d,
+                                 int32_t f, int64_t C, int32_t G,
+                                 const int32_t *idx, const double *w,
+                                 const int32_t *counts, const int32_t *offsets,
+                                 const int32_t *perm, const int32_t *round_of,
+                                 const int32_t *row_of, int32_t R,
+                                 const int32_t *alloc, const float *x,
+                                 const float *Wg, const float *Wu,
+                                 const float *Wd, double *Z, double *y) {
+  if (T < 1 || E < 1 || k < 1 || d < 1 || f < 1 || C < 1 || G < 1 ||
+      E % G != 0 || R < 0 || !idx || !w || !counts || !offsets || !perm ||
+      !round_of || !row_of || !alloc || !x || !Wg || !Wu || !Wd || !Z || !y)
+    return OR_ERR_ARG;
+  const int64_t TK = T * k;
+  const int64_t Ce = min_i64(C, T);
+  const double nan = NAN;
+  for (int64_t i = 0; i < TK * d; ++i) Z[i] = nan;
+  unsigned char *filled = (unsigned char *)calloc((size_t)TK, 1);
+  double *Xr = (double *)malloc(sizeof(double) * (size_t)(E * Ce * d));
+  int64_t *slot_a = (int64_t *)malloc(sizeof(int64_t) * (size_t)(E * Ce));
+  int64_t *used = (int64_t *)calloc((size_t)E, sizeof(int64_t));
+  if (!filled || !Xr || !slot_a || !used) {
+    free(filled);
+    free(Xr);
+    free(slot_a);
+    free(used);
+    return OR_ERR_NOMEM;
+  }
+  int err = OR_OK;
+  for (int32_t r = 0; r < R && err == OR_OK; ++r) {
+    for (int64_t s = 0; s < E * Ce; ++s) slot_a[s] = -1;
+    for (int32_t g0 = 0; g0 < E && err == OR_OK; g0 += G) {
+      int64_t base = (int64_t)g0 * Ce;
+      for (int32_t e = g0; e < g0 + G && err == OR_OK; ++e) {
+        const int64_t m = alloc[(int64_t)r * E + e];
+        if (m < 0 || base + m > (int64_t)(g0 + G) * Ce ||
+            used[e] + m > counts[e]) {
+          err = OR_ERR_PLAN;
+          break;
+        }
+        for (int64_t c = 0; c < m; ++c) {
+          const int64_t a = perm[offsets[e] + used[e] + c];
+          const int64_t row = base + c;
+          if (idx[a] != e || round_of[a] != r || row_of[a] != row ||
+              slot_a[row] != -1) {
+            err = OR_ERR_PLAN;
+            break;
+          }
+          const int64_t t = a / k;
+          for (int32_t i = 0; i < d; ++i)
+            Xr[row * d + i] = (double)x[t * d + i];
+          slot_a[row] = a;
+        }
+        used[e] += m;
+        base += m;
+      }
+    }
+    if (err != OR_OK) break;
+#pragma omp parallel
+    {
+      double *h = (double *)malloc(sizeof(double) * (size_t)f);
+      if (!h) {
+#pragma omp atomic write
+        err = OR_ERR_NOMEM;
+      } else {
+#pragma omp for schedule(static)
+        for (int64_t row = 0; row < E * Ce; ++row) {
+          const int64_t a = slot_a[row];
+          if (a < 0) continue;
+          const int64_t e = idx[a];
+          const int64_t wo = e * f * d;
+          expert_ffn_row(d, f, Xr + row * d, Wg + wo, Wu + wo, Wd + wo, h,
+                         Z + a * d);
+        }
+      }
+      free(h);
+    }
+    for (int64_t row = 0; row < E * Ce && err == OR_OK; ++row) {
+      const int64_t a = slot_a[row];
+      if (a < 0) continue;
+      if (filled[a]) err = OR_ERR_PLAN;
+      filled[a] = 1;
+    }
+  }
+  for (int64_t a = 0; a < TK && err == OR_OK; ++a)
+    if (!filled[a]) err = OR_ERR_PLAN;
+  if (err == OR_OK) {
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+      double *yt = y + t * d;
+      for (int32_t m = 0; m < d; ++m) yt[m] = 0.0;
+      for (int32_t j = 0; j < k; ++j) {
+        const double *zr = Z + (t * k + j) * d;
+        for (int32_t m = 0; m < d; ++m) yt[m] += w[t * k + j] * zr[m];
+      }
+    }
+  }
+  free(filled);
+  free(Xr);
+  free(slot_a);
+  free(used);
   return err;
 }
