@@ -14,11 +14,20 @@
  * layer needs depends only on the shapes and C, never on how skewed the
  * routing is.
  *
+ * Capacity groups (same sources: an overloaded expert first uses capacity
+ * that other experts of its group leave unused, and only what still does
+ * not fit waits for another round): experts e with the same e / G form a
+ * group that owns G*C' slots per round. In every round each expert first
+ * takes up to C' of its remaining assignments; the group's unused slots
+ * then go to its overloaded experts in ascending expert order. G = 1 is a
+ * strict per-expert capacity.
+ *
  * Notation: T tokens, E experts, top-k routing, d = d_model, f = d_ff,
  * assignment id a = t*k + j (j-th choice of token t), n_e = assignments of
- * expert e, C' = min(C, T) (a capacity above T acts as T),
- * m(r,e) = clamp(n_e - r*C', 0, C') rows of expert e in round r,
- * R = max_e ceil(n_e / C') rounds.
+ * expert e, C' = min(C, T) (a capacity above T acts as T), G experts per
+ * capacity group, m(r,e) = rows of expert e in round r (for G = 1,
+ * clamp(n_e - r*C', 0, C')), R rounds (for G = 1, max_e ceil(n_e / C');
+ * in general max over groups of ceil(sum of the group's n_e / (G*C'))).
  *
  * Layouts (row-major, contiguous, no padding):
  *   logits  float32 [T][E]            (always fp32)
@@ -45,8 +54,10 @@
  * unspecified (but in-bounds) routing.
  *
  * Limits of this version: 1 <= E <= 64, 1 <= k <= E, T >= 1, T*k < 2^31,
- * C >= 1, d and f positive multiples of 64, and E*C', C'*max(d, f) and d*f
- * each below 2^31 (MOE_ERR_UNSUPPORTED otherwise).
+ * C >= 1, G divides E, d and f positive multiples of 64, and the
+ * round-buffer rows (E*P for G = 1, E*(P+64) otherwise, P = C' rounded up
+ * to 64), G*(P+64)*max(d, f) elements' bytes and d*f elements' bytes each
+ * below 2^31 (MOE_ERR_UNSUPPORTED otherwise).
  */
 #ifndef MOE_ROUNDS_H
 #define MOE_ROUNDS_H
@@ -86,6 +97,7 @@ typedef struct {
   int64_t C;             /* per-expert capacity of one round */
   int32_t dtype;         /* moe_dtype_t of x, weights and y */
   int32_t weight_layout; /* moe_weight_layout_t of the expert weights */
+  int32_t group;         /* G: experts per capacity group (0 means 1) */
 } moe_config_t;
 
 /* Tiled layout. A matrix with R rows (R padded up to a multiple of 64) and
@@ -109,14 +121,27 @@ typedef struct {
  *   n_rounds int32 [1]       R
  *   perm     int32 [T*k]     assignment ids sorted by (expert, a) -- stable
  *   pos      int32 [T*k]     inverse of perm
- *   round_of int32 [T*k]     round of assignment a: i / C'
- *   row_of   int32 [T*k]     round-buffer row of a: e*C' + i % C'
- *                            (i = pos[a] - offsets[e])
- *   xr       elem [E][P][d]  round buffer of gathered token rows, P =
- *                            C' rounded up to a multiple of 64; expert e's
- *                            P x d matrix in the tiled layout (slot c is row
- *                            c; rows at or beyond m(r,e) hold stale data)
- *   h        elem [E][P][f]  SwiGLU activations of the round, same layout
+ *   round_of int32 [T*k]     round of assignment a (for G = 1: i / C')
+ *   row_of   int32 [T*k]     slot of a in its round: g*G*C' + (rows of the
+ *                            lower experts of its group in that round) +
+ *                            c (for G = 1: e*C' + i % C'), i = pos[a] -
+ *                            offsets[e] its index in expert e's list, c
+ *                            its index among e's entries of the round
+ *   rounds   int32 [4][M][E] per round r < M = ceil(T/C') and expert e:
+ *                            m(r,e); the index in e's list of its first
+ *                            entry of round r; the rows of the lower
+ *                            experts of e's group in round r; the same
+ *                            with each expert's rows rounded up to 64
+ *                            (rows r >= R are unused)
+ *   xr       elem [E/G][Q][d] round buffer of gathered token rows: Q = P
+ *                            (G = 1) or G*(P+64) rows per group, P = C'
+ *                            rounded up to a multiple of 64. In round r
+ *                            expert e's rows start at row (padded rounds
+ *                            table entry) of its group's block, as an
+ *                            m(r,e) x d matrix in the tiled layout (its
+ *                            slot c is row c; rows up to the next multiple
+ *                            of 64 hold stale data)
+ *   h        elem [E/G][Q][f] SwiGLU activations of the round, same layout
  *   z        elem [T*k][d]   unweighted expert output of every assignment,
  *                            in expert-sorted order: row i holds the output
  *                            of assignment perm[i] (so assignment a's row
@@ -126,7 +151,7 @@ typedef struct {
  */
 typedef struct {
   size_t idx, weight, counts, offsets, n_rounds, perm, pos, round_of, row_of,
-      scratch, xr, h, z;
+      rounds, scratch, xr, h, z;
   size_t total;
 } moe_workspace_layout_t;
 
@@ -154,19 +179,20 @@ moe_status_t moe_workspace_layout(const moe_config_t *cfg,
                                   moe_workspace_layout_t *out);
 
 /* Route and plan: every token picks its top-k experts; each expert's
- * assignments are then split into rounds of at most C' (the per-expert
- * capacity is fixed, and what does not fit waits for a later round).
- * Reads logits [T][E]; writes idx, weight, counts, offsets, perm, pos,
- * round_of, row_of and n_rounds in the workspace. If plan_host is not NULL
+ * assignments are then split into rounds (the capacity per round is fixed:
+ * C' per expert, shared inside its group of G; what does not fit waits for
+ * a later round). Reads logits [T][E]; writes idx, weight, counts, offsets,
+ * perm, pos, round_of, row_of, rounds and n_rounds in the workspace. If plan_host is not NULL
  * (host memory, E + 1 int32) the call waits for the stream and stores the
  * E counts n_e followed by R there; otherwise it is asynchronous. */
 moe_status_t moe_plan(const moe_config_t *cfg, const float *logits, void *ws,
                       size_t ws_bytes, int32_t *plan_host, void *stream);
 
 /* Dispatch of round r ("dispatch -> compute -> collect rounds"): for every
- * expert e and slot c < m(r,e), copies x[perm[offsets[e] + r*C' + c] / k]
- * into row c of expert e's round buffer (tiled layout). Rows c >= m(r,e)
- * are left untouched.
+ * expert e and slot c < m(r,e), copies x[perm[offsets[e] + s + c] / k]
+ * (s = the index of e's first entry of round r) into row c of expert e's
+ * matrix of the round buffer (tiled layout). Other rows are left
+ * untouched.
  * 0 <= round < ceil(T / C'); a round >= R moves nothing. Asynchronous. */
 moe_status_t moe_dispatch(const moe_config_t *cfg, int32_t round,
                           const void *x, void *ws, size_t ws_bytes,
@@ -174,18 +200,19 @@ moe_status_t moe_dispatch(const moe_config_t *cfg, int32_t round,
 
 /* Expert compute and collect of round r: for every expert e with
  * m(r,e) > 0, h = silu(xr_e . w_gate[e]^T) * (xr_e . w_up[e]^T) on the
- * first m(r,e) rows of expert e's region, then o = h . w_down[e]^T, and
- * row c of o is stored at z[offsets[e] + r*C' + c], the row of assignment
- * perm[offsets[e] + r*C' + c] (the combine collects these rows back to
- * token order). Grouped GEMMs over all active experts in one launch
+ * first m(r,e) rows of expert e's matrix, then o = h . w_down[e]^T, and
+ * row c of o is stored at z[offsets[e] + s + c], the row of assignment
+ * perm[offsets[e] + s + c] (s as for moe_dispatch; the combine collects
+ * these rows back to token order). Grouped GEMMs over all active experts in one launch
  * each ("grouped GEMM" per expert group, section "Reducing per-expert
  * overhead" as quoted in "Key claims").
  * counts_host: NULL, or a host copy of the E counts n_e (the first E values
  * moe_plan stores in plan_host). With it the launch shape fits the round:
- * a 256 x 256 output tile when that gives every CU a tile, else a 128 x 64
- * tile, and no more workgroups than tiles (what moe_forward does); without
- * it the 256 x 256 tile and one workgroup per CU are used. The results are
- * bit-identical either way. Asynchronous. */
+ * the output tile (256 x 256, 256 x 128 or 128 x 64) with the least
+ * estimated time for the round's rows, and no more workgroups than tiles
+ * (what moe_forward does); without it the 256 x 256 tile and one workgroup
+ * per CU are used. The results are bit-identical either way.
+ * Asynchronous. */
 moe_status_t moe_expert_ffn(const moe_config_t *cfg, int32_t round,
                             const void *w_gate, const void *w_up,
                             const void *w_down, const int32_t *counts_host,

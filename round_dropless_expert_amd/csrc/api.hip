@@ -39,6 +39,14 @@ constexpr int kMaxExperts = 64;
 
 int64_t eff_capacity(const moe_config_t* c) { return c->C < c->T ? c->C : c->T; }
 
+int group_of(const moe_config_t* c) { return c->group == 0 ? 1 : c->group; }
+
+moe::Shape shape_of(const moe_config_t* c) {
+  return moe::Shape{c->T,       c->E, c->k, c->d_model, c->d_ff, (int)eff_capacity(c),
+                    c->dtype == MOE_BF16, c->weight_layout == MOE_WEIGHTS_TILED,
+                    group_of(c)};
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 moe_status_t check_cfg(const moe_config_t* c) {
@@ -54,21 +62,24 @@ moe_status_t check_cfg(const moe_config_t* c) {
     return fail(MOE_ERR_INVALID_ARGUMENT, "unknown dtype");
   if (c->weight_layout != MOE_WEIGHTS_ROW_MAJOR && c->weight_layout != MOE_WEIGHTS_TILED)
     return fail(MOE_ERR_INVALID_ARGUMENT, "unknown weight layout");
+  if (c->group < 0 || (c->group > 0 && c->E % c->group != 0))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "group must divide E (0 means 1)");
   if (c->E > kMaxExperts) return fail(MOE_ERR_UNSUPPORTED, "E > 64 is not supported");
   if (c->d_model % 64 || c->d_ff % 64)
     return fail(MOE_ERR_UNSUPPORTED, "d_model and d_ff must be multiples of 64");
   const int64_t TK = c->T * (int64_t)c->k;
   if (c->T >= (int64_t(1) << 31) || TK >= (int64_t(1) << 31))
     return fail(MOE_ERR_UNSUPPORTED, "T*k must be < 2^31");
-  // per-expert matrices are addressed with 32-bit byte offsets
+  // per-expert and per-group matrices are addressed with 32-bit byte offsets
   const int64_t ce_pad = (eff_capacity(c) + 63) / 64 * 64;
   const int64_t dm = c->d_model > c->d_ff ? c->d_model : c->d_ff;
   const int64_t es = c->dtype == MOE_BF16 ? 2 : 4;
-  if ((int64_t)c->E * ce_pad >= (int64_t(1) << 31) ||
-      ce_pad * dm * es >= (int64_t(1) << 31) ||
+  const int64_t G = group_of(c);
+  if ((int64_t)c->E * (G == 1 ? ce_pad : ce_pad + 64) >= (int64_t(1) << 31) ||
+      G * (ce_pad + 64) * dm * es >= (int64_t(1) << 31) ||
       (int64_t)c->d_model * c->d_ff * es >= (int64_t(1) << 31))
     return fail(MOE_ERR_UNSUPPORTED,
-                "E*C', C'*max(d,f)*elem and d*f*elem must be < 2^31");
+                "round-buffer rows, their bytes per group and d*f*elem must be < 2^31");
   return MOE_OK;
 }
 
@@ -77,9 +88,8 @@ void layout_of(const moe_config_t* c, moe_workspace_layout_t* L) {
   const size_t E = (size_t)c->E;
   const size_t ce = (size_t)eff_capacity(c);
   const size_t es = c->dtype == MOE_BF16 ? 2 : 4;
-  moe::Shape s{c->T, c->E, c->k, c->d_model, c->d_ff, (int)ce, c->dtype == MOE_BF16,
-               c->weight_layout == MOE_WEIGHTS_TILED};
-  const size_t ce_pad = (size_t)s.ce_pad();
+  const moe::Shape s = shape_of(c);
+  (void)ce;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -96,9 +106,10 @@ void layout_of(const moe_config_t* c, moe_workspace_layout_t* L) {
   L->pos = take(TK * 4);
   L->round_of = take(TK * 4);
   L->row_of = take(TK * 4);
+  L->rounds = take(4 * (size_t)s.max_rounds() * E * 4);
   L->scratch = take((size_t)moe::plan_scratch_ints(s) * 4);
-  L->xr = take(E * ce_pad * (size_t)c->d_model * es);
-  L->h = take(E * ce_pad * (size_t)c->d_ff * es);
+  L->xr = take((size_t)s.buf_rows() * (size_t)c->d_model * es);
+  L->h = take((size_t)s.buf_rows() * (size_t)c->d_ff * es);
   L->z = take(TK * (size_t)c->d_model * es);
   L->total = off;
 }
@@ -119,8 +130,7 @@ moe_status_t bind(const moe_config_t* c, void* ws, size_t ws_bytes, Bound* b) {
   layout_of(c, &b->L);
   if (ws_bytes < b->L.total)
     return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace too small");
-  b->s = moe::Shape{c->T, c->E, c->k, c->d_model, c->d_ff, (int)eff_capacity(c),
-                    c->dtype == MOE_BF16, c->weight_layout == MOE_WEIGHTS_TILED};
+  b->s = shape_of(c);
   b->ws = static_cast<char*>(ws);
   char* w = b->ws;
   const moe_workspace_layout_t& L = b->L;
@@ -129,7 +139,8 @@ moe_status_t bind(const moe_config_t* c, void* ws, size_t ws_bytes, Bound* b) {
       reinterpret_cast<int32_t*>(w + L.counts),   reinterpret_cast<int32_t*>(w + L.offsets),
       reinterpret_cast<int32_t*>(w + L.n_rounds), reinterpret_cast<int32_t*>(w + L.perm),
       reinterpret_cast<int32_t*>(w + L.pos),      reinterpret_cast<int32_t*>(w + L.round_of),
-      reinterpret_cast<int32_t*>(w + L.row_of),   reinterpret_cast<int32_t*>(w + L.scratch)};
+      reinterpret_cast<int32_t*>(w + L.row_of),   reinterpret_cast<int32_t*>(w + L.scratch),
+      reinterpret_cast<int32_t*>(w + L.rounds)};
   return MOE_OK;
 }
 
@@ -235,15 +246,25 @@ moe_status_t read_plan(const Bound& b, int32_t* out, hipStream_t st) {
 }
 
 moe_status_t run_ffn(const Bound& b, int r, const void* wg, const void* wu,
-                     const void* wd, const int32_t* counts_host, int cus,
+                     const void* wd, const int32_t* rows_host, int cus,
                      hipStream_t st) {
-  MOE_HIP(moe::launch_gate_up(b.s, r, b.ws + b.L.xr, wg, wu, b.pb.counts,
-                              counts_host, b.ws + b.L.h, cus, st),
+  MOE_HIP(moe::launch_gate_up(b.s, r, b.ws + b.L.xr, wg, wu, b.pb, rows_host,
+                              b.ws + b.L.h, cus, st),
           "gate/up launch");
-  MOE_HIP(moe::launch_down(b.s, r, b.ws + b.L.h, wd, b.pb, counts_host,
+  MOE_HIP(moe::launch_down(b.s, r, b.ws + b.L.h, wd, b.pb, rows_host,
                            b.ws + b.L.z, cus, st),
           "down launch");
   return MOE_OK;
+}
+
+// Rows of every expert in round r from host counts (NULL if counts is NULL).
+const int32_t* rows_from_counts(const moe::Shape& s, const int32_t* counts, int r,
+                                int32_t* rows) {
+  if (!counts) return nullptr;
+  int64_t rem[kMaxExperts];
+  for (int e = 0; e < s.E; ++e) rem[e] = counts[e];
+  for (int rr = 0; rr <= r; ++rr) moe::host_next_round(s, rem, rows);
+  return rows;
 }
 
 }  // namespace
@@ -330,7 +351,9 @@ moe_status_t moe_expert_ffn(const moe_config_t* cfg, int32_t round,
   if ((st = check_round(b, round)) != MOE_OK) return st;
   int cus = 0;
   if ((st = num_cus(&cus)) != MOE_OK) return st;
-  return run_ffn(b, round, w_gate, w_up, w_down, counts_host, cus,
+  int32_t rows[kMaxExperts];
+  return run_ffn(b, round, w_gate, w_up, w_down,
+                 rows_from_counts(b.s, counts_host, round, rows), cus,
                  static_cast<hipStream_t>(stream));
 }
 
@@ -346,9 +369,10 @@ moe_status_t moe_expert_gate_up(const moe_config_t* cfg, int32_t round,
   if ((st = check_round(b, round)) != MOE_OK) return st;
   int cus = 0;
   if ((st = num_cus(&cus)) != MOE_OK) return st;
-  MOE_HIP(moe::launch_gate_up(b.s, round, b.ws + b.L.xr, w_gate, w_up,
-                              b.pb.counts, counts_host, b.ws + b.L.h, cus,
-                              static_cast<hipStream_t>(stream)),
+  int32_t rows[kMaxExperts];
+  MOE_HIP(moe::launch_gate_up(b.s, round, b.ws + b.L.xr, w_gate, w_up, b.pb,
+                              rows_from_counts(b.s, counts_host, round, rows),
+                              b.ws + b.L.h, cus, static_cast<hipStream_t>(stream)),
           "gate/up launch");
   return MOE_OK;
 }
@@ -363,7 +387,9 @@ moe_status_t moe_expert_down(const moe_config_t* cfg, int32_t round,
   if ((st = check_round(b, round)) != MOE_OK) return st;
   int cus = 0;
   if ((st = num_cus(&cus)) != MOE_OK) return st;
-  MOE_HIP(moe::launch_down(b.s, round, b.ws + b.L.h, w_down, b.pb, counts_host,
+  int32_t rows[kMaxExperts];
+  MOE_HIP(moe::launch_down(b.s, round, b.ws + b.L.h, w_down, b.pb,
+                           rows_from_counts(b.s, counts_host, round, rows),
                            b.ws + b.L.z, cus, static_cast<hipStream_t>(stream)),
           "down launch");
   return MOE_OK;
@@ -387,8 +413,7 @@ moe_status_t moe_pack_weights(const moe_config_t* cfg, const void* w_gate,
   }
   int cus = 0;
   if ((st = num_cus(&cus)) != MOE_OK) return st;
-  moe::Shape s{c.T, c.E, c.k, c.d_model, c.d_ff, (int)eff_capacity(&c),
-               c.dtype == MOE_BF16, false};
+  const moe::Shape s = shape_of(&c);
   hipStream_t hs = static_cast<hipStream_t>(stream);
   MOE_HIP(moe::launch_pack_weights(s, w_gate, out_gate, c.d_ff, c.d_model, cus, hs),
           "pack launch");
@@ -451,11 +476,15 @@ moe_status_t moe_forward(const moe_config_t* cfg, const float* logits,
   const int64_t max_rounds = (b.s.T + b.s.ce - 1) / b.s.ce;
   if (R < 1 || R > max_rounds)
     return fail(MOE_ERR_HIP, "device plan reported an impossible round count");
+  int64_t rem[kMaxExperts];
+  for (int e = 0; e < b.s.E; ++e) rem[e] = counts_r[e];
+  int32_t rows[kMaxExperts];
   for (int r = 0; r < R; ++r) {
     if (r > 0)
       MOE_HIP(moe::launch_dispatch(b.s, r, x, b.pb, b.ws + b.L.xr, cus, s),
               "dispatch launch");
-    if ((st = run_ffn(b, r, w_gate, w_up, w_down, counts_r, cus, s)) != MOE_OK)
+    moe::host_next_round(b.s, rem, rows);
+    if ((st = run_ffn(b, r, w_gate, w_up, w_down, rows, cus, s)) != MOE_OK)
       return st;
   }
   MOE_HIP(moe::launch_combine(b.s, b.ws + b.L.z, b.pb.weight, b.pb.pos, y, cus, s),

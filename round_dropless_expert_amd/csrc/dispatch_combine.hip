@@ -14,31 +14,37 @@ namespace moe {
 // Round r, token-major: one wavefront per token reads the token's row of x
 // once and writes it to every slot the token holds in round r. The token's
 // k assignments a = t*k + j carry their expert idx[a], round round_of[a]
-// and round-buffer row row_of[a] = e*C' + c; assignment j goes to slot c of
-// expert e's tiled round-buffer matrix if round_of[a] == r. Each lane moves
-// 16-byte chunks q = lane + 64 i of the row: chunk q lands in 4 KiB block
-// q / 4 of the row's 64-row band, at row c % 64 and chunk position
-// (q % 4) ^ ((c / 4) % 4) (the tiled layout).
+// and slot row_of[a] = g*G*C' + ubase(r,e) + c (g = e / G); assignment j
+// goes to slot c of expert e's matrix if round_of[a] == r. That matrix
+// starts at buffer row g*Q + pbase(r,e) (Q rows per group), a multiple of
+// 64, so the whole buffer is one tiled matrix: each lane moves 16-byte
+// chunks q = lane + 64 i of the row, and chunk q of buffer row p lands in
+// 4 KiB block q / 4 of p's 64-row band, at row p % 64 and chunk position
+// (q % 4) ^ ((p / 4) % 4).
 template <int kChunks>  // 16-byte chunks per lane held in registers
 __global__ __launch_bounds__(256) void dispatch_kernel(
-    const char* __restrict__ x, int64_t T, int row_bytes, int k, int ce,
-    int ce_pad, int r, const int32_t* __restrict__ idx,
+    const char* __restrict__ x, int64_t T, int row_bytes, int E, int k, int ce,
+    int G, int64_t pool_rows, int r, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ round_of, const int32_t* __restrict__ row_of,
+    const int32_t* __restrict__ ubase, const int32_t* __restrict__ pbase,
     char* __restrict__ xr) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kWave;
   const int64_t nwaves = (int64_t)gridDim.x * blockDim.x / kWave;
   const int n16 = row_bytes / 16;
-  const int64_t mat_bytes = (int64_t)ce_pad * row_bytes;
   const int64_t band_bytes = (int64_t)row_bytes * kTileRows;
   for (int64_t t = wave; t < T; t += nwaves) {
-    int e = 0, row = 0;
+    int64_t prow = 0;  // buffer row of this lane's assignment
     bool mine = false;
     if (lane < k) {
       const int64_t a = t * k + lane;
       mine = round_of[a] == r;
-      e = idx[a];
-      row = row_of[a];
+      if (mine) {
+        const int e = idx[a];
+        const int g = e / G;
+        const int c = row_of[a] - g * G * ce - ubase[(int64_t)r * E + e];
+        prow = (int64_t)g * pool_rows + pbase[(int64_t)r * E + e] + c;
+      }
     }
     uint64_t todo = __builtin_amdgcn_ballot_w64(mine);
     if (todo == 0) continue;
@@ -52,11 +58,9 @@ __global__ __launch_bounds__(256) void dispatch_kernel(
       }
       for (uint64_t m = todo; m; m &= m - 1) {
         const int j = __builtin_ctzll(m);
-        const int ej = __shfl(e, j, kWave);
-        const int c = __shfl(row, j, kWave) - ej * ce;
-        char* dst = xr + ej * mat_bytes + (int64_t)(c >> 6) * band_bytes +
-                    (c & 63) * kTileRowBytes;
-        const int sw = (c >> 2) & 3;
+        const int64_t pj = __shfl(prow, j, kWave);
+        char* dst = xr + (pj >> 6) * band_bytes + (pj & 63) * kTileRowBytes;
+        const int sw = (int)((pj >> 2) & 3);
 #pragma unroll
         for (int i = 0; i < kChunks; ++i) {
           const int q = base + lane + i * kWave;
@@ -77,9 +81,11 @@ hipError_t launch_dispatch(const Shape& s, int r, const void* x,
   const int64_t cap = (int64_t)num_cus * 8;
   if (blocks > cap) blocks = cap;
   if (blocks < 1) blocks = 1;
+  const int64_t tbl = s.max_rounds() * s.E;
   hipLaunchKernelGGL(dispatch_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, st,
-                     static_cast<const char*>(x), s.T, row_bytes, s.k, s.ce,
-                     s.ce_pad(), r, b.idx, b.round_of, b.row_of,
+                     static_cast<const char*>(x), s.T, row_bytes, s.E, s.k, s.ce,
+                     s.G, s.pool_rows(), r, b.idx, b.round_of, b.row_of,
+                     b.rounds + kUbase * tbl, b.rounds + kPbase * tbl,
                      static_cast<char*>(xr));
   return hipGetLastError();
 }

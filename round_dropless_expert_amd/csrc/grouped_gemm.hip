@@ -84,15 +84,16 @@ struct MmaOp<float> {
 
 template <typename Elem>
 struct GemmParams {
-  const Elem* act;   // round rows [E*ce][K]: xr (gate/up) or h (down)
+  const Elem* act;   // round buffer [rows][K]: xr (gate/up) or h (down)
   const Elem* w0;    // [E][*][K]: gate (gate/up) or down weights
   const Elem* w1;    // [E][N][K]: up weights (gate/up only)
-  Elem* out;         // h [E*ce][N] (gate/up) or z [T*k][N] (down)
-  const int32_t* counts;
-  const int32_t* offsets;
-  const int32_t* perm;
-  int E, ce, r, K, N;  // N = output features: f (gate/up) or d (down)
-  int ce_pad;          // round-buffer rows per expert (multiple of 64)
+  Elem* out;         // h [rows][N] (gate/up) or z [T*k][N] (down)
+  const int32_t* rounds;   // the plan's round tables [4][max_rounds][E]
+  const int32_t* offsets;  // [E+1]
+  int E, r, K, N;      // N = output features: f (gate/up) or d (down)
+  int max_rounds;      // rows of each round table
+  int G;               // experts per capacity group
+  int pool_rows;       // round-buffer rows per group (multiple of 64)
   int tiled_w;         // weights in the tiled layout (else row-major)
 };
 
@@ -281,13 +282,19 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
   const int l32 = lane & 31;
 
   // Every wavefront keeps the round's tile table in registers: lane e holds
-  // expert e's rows m_e and the inclusive prefix of the tile counts.
+  // expert e's rows m_e, the inclusive prefix of the tile counts, the first
+  // buffer row of e's matrix (its group's block plus the padded rows of the
+  // group's lower experts) and, for down, e's first row of z in the round
+  // (offsets[e] + the index of its first entry of the round).
   const int nt = (p.N + NF - 1) / NF;
-  const int lane_m = lane < p.E ? rows_in_round(p.counts[lane], p.r, p.ce) : 0;
+  const int64_t tbl = (int64_t)p.max_rounds * p.E;
+  const int64_t at = (int64_t)p.r * p.E + lane;
+  const bool lv = lane < p.E;
+  const int lane_m = lv ? p.rounds[kAlloc * tbl + at] : 0;
   const int lane_incl = wave_inclusive_scan(((lane_m + BM - 1) / BM) * nt);
   const int total = __builtin_amdgcn_readlane(lane_incl, kWave - 1);
-  // (down) lane e also holds offsets[e]: the epilogue then needs no load
-  const int lane_off = !kGateUp && lane < p.E ? p.offsets[lane] : 0;
+  const int lane_row = lv ? (lane / p.G) * p.pool_rows + p.rounds[kPbase * tbl + at] : 0;
+  const int lane_off = !kGateUp && lv ? p.offsets[lane] + p.rounds[kCum * tbl + at] : 0;
 
   // XCD-contiguous walk: workgroup b runs on XCD b % 8.
   const int G = gridDim.x;
@@ -335,9 +342,10 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
     S.rw1 = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(kGateUp ? p.w1 + (int64_t)te * p.N * p.K : p.w0), 0, (int)wb,
         kRsrcWord3);
+    // expert te's matrix: its m rows padded to 64, from its first row
     S.ra = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(p.act + (int64_t)te * p.ce_pad * p.K), 0,
-        exists ? (int)((uint32_t)p.ce_pad * kbytes) : 0, kRsrcWord3);
+        (void*)(p.act + (int64_t)__builtin_amdgcn_readlane(lane_row, te) * p.K), 0,
+        exists ? (int)((uint32_t)((tm + 63) & ~63) * kbytes) : 0, kRsrcWord3);
 #pragma unroll
     for (int i = 0; i < kWPasses; ++i) {
       int feat0 = tn0 + 64 * i;
@@ -490,10 +498,10 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(st_t, o), rs, off, 0, 0);
     };
     if (kGateUp) {
-      // h: expert e's tiled matrix, row c
+      // h: expert e's tiled matrix of the round, row c
       const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(p.out + (int64_t)e * p.ce_pad * p.N), 0,
-          (int)((uint32_t)p.ce_pad * p.N * kEs), kRsrcWord3);
+          (void*)(p.out + (int64_t)__builtin_amdgcn_readlane(lane_row, e) * p.N), 0,
+          (int)((uint32_t)((m + 63) & ~63) * p.N * kEs), kRsrcWord3);
 #pragma unroll
       for (int jb = 0; jb < WJ; ++jb) {
         const int c = m0 + wm * (BM / 2) + jb * 32 + l32;
@@ -517,10 +525,10 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
         }
       }
     } else {
-      // z: rows offsets[e] + r*C' + c (c < m) of the expert-sorted order, i.e.
-      // the slot of assignment perm[offsets[e] + r*C' + c]
-      const int64_t i0 = (int64_t)__builtin_amdgcn_readlane(lane_off, e) +
-                         (int64_t)p.r * p.ce;
+      // z: rows i0 + c (c < m) of the expert-sorted order, i0 = offsets[e]
+      // + the index of e's first entry of the round: the slot of assignment
+      // perm[i0 + c]
+      const int64_t i0 = (int64_t)__builtin_amdgcn_readlane(lane_off, e);
       const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc(
           (void*)(p.out + i0 * p.N), 0, (int)((uint32_t)m * p.N * kEs), kRsrcWord3);
 #pragma unroll
@@ -560,19 +568,16 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-// Tiles one round needs under configuration Cfg (host side, from counts).
+// Tiles one round needs under configuration Cfg (host side, from the rows
+// of every expert in the round).
 template <typename Cfg>
-static int64_t round_tiles(const Shape& s, const int32_t* counts_host, int r,
-                           int N, bool gate_up) {
+static int64_t round_tiles(const Shape& s, const int32_t* rows, int N,
+                           bool gate_up) {
   const int BM = 64 * Cfg::WJ;
   const int NF = gate_up ? 32 * Cfg::WI : 64 * Cfg::WI;
   const int64_t nt = (N + NF - 1) / NF;
   int64_t tiles = 0;
-  for (int e = 0; e < s.E; ++e) {
-    int64_t m = (int64_t)counts_host[e] - (int64_t)r * s.ce;
-    m = m < 0 ? 0 : (m > s.ce ? s.ce : m);
-    tiles += (m + BM - 1) / BM * nt;
-  }
+  for (int e = 0; e < s.E; ++e) tiles += ((int64_t)rows[e] + BM - 1) / BM * nt;
   return tiles;
 }
 
@@ -601,26 +606,23 @@ static hipError_t launch_gemm_cfg(const GemmParams<Elem>& p, int grid,
   return hipGetLastError();
 }
 
-// counts_host (nullable): per-expert counts on the host. With them the
-// round's tile shape and grid are chosen from its tile counts; without them
-// the large tile and one workgroup per CU are used. Every shape runs the
-// same MFMA sequence over K for every output, so results are identical.
+// rows_host (nullable): rows of every expert in this round, on the host.
+// With them the round's tile shape and grid are chosen from its tile counts;
+// without them the large tile and one workgroup per CU are used. Every shape
+// runs the same MFMA sequence over K for every output, so results are
+// identical.
 template <typename Elem, bool kGateUp>
 static hipError_t launch_gemm(const Shape& s, const GemmParams<Elem>& p,
-                              const int32_t* counts_host, int num_cus,
+                              const int32_t* rows_host, int num_cus,
                               hipStream_t st) {
   const int N = kGateUp ? s.f : s.d;
-  if (counts_host) {
+  if (rows_host) {
     int64_t mmax = 0;
-    for (int e = 0; e < s.E; ++e) {
-      int64_t m = (int64_t)counts_host[e] - (int64_t)p.r * s.ce;
-      m = m < 0 ? 0 : (m > s.ce ? s.ce : m);
-      mmax = m > mmax ? m : mmax;
-    }
+    for (int e = 0; e < s.E; ++e) mmax = rows_host[e] > mmax ? rows_host[e] : mmax;
     if (mmax == 0) return hipSuccess;  // nothing in this round
-    const int64_t tb = round_tiles<TileBig>(s, counts_host, p.r, N, kGateUp);
-    const int64_t tm = round_tiles<TileMedium>(s, counts_host, p.r, N, kGateUp);
-    const int64_t ts = round_tiles<TileSmall>(s, counts_host, p.r, N, kGateUp);
+    const int64_t tb = round_tiles<TileBig>(s, rows_host, N, kGateUp);
+    const int64_t tm = round_tiles<TileMedium>(s, rows_host, N, kGateUp);
+    const int64_t ts = round_tiles<TileSmall>(s, rows_host, N, kGateUp);
     const float cb = est_cost<TileBig>(tb, num_cus);
     const float cm = est_cost<TileMedium>(tm, num_cus);
     const float cs = est_cost<TileSmall>(ts, num_cus);
@@ -634,36 +636,36 @@ static hipError_t launch_gemm(const Shape& s, const GemmParams<Elem>& p,
 }
 
 hipError_t launch_gate_up(const Shape& s, int r, const void* xr,
-                          const void* wg, const void* wu, const int32_t* counts,
-                          const int32_t* counts_host, void* h, int num_cus,
+                          const void* wg, const void* wu, const PlanBuffers& b,
+                          const int32_t* rows_host, void* h, int num_cus,
                           hipStream_t st) {
+  const int mr = (int)s.max_rounds(), pr = (int)s.pool_rows();
   if (s.bf16) {
     GemmParams<bf16> p{static_cast<const bf16*>(xr), static_cast<const bf16*>(wg),
                        static_cast<const bf16*>(wu), static_cast<bf16*>(h),
-                       counts, nullptr, nullptr, s.E, s.ce, r, s.d, s.f,
-                       s.ce_pad(), s.tiled_w};
-    return launch_gemm<bf16, true>(s, p, counts_host, num_cus, st);
+                       b.rounds, b.offsets, s.E, r, s.d, s.f, mr, s.G, pr, s.tiled_w};
+    return launch_gemm<bf16, true>(s, p, rows_host, num_cus, st);
   }
   GemmParams<float> p{static_cast<const float*>(xr), static_cast<const float*>(wg),
                       static_cast<const float*>(wu), static_cast<float*>(h),
-                      counts, nullptr, nullptr, s.E, s.ce, r, s.d, s.f,
-                      s.ce_pad(), s.tiled_w};
-  return launch_gemm<float, true>(s, p, counts_host, num_cus, st);
+                      b.rounds, b.offsets, s.E, r, s.d, s.f, mr, s.G, pr, s.tiled_w};
+  return launch_gemm<float, true>(s, p, rows_host, num_cus, st);
 }
 
 hipError_t launch_down(const Shape& s, int r, const void* h, const void* wd,
-                       const PlanBuffers& b, const int32_t* counts_host, void* z,
+                       const PlanBuffers& b, const int32_t* rows_host, void* z,
                        int num_cus, hipStream_t st) {
+  const int mr = (int)s.max_rounds(), pr = (int)s.pool_rows();
   if (s.bf16) {
     GemmParams<bf16> p{static_cast<const bf16*>(h), static_cast<const bf16*>(wd),
-                       nullptr, static_cast<bf16*>(z), b.counts, b.offsets,
-                       b.perm, s.E, s.ce, r, s.f, s.d, s.ce_pad(), s.tiled_w};
-    return launch_gemm<bf16, false>(s, p, counts_host, num_cus, st);
+                       nullptr, static_cast<bf16*>(z), b.rounds, b.offsets, s.E, r,
+                       s.f, s.d, mr, s.G, pr, s.tiled_w};
+    return launch_gemm<bf16, false>(s, p, rows_host, num_cus, st);
   }
   GemmParams<float> p{static_cast<const float*>(h), static_cast<const float*>(wd),
-                      nullptr, static_cast<float*>(z), b.counts, b.offsets,
-                      b.perm, s.E, s.ce, r, s.f, s.d, s.ce_pad(), s.tiled_w};
-  return launch_gemm<float, false>(s, p, counts_host, num_cus, st);
+                      nullptr, static_cast<float*>(z), b.rounds, b.offsets, s.E, r,
+                      s.f, s.d, mr, s.G, pr, s.tiled_w};
+  return launch_gemm<float, false>(s, p, rows_host, num_cus, st);
 }
 
 }  // namespace moe

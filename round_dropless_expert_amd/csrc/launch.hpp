@@ -14,7 +14,15 @@ struct Shape {
   int ce;        // min(C, T)
   bool bf16;     // element type of x, weights, y and the round buffers
   bool tiled_w;  // weights in the tiled layout of moe_pack_weights
-  int ce_pad() const { return (ce + 63) / 64 * 64; }  // round-buffer rows per expert
+  int G;         // experts per capacity group
+  int ce_pad() const { return (ce + 63) / 64 * 64; }
+  // round-buffer rows per group: each expert's rows of a round start at a
+  // multiple of 64, so a group of G > 1 needs up to 64 more per expert
+  int64_t pool_rows() const {
+    return G == 1 ? (int64_t)ce_pad() : (int64_t)G * (ce_pad() + 64);
+  }
+  int64_t buf_rows() const { return (int64_t)(E / G) * pool_rows(); }
+  int64_t max_rounds() const { return (T + ce - 1) / ce; }
 };
 
 // Plan-internal granularity: the router counts an expert histogram for
@@ -45,7 +53,13 @@ struct PlanBuffers {
   int32_t* round_of;
   int32_t* row_of;
   int32_t* scratch;  // hist [hist_rows][E], chunk sums [rank_blocks][E]
+  // [4][max_rounds][E]: rows m(r,e), first list index cum(r,e), rows of the
+  // lower experts of the group ubase(r,e), the same padded to 64 pbase(r,e)
+  int32_t* rounds;
 };
+
+// Tables of PlanBuffers::rounds.
+enum RoundTable { kAlloc = 0, kCum = 1, kUbase = 2, kPbase = 3 };
 
 hipError_t launch_route(const Shape& s, const float* logits, PlanBuffers b,
                         hipStream_t st);
@@ -53,17 +67,21 @@ hipError_t launch_plan(const Shape& s, PlanBuffers b, hipStream_t st);
 hipError_t launch_dispatch(const Shape& s, int r, const void* x,
                            const PlanBuffers& b, void* xr, int num_cus,
                            hipStream_t st);
-// counts_host: the plan's per-expert counts read back to the host, or NULL.
-// With them each round gets the tile shape and grid that fit its largest
-// expert (results are identical either way); without them the large tile
-// and one workgroup per CU are used.
+// rows_host: the round's rows m(r,e) of every expert on the host, or NULL.
+// With them the round gets the tile shape and grid that fit it (results are
+// identical either way); without them the large tile and one workgroup per
+// CU are used.
 hipError_t launch_gate_up(const Shape& s, int r, const void* xr,
-                          const void* wg, const void* wu, const int32_t* counts,
-                          const int32_t* counts_host, void* h, int num_cus,
+                          const void* wg, const void* wu, const PlanBuffers& b,
+                          const int32_t* rows_host, void* h, int num_cus,
                           hipStream_t st);
 hipError_t launch_down(const Shape& s, int r, const void* h, const void* wd,
-                       const PlanBuffers& b, const int32_t* counts_host, void* z,
+                       const PlanBuffers& b, const int32_t* rows_host, void* z,
                        int num_cus, hipStream_t st);
+
+// Host copy of the plan's fill rule: from the entries each expert has left
+// (rem[E], updated), the rows m(r,e) of every expert in the next round.
+void host_next_round(const Shape& s, int64_t* rem, int32_t* rows_out);
 hipError_t launch_pack_weights(const Shape& s, const void* src, void* dst,
                                int rows, int cols, int num_cus, hipStream_t st);
 hipError_t launch_combine(const Shape& s, const void* z, const float* weight,

@@ -130,17 +130,26 @@ __global__ __launch_bounds__(256) void plan_chunk_sum_kernel(
         part[3][threadIdx.x];
 }
 
-// Phase 2, the prefix sums over chunks: counts n_e = sum_b sums[b][e],
-// exclusive offsets over e, R = max_e ceil(n_e / C'), and for every chunk b
-// the first position of expert e's entries from it, offsets[e] +
-// sum_{b' < b} sums[b'][e]. With up to kSelfScanMaxChunks chunks every
-// ranking workgroup sums the columns it needs itself (kSelfScan);
-// otherwise one workgroup does it here and leaves the chunk starts in place
-// of the sums.
+// Phase 2 (one workgroup): counts n_e = sum_b sums[b][e], exclusive offsets
+// over e, the rounds and their tables, and, when there are more than
+// kSelfScanMaxChunks chunks, every chunk's first position of expert e's
+// entries, offsets[e] + sum_{b' < b} sums[b'][e], written in place of the
+// sums (with fewer chunks each ranking workgroup sums its prefix itself).
+//
+// Rounds (wavefront 0, lane e = expert): with rem_e entries left, expert e
+// first takes min(rem_e, C') rows; the slots its group of G experts leaves
+// unused (G*C' minus the group's sum) then go to the group's experts with
+// entries left over, in ascending expert order. Group sums and prefixes are
+// segments of a wavefront-wide inclusive scan. Per round r the tables get
+// m(r,e), the index of e's first entry of the round, and the rows of the
+// lower experts of e's group in the round (plain and each rounded up to 64,
+// which is where e's rows start in the group's block of the round buffer).
+// R is the number of rounds until nothing is left.
 __global__ __launch_bounds__(1024) void plan_scan_kernel(
-    int32_t* __restrict__ hist, int64_t nrows, int E, int ce,
-    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ n_rounds) {
+    int32_t* __restrict__ sums, int64_t nchunks, int E, int ce, int G,
+    bool write_starts, int64_t max_rounds, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ n_rounds,
+    int32_t* __restrict__ rounds) {
   constexpr int kWaves = 16;
   __shared__ int part[kWaves][kWave];
   __shared__ int base[kWave];
@@ -150,7 +159,7 @@ __global__ __launch_bounds__(1024) void plan_scan_kernel(
   // column sums: wavefront w takes chunks w, w + 16, ...
   int n = 0;
   if (on)
-    for (int64_t b = wv; b < nrows; b += kWaves) n += hist[b * E + lane];
+    for (int64_t b = wv; b < nchunks; b += kWaves) n += sums[b * E + lane];
   part[wv][lane] = n;
   __syncthreads();
   if (wv == 0) {
@@ -165,22 +174,57 @@ __global__ __launch_bounds__(1024) void plan_scan_kernel(
       offsets[lane] = excl;
     }
     if (lane == E - 1) offsets[E] = incl;
-    const int r = on ? (int)(((int64_t)tot + ce - 1) / ce) : 0;
-    const int rmax = wave_max(r);
-    if (lane == 0) *n_rounds = rmax;
     base[lane] = excl;
+
+    // the rounds
+    const int g0 = lane - lane % G;  // first lane of this lane's group
+    auto in_group_excl = [&](int v) {  // exclusive prefix inside the group
+      const int inc = wave_inclusive_scan(v);
+      const int before = __shfl(inc, g0 > 0 ? g0 - 1 : 0, kWave);
+      return inc - v - (g0 > 0 ? before : 0);
+    };
+    auto group_sum = [&](int v) {
+      const int inc = wave_inclusive_scan(v);
+      const int last = __shfl(inc, g0 + G - 1, kWave);
+      const int before = __shfl(inc, g0 > 0 ? g0 - 1 : 0, kWave);
+      return last - (g0 > 0 ? before : 0);
+    };
+    const int64_t tbl = max_rounds * E;
+    int rem = tot;
+    int r = 0;
+    while (__ballot(rem > 0) != 0ull) {
+      const int own = rem < ce ? rem : ce;
+      const int spare = G * ce - group_sum(own);
+      const int over = rem - own;
+      int extra = spare - in_group_excl(over);
+      extra = extra < 0 ? 0 : (extra > over ? over : extra);
+      const int m = own + extra;
+      const int ub = in_group_excl(m);
+      const int pb = in_group_excl((m + 63) & ~63);
+      if (on && r < max_rounds) {
+        const int64_t at = (int64_t)r * E + lane;
+        rounds[kAlloc * tbl + at] = m;
+        rounds[kCum * tbl + at] = tot - rem;
+        rounds[kUbase * tbl + at] = ub;
+        rounds[kPbase * tbl + at] = pb;
+      }
+      rem -= m;
+      ++r;
+    }
+    if (lane == 0) *n_rounds = r;
   }
   __syncthreads();
+  if (!write_starts) return;
   // chunk starts, 16 consecutive chunks at a time: wavefront w takes chunk
   // 16 t + w, and the starts follow from an exclusive scan over the group
-  for (int64_t b0 = 0; b0 < nrows; b0 += kWaves) {
+  for (int64_t b0 = 0; b0 < nchunks; b0 += kWaves) {
     const int64_t b = b0 + wv;
-    const int c = on && b < nrows ? hist[b * E + lane] : 0;
+    const int c = on && b < nchunks ? sums[b * E + lane] : 0;
     part[wv][lane] = c;
     __syncthreads();
     int pre = base[lane];
     for (int w = 0; w < wv; ++w) pre += part[w][lane];
-    if (on && b < nrows) hist[b * E + lane] = pre;
+    if (on && b < nchunks) sums[b * E + lane] = pre;
     __syncthreads();
     if (wv == 0) {
       int add = 0;
@@ -197,17 +241,21 @@ __global__ __launch_bounds__(1024) void plan_scan_kernel(
 // expert are found with six ballots (one per bit of the expert index), the
 // rank is the number of such lanes below, and per-wave totals are combined
 // in wave order through LDS. Then the position, its inverse and the round
-// split are written. Workgroup b ranks the assignments of tokens
-// [256 b, 256 b + 256). With kSelfScan the workgroup first derives its
-// starts (and, in workgroup 0, counts, offsets and R) from the chunk sums.
+// and row are written. Workgroup b ranks the assignments of tokens
+// [256 b, 256 b + 256); its starts are offsets[e] plus the chunk sums of
+// the chunks before it (summed here with kSelfScan, else left by phase 2).
+// An entry's round is i / C' and its row e*C' + i % C' for G = 1; with
+// groups, the last round whose first index is <= i (binary search in the
+// tables), and its row g*G*C' + (rows of the group's lower experts) +
+// (i - first index).
 template <bool kSelfScan>
 __global__ __launch_bounds__(256) void plan_rank_kernel(
-    const int32_t* __restrict__ idx, int64_t TK, int E, int k, int ce,
-    int64_t nrows, const int32_t* __restrict__ hist,
-    int32_t* __restrict__ counts, int32_t* __restrict__ offsets_out,
-    int32_t* __restrict__ n_rounds, int32_t* __restrict__ perm,
-    int32_t* __restrict__ pos, int32_t* __restrict__ round_of,
-    int32_t* __restrict__ row_of) {
+    const int32_t* __restrict__ idx, int64_t TK, int E, int k, int ce, int G,
+    int64_t nchunks, const int32_t* __restrict__ sums,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ n_rounds,
+    const int32_t* __restrict__ rounds, int64_t max_rounds,
+    int32_t* __restrict__ perm, int32_t* __restrict__ pos,
+    int32_t* __restrict__ round_of, int32_t* __restrict__ row_of) {
   __shared__ int running[kWave];
   __shared__ int offs[kWave];
   __shared__ int cnt[4][kWave];
@@ -216,56 +264,30 @@ __global__ __launch_bounds__(256) void plan_rank_kernel(
   const int wv = tid / kWave;
   const int64_t blk = blockIdx.x;
   if (kSelfScan) {
-    // column totals and the prefix over the chunks before this one:
-    // wavefront w takes chunks w, w + 4, ... (a sum does not depend on the
-    // order of its terms)
-    const int64_t row0 = blk;
-    int tot = 0, pre = 0;
+    // the prefix over the chunks before this one: wavefront w takes chunks
+    // w, w + 4, ... (a sum does not depend on the order of its terms)
+    int pre = 0;
     if (lane < E) {
       int64_t q = wv;
-      for (; q + 12 < nrows; q += 16) {  // four loads in flight
-        const int v0 = hist[q * E + lane], v1 = hist[(q + 4) * E + lane];
-        const int v2 = hist[(q + 8) * E + lane], v3 = hist[(q + 12) * E + lane];
-        tot += v0 + v1 + v2 + v3;
-        pre += (q < row0 ? v0 : 0) + (q + 4 < row0 ? v1 : 0) +
-               (q + 8 < row0 ? v2 : 0) + (q + 12 < row0 ? v3 : 0);
-      }
-      for (; q < nrows; q += 4) {
-        const int v = hist[q * E + lane];
-        tot += v;
-        if (q < row0) pre += v;
-      }
+      for (; q + 12 < blk; q += 16)  // four loads in flight
+        pre += sums[q * E + lane] + sums[(q + 4) * E + lane] +
+               sums[(q + 8) * E + lane] + sums[(q + 12) * E + lane];
+      for (; q < blk; q += 4) pre += sums[q * E + lane];
     }
-    cnt[wv][lane] = tot;
-    running[lane] = 0;
-    __syncthreads();
-    if (wv == 0) {
-      int n = cnt[0][lane] + cnt[1][lane] + cnt[2][lane] + cnt[3][lane];
-      if (lane >= E) n = 0;
-      const int incl = wave_inclusive_scan(n);
-      offs[lane] = incl - n;
-      if (blk == 0) {
-        if (lane < E) {
-          counts[lane] = n;
-          offsets_out[lane] = incl - n;
-        }
-        if (lane == E - 1) offsets_out[E] = incl;
-        const int r = lane < E ? (int)(((int64_t)n + ce - 1) / ce) : 0;
-        const int rmax = wave_max(r);
-        if (lane == 0) *n_rounds = rmax;
-      }
-    }
-    __syncthreads();
     cnt[wv][lane] = pre;
     __syncthreads();
-    if (tid < kWave)
+    if (tid < kWave) {
+      offs[tid] = tid < E ? offsets[tid] : 0;
       running[tid] = offs[tid] + cnt[0][tid] + cnt[1][tid] + cnt[2][tid] + cnt[3][tid];
+    }
   } else {
     if (tid < kWave) {
-      running[tid] = tid < E ? hist[blk * E + tid] : 0;
-      offs[tid] = tid < E ? offsets_out[tid] : 0;
+      running[tid] = tid < E ? sums[blk * E + tid] : 0;
+      offs[tid] = tid < E ? offsets[tid] : 0;
     }
   }
+  const int R = *n_rounds;
+  const int64_t tbl = max_rounds * E;
   const int64_t start = blk * kRankTokens * k;
   const int64_t end = start + (int64_t)kRankTokens * k < TK
                           ? start + (int64_t)kRankTokens * k : TK;
@@ -300,14 +322,26 @@ __global__ __launch_bounds__(256) void plan_rank_kernel(
       perm[p] = (int32_t)a;
       pos[a] = p;
       const int i = p - offs[e];
-      round_of[a] = i / ce;
-      row_of[a] = e * ce + i % ce;
+      if (G == 1) {
+        round_of[a] = i / ce;
+        row_of[a] = e * ce + i % ce;
+      } else {
+        int lo = 0, hi = R - 1;
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (rounds[kCum * tbl + (int64_t)mid * E + e] <= i) lo = mid; else hi = mid - 1;
+        }
+        const int64_t at = (int64_t)lo * E + e;
+        round_of[a] = lo;
+        row_of[a] = (e - e % G) * ce + rounds[kUbase * tbl + at] +
+                    (i - rounds[kCum * tbl + at]);
+      }
     }
   }
 }
 
-// Chunks up to which every ranking workgroup sums the columns itself
-// (chunks * E reads per workgroup, from L2).
+// Chunks up to which every ranking workgroup sums its prefix itself
+// (up to chunks * E reads per workgroup, from L2).
 constexpr int64_t kSelfScanMaxChunks = 1024;
 
 hipError_t launch_plan(const Shape& s, PlanBuffers b, hipStream_t st) {
@@ -319,20 +353,43 @@ hipError_t launch_plan(const Shape& s, PlanBuffers b, hipStream_t st) {
                      b.scratch, nrows, s.E, sums);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  if (nb <= kSelfScanMaxChunks) {
-    hipLaunchKernelGGL(plan_rank_kernel<true>, dim3((unsigned)nb), dim3(256), 0,
-                       st, b.idx, TK, s.E, s.k, s.ce, nb, sums, b.counts,
-                       b.offsets, b.n_rounds, b.perm, b.pos, b.round_of, b.row_of);
-    return hipGetLastError();
-  }
+  const bool self = nb <= kSelfScanMaxChunks;
   hipLaunchKernelGGL(plan_scan_kernel, dim3(1), dim3(1024), 0, st, sums, nb, s.E,
-                     s.ce, b.counts, b.offsets, b.n_rounds);
+                     s.ce, s.G, !self, s.max_rounds(), b.counts, b.offsets,
+                     b.n_rounds, b.rounds);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(plan_rank_kernel<false>, dim3((unsigned)nb), dim3(256), 0, st,
-                     b.idx, TK, s.E, s.k, s.ce, nb, sums, b.counts, b.offsets,
-                     b.n_rounds, b.perm, b.pos, b.round_of, b.row_of);
+  if (self)
+    hipLaunchKernelGGL(plan_rank_kernel<true>, dim3((unsigned)nb), dim3(256), 0,
+                       st, b.idx, TK, s.E, s.k, s.ce, s.G, nb, sums, b.offsets,
+                       b.n_rounds, b.rounds, s.max_rounds(), b.perm, b.pos,
+                       b.round_of, b.row_of);
+  else
+    hipLaunchKernelGGL(plan_rank_kernel<false>, dim3((unsigned)nb), dim3(256), 0,
+                       st, b.idx, TK, s.E, s.k, s.ce, s.G, nb, sums, b.offsets,
+                       b.n_rounds, b.rounds, s.max_rounds(), b.perm, b.pos,
+                       b.round_of, b.row_of);
   return hipGetLastError();
+}
+
+// The same fill rule on the host, for launch shapes: from the entries each
+// expert has left (rem, updated), the rows of every expert in the next
+// round.
+void host_next_round(const Shape& s, int64_t* rem, int32_t* rows_out) {
+  for (int g0 = 0; g0 < s.E; g0 += s.G) {
+    int64_t spare = (int64_t)s.G * s.ce;
+    for (int e = g0; e < g0 + s.G; ++e) {
+      rows_out[e] = (int32_t)(rem[e] < s.ce ? rem[e] : s.ce);
+      spare -= rows_out[e];
+    }
+    for (int e = g0; e < g0 + s.G; ++e) {
+      const int64_t over = rem[e] - rows_out[e];
+      const int64_t more = over < spare ? over : spare;
+      rows_out[e] += (int32_t)more;
+      spare -= more;
+    }
+    for (int e = g0; e < g0 + s.G; ++e) rem[e] -= rows_out[e];
+  }
 }
 
 }  // namespace moe

@@ -44,10 +44,10 @@ class Case:
         self.wd = up(self.inp.Wd)
         self.idx, self.wt = oracle.route(self.inp.logits, w.k)
 
-    def cfg(self, C=None, weight_layout="tiled"):
+    def cfg(self, C=None, weight_layout="tiled", group=1):
         w = self.w
         return B.config(w.T, w.E, w.k, w.d_model, w.d_ff,
-                        w.C if C is None else C, w.dtype, weight_layout)
+                        w.C if C is None else C, w.dtype, weight_layout, group)
 
     def weights(self, layout="tiled"):
         """(w_gate, w_up, w_down) on the device in the given layout."""
@@ -106,6 +106,34 @@ def assert_plan_equal(views: dict, p: oracle.Plan, idx: np.ndarray):
     np.testing.assert_array_equal(views["round_of"].cpu().numpy(), p.round_of)
     np.testing.assert_array_equal(views["row_of"].cpu().numpy(), p.row_of)
     assert int(views["n_rounds"].item()) == p.R
+    # round tables: rows, first index, rows of the group's lower experts
+    # (plain and padded to 64), from the oracle's allocation
+    t = views["rounds"].cpu().numpy()[:, :p.R].astype(np.int64)
+    E = p.counts.size
+    for r in range(p.R):
+        m = p.rows_in_round(r)
+        np.testing.assert_array_equal(t[0, r], m)
+        np.testing.assert_array_equal(t[1, r], p.first_in_round(r))
+        mp = (m + 63) // 64 * 64
+        for name, v, row in (("ubase", m, t[2, r]), ("pbase", mp, t[3, r])):
+            ex = np.zeros(E, dtype=np.int64)
+            for e in range(E):
+                g0 = e - e % p.G
+                ex[e] = v[g0:e].sum()
+            np.testing.assert_array_equal(row, ex, err_msg=f"{name} round {r}")
+
+
+def expert_rows(views: dict, cfg, r: int, e: int, m: int, cols: int, dtype,
+                buf: str = "xr") -> torch.Tensor:
+    """Rows 0..m-1 of expert e's matrix of round r in the xr (or h) round
+    buffer: it starts at row (e // G) * Q + pbase(r, e), padded to 64."""
+    geo = B.buffer_geometry(cfg)
+    es = torch.empty(0, dtype=dtype).element_size()
+    rb = cols * es
+    start = (e // geo["G"]) * geo["Q"] + int(views["rounds"][3, r, e].item())
+    rows = (m + 63) // 64 * 64
+    seg = views[buf][start * rb:(start + rows) * rb]
+    return untile(seg, rows, cols, dtype)[:m]
 
 
 def sample_tokens(T: int, p: oracle.Plan, k: int, n: int, seed: int = 1):

@@ -50,15 +50,19 @@ def ceil_div(a, b):
     return -(-a // b)
 
 
-def expected_total(T, E, k, d, f, C, es):
+def expected_total(T, E, k, d, f, C, es, G=1):
     al = lambda v: (v + 255) // 256 * 256
     ce = min(C, T)
     pad = ceil_div(ce, 64) * 64  # round-buffer rows per expert, tiled
+    Q = pad if G == 1 else G * (pad + 64)  # rows per capacity group
+    rows = E // G * Q
+    M = ceil_div(T, ce)  # rounds at most
     TK = T * k
     nb = ceil_div(T, 8) + ceil_div(T, 256)  # plan histogram rows, chunk sums
     # counts and R share one block: [E counts][R]
     parts = [TK * 4, TK * 4, (E + 1) * 4, (E + 1) * 4, TK * 4, TK * 4, TK * 4,
-             TK * 4, nb * E * 4, E * pad * d * es, E * pad * f * es, TK * d * es]
+             TK * 4, 4 * M * E * 4, nb * E * 4, rows * d * es, rows * f * es,
+             TK * d * es]
     return sum(al(p) for p in parts)
 
 
@@ -79,6 +83,10 @@ def test_workspace_is_a_function_of_the_config_only(B):
     # skewed routing needs exactly the balanced workload's memory
     assert sizes["skewed_bf16"] == sizes["balanced_bf16"]
     assert 336_000_000 < sizes["balanced_bf16"] < 337_000_000
+    # group 0 means 1
+    w = configs.BALANCED_BF16
+    assert B.workspace_size(B.config(w.T, w.E, w.k, w.d_model, w.d_ff, w.C, "bf16",
+                                     group=0)) == sizes["balanced_bf16"]
     # capacity costs memory; above T it acts as T
     w = configs.HOT_EXPERT_BF16
     prev = 0
@@ -88,12 +96,17 @@ def test_workspace_is_a_function_of_the_config_only(B):
         prev = n
     big = B.workspace_size(B.config(w.T, w.E, w.k, w.d_model, w.d_ff, 10 * w.T, "bf16"))
     assert big == prev
+    # capacity groups: G*(P+64) rows per group of G experts
+    for G in (2, 4, 64):
+        n = B.workspace_size(B.config(w.T, w.E, w.k, w.d_model, w.d_ff, w.C,
+                                      "bf16", group=G))
+        assert n == expected_total(w.T, w.E, w.k, w.d_model, w.d_ff, w.C, 2, G)
 
 
 BAD_CONFIGS = [
     (dict(T=0), 1), (dict(E=0), 1), (dict(k=0), 1), (dict(k=9), 1),
     (dict(C=0), 1), (dict(d_model=0), 1), (dict(dtype=7), 1),
-    (dict(weight_layout=2), 1),
+    (dict(weight_layout=2), 1), (dict(group=3), 1), (dict(group=-1), 1),
     (dict(E=65, k=2), 2), (dict(d_model=96), 2), (dict(d_ff=100), 2),
     (dict(T=1 << 29, k=4), 2),
 ]
@@ -102,7 +115,7 @@ BAD_CONFIGS = [
 @pytest.mark.parametrize("change,status", BAD_CONFIGS)
 def test_config_validation(B, change, status):
     base = dict(T=512, E=8, k=2, d_model=64, d_ff=128, C=64, dtype=0,
-                weight_layout=0)
+                weight_layout=0, group=1)
     base.update(change)
     cfg = B.config(**base)
     assert B.check_config(cfg) == status

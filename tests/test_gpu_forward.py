@@ -23,12 +23,12 @@ def get_case(name):
     return _cache[name]
 
 
-def forward(case, C=None, poison=True, layout="tiled"):
-    cfg = case.cfg(C, weight_layout=layout)
+def forward(case, C=None, poison=True, layout="tiled", group=1):
+    cfg = case.cfg(C, weight_layout=layout, group=group)
     wg, wu, wd = case.weights(layout)
     ws = case.workspace(cfg, poison=poison)
     y = case.new_y()
-    note(f"{case.w.name}: moe_forward C={cfg.C} weights={layout}")
+    note(f"{case.w.name}: moe_forward C={cfg.C} G={group} weights={layout}")
     B.moe_forward(cfg, case.logits, case.x, wg, wu, wd, y, ws)
     torch.cuda.synchronize()
     return cfg, ws, y
@@ -110,6 +110,29 @@ def test_capacity_sweep_small_every_C():
         if ref is None:
             ref = yb.clone()
         assert torch.equal(ref, yb), f"C={C}"
+
+
+@pytest.mark.parametrize("name,groups", [
+    ("skewed_bf16", (2, 8, 32)), ("hot_expert_bf16", (4, 32)),
+    ("tiny_f32", (2, 4))])
+def test_capacity_groups_match_oracle_and_are_bit_identical(name, groups):
+    """Sharing capacity inside groups of G experts changes the plan (fewer
+    rounds under skew) but not the layer's output: every G gives the same
+    bits, and each plan matches the oracle's."""
+    case = get_case(name)
+    w = case.w
+    ib = torch.int16 if w.dtype == "bf16" else torch.int32
+    _, _, y1 = forward(case, poison=False)
+    ref = y1.view(ib).clone()
+    del y1
+    for G in groups:
+        cfg, ws, y = forward(case, group=G)
+        p = oracle.plan_groups(case.idx, w.E, w.C, G)
+        assert_plan_equal(B.workspace_views(cfg, ws), p, case.idx)
+        assert torch.equal(ref, y.view(ib)), f"G={G} differs from G=1"
+        assert torch.isfinite(B.workspace_views(cfg, ws)["z"].float()).all()
+        del ws, y
+        torch.cuda.empty_cache()
 
 
 def _peak_for(name):

@@ -10,8 +10,8 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import (Case, assert_close, assert_plan_equal, el_dtype, note,
-                      tiled_index, to_np, untile)
+from gpu_util import (Case, assert_close, assert_plan_equal, el_dtype,
+                      expert_rows, note, tiled_index, to_np)
 from round_dropless_expert_amd import binding as B
 from round_dropless_expert_amd import configs
 
@@ -40,18 +40,26 @@ STAGE_CASES = [
 ]
 
 
+# (workload, capacity group size) for the stage tests; group > 1 shares the
+# capacity of each group of experts
+GROUP_CASES = [(w, 1) for w in STAGE_CASES] + [
+    (STAGE_CASES[2], 2), (STAGE_CASES[2], 6), (STAGE_CASES[3], 5),
+    (STAGE_CASES[4], 5), (STAGE_CASES[6], 4), (STAGE_CASES[1], 8)]
+
+
 @pytest.mark.parametrize("layout", ["tiled", "row_major"])
-@pytest.mark.parametrize("w", STAGE_CASES, ids=lambda w: w.name)
-def test_stages_match_oracle(w, layout):
+@pytest.mark.parametrize("w,G", GROUP_CASES,
+                         ids=lambda v: v.name if hasattr(v, "name") else f"G{v}")
+def test_stages_match_oracle(w, G, layout):
     torch.cuda.synchronize()
     case = Case(w)
-    cfg = case.cfg(weight_layout=layout)
+    cfg = case.cfg(weight_layout=layout, group=G)
     wg, wu, wd = case.weights(layout)
     ws = case.workspace(cfg)
-    note(f"{w.name}/{layout}: moe_plan")
+    note(f"{w.name}/G{G}/{layout}: moe_plan")
     R, counts = B.moe_plan(cfg, case.logits, ws, return_counts=True)
     views = B.workspace_views(cfg, ws)
-    p = oracle.plan(case.idx, w.E, w.C)
+    p = oracle.plan_groups(case.idx, w.E, w.C, G)
     assert R == p.R
     np.testing.assert_array_equal(counts, p.counts)
     # tiled weights: launch shapes fitted to each round (as moe_forward);
@@ -61,38 +69,37 @@ def test_stages_match_oracle(w, layout):
     wt = views["weight"].cpu().numpy().astype(np.float64)
     assert np.all(np.abs(wt - case.wt) <= 1e-6 * case.wt), "routing weights"
 
-    ce = p.C_eff
-    pad = (ce + 63) // 64 * 64
     dt = el_dtype(w)
     ibits = torch.int16 if w.dtype == "bf16" else torch.int32
     for r in range(R):
-        note(f"{w.name}/{layout}: moe_dispatch round {r}")
+        note(f"{w.name}/G{G}/{layout}: moe_dispatch round {r}")
         B.moe_dispatch(cfg, r, case.x, ws)
         torch.cuda.synchronize()
         m = p.rows_in_round(r)
+        first = p.first_in_round(r)
         experts = [e for e in range(w.E) if m[e] > 0]
-        assigns = [int(p.perm[p.offsets[e] + r * ce + c])
+        assigns = [int(p.perm[p.offsets[e] + first[e] + c])
                    for e in experts for c in range(int(m[e]))]
         a_t = torch.tensor(assigns, device=case.dev, dtype=torch.long)
-        xr = torch.cat([untile(views["xr"][e], pad, w.d_model, dt)[:int(m[e])]
+        xr = torch.cat([expert_rows(views, cfg, r, e, int(m[e]), w.d_model, dt)
                         for e in experts])
         assert torch.equal(xr.view(ibits), case.x[a_t // w.k].view(ibits)), \
             f"xr round {r}"
 
-        note(f"{w.name}/{layout}: moe_expert_ffn round {r}")
+        note(f"{w.name}/G{G}/{layout}: moe_expert_ffn round {r}")
         B.moe_expert_ffn(cfg, r, wg, wu, wd, ws, counts_host=counts_host)
         torch.cuda.synchronize()
         h_ref, o_ref = oracle.assignment_outputs(
             np.array(assigns), case.idx, case.inp.x, case.inp.Wg, case.inp.Wu,
             case.inp.Wd, want_h=True)
-        h = torch.cat([untile(views["h"][e], pad, w.d_ff, dt)[:int(m[e])]
+        h = torch.cat([expert_rows(views, cfg, r, e, int(m[e]), w.d_ff, dt, "h")
                        for e in experts])
         assert_close(to_np(h), h_ref, w.dtype, f"h round {r}")
         # z is in expert-sorted order: assignment a's row is pos[a]
         rows = torch.from_numpy(p.pos[np.array(assigns)]).to(case.dev).long()
         assert_close(to_np(views["z"][rows]), o_ref, w.dtype, f"z round {r}")
 
-    note(f"{w.name}/{layout}: moe_combine")
+    note(f"{w.name}/G{G}/{layout}: moe_combine")
     y = case.new_y()
     B.moe_combine(cfg, ws, y)
     torch.cuda.synchronize()
@@ -124,7 +131,8 @@ def test_pack_weights_is_the_tiled_permutation(dtype):
             assert torch.equal(ob[idx], sb)
 
 
-def test_plan_with_more_chunks_than_the_self_scan_limit():
+@pytest.mark.parametrize("G", [1, 4])
+def test_plan_with_more_chunks_than_the_self_scan_limit(G):
     """Above 1024 plan chunks (256 tokens each) the prefix sums run in a
     separate scan kernel: the plan stays bit-exact."""
     w = W("many_chunks", T=1100 * 256 + 77, d_model=64, d_ff=64, E=16, k=3,
@@ -133,11 +141,11 @@ def test_plan_with_more_chunks_than_the_self_scan_limit():
     note(f"{w.name}: logits")
     logits = synth.generate_activations(w).logits
     idx, _ = oracle.route(logits, w.k)
-    p = oracle.plan(idx, w.E, w.C)
-    cfg = B.config(w.T, w.E, w.k, w.d_model, w.d_ff, w.C, w.dtype)
+    p = oracle.plan_groups(idx, w.E, w.C, G)
+    cfg = B.config(w.T, w.E, w.k, w.d_model, w.d_ff, w.C, w.dtype, group=G)
     ws = torch.empty(B.workspace_size(cfg), dtype=torch.uint8, device="cuda:0")
     ws.fill_(0xFF)
-    note(f"{w.name}: moe_plan T={w.T}")
+    note(f"{w.name}: moe_plan T={w.T} G={G}")
     R, counts = B.moe_plan(cfg, torch.from_numpy(logits).cuda(), ws,
                            return_counts=True)
     assert R == p.R
