@@ -45,6 +45,9 @@ def parse():
                     help="only run torch's device-to-device copy of a known "
                          "size (256 MiB, 5 times): the reference kernel for "
                          "scaling the FETCH_SIZE / WRITE_SIZE counters")
+    ap.add_argument("--group", type=int, default=1,
+                    help="experts per capacity group (1 = each expert keeps "
+                         "its own capacity)")
     ap.add_argument("--weights", choices=("tiled", "row_major"), default="tiled",
                     help="expert weight layout the layer reads (tiled = packed "
                          "once by moe_pack_weights before timing)")
@@ -145,7 +148,8 @@ def main():
     logits = torch.from_numpy(inp.logits).to(dev)
     x, wg_rm, wu_rm, wd_rm = up(inp.x), up(inp.Wg), up(inp.Wu), up(inp.Wd)
     layout = args.weights
-    cfg = B.config(w.T, w.E, w.k, w.d_model, w.d_ff, w.C, w.dtype, layout)
+    cfg = B.config(w.T, w.E, w.k, w.d_model, w.d_ff, w.C, w.dtype, layout,
+                   args.group)
     if layout == "tiled":
         # one-time repack at load time, outside the timed region
         wg, wu, wd = (torch.empty_like(t) for t in (wg_rm, wu_rm, wd_rm))
@@ -283,7 +287,7 @@ def main():
                 "N(0,1/fan_in) weights)",
         "config": {"workload": w.name, "T": w.T, "d_model": w.d_model,
                    "d_ff": w.d_ff, "E": w.E, "k": w.k, "C": w.C,
-                   "weight_layout": layout,
+                   "weight_layout": layout, "group": args.group,
                    "skew": list(w.skew), "rounds": R,
                    "rows_per_round": A.tolist()},
         "grouped_gemm_mfma_util_pct": 100.0 * gemm_util,

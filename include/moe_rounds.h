@@ -212,7 +212,7 @@ moe_status_t moe_dispatch(const moe_config_t *cfg, int32_t round,
  * estimated time for the round's rows, and no more workgroups than tiles
  * (what moe_forward does); without it the 256 x 256 tile and one workgroup
  * per CU are used. The results are bit-identical either way.
- * Asynchronous. */
+ * 0 <= round < ceil(T / C'); a round >= R computes nothing. Asynchronous. */
 moe_status_t moe_expert_ffn(const moe_config_t *cfg, int32_t round,
                             const void *w_gate, const void *w_up,
                             const void *w_down, const int32_t *counts_host,

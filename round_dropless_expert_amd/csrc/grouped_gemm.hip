@@ -90,6 +90,7 @@ struct GemmParams {
   Elem* out;         // h [rows][N] (gate/up) or z [T*k][N] (down)
   const int32_t* rounds;   // the plan's round tables [4][max_rounds][E]
   const int32_t* offsets;  // [E+1]
+  const int32_t* n_rounds; // R: a round r >= R has no rows (its tables are unset)
   int E, r, K, N;      // N = output features: f (gate/up) or d (down)
   int max_rounds;      // rows of each round table
   int G;               // experts per capacity group
@@ -245,7 +246,6 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
   constexpr int kSlotBytes = SPB * kStageBytes;
   constexpr int kLoads = SPB * kPasses;          // loads per slot and thread
   constexpr int kSteps = MmaOp<Elem>::kSteps;
-  constexpr int kMfmaPerStep = WI * WJ;
   constexpr int kReadsPerStep = WI + WJ;
   // The fetch of a super-stage is spread over all its MFMA steps (at most
   // kLoadsPerStep loads after the fragment reads of each step), so that the
@@ -289,7 +289,7 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
   const int nt = (p.N + NF - 1) / NF;
   const int64_t tbl = (int64_t)p.max_rounds * p.E;
   const int64_t at = (int64_t)p.r * p.E + lane;
-  const bool lv = lane < p.E;
+  const bool lv = lane < p.E && p.r < *p.n_rounds;
   const int lane_m = lv ? p.rounds[kAlloc * tbl + at] : 0;
   const int lane_incl = wave_inclusive_scan(((lane_m + BM - 1) / BM) * nt);
   const int total = __builtin_amdgcn_readlane(lane_incl, kWave - 1);
@@ -524,10 +524,67 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
           }
         }
       }
-    } else {
+    } else if constexpr (kEs == 2) {
       // z: rows i0 + c (c < m) of the expert-sorted order, i0 = offsets[e]
       // + the index of e's first entry of the round: the slot of assignment
-      // perm[i0 + c]
+      // perm[i0 + c]. z rows are long (N features), so the lane layout of
+      // the accumulators (one token per lane, 8 bytes of it per store) would
+      // touch 32 rows per store; instead each wavefront turns a block of 32
+      // tokens x 64 features around in LDS and stores whole 128-byte row
+      // pieces, 8 rows per store. The staging area is slot3, which the last
+      // super-stage has consumed (every wavefront passed the barrier after
+      // its last read of it) and which the next tile's ring first fills in
+      // its super-stage 0, after the barrier below.
+      const int64_t i0 = (int64_t)__builtin_amdgcn_readlane(lane_off, e);
+      const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(p.out + i0 * p.N), 0, (int)((uint32_t)m * p.N * kEs), kRsrcWord3);
+      // 32 rows of 128 bytes per wavefront; 16-byte chunk q of row r sits at
+      // chunk q ^ (r % 8), so that neither the writes (32 rows, one chunk
+      // each) nor the reads (8 rows, all chunks) pile onto a few banks
+      char* stg = slot3 + wave_id * 4096;
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+      const int rrow = lane >> 3, rchunk = lane & 7;  // read-back position
+#pragma unroll
+      for (int jb = 0; jb < WJ; ++jb) {
+        const int cb = m0 + wm * (BM / 2) + jb * 32;  // first token of the block
+#pragma unroll
+        for (int ip = 0; ip < WI / 2; ++ip) {
+          // lane (l32, half) holds token l32's features 32 u + 8 g4 + 4 half
+          // + q of the 64, q < 4
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+              vec4_t o;
+#pragma unroll
+              for (int q = 0; q < 4; ++q)
+                o[q] = from_f32<Elem>(acc_read(acc[2 * ip + u][jb][4 * g4 + q]));
+              const int chunk = (u * 4 + g4) ^ (l32 & 7);
+              *reinterpret_cast<u32x2*>(stg + l32 * 128 + chunk * 16 + half * 8) =
+                  __builtin_bit_cast(u32x2, o);
+            }
+          }
+          const int feat = n0 + wn * (BN / 2) + ip * 64 + rchunk * 8;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = i * 8 + rrow;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(
+                stg + r * 128 + ((rchunk ^ (r & 7)) * 16));
+            // rows c >= m fall past the descriptor's range
+            const uint32_t off =
+                feat < p.N ? ((uint32_t)(cb + r) * p.N + feat) * kEs : kOutOfRange;
+            __builtin_amdgcn_raw_buffer_store_b128(v, rz, off, 0, 0);
+          }
+        }
+      }
+      // every wavefront's staging reads are done before the next tile's ring
+      // writes slot3
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    } else {
+      // z (fp32): as above, straight from the accumulator layout
       const int64_t i0 = (int64_t)__builtin_amdgcn_readlane(lane_off, e);
       const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc(
           (void*)(p.out + i0 * p.N), 0, (int)((uint32_t)m * p.N * kEs), kRsrcWord3);
@@ -643,12 +700,12 @@ hipError_t launch_gate_up(const Shape& s, int r, const void* xr,
   if (s.bf16) {
     GemmParams<bf16> p{static_cast<const bf16*>(xr), static_cast<const bf16*>(wg),
                        static_cast<const bf16*>(wu), static_cast<bf16*>(h),
-                       b.rounds, b.offsets, s.E, r, s.d, s.f, mr, s.G, pr, s.tiled_w};
+                       b.rounds, b.offsets, b.n_rounds, s.E, r, s.d, s.f, mr, s.G, pr, s.tiled_w};
     return launch_gemm<bf16, true>(s, p, rows_host, num_cus, st);
   }
   GemmParams<float> p{static_cast<const float*>(xr), static_cast<const float*>(wg),
                       static_cast<const float*>(wu), static_cast<float*>(h),
-                      b.rounds, b.offsets, s.E, r, s.d, s.f, mr, s.G, pr, s.tiled_w};
+                      b.rounds, b.offsets, b.n_rounds, s.E, r, s.d, s.f, mr, s.G, pr, s.tiled_w};
   return launch_gemm<float, true>(s, p, rows_host, num_cus, st);
 }
 
@@ -658,12 +715,12 @@ hipError_t launch_down(const Shape& s, int r, const void* h, const void* wd,
   const int mr = (int)s.max_rounds(), pr = (int)s.pool_rows();
   if (s.bf16) {
     GemmParams<bf16> p{static_cast<const bf16*>(h), static_cast<const bf16*>(wd),
-                       nullptr, static_cast<bf16*>(z), b.rounds, b.offsets, s.E, r,
+                       nullptr, static_cast<bf16*>(z), b.rounds, b.offsets, b.n_rounds, s.E, r,
                        s.f, s.d, mr, s.G, pr, s.tiled_w};
     return launch_gemm<bf16, false>(s, p, rows_host, num_cus, st);
   }
   GemmParams<float> p{static_cast<const float*>(h), static_cast<const float*>(wd),
-                      nullptr, static_cast<float*>(z), b.rounds, b.offsets, s.E, r,
+                      nullptr, static_cast<float*>(z), b.rounds, b.offsets, b.n_rounds, s.E, r,
                       s.f, s.d, mr, s.G, pr, s.tiled_w};
   return launch_gemm<float, false>(s, p, rows_host, num_cus, st);
 }

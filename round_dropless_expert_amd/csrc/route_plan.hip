@@ -236,6 +236,15 @@ __global__ __launch_bounds__(1024) void plan_scan_kernel(
   }
 }
 
+// Where a ranking workgroup's starts come from.
+enum RankMode {
+  kStartsGiven = 0,  // phase 2 left each chunk's starts in place of its sums
+  kSelfPrefix = 1,   // offsets from phase 2; the prefix over chunks summed here
+  kSelfAll = 2,      // G = 1, no phase 2: totals, offsets and the prefix
+                     // summed here; workgroup 0 also writes counts, offsets,
+                     // R and the round tables (closed form for G = 1)
+};
+
 // Phase 3: stable ranking inside each chunk. The chunk is walked in order,
 // 256 assignments per step; inside a wavefront the lanes holding the same
 // expert are found with six ballots (one per bit of the expert index), the
@@ -243,18 +252,18 @@ __global__ __launch_bounds__(1024) void plan_scan_kernel(
 // in wave order through LDS. Then the position, its inverse and the round
 // and row are written. Workgroup b ranks the assignments of tokens
 // [256 b, 256 b + 256); its starts are offsets[e] plus the chunk sums of
-// the chunks before it (summed here with kSelfScan, else left by phase 2).
+// the chunks before it (see RankMode).
 // An entry's round is i / C' and its row e*C' + i % C' for G = 1; with
 // groups, the last round whose first index is <= i (binary search in the
 // tables), and its row g*G*C' + (rows of the group's lower experts) +
 // (i - first index).
-template <bool kSelfScan>
+template <int kMode>
 __global__ __launch_bounds__(256) void plan_rank_kernel(
     const int32_t* __restrict__ idx, int64_t TK, int E, int k, int ce, int G,
     int64_t nchunks, const int32_t* __restrict__ sums,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ n_rounds,
-    const int32_t* __restrict__ rounds, int64_t max_rounds,
-    int32_t* __restrict__ perm, int32_t* __restrict__ pos,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ n_rounds, int32_t* __restrict__ rounds,
+    int64_t max_rounds, int32_t* __restrict__ perm, int32_t* __restrict__ pos,
     int32_t* __restrict__ round_of, int32_t* __restrict__ row_of) {
   __shared__ int running[kWave];
   __shared__ int offs[kWave];
@@ -263,9 +272,71 @@ __global__ __launch_bounds__(256) void plan_rank_kernel(
   const int lane = tid & (kWave - 1);
   const int wv = tid / kWave;
   const int64_t blk = blockIdx.x;
-  if (kSelfScan) {
-    // the prefix over the chunks before this one: wavefront w takes chunks
-    // w, w + 4, ... (a sum does not depend on the order of its terms)
+  const int64_t tbl = max_rounds * E;
+  if (kMode == kSelfAll) {
+    // column totals and the prefix over the chunks before this one:
+    // wavefront w takes chunks w, w + 4, ... (a sum does not depend on the
+    // order of its terms)
+    int tot = 0, pre = 0;
+    if (lane < E) {
+      int64_t q = wv;
+      for (; q + 12 < nchunks; q += 16) {  // four loads in flight
+        const int v0 = sums[q * E + lane], v1 = sums[(q + 4) * E + lane];
+        const int v2 = sums[(q + 8) * E + lane], v3 = sums[(q + 12) * E + lane];
+        tot += v0 + v1 + v2 + v3;
+        pre += (q < blk ? v0 : 0) + (q + 4 < blk ? v1 : 0) +
+               (q + 8 < blk ? v2 : 0) + (q + 12 < blk ? v3 : 0);
+      }
+      for (; q < nchunks; q += 4) {
+        const int v = sums[q * E + lane];
+        tot += v;
+        if (q < blk) pre += v;
+      }
+    }
+    cnt[wv][lane] = tot;
+    __syncthreads();
+    __shared__ int tots[kWave];
+    __shared__ int rmax_sh;
+    if (wv == 0) {
+      int n = cnt[0][lane] + cnt[1][lane] + cnt[2][lane] + cnt[3][lane];
+      if (lane >= E) n = 0;
+      const int incl = wave_inclusive_scan(n);
+      offs[lane] = incl - n;
+      tots[lane] = n;
+      const int rmax = wave_max(lane < E ? (int)(((int64_t)n + ce - 1) / ce) : 0);
+      if (lane == 0) rmax_sh = rmax;
+      if (blk == 0) {
+        if (lane < E) {
+          counts[lane] = n;
+          offsets[lane] = incl - n;
+        }
+        if (lane == E - 1) offsets[E] = incl;
+        if (lane == 0) *n_rounds = rmax;
+      }
+    }
+    __syncthreads();
+    if (blk == 0) {
+      // round r: expert e has min(C', n_e - r C') rows (none past its last
+      // round), its first entry is the round's r C'-th, and with one expert
+      // per group there are no lower experts in its group
+      const int64_t cells = (int64_t)rmax_sh * E;
+      for (int64_t c = tid; c < cells; c += blockDim.x) {
+        const int e = (int)(c % E);
+        const int64_t first = (c / E) * ce;
+        const int64_t n = tots[e];
+        const int64_t left = n - first;
+        rounds[kAlloc * tbl + c] = (int)(left <= 0 ? 0 : (left < ce ? left : ce));
+        rounds[kCum * tbl + c] = (int)(first < n ? first : n);
+        rounds[kUbase * tbl + c] = 0;
+        rounds[kPbase * tbl + c] = 0;
+      }
+    }
+    cnt[wv][lane] = pre;
+    __syncthreads();
+    if (tid < kWave)
+      running[tid] = offs[tid] + cnt[0][tid] + cnt[1][tid] + cnt[2][tid] + cnt[3][tid];
+  } else if (kMode == kSelfPrefix) {
+    // the prefix over the chunks before this one, as above
     int pre = 0;
     if (lane < E) {
       int64_t q = wv;
@@ -286,8 +357,8 @@ __global__ __launch_bounds__(256) void plan_rank_kernel(
       offs[tid] = tid < E ? offsets[tid] : 0;
     }
   }
-  const int R = *n_rounds;
-  const int64_t tbl = max_rounds * E;
+  // rounds (only needed for G > 1, when phase 2 has written them)
+  const int R = G == 1 ? 0 : *n_rounds;
   const int64_t start = blk * kRankTokens * k;
   const int64_t end = start + (int64_t)kRankTokens * k < TK
                           ? start + (int64_t)kRankTokens * k : TK;
@@ -354,20 +425,28 @@ hipError_t launch_plan(const Shape& s, PlanBuffers b, hipStream_t st) {
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const bool self = nb <= kSelfScanMaxChunks;
+  const int64_t mr = s.max_rounds();
+  if (self && s.G == 1) {  // one pass: no phase 2
+    hipLaunchKernelGGL(plan_rank_kernel<kSelfAll>, dim3((unsigned)nb), dim3(256), 0,
+                       st, b.idx, TK, s.E, s.k, s.ce, s.G, nb, sums, b.counts,
+                       b.offsets, b.n_rounds, b.rounds, mr, b.perm, b.pos,
+                       b.round_of, b.row_of);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(plan_scan_kernel, dim3(1), dim3(1024), 0, st, sums, nb, s.E,
-                     s.ce, s.G, !self, s.max_rounds(), b.counts, b.offsets,
-                     b.n_rounds, b.rounds);
+                     s.ce, s.G, !self, mr, b.counts, b.offsets, b.n_rounds,
+                     b.rounds);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (self)
-    hipLaunchKernelGGL(plan_rank_kernel<true>, dim3((unsigned)nb), dim3(256), 0,
-                       st, b.idx, TK, s.E, s.k, s.ce, s.G, nb, sums, b.offsets,
-                       b.n_rounds, b.rounds, s.max_rounds(), b.perm, b.pos,
+    hipLaunchKernelGGL(plan_rank_kernel<kSelfPrefix>, dim3((unsigned)nb), dim3(256),
+                       0, st, b.idx, TK, s.E, s.k, s.ce, s.G, nb, sums, b.counts,
+                       b.offsets, b.n_rounds, b.rounds, mr, b.perm, b.pos,
                        b.round_of, b.row_of);
   else
-    hipLaunchKernelGGL(plan_rank_kernel<false>, dim3((unsigned)nb), dim3(256), 0,
-                       st, b.idx, TK, s.E, s.k, s.ce, s.G, nb, sums, b.offsets,
-                       b.n_rounds, b.rounds, s.max_rounds(), b.perm, b.pos,
+    hipLaunchKernelGGL(plan_rank_kernel<kStartsGiven>, dim3((unsigned)nb), dim3(256),
+                       0, st, b.idx, TK, s.E, s.k, s.ce, s.G, nb, sums, b.counts,
+                       b.offsets, b.n_rounds, b.rounds, mr, b.perm, b.pos,
                        b.round_of, b.row_of);
   return hipGetLastError();
 }

@@ -99,6 +99,19 @@ def test_stages_match_oracle(w, G, layout):
         rows = torch.from_numpy(p.pos[np.array(assigns)]).to(case.dev).long()
         assert_close(to_np(views["z"][rows]), o_ref, w.dtype, f"z round {r}")
 
+    M = B.buffer_geometry(cfg)["M"]
+    if R < M:
+        # a round past R computes nothing, whatever its (unset) tables hold
+        note(f"{w.name}/G{G}/{layout}: round {R} of {M} (past R)")
+        views["rounds"][:, R:] = 1 << 29
+        before = [views[n].view(torch.uint8).clone() for n in ("xr", "h", "z")]
+        B.moe_dispatch(cfg, R, case.x, ws)
+        B.moe_expert_ffn(cfg, R, wg, wu, wd, ws)
+        B.moe_expert_ffn(cfg, R, wg, wu, wd, ws, counts_host=counts)
+        torch.cuda.synchronize()
+        for n, b in zip(("xr", "h", "z"), before):
+            assert torch.equal(views[n].view(torch.uint8), b), n
+
     note(f"{w.name}/G{G}/{layout}: moe_combine")
     y = case.new_y()
     B.moe_combine(cfg, ws, y)
