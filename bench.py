@@ -29,6 +29,10 @@ PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}  # dense MFMA, MI355X
 PEAK_HBM_GBPS = 8000.0
 
 
+# GPU clock cycles of the spin that leads each per-kernel pass (~1 ms)
+SPIN_CYCLES = 2_000_000
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -194,12 +198,16 @@ def main():
     es = 2 if w.dtype == "bf16" else 4
     TK = w.T * w.k
 
-    # per-kernel pass: HIP events on the same stream around each launch
+    # per-kernel pass: HIP events on the same stream around each launch. A
+    # spin kernel of about a millisecond goes first, so that the host has
+    # queued the whole pass before the GPU reaches it: each event pair then
+    # brackets its launch's execution and not the host's time to issue it.
     stages = ["plan"] + [f"{n}[{r}]" for r in range(R)
                          for n in ("dispatch", "gate_up", "down")] + ["combine"]
     tot = {n: 0.0 for n in stages}
     for it in range(args.kernel_steps + 2):
         ev = {}
+        torch.cuda._sleep(SPIN_CYCLES)
 
         def timed(name, fn):
             e0 = torch.cuda.Event(enable_timing=True)

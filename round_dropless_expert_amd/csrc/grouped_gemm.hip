@@ -216,6 +216,9 @@ struct TileSmall {   // 128 x 64, two K stages per slot: rounds of a few
   static constexpr float kEff = 0.45f;
 };
 
+// Cache-policy operand of a buffer store: non-temporal (streaming).
+constexpr int kNonTemporal = 2;
+
 // Offset that puts a buffer load out of range: the load returns zeros and
 // touches no memory (every real offset is below 2^31).
 constexpr uint32_t kOutOfRange = 0x80000000u;
@@ -574,7 +577,10 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
             // rows c >= m fall past the descriptor's range
             const uint32_t off =
                 feat < p.N ? ((uint32_t)(cb + r) * p.N + feat) * kEs : kOutOfRange;
-            __builtin_amdgcn_raw_buffer_store_b128(v, rz, off, 0, 0);
+            // non-temporal: z is next read by the combine, after every
+            // round, so its lines should not displace the operands that
+            // the following tiles fetch through L2
+            __builtin_amdgcn_raw_buffer_store_b128(v, rz, off, 0, kNonTemporal);
           }
         }
       }
