@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--group", type=int, default=1,
                     help="experts per capacity group (1 = each expert keeps "
                          "its own capacity)")
+    ap.add_argument("--round-buffers", type=int, default=1, choices=(1, 2),
+                    help="sets of round buffers: 2 overlaps consecutive rounds "
+                         "(odd rounds on a second stream)")
     ap.add_argument("--weights", choices=("tiled", "row_major"), default="tiled",
                     help="expert weight layout the layer reads (tiled = packed "
                          "once by moe_pack_weights before timing)")
@@ -153,7 +156,7 @@ def main():
     x, wg_rm, wu_rm, wd_rm = up(inp.x), up(inp.Wg), up(inp.Wu), up(inp.Wd)
     layout = args.weights
     cfg = B.config(w.T, w.E, w.k, w.d_model, w.d_ff, w.C, w.dtype, layout,
-                   args.group)
+                   args.group, args.round_buffers)
     if layout == "tiled":
         # one-time repack at load time, outside the timed region
         wg, wu, wd = (torch.empty_like(t) for t in (wg_rm, wu_rm, wd_rm))
@@ -296,6 +299,7 @@ def main():
         "config": {"workload": w.name, "T": w.T, "d_model": w.d_model,
                    "d_ff": w.d_ff, "E": w.E, "k": w.k, "C": w.C,
                    "weight_layout": layout, "group": args.group,
+                   "round_buffers": args.round_buffers,
                    "skew": list(w.skew), "rounds": R,
                    "rows_per_round": A.tolist()},
         "grouped_gemm_mfma_util_pct": 100.0 * gemm_util,

@@ -98,6 +98,9 @@ typedef struct {
   int32_t dtype;         /* moe_dtype_t of x, weights and y */
   int32_t weight_layout; /* moe_weight_layout_t of the expert weights */
   int32_t group;         /* G: experts per capacity group (0 means 1) */
+  int32_t round_buffers; /* S: sets of round buffers, 1 or 2 (0 means 1);
+                            round r uses set r % S. With 2, moe_forward
+                            overlaps consecutive rounds (see there) */
 } moe_config_t;
 
 /* Tiled layout. A matrix with R rows (R padded up to a multiple of 64) and
@@ -133,7 +136,8 @@ typedef struct {
  *                            experts of e's group in round r; the same
  *                            with each expert's rows rounded up to 64
  *                            (rows r >= R are unused)
- *   xr       elem [E/G][Q][d] round buffer of gathered token rows: Q = P
+ *   xr       elem [S][E/G][Q][d] round buffers of gathered token rows (set
+ *                            r % S for round r): Q = P
  *                            (G = 1) or G*(P+64) rows per group, P = C'
  *                            rounded up to a multiple of 64. In round r
  *                            expert e's rows start at row (padded rounds
@@ -141,7 +145,7 @@ typedef struct {
  *                            m(r,e) x d matrix in the tiled layout (its
  *                            slot c is row c; rows up to the next multiple
  *                            of 64 hold stale data)
- *   h        elem [E/G][Q][f] SwiGLU activations of the round, same layout
+ *   h        elem [S][E/G][Q][f] SwiGLU activations of the round, same layout
  *   z        elem [T*k][d]   unweighted expert output of every assignment,
  *                            in expert-sorted order: row i holds the output
  *                            of assignment perm[i] (so assignment a's row
@@ -169,7 +173,7 @@ int32_t moe_hip_runtime_version(void);
 moe_status_t moe_check_config(const moe_config_t *cfg);
 
 /* Workspace bytes for a config: a pure host function, no HIP call. The size
- * depends on (T, E, k, d, f, C, dtype) only, never on routing -- the fixed
+ * depends on (T, E, k, d, f, C, dtype, G, S) only, never on routing -- the fixed
  * memory of the method ("Expert groups keep memory fixed when tokens pile
  * up"). */
 moe_status_t moe_workspace_size(const moe_config_t *cfg, size_t *bytes);
@@ -253,8 +257,14 @@ moe_status_t moe_combine(const moe_config_t *cfg, const void *ws,
  * Returns after enqueueing the combine (the plan's wait is the only host
  * synchronisation; round 0's dispatch is queued before it). For that read
  * the library keeps, per calling thread and device, a pinned host buffer of
- * 65 int32, a side stream of default priority that does the copy, and two
- * events, created on first use. The result does not depend on C. */
+ * 65 int32, a side stream of default priority that does the copy, and three
+ * events, created on first use. With S = 2 the rounds overlap as the method
+ * overlaps dispatch with compute ("Frontier Pre-training at Microsoft AI
+ * (MAI-Base-2)", section "Key claims"): odd rounds run on the side stream with buffer set 1, even rounds
+ * on the caller's stream with set 0 (round 1's dispatch is also queued
+ * before the wait), and the caller's stream waits for the side stream
+ * before the combine, so the caller still sees one stream's order. The
+ * result does not depend on C, G or S. */
 moe_status_t moe_forward(const moe_config_t *cfg, const float *logits,
                          const void *x, const void *w_gate, const void *w_up,
                          const void *w_down, void *y, void *ws,

@@ -40,7 +40,7 @@ class MoeConfig(ctypes.Structure):
                 ("k", ctypes.c_int32), ("d_model", ctypes.c_int32),
                 ("d_ff", ctypes.c_int32), ("C", ctypes.c_int64),
                 ("dtype", ctypes.c_int32), ("weight_layout", ctypes.c_int32),
-                ("group", ctypes.c_int32)]
+                ("group", ctypes.c_int32), ("round_buffers", ctypes.c_int32)]
 
 
 LAYOUT_FIELDS = ("idx", "weight", "counts", "offsets", "n_rounds", "perm",
@@ -121,8 +121,10 @@ def _check(status: int) -> None:
 
 
 def config(T, E, k, d_model, d_ff, C, dtype,
-           weight_layout=MOE_WEIGHTS_ROW_MAJOR, group=1) -> MoeConfig:
-    """group: experts per capacity group (1 = strict per-expert capacity)."""
+           weight_layout=MOE_WEIGHTS_ROW_MAJOR, group=1,
+           round_buffers=1) -> MoeConfig:
+    """group: experts per capacity group (1 = strict per-expert capacity);
+    round_buffers: 1, or 2 to overlap consecutive rounds in moe_forward."""
     if isinstance(dtype, str):
         dtype = {"f32": MOE_F32, "bf16": MOE_BF16}[dtype]
     elif isinstance(dtype, torch.dtype):
@@ -131,19 +133,22 @@ def config(T, E, k, d_model, d_ff, C, dtype,
         weight_layout = {"row_major": MOE_WEIGHTS_ROW_MAJOR,
                          "tiled": MOE_WEIGHTS_TILED}[weight_layout]
     return MoeConfig(int(T), int(E), int(k), int(d_model), int(d_ff), int(C),
-                     int(dtype), int(weight_layout), int(group))
+                     int(dtype), int(weight_layout), int(group),
+                     int(round_buffers))
 
 
 def buffer_geometry(cfg: MoeConfig) -> dict:
     """Round-buffer geometry: C' = min(C, T), P = C' rounded up to 64, the
     group size G, rows per group Q (P for G = 1, else G*(P+64)), the rows of
-    the whole buffer and the rows M of each round table."""
+    one set of round buffers, the number of sets S (round r uses set r % S)
+    and the rows M of each round table."""
     ce = min(cfg.C, cfg.T)
     pad = (ce + 63) // 64 * 64
     G = cfg.group if cfg.group > 0 else 1
     Q = pad if G == 1 else G * (pad + 64)
+    S = cfg.round_buffers if cfg.round_buffers > 0 else 1
     return {"ce": ce, "pad": pad, "G": G, "Q": Q, "rows": (cfg.E // G) * Q,
-            "M": -(-cfg.T // ce)}
+            "S": S, "M": -(-cfg.T // ce)}
 
 
 def check_config(cfg: MoeConfig) -> int:
@@ -253,14 +258,14 @@ def moe_forward(cfg, logits, x, w_gate, w_up, w_down, y, ws, stream=None):
 
 def workspace_views(cfg: MoeConfig, ws: torch.Tensor) -> dict:
     """torch views of the internal buffers of a uint8 workspace tensor.
-    xr and h are returned as raw bytes of the whole round buffer (rows of
-    d (f) elements in the tiled layout, see buffer_geometry); rounds is
+    xr and h are returned as raw bytes of all sets of the round buffer (rows
+    of d (f) elements in the tiled layout, see buffer_geometry); rounds is
     [4, M, E]: rows, first index, rows of the group's lower experts, and
     the same padded to 64."""
     L = workspace_layout(cfg)
     T, E, k = cfg.T, cfg.E, cfg.k
     geo = buffer_geometry(cfg)
-    rows, M = geo["rows"], geo["M"]
+    rows, M = geo["rows"] * geo["S"], geo["M"]
     el = torch.bfloat16 if cfg.dtype == MOE_BF16 else torch.float32
     es = 2 if cfg.dtype == MOE_BF16 else 4
 

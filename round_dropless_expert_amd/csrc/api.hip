@@ -41,6 +41,11 @@ int64_t eff_capacity(const moe_config_t* c) { return c->C < c->T ? c->C : c->T; 
 
 int group_of(const moe_config_t* c) { return c->group == 0 ? 1 : c->group; }
 
+// Sets of round buffers (xr, h): round r uses set r % sets.
+int sets_of(const moe_config_t* c) {
+  return c->round_buffers == 0 ? 1 : c->round_buffers;
+}
+
 moe::Shape shape_of(const moe_config_t* c) {
   return moe::Shape{c->T,       c->E, c->k, c->d_model, c->d_ff, (int)eff_capacity(c),
                     c->dtype == MOE_BF16, c->weight_layout == MOE_WEIGHTS_TILED,
@@ -64,6 +69,8 @@ moe_status_t check_cfg(const moe_config_t* c) {
     return fail(MOE_ERR_INVALID_ARGUMENT, "unknown weight layout");
   if (c->group < 0 || (c->group > 0 && c->E % c->group != 0))
     return fail(MOE_ERR_INVALID_ARGUMENT, "group must divide E (0 means 1)");
+  if (c->round_buffers < 0 || c->round_buffers > 2)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "round_buffers must be 0, 1 or 2");
   if (c->E > kMaxExperts) return fail(MOE_ERR_UNSUPPORTED, "E > 64 is not supported");
   if (c->d_model % 64 || c->d_ff % 64)
     return fail(MOE_ERR_UNSUPPORTED, "d_model and d_ff must be multiples of 64");
@@ -108,8 +115,9 @@ void layout_of(const moe_config_t* c, moe_workspace_layout_t* L) {
   L->row_of = take(TK * 4);
   L->rounds = take(4 * (size_t)s.max_rounds() * E * 4);
   L->scratch = take((size_t)moe::plan_scratch_ints(s) * 4);
-  L->xr = take((size_t)s.buf_rows() * (size_t)c->d_model * es);
-  L->h = take((size_t)s.buf_rows() * (size_t)c->d_ff * es);
+  const size_t sets = (size_t)sets_of(c);
+  L->xr = take(sets * (size_t)s.buf_rows() * (size_t)c->d_model * es);
+  L->h = take(sets * (size_t)s.buf_rows() * (size_t)c->d_ff * es);
   L->z = take(TK * (size_t)c->d_model * es);
   L->total = off;
 }
@@ -119,6 +127,14 @@ struct Bound {
   moe_workspace_layout_t L;
   char* ws;
   moe::PlanBuffers pb;
+  int sets;  // round-buffer sets
+  // round r's set of the round buffers
+  char* xr(int r) const {
+    return ws + L.xr + (size_t)(r % sets) * (size_t)s.buf_rows() * s.d * (s.bf16 ? 2 : 4);
+  }
+  char* h(int r) const {
+    return ws + L.h + (size_t)(r % sets) * (size_t)s.buf_rows() * s.f * (s.bf16 ? 2 : 4);
+  }
 };
 
 moe_status_t bind(const moe_config_t* c, void* ws, size_t ws_bytes, Bound* b) {
@@ -131,6 +147,7 @@ moe_status_t bind(const moe_config_t* c, void* ws, size_t ws_bytes, Bound* b) {
   if (ws_bytes < b->L.total)
     return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace too small");
   b->s = shape_of(c);
+  b->sets = sets_of(c);
   b->ws = static_cast<char*>(ws);
   char* w = b->ws;
   const moe_workspace_layout_t& L = b->L;
@@ -193,6 +210,7 @@ struct PlanReadback {
   hipStream_t side = nullptr;
   hipEvent_t planned = nullptr;
   hipEvent_t done = nullptr;
+  hipEvent_t joined = nullptr;  // the side stream's rounds are done
 };
 thread_local PlanReadback g_readback[64];
 
@@ -218,6 +236,10 @@ moe_status_t plan_readback(PlanReadback** out) {
   }
   if (!r.done) {
     e = hipEventCreateWithFlags(&r.done, hipEventDisableTiming);
+    if (e != hipSuccess) return hip_fail(e, "hipEventCreateWithFlags");
+  }
+  if (!r.joined) {
+    e = hipEventCreateWithFlags(&r.joined, hipEventDisableTiming);
     if (e != hipSuccess) return hip_fail(e, "hipEventCreateWithFlags");
   }
   *out = &r;
@@ -248,10 +270,10 @@ moe_status_t read_plan(const Bound& b, int32_t* out, hipStream_t st) {
 moe_status_t run_ffn(const Bound& b, int r, const void* wg, const void* wu,
                      const void* wd, const int32_t* rows_host, int cus,
                      hipStream_t st) {
-  MOE_HIP(moe::launch_gate_up(b.s, r, b.ws + b.L.xr, wg, wu, b.pb, rows_host,
-                              b.ws + b.L.h, cus, st),
+  MOE_HIP(moe::launch_gate_up(b.s, r, b.xr(r), wg, wu, b.pb, rows_host, b.h(r),
+                              cus, st),
           "gate/up launch");
-  MOE_HIP(moe::launch_down(b.s, r, b.ws + b.L.h, wd, b.pb, rows_host,
+  MOE_HIP(moe::launch_down(b.s, r, b.h(r), wd, b.pb, rows_host,
                            b.ws + b.L.z, cus, st),
           "down launch");
   return MOE_OK;
@@ -332,7 +354,7 @@ moe_status_t moe_dispatch(const moe_config_t* cfg, int32_t round, const void* x,
   if ((st = check_round(b, round)) != MOE_OK) return st;
   int cus = 0;
   if ((st = num_cus(&cus)) != MOE_OK) return st;
-  MOE_HIP(moe::launch_dispatch(b.s, round, x, b.pb, b.ws + b.L.xr, cus,
+  MOE_HIP(moe::launch_dispatch(b.s, round, x, b.pb, b.xr(round), cus,
                                static_cast<hipStream_t>(stream)),
           "dispatch launch");
   return MOE_OK;
@@ -370,9 +392,9 @@ moe_status_t moe_expert_gate_up(const moe_config_t* cfg, int32_t round,
   int cus = 0;
   if ((st = num_cus(&cus)) != MOE_OK) return st;
   int32_t rows[kMaxExperts];
-  MOE_HIP(moe::launch_gate_up(b.s, round, b.ws + b.L.xr, w_gate, w_up, b.pb,
+  MOE_HIP(moe::launch_gate_up(b.s, round, b.xr(round), w_gate, w_up, b.pb,
                               rows_from_counts(b.s, counts_host, round, rows),
-                              b.ws + b.L.h, cus, static_cast<hipStream_t>(stream)),
+                              b.h(round), cus, static_cast<hipStream_t>(stream)),
           "gate/up launch");
   return MOE_OK;
 }
@@ -388,7 +410,7 @@ moe_status_t moe_expert_down(const moe_config_t* cfg, int32_t round,
   int cus = 0;
   if ((st = num_cus(&cus)) != MOE_OK) return st;
   int32_t rows[kMaxExperts];
-  MOE_HIP(moe::launch_down(b.s, round, b.ws + b.L.h, w_down, b.pb,
+  MOE_HIP(moe::launch_down(b.s, round, b.h(round), w_down, b.pb,
                            rows_from_counts(b.s, counts_host, round, rows),
                            b.ws + b.L.z, cus, static_cast<hipStream_t>(stream)),
           "down launch");
@@ -467,25 +489,39 @@ moe_status_t moe_forward(const moe_config_t* cfg, const float* logits,
                          hipMemcpyDeviceToHost, rb->side),
           "read of counts and R");
   MOE_HIP(hipEventRecord(rb->done, rb->side), "hipEventRecord");
-  MOE_HIP(moe::launch_dispatch(b.s, 0, x, b.pb, b.ws + b.L.xr, cus, s),
-          "dispatch launch");
+  MOE_HIP(moe::launch_dispatch(b.s, 0, x, b.pb, b.xr(0), cus, s), "dispatch launch");
+  // With two sets of round buffers the odd rounds run on the side stream
+  // (set 1) and the even rounds on the caller's (set 0): consecutive rounds
+  // use different buffers, so the dispatch of round r + 1 and the expert
+  // compute of round r overlap, and each stream keeps its own rounds in
+  // order. Round 1's dispatch is queued before the wait as well; with R = 1
+  // it finds no assignment of round 1 and moves nothing.
+  const int64_t max_rounds = (b.s.T + b.s.ce - 1) / b.s.ce;
+  const bool two = b.sets == 2 && max_rounds >= 2;
+  if (two)
+    MOE_HIP(moe::launch_dispatch(b.s, 1, x, b.pb, b.xr(1), cus, rb->side),
+            "dispatch launch");
   MOE_HIP(hipEventSynchronize(rb->done), "wait for the plan");
   int32_t counts_r[kMaxExperts + 1];
   std::memcpy(counts_r, rb->host, (b.s.E + 1) * sizeof(int32_t));
   const int32_t R = counts_r[b.s.E];
-  const int64_t max_rounds = (b.s.T + b.s.ce - 1) / b.s.ce;
   if (R < 1 || R > max_rounds)
     return fail(MOE_ERR_HIP, "device plan reported an impossible round count");
   int64_t rem[kMaxExperts];
   for (int e = 0; e < b.s.E; ++e) rem[e] = counts_r[e];
   int32_t rows[kMaxExperts];
   for (int r = 0; r < R; ++r) {
-    if (r > 0)
-      MOE_HIP(moe::launch_dispatch(b.s, r, x, b.pb, b.ws + b.L.xr, cus, s),
+    hipStream_t sr = two && (r & 1) ? rb->side : s;
+    if (r > (two ? 1 : 0))
+      MOE_HIP(moe::launch_dispatch(b.s, r, x, b.pb, b.xr(r), cus, sr),
               "dispatch launch");
     moe::host_next_round(b.s, rem, rows);
-    if ((st = run_ffn(b, r, w_gate, w_up, w_down, rows, cus, s)) != MOE_OK)
+    if ((st = run_ffn(b, r, w_gate, w_up, w_down, rows, cus, sr)) != MOE_OK)
       return st;
+  }
+  if (two) {  // the combine reads z rows of every round
+    MOE_HIP(hipEventRecord(rb->joined, rb->side), "hipEventRecord");
+    MOE_HIP(hipStreamWaitEvent(s, rb->joined, 0), "hipStreamWaitEvent");
   }
   MOE_HIP(moe::launch_combine(b.s, b.ws + b.L.z, b.pb.weight, b.pb.pos, y, cus, s),
           "combine launch");

@@ -44,10 +44,11 @@ class Case:
         self.wd = up(self.inp.Wd)
         self.idx, self.wt = oracle.route(self.inp.logits, w.k)
 
-    def cfg(self, C=None, weight_layout="tiled", group=1):
+    def cfg(self, C=None, weight_layout="tiled", group=1, round_buffers=1):
         w = self.w
         return B.config(w.T, w.E, w.k, w.d_model, w.d_ff,
-                        w.C if C is None else C, w.dtype, weight_layout, group)
+                        w.C if C is None else C, w.dtype, weight_layout, group,
+                        round_buffers)
 
     def weights(self, layout="tiled"):
         """(w_gate, w_up, w_down) on the device in the given layout."""
@@ -126,11 +127,13 @@ def assert_plan_equal(views: dict, p: oracle.Plan, idx: np.ndarray):
 def expert_rows(views: dict, cfg, r: int, e: int, m: int, cols: int, dtype,
                 buf: str = "xr") -> torch.Tensor:
     """Rows 0..m-1 of expert e's matrix of round r in the xr (or h) round
-    buffer: it starts at row (e // G) * Q + pbase(r, e), padded to 64."""
+    buffer: in set r % S it starts at row (e // G) * Q + pbase(r, e), padded
+    to 64."""
     geo = B.buffer_geometry(cfg)
     es = torch.empty(0, dtype=dtype).element_size()
     rb = cols * es
-    start = (e // geo["G"]) * geo["Q"] + int(views["rounds"][3, r, e].item())
+    start = (r % geo["S"]) * geo["rows"] + (e // geo["G"]) * geo["Q"] + \
+        int(views["rounds"][3, r, e].item())
     rows = (m + 63) // 64 * 64
     seg = views[buf][start * rb:(start + rows) * rb]
     return untile(seg, rows, cols, dtype)[:m]

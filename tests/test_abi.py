@@ -50,7 +50,7 @@ def ceil_div(a, b):
     return -(-a // b)
 
 
-def expected_total(T, E, k, d, f, C, es, G=1):
+def expected_total(T, E, k, d, f, C, es, G=1, S=1):
     al = lambda v: (v + 255) // 256 * 256
     ce = min(C, T)
     pad = ceil_div(ce, 64) * 64  # round-buffer rows per expert, tiled
@@ -61,7 +61,7 @@ def expected_total(T, E, k, d, f, C, es, G=1):
     nb = ceil_div(T, 8) + ceil_div(T, 256)  # plan histogram rows, chunk sums
     # counts and R share one block: [E counts][R]
     parts = [TK * 4, TK * 4, (E + 1) * 4, (E + 1) * 4, TK * 4, TK * 4, TK * 4,
-             TK * 4, 4 * M * E * 4, nb * E * 4, rows * d * es, rows * f * es,
+             TK * 4, 4 * M * E * 4, nb * E * 4, S * rows * d * es, S * rows * f * es,
              TK * d * es]
     return sum(al(p) for p in parts)
 
@@ -101,12 +101,24 @@ def test_workspace_is_a_function_of_the_config_only(B):
         n = B.workspace_size(B.config(w.T, w.E, w.k, w.d_model, w.d_ff, w.C,
                                       "bf16", group=G))
         assert n == expected_total(w.T, w.E, w.k, w.d_model, w.d_ff, w.C, 2, G)
+    # two sets of round buffers: one more xr and h; 0 means 1
+    for G in (1, 4):
+        one = B.workspace_size(B.config(w.T, w.E, w.k, w.d_model, w.d_ff, w.C,
+                                        "bf16", group=G, round_buffers=0))
+        two = B.workspace_size(B.config(w.T, w.E, w.k, w.d_model, w.d_ff, w.C,
+                                        "bf16", group=G, round_buffers=2))
+        assert two == expected_total(w.T, w.E, w.k, w.d_model, w.d_ff, w.C, 2,
+                                     G, 2)
+        geo = B.buffer_geometry(B.config(w.T, w.E, w.k, w.d_model, w.d_ff,
+                                         w.C, "bf16", group=G))
+        assert two - one == geo["rows"] * (w.d_model + w.d_ff) * 2
 
 
 BAD_CONFIGS = [
     (dict(T=0), 1), (dict(E=0), 1), (dict(k=0), 1), (dict(k=9), 1),
     (dict(C=0), 1), (dict(d_model=0), 1), (dict(dtype=7), 1),
     (dict(weight_layout=2), 1), (dict(group=3), 1), (dict(group=-1), 1),
+    (dict(round_buffers=3), 1), (dict(round_buffers=-1), 1),
     (dict(E=65, k=2), 2), (dict(d_model=96), 2), (dict(d_ff=100), 2),
     (dict(T=1 << 29, k=4), 2),
 ]
@@ -115,7 +127,7 @@ BAD_CONFIGS = [
 @pytest.mark.parametrize("change,status", BAD_CONFIGS)
 def test_config_validation(B, change, status):
     base = dict(T=512, E=8, k=2, d_model=64, d_ff=128, C=64, dtype=0,
-                weight_layout=0, group=1)
+                weight_layout=0, group=1, round_buffers=1)
     base.update(change)
     cfg = B.config(**base)
     assert B.check_config(cfg) == status

@@ -23,12 +23,13 @@ def get_case(name):
     return _cache[name]
 
 
-def forward(case, C=None, poison=True, layout="tiled", group=1):
-    cfg = case.cfg(C, weight_layout=layout, group=group)
+def forward(case, C=None, poison=True, layout="tiled", group=1, sets=1):
+    cfg = case.cfg(C, weight_layout=layout, group=group, round_buffers=sets)
     wg, wu, wd = case.weights(layout)
     ws = case.workspace(cfg, poison=poison)
     y = case.new_y()
-    note(f"{case.w.name}: moe_forward C={cfg.C} G={group} weights={layout}")
+    note(f"{case.w.name}: moe_forward C={cfg.C} G={group} S={sets} "
+         f"weights={layout}")
     B.moe_forward(cfg, case.logits, case.x, wg, wu, wd, y, ws)
     torch.cuda.synchronize()
     return cfg, ws, y
@@ -131,6 +132,33 @@ def test_capacity_groups_match_oracle_and_are_bit_identical(name, groups):
         assert_plan_equal(B.workspace_views(cfg, ws), p, case.idx)
         assert torch.equal(ref, y.view(ib)), f"G={G} differs from G=1"
         assert torch.isfinite(B.workspace_views(cfg, ws)["z"].float()).all()
+        del ws, y
+        torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name", list(configs.WORKLOADS))
+def test_two_round_buffer_sets_are_bit_identical(name):
+    """Overlapping consecutive rounds (odd rounds on a second stream with a
+    second set of round buffers) changes nothing in the output, alone and
+    with capacity groups; twice in a row, since the side stream carries
+    over between calls."""
+    case = get_case(name)
+    w = case.w
+    ib = torch.int16 if w.dtype == "bf16" else torch.int32
+    _, _, y1 = forward(case, poison=False)
+    ref = y1.view(ib).clone()
+    del y1
+    for G in (1, 2):
+        cfg, ws, y = forward(case, group=G, sets=2)
+        assert torch.equal(ref, y.view(ib)), f"S=2 G={G} differs from S=1"
+        p = oracle.plan_groups(case.idx, w.E, w.C, G)
+        assert_plan_equal(B.workspace_views(cfg, ws), p, case.idx)
+        assert torch.isfinite(B.workspace_views(cfg, ws)["z"].float()).all()
+        y.fill_(float("nan"))
+        note(f"{name}: moe_forward S=2 G={G} again")
+        B.moe_forward(cfg, case.logits, case.x, *case.weights(), y, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(ref, y.view(ib)), f"S=2 G={G} second call"
         del ws, y
         torch.cuda.empty_cache()
 

@@ -40,23 +40,28 @@ STAGE_CASES = [
 ]
 
 
-# (workload, capacity group size) for the stage tests; group > 1 shares the
-# capacity of each group of experts
-GROUP_CASES = [(w, 1) for w in STAGE_CASES] + [
-    (STAGE_CASES[2], 2), (STAGE_CASES[2], 6), (STAGE_CASES[3], 5),
-    (STAGE_CASES[4], 5), (STAGE_CASES[6], 4), (STAGE_CASES[1], 8)]
+# (workload, capacity group size G, round-buffer sets S) for the stage
+# tests; G > 1 shares the capacity of each group of experts, S = 2 puts odd
+# rounds in a second set of round buffers
+GROUP_CASES = [(w, 1, 1) for w in STAGE_CASES] + [
+    (STAGE_CASES[2], 2, 1), (STAGE_CASES[2], 6, 1), (STAGE_CASES[3], 5, 1),
+    (STAGE_CASES[4], 5, 1), (STAGE_CASES[6], 4, 1), (STAGE_CASES[1], 8, 1),
+    (STAGE_CASES[0], 1, 2), (STAGE_CASES[1], 1, 2), (STAGE_CASES[2], 2, 2)]
+
+
+def _case_id(v):
+    return v.name if hasattr(v, "name") else str(v)
 
 
 @pytest.mark.parametrize("layout", ["tiled", "row_major"])
-@pytest.mark.parametrize("w,G", GROUP_CASES,
-                         ids=lambda v: v.name if hasattr(v, "name") else f"G{v}")
-def test_stages_match_oracle(w, G, layout):
+@pytest.mark.parametrize("w,G,S", GROUP_CASES, ids=_case_id)
+def test_stages_match_oracle(w, G, S, layout):
     torch.cuda.synchronize()
     case = Case(w)
-    cfg = case.cfg(weight_layout=layout, group=G)
+    cfg = case.cfg(weight_layout=layout, group=G, round_buffers=S)
     wg, wu, wd = case.weights(layout)
     ws = case.workspace(cfg)
-    note(f"{w.name}/G{G}/{layout}: moe_plan")
+    note(f"{w.name}/G{G}/S{S}/{layout}: moe_plan")
     R, counts = B.moe_plan(cfg, case.logits, ws, return_counts=True)
     views = B.workspace_views(cfg, ws)
     p = oracle.plan_groups(case.idx, w.E, w.C, G)
@@ -72,7 +77,7 @@ def test_stages_match_oracle(w, G, layout):
     dt = el_dtype(w)
     ibits = torch.int16 if w.dtype == "bf16" else torch.int32
     for r in range(R):
-        note(f"{w.name}/G{G}/{layout}: moe_dispatch round {r}")
+        note(f"{w.name}/G{G}/S{S}/{layout}: moe_dispatch round {r}")
         B.moe_dispatch(cfg, r, case.x, ws)
         torch.cuda.synchronize()
         m = p.rows_in_round(r)
@@ -86,7 +91,7 @@ def test_stages_match_oracle(w, G, layout):
         assert torch.equal(xr.view(ibits), case.x[a_t // w.k].view(ibits)), \
             f"xr round {r}"
 
-        note(f"{w.name}/G{G}/{layout}: moe_expert_ffn round {r}")
+        note(f"{w.name}/G{G}/S{S}/{layout}: moe_expert_ffn round {r}")
         B.moe_expert_ffn(cfg, r, wg, wu, wd, ws, counts_host=counts_host)
         torch.cuda.synchronize()
         h_ref, o_ref = oracle.assignment_outputs(
@@ -102,7 +107,7 @@ def test_stages_match_oracle(w, G, layout):
     M = B.buffer_geometry(cfg)["M"]
     if R < M:
         # a round past R computes nothing, whatever its (unset) tables hold
-        note(f"{w.name}/G{G}/{layout}: round {R} of {M} (past R)")
+        note(f"{w.name}/G{G}/S{S}/{layout}: round {R} of {M} (past R)")
         views["rounds"][:, R:] = 1 << 29
         before = [views[n].view(torch.uint8).clone() for n in ("xr", "h", "z")]
         B.moe_dispatch(cfg, R, case.x, ws)
@@ -112,7 +117,7 @@ def test_stages_match_oracle(w, G, layout):
         for n, b in zip(("xr", "h", "z"), before):
             assert torch.equal(views[n].view(torch.uint8), b), n
 
-    note(f"{w.name}/G{G}/{layout}: moe_combine")
+    note(f"{w.name}/G{G}/S{S}/{layout}: moe_combine")
     y = case.new_y()
     B.moe_combine(cfg, ws, y)
     torch.cuda.synchronize()
