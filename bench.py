@@ -55,6 +55,12 @@ def parse():
     ap.add_argument("--round-buffers", type=int, default=1, choices=(1, 2),
                     help="sets of round buffers: 2 overlaps consecutive rounds "
                          "(odd rounds on a second stream)")
+    ap.add_argument("--capacity-curve", action="store_true",
+                    help="instead of the step benchmark: the memory-against-"
+                         "rounds curve of the workload (default hot_expert_bf16)"
+                         " over its capacity sweep and the capacities the "
+                         "helper picks for 1 and 2 rounds, each with its "
+                         "measured ms per moe_forward")
     ap.add_argument("--weights", choices=("tiled", "row_major"), default="tiled",
                     help="expert weight layout the layer reads (tiled = packed "
                          "once by moe_pack_weights before timing)")
@@ -126,10 +132,75 @@ def measured_traffic():
     return float(t.group(1))
 
 
+def capacity_curve(args):
+    """Workspace bytes, rounds and measured time of moe_forward at each
+    capacity of the workload's sweep and at the capacities
+    moe_capacity_for_rounds picks for one and two rounds."""
+    import torch
+
+    from round_dropless_expert_amd import binding as B
+    from round_dropless_expert_amd import configs, synth
+
+    w = configs.WORKLOADS[args.workload or "hot_expert_bf16"]
+    B.load()
+    B.check_runtime()
+    dev = "cuda:0"
+    print(f"[bench] generating {w.name}", file=sys.stderr, flush=True)
+    inp = synth.generate(w)
+    el = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    up = lambda a: torch.from_numpy(a).to(dev).to(el).contiguous()
+    logits = torch.from_numpy(inp.logits).to(dev)
+    x = up(inp.x)
+    cfg0 = B.config(w.T, w.E, w.k, w.d_model, w.d_ff, w.C, w.dtype, "tiled",
+                    args.group, args.round_buffers)
+    rm = [up(inp.Wg), up(inp.Wu), up(inp.Wd)]
+    wts = [torch.empty_like(t) for t in rm]
+    B.moe_pack_weights(cfg0, *rm, *wts)
+    del inp, rm
+    y = torch.empty(w.T, w.d_model, dtype=el, device=dev)
+    ws = torch.empty(B.workspace_size(cfg0), dtype=torch.uint8, device=dev)
+    _, counts = B.moe_plan(cfg0, logits, ws, return_counts=True)
+    del ws
+    picks = {t: B.capacity_for_rounds(cfg0, counts, t) for t in (1, 2)}
+    sweep = w.sweep_C or tuple(min(w.T, max(1, int(w.C * f)))
+                               for f in (0.25, 0.5, 1, 2, 4))
+    caps = sorted(set(list(sweep) + list(picks.values())))
+    rounds, ws_bytes = B.capacity_curve(cfg0, counts, caps)
+    rows = []
+    for i, C in enumerate(caps):
+        cfg = B.config(w.T, w.E, w.k, w.d_model, w.d_ff, C, w.dtype, "tiled",
+                       args.group, args.round_buffers)
+        torch.cuda.empty_cache()
+        ws = torch.empty(int(ws_bytes[i]), dtype=torch.uint8, device=dev)
+        print(f"[bench] C={C}: {int(rounds[i, 0])} rounds, "
+              f"{ws_bytes[i] / 2**30:.2f} GiB", file=sys.stderr, flush=True)
+        for _ in range(2):
+            B.moe_forward(cfg, logits, x, *wts, y, ws)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        n = 5
+        for _ in range(n):
+            B.moe_forward(cfg, logits, x, *wts, y, ws)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / n
+        R = int(B.workspace_views(cfg, ws)["n_rounds"].item())
+        assert R == int(rounds[i, 0]), "helper and plan disagree on R"
+        rows.append({"C": int(C), "rounds": R, "workspace_bytes": int(ws_bytes[i]),
+                     "ms_per_step": ms, "tokens_per_s": w.T / ms * 1e3})
+        del ws
+    print(json.dumps({"capacity_curve": w.name, "group": args.group,
+                      "round_buffers": args.round_buffers,
+                      "picked": {f"{t}_rounds": c for t, c in picks.items()},
+                      "points": rows}), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.capacity_curve:
+        capacity_curve(args)
         return
     if args.gpus != 1:
         print(f"bench.py: this layer runs on one GPU; --gpus {args.gpus} is not "

@@ -182,6 +182,41 @@ moe_status_t moe_workspace_size(const moe_config_t *cfg, size_t *bytes);
 moe_status_t moe_workspace_layout(const moe_config_t *cfg,
                                   moe_workspace_layout_t *out);
 
+/* Capacity tuning ("Microsoft AI's MAI-Base-2 trained on 16K GPUs with
+ * Muon", section "Expert groups keep memory fixed when tokens pile up": a
+ * larger capacity needs more memory and fewer rounds; "Frontier
+ * Pre-training at Microsoft AI (MAI-Base-2)", section "Key claims": the
+ * capacity is tunable). Pure host functions, no HIP call.
+ *
+ * counts: host, n_steps x E int32, row s the per-expert counts n_e of one
+ * observed step (the first E values moe_plan stores in plan_host); every
+ * n_e must lie in [0, T] and each row must sum to T*k, else
+ * MOE_ERR_INVALID_ARGUMENT. The rounds a plan needs at capacity C follow
+ * from the counts alone: a round gives each group of G experts min(left,
+ * G*C') rows (C' = min(C, T)), so R = max over groups of ceil(N_g /
+ * (G*C')) with N_g the group's total (for G = 1, max_e ceil(n_e / C')),
+ * the same R moe_plan reports for that step.
+ *
+ * moe_capacity_curve: for each of the n_capacities values C_i (each must
+ * give a valid config with the other fields of cfg), writes
+ * rounds[i * n_steps + s] = R of step s at C_i and ws_bytes[i] = the
+ * workspace size of cfg with C = C_i: the memory-against-rounds curve.
+ *
+ * moe_capacity_for_rounds: the smallest C such that at least a share
+ * `quantile` (in (0, 1]) of the observed steps needs at most target_rounds
+ * rounds (>= 1): per step the least such C is ceil(max_g N_g / (G *
+ * target_rounds)), at most T; *capacity gets the ceil(quantile *
+ * n_steps)-th smallest of these. quantile = 1 covers every observed step;
+ * target_rounds = 1 gives the steady-state single round. */
+moe_status_t moe_capacity_curve(const moe_config_t *cfg, const int32_t *counts,
+                                int64_t n_steps, const int64_t *capacities,
+                                int32_t n_capacities, int32_t *rounds,
+                                size_t *ws_bytes);
+moe_status_t moe_capacity_for_rounds(const moe_config_t *cfg,
+                                     const int32_t *counts, int64_t n_steps,
+                                     int32_t target_rounds, double quantile,
+                                     int64_t *capacity);
+
 /* Route and plan: every token picks its top-k experts; each expert's
  * assignments are then split into rounds (the capacity per round is fixed:
  * C' per expert, shared inside its group of G; what does not fit waits for

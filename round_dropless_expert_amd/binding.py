@@ -32,7 +32,8 @@ MOE_WEIGHTS_TILED = 1
 EXPORTS = ("moe_status_string", "moe_last_error", "moe_hip_runtime_version",
            "moe_check_config", "moe_workspace_size", "moe_workspace_layout",
            "moe_plan", "moe_dispatch", "moe_expert_ffn", "moe_expert_gate_up",
-           "moe_expert_down", "moe_pack_weights", "moe_combine", "moe_forward")
+           "moe_expert_down", "moe_pack_weights", "moe_combine", "moe_forward",
+           "moe_capacity_curve", "moe_capacity_for_rounds")
 
 
 class MoeConfig(ctypes.Structure):
@@ -93,10 +94,16 @@ def load() -> ctypes.CDLL:
     L.moe_pack_weights.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp]
     L.moe_combine.argtypes = [cfgp, vp, sz, vp, vp]
     L.moe_forward.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    i64, i64p = ctypes.c_int64, ctypes.POINTER(ctypes.c_int64)
+    L.moe_capacity_curve.argtypes = [cfgp, i32p, i64, i64p, i32, i32p,
+                                     ctypes.POINTER(ctypes.c_size_t)]
+    L.moe_capacity_for_rounds.argtypes = [cfgp, i32p, i64, i32, ctypes.c_double,
+                                          i64p]
     for n in ("moe_check_config", "moe_workspace_size", "moe_workspace_layout",
               "moe_plan", "moe_dispatch", "moe_expert_ffn",
               "moe_expert_gate_up", "moe_expert_down", "moe_pack_weights",
-              "moe_combine", "moe_forward"):
+              "moe_combine", "moe_forward", "moe_capacity_curve",
+              "moe_capacity_for_rounds"):
         getattr(L, n).restype = ctypes.c_int
     _lib = L
     return L
@@ -254,6 +261,44 @@ def moe_forward(cfg, logits, x, w_gate, w_up, w_down, y, ws, stream=None):
     _check(load().moe_forward(ctypes.byref(cfg), _ptr(logits), _ptr(x),
                               _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(y),
                               _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def _counts_rows(cfg: MoeConfig, counts):
+    """Observed counts as a C-contiguous int32 [n_steps, E] array."""
+    import numpy as np
+    a = np.ascontiguousarray(np.asarray(counts, dtype=np.int32))
+    if a.ndim == 1:
+        a = a.reshape(1, -1)
+    if a.ndim != 2 or a.shape[1] != cfg.E:
+        raise ValueError(f"counts must be [n_steps, {cfg.E}]")
+    return a
+
+
+def capacity_curve(cfg: MoeConfig, counts, capacities):
+    """(rounds [n_C, n_steps], workspace bytes [n_C]) for each capacity C:
+    the memory-against-rounds curve of the observed steps' counts."""
+    import numpy as np
+    a = _counts_rows(cfg, counts)
+    caps = np.ascontiguousarray(np.asarray(capacities, dtype=np.int64))
+    rounds = np.zeros((caps.size, a.shape[0]), dtype=np.int32)
+    ws = (ctypes.c_size_t * caps.size)()
+    _check(load().moe_capacity_curve(
+        ctypes.byref(cfg), a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+        a.shape[0], caps.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+        caps.size, rounds.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), ws))
+    return rounds, np.array(list(ws), dtype=np.int64)
+
+
+def capacity_for_rounds(cfg: MoeConfig, counts, target_rounds=1,
+                        quantile=1.0) -> int:
+    """Smallest C with at most target_rounds rounds on a share `quantile` of
+    the observed steps."""
+    a = _counts_rows(cfg, counts)
+    out = ctypes.c_int64(0)
+    _check(load().moe_capacity_for_rounds(
+        ctypes.byref(cfg), a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+        a.shape[0], int(target_rounds), float(quantile), ctypes.byref(out)))
+    return out.value
 
 
 def workspace_views(cfg: MoeConfig, ws: torch.Tensor) -> dict:

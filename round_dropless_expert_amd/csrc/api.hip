@@ -10,7 +10,10 @@
 // host reads back only the round count R.
 #include <atomic>
 #include <cstdio>
+#include <algorithm>
+#include <cmath>
 #include <cstring>
+#include <vector>
 
 #include "../../include/moe_rounds.h"
 #include "launch.hpp"
@@ -289,6 +292,42 @@ const int32_t* rows_from_counts(const moe::Shape& s, const int32_t* counts, int 
   return rows;
 }
 
+// Observed counts must be a plan's: every n_e in [0, T] and their sum T*k.
+moe_status_t check_counts(const moe_config_t* c, const int32_t* counts,
+                          int64_t n_steps) {
+  if (!counts) return fail(MOE_ERR_INVALID_ARGUMENT, "counts is NULL");
+  if (n_steps < 1) return fail(MOE_ERR_INVALID_ARGUMENT, "n_steps must be >= 1");
+  for (int64_t s = 0; s < n_steps; ++s) {
+    int64_t sum = 0;
+    for (int e = 0; e < c->E; ++e) {
+      const int64_t n = counts[s * c->E + e];
+      if (n < 0 || n > c->T)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "a count is outside [0, T]");
+      sum += n;
+    }
+    if (sum != c->T * (int64_t)c->k)
+      return fail(MOE_ERR_INVALID_ARGUMENT, "counts of a step do not sum to T*k");
+  }
+  return MOE_OK;
+}
+
+// Rounds of the plan at capacity C for one step's counts: every round gives
+// a group of G experts min(left, G*C') rows (C' = min(C, T)), so R is the
+// largest ceil(N_g / (G*C')) over the groups' totals N_g.
+int64_t rounds_at(const moe_config_t* c, const int32_t* n, int64_t C) {
+  const int64_t ce = C < c->T ? C : c->T;
+  const int64_t G = group_of(c);
+  int64_t R = 0;
+  for (int g0 = 0; g0 < c->E; g0 += (int)G) {
+    int64_t N = 0;
+    for (int e = g0; e < g0 + G; ++e) N += n[e];
+    const int64_t r = (N + G * ce - 1) / (G * ce);
+    R = r > R ? r : R;
+  }
+  return R;
+}
+
+
 }  // namespace
 
 extern "C" {
@@ -321,6 +360,66 @@ moe_status_t moe_workspace_size(const moe_config_t* cfg, size_t* bytes) {
   moe_workspace_layout_t L;
   layout_of(cfg, &L);
   *bytes = L.total;
+  return MOE_OK;
+}
+
+moe_status_t moe_capacity_curve(const moe_config_t* cfg, const int32_t* counts,
+                                int64_t n_steps, const int64_t* capacities,
+                                int32_t n_capacities, int32_t* rounds,
+                                size_t* ws_bytes) {
+  moe_status_t st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if ((st = check_counts(cfg, counts, n_steps)) != MOE_OK) return st;
+  if (!capacities || !rounds || !ws_bytes || n_capacities < 1)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "capacity list or outputs missing");
+  for (int32_t i = 0; i < n_capacities; ++i) {
+    moe_config_t c = *cfg;
+    c.C = capacities[i];
+    if ((st = check_cfg(&c)) != MOE_OK) return st;
+  }
+  for (int32_t i = 0; i < n_capacities; ++i) {
+    moe_config_t c = *cfg;
+    c.C = capacities[i];
+    moe_workspace_layout_t L;
+    layout_of(&c, &L);
+    ws_bytes[i] = L.total;
+    for (int64_t s = 0; s < n_steps; ++s)
+      rounds[i * n_steps + s] = (int32_t)rounds_at(&c, counts + s * cfg->E, c.C);
+  }
+  return MOE_OK;
+}
+
+moe_status_t moe_capacity_for_rounds(const moe_config_t* cfg, const int32_t* counts,
+                                     int64_t n_steps, int32_t target_rounds,
+                                     double quantile, int64_t* capacity) {
+  moe_status_t st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if ((st = check_counts(cfg, counts, n_steps)) != MOE_OK) return st;
+  if (target_rounds < 1 || !capacity || !(quantile > 0.0 && quantile <= 1.0))
+    return fail(MOE_ERR_INVALID_ARGUMENT,
+                "target_rounds >= 1, quantile in (0, 1] and capacity required");
+  // per step: the smallest C with R <= target is ceil(max_g N_g / (G*target))
+  // (R falls as C grows, and C = T always gives one round)
+  const int64_t G = group_of(cfg);
+  std::vector<int64_t> need((size_t)n_steps);
+  for (int64_t s = 0; s < n_steps; ++s) {
+    const int32_t* n = counts + s * cfg->E;
+    int64_t top = 0;
+    for (int g0 = 0; g0 < cfg->E; g0 += (int)G) {
+      int64_t N = 0;
+      for (int e = g0; e < g0 + G; ++e) N += n[e];
+      top = N > top ? N : top;
+    }
+    int64_t C = (top + G * target_rounds - 1) / (G * target_rounds);
+    C = C < 1 ? 1 : (C > cfg->T ? cfg->T : C);
+    need[(size_t)s] = C;
+  }
+  std::sort(need.begin(), need.end());
+  // the ceil(quantile * n_steps)-th smallest: at least that share of the
+  // observed steps fits in target_rounds rounds
+  int64_t rank = (int64_t)std::ceil(quantile * (double)n_steps);
+  rank = rank < 1 ? 1 : (rank > n_steps ? n_steps : rank);
+  *capacity = need[(size_t)(rank - 1)];
   return MOE_OK;
 }
 
