@@ -55,7 +55,14 @@ def lib():
             _i64, _i32, _i32, _i32, _i32, _i64, _i32, _i32p, _f64p, _i32p,
             _i32p, _i32p, _i32p, _i32p, _i32, _i32p, _f32p, _f32p, _f32p,
             _f32p, _f64p, _f64p]
+        L.oracle_backward_tokens.argtypes = [
+            _i64, _i32, _i32, _i32, _i32, _i64, _i64p, _i32p, _f64p, _f32p,
+            _f32p, _f32p, _f32p, _f32p, _f64p, _f64p]
+        L.oracle_weight_grads.argtypes = [
+            _i64, _i32, _i32, _i32, _i32, _i32, _i32p, _f64p, _f32p, _f32p,
+            _f32p, _f32p, _f32p, _f64p, _f64p, _f64p]
         for name in ("oracle_route", "oracle_plan", "oracle_assignment_outputs",
+                     "oracle_backward_tokens", "oracle_weight_grads",
                      "oracle_forward_tokens", "oracle_round_executor",
                      "oracle_plan_groups", "oracle_round_executor_groups",
                      "oracle_max_threads"):
@@ -226,3 +233,37 @@ def round_executor(idx, w, p: Plan, C: int, x, Wg, Wu, Wd):
         p.perm, p.round_of, p.row_of, p.R, _f32(x), _f32(Wg), _f32(Wu),
         _f32(Wd), Z, y), "oracle_round_executor")
     return Z, y
+
+
+def backward_tokens(tokens, idx, w, x, Wg, Wu, Wd, dy):
+    """Gradients of L = sum_t <y_t, dy_t> for a list of tokens: dx [n, d]
+    and dlogits [n, E] (fp64)."""
+    tokens = np.ascontiguousarray(tokens, dtype=np.int64)
+    x, Wg, Wu, Wd, dy = (_f32(a) for a in (x, Wg, Wu, Wd, dy))
+    T, d = x.shape
+    E, f, _ = Wg.shape
+    k = idx.shape[1]
+    n = tokens.size
+    dx = np.empty((n, d), dtype=np.float64)
+    dl = np.empty((n, E), dtype=np.float64)
+    _check(lib().oracle_backward_tokens(
+        T, E, k, d, f, n, tokens, np.ascontiguousarray(idx, dtype=np.int32),
+        np.ascontiguousarray(w, dtype=np.float64), x, Wg, Wu, Wd, dy, dx, dl),
+        "oracle_backward_tokens")
+    return dx, dl
+
+
+def weight_grads(e, idx, w, x, Wg, Wu, Wd, dy):
+    """Weight gradients of expert e: dWg, dWu [f, d] and dWd [d, f] (fp64)."""
+    x, Wg, Wu, Wd, dy = (_f32(a) for a in (x, Wg, Wu, Wd, dy))
+    T, d = x.shape
+    E, f, _ = Wg.shape
+    k = idx.shape[1]
+    dWg = np.empty((f, d), dtype=np.float64)
+    dWu = np.empty((f, d), dtype=np.float64)
+    dWd = np.empty((d, f), dtype=np.float64)
+    _check(lib().oracle_weight_grads(
+        T, E, k, d, f, int(e), np.ascontiguousarray(idx, dtype=np.int32),
+        np.ascontiguousarray(w, dtype=np.float64), x, Wg, Wu, Wd, dy, dWg, dWu,
+        dWd), "oracle_weight_grads")
+    return dWg, dWu, dWd

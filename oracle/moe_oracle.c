@@ -1,5 +1,6 @@
 /*
- * CPU oracle for the multi-round dropless mixture-of-experts layer forward.
+ * CPU oracle for the multi-round dropless mixture-of-experts layer: forward,
+ * and the backward of its plain definition.
  *
  * TEST INFRASTRUCTURE ONLY. Only the test suite, the smoke check and the
  * CPU-baseline leg of the benchmark load this file's library. The HIP
@@ -41,7 +42,10 @@
  * library sort/histogram, closed forms, a library SwiGLU for E = k = 1,
  * bit-identity of the round executors with the per-token loop for every C
  * and group size, a Python simulation of the group fill rule, and
- * hand-worked fixtures).
+ * hand-worked fixtures; for the backward, central finite differences of
+ * the forward for every gradient entry of a small layer, a library
+ * autograd of the SwiGLU FFN for E = k = 1, and router-gradient
+ * identities).
  */
 #include <math.h>
 #include <stdint.h>
@@ -598,5 +602,214 @@ int oracle_round_executor_groups(int64_t T, int32_t E, int32_t k, int32_t d,
   free(Xr);
   free(slot_a);
   free(used);
+  return err;
+}
+
+/* ------------------------------------------------------------------------
+ * Backward of the layer (the gradient of a loss L = sum_t <y_t, dy_t> with
+ * respect to x, the expert weights and the router logits), as the plain
+ * chain rule of the definition above, in fp64. Where the pages are silent
+ * this file reads: the routing selection (top-k) passes no gradient; the k
+ * weights are the softmax of the k chosen logits, so only those logits get
+ * one; the expert FFN is recomputed from x (nothing but the routing and the
+ * unweighted expert outputs is kept from the forward).
+ *
+ * For one assignment (t, j) with expert e and weight w:
+ *   g = x Wg_e^T, u = x Wu_e^T, s = sigmoid(g), a = g s, h = a u,
+ *   o = h Wd_e^T;
+ *   dw_j = <o, dy_t>;  dO = w dy_t;
+ *   dh = dO Wd_e;      dWd_e += dO^T h;
+ *   du = dh a;         dg = dh u s (1 + g (1 - s))   (silu'(g));
+ *   dWg_e += dg^T x;   dWu_e += du^T x;
+ *   dx_t += dg Wg_e + du Wu_e;
+ * and for the token: dlogit(e_j) = w_j (dw_j - sum_j' w_j' dw_j'), every
+ * other logit 0.
+ * ---------------------------------------------------------------------- */
+
+/* The per-assignment recompute and local gradients: fills g, u, a (f) and o
+ * (d) for token row xr through expert weights of e. */
+static void expert_recompute(int32_t d, int32_t f, const double *xr,
+                             const float *Wg_e, const float *Wu_e,
+                             const float *Wd_e, double *g, double *u,
+                             double *a, double *h, double *o) {
+  for (int32_t q = 0; q < f; ++q) {
+    const float *wg = Wg_e + (int64_t)q * d;
+    const float *wu = Wu_e + (int64_t)q * d;
+    double gq = 0.0, uq = 0.0;
+    for (int32_t i = 0; i < d; ++i) {
+      gq += xr[i] * (double)wg[i];
+      uq += xr[i] * (double)wu[i];
+    }
+    g[q] = gq;
+    u[q] = uq;
+    a[q] = gq / (1.0 + exp(-gq));
+    h[q] = a[q] * uq;
+  }
+  for (int32_t m = 0; m < d; ++m) {
+    const float *wd = Wd_e + (int64_t)m * f;
+    double acc = 0.0;
+    for (int32_t q = 0; q < f; ++q) acc += h[q] * (double)wd[q];
+    o[m] = acc;
+  }
+}
+
+/* dh = dO Wd_e, then dg and du from the recomputed g, u, a. */
+static void expert_dgate(int32_t d, int32_t f, const double *dO,
+                         const float *Wd_e, const double *g, const double *u,
+                         const double *a, double *dg, double *du) {
+  for (int32_t q = 0; q < f; ++q) {
+    double dh = 0.0;
+    for (int32_t m = 0; m < d; ++m) dh += dO[m] * (double)Wd_e[(int64_t)m * f + q];
+    const double s = 1.0 / (1.0 + exp(-g[q]));
+    du[q] = dh * a[q];
+    dg[q] = dh * u[q] * s * (1.0 + g[q] * (1.0 - s));
+  }
+}
+
+/* Per-token gradients for a list of tokens: dx [n][d] and dlogits [n][E]. */
+int oracle_backward_tokens(int64_t T, int32_t E, int32_t k, int32_t d,
+                           int32_t f, int64_t n, const int64_t *tokens,
+                           const int32_t *idx, const double *w, const float *x,
+                           const float *Wg, const float *Wu, const float *Wd,
+                           const float *dy, double *dx, double *dlogits) {
+  if (T < 1 || E < 1 || k < 1 || d < 1 || f < 1 || n < 0 || !tokens ||
+      !idx || !w || !x || !Wg || !Wu || !Wd || !dy || !dx || !dlogits)
+    return OR_ERR_ARG;
+  for (int64_t s = 0; s < n; ++s)
+    if (tokens[s] < 0 || tokens[s] >= T) return OR_ERR_ARG;
+  int err = OR_OK;
+#pragma omp parallel
+  {
+    const size_t F = (size_t)f, D = (size_t)d;
+    double *buf = (double *)malloc(sizeof(double) * (6 * F + 3 * D + (size_t)k));
+    if (!buf) {
+#pragma omp atomic write
+      err = OR_ERR_NOMEM;
+    } else {
+      double *g = buf, *u = g + F, *a = u + F, *h = a + F, *dg = h + F,
+             *du = dg + F, *xr = du + F, *o = xr + D, *dO = o + D,
+             *dw = dO + D;
+#pragma omp for schedule(static)
+      for (int64_t s = 0; s < n; ++s) {
+        const int64_t t = tokens[s];
+        double *dxt = dx + s * d;
+        double *dlt = dlogits + s * E;
+        for (int32_t i = 0; i < d; ++i) {
+          xr[i] = (double)x[t * d + i];
+          dxt[i] = 0.0;
+        }
+        for (int32_t e = 0; e < E; ++e) dlt[e] = 0.0;
+        for (int32_t j = 0; j < k; ++j) {
+          const int32_t e = idx[t * k + j];
+          const int64_t wo = (int64_t)e * f * d;
+          const double wj = w[t * k + j];
+          expert_recompute(d, f, xr, Wg + wo, Wu + wo, Wd + wo, g, u, a, h, o);
+          double acc = 0.0;
+          for (int32_t m = 0; m < d; ++m) {
+            acc += o[m] * (double)dy[t * d + m];
+            dO[m] = wj * (double)dy[t * d + m];
+          }
+          dw[j] = acc;
+          expert_dgate(d, f, dO, Wd + wo, g, u, a, dg, du);
+          for (int32_t i = 0; i < d; ++i) {
+            double v = 0.0;
+            for (int32_t q = 0; q < f; ++q)
+              v += dg[q] * (double)Wg[wo + (int64_t)q * d + i] +
+                   du[q] * (double)Wu[wo + (int64_t)q * d + i];
+            dxt[i] += v;
+          }
+        }
+        double mean = 0.0;
+        for (int32_t j = 0; j < k; ++j) mean += w[t * k + j] * dw[j];
+        for (int32_t j = 0; j < k; ++j)
+          dlt[idx[t * k + j]] = w[t * k + j] * (dw[j] - mean);
+      }
+    }
+    free(buf);
+  }
+  return err;
+}
+
+/* Weight gradients of one expert e: dWg_e, dWu_e [f][d] and dWd_e [d][f],
+ * summed over every assignment routed to e. Rows of the outputs are split
+ * over threads; each thread walks all of e's assignments (recomputing
+ * them), so no reduction across threads is needed. */
+int oracle_weight_grads(int64_t T, int32_t E, int32_t k, int32_t d, int32_t f,
+                        int32_t e, const int32_t *idx, const double *w,
+                        const float *x, const float *Wg, const float *Wu,
+                        const float *Wd, const float *dy, double *dWg,
+                        double *dWu, double *dWd) {
+  if (T < 1 || E < 1 || k < 1 || d < 1 || f < 1 || e < 0 || e >= E || !idx ||
+      !w || !x || !Wg || !Wu || !Wd || !dy || !dWg || !dWu || !dWd)
+    return OR_ERR_ARG;
+  const int64_t TK = T * k;
+  int64_t n = 0;
+  for (int64_t a = 0; a < TK; ++a) n += idx[a] == e;
+  int64_t *list = (int64_t *)malloc(sizeof(int64_t) * (size_t)(n > 0 ? n : 1));
+  /* per assignment of e: dO (d), h, dg, du (f), x row (d), kept in fp64 */
+  double *keep = (double *)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1) *
+                                  (size_t)(2 * d + 3 * f));
+  if (!list || !keep) {
+    free(list);
+    free(keep);
+    return OR_ERR_NOMEM;
+  }
+  n = 0;
+  for (int64_t a = 0; a < TK; ++a)
+    if (idx[a] == e) list[n++] = a;
+  const int64_t wo = (int64_t)e * f * d;
+  const int64_t stride = 2 * (int64_t)d + 3 * (int64_t)f;
+  int err = OR_OK;
+#pragma omp parallel
+  {
+    double *buf = (double *)malloc(sizeof(double) * (size_t)(4 * f + d));
+    if (!buf) {
+#pragma omp atomic write
+      err = OR_ERR_NOMEM;
+    } else {
+      double *g = buf, *u = g + f, *a = u + f, *o = a + f;
+#pragma omp for schedule(static)
+      for (int64_t s = 0; s < n; ++s) {
+        const int64_t asg = list[s];
+        const int64_t t = asg / k;
+        double *kp = keep + s * stride;
+        double *xr = kp, *dO = xr + d, *h = dO + d, *dg = h + f, *du = dg + f;
+        for (int32_t i = 0; i < d; ++i) xr[i] = (double)x[t * d + i];
+        expert_recompute(d, f, xr, Wg + wo, Wu + wo, Wd + wo, g, u, a, h, o);
+        for (int32_t m = 0; m < d; ++m) dO[m] = w[asg] * (double)dy[t * d + m];
+        expert_dgate(d, f, dO, Wd + wo, g, u, a, dg, du);
+      }
+    }
+    free(buf);
+  }
+  if (err == OR_OK) {
+    /* sums over e's assignments in ascending assignment order */
+#pragma omp parallel for schedule(static)
+    for (int32_t q = 0; q < f; ++q) {
+      for (int32_t i = 0; i < d; ++i) {
+        double sg = 0.0, su = 0.0;
+        for (int64_t s = 0; s < n; ++s) {
+          const double *kp = keep + s * stride;
+          sg += kp[2 * d + f + q] * kp[i];
+          su += kp[2 * d + 2 * f + q] * kp[i];
+        }
+        dWg[(int64_t)q * d + i] = sg;
+        dWu[(int64_t)q * d + i] = su;
+      }
+    }
+#pragma omp parallel for schedule(static)
+    for (int32_t m = 0; m < d; ++m) {
+      for (int32_t q = 0; q < f; ++q) {
+        double sd = 0.0;
+        for (int64_t s = 0; s < n; ++s) {
+          const double *kp = keep + s * stride;
+          sd += kp[d + m] * kp[2 * d + q];
+        }
+        dWd[(int64_t)m * f + q] = sd;
+      }
+    }
+  }
+  free(list);
+  free(keep);
   return err;
 }
