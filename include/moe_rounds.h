@@ -305,6 +305,73 @@ moe_status_t moe_forward(const moe_config_t *cfg, const float *logits,
                          const void *w_down, void *y, void *ws,
                          size_t ws_bytes, void *stream);
 
+/* ------------------------------------------------------------------------
+ * Backward (bf16 only). The gradient of a loss through y = layer(x, logits,
+ * W), given dy = dL/dy [T][d], with respect to x, the router logits and the
+ * expert weights, computed on the forward's round schedule ("Frontier
+ * Pre-training at Microsoft AI (MAI-Base-2)", section "Key claims": rounds
+ * of dispatch, expert compute and collect with fixed per-round memory; the
+ * backward keeps that memory fixed by recomputing each round's expert
+ * activations from x instead of storing them). Readings: the top-k
+ * selection passes no gradient; the k routing weights are the softmax of
+ * the k chosen logits, so only those logits get a gradient:
+ * dlogits[t][idx[t][j]] = w_j (dw_j - sum_j' w_j' dw_j') with dw_j =
+ * <z[pos[t*k + j]], dy[t]> (z, the forward's unweighted expert outputs);
+ * every other logit 0. Per round r, for expert e's rows c (assignment a,
+ * token t, weight w):
+ *   xr, dyr   gathered rows of x and dy (as moe_dispatch)
+ *   g, u      xr Wg^T, xr Wu^T (recomputed; stored bf16 in gu)
+ *   hw        w * silu(g) u (bf16)
+ *   dh        w * (dyr Wd);  du = dh silu(g);  dg = dh u silu'(g)
+ *   dz[pos[a]] = dg Wg + du Wu  (the assignment's input gradient)
+ *   dW_down[e] += dyr^T hw;  dW_gate[e] += dg^T xr;  dW_up[e] += du^T xr
+ * and finally dx[t] = sum_j dz[pos[t*k + j]] (fp32, j ascending, rounded
+ * once). GEMMs take bf16 operands with fp32 accumulation; the weight
+ * gradients are fp32 and sum an expert's rows round by round. */
+
+/* Byte offsets of the backward workspace's buffers (a pure function of the
+ * config; 256-byte aligned): round buffers xr, dyr [E/G][Q][d], gu, dgu
+ * [E/G][Q][2f], hw [E/G][Q][f] (tiled, as the forward's xr), dz [T*k][d]
+ * (expert-sorted order, as z) and ones [T*k] float. */
+typedef struct {
+  size_t xr, dyr, gu, hw, dgu, dz, ones;
+  size_t total;
+} moe_backward_layout_t;
+
+/* Bytes of the backward workspace (pure host function; MOE_ERR_UNSUPPORTED
+ * for fp32 configs). */
+moe_status_t moe_backward_workspace_size(const moe_config_t *cfg, size_t *bytes);
+moe_status_t moe_backward_layout(const moe_config_t *cfg,
+                                 moe_backward_layout_t *out);
+
+/* The weights the backward's input-gradient GEMMs read, from the row-major
+ * forward weights (w_gate, w_up [E][f][d], w_down [E][d][f], bf16):
+ * out_down_t = w_down transposed to [E][f][d] and out_gate_up_t = [w_gate;
+ * w_up] transposed to [E][d][2f], both in the tiled layout. Call again
+ * whenever the weights change. Asynchronous. */
+moe_status_t moe_pack_backward_weights(const moe_config_t *cfg,
+                                       const void *w_gate, const void *w_up,
+                                       const void *w_down, void *out_down_t,
+                                       void *out_gate_up_t, void *stream);
+
+/* The backward of the layer. ws: the forward's workspace after moe_forward
+ * with the same cfg, logits and x (its plan and z are read, nothing in it
+ * is written). x, w_gate and w_up as given to moe_forward (w_gate/w_up in
+ * cfg->weight_layout); w_down_t and w_gate_up_t from
+ * moe_pack_backward_weights. dy [T][d] bf16. Outputs (written in full): dx
+ * [T][d] bf16, dlogits [T][E] float, dw_gate, dw_up [E][f][d] and dw_down
+ * [E][d][f] float. bws: moe_backward_workspace_size bytes. Waits once for
+ * the forward's counts and R (as moe_forward), then asynchronous on stream.
+ * dx and dlogits do not depend on C or G; the weight gradients' summation
+ * order follows the rounds. */
+moe_status_t moe_backward(const moe_config_t *cfg, const void *x,
+                          const void *w_gate, const void *w_up,
+                          const void *w_down_t, const void *w_gate_up_t,
+                          const void *dy, void *dx, float *dlogits,
+                          float *dw_gate, float *dw_up, float *dw_down,
+                          const void *ws, size_t ws_bytes, void *bws,
+                          size_t bws_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

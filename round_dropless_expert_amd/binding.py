@@ -33,7 +33,9 @@ EXPORTS = ("moe_status_string", "moe_last_error", "moe_hip_runtime_version",
            "moe_check_config", "moe_workspace_size", "moe_workspace_layout",
            "moe_plan", "moe_dispatch", "moe_expert_ffn", "moe_expert_gate_up",
            "moe_expert_down", "moe_pack_weights", "moe_combine", "moe_forward",
-           "moe_capacity_curve", "moe_capacity_for_rounds")
+           "moe_capacity_curve", "moe_capacity_for_rounds",
+           "moe_backward_workspace_size", "moe_backward_layout",
+           "moe_pack_backward_weights", "moe_backward")
 
 
 class MoeConfig(ctypes.Structure):
@@ -51,6 +53,14 @@ LAYOUT_FIELDS = ("idx", "weight", "counts", "offsets", "n_rounds", "perm",
 
 class MoeLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in LAYOUT_FIELDS] + \
+        [("total", ctypes.c_size_t)]
+
+
+BWD_LAYOUT_FIELDS = ("xr", "dyr", "gu", "hw", "dgu", "dz", "ones")
+
+
+class MoeBackwardLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in BWD_LAYOUT_FIELDS] + \
         [("total", ctypes.c_size_t)]
 
 
@@ -99,11 +109,17 @@ def load() -> ctypes.CDLL:
                                      ctypes.POINTER(ctypes.c_size_t)]
     L.moe_capacity_for_rounds.argtypes = [cfgp, i32p, i64, i32, ctypes.c_double,
                                           i64p]
+    L.moe_backward_workspace_size.argtypes = [cfgp, ctypes.POINTER(ctypes.c_size_t)]
+    L.moe_backward_layout.argtypes = [cfgp, ctypes.POINTER(MoeBackwardLayout)]
+    L.moe_pack_backward_weights.argtypes = [cfgp, vp, vp, vp, vp, vp, vp]
+    L.moe_backward.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                               vp, sz, vp, sz, vp]
     for n in ("moe_check_config", "moe_workspace_size", "moe_workspace_layout",
               "moe_plan", "moe_dispatch", "moe_expert_ffn",
               "moe_expert_gate_up", "moe_expert_down", "moe_pack_weights",
               "moe_combine", "moe_forward", "moe_capacity_curve",
-              "moe_capacity_for_rounds"):
+              "moe_capacity_for_rounds", "moe_backward_workspace_size",
+              "moe_backward_layout", "moe_pack_backward_weights", "moe_backward"):
         getattr(L, n).restype = ctypes.c_int
     _lib = L
     return L
@@ -261,6 +277,37 @@ def moe_forward(cfg, logits, x, w_gate, w_up, w_down, y, ws, stream=None):
     _check(load().moe_forward(ctypes.byref(cfg), _ptr(logits), _ptr(x),
                               _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(y),
                               _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def backward_workspace_size(cfg: MoeConfig) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().moe_backward_workspace_size(ctypes.byref(cfg), ctypes.byref(n)))
+    return n.value
+
+
+def backward_layout(cfg: MoeConfig) -> dict:
+    L = MoeBackwardLayout()
+    _check(load().moe_backward_layout(ctypes.byref(cfg), ctypes.byref(L)))
+    return {n: getattr(L, n) for n in BWD_LAYOUT_FIELDS + ("total",)}
+
+
+def moe_pack_backward_weights(cfg, w_gate, w_up, w_down, out_down_t,
+                              out_gate_up_t, stream=None):
+    """Row-major forward weights -> the backward's transposed tiled weights
+    (out_down_t [E][f][d], out_gate_up_t [E][d][2f])."""
+    _check(load().moe_pack_backward_weights(
+        ctypes.byref(cfg), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
+        _ptr(out_down_t), _ptr(out_gate_up_t), _stream(stream)))
+
+
+def moe_backward(cfg, x, w_gate, w_up, w_down_t, w_gate_up_t, dy, dx, dlogits,
+                 dw_gate, dw_up, dw_down, ws, bws, stream=None):
+    """The layer's backward after moe_forward (ws: its workspace)."""
+    _check(load().moe_backward(
+        ctypes.byref(cfg), _ptr(x), _ptr(w_gate), _ptr(w_up), _ptr(w_down_t),
+        _ptr(w_gate_up_t), _ptr(dy), _ptr(dx), _ptr(dlogits), _ptr(dw_gate),
+        _ptr(dw_up), _ptr(dw_down), _ptr(ws), _nbytes(ws), _ptr(bws),
+        _nbytes(bws), _stream(stream)))
 
 
 def _counts_rows(cfg: MoeConfig, counts):

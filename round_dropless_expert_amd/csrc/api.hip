@@ -328,6 +328,38 @@ int64_t rounds_at(const moe_config_t* c, const int32_t* n, int64_t C) {
 }
 
 
+void bwd_layout_of(const moe_config_t* c, moe_backward_layout_t* L) {
+  const moe::Shape s = shape_of(c);
+  const size_t rows = (size_t)s.buf_rows(), d = (size_t)s.d, f = (size_t)s.f;
+  const size_t TK = (size_t)s.T * (size_t)s.k;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += (bytes + 255) / 256 * 256;
+    return o;
+  };
+  L->xr = take(rows * d * 2);
+  L->dyr = take(rows * d * 2);
+  L->gu = take(rows * 2 * f * 2);
+  L->hw = take(rows * f * 2);
+  L->dgu = take(rows * 2 * f * 2);
+  L->dz = take(TK * d * 2);
+  L->ones = take(TK * 4);
+  L->total = off;
+}
+
+moe_status_t check_bwd_cfg(const moe_config_t* c) {
+  moe_status_t st = check_cfg(c);
+  if (st != MOE_OK) return st;
+  if (c->dtype != MOE_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "the backward supports bf16 only");
+  const int64_t ce_pad = (eff_capacity(c) + 63) / 64 * 64;
+  if ((int64_t)group_of(c) * (ce_pad + 64) * 2 * c->d_ff * 2 >= (int64_t(1) << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "G*(C'+64)*2*d_ff*2 must be < 2^31");
+  return MOE_OK;
+}
+
+
 }  // namespace
 
 extern "C" {
@@ -542,6 +574,113 @@ moe_status_t moe_pack_weights(const moe_config_t* cfg, const void* w_gate,
           "pack launch");
   MOE_HIP(moe::launch_pack_weights(s, w_down, out_down, c.d_model, c.d_ff, cus, hs),
           "pack launch");
+  return MOE_OK;
+}
+
+moe_status_t moe_backward_workspace_size(const moe_config_t* cfg, size_t* bytes) {
+  moe_status_t st = check_bwd_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if (!bytes) return fail(MOE_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  moe_backward_layout_t L;
+  bwd_layout_of(cfg, &L);
+  *bytes = L.total;
+  return MOE_OK;
+}
+
+moe_status_t moe_backward_layout(const moe_config_t* cfg, moe_backward_layout_t* out) {
+  moe_status_t st = check_bwd_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if (!out) return fail(MOE_ERR_INVALID_ARGUMENT, "out is NULL");
+  bwd_layout_of(cfg, out);
+  return MOE_OK;
+}
+
+moe_status_t moe_pack_backward_weights(const moe_config_t* cfg, const void* w_gate,
+                                       const void* w_up, const void* w_down,
+                                       void* out_down_t, void* out_gate_up_t,
+                                       void* stream) {
+  moe_status_t st = check_bwd_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if ((st = check_ptr(w_gate, "w_gate")) != MOE_OK) return st;
+  if ((st = check_ptr(w_up, "w_up")) != MOE_OK) return st;
+  if ((st = check_ptr(w_down, "w_down")) != MOE_OK) return st;
+  if ((st = check_ptr(out_down_t, "out_down_t")) != MOE_OK) return st;
+  if ((st = check_ptr(out_gate_up_t, "out_gate_up_t")) != MOE_OK) return st;
+  int cus = 0;
+  if ((st = num_cus(&cus)) != MOE_OK) return st;
+  MOE_HIP(moe::launch_pack_backward(shape_of(cfg), w_gate, w_up, w_down, out_down_t,
+                                    out_gate_up_t, cus, static_cast<hipStream_t>(stream)),
+          "backward pack launch");
+  return MOE_OK;
+}
+
+moe_status_t moe_backward(const moe_config_t* cfg, const void* x, const void* w_gate,
+                          const void* w_up, const void* w_down_t,
+                          const void* w_gate_up_t, const void* dy, void* dx,
+                          float* dlogits, float* dw_gate, float* dw_up, float* dw_down,
+                          const void* ws, size_t ws_bytes, void* bws, size_t bws_bytes,
+                          void* stream) {
+  moe_status_t st = check_bwd_cfg(cfg);
+  if (st != MOE_OK) return st;
+  Bound b;
+  if ((st = bind(cfg, const_cast<void*>(ws), ws_bytes, &b)) != MOE_OK) return st;
+  const void* ptrs[] = {x, w_gate, w_up, w_down_t, w_gate_up_t, dy, dx, dlogits,
+                        dw_gate, dw_up, dw_down, bws};
+  const char* names[] = {"x", "w_gate", "w_up", "w_down_t", "w_gate_up_t", "dy", "dx",
+                         "dlogits", "dw_gate", "dw_up", "dw_down", "bws"};
+  for (int i = 0; i < 12; ++i)
+    if ((st = check_ptr(ptrs[i], names[i])) != MOE_OK) return st;
+  moe_backward_layout_t L;
+  bwd_layout_of(cfg, &L);
+  if (bws_bytes < L.total)
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "backward workspace too small");
+  char* w = static_cast<char*>(bws);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int cus = 0;
+  if ((st = num_cus(&cus)) != MOE_OK) return st;
+  // the forward's counts and R, read once (as in moe_forward)
+  PlanReadback* rb = nullptr;
+  if ((st = plan_readback(&rb)) != MOE_OK) return st;
+  MOE_HIP(hipEventRecord(rb->planned, s), "hipEventRecord");
+  MOE_HIP(hipStreamWaitEvent(rb->side, rb->planned, 0), "hipStreamWaitEvent");
+  MOE_HIP(hipMemcpyAsync(rb->host, b.pb.counts, (b.s.E + 1) * sizeof(int32_t),
+                         hipMemcpyDeviceToHost, rb->side),
+          "read of counts and R");
+  MOE_HIP(hipEventRecord(rb->done, rb->side), "hipEventRecord");
+  // independent of the rounds: the router gradient and the combine weights
+  MOE_HIP(moe::launch_router_backward(b.s, b.ws + b.L.z, dy, b.pb, dlogits, cus, s),
+          "router backward launch");
+  float* ones = reinterpret_cast<float*>(w + L.ones);
+  MOE_HIP(moe::launch_fill(ones, b.s.T * (int64_t)b.s.k, 1.0f, cus, s), "fill launch");
+  MOE_HIP(hipEventSynchronize(rb->done), "wait for the plan");
+  int32_t counts_r[kMaxExperts + 1];
+  std::memcpy(counts_r, rb->host, (b.s.E + 1) * sizeof(int32_t));
+  const int32_t R = counts_r[b.s.E];
+  const int64_t max_rounds = (b.s.T + b.s.ce - 1) / b.s.ce;
+  if (R < 1 || R > max_rounds)
+    return fail(MOE_ERR_HIP, "device plan reported an impossible round count");
+  int64_t rem[kMaxExperts];
+  for (int e = 0; e < b.s.E; ++e) rem[e] = counts_r[e];
+  int32_t rows[kMaxExperts];
+  char *xr = w + L.xr, *dyr = w + L.dyr, *gu = w + L.gu, *hw = w + L.hw,
+       *dgu = w + L.dgu, *dz = w + L.dz;
+  const int d = b.s.d, f = b.s.f;
+  for (int r = 0; r < R; ++r) {
+    moe::host_next_round(b.s, rem, rows);
+    MOE_HIP(moe::launch_dispatch(b.s, r, x, b.pb, xr, cus, s), "dispatch launch");
+    MOE_HIP(moe::launch_dispatch(b.s, r, dy, b.pb, dyr, cus, s), "dispatch launch");
+    MOE_HIP(moe::launch_recompute(b.s, r, xr, w_gate, w_up, b.pb, rows, gu, hw, cus, s),
+            "recompute launch");
+    MOE_HIP(moe::launch_dgate(b.s, r, dyr, w_down_t, b.pb, rows, gu, dgu, cus, s),
+            "dgate launch");
+    MOE_HIP(moe::launch_dx(b.s, r, dgu, w_gate_up_t, b.pb, rows, dz, cus, s),
+            "dx launch");
+    MOE_HIP(moe::launch_wgrad(b.s, r, dyr, hw, d, d, f, dw_down, nullptr, b.pb, rows, s),
+            "wgrad launch");
+    MOE_HIP(moe::launch_wgrad(b.s, r, dgu, xr, 2 * f, f, d, dw_gate, dw_up, b.pb, rows, s),
+            "wgrad launch");
+  }
+  MOE_HIP(moe::launch_combine(b.s, dz, ones, b.pb.pos, dx, cus, s), "combine launch");
   return MOE_OK;
 }
 

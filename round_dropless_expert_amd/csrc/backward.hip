@@ -1,0 +1,147 @@
+// Backward helpers of the layer that are not GEMMs: the router-weight
+// gradient from the unweighted expert outputs z, the one-time packing of the
+// weights the dgrad GEMMs read (transposed, tiled), and a fill.
+//
+// Router (readings: the selection passes no gradient; the k weights are the
+// softmax of the k chosen logits): with dw_j = <z[pos[t*k + j]], dy[t]>,
+// dlogit[t][idx[t][j]] = w_j (dw_j - sum_j' w_j' dw_j'), every other logit
+// of the token 0.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kMaxK = 8;
+
+// One wavefront per token: each lane takes 8-element (16-byte) pieces of
+// the row, k partial dot products, then a butterfly sum over the lanes.
+__global__ __launch_bounds__(256) void router_backward_kernel(
+    const bf16* __restrict__ z, const bf16* __restrict__ dy,
+    const int32_t* __restrict__ pos, const int32_t* __restrict__ idx,
+    const float* __restrict__ weight, int64_t T, int k, int E, int d,
+    float* __restrict__ dlogits) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kWave;
+  const int64_t nwaves = (int64_t)gridDim.x * blockDim.x / kWave;
+  const int nv = d / 8;
+  for (int64_t t = wave; t < T; t += nwaves) {
+    float part[kMaxK];
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) part[j] = 0.f;
+    const bf16x8* dyr = reinterpret_cast<const bf16x8*>(dy + t * (int64_t)d);
+    for (int v = lane; v < nv; v += kWave) {
+      const bf16x8 g = dyr[v];
+#pragma unroll
+      for (int j = 0; j < kMaxK; ++j) {
+        if (j < k) {
+          const int64_t row = pos[t * k + j];
+          const bf16x8 o = reinterpret_cast<const bf16x8*>(z + row * (int64_t)d)[v];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) part[j] = fmaf(to_f32(o[q]), to_f32(g[q]), part[j]);
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j)
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) part[j] += __shfl_xor(part[j], off, kWave);
+    float mean = 0.f;
+    for (int j = 0; j < k; ++j) mean += weight[t * k + j] * part[j];
+    if (lane < E) {
+      float val = 0.f;
+#pragma unroll
+      for (int j = 0; j < kMaxK; ++j)
+        if (j < k && idx[t * k + j] == lane) val = weight[t * k + j] * (part[j] - mean);
+      dlogits[t * E + lane] = val;
+    }
+  }
+}
+
+// out (tiled, [E][rows][cols]) with out_e[i][j] = src_e[j][i], where src_e
+// is src0[e] for j < split and src1[e] (row j - split) otherwise; both
+// sources row-major with `rows` elements per row. Thread -> one 16-byte
+// output piece (i, j0 .. j0+7): eight loads down a source column, adjacent
+// threads taking adjacent i so that each load is contiguous across lanes.
+__global__ __launch_bounds__(256) void pack_transposed_kernel(
+    const bf16* __restrict__ src0, const bf16* __restrict__ src1, int split,
+    int64_t E, int rows, int cols, char* __restrict__ out) {
+  const int64_t per = (int64_t)rows * (cols / 8);
+  const int64_t total = E * per;
+  const int64_t row_bytes = (int64_t)cols * 2;
+  for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < total;
+       g += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t e = g / per;
+    const int64_t w = g - e * per;
+    const int i = (int)(w % rows);
+    const int j0 = (int)(w / rows) * 8;
+    bf16x8 v;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int j = j0 + q;
+      const bf16* src = j < split ? src0 + (e * split + j) * (int64_t)rows
+                                  : src1 + (e * (cols - split) + (j - split)) * (int64_t)rows;
+      v[q] = src[i];
+    }
+    *reinterpret_cast<bf16x8*>(out + e * rows * row_bytes +
+                               tiled_offset(i, (int64_t)j0 * 2, row_bytes)) = v;
+  }
+}
+
+__global__ __launch_bounds__(256) void fill_kernel(float* __restrict__ p, int64_t n,
+                                                   float value) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = value;
+}
+
+int64_t blocks_for(int64_t items, int per_block, int num_cus, int per_cu) {
+  int64_t b = (items + per_block - 1) / per_block;
+  const int64_t cap = (int64_t)num_cus * per_cu;
+  if (b > cap) b = cap;
+  return b < 1 ? 1 : b;
+}
+
+}  // namespace
+
+hipError_t launch_router_backward(const Shape& s, const void* z, const void* dy,
+                                  const PlanBuffers& b, float* dlogits, int num_cus,
+                                  hipStream_t st) {
+  hipLaunchKernelGGL(router_backward_kernel,
+                     dim3((unsigned)blocks_for(s.T, 4, num_cus, 8)), dim3(256), 0, st,
+                     static_cast<const bf16*>(z), static_cast<const bf16*>(dy), b.pos,
+                     b.idx, b.weight, s.T, s.k, s.E, s.d, dlogits);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_backward(const Shape& s, const void* w_gate, const void* w_up,
+                                const void* w_down, void* out_down_t, void* out_gu_t,
+                                int num_cus, hipStream_t st) {
+  // Wd [E][d][f] -> [E][f][d]: out rows f, cols d
+  const int64_t n1 = (int64_t)s.E * s.f * (s.d / 8);
+  hipLaunchKernelGGL(pack_transposed_kernel,
+                     dim3((unsigned)blocks_for(n1, 256, num_cus, 16)), dim3(256), 0, st,
+                     static_cast<const bf16*>(w_down), static_cast<const bf16*>(w_down),
+                     s.d, (int64_t)s.E, s.f, s.d, static_cast<char*>(out_down_t));
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  // [Wg; Wu] [E][2f][d] -> [E][d][2f]: out rows d, cols 2f
+  const int64_t n2 = (int64_t)s.E * s.d * (2 * s.f / 8);
+  hipLaunchKernelGGL(pack_transposed_kernel,
+                     dim3((unsigned)blocks_for(n2, 256, num_cus, 16)), dim3(256), 0, st,
+                     static_cast<const bf16*>(w_gate), static_cast<const bf16*>(w_up),
+                     s.f, (int64_t)s.E, s.d, 2 * s.f, static_cast<char*>(out_gu_t));
+  return hipGetLastError();
+}
+
+hipError_t launch_fill(float* p, int64_t n, float value, int num_cus, hipStream_t st) {
+  hipLaunchKernelGGL(fill_kernel, dim3((unsigned)blocks_for(n, 256, num_cus, 8)),
+                     dim3(256), 0, st, p, n, value);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -19,7 +19,7 @@ LIB = os.path.join(OUT_DIR, "libmoe_rounds.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["route_plan.hip", "dispatch_combine.hip", "grouped_gemm.hip",
-           "api.hip"]
+           "wgrad.hip", "backward.hip", "api.hip"]
 HEADERS = ["device_common.hpp", "launch.hpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

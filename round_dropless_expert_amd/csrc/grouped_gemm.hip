@@ -82,12 +82,27 @@ struct MmaOp<float> {
   }
 };
 
+// What a launch computes (the operand passes and the epilogue):
+//   kModeGateUp    forward: h = silu(xr Wg^T) * (xr Wu^T) into h
+//   kModeDown      forward: o = h Wd^T into z rows (also the backward's
+//                  dx rows: dgu [Wg | Wu], weights packed as [d][2f])
+//   kModeRecompute backward: g = xr Wg^T and u = xr Wu^T into gu
+//                  ([rows][2f]: g, then u) and w * silu(g) u into hw
+//   kModeDgate     backward: dh = dyr Wd (weights packed as [f][d]), then
+//                  dg = w dh u silu'(g) and du = w dh silu(g) into dgu
+//                  ([rows][2f]), with g, u read from gu
+enum GemmMode { kModeGateUp = 0, kModeDown = 1, kModeRecompute = 2, kModeDgate = 3 };
+
 template <typename Elem>
 struct GemmParams {
   const Elem* act;   // round buffer [rows][K]: xr (gate/up) or h (down)
   const Elem* w0;    // [E][*][K]: gate (gate/up) or down weights
   const Elem* w1;    // [E][N][K]: up weights (gate/up only)
   Elem* out;         // h [rows][N] (gate/up) or z [T*k][N] (down)
+  Elem* out2;        // hw [rows][N] (recompute only)
+  const Elem* aux;   // gu [rows][2N] (dgate only)
+  const float* weight;     // routing weights [T*k] (recompute, dgate)
+  const int32_t* perm;     // the plan's permutation (recompute, dgate)
   const int32_t* rounds;   // the plan's round tables [4][max_rounds][E]
   const int32_t* offsets;  // [E+1]
   const int32_t* n_rounds; // R: a round r >= R has no rows (its tables are unset)
@@ -233,9 +248,12 @@ struct TileSrc {
   uint32_t tbase[kTPasses];  // token pass offsets, kOutOfRange if dead
 };
 
-template <typename Elem, int WI, int WJ, int SPB, bool kGateUp>
+template <typename Elem, int WI, int WJ, int SPB, int kMode>
 __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
     GemmParams<Elem> p) {
+  // two weight matrices per tile (gate rows, then up rows of the same
+  // features)
+  constexpr bool kGateUp = kMode == kModeGateUp || kMode == kModeRecompute;
   typedef Frags<Elem, WI, WJ> frags_t;
   constexpr int kEs = sizeof(Elem);
   constexpr int kStageK = kRowBytes / kEs;       // k elements per stage
@@ -297,7 +315,8 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
   const int lane_incl = wave_inclusive_scan(((lane_m + BM - 1) / BM) * nt);
   const int total = __builtin_amdgcn_readlane(lane_incl, kWave - 1);
   const int lane_row = lv ? (lane / p.G) * p.pool_rows + p.rounds[kPbase * tbl + at] : 0;
-  const int lane_off = !kGateUp && lv ? p.offsets[lane] + p.rounds[kCum * tbl + at] : 0;
+  const int lane_off =
+      kMode != kModeGateUp && lv ? p.offsets[lane] + p.rounds[kCum * tbl + at] : 0;
 
   // XCD-contiguous walk: workgroup b runs on XCD b % 8.
   const int G = gridDim.x;
@@ -500,7 +519,113 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
       else
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(st_t, o), rs, off, 0, 0);
     };
-    if (kGateUp) {
+    if constexpr (kMode == kModeRecompute) {
+      // gu (g in columns [0, N), u in [N, 2N)) and hw = w * silu(g) u: rows
+      // c of expert e's tiled matrices of the round; w is the routing
+      // weight of the row's assignment perm[i0 + c]
+      const int rowb = __builtin_amdgcn_readlane(lane_row, e);
+      const int64_t i0 = (int64_t)__builtin_amdgcn_readlane(lane_off, e);
+      const uint32_t mrows = (uint32_t)((m + 63) & ~63);
+      const __amdgpu_buffer_rsrc_t rgu = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(p.out + (int64_t)rowb * 2 * p.N), 0,
+          (int)(mrows * 2 * p.N * kEs), kRsrcWord3);
+      const __amdgpu_buffer_rsrc_t rhw = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(p.out2 + (int64_t)rowb * p.N), 0, (int)(mrows * p.N * kEs),
+          kRsrcWord3);
+#pragma unroll
+      for (int jb = 0; jb < WJ; ++jb) {
+        const int c = m0 + wm * (BM / 2) + jb * 32 + l32;
+        const float wc = c < m ? p.weight[p.perm[i0 + c]] : 0.f;
+#pragma unroll
+        for (int ib = 0; ib < WI / 2; ++ib) {
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int feat = n0 + wn * (BN / 4) + ib * 32 + 8 * g4 + 4 * half;
+            vec4_t og, ou, oh;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float g = acc_read(acc[ib][jb][4 * g4 + q]);
+              const float u = acc_read(acc[ib + WI / 2][jb][4 * g4 + q]);
+              og[q] = from_f32<Elem>(g);
+              ou[q] = from_f32<Elem>(u);
+              oh[q] = from_f32<Elem>(wc * silu_mul(g, u));
+            }
+            const bool ok = c < m && feat < p.N;
+            const int64_t rb2 = (int64_t)2 * p.N * kEs;
+            store4(rgu, ok ? (uint32_t)tiled_offset(c, (int64_t)feat * kEs, rb2)
+                           : kOutOfRange, og);
+            store4(rgu, ok ? (uint32_t)tiled_offset(c, (int64_t)(p.N + feat) * kEs, rb2)
+                           : kOutOfRange, ou);
+            store4(rhw, ok ? (uint32_t)tiled_offset(c, (int64_t)feat * kEs,
+                                                    (int64_t)p.N * kEs)
+                           : kOutOfRange, oh);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      }
+    } else if constexpr (kMode == kModeDgate) {
+      // dh = w * (dyr Wd) for row c and features feat..feat+3; with g, u of
+      // the same row and features (from gu): du = dh silu(g), dg = dh u
+      // silu'(g) = dh u s (1 + g (1 - s)), s = sigmoid(g); into dgu (dg in
+      // columns [0, N), du in [N, 2N)), rows c of expert e's tiled matrix
+      const int rowb = __builtin_amdgcn_readlane(lane_row, e);
+      const int64_t i0 = (int64_t)__builtin_amdgcn_readlane(lane_off, e);
+      const uint32_t range =
+          (uint32_t)((m + 63) & ~63) * 2 * (uint32_t)p.N * kEs;
+      const __amdgpu_buffer_rsrc_t rin = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(p.aux + (int64_t)rowb * 2 * p.N), 0, (int)range, kRsrcWord3);
+      const __amdgpu_buffer_rsrc_t rout = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(p.out + (int64_t)rowb * 2 * p.N), 0, (int)range, kRsrcWord3);
+      const int64_t rb2 = (int64_t)2 * p.N * kEs;
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+      for (int jb = 0; jb < WJ; ++jb) {
+        const int c = m0 + wm * (BM / 2) + jb * 32 + l32;
+        const float wc = c < m ? p.weight[p.perm[i0 + c]] : 0.f;
+        // this token's g and u for every output of the block, loaded first
+        u32x2 gv[WI][4], uv[WI][4];
+#pragma unroll
+        for (int ib = 0; ib < WI; ++ib) {
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int feat = n0 + wn * (BN / 2) + ib * 32 + 8 * g4 + 4 * half;
+            const bool ok = c < m && feat < p.N;
+            gv[ib][g4] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                rin, ok ? (uint32_t)tiled_offset(c, (int64_t)feat * kEs, rb2) : kOutOfRange,
+                0, 0));
+            uv[ib][g4] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                rin, ok ? (uint32_t)tiled_offset(c, (int64_t)(p.N + feat) * kEs, rb2)
+                        : kOutOfRange,
+                0, 0));
+          }
+        }
+#pragma unroll
+        for (int ib = 0; ib < WI; ++ib) {
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int feat = n0 + wn * (BN / 2) + ib * 32 + 8 * g4 + 4 * half;
+            const vec4_t gq = __builtin_bit_cast(vec4_t, gv[ib][g4]);
+            const vec4_t uq = __builtin_bit_cast(vec4_t, uv[ib][g4]);
+            vec4_t odg, odu;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float dh = wc * acc_read(acc[ib][jb][4 * g4 + q]);
+              const float g = to_f32(gq[q]), u = to_f32(uq[q]);
+              const float sg = __builtin_amdgcn_rcpf(
+                  1.0f + __builtin_amdgcn_exp2f(g * -1.44269504088896341f));
+              odu[q] = from_f32<Elem>(dh * (g * sg));
+              odg[q] = from_f32<Elem>(dh * u * sg * (1.0f + g * (1.0f - sg)));
+            }
+            const bool ok = c < m && feat < p.N;
+            store4(rout, ok ? (uint32_t)tiled_offset(c, (int64_t)feat * kEs, rb2)
+                            : kOutOfRange, odg);
+            store4(rout, ok ? (uint32_t)tiled_offset(c, (int64_t)(p.N + feat) * kEs, rb2)
+                            : kOutOfRange, odu);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      }
+    } else if constexpr (kMode == kModeGateUp) {
       // h: expert e's tiled matrix of the round, row c
       const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(
           (void*)(p.out + (int64_t)__builtin_amdgcn_readlane(lane_row, e) * p.N), 0,
@@ -660,11 +785,11 @@ static int grid_for(int64_t tiles, int num_cus) {
   return (int)(g < 8 ? 8 : g);
 }
 
-template <typename Elem, typename Cfg, bool kGateUp>
+template <typename Elem, typename Cfg, int kMode>
 static hipError_t launch_gemm_cfg(const GemmParams<Elem>& p, int grid,
                                   hipStream_t st) {
   hipLaunchKernelGGL(
-      (grouped_ffn_gemm_kernel<Elem, Cfg::WI, Cfg::WJ, Cfg::SPB, kGateUp>),
+      (grouped_ffn_gemm_kernel<Elem, Cfg::WI, Cfg::WJ, Cfg::SPB, kMode>),
       dim3(grid), dim3(256), 0, st, p);
   return hipGetLastError();
 }
@@ -673,62 +798,107 @@ static hipError_t launch_gemm_cfg(const GemmParams<Elem>& p, int grid,
 // With them the round's tile shape and grid are chosen from its tile counts;
 // without them the large tile and one workgroup per CU are used. Every shape
 // runs the same MFMA sequence over K for every output, so results are
-// identical.
-template <typename Elem, bool kGateUp>
+// identical. p.N is the number of output features.
+template <typename Elem, int kMode>
 static hipError_t launch_gemm(const Shape& s, const GemmParams<Elem>& p,
                               const int32_t* rows_host, int num_cus,
                               hipStream_t st) {
-  const int N = kGateUp ? s.f : s.d;
+  constexpr bool kDual = kMode == kModeGateUp || kMode == kModeRecompute;
+  const int N = p.N;
   if (rows_host) {
     int64_t mmax = 0;
     for (int e = 0; e < s.E; ++e) mmax = rows_host[e] > mmax ? rows_host[e] : mmax;
     if (mmax == 0) return hipSuccess;  // nothing in this round
-    const int64_t tb = round_tiles<TileBig>(s, rows_host, N, kGateUp);
-    const int64_t tm = round_tiles<TileMedium>(s, rows_host, N, kGateUp);
-    const int64_t ts = round_tiles<TileSmall>(s, rows_host, N, kGateUp);
+    const int64_t tb = round_tiles<TileBig>(s, rows_host, N, kDual);
+    const int64_t tm = round_tiles<TileMedium>(s, rows_host, N, kDual);
+    const int64_t ts = round_tiles<TileSmall>(s, rows_host, N, kDual);
     const float cb = est_cost<TileBig>(tb, num_cus);
     const float cm = est_cost<TileMedium>(tm, num_cus);
     const float cs = est_cost<TileSmall>(ts, num_cus);
     if (cb <= cm && cb <= cs)
-      return launch_gemm_cfg<Elem, TileBig, kGateUp>(p, grid_for(tb, num_cus), st);
+      return launch_gemm_cfg<Elem, TileBig, kMode>(p, grid_for(tb, num_cus), st);
     if (cm <= cs)
-      return launch_gemm_cfg<Elem, TileMedium, kGateUp>(p, grid_for(tm, num_cus), st);
-    return launch_gemm_cfg<Elem, TileSmall, kGateUp>(p, grid_for(ts, num_cus), st);
+      return launch_gemm_cfg<Elem, TileMedium, kMode>(p, grid_for(tm, num_cus), st);
+    return launch_gemm_cfg<Elem, TileSmall, kMode>(p, grid_for(ts, num_cus), st);
   }
-  return launch_gemm_cfg<Elem, TileBig, kGateUp>(p, grid_for(num_cus, num_cus), st);
+  return launch_gemm_cfg<Elem, TileBig, kMode>(p, grid_for(num_cus, num_cus), st);
+}
+
+// Parameters of a launch over round r: activations act [rows][K], weights
+// w0 (and w1) [E][N][K], output out; K and N as given.
+template <typename Elem>
+static GemmParams<Elem> params(const Shape& s, int r, const void* act,
+                               const void* w0, const void* w1, void* out,
+                               const PlanBuffers& b, int K, int N, bool tiled_w) {
+  GemmParams<Elem> p{};
+  p.act = static_cast<const Elem*>(act);
+  p.w0 = static_cast<const Elem*>(w0);
+  p.w1 = static_cast<const Elem*>(w1);
+  p.out = static_cast<Elem*>(out);
+  p.weight = b.weight;
+  p.perm = b.perm;
+  p.rounds = b.rounds;
+  p.offsets = b.offsets;
+  p.n_rounds = b.n_rounds;
+  p.E = s.E;
+  p.r = r;
+  p.K = K;
+  p.N = N;
+  p.max_rounds = (int)s.max_rounds();
+  p.G = s.G;
+  p.pool_rows = (int)s.pool_rows();
+  p.tiled_w = tiled_w ? 1 : 0;
+  return p;
 }
 
 hipError_t launch_gate_up(const Shape& s, int r, const void* xr,
                           const void* wg, const void* wu, const PlanBuffers& b,
                           const int32_t* rows_host, void* h, int num_cus,
                           hipStream_t st) {
-  const int mr = (int)s.max_rounds(), pr = (int)s.pool_rows();
-  if (s.bf16) {
-    GemmParams<bf16> p{static_cast<const bf16*>(xr), static_cast<const bf16*>(wg),
-                       static_cast<const bf16*>(wu), static_cast<bf16*>(h),
-                       b.rounds, b.offsets, b.n_rounds, s.E, r, s.d, s.f, mr, s.G, pr, s.tiled_w};
-    return launch_gemm<bf16, true>(s, p, rows_host, num_cus, st);
-  }
-  GemmParams<float> p{static_cast<const float*>(xr), static_cast<const float*>(wg),
-                      static_cast<const float*>(wu), static_cast<float*>(h),
-                      b.rounds, b.offsets, b.n_rounds, s.E, r, s.d, s.f, mr, s.G, pr, s.tiled_w};
-  return launch_gemm<float, true>(s, p, rows_host, num_cus, st);
+  if (s.bf16)
+    return launch_gemm<bf16, kModeGateUp>(
+        s, params<bf16>(s, r, xr, wg, wu, h, b, s.d, s.f, s.tiled_w), rows_host,
+        num_cus, st);
+  return launch_gemm<float, kModeGateUp>(
+      s, params<float>(s, r, xr, wg, wu, h, b, s.d, s.f, s.tiled_w), rows_host,
+      num_cus, st);
 }
 
 hipError_t launch_down(const Shape& s, int r, const void* h, const void* wd,
                        const PlanBuffers& b, const int32_t* rows_host, void* z,
                        int num_cus, hipStream_t st) {
-  const int mr = (int)s.max_rounds(), pr = (int)s.pool_rows();
-  if (s.bf16) {
-    GemmParams<bf16> p{static_cast<const bf16*>(h), static_cast<const bf16*>(wd),
-                       nullptr, static_cast<bf16*>(z), b.rounds, b.offsets, b.n_rounds, s.E, r,
-                       s.f, s.d, mr, s.G, pr, s.tiled_w};
-    return launch_gemm<bf16, false>(s, p, rows_host, num_cus, st);
-  }
-  GemmParams<float> p{static_cast<const float*>(h), static_cast<const float*>(wd),
-                      nullptr, static_cast<float*>(z), b.rounds, b.offsets, b.n_rounds, s.E, r,
-                      s.f, s.d, mr, s.G, pr, s.tiled_w};
-  return launch_gemm<float, false>(s, p, rows_host, num_cus, st);
+  if (s.bf16)
+    return launch_gemm<bf16, kModeDown>(
+        s, params<bf16>(s, r, h, wd, nullptr, z, b, s.f, s.d, s.tiled_w), rows_host,
+        num_cus, st);
+  return launch_gemm<float, kModeDown>(
+      s, params<float>(s, r, h, wd, nullptr, z, b, s.f, s.d, s.tiled_w), rows_host,
+      num_cus, st);
+}
+
+hipError_t launch_recompute(const Shape& s, int r, const void* xr, const void* wg,
+                            const void* wu, const PlanBuffers& b,
+                            const int32_t* rows_host, void* gu, void* hw,
+                            int num_cus, hipStream_t st) {
+  GemmParams<bf16> p = params<bf16>(s, r, xr, wg, wu, gu, b, s.d, s.f, s.tiled_w);
+  p.out2 = static_cast<bf16*>(hw);
+  return launch_gemm<bf16, kModeRecompute>(s, p, rows_host, num_cus, st);
+}
+
+hipError_t launch_dgate(const Shape& s, int r, const void* dyr, const void* wd_t,
+                        const PlanBuffers& b, const int32_t* rows_host,
+                        const void* gu, void* dgu, int num_cus, hipStream_t st) {
+  GemmParams<bf16> p = params<bf16>(s, r, dyr, wd_t, nullptr, dgu, b, s.d, s.f, true);
+  p.aux = static_cast<const bf16*>(gu);
+  return launch_gemm<bf16, kModeDgate>(s, p, rows_host, num_cus, st);
+}
+
+hipError_t launch_dx(const Shape& s, int r, const void* dgu, const void* wgu_t,
+                     const PlanBuffers& b, const int32_t* rows_host, void* dz,
+                     int num_cus, hipStream_t st) {
+  return launch_gemm<bf16, kModeDown>(
+      s, params<bf16>(s, r, dgu, wgu_t, nullptr, dz, b, 2 * s.f, s.d, true),
+      rows_host, num_cus, st);
 }
 
 }  // namespace moe

@@ -79,6 +79,44 @@ hipError_t launch_down(const Shape& s, int r, const void* h, const void* wd,
                        const PlanBuffers& b, const int32_t* rows_host, void* z,
                        int num_cus, hipStream_t st);
 
+// Backward GEMMs of round r (bf16; weights of the dgrad launches packed by
+// launch_pack_backward): the recompute of g and u into gu [rows][2f] and of
+// w * h into hw [rows][f]; dh = dyr Wd turned into dg and du (with gu) in
+// dgu [rows][2f]; and dx rows = dgu [Wg | Wu] into dz [T*k][d] at the
+// assignments' expert-sorted rows, like z.
+hipError_t launch_recompute(const Shape& s, int r, const void* xr, const void* wg,
+                            const void* wu, const PlanBuffers& b,
+                            const int32_t* rows_host, void* gu, void* hw,
+                            int num_cus, hipStream_t st);
+hipError_t launch_dgate(const Shape& s, int r, const void* dyr, const void* wd_t,
+                        const PlanBuffers& b, const int32_t* rows_host,
+                        const void* gu, void* dgu, int num_cus, hipStream_t st);
+hipError_t launch_dx(const Shape& s, int r, const void* dgu, const void* wgu_t,
+                     const PlanBuffers& b, const int32_t* rows_host, void* dz,
+                     int num_cus, hipStream_t st);
+
+// Weight gradients of round r: out_e[a][b] (+)= sum over expert e's rows c
+// of the round of U[c][a] V[c][b] (U: A features per row, V: B, both tiled
+// round buffers), rows a < A0 into out0 [E][A0][B], the rest into out1
+// [E][A-A0][B]; fp32. Round 0 stores (every expert, zeros where it has no
+// rows), later rounds add. rows_host: the round's rows per expert.
+hipError_t launch_wgrad(const Shape& s, int r, const void* U, const void* V,
+                        int A, int A0, int B, float* out0, float* out1,
+                        const PlanBuffers& b, const int32_t* rows_host,
+                        hipStream_t st);
+
+// Router-weight gradient dlogits [T][E] (fp32) from z and dy (bf16).
+hipError_t launch_router_backward(const Shape& s, const void* z, const void* dy,
+                                  const PlanBuffers& b, float* dlogits, int num_cus,
+                                  hipStream_t st);
+// The dgrad GEMMs' weights from row-major Wg, Wu [E][f][d] and Wd [E][d][f]
+// (bf16): Wd transposed to [E][f][d] and [Wg; Wu] transposed to
+// [E][d][2f], both tiled.
+hipError_t launch_pack_backward(const Shape& s, const void* w_gate, const void* w_up,
+                                const void* w_down, void* out_down_t, void* out_gu_t,
+                                int num_cus, hipStream_t st);
+hipError_t launch_fill(float* p, int64_t n, float value, int num_cus, hipStream_t st);
+
 // Host copy of the plan's fill rule: from the entries each expert has left
 // (rem[E], updated), the rows m(r,e) of every expert in the next round.
 void host_next_round(const Shape& s, int64_t* rem, int32_t* rows_out);
