@@ -61,6 +61,10 @@ def parse():
                          " over its capacity sweep and the capacities the "
                          "helper picks for 1 and 2 rounds, each with its "
                          "measured ms per moe_forward")
+    ap.add_argument("--backward", action="store_true",
+                    help="instead of the forward step: one training step of "
+                         "the layer, moe_forward + moe_backward (bf16), with "
+                         "per-launch times of the backward's kernels")
     ap.add_argument("--weights", choices=("tiled", "row_major"), default="tiled",
                     help="expert weight layout the layer reads (tiled = packed "
                          "once by moe_pack_weights before timing)")
@@ -194,8 +198,93 @@ def capacity_curve(args):
                       "points": rows}), flush=True)
 
 
+def backward_bench(args):
+    """Forward + backward of the layer per step (the backward weights packed
+    once per step, as after a weight update), plus per-launch times of one
+    backward from a kernel trace of HIP events."""
+    import numpy as np
+    import torch
+
+    from round_dropless_expert_amd import binding as B
+    from round_dropless_expert_amd import configs, synth
+
+    w = configs.WORKLOADS[args.workload] if args.workload else configs.BENCH_WORKLOAD
+    B.load()
+    B.check_runtime()
+    dev = "cuda:0"
+    print(f"[bench] generating {w.name}", file=sys.stderr, flush=True)
+    inp = synth.generate(w)
+    up = lambda a: torch.from_numpy(a).to(dev).to(torch.bfloat16).contiguous()
+    logits = torch.from_numpy(inp.logits).to(dev)
+    x = up(inp.x)
+    rm = [up(inp.Wg), up(inp.Wu), up(inp.Wd)]
+    del inp
+    cfg = B.config(w.T, w.E, w.k, w.d_model, w.d_ff, w.C, "bf16", "tiled",
+                   args.group, args.round_buffers)
+    wts = [torch.empty_like(t) for t in rm]
+    B.moe_pack_weights(cfg, *rm, *wts)
+    wdt = torch.empty(w.E, w.d_ff, w.d_model, dtype=torch.bfloat16, device=dev)
+    wgut = torch.empty(w.E, w.d_model, 2 * w.d_ff, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(B.workspace_size(cfg), dtype=torch.uint8, device=dev)
+    bws = torch.empty(B.backward_workspace_size(cfg), dtype=torch.uint8, device=dev)
+    y = torch.empty(w.T, w.d_model, dtype=torch.bfloat16, device=dev)
+    gen = torch.Generator().manual_seed(1)
+    dy = torch.randn(w.T, w.d_model, generator=gen).to(torch.bfloat16).to(dev)
+    dx = torch.empty_like(y)
+    dl = torch.empty(w.T, w.E, device=dev)
+    dWg = torch.empty(w.E, w.d_ff, w.d_model, device=dev)
+    dWu = torch.empty_like(dWg)
+    dWd = torch.empty(w.E, w.d_model, w.d_ff, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def fwd():
+        B.moe_forward(cfg, logits, x, *wts, y, ws, stream)
+
+    def bwd():
+        B.moe_pack_backward_weights(cfg, *rm, wdt, wgut, stream)
+        B.moe_backward(cfg, x, wts[0], wts[1], wdt, wgut, dy, dx, dl, dWg, dWu, dWd,
+                       ws, bws, stream)
+
+    for _ in range(args.warmup):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    fwd()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        bwd()
+    torch.cuda.synchronize()
+    ms_bwd = (time.perf_counter() - t0) * 1e3 / args.steps
+    TK = w.T * w.k
+    flops_fwd = 6.0 * TK * w.d_model * w.d_ff
+    # backward GEMMs: recompute (4), dh (2), dx (4), weight gradients (6)
+    flops_bwd = 16.0 * TK * w.d_model * w.d_ff
+    print(json.dumps({
+        "metric": "MoE-layer training-step tokens/sec (forward + backward) on 1 MI355X",
+        "value": w.T / ms_step * 1e3, "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "ms_backward": ms_bwd, "higher_is_better": True, "dtype": "bf16",
+        "data": "synthetic (seeded numpy PCG64)",
+        "config": {"workload": w.name, "T": w.T, "d_model": w.d_model,
+                   "d_ff": w.d_ff, "E": w.E, "k": w.k, "C": w.C,
+                   "group": args.group},
+        "backward_gemm_TFLOPs": flops_bwd / ms_bwd / 1e9,
+        "step_gemm_TFLOPs": (flops_fwd + flops_bwd) / ms_step / 1e9,
+        "backward_workspace_bytes": B.backward_workspace_size(cfg)}), flush=True)
+
+
 def main():
     args = parse()
+    if args.backward:
+        backward_bench(args)
+        return
     if args.copy_calibration:
         copy_calibration()
         return

@@ -64,31 +64,53 @@ __global__ __launch_bounds__(256) void router_backward_kernel(
 
 // out (tiled, [E][rows][cols]) with out_e[i][j] = src_e[j][i], where src_e
 // is src0[e] for j < split and src1[e] (row j - split) otherwise; both
-// sources row-major with `rows` elements per row. Thread -> one 16-byte
-// output piece (i, j0 .. j0+7): eight loads down a source column, adjacent
-// threads taking adjacent i so that each load is contiguous across lanes.
+// sources row-major with `rows` elements per row. A workgroup turns a
+// 64 (j) x 64 (i) tile around in LDS: it reads the 64 source rows as 128-byte
+// pieces (16 bytes a lane), and writes the tile's output, two 4 KiB blocks
+// of the tiled layout (rows i, 32 j per block), as whole 1 KiB pieces per
+// wavefront. rows and cols are multiples of 64 and split a multiple of 64,
+// so a tile lies in one source.
 __global__ __launch_bounds__(256) void pack_transposed_kernel(
     const bf16* __restrict__ src0, const bf16* __restrict__ src1, int split,
     int64_t E, int rows, int cols, char* __restrict__ out) {
-  const int64_t per = (int64_t)rows * (cols / 8);
-  const int64_t total = E * per;
+  constexpr int kLdsPitch = 64 * 2 + 4;  // bytes per j row of the tile
+  __shared__ __attribute__((aligned(16))) char tile[64 * kLdsPitch];
+  const int tid = threadIdx.x;
+  const int ti = rows / 64, tj = cols / 64;
+  const int64_t t = blockIdx.x;
+  const int64_t e = t / ((int64_t)ti * tj);
+  const int rem = (int)(t % ((int64_t)ti * tj));
+  const int i0 = (rem / tj) * 64, j0 = (rem % tj) * 64;
+  const bf16* src = j0 < split ? src0 + (e * split + j0) * (int64_t)rows
+                               : src1 + (e * (cols - split) + (j0 - split)) * (int64_t)rows;
+  // 64 rows x 128 bytes: thread -> row tid / 8 (+ 32), 16-byte piece tid % 8
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int r = tid / 8 + 32 * u, q = tid % 8;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(src + (int64_t)r * rows + i0 + 8 * q);
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(&v);
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      *reinterpret_cast<uint32_t*>(&tile[r * kLdsPitch + q * 16 + 4 * k]) = w[k];
+  }
+  __syncthreads();
+  // output: 512 16-byte chunks; chunk q = tid + 256 u -> block q / 256 (32 j
+  // each), row i = (q % 256) / 4, physical chunk position q % 4 (logical
+  // chunk position ^ ((i / 4) % 4), the tiled layout's swizzle)
   const int64_t row_bytes = (int64_t)cols * 2;
-  for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < total;
-       g += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t e = g / per;
-    const int64_t w = g - e * per;
-    const int i = (int)(w % rows);
-    const int j0 = (int)(w / rows) * 8;
+  char* base = out + e * (int64_t)rows * row_bytes +
+               ((int64_t)(i0 / 64) * (row_bytes / 64) + j0 / 32) * 4096;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int q = tid + 256 * u;
+    const int blk = q / 256, i = (q % 256) / 4, pos = q % 4;
+    const int c = pos ^ ((i >> 2) & 3);
+    const int jb = blk * 32 + c * 8;
     bf16x8 v;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int j = j0 + q;
-      const bf16* src = j < split ? src0 + (e * split + j) * (int64_t)rows
-                                  : src1 + (e * (cols - split) + (j - split)) * (int64_t)rows;
-      v[q] = src[i];
-    }
-    *reinterpret_cast<bf16x8*>(out + e * rows * row_bytes +
-                               tiled_offset(i, (int64_t)j0 * 2, row_bytes)) = v;
+    for (int k = 0; k < 8; ++k)
+      v[k] = *reinterpret_cast<const bf16*>(&tile[(jb + k) * kLdsPitch + i * 2]);
+    *reinterpret_cast<bf16x8*>(base + blk * 4096 + i * 64 + pos * 16) = v;
   }
 }
 
@@ -121,18 +143,17 @@ hipError_t launch_router_backward(const Shape& s, const void* z, const void* dy,
 hipError_t launch_pack_backward(const Shape& s, const void* w_gate, const void* w_up,
                                 const void* w_down, void* out_down_t, void* out_gu_t,
                                 int num_cus, hipStream_t st) {
+  (void)num_cus;
   // Wd [E][d][f] -> [E][f][d]: out rows f, cols d
-  const int64_t n1 = (int64_t)s.E * s.f * (s.d / 8);
-  hipLaunchKernelGGL(pack_transposed_kernel,
-                     dim3((unsigned)blocks_for(n1, 256, num_cus, 16)), dim3(256), 0, st,
+  const int64_t n1 = (int64_t)s.E * (s.f / 64) * (s.d / 64);
+  hipLaunchKernelGGL(pack_transposed_kernel, dim3((unsigned)n1), dim3(256), 0, st,
                      static_cast<const bf16*>(w_down), static_cast<const bf16*>(w_down),
                      s.d, (int64_t)s.E, s.f, s.d, static_cast<char*>(out_down_t));
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   // [Wg; Wu] [E][2f][d] -> [E][d][2f]: out rows d, cols 2f
-  const int64_t n2 = (int64_t)s.E * s.d * (2 * s.f / 8);
-  hipLaunchKernelGGL(pack_transposed_kernel,
-                     dim3((unsigned)blocks_for(n2, 256, num_cus, 16)), dim3(256), 0, st,
+  const int64_t n2 = (int64_t)s.E * (s.d / 64) * (2 * s.f / 64);
+  hipLaunchKernelGGL(pack_transposed_kernel, dim3((unsigned)n2), dim3(256), 0, st,
                      static_cast<const bf16*>(w_gate), static_cast<const bf16*>(w_up),
                      s.f, (int64_t)s.E, s.d, 2 * s.f, static_cast<char*>(out_gu_t));
   return hipGetLastError();

@@ -14,13 +14,21 @@
 //
 // The contraction runs over tokens, which are rows of both operands, while
 // the matrix cores want each lane to hold consecutive K (token) values of
-// one feature: every 32-token stage is therefore written to LDS turned
-// around ([feature][token]), from registers, and read back as 16-byte MFMA
-// fragments. A workgroup computes a 128 (b) x 128 (a) tile with 2 x 2
-// wavefronts of 64 x 64 (2 x 2 blocks of v_mfma_f32_32x32x16_bf16; the
-// output block is [b][a], so a lane holds four consecutive b of one a: one
-// 16-byte fp32 store). Stages are double-buffered: the next stage's global
-// loads are in flight while the current one is multiplied.
+// one feature. Stages of 32 tokens are copied into LDS as they lie in the
+// tiled round buffers (halves of 4 KiB blocks: 32 tokens x 32 features,
+// 64-byte rows with the block's XOR swizzle) by LDS-direct loads, and the
+// fragments are read back with gfx950's transposing LDS read
+// (ds_read_b64_tr_b16): in each group of 16 lanes, lane i receives 16-bit
+// element i % 4 of the 8 bytes addressed by lanes 4 j + i / 4, j = 0..3
+// (checked on the device). Lanes 4 j + p of a group address tokens t0 + j,
+// features c0 + 4 p .. + 3, so lane i gets feature c0 + i at tokens t0 ..
+// t0 + 3: two such reads make one 8-token fragment, and the four rows a
+// group touches cover different banks. A workgroup computes a 256 (b) x
+// 256 (a) tile with 2 x 2 wavefronts of 128 x 128 (4 x 4 blocks of
+// v_mfma_f32_32x32x16_bf16, 256 accumulators); the output block is [b][a],
+// so a lane holds four consecutive b of one a: one 16-byte fp32 store.
+// Four LDS slots form a ring with three stages in flight; the kernel waits
+// on its own loads with exact vmcnt counts, as the grouped GEMM does.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -31,10 +39,61 @@
 namespace moe {
 namespace {
 
-constexpr int kTile = 128;        // a and b extent of a tile
+constexpr int kTile = 256;        // a and b extent of a tile
 constexpr int kStageTok = 32;     // tokens per stage
-constexpr int kPitch = 80;        // bytes per LDS row: 32 tokens + 16 pad
-constexpr int kOpBytes = kTile * kPitch;  // one operand of one stage
+constexpr int kHalfBlock = 2048;  // 32 tokens x 64 bytes
+constexpr int kOpBytes = 8 * kHalfBlock;   // 256 features of one operand
+constexpr int kSlotBytes = 2 * kOpBytes;   // U then V
+constexpr int kSlots = 4;
+constexpr int kLoads = kSlotBytes / (256 * 16);  // 16-byte loads per thread per stage
+constexpr uint32_t kOutOfRange = 0x80000000u;
+constexpr int kRsrcWord3 = 0x00020000;
+
+typedef __attribute__((address_space(3))) char lds_char;
+
+// Buffer-to-LDS load (LDS-direct): lane i reads 16 bytes at voff + soff of
+// the buffer and writes them to LDS at m0 + 16 i. Asm, with M0 saved and
+// restored, so that the compiler neither moves nor waits on it: every wait
+// on these loads is the kernel's own, exact vmcnt count.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff,
+                                           uint32_t soff, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+      : "m0");
+}
+#pragma clang diagnostic pop
+
+// At most N of this wavefront's vector-memory operations outstanding, its
+// LDS reads done, then the workgroup barrier.
+template <int N>
+__device__ __forceinline__ void wait_vmem_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(N) : "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// An accumulator element, read from its AGPR at this point of the program
+// (asm: the epilogue then moves four values at a time into VGPRs instead of
+// the compiler copying all 256 accumulators out at once).
+__device__ __forceinline__ float acc_get(float a) {
+  float v;
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
+  return v;
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 struct WgradParams {
   const bf16* U;   // round buffer, A features per row (tiled)
@@ -48,12 +107,12 @@ struct WgradParams {
   int accumulate;   // add to out (else store)
 };
 
-__global__ __launch_bounds__(256) void wgrad_kernel(WgradParams p) {
-  __shared__ __attribute__((aligned(16))) char lds[2][2][kOpBytes];  // [buf][U|V]
+__global__ __launch_bounds__(256, 1) void wgrad_kernel(WgradParams p) {
+  __shared__ __attribute__((aligned(1024))) char lds[kSlots][kSlotBytes];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wa = wave & 1, wb = wave >> 1;  // this wavefront's 64 x 64 quarter
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wa = wave & 1, wb = wave >> 1;  // this wavefront's 128 x 128 quarter
   const int l32 = lane & 31, half = lane >> 5;
   if (p.r >= *p.n_rounds) return;
 
@@ -77,97 +136,129 @@ __global__ __launch_bounds__(256) void wgrad_kernel(WgradParams p) {
   }
   if (e >= p.E) return;
   const int64_t at = (int64_t)p.r * p.E + e;
-  const int m = p.rounds[kAlloc * tbl + at];
+  const int m = __builtin_amdgcn_readfirstlane(p.rounds[kAlloc * tbl + at]);
   const int64_t row0 = (int64_t)(e / p.G) * p.pool_rows + p.rounds[kPbase * tbl + at];
   const int a0 = (local / tb) * kTile, b0 = (local % tb) * kTile;
 
-  // loads of a stage: thread -> token c = tid % 32, 16-byte chunks
-  // j = tid / 32 and j + 8 of the tile's 128 features (8 per chunk)
-  const int lc = tid & 31, lj = tid >> 5;
-  const int64_t ubytes = (int64_t)p.A * 2, vbytes = (int64_t)p.B * 2;
-  auto load = [&](int k0, u32x4 (&ur)[2], u32x4 (&vr)[2]) {
-    const int c = k0 + lc;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int fa = a0 + (lj + 8 * i) * 8, fb = b0 + (lj + 8 * i) * 8;
-      ur[i] = u32x4{0, 0, 0, 0};
-      vr[i] = u32x4{0, 0, 0, 0};
-      if (c < m && fa < p.A)
-        ur[i] = *reinterpret_cast<const u32x4*>(
-            reinterpret_cast<const char*>(p.U) +
-            tiled_offset(row0 + c, (int64_t)fa * 2, ubytes));
-      if (c < m && fb < p.B)
-        vr[i] = *reinterpret_cast<const u32x4*>(
-            reinterpret_cast<const char*>(p.V) +
-            tiled_offset(row0 + c, (int64_t)fb * 2, vbytes));
-    }
-  };
-  // turned around: feature row (8 chunk + v), token column c
-  auto store_lds = [&](int buf, const u32x4 (&ur)[2], const u32x4 (&vr)[2]) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int f0 = (lj + 8 * i) * 8;
-      const bf16x8 uv = __builtin_bit_cast(bf16x8, ur[i]);
-      const bf16x8 vv = __builtin_bit_cast(bf16x8, vr[i]);
-#pragma unroll
-      for (int v = 0; v < 8; ++v) {
-        *reinterpret_cast<bf16*>(&lds[buf][0][(f0 + v) * kPitch + lc * 2]) = uv[v];
-        *reinterpret_cast<bf16*>(&lds[buf][1][(f0 + v) * kPitch + lc * 2]) = vv[v];
-      }
-    }
+  // the expert's matrices of the round: m rows padded to 64
+  const uint32_t ubytes = (uint32_t)p.A * 2, vbytes = (uint32_t)p.B * 2;
+  const uint32_t mpad = (uint32_t)((m + 63) & ~63);
+  const __amdgpu_buffer_rsrc_t ru = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.U + row0 * p.A), 0, (int)(mpad * ubytes), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.V + row0 * p.B), 0, (int)(mpad * vbytes), kRsrcWord3);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char*)&lds[0][0];
+
+  // Loads of a stage: wavefronts 0-1 fetch U, 2-3 fetch V; load x of a
+  // wavefront moves 1 KiB = part x % 2 of the 32-feature half block
+  // h = 4 (wave % 2) + x / 2; lane i moves 16 bytes, of token
+  // s*32 + 16 (x % 2) + i / 4 (zeros past m, and past A or B).
+  const int op = wave >> 1;
+  const __amdgpu_buffer_rsrc_t rsrc = op == 0 ? ru : rv;
+  const uint32_t rb = op == 0 ? ubytes : vbytes;
+  const int fbase = (op == 0 ? a0 : b0) + 128 * (wave & 1);
+  const int flim = op == 0 ? p.A : p.B;
+  const uint32_t dst0 = lds0 + (uint32_t)(op * kOpBytes + 4 * (wave & 1) * kHalfBlock);
+  auto fetch = [&](int s, int x) {
+    const int h = x >> 1, part = x & 1;
+    const int k0 = s * kStageTok;
+    const bool fin = fbase + 32 * h < flim;
+    const uint32_t soff =
+        fin ? ((uint32_t)(k0 >> 6) * (rb >> 6) + (uint32_t)((fbase >> 5) + h)) * 4096u +
+                  (uint32_t)((k0 >> 5) & 1) * kHalfBlock + (uint32_t)part * 1024u
+            : 0u;
+    const int tok = k0 + part * 16 + (lane >> 2);
+    const uint32_t vo = fin && tok < m ? (uint32_t)lane * 16u : kOutOfRange;
+    const uint32_t dst =
+        dst0 + (uint32_t)((s & 3) * kSlotBytes + h * kHalfBlock + part * 1024);
+    lds_load16(rsrc, vo, soff, dst);
   };
 
-  f32x16 acc[2][2];  // [b block][a block]
+  // this lane's part of a transposed read: group g = lane / 16, position
+  // 4 j + q in it -> token 8 (g / 2) + j (+ 4 for the second read) and
+  // features 16 (g % 2) + 4 q of a 32-feature block: 16-byte chunk
+  // 2 (g % 2) + q / 2, 8-byte half q % 2, swizzled by the row
+  const int grp = lane >> 4, gj = (lane >> 2) & 3, gq = lane & 3;
+  const int tr_row = 8 * (grp >> 1) + gj;
+  const int tr_chunk = 2 * (grp & 1) + (gq >> 1);
+  const int tr_half = (gq & 1) * 8;
+  auto frag = [&](const char* op_base, int feat0, int tok0) {
+    const char* blk = op_base + (feat0 >> 5) * kHalfBlock;
+    const int r0 = tok0 + tr_row, r1 = r0 + 4;
+    const char* p0 = blk + r0 * 64 + ((tr_chunk ^ ((r0 >> 2) & 3)) << 4) + tr_half;
+    const char* p1 = blk + r1 * 64 + ((tr_chunk ^ ((r1 >> 2) & 3)) << 4) + tr_half;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4*)(lds_char*)p0);
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4*)(lds_char*)p1);
+    const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, v);
+  };
+
+  f32x16 acc[4][4];  // [b block][a block]
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
   const int stages = (m + kStageTok - 1) / kStageTok;
-  u32x4 ur[2], vr[2];
-  if (stages > 0) load(0, ur, vr);
+  // prologue: stages 0, 1, 2 in flight, wait for stage 0
+#pragma unroll
+  for (int st = 0; st < 3; ++st)
+#pragma unroll
+    for (int x = 0; x < kLoads; ++x) fetch(st, x);
+  wait_vmem_barrier<2 * kLoads>();
   for (int s = 0; s < stages; ++s) {
-    const int buf = s & 1;
-    store_lds(buf, ur, vr);
-    __syncthreads();
-    if (s + 1 < stages) load((s + 1) * kStageTok, ur, vr);
+    const char* cur = &lds[s & 3][0];
 #pragma unroll
     for (int ks = 0; ks < kStageTok / 16; ++ks) {
-      const int tok = ks * 16 + half * 8;
-      bf16x8 fa[2], fb[2];
+      bf16x8 fb[4], fa[4];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int brow = wb * 64 + i * 32 + l32;
-        const int arow = wa * 64 + i * 32 + l32;
-        fb[i] = *reinterpret_cast<const bf16x8*>(&lds[buf][1][brow * kPitch + tok * 2]);
-        fa[i] = *reinterpret_cast<const bf16x8*>(&lds[buf][0][arow * kPitch + tok * 2]);
+      for (int i = 0; i < 4; ++i) {
+        fb[i] = frag(cur + kOpBytes, wb * 128 + i * 32, ks * 16);
+        fa[i] = frag(cur, wa * 128 + i * 32, ks * 16);
       }
+      // stage s + 3 into the slot read at s - 1 (the barrier that ended
+      // s - 1 saw every wavefront's reads of it done), half per K step
+      asm volatile("" ::: "memory");
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int x = 0; x < kLoads / 2; ++x) fetch(s + 3, ks * (kLoads / 2) + x);
+      asm volatile("" ::: "memory");
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[i], fa[j], acc[i][j],
                                                               0, 0, 0);
     }
+    // stage s + 1 has landed (s + 2 and s + 3 may be in flight)
+    wait_vmem_barrier<2 * kLoads>();
   }
+  // the loads that ran past the last stage read nothing but still write
+  // LDS: let them land before the workgroup ends
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  // lane: a = column l32 of the block, b = rows 8 g4 + 4 half + q
+  // lane: a = column l32 of the block, b = rows 8 g4 + 4 half + q. (The
+  // accumulators are read by asm: give the last MFMAs the wait states a
+  // VALU read of their results needs, which the compiler cannot see.)
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < 4; ++i) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int a = a0 + wa * 64 + j * 32 + l32;
+    for (int j = 0; j < 4; ++j) {
+      const int a = a0 + wa * 128 + j * 32 + l32;
       if (a >= p.A) continue;
       float* row = a < p.A0 ? p.out0 + ((int64_t)e * p.A0 + a) * p.B
                             : p.out1 + ((int64_t)e * (p.A - p.A0) + (a - p.A0)) * p.B;
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const int b = b0 + wb * 64 + i * 32 + 8 * g4 + 4 * half;
+        const int b = b0 + wb * 128 + i * 32 + 8 * g4 + 4 * half;
         if (b >= p.B) continue;
-        float4 v = make_float4(acc[i][j][4 * g4], acc[i][j][4 * g4 + 1],
-                               acc[i][j][4 * g4 + 2], acc[i][j][4 * g4 + 3]);
+        float4 v = make_float4(acc_get(acc[i][j][4 * g4]), acc_get(acc[i][j][4 * g4 + 1]),
+                               acc_get(acc[i][j][4 * g4 + 2]),
+                               acc_get(acc[i][j][4 * g4 + 3]));
         float4* dst = reinterpret_cast<float4*>(row + b);
         if (p.accumulate) {
           const float4 o = *dst;

@@ -176,3 +176,60 @@ def test_pointer_and_workspace_checks_before_any_hip_call(B):
     assert L.moe_pack_weights(c, p, p, None, p, p, p, None) == \
         B.MOE_ERR_INVALID_ARGUMENT
     assert L.moe_status_string(3) == b"MOE_ERR_WORKSPACE_TOO_SMALL"
+
+
+def expected_backward_total(T, E, k, d, f, C, G=1):
+    al = lambda v: (v + 255) // 256 * 256
+    ce = min(C, T)
+    pad = ceil_div(ce, 64) * 64
+    Q = pad if G == 1 else G * (pad + 64)
+    rows = E // G * Q
+    TK = T * k
+    parts = [rows * d * 2, rows * d * 2, rows * 2 * f * 2, rows * f * 2,
+             rows * 2 * f * 2, TK * d * 2, TK * 4]
+    return sum(al(p) for p in parts)
+
+
+def test_backward_workspace_is_a_function_of_the_config_only(B):
+    from round_dropless_expert_amd import configs
+    for name, w in configs.WORKLOADS.items():
+        for G in (1, 2):
+            cfg = B.config(w.T, w.E, w.k, w.d_model, w.d_ff, w.C, w.dtype, group=G)
+            if w.dtype != "bf16":
+                with pytest.raises(B.MoeError):
+                    B.backward_workspace_size(cfg)
+                continue
+            n = B.backward_workspace_size(cfg)
+            assert n == expected_backward_total(w.T, w.E, w.k, w.d_model, w.d_ff,
+                                                w.C, G)
+            lay = B.backward_layout(cfg)
+            offs = [lay[f] for f in B.BWD_LAYOUT_FIELDS]
+            assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+            assert lay["total"] == n
+
+
+def test_backward_argument_checks_before_any_hip_call(B):
+    L = B.load()
+    cfg = B.config(512, 8, 2, 64, 128, 64, "bf16")
+    need = B.workspace_size(cfg)
+    bneed = B.backward_workspace_size(cfg)
+    p = 1 << 20
+    c = ctypes.byref(cfg)
+    ptrs = [p] * 11
+    assert L.moe_backward(c, *ptrs, p, need, p, bneed - 1, None) == \
+        B.MOE_ERR_WORKSPACE_TOO_SMALL
+    assert L.moe_backward(c, *ptrs, p, need - 1, p, bneed, None) == \
+        B.MOE_ERR_WORKSPACE_TOO_SMALL
+    for i in range(11):
+        bad = list(ptrs)
+        bad[i] = None
+        assert L.moe_backward(c, *bad, p, need, p, bneed, None) == \
+            B.MOE_ERR_INVALID_ARGUMENT, i
+    bad = list(ptrs)
+    bad[6] = p + 2  # dx misaligned
+    assert L.moe_backward(c, *bad, p, need, p, bneed, None) == B.MOE_ERR_INVALID_ARGUMENT
+    f32 = B.config(512, 8, 2, 64, 128, 64, "f32")
+    assert L.moe_backward(ctypes.byref(f32), *ptrs, p, need, p, bneed, None) == \
+        B.MOE_ERR_UNSUPPORTED
+    assert L.moe_pack_backward_weights(c, p, p, None, p, p, None) == \
+        B.MOE_ERR_INVALID_ARGUMENT
