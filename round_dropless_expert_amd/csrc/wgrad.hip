@@ -103,6 +103,7 @@ struct WgradParams {
   const int32_t* rounds;
   const int32_t* n_rounds;
   int E, r, A, A0, B, G, max_rounds, pool_rows;
+  int tiles;        // tiles of the launch (the grid is this rounded up to 8)
   int all_experts;  // tiles of every expert (round 0: experts without rows get zeros)
   int accumulate;   // add to out (else store)
 };
@@ -120,8 +121,14 @@ __global__ __launch_bounds__(256, 1) void wgrad_kernel(WgradParams p) {
   const int ta = (p.A + kTile - 1) / kTile, tb = (p.B + kTile - 1) / kTile;
   const int per = ta * tb;
   const int64_t tbl = (int64_t)p.max_rounds * p.E;
-  const int slot = (int)blockIdx.x / per;
-  const int local = (int)blockIdx.x % per;
+  // XCD-contiguous walk: workgroup b runs on XCD b % 8, so XCD x takes
+  // tiles [x n / 8, (x + 1) n / 8): an expert's tiles, which share its
+  // operand panels, stay on one XCD's L2
+  const int per_xcd = (int)gridDim.x / 8;
+  const int tile = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+  if (tile >= p.tiles) return;
+  const int slot = tile / per;
+  const int local = tile % per;
   int e;
   if (p.all_experts) {
     e = slot;
@@ -285,10 +292,12 @@ hipError_t launch_wgrad(const Shape& s, int r, const void* U, const void* V,
   const int n = all ? s.E : active;
   if (n == 0) return hipSuccess;
   const int per = ((A + kTile - 1) / kTile) * ((B + kTile - 1) / kTile);
+  const int tiles = n * per;
   WgradParams p{static_cast<const bf16*>(U), static_cast<const bf16*>(V), out0, out1,
                 b.rounds, b.n_rounds, s.E, r, A, A0, B, s.G, (int)s.max_rounds(),
-                (int)s.pool_rows(), all ? 1 : 0, r == 0 ? 0 : 1};
-  hipLaunchKernelGGL(wgrad_kernel, dim3((unsigned)(n * per)), dim3(256), 0, st, p);
+                (int)s.pool_rows(), tiles, all ? 1 : 0, r == 0 ? 0 : 1};
+  hipLaunchKernelGGL(wgrad_kernel, dim3((unsigned)((tiles + 7) / 8 * 8)), dim3(256), 0,
+                     st, p);
   return hipGetLastError();
 }
 
