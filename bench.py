@@ -449,6 +449,22 @@ def main():
                 "avg_launch_us": sec["gate_up[0]"] * 1e6}
     kernels = per_launch
 
+    # the layer's attainable time with no overlap: per round the larger of
+    # its GEMM FLOPs at the bf16 peak and the bytes it must stream at 8 TB/s
+    # (active experts' three weight matrices, the round's rows in and out),
+    # plus dispatch and combine bytes at 8 TB/s
+    views_r = views["rounds"].cpu().numpy()
+    hbm = 8.0e12
+    bound_s = 0.0
+    for r in range(R):
+        active = int((views_r[0, r] > 0).sum())
+        f_r = 6.0 * A[r] * df
+        b_r = (active * 3.0 * df * es + A[r] * (2 * w.d_model + 2 * w.d_ff) * es)
+        bound_s += max(f_r / (peak_tf * 1e12), b_r / hbm)
+    bound_s += (sum(disp_bytes) + comb_bytes) / hbm
+    layer_bound = {"us": bound_s * 1e6, "tokens_per_s": w.T / bound_s,
+                   "frac": tokens_per_s * bound_s / w.T}
+
     out = {
         "metric": METRIC, "value": tokens_per_s, "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -467,7 +483,7 @@ def main():
         "combine_GBps": kernels["combine"]["GB/s"],
         "device_copy_GBps": copy_gbps,
         "workspace_bytes": ws_bytes, "peak_allocated_bytes": peak_bytes,
-        "roofline": roofline, "kernels": kernels,
+        "roofline": roofline, "layer_bound": layer_bound, "kernels": kernels,
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
