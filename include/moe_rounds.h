@@ -1,6 +1,7 @@
 /*
  * moe_rounds.h -- C ABI of the multi-round dropless mixture-of-experts layer
- * forward on one AMD Instinct MI355X (gfx950).
+ * (forward, backward and capacity helpers) on one AMD Instinct MI355X
+ * (gfx950).
  *
  * The method (sources: "Frontier Pre-training at Microsoft AI (MAI-Base-2)",
  * section "Key claims", item on multi-round dropless MoE; "Microsoft AI's
@@ -41,11 +42,13 @@
  * row once, and y once after an fp32 weighted sum.
  *
  * Ownership: the caller allocates every buffer, including the workspace of
- * moe_workspace_size() bytes. The library allocates no device memory and
- * keeps no mutable global state; all work is enqueued on the caller's HIP
- * stream (`stream` is a hipStream_t; NULL means the null stream). Calls on
- * one workspace must not overlap in time. Device pointers must be 16-byte
- * aligned.
+ * moe_workspace_size() bytes. The library allocates no device memory; its
+ * only state is, per calling thread and device, the small pinned host
+ * buffer, side stream and events moe_forward and moe_backward use to read
+ * the plan's counts (see moe_forward). All work is enqueued on the caller's
+ * HIP stream (`stream` is a hipStream_t; NULL means the null stream). Calls
+ * on one workspace must not overlap in time. Device pointers must be
+ * 16-byte aligned.
  *
  * Errors: every call returns a moe_status_t and validates its arguments
  * before touching the GPU, so an argument error enqueues nothing. A failed
@@ -227,7 +230,8 @@ moe_status_t moe_capacity_for_rounds(const moe_config_t *cfg,
 moe_status_t moe_plan(const moe_config_t *cfg, const float *logits, void *ws,
                       size_t ws_bytes, int32_t *plan_host, void *stream);
 
-/* Dispatch of round r ("dispatch -> compute -> collect rounds"): for every
+/* Dispatch of round r (the first of a round's dispatch, compute and collect
+ * steps): for every
  * expert e and slot c < m(r,e), copies x[perm[offsets[e] + s + c] / k]
  * (s = the index of e's first entry of round r) into row c of expert e's
  * matrix of the round buffer (tiled layout). Other rows are left
@@ -242,9 +246,10 @@ moe_status_t moe_dispatch(const moe_config_t *cfg, int32_t round,
  * first m(r,e) rows of expert e's matrix, then o = h . w_down[e]^T, and
  * row c of o is stored at z[offsets[e] + s + c], the row of assignment
  * perm[offsets[e] + s + c] (s as for moe_dispatch; the combine collects
- * these rows back to token order). Grouped GEMMs over all active experts in one launch
- * each ("grouped GEMM" per expert group, section "Reducing per-expert
- * overhead" as quoted in "Key claims").
+ * these rows back to token order). Each product is one grouped GEMM launch
+ * over all active experts (one GEMM per expert group rather than per
+ * expert: "Frontier Pre-training at Microsoft AI (MAI-Base-2)", section
+ * "Key claims", summarizing the post's "Reducing per-expert overhead").
  * counts_host: NULL, or a host copy of the E counts n_e (the first E values
  * moe_plan stores in plan_host). With it the launch shape fits the round:
  * the output tile (256 x 256, 256 x 128 or 128 x 64) with the least

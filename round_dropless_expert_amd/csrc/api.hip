@@ -1,13 +1,15 @@
-// C ABI of the multi-round dropless MoE layer forward: argument validation,
-// the workspace layout (a pure function of the config), and the round loop.
+// C ABI of the multi-round dropless MoE layer: argument validation, the
+// workspace layouts (pure functions of the config), the round loops of the
+// forward and the backward, and the capacity helpers.
 //
 // The round loop follows "Frontier Pre-training at Microsoft AI
-// (MAI-Base-2)", section "Key claims" (one or more dispatch -> compute ->
-// collect rounds with a fixed per-expert capacity; memory static regardless
-// of token imbalance) and "Microsoft AI's MAI-Base-2 trained on 16K GPUs with
-// Muon", section "Expert groups keep memory fixed when tokens pile up"
-// (overflow tokens go into extra rounds). The plan stays on the device; the
-// host reads back only the round count R.
+// (MAI-Base-2)", section "Key claims" (one or more rounds of dispatch,
+// expert compute and collect with a fixed per-expert capacity; memory
+// static whatever the token imbalance) and "Microsoft AI's MAI-Base-2
+// trained on 16K GPUs with Muon", section "Expert groups keep memory fixed
+// when tokens pile up" (overflow waits for an extra round). The plan stays
+// on the device; the host reads back only the E counts and R, once, to
+// size each round's launches.
 #include <atomic>
 #include <cstdio>
 #include <algorithm>
