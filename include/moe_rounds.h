@@ -332,11 +332,13 @@ moe_status_t moe_forward(const moe_config_t *cfg, const float *logits,
  *   dW_down[e] += dyr^T hw;  dW_gate[e] += dg^T xr;  dW_up[e] += du^T xr
  * and finally dx[t] = sum_j dz[pos[t*k + j]] (fp32, j ascending, rounded
  * once). GEMMs take bf16 operands with fp32 accumulation; the weight
- * gradients are fp32 and sum an expert's rows round by round. */
+ * gradients are fp32 and sum an expert's rows a pair of rounds at a time. */
 
 /* Byte offsets of the backward workspace's buffers (a pure function of the
- * config; 256-byte aligned): round buffers xr, dyr [E/G][Q][d], gu, dgu
- * [E/G][Q][2f], hw [E/G][Q][f] (tiled, as the forward's xr), dz [T*k][d]
+ * config; 256-byte aligned): round buffers xr, dyr [2][E/G][Q][d], gu
+ * [E/G][Q][2f], dgu [2][E/G][Q][2f], hw [2][E/G][Q][f] (tiled, as the
+ * forward's xr; rounds are taken in pairs, the second round of a pair in
+ * set 1, and the weight gradients contract both in one pass), dz [T*k][d]
  * (expert-sorted order, as z) and ones [T*k] float. */
 typedef struct {
   size_t xr, dyr, gu, hw, dgu, dz, ones;

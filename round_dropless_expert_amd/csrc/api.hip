@@ -340,11 +340,12 @@ void bwd_layout_of(const moe_config_t* c, moe_backward_layout_t* L) {
     off += (bytes + 255) / 256 * 256;
     return o;
   };
-  L->xr = take(rows * d * 2);
-  L->dyr = take(rows * d * 2);
+  // two sets of xr, dyr, hw and dgu (rounds r and r + 1 of a pair), one gu
+  L->xr = take(2 * rows * d * 2);
+  L->dyr = take(2 * rows * d * 2);
   L->gu = take(rows * 2 * f * 2);
-  L->hw = take(rows * f * 2);
-  L->dgu = take(rows * 2 * f * 2);
+  L->hw = take(2 * rows * f * 2);
+  L->dgu = take(2 * rows * 2 * f * 2);
   L->dz = take(TK * d * 2);
   L->ones = take(TK * 4);
   L->total = off;
@@ -663,23 +664,37 @@ moe_status_t moe_backward(const moe_config_t* cfg, const void* x, const void* w_
     return fail(MOE_ERR_HIP, "device plan reported an impossible round count");
   int64_t rem[kMaxExperts];
   for (int e = 0; e < b.s.E; ++e) rem[e] = counts_r[e];
-  int32_t rows[kMaxExperts];
-  char *xr = w + L.xr, *dyr = w + L.dyr, *gu = w + L.gu, *hw = w + L.hw,
-       *dgu = w + L.dgu, *dz = w + L.dz;
+  int32_t rows[2][kMaxExperts];
   const int d = b.s.d, f = b.s.f;
-  for (int r = 0; r < R; ++r) {
-    moe::host_next_round(b.s, rem, rows);
-    MOE_HIP(moe::launch_dispatch(b.s, r, x, b.pb, xr, cus, s), "dispatch launch");
-    MOE_HIP(moe::launch_dispatch(b.s, r, dy, b.pb, dyr, cus, s), "dispatch launch");
-    MOE_HIP(moe::launch_recompute(b.s, r, xr, w_gate, w_up, b.pb, rows, gu, hw, cus, s),
-            "recompute launch");
-    MOE_HIP(moe::launch_dgate(b.s, r, dyr, w_down_t, b.pb, rows, gu, dgu, cus, s),
-            "dgate launch");
-    MOE_HIP(moe::launch_dx(b.s, r, dgu, w_gate_up_t, b.pb, rows, dz, cus, s),
-            "dx launch");
-    MOE_HIP(moe::launch_wgrad(b.s, r, dyr, hw, d, d, f, dw_down, nullptr, b.pb, rows, s),
+  const size_t set = (size_t)b.s.buf_rows() * 2;  // bytes per feature of a set
+  char* xr[2] = {w + L.xr, w + L.xr + set * d};
+  char* dyr[2] = {w + L.dyr, w + L.dyr + set * d};
+  char* hw[2] = {w + L.hw, w + L.hw + set * f};
+  char* dgu[2] = {w + L.dgu, w + L.dgu + set * 2 * f};
+  char *gu = w + L.gu, *dz = w + L.dz;
+  // rounds in pairs: each round's gathers, recompute and dgrad GEMMs into
+  // its set, then one weight-gradient contraction over both rounds
+  for (int r = 0; r < R; r += 2) {
+    const int nr = R - r >= 2 ? 2 : 1;
+    for (int q = 0; q < nr; ++q) {
+      const int rr = r + q;
+      moe::host_next_round(b.s, rem, rows[q]);
+      MOE_HIP(moe::launch_dispatch(b.s, rr, x, b.pb, xr[q], cus, s), "dispatch launch");
+      MOE_HIP(moe::launch_dispatch(b.s, rr, dy, b.pb, dyr[q], cus, s), "dispatch launch");
+      MOE_HIP(moe::launch_recompute(b.s, rr, xr[q], w_gate, w_up, b.pb, rows[q], gu, hw[q],
+                                    cus, s),
+              "recompute launch");
+      MOE_HIP(moe::launch_dgate(b.s, rr, dyr[q], w_down_t, b.pb, rows[q], gu, dgu[q], cus,
+                                s),
+              "dgate launch");
+      MOE_HIP(moe::launch_dx(b.s, rr, dgu[q], w_gate_up_t, b.pb, rows[q], dz, cus, s),
+              "dx launch");
+    }
+    MOE_HIP(moe::launch_wgrad(b.s, r, nr, dyr[0], hw[0], dyr[1], hw[1], d, d, f, dw_down,
+                              nullptr, b.pb, rows[0], rows[1], s),
             "wgrad launch");
-    MOE_HIP(moe::launch_wgrad(b.s, r, dgu, xr, 2 * f, f, d, dw_gate, dw_up, b.pb, rows, s),
+    MOE_HIP(moe::launch_wgrad(b.s, r, nr, dgu[0], xr[0], dgu[1], xr[1], 2 * f, f, d,
+                              dw_gate, dw_up, b.pb, rows[0], rows[1], s),
             "wgrad launch");
   }
   MOE_HIP(moe::launch_combine(b.s, dz, ones, b.pb.pos, dx, cus, s), "combine launch");

@@ -95,15 +95,17 @@ hipError_t launch_dx(const Shape& s, int r, const void* dgu, const void* wgu_t,
                      const PlanBuffers& b, const int32_t* rows_host, void* dz,
                      int num_cus, hipStream_t st);
 
-// Weight gradients of round r: out_e[a][b] (+)= sum over expert e's rows c
-// of the round of U[c][a] V[c][b] (U: A features per row, V: B, both tiled
-// round buffers), rows a < A0 into out0 [E][A0][B], the rest into out1
-// [E][A-A0][B]; fp32. Round 0 stores (every expert, zeros where it has no
-// rows), later rounds add. rows_host: the round's rows per expert.
-hipError_t launch_wgrad(const Shape& s, int r, const void* U, const void* V,
-                        int A, int A0, int B, float* out0, float* out1,
-                        const PlanBuffers& b, const int32_t* rows_host,
-                        hipStream_t st);
+// Weight gradients of rounds r .. r + nr - 1 (nr = 1 or 2; round r's
+// buffers U, V, round r + 1's U1, V1): out_e[a][b] (+)= sum over expert e's
+// rows c of those rounds of U[c][a] V[c][b] (U: A features per row, V: B,
+// tiled round buffers), rows a < A0 into out0 [E][A0][B], the rest into
+// out1 [E][A-A0][B]; fp32. The launch with r = 0 stores (every expert,
+// zeros where it has no rows), later launches add. rows0, rows1: the
+// rounds' rows per expert on the host.
+hipError_t launch_wgrad(const Shape& s, int r, int nr, const void* U, const void* V,
+                        const void* U1, const void* V1, int A, int A0, int B,
+                        float* out0, float* out1, const PlanBuffers& b,
+                        const int32_t* rows0, const int32_t* rows1, hipStream_t st);
 
 // Router-weight gradient dlogits [T][E] (fp32) from z and dy (bf16).
 hipError_t launch_router_backward(const Shape& s, const void* z, const void* dy,

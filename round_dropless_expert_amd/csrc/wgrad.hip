@@ -3,14 +3,16 @@
 // section "Key claims": grouped expert compute per round; here its
 // gradient with respect to the expert weights).
 //
-// For every expert e with rows in round r, out_e[a][b] (+)= sum over the
-// expert's rows c of the round of U[c][a] * V[c][b], where U (A features)
-// and V (B features) are token-major round buffers in the tiled layout,
-// expert e's matrix starting at buffer row (e / G) * Q + pbase(r, e). Rows
-// a < A0 go to out0[e][a][b], the others to out1[e][a - A0][b] (dW_gate and
-// dW_up from one dgu buffer). out is fp32, row-major; round 0 stores, later
-// rounds add (the contraction over an expert's rows is then split at the
-// round boundaries).
+// For every expert e with rows in round r (or in rounds r and r + 1, whose
+// buffers are the two sets of the backward's round buffers), out_e[a][b]
+// (+)= sum over the expert's rows c of those rounds of U[c][a] * V[c][b],
+// where U (A features) and V (B features) are token-major round buffers in
+// the tiled layout, expert e's matrix of round r starting at buffer row
+// (e / G) * Q + pbase(r, e). Rows a < A0 go to out0[e][a][b], the others to
+// out1[e][a - A0][b] (dW_gate and dW_up from one dgu buffer). out is fp32,
+// row-major; the launch that covers round 0 stores, later ones add (the
+// contraction over an expert's rows is then split at every second round
+// boundary).
 //
 // The contraction runs over tokens, which are rows of both operands, while
 // the matrix cores want each lane to hold consecutive K (token) values of
@@ -96,13 +98,16 @@ typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 struct WgradParams {
-  const bf16* U;   // round buffer, A features per row (tiled)
-  const bf16* V;   // round buffer, B features per row (tiled)
+  const bf16* U;   // round r's buffer, A features per row (tiled)
+  const bf16* V;   // round r's buffer, B features per row (tiled)
+  const bf16* U1;  // round r + 1's buffers (second set; used when nr == 2)
+  const bf16* V1;
   float* out0;     // [E][A0][B]
   float* out1;     // [E][A - A0][B] (NULL when A0 == A)
   const int32_t* rounds;
   const int32_t* n_rounds;
   int E, r, A, A0, B, G, max_rounds, pool_rows;
+  int nr;           // rounds contracted by this launch: r, or r and r + 1
   int tiles;        // tiles of the launch (the grid is this rounded up to 8)
   int all_experts;  // tiles of every expert (round 0: experts without rows get zeros)
   int accumulate;   // add to out (else store)
@@ -115,7 +120,9 @@ __global__ __launch_bounds__(256, 1) void wgrad_kernel(WgradParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wa = wave & 1, wb = wave >> 1;  // this wavefront's 128 x 128 quarter
   const int l32 = lane & 31, half = lane >> 5;
-  if (p.r >= *p.n_rounds) return;
+  const int R = *p.n_rounds;
+  if (p.r >= R) return;
+  const bool two = p.nr == 2 && p.r + 1 < R;
 
   // tile -> expert: expert-major, tiles_a x tiles_b per expert
   const int ta = (p.A + kTile - 1) / kTile, tb = (p.B + kTile - 1) / kTile;
@@ -132,8 +139,10 @@ __global__ __launch_bounds__(256, 1) void wgrad_kernel(WgradParams p) {
   int e;
   if (p.all_experts) {
     e = slot;
-  } else {  // the slot-th expert with rows in this round
-    const bool act = lane < p.E && p.rounds[kAlloc * tbl + (int64_t)p.r * p.E + lane] > 0;
+  } else {  // the slot-th expert with rows in these rounds
+    const bool act =
+        lane < p.E && (p.rounds[kAlloc * tbl + (int64_t)p.r * p.E + lane] > 0 ||
+                       (two && p.rounds[kAlloc * tbl + (int64_t)(p.r + 1) * p.E + lane] > 0));
     const uint64_t mask = __builtin_amdgcn_ballot_w64(act);
     const uint64_t below = lane == 0 ? 0ull : (mask & (~0ull >> (64 - lane)));
     const bool hit = act && __builtin_popcountll(below) == slot;
@@ -142,33 +151,46 @@ __global__ __launch_bounds__(256, 1) void wgrad_kernel(WgradParams p) {
     e = __builtin_ctzll(h);
   }
   if (e >= p.E) return;
-  const int64_t at = (int64_t)p.r * p.E + e;
-  const int m = __builtin_amdgcn_readfirstlane(p.rounds[kAlloc * tbl + at]);
-  const int64_t row0 = (int64_t)(e / p.G) * p.pool_rows + p.rounds[kPbase * tbl + at];
+  // the expert's rows in round r (segment 0) and, with two rounds, in round
+  // r + 1 (segment 1, the second buffer set): m rows padded to 64 each
+  const int64_t at0 = (int64_t)p.r * p.E + e, at1 = at0 + p.E;
+  const int m0 = __builtin_amdgcn_readfirstlane(p.rounds[kAlloc * tbl + at0]);
+  const int m1 = two ? __builtin_amdgcn_readfirstlane(p.rounds[kAlloc * tbl + at1]) : 0;
+  const int64_t gbase = (int64_t)(e / p.G) * p.pool_rows;
+  const int64_t row00 = gbase + p.rounds[kPbase * tbl + at0];
+  const int64_t row01 = two ? gbase + p.rounds[kPbase * tbl + at1] : 0;
   const int a0 = (local / tb) * kTile, b0 = (local % tb) * kTile;
 
-  // the expert's matrices of the round: m rows padded to 64
   const uint32_t ubytes = (uint32_t)p.A * 2, vbytes = (uint32_t)p.B * 2;
-  const uint32_t mpad = (uint32_t)((m + 63) & ~63);
-  const __amdgpu_buffer_rsrc_t ru = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(p.U + row0 * p.A), 0, (int)(mpad * ubytes), kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(p.V + row0 * p.B), 0, (int)(mpad * vbytes), kRsrcWord3);
+  const uint32_t mpad0 = (uint32_t)((m0 + 63) & ~63), mpad1 = (uint32_t)((m1 + 63) & ~63);
+  const __amdgpu_buffer_rsrc_t ru0 = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.U + row00 * p.A), 0, (int)(mpad0 * ubytes), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rv0 = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.V + row00 * p.B), 0, (int)(mpad0 * vbytes), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t ru1 = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(two ? p.U1 + row01 * p.A : p.U), 0, (int)(mpad1 * ubytes), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rv1 = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(two ? p.V1 + row01 * p.B : p.V), 0, (int)(mpad1 * vbytes), kRsrcWord3);
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char*)&lds[0][0];
 
   // Loads of a stage: wavefronts 0-1 fetch U, 2-3 fetch V; load x of a
   // wavefront moves 1 KiB = part x % 2 of the 32-feature half block
   // h = 4 (wave % 2) + x / 2; lane i moves 16 bytes, of token
-  // s*32 + 16 (x % 2) + i / 4 (zeros past m, and past A or B).
+  // k0 + 16 (x % 2) + i / 4 of the stage's segment (zeros past its m, and
+  // past A or B). Stages 0 .. S0-1 are segment 0's, then segment 1's.
   const int op = wave >> 1;
-  const __amdgpu_buffer_rsrc_t rsrc = op == 0 ? ru : rv;
+  const __amdgpu_buffer_rsrc_t rsrc0 = op == 0 ? ru0 : rv0;
+  const __amdgpu_buffer_rsrc_t rsrc1 = op == 0 ? ru1 : rv1;
+  const int S0 = (m0 + kStageTok - 1) / kStageTok;
   const uint32_t rb = op == 0 ? ubytes : vbytes;
   const int fbase = (op == 0 ? a0 : b0) + 128 * (wave & 1);
   const int flim = op == 0 ? p.A : p.B;
   const uint32_t dst0 = lds0 + (uint32_t)(op * kOpBytes + 4 * (wave & 1) * kHalfBlock);
   auto fetch = [&](int s, int x) {
     const int h = x >> 1, part = x & 1;
-    const int k0 = s * kStageTok;
+    const bool seg1 = s >= S0;
+    const int k0 = (seg1 ? s - S0 : s) * kStageTok;
+    const int m = seg1 ? m1 : m0;
     const bool fin = fbase + 32 * h < flim;
     const uint32_t soff =
         fin ? ((uint32_t)(k0 >> 6) * (rb >> 6) + (uint32_t)((fbase >> 5) + h)) * 4096u +
@@ -178,7 +200,7 @@ __global__ __launch_bounds__(256, 1) void wgrad_kernel(WgradParams p) {
     const uint32_t vo = fin && tok < m ? (uint32_t)lane * 16u : kOutOfRange;
     const uint32_t dst =
         dst0 + (uint32_t)((s & 3) * kSlotBytes + h * kHalfBlock + part * 1024);
-    lds_load16(rsrc, vo, soff, dst);
+    lds_load16(seg1 ? rsrc1 : rsrc0, vo, soff, dst);
   };
 
   // this lane's part of a transposed read: group g = lane / 16, position
@@ -210,7 +232,7 @@ __global__ __launch_bounds__(256, 1) void wgrad_kernel(WgradParams p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  const int stages = (m + kStageTok - 1) / kStageTok;
+  const int stages = S0 + (m1 + kStageTok - 1) / kStageTok;
   // prologue: stages 0, 1, 2 in flight, wait for stage 0
 #pragma unroll
   for (int st = 0; st < 3; ++st)
@@ -282,20 +304,21 @@ __global__ __launch_bounds__(256, 1) void wgrad_kernel(WgradParams p) {
 
 }  // namespace
 
-hipError_t launch_wgrad(const Shape& s, int r, const void* U, const void* V,
-                        int A, int A0, int B, float* out0, float* out1,
-                        const PlanBuffers& b, const int32_t* rows_host,
-                        hipStream_t st) {
+hipError_t launch_wgrad(const Shape& s, int r, int nr, const void* U, const void* V,
+                        const void* U1, const void* V1, int A, int A0, int B,
+                        float* out0, float* out1, const PlanBuffers& b,
+                        const int32_t* rows0, const int32_t* rows1, hipStream_t st) {
   int active = 0;
-  for (int e = 0; e < s.E; ++e) active += rows_host[e] > 0;
+  for (int e = 0; e < s.E; ++e) active += rows0[e] > 0 || (nr == 2 && rows1[e] > 0);
   const bool all = r == 0;
   const int n = all ? s.E : active;
   if (n == 0) return hipSuccess;
   const int per = ((A + kTile - 1) / kTile) * ((B + kTile - 1) / kTile);
   const int tiles = n * per;
-  WgradParams p{static_cast<const bf16*>(U), static_cast<const bf16*>(V), out0, out1,
+  WgradParams p{static_cast<const bf16*>(U), static_cast<const bf16*>(V),
+                static_cast<const bf16*>(U1), static_cast<const bf16*>(V1), out0, out1,
                 b.rounds, b.n_rounds, s.E, r, A, A0, B, s.G, (int)s.max_rounds(),
-                (int)s.pool_rows(), tiles, all ? 1 : 0, r == 0 ? 0 : 1};
+                (int)s.pool_rows(), nr, tiles, all ? 1 : 0, r == 0 ? 0 : 1};
   hipLaunchKernelGGL(wgrad_kernel, dim3((unsigned)((tiles + 7) / 8 * 8)), dim3(256), 0,
                      st, p);
   return hipGetLastError();

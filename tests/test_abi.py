@@ -185,8 +185,9 @@ def expected_backward_total(T, E, k, d, f, C, G=1):
     Q = pad if G == 1 else G * (pad + 64)
     rows = E // G * Q
     TK = T * k
-    parts = [rows * d * 2, rows * d * 2, rows * 2 * f * 2, rows * f * 2,
-             rows * 2 * f * 2, TK * d * 2, TK * 4]
+    # xr, dyr, hw and dgu in two sets (a pair of rounds), gu in one
+    parts = [2 * rows * d * 2, 2 * rows * d * 2, rows * 2 * f * 2, 2 * rows * f * 2,
+             2 * rows * 2 * f * 2, TK * d * 2, TK * 4]
     return sum(al(p) for p in parts)
 
 
