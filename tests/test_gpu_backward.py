@@ -110,3 +110,24 @@ def test_backward_with_row_major_forward_weights_is_identical():
     b = run_backward(case, layout="row_major")
     for name in ("dx", "dl", "dWg", "dWu", "dWd"):
         assert torch.equal(a[name], b[name]), name
+
+
+def test_backward_of_a_single_token():
+    """T = 1 (one round, k experts with one row each) against the oracle."""
+    w = W("bwd_one_token", T=1, d_model=64, d_ff=128, E=3, k=2, C=1, dtype="bf16")
+    case = Case(w)
+    out = run_backward(case)
+    dy = to_np(out["dy"])
+    inp = case.inp
+    dx_ref, dl_ref = oracle.backward_tokens(np.arange(w.T), case.idx, case.wt, inp.x,
+                                            inp.Wg, inp.Wu, inp.Wd, dy)
+    assert_close(to_np(out["dx"]), dx_ref, "bf16", "dx")
+    assert_close(out["dl"].cpu().numpy(), dl_ref, "bf16", "dlogits")
+    for e in range(w.E):
+        ref = oracle.weight_grads(e, case.idx, case.wt, inp.x, inp.Wg, inp.Wu, inp.Wd, dy)
+        for name, r in zip(("dWg", "dWu", "dWd"), ref):
+            got = out[name][e].cpu().numpy()
+            if np.max(np.abs(r)) == 0.0:
+                assert np.all(got == 0.0), f"{name}[{e}] of an unused expert"
+            else:
+                assert_close(got, r, "bf16", f"{name}[{e}]")

@@ -169,3 +169,33 @@ def test_plan_with_more_chunks_than_the_self_scan_limit(G):
     assert R == p.R
     np.testing.assert_array_equal(counts, p.counts)
     assert_plan_equal(B.workspace_views(cfg, ws), p, idx)
+
+
+EDGE_CASES = [
+    # one token, capacity 1: every expert holds at most one row, one round
+    W("one_token_bf16", T=1, d_model=64, d_ff=64, E=3, k=2, C=1, dtype="bf16"),
+    # 64 experts, 8 per token, 7 tokens: most experts empty, C = 1 gives
+    # up to 7 rounds
+    W("sparse_experts_bf16", T=7, d_model=64, d_ff=128, E=64, k=8, C=1, dtype="bf16"),
+    # fp32, C above T (acts as T), E = 2
+    W("cap_above_T_f32", T=33, d_model=128, d_ff=64, E=2, k=2, C=1000, dtype="f32"),
+]
+
+
+@pytest.mark.parametrize("w", EDGE_CASES, ids=lambda w: w.name)
+def test_degenerate_shapes_forward(w):
+    """The forward through moe_forward on degenerate shapes: plan bit-exact,
+    y within tolerance, every z row written."""
+    case = Case(w)
+    cfg = case.cfg()
+    wg, wu, wd = case.weights()
+    ws = case.workspace(cfg)
+    y = case.new_y()
+    note(f"{w.name}: moe_forward")
+    B.moe_forward(cfg, case.logits, case.x, wg, wu, wd, y, ws)
+    torch.cuda.synchronize()
+    views = B.workspace_views(cfg, ws)
+    p = oracle.plan(case.idx, w.E, w.C)
+    assert_plan_equal(views, p, case.idx)
+    assert_close(to_np(y), case.oracle_y(np.arange(w.T)), w.dtype, "y")
+    assert torch.isfinite(views["z"].float()).all()
