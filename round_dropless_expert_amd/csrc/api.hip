@@ -357,8 +357,9 @@ moe_status_t check_bwd_cfg(const moe_config_t* c) {
   if (c->dtype != MOE_BF16)
     return fail(MOE_ERR_UNSUPPORTED, "the backward supports bf16 only");
   const int64_t ce_pad = (eff_capacity(c) + 63) / 64 * 64;
-  if ((int64_t)group_of(c) * (ce_pad + 64) * 2 * c->d_ff * 2 >= (int64_t(1) << 31))
-    return fail(MOE_ERR_UNSUPPORTED, "G*(C'+64)*2*d_ff*2 must be < 2^31");
+  if ((int64_t)group_of(c) * (ce_pad + 64) * 2 * c->d_ff * 2 >= (int64_t(1) << 31) ||
+      (int64_t)c->d_model * 2 * c->d_ff * 2 >= (int64_t(1) << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "G*(C'+64)*2*d_ff*2 and d*2*d_ff*2 must be < 2^31");
   return MOE_OK;
 }
 
