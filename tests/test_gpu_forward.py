@@ -179,3 +179,32 @@ def test_memory_is_flat_under_skew():
     p3, ws3 = _peak_for("skewed_bf16")
     assert ws2 == ws3
     assert p2 == p3, f"peak bytes differ: {p2} vs {p3}"
+
+
+@pytest.mark.parametrize("name,G", [("skewed_bf16", 1), ("skewed_bf16", 4),
+                                    ("hot_expert_bf16", 1), ("tiny_f32", 2)])
+def test_capacity_helper_matches_the_device_plan(name, G):
+    """The rounds moe_capacity_curve derives from a step's counts are the R
+    the device plan reports at each capacity, and the capacity picked for one
+    and two rounds gives at most that many."""
+    case = get_case(name)
+    w = case.w
+    cfg0 = case.cfg(group=G)
+    ws = case.workspace(cfg0, poison=False)
+    note(f"{name}: moe_plan G={G}")
+    _, counts = B.moe_plan(cfg0, case.logits, ws, return_counts=True)
+    picks = [B.capacity_for_rounds(cfg0, counts, t) for t in (1, 2)]
+    caps = sorted(set([1 + w.C // 3, w.C, 2 * w.C] + picks))
+    rounds, sizes = B.capacity_curve(cfg0, counts, caps)
+    del ws
+    for i, C in enumerate(caps):
+        cfg = case.cfg(C, group=G)
+        assert sizes[i] == B.workspace_size(cfg)
+        ws = case.workspace(cfg, poison=False)
+        note(f"{name}: moe_plan C={C} G={G}")
+        R = B.moe_plan(cfg, case.logits, ws)
+        assert R == rounds[i, 0], (C, R, rounds[i, 0])
+        if C in picks:
+            assert R <= 1 + picks.index(C)
+        del ws
+        torch.cuda.empty_cache()
