@@ -21,8 +21,8 @@
 //
 // Tiles: 256 threads = 2 x 2 wavefronts; wavefront (wm, wn) owns WJ 32-token
 // blocks and WI 32-weight-row blocks. K advances 64 bytes per stage (32 bf16
-// or 16 fp32); SPB stages form a slot of a five-slot LDS ring filled by
-// LDS-direct buffer loads, with up to four slots in flight and one barrier
+// or 16 fp32); SPB stages form a slot of a four-slot LDS ring filled by
+// LDS-direct buffer loads, with up to three slots in flight and one barrier
 // per slot. Fragment reads run one MFMA step ahead of the MFMAs that use
 // them. Three tile shapes, chosen per round: 256 weight rows x 256 tokens,
 // 256 x 128, and 128 x 64 (two stages per slot) for rounds of a few rows
@@ -142,20 +142,17 @@ typedef __attribute__((address_space(3))) char lds_char;
 // the compiler then neither tracks them (every wait on them is the kernel's
 // own, explicit and exact, vmcnt count) nor moves them, so they stay
 // exactly where the stage loop interleaves them with the MFMAs. They have
-// no register results. M0 is saved and restored around each one, with the
-// wait state an LDS-direct load needs after an M0 write.
+// no register results. M0 is declared clobbered (the compiler restores it
+// where it needs it); one wait state separates the M0 write from the load.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff,
                                            uint32_t soff, uint32_t lds) {
-  uint32_t saved;
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
+      "s_mov_b32 m0, %0\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
+      "buffer_load_dwordx4 %1, %2, %3 offen lds"
+      :
       : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
       : "m0");
 }
@@ -235,7 +232,8 @@ struct TileSmall {   // 128 x 64, two K stages per slot: rounds of a few
 constexpr int kNonTemporal = 2;
 
 // Offset that puts a buffer load out of range: the load returns zeros and
-// touches no memory (every real offset is below 2^31).
+// touches no memory (every real offset is below 2^31, so a real base plus
+// this offset is still out of range).
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
 // Where one tile's operands live: buffer descriptors over the expert's
@@ -245,7 +243,7 @@ template <int kWPasses, int kTPasses>
 struct TileSrc {
   __amdgpu_buffer_rsrc_t rw0, rw1, ra;
   uint32_t wbase[kWPasses];  // weight pass offsets
-  uint32_t tbase[kTPasses];  // token pass offsets, kOutOfRange if dead
+  uint32_t tbase[kTPasses];  // token pass offsets (past the rows: out of range)
 };
 
 template <typename Elem, int WI, int WJ, int SPB, int kMode>
@@ -343,9 +341,10 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
   const uint32_t vo_t = (uint32_t)tid * 16;
 
   // Tile t: expert, feature block and token block, and its operand sources.
-  // Weight rows at or past N and token bands past m or past the round
-  // buffer fall outside the descriptors' ranges or get kOutOfRange, so they
-  // read as zeros; they only feed outputs that are never stored.
+  // Weight rows at or past N and token bands past the expert's m rows fall
+  // outside the descriptors' ranges, so they read as zeros; they only feed
+  // outputs that are never stored. Offsets stay below 2^32: the matrices'
+  // bytes are below 2^31 and a tile reaches at most three bands past them.
   int e = 0, m = 0, n0 = 0, m0 = 0;
   auto locate = [&](int t, int& te, int& tm, int& tn0, int& tm0) {
     // expert of the tile: the number of experts whose tiles all come first
@@ -377,8 +376,7 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
     }
 #pragma unroll
     for (int j = 0; j < kTPasses; ++j)
-      S.tbase[j] = tm0 + 64 * j < tm ? (uint32_t)(tm0 / 64 + j) * band_bytes
-                                     : kOutOfRange;
+      S.tbase[j] = (uint32_t)(tm0 / 64 + j) * band_bytes;
     return S;
   };
 
@@ -386,24 +384,35 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
   const int KS = (KT + SPB - 1) / SPB;     // super-stages of one tile
   const int KS4 = (KS + kSlots - 1) / kSlots * kSlots;
 
-  // Load x of the fetch of super-stage ks of the tile with sources S into
-  // `slot_mem`: stage sub = x / kPasses of the super-stage, pass
-  // i = x % kPasses (64 rows: weight rows, then token rows); lane i of a
-  // wavefront writes bytes [16 i, 16 i + 16) of its 1 KiB share of the
-  // pass's 4 KiB. A stage at or past the end of K reads as zeros and adds
-  // exact zeros.
+  // Load x of a super-stage's fetch into `slot_mem`: stage sub = x /
+  // kPasses of the super-stage, pass i = x % kPasses (64 rows: weight rows,
+  // then token rows); lane i of a wavefront writes bytes [16 i, 16 i + 16)
+  // of its 1 KiB share of the pass's 4 KiB. The stage offsets along K are
+  // computed once per super-stage (stage_off); a stage at or past the end of
+  // K gets an out-of-range offset, reads as zeros and adds exact zeros. The
+  // per-load scalar work is then one add: with one wavefront per SIMD every
+  // instruction takes an issue slot the MFMA stream could use.
   const uint32_t lds_wave = (uint32_t)wave_id * 1024;
-  auto fetch_one = [&](char* slot_mem, int ks, const src_t& S, int x) {
+  struct StageOff {
+    uint32_t w[SPB], t[SPB];
+  };
+  auto stage_off = [&](int ks) {
+    StageOff o;
+#pragma unroll
+    for (int sub = 0; sub < SPB; ++sub) {
+      const int g = ks * SPB + sub;
+      const bool in = g < KT;
+      o.w[sub] = in ? (uint32_t)g * wstride : kOutOfRange;
+      o.t[sub] = in ? (uint32_t)g * (uint32_t)kTileBytes : kOutOfRange;
+    }
+    return o;
+  };
+  auto fetch_one = [&](char* slot_mem, const StageOff& o, const src_t& S, int x) {
     const int sub = x / kPasses, i = x % kPasses;
-    const int g = ks * SPB + sub;
     const bool w = i < kWPasses;
     const __amdgpu_buffer_rsrc_t rs =
         !w ? S.ra : ((kGateUp && 64 * i >= BN / 2) ? S.rw1 : S.rw0);
-    const uint32_t base = w ? S.wbase[i] : S.tbase[i - kWPasses];
-    const uint32_t soff =
-        g < KT && base != kOutOfRange
-            ? base + (uint32_t)g * (w ? wstride : (uint32_t)kTileBytes)
-            : kOutOfRange;
+    const uint32_t soff = w ? S.wbase[i] + o.w[sub] : S.tbase[i - kWPasses] + o.t[sub];
     const uint32_t lds = (uint32_t)(uintptr_t)(lds_char*)slot_mem +
                          sub * kStageBytes + i * 4096 + lds_wave;
     lds_load16(rs, w ? vo_w : vo_t, soff, lds);
@@ -429,12 +438,15 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
   // wait for the first
   locate(tile, e, m, n0, m0);
   src_t cur = sources(e, m, n0, m0, true);
+  {
+    const StageOff o0 = stage_off(0), o1 = stage_off(1), o2 = stage_off(2);
 #pragma unroll
-  for (int x = 0; x < kLoads; ++x) fetch_one(slot0, 0, cur, x);
+    for (int x = 0; x < kLoads; ++x) fetch_one(slot0, o0, cur, x);
 #pragma unroll
-  for (int x = 0; x < kLoads; ++x) fetch_one(slot1, 1, cur, x);
+    for (int x = 0; x < kLoads; ++x) fetch_one(slot1, o1, cur, x);
 #pragma unroll
-  for (int x = 0; x < kLoads; ++x) fetch_one(slot2, 2, cur, x);
+    for (int x = 0; x < kLoads; ++x) fetch_one(slot2, o2, cur, x);
+  }
   wait_vmem_barrier<kWait>();
 #pragma unroll
   for (int r = 0; r < kReadsPerStep; ++r) read_one(f0, slot0, 0, r);
@@ -463,9 +475,7 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
     // step; the last step follows the barrier, which waits for ks + 1.
 #define MOE_SUPER(CUR, NXT, FSLOT, KS_)                                          \
     {                                                                           \
-      const int vf = (KS_) + kSlots - 1;                                        \
-      const src_t& SF = vf < KS4 ? cur : nxt;                                   \
-      const int kf = vf < KS4 ? vf : vf - KS4;                                  \
+      const StageOff SO = stage_off((KS_) + kSlots - 1 - fofs);                 \
       _Pragma("unroll") for (int sub = 0; sub < SPB; ++sub) {                   \
         const char* cs = CUR + sub * kStageBytes;                               \
         const char* ns = sub + 1 < SPB ? CUR + (sub + 1) * kStageBytes : NXT;   \
@@ -477,7 +487,7 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
               read_one(f1, cs, s + 1, x);                                       \
             } else {                                                            \
               const int li = ja * kLoadsPerStep + x - kReadsPerStep;            \
-              if (li < kLoads) fetch_one(FSLOT, kf, SF, li);                    \
+              if (li < kLoads) fetch_one(FSLOT, SO, F, li);                    \
             }                                                                   \
           });                                                                   \
           if (last) wait_vmem_barrier<kWait>();                                 \
@@ -488,15 +498,23 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
               read_one(f0, rs_, rstep, x);                                      \
             } else {                                                            \
               const int li = (ja + 1) * kLoadsPerStep + x - kReadsPerStep;      \
-              if (li < kLoads) fetch_one(FSLOT, kf, SF, li);                    \
+              if (li < kLoads) fetch_one(FSLOT, SO, F, li);                    \
             }                                                                   \
           });                                                                   \
         }                                                                       \
       }                                                                         \
     }
 
+    // fetch source: this tile's until the ring reaches position KS4, then
+    // the next tile's (from the second super-stage of the last pass on)
+    src_t F = cur;
+    int fofs = 0;
     for (int ks = 0; ks < KS4; ks += kSlots) {
       MOE_SUPER(slot0, slot1, slot3, ks)
+      if (ks + kSlots == KS4) {
+        F = nxt;
+        fofs = KS4;
+      }
       MOE_SUPER(slot1, slot2, slot0, ks + 1)
       MOE_SUPER(slot2, slot3, slot1, ks + 2)
       MOE_SUPER(slot3, slot0, slot2, ks + 3)
