@@ -338,13 +338,20 @@ def main():
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
+    # an event after every step (they only mark the stream) gives the
+    # per-step GPU times for the median and the minimum; the wall clock over
+    # the whole bracket gives the value
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    marks[0].record(stream)
+    for i in range(args.steps):
         step()
+        marks[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
+    step_ms = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
     tokens_per_s = w.T * args.steps / wall
     peak_bytes = torch.cuda.max_memory_allocated() - base_alloc
     print(f"[bench] timed {args.steps} steps: {ms_per_step:.4f} ms/step",
@@ -469,6 +476,8 @@ def main():
         "metric": METRIC, "value": tokens_per_s, "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms_per_step, "higher_is_better": True,
+        "ms_per_step_median": float(np.median(step_ms)),
+        "ms_per_step_min": step_ms[0],
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic (seeded numpy PCG64; N(0,1) logits and tokens, "
                 "N(0,1/fan_in) weights)",
