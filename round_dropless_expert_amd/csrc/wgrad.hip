@@ -30,7 +30,9 @@
 // v_mfma_f32_32x32x16_bf16, 256 accumulators); the output block is [b][a],
 // so a lane holds four consecutive b of one a: one 16-byte fp32 store.
 // Four LDS slots form a ring with three stages in flight; the kernel waits
-// on its own loads with exact vmcnt counts, as the grouped GEMM does.
+// on its own loads with exact vmcnt counts, as the grouped GEMM does. The
+// fragments of one K step are read while the previous step's MFMAs run
+// (two register sets), interleaved with the MFMAs at fixed points.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -54,21 +56,19 @@ constexpr int kRsrcWord3 = 0x00020000;
 typedef __attribute__((address_space(3))) char lds_char;
 
 // Buffer-to-LDS load (LDS-direct): lane i reads 16 bytes at voff + soff of
-// the buffer and writes them to LDS at m0 + 16 i. Asm, with M0 saved and
-// restored, so that the compiler neither moves nor waits on it: every wait
-// on these loads is the kernel's own, exact vmcnt count.
+// the buffer and writes them to LDS at m0 + 16 i. Asm, so that the compiler
+// neither moves nor waits on it: every wait on these loads is the kernel's
+// own, exact vmcnt count. M0 is declared clobbered (the compiler restores
+// it where it needs it); one wait state separates its write from the load.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff,
                                            uint32_t soff, uint32_t lds) {
-  uint32_t saved;
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
+      "s_mov_b32 m0, %0\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
+      "buffer_load_dwordx4 %1, %2, %3 offen lds"
+      :
       : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
       : "m0");
 }
@@ -186,21 +186,40 @@ __global__ __launch_bounds__(256, 1) void wgrad_kernel(WgradParams p) {
   const int fbase = (op == 0 ? a0 : b0) + 128 * (wave & 1);
   const int flim = op == 0 ? p.A : p.B;
   const uint32_t dst0 = lds0 + (uint32_t)(op * kOpBytes + 4 * (wave & 1) * kHalfBlock);
-  auto fetch = [&](int s, int x) {
+  // per tile: the buffer offset of load x's 1 KiB inside a stage's 64-row
+  // band (out of range for feature blocks at or past A or B)
+  uint32_t xoff[kLoads];
+#pragma unroll
+  for (int x = 0; x < kLoads; ++x) {
     const int h = x >> 1, part = x & 1;
+    xoff[x] = fbase + 32 * h < flim
+                  ? (uint32_t)((fbase >> 5) + h) * 4096u + (uint32_t)part * 1024u
+                  : kOutOfRange;
+  }
+  // Per stage: the segment's descriptor, the stage's offset and, per part,
+  // this lane's offset (out of range for tokens past the segment's m).
+  struct StageLd {
+    __amdgpu_buffer_rsrc_t rs;
+    uint32_t koff;
+    uint32_t vo[2];
+  };
+  auto stage_ld = [&](int s) {
+    StageLd L;
     const bool seg1 = s >= S0;
     const int k0 = (seg1 ? s - S0 : s) * kStageTok;
     const int m = seg1 ? m1 : m0;
-    const bool fin = fbase + 32 * h < flim;
-    const uint32_t soff =
-        fin ? ((uint32_t)(k0 >> 6) * (rb >> 6) + (uint32_t)((fbase >> 5) + h)) * 4096u +
-                  (uint32_t)((k0 >> 5) & 1) * kHalfBlock + (uint32_t)part * 1024u
-            : 0u;
-    const int tok = k0 + part * 16 + (lane >> 2);
-    const uint32_t vo = fin && tok < m ? (uint32_t)lane * 16u : kOutOfRange;
+    L.rs = seg1 ? rsrc1 : rsrc0;
+    L.koff = (uint32_t)(k0 >> 6) * (rb >> 6) * 4096u + (uint32_t)((k0 >> 5) & 1) * kHalfBlock;
+#pragma unroll
+    for (int part = 0; part < 2; ++part)
+      L.vo[part] = k0 + part * 16 + (lane >> 2) < m ? (uint32_t)lane * 16u : kOutOfRange;
+    return L;
+  };
+  auto fetch = [&](const StageLd& L, int s, int x) {
+    const int h = x >> 1, part = x & 1;
     const uint32_t dst =
         dst0 + (uint32_t)((s & 3) * kSlotBytes + h * kHalfBlock + part * 1024);
-    lds_load16(seg1 ? rsrc1 : rsrc0, vo, soff, dst);
+    lds_load16(L.rs, L.vo[part], L.koff + xoff[x], dst);
   };
 
   // this lane's part of a transposed read: group g = lane / 16, position
@@ -233,37 +252,69 @@ __global__ __launch_bounds__(256, 1) void wgrad_kernel(WgradParams p) {
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
   const int stages = S0 + (m1 + kStageTok - 1) / kStageTok;
-  // prologue: stages 0, 1, 2 in flight, wait for stage 0
+  // the fragments of one K step (16 tokens): b blocks, then a blocks
+  bf16x8 fb0[4], fa0[4], fb1[4], fa1[4];
+  // fragment x of a K step, in the order the MFMAs first use them: b
+  // block 0, a blocks 0 .. 3, b blocks 1 .. 3
+  auto read_one = [&](bf16x8 (&fb)[4], bf16x8 (&fa)[4], const char* stage, int ks, int x) {
+    if (x == 0)
+      fb[0] = frag(stage + kOpBytes, wb * 128, ks * 16);
+    else if (x <= 4)
+      fa[x - 1] = frag(stage, wa * 128 + (x - 1) * 32, ks * 16);
+    else
+      fb[x - 4] = frag(stage + kOpBytes, wb * 128 + (x - 4) * 32, ks * 16);
+  };
+  auto read_step = [&](bf16x8 (&fb)[4], bf16x8 (&fa)[4], const char* stage, int ks) {
 #pragma unroll
-  for (int st = 0; st < 3; ++st)
+    for (int x = 0; x < 8; ++x) read_one(fb, fa, stage, ks, x);
+  };
+  // One K step's 16 MFMAs with kOps other operations spread over them in a
+  // fixed order (op(x) after MFMA i for x in [i kOps / 16, (i + 1) kOps /
+  // 16)), each group fenced so that the compiler keeps the order.
+  constexpr int kOps = 8 + kLoads / 2;
+  auto mma_step = [&](const bf16x8 (&fb)[4], const bf16x8 (&fa)[4], auto op) {
 #pragma unroll
-    for (int x = 0; x < kLoads; ++x) fetch(st, x);
+    for (int n = 0; n < 16; ++n) {
+      const int i = n / 4, j = n % 4;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[i], fa[j], acc[i][j], 0, 0, 0);
+#pragma unroll
+      for (int x = n * kOps / 16; x < (n + 1) * kOps / 16; ++x) op(x);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // prologue: stages 0, 1, 2 in flight, wait for stage 0, read its first
+  // step
+#pragma unroll
+  for (int st = 0; st < 3; ++st) {
+    const StageLd L = stage_ld(st);
+#pragma unroll
+    for (int x = 0; x < kLoads; ++x) fetch(L, st, x);
+  }
   wait_vmem_barrier<2 * kLoads>();
+  read_step(fb0, fa0, &lds[0][0], 0);
+  // Stage s: the first K step's MFMAs run while the second step's fragments
+  // are read and half of stage s + 3 is fetched into the slot of s - 1 (every
+  // wavefront's reads of it finished before the previous barrier); then the
+  // barrier waits for stage s + 1 (s + 2 and the first half of s + 3 stay in
+  // flight), and the second step's MFMAs run while stage s + 1's first
+  // fragments are read and the rest of s + 3 is fetched.
   for (int s = 0; s < stages; ++s) {
     const char* cur = &lds[s & 3][0];
-#pragma unroll
-    for (int ks = 0; ks < kStageTok / 16; ++ks) {
-      bf16x8 fb[4], fa[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        fb[i] = frag(cur + kOpBytes, wb * 128 + i * 32, ks * 16);
-        fa[i] = frag(cur, wa * 128 + i * 32, ks * 16);
-      }
-      // stage s + 3 into the slot read at s - 1 (the barrier that ended
-      // s - 1 saw every wavefront's reads of it done), half per K step
-      asm volatile("" ::: "memory");
-#pragma unroll
-      for (int x = 0; x < kLoads / 2; ++x) fetch(s + 3, ks * (kLoads / 2) + x);
-      asm volatile("" ::: "memory");
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[i], fa[j], acc[i][j],
-                                                              0, 0, 0);
-    }
-    // stage s + 1 has landed (s + 2 and s + 3 may be in flight)
-    wait_vmem_barrier<2 * kLoads>();
+    const char* nxt = &lds[(s + 1) & 3][0];
+    const StageLd L = stage_ld(s + 3);
+    mma_step(fb0, fa0, [&](int x) {
+      if (x < 8)
+        read_one(fb1, fa1, cur, 1, x);
+      else
+        fetch(L, s + 3, x - 8);
+    });
+    wait_vmem_barrier<kLoads + kLoads / 2>();
+    mma_step(fb1, fa1, [&](int x) {
+      if (x < 8)
+        read_one(fb0, fa0, nxt, 0, x);
+      else
+        fetch(L, s + 3, kLoads / 2 + x - 8);
+    });
   }
   // the loads that ran past the last stage read nothing but still write
   // LDS: let them land before the workgroup ends
