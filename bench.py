@@ -119,11 +119,16 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes": COPY_BYTES, "launches": 5}), flush=True)
 
 
-def measured_traffic():
+def measured_traffic(w, args):
     """HBM bytes per launch of the round-0 gate/up kernel from the committed
-    counter summary, or None if the kernel source changed since then."""
+    counter summary, or None if the kernel source changed since then or the
+    run is not the launch the summary measured (the balanced bf16 workload
+    with tiled weights, one capacity group and one set of round buffers)."""
     import hashlib
     import re
+    if (w.name != "balanced_bf16" or args.weights != "tiled" or args.group != 1
+            or args.round_buffers != 1):
+        return None
     if not os.path.exists(TRAFFIC_FILE):
         return None
     text = open(TRAFFIC_FILE).read()
@@ -282,6 +287,11 @@ def backward_bench(args):
 
 def main():
     args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this layer runs on one GPU; --gpus {args.gpus} is not "
+              "supported (multi-GPU expert parallelism is not built)",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
     if args.backward:
         backward_bench(args)
         return
@@ -291,11 +301,6 @@ def main():
     if args.capacity_curve:
         capacity_curve(args)
         return
-    if args.gpus != 1:
-        print(f"bench.py: this layer runs on one GPU; --gpus {args.gpus} is not "
-              "supported (multi-GPU expert parallelism is not built)",
-              file=sys.stderr, flush=True)
-        sys.exit(2)
 
     import numpy as np
     import torch
@@ -451,7 +456,7 @@ def main():
     achieved = flops_g0 / sec["gate_up[0]"] / 1e12
     roofline = {"bound": "mfma", "kernel": "grouped gate/up GEMM + SwiGLU, round 0",
                 "achieved": achieved, "peak": peak_tf, "unit": "TFLOP/s",
-                "frac": achieved / peak_tf, "traffic": measured_traffic(),
+                "frac": achieved / peak_tf, "traffic": measured_traffic(w, args),
                 "flops_per_launch": flops_g0,
                 "avg_launch_us": sec["gate_up[0]"] * 1e6}
     kernels = per_launch
