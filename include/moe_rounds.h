@@ -346,8 +346,8 @@ typedef struct {
 } moe_backward_layout_t;
 
 /* Bytes of the backward workspace (pure host function). MOE_ERR_UNSUPPORTED
- * for fp32 configs, and unless G*(P+64)*2f and d*2f bf16 elements stay
- * below 2^31 bytes (P = C' rounded up to 64). */
+ * for fp32 configs, for k > 8, and unless G*(P+64)*2f and d*2f bf16
+ * elements stay below 2^31 bytes (P = C' rounded up to 64). */
 moe_status_t moe_backward_workspace_size(const moe_config_t *cfg, size_t *bytes);
 moe_status_t moe_backward_layout(const moe_config_t *cfg,
                                  moe_backward_layout_t *out);

@@ -356,6 +356,9 @@ moe_status_t check_bwd_cfg(const moe_config_t* c) {
   if (st != MOE_OK) return st;
   if (c->dtype != MOE_BF16)
     return fail(MOE_ERR_UNSUPPORTED, "the backward supports bf16 only");
+  // the router gradient keeps the k dot products of a token in registers
+  if (c->k > moe::kBackwardMaxK)
+    return fail(MOE_ERR_UNSUPPORTED, "the backward supports k <= 8");
   const int64_t ce_pad = (eff_capacity(c) + 63) / 64 * 64;
   if ((int64_t)group_of(c) * (ce_pad + 64) * 2 * c->d_ff * 2 >= (int64_t(1) << 31) ||
       (int64_t)c->d_model * 2 * c->d_ff * 2 >= (int64_t(1) << 31))

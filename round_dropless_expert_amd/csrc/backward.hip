@@ -16,7 +16,7 @@
 namespace moe {
 namespace {
 
-constexpr int kMaxK = 8;
+constexpr int kMaxK = kBackwardMaxK;
 
 // One wavefront per token: each lane takes 8-element (16-byte) pieces of
 // the row, k partial dot products, then a butterfly sum over the lanes.

@@ -42,6 +42,10 @@ inline int64_t plan_scratch_ints(const Shape& s) {
   return (hist_rows(s) + rank_blocks(s)) * s.E;
 }
 
+// Largest k the backward supports (the router gradient keeps a token's k
+// dot products in registers).
+constexpr int kBackwardMaxK = 8;
+
 struct PlanBuffers {
   int32_t* idx;
   float* weight;

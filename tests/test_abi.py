@@ -232,5 +232,13 @@ def test_backward_argument_checks_before_any_hip_call(B):
     f32 = B.config(512, 8, 2, 64, 128, 64, "f32")
     assert L.moe_backward(ctypes.byref(f32), *ptrs, p, need, p, bneed, None) == \
         B.MOE_ERR_UNSUPPORTED
+    # k up to E is a valid forward config; the backward takes k <= 8
+    k9 = B.config(512, 16, 9, 64, 128, 64, "bf16")
+    assert B.check_config(k9) == B.MOE_OK
+    assert L.moe_backward(ctypes.byref(k9), *ptrs, p, need, p, bneed, None) == \
+        B.MOE_ERR_UNSUPPORTED
+    assert "k <= 8" in L.moe_last_error().decode()
+    with pytest.raises(B.MoeError):
+        B.backward_workspace_size(k9)
     assert L.moe_pack_backward_weights(c, p, p, None, p, p, None) == \
         B.MOE_ERR_INVALID_ARGUMENT
