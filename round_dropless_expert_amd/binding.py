@@ -198,6 +198,31 @@ def _ptr(t) -> int:
     return t.data_ptr()
 
 
+def _arg(t, name, dtype=None, numel=None):
+    """Device address of a tensor argument, after checking what the C ABI
+    cannot see from a pointer: a device (cuda) tensor, contiguous, of the
+    element type and with at least the elements the config implies. A host
+    tensor would otherwise reach a kernel as a host address. None and raw
+    integer addresses pass unchanged."""
+    if t is None or isinstance(t, int):
+        return t
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor or an int address")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a device (cuda) tensor, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name}: {t.numel()} elements, the config needs {numel}")
+    return t.data_ptr()
+
+
+def _el(cfg) -> "torch.dtype":
+    return torch.bfloat16 if cfg.dtype == MOE_BF16 else torch.float32
+
+
 def _stream(stream) -> int:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -216,7 +241,9 @@ def moe_plan(cfg, logits, ws, read_rounds=True, stream=None,
     (R, counts) with return_counts (counts: int32 numpy array of E, the
     counts_host argument of the expert calls)."""
     out = (ctypes.c_int32 * (cfg.E + 1))()
-    _check(load().moe_plan(ctypes.byref(cfg), _ptr(logits), _ptr(ws),
+    _check(load().moe_plan(ctypes.byref(cfg),
+                           _arg(logits, "logits", torch.float32, cfg.T * cfg.E),
+                           _arg(ws, "ws"),
                            _nbytes(ws), out if read_rounds else None,
                            _stream(stream)))
     if not read_rounds:
@@ -233,50 +260,67 @@ def _counts(counts_host):
 
 
 def moe_dispatch(cfg, round_, x, ws, stream=None):
-    _check(load().moe_dispatch(ctypes.byref(cfg), int(round_), _ptr(x),
-                               _ptr(ws), _nbytes(ws), _stream(stream)))
+    _check(load().moe_dispatch(ctypes.byref(cfg), int(round_),
+                               _arg(x, "x", _el(cfg), cfg.T * cfg.d_model),
+                               _arg(ws, "ws"), _nbytes(ws), _stream(stream)))
 
 
 def moe_expert_ffn(cfg, round_, w_gate, w_up, w_down, ws, stream=None,
                    counts_host=None):
     c = _counts(counts_host)
-    _check(load().moe_expert_ffn(ctypes.byref(cfg), int(round_), _ptr(w_gate),
-                                 _ptr(w_up), _ptr(w_down), c and c[0],
-                                 _ptr(ws), _nbytes(ws), _stream(stream)))
+    nw = cfg.E * cfg.d_model * cfg.d_ff
+    _check(load().moe_expert_ffn(ctypes.byref(cfg), int(round_),
+                                 _arg(w_gate, "w_gate", _el(cfg), nw),
+                                 _arg(w_up, "w_up", _el(cfg), nw),
+                                 _arg(w_down, "w_down", _el(cfg), nw), c and c[0],
+                                 _arg(ws, "ws"), _nbytes(ws), _stream(stream)))
 
 
 def moe_expert_gate_up(cfg, round_, w_gate, w_up, ws, stream=None,
                        counts_host=None):
     c = _counts(counts_host)
+    nw = cfg.E * cfg.d_model * cfg.d_ff
     _check(load().moe_expert_gate_up(ctypes.byref(cfg), int(round_),
-                                     _ptr(w_gate), _ptr(w_up), c and c[0],
-                                     _ptr(ws), _nbytes(ws), _stream(stream)))
+                                     _arg(w_gate, "w_gate", _el(cfg), nw),
+                                     _arg(w_up, "w_up", _el(cfg), nw), c and c[0],
+                                     _arg(ws, "ws"), _nbytes(ws), _stream(stream)))
 
 
 def moe_expert_down(cfg, round_, w_down, ws, stream=None, counts_host=None):
     c = _counts(counts_host)
     _check(load().moe_expert_down(ctypes.byref(cfg), int(round_),
-                                  _ptr(w_down), c and c[0], _ptr(ws),
+                                  _arg(w_down, "w_down", _el(cfg),
+                                       cfg.E * cfg.d_model * cfg.d_ff),
+                                  c and c[0], _arg(ws, "ws"),
                                   _nbytes(ws), _stream(stream)))
 
 
 def moe_pack_weights(cfg, w_gate, w_up, w_down, out_gate, out_up, out_down,
                      stream=None):
     """Row-major expert weights -> the tiled layout (MOE_WEIGHTS_TILED)."""
-    _check(load().moe_pack_weights(ctypes.byref(cfg), _ptr(w_gate), _ptr(w_up),
-                                   _ptr(w_down), _ptr(out_gate), _ptr(out_up),
-                                   _ptr(out_down), _stream(stream)))
+    nw, el = cfg.E * cfg.d_model * cfg.d_ff, _el(cfg)
+    _check(load().moe_pack_weights(ctypes.byref(cfg), _arg(w_gate, "w_gate", el, nw),
+                                   _arg(w_up, "w_up", el, nw),
+                                   _arg(w_down, "w_down", el, nw),
+                                   _arg(out_gate, "out_gate", el, nw),
+                                   _arg(out_up, "out_up", el, nw),
+                                   _arg(out_down, "out_down", el, nw), _stream(stream)))
 
 
 def moe_combine(cfg, ws, y, stream=None):
-    _check(load().moe_combine(ctypes.byref(cfg), _ptr(ws), _nbytes(ws),
-                              _ptr(y), _stream(stream)))
+    _check(load().moe_combine(ctypes.byref(cfg), _arg(ws, "ws"), _nbytes(ws),
+                              _arg(y, "y", _el(cfg), cfg.T * cfg.d_model),
+                              _stream(stream)))
 
 
 def moe_forward(cfg, logits, x, w_gate, w_up, w_down, y, ws, stream=None):
-    _check(load().moe_forward(ctypes.byref(cfg), _ptr(logits), _ptr(x),
-                              _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(y),
-                              _ptr(ws), _nbytes(ws), _stream(stream)))
+    nw, el, nx = cfg.E * cfg.d_model * cfg.d_ff, _el(cfg), cfg.T * cfg.d_model
+    _check(load().moe_forward(ctypes.byref(cfg),
+                              _arg(logits, "logits", torch.float32, cfg.T * cfg.E),
+                              _arg(x, "x", el, nx), _arg(w_gate, "w_gate", el, nw),
+                              _arg(w_up, "w_up", el, nw), _arg(w_down, "w_down", el, nw),
+                              _arg(y, "y", el, nx), _arg(ws, "ws"), _nbytes(ws),
+                              _stream(stream)))
 
 
 def backward_workspace_size(cfg: MoeConfig) -> int:
@@ -295,19 +339,26 @@ def moe_pack_backward_weights(cfg, w_gate, w_up, w_down, out_down_t,
                               out_gate_up_t, stream=None):
     """Row-major forward weights -> the backward's transposed tiled weights
     (out_down_t [E][f][d], out_gate_up_t [E][d][2f])."""
+    nw, el = cfg.E * cfg.d_model * cfg.d_ff, _el(cfg)
     _check(load().moe_pack_backward_weights(
-        ctypes.byref(cfg), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
-        _ptr(out_down_t), _ptr(out_gate_up_t), _stream(stream)))
+        ctypes.byref(cfg), _arg(w_gate, "w_gate", el, nw), _arg(w_up, "w_up", el, nw),
+        _arg(w_down, "w_down", el, nw), _arg(out_down_t, "out_down_t", el, nw),
+        _arg(out_gate_up_t, "out_gate_up_t", el, 2 * nw), _stream(stream)))
 
 
 def moe_backward(cfg, x, w_gate, w_up, w_down_t, w_gate_up_t, dy, dx, dlogits,
                  dw_gate, dw_up, dw_down, ws, bws, stream=None):
     """The layer's backward after moe_forward (ws: its workspace)."""
+    nw, el, nx = cfg.E * cfg.d_model * cfg.d_ff, _el(cfg), cfg.T * cfg.d_model
+    f32 = torch.float32
     _check(load().moe_backward(
-        ctypes.byref(cfg), _ptr(x), _ptr(w_gate), _ptr(w_up), _ptr(w_down_t),
-        _ptr(w_gate_up_t), _ptr(dy), _ptr(dx), _ptr(dlogits), _ptr(dw_gate),
-        _ptr(dw_up), _ptr(dw_down), _ptr(ws), _nbytes(ws), _ptr(bws),
-        _nbytes(bws), _stream(stream)))
+        ctypes.byref(cfg), _arg(x, "x", el, nx), _arg(w_gate, "w_gate", el, nw),
+        _arg(w_up, "w_up", el, nw), _arg(w_down_t, "w_down_t", el, nw),
+        _arg(w_gate_up_t, "w_gate_up_t", el, 2 * nw), _arg(dy, "dy", el, nx),
+        _arg(dx, "dx", el, nx), _arg(dlogits, "dlogits", f32, cfg.T * cfg.E),
+        _arg(dw_gate, "dw_gate", f32, nw), _arg(dw_up, "dw_up", f32, nw),
+        _arg(dw_down, "dw_down", f32, nw), _arg(ws, "ws"), _nbytes(ws),
+        _arg(bws, "bws"), _nbytes(bws), _stream(stream)))
 
 
 def _counts_rows(cfg: MoeConfig, counts):

@@ -242,3 +242,25 @@ def test_backward_argument_checks_before_any_hip_call(B):
         B.backward_workspace_size(k9)
     assert L.moe_pack_backward_weights(c, p, p, None, p, p, None) == \
         B.MOE_ERR_INVALID_ARGUMENT
+
+
+def test_binding_rejects_host_tensors_before_the_library(B):
+    """A host tensor would reach a kernel as a host address: the binding
+    refuses it (no HIP call is made, so this runs without a GPU)."""
+    import torch
+    T, E, k, d, f = 64, 4, 2, 64, 128
+    cfg = B.config(T, E, k, d, f, 64, "bf16")
+    ws = torch.empty(B.workspace_size(cfg), dtype=torch.uint8)
+    logits = torch.zeros(T, E)
+    x = torch.zeros(T, d, dtype=torch.bfloat16)
+    w = torch.zeros(E, f, d, dtype=torch.bfloat16)
+    wd = torch.zeros(E, d, f, dtype=torch.bfloat16)
+    y = torch.empty_like(x)
+    with pytest.raises(ValueError, match="cuda"):
+        B.moe_forward(cfg, logits, x, w, w, wd, y, ws)
+    with pytest.raises(ValueError, match="cuda"):
+        B.moe_plan(cfg, logits, ws)
+    with pytest.raises(ValueError, match="cuda"):
+        B.moe_pack_weights(cfg, w, w, wd, w, w, wd)
+    with pytest.raises(TypeError):
+        B.moe_forward(cfg, logits.numpy(), x, w, w, wd, y, ws)
