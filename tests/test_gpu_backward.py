@@ -34,13 +34,13 @@ CASES = [
 ]
 
 
-def run_backward(case, C=None, G=1, layout="tiled", seed=7):
+def run_backward(case, C=None, G=1, layout="tiled", seed=7, S=1):
     w = case.w
-    cfg = case.cfg(C, weight_layout=layout, group=G)
+    cfg = case.cfg(C, weight_layout=layout, group=G, round_buffers=S)
     wg, wu, wd = case.weights(layout)
     ws = case.workspace(cfg)
     y = case.new_y()
-    note(f"{w.name}: moe_forward C={cfg.C} G={G} ({layout})")
+    note(f"{w.name}: moe_forward C={cfg.C} G={G} S={S} ({layout})")
     B.moe_forward(cfg, case.logits, case.x, wg, wu, wd, y, ws)
     gen = torch.Generator().manual_seed(seed)
     dy = torch.randn(w.T, w.d_model, generator=gen).to(torch.bfloat16).to(case.dev)
@@ -131,3 +131,16 @@ def test_backward_of_a_single_token():
                 assert np.all(got == 0.0), f"{name}[{e}] of an unused expert"
             else:
                 assert_close(got, r, "bf16", f"{name}[{e}]")
+
+
+@pytest.mark.parametrize("G", [1, 3])
+def test_backward_after_a_two_buffer_forward_is_identical(G):
+    """With two sets of forward round buffers (odd rounds on a side stream)
+    the workspace layout differs; the backward reads the forward's plan and z
+    through it and must give the same bits."""
+    w = CASES[3][0] if G == 3 else CASES[0][0]
+    case = Case(w)
+    a = run_backward(case, G=G, S=1)
+    b = run_backward(case, G=G, S=2)
+    for name in ("dx", "dl", "dWg", "dWu", "dWd"):
+        assert torch.equal(a[name], b[name]), name
