@@ -48,7 +48,10 @@
  * the plan's counts (see moe_forward). All work is enqueued on the caller's
  * HIP stream (`stream` is a hipStream_t; NULL means the null stream). Calls
  * on one workspace must not overlap in time. Device pointers must be
- * 16-byte aligned.
+ * 16-byte aligned and point to memory of the current device: the library
+ * sees plain addresses and cannot tell a host pointer from a device one (a
+ * host address reaching a kernel faults the GPU; the Python binding checks
+ * that its tensor arguments live on the device).
  *
  * Errors: every call returns a moe_status_t and validates its arguments
  * before touching the GPU, so an argument error enqueues nothing. A failed
