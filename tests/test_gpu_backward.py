@@ -89,6 +89,37 @@ def test_backward_matches_oracle(w, G):
         assert torch.isfinite(out[name]).all(), f"unwritten entries in {name}"
 
 
+def test_backward_at_full_balanced_size_on_sampled_tokens_and_experts():
+    """The balanced layer at full size (T = 8192, d = 2048, f = 1024, E = 32,
+    k = 4, C = 1024; tiled weights, the configuration the training-step
+    benchmark runs): dx and dlogits of 48 seeded tokens and the three weight
+    gradients of the first and the last expert against the oracle, which
+    computes them one token or one expert at a time."""
+    w = configs.BALANCED_BF16
+    case = Case(w)
+    out = run_backward(case)
+    dy = to_np(out["dy"])
+    inp = case.inp
+    tokens = np.sort(np.random.default_rng(11).choice(w.T, 48, replace=False))
+    note(f"{w.name}: oracle backward of {tokens.size} tokens")
+    dx_ref, dl_ref = oracle.backward_tokens(tokens, case.idx, case.wt, inp.x, inp.Wg,
+                                            inp.Wu, inp.Wd, dy)
+    assert_close(to_np(out["dx"])[tokens], dx_ref, "bf16", "dx (sampled tokens)")
+    dl = out["dl"].cpu().numpy()
+    assert_close(dl[tokens], dl_ref, "bf16", "dlogits (sampled tokens)")
+    chosen = np.zeros_like(dl, dtype=bool)
+    np.put_along_axis(chosen, case.idx.astype(np.int64), True, axis=1)
+    assert np.all(dl[~chosen] == 0.0)
+    assert torch.isfinite(out["dx"]).all()
+    for e in (0, w.E - 1):
+        note(f"{w.name}: oracle weight gradients of expert {e}")
+        ref = oracle.weight_grads(e, case.idx, case.wt, inp.x, inp.Wg, inp.Wu, inp.Wd, dy)
+        for name, r in zip(("dWg", "dWu", "dWd"), ref):
+            assert_close(out[name][e].cpu().numpy(), r, "bf16", f"{name}[{e}]")
+    for name in ("dWg", "dWu", "dWd"):
+        assert torch.isfinite(out[name]).all(), f"unwritten entries in {name}"
+
+
 def test_backward_input_gradients_do_not_depend_on_capacity():
     w = CASES[0][0]
     case = Case(w)
