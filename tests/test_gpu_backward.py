@@ -89,13 +89,20 @@ def test_backward_matches_oracle(w, G):
         assert torch.isfinite(out[name]).all(), f"unwritten entries in {name}"
 
 
-def test_backward_at_full_balanced_size_on_sampled_tokens_and_experts():
-    """The balanced layer at full size (T = 8192, d = 2048, f = 1024, E = 32,
-    k = 4, C = 1024; tiled weights, the configuration the training-step
-    benchmark runs): dx and dlogits of 48 seeded tokens and the three weight
-    gradients of the first and the last expert against the oracle, which
-    computes them one token or one expert at a time."""
-    w = configs.BALANCED_BF16
+@pytest.mark.parametrize("name,experts", [
+    ("balanced_bf16", (0, 31)),
+    # expert 4 has 2397 rows: rounds 0-2, so its second round pair adds to
+    # the gradient the first pair stored
+    ("skewed_bf16", (4, 31)),
+])
+def test_backward_at_full_size_on_sampled_tokens_and_experts(name, experts):
+    """The layer at full size (T = 8192, d = 2048, f = 1024, E = 32, k = 4,
+    C = 1024; tiled weights, the configuration the training-step benchmark
+    runs), with balanced and with skewed routing (8 rounds): dx and dlogits
+    of 48 seeded tokens and the three weight gradients of two experts
+    against the oracle, which computes them one token or one expert at a
+    time."""
+    w = configs.WORKLOADS[name]
     case = Case(w)
     out = run_backward(case)
     dy = to_np(out["dy"])
@@ -111,7 +118,7 @@ def test_backward_at_full_balanced_size_on_sampled_tokens_and_experts():
     np.put_along_axis(chosen, case.idx.astype(np.int64), True, axis=1)
     assert np.all(dl[~chosen] == 0.0)
     assert torch.isfinite(out["dx"]).all()
-    for e in (0, w.E - 1):
+    for e in experts:
         note(f"{w.name}: oracle weight gradients of expert {e}")
         ref = oracle.weight_grads(e, case.idx, case.wt, inp.x, inp.Wg, inp.Wu, inp.Wd, dy)
         for name, r in zip(("dWg", "dWu", "dWd"), ref):
