@@ -56,8 +56,10 @@
  * Errors: every call returns a moe_status_t and validates its arguments
  * before touching the GPU, so an argument error enqueues nothing. A failed
  * HIP call returns MOE_ERR_HIP and moe_last_error() gives its text (thread
- * local). Device data are not validated: NaN or infinite logits give an
- * unspecified (but in-bounds) routing.
+ * local). Device data are not validated. A NaN logit ranks as -inf; a row
+ * with NaN or infinite logits still gets k distinct experts in [0, E) (so
+ * the plan and every buffer access stay in range), but which ones, and its
+ * routing weights (NaN where the top logit is infinite), are unspecified.
  *
  * Limits of this version: 1 <= E <= 64, 1 <= k <= E, T >= 1, T*k < 2^31,
  * C >= 1, G divides E, d and f positive multiples of 64, and the
@@ -223,18 +225,26 @@ moe_status_t moe_capacity_for_rounds(const moe_config_t *cfg,
                                      int32_t target_rounds, double quantile,
                                      int64_t *capacity);
 
-/* Route and plan: every token picks its top-k experts; each expert's
- * assignments are then split into rounds (the capacity per round is fixed:
- * C' per expert, shared inside its group of G; what does not fit waits for
- * a later round). Reads logits [T][E]; writes idx, weight, counts, offsets,
+/* Route and plan. Routing: every token is sent to a few experts ("Microsoft
+ * AI's MAI-Base-2 trained on 16K GPUs with Muon", section "Expert groups
+ * keep memory fixed when tokens pile up"), here its top-k by logit with the
+ * softmax of the k chosen logits as weights. Plan: each expert's
+ * assignments, in stable token order, are split into rounds of fixed
+ * capacity, C' per expert, shared inside its group of G; what does not fit
+ * waits for a later round and nothing is dropped ("Frontier Pre-training at
+ * Microsoft AI (MAI-Base-2)", section "Key claims", item on multi-round
+ * dropless MoE; same section of the page above). The plan stays on the
+ * device: the later calls read it there. Reads logits [T][E]; writes idx, weight, counts, offsets,
  * perm, pos, round_of, row_of, rounds and n_rounds in the workspace. If plan_host is not NULL
  * (host memory, E + 1 int32) the call waits for the stream and stores the
  * E counts n_e followed by R there; otherwise it is asynchronous. */
 moe_status_t moe_plan(const moe_config_t *cfg, const float *logits, void *ws,
                       size_t ws_bytes, int32_t *plan_host, void *stream);
 
-/* Dispatch of round r (the first of a round's dispatch, compute and collect
- * steps): for every
+/* Dispatch of round r, the first of a round's dispatch, compute and collect
+ * steps ("Frontier Pre-training at Microsoft AI (MAI-Base-2)", section "Key
+ * claims", item on multi-round dropless MoE: each round moves at most the
+ * fixed capacity of tokens to every expert): for every
  * expert e and slot c < m(r,e), copies x[perm[offsets[e] + s + c] / k]
  * (s = the index of e's first entry of round r) into row c of expert e's
  * matrix of the round buffer (tiled layout). Other rows are left
@@ -286,7 +296,11 @@ moe_status_t moe_pack_weights(const moe_config_t *cfg, const void *w_gate,
                               void *out_gate, void *out_up, void *out_down,
                               void *stream);
 
-/* Collect and weighted combine after the last round: y[t] =
+/* Collect and weighted combine after the last round, the collect step of
+ * the rounds ("Frontier Pre-training at Microsoft AI (MAI-Base-2)", section
+ * "Key claims", item on multi-round dropless MoE); the k outputs of a token
+ * are weighted by its routing weights (the pages leave the combine open;
+ * this is the plain reading): y[t] =
  * sum_{j<k} weight[t][j] * z[pos[t*k + j]] (gathering every assignment's
  * expert output back to its token), summed in fp32 over ascending j and
  * rounded once to elem. Reads only the workspace. Asynchronous. */

@@ -44,6 +44,14 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(
     const int64_t row = row0 + seg;
     const bool live = row < last && e < E;
     float v = live ? logits[row * E + e] : -INFINITY;
+    // A NaN compares false both ways and would break the total order: every
+    // NaN lane would keep its own value, consider itself the winner, and a
+    // later pick could fall on a retired or padding key (>= 64), i.e. an
+    // expert index out of range. As -inf it still ranks below every number
+    // and, with key e < 64, above padding (64 + e) and retired lanes
+    // (128 + e); k <= E leaves enough live lanes, so the k picks are always
+    // k distinct experts in [0, E).
+    if (!(v == v)) v = -INFINITY;
     int key = live ? e : kWave + e;  // padding lanes lose every tie
     int sel_e = 0;
     float sel_v = 0.f, top = 0.f;

@@ -199,3 +199,59 @@ def test_degenerate_shapes_forward(w):
     assert_plan_equal(views, p, case.idx)
     assert_close(to_np(y), case.oracle_y(np.arange(w.T)), w.dtype, "y")
     assert torch.isfinite(views["z"].float()).all()
+
+
+@pytest.mark.parametrize("E,k", [(8, 2), (5, 5), (64, 8)])
+def test_nonfinite_logits_give_an_in_range_plan(E, k):
+    """NaN and infinite logits: the routing of such a row is unspecified, but
+    its k picks are distinct experts in [0, E), so the plan stays a valid
+    permutation and every buffer access stays in range; rows with finite
+    logits route and compute exactly as usual."""
+    T, d, f = 96, 64, 128
+    w = W(f"nonfinite_E{E}", T=T, d_model=d, d_ff=f, E=E, k=k, C=17, dtype="f32")
+    from round_dropless_expert_amd import synth
+    inp = synth.generate(w)
+    logits = inp.logits.copy()
+    nan, inf = np.float32("nan"), np.float32("inf")
+    logits[0, :] = nan                                   # all NaN
+    logits[1, :] = nan
+    logits[1, E // 2] = 0.5                              # one finite, rest NaN
+    logits[2, :] = np.array([(nan, inf, -inf, 1.0)[e % 4] for e in range(E)],
+                            dtype=np.float32)            # NaN / inf mix
+    logits[3, :] = -inf                                  # all -inf
+    logits[4, :] = inf                                   # all +inf
+    logits[5, 0] = nan                                   # one NaN in a finite row
+    bad = 6
+    cfg = B.config(T, E, k, d, f, w.C, "f32")
+    ws = torch.full((B.workspace_size(cfg),), 0xFF, dtype=torch.uint8, device="cuda:0")
+    dev_logits = torch.from_numpy(logits).cuda()
+    note(f"{w.name}: moe_plan with non-finite logits")
+    R, counts = B.moe_plan(cfg, dev_logits, ws, return_counts=True)
+    views = B.workspace_views(cfg, ws)
+    idx = views["idx"].cpu().numpy()
+    assert idx.min() >= 0 and idx.max() < E
+    for t in range(T):
+        assert np.unique(idx[t]).size == k, (t, idx[t])
+    assert int(counts.sum()) == T * k
+    np.testing.assert_array_equal(counts, np.bincount(idx.reshape(-1), minlength=E))
+    perm = views["perm"].cpu().numpy()
+    np.testing.assert_array_equal(np.sort(perm), np.arange(T * k))
+    # rows with only finite logits route exactly as the oracle routes them
+    idx_ref, _ = oracle.route(np.ascontiguousarray(logits[bad:]), k)
+    np.testing.assert_array_equal(idx[bad:], idx_ref)
+    # the plan of the whole batch is the oracle's plan of these picks
+    p = oracle.plan(idx, E, w.C)
+    assert R == p.R
+    assert_plan_equal(views, p, idx)
+
+    x, wg, wu, wd = (torch.from_numpy(a).cuda() for a in (inp.x, inp.Wg, inp.Wu, inp.Wd))
+    y = torch.full((T, d), float("nan"), device="cuda:0")
+    note(f"{w.name}: moe_forward with non-finite logits")
+    B.moe_forward(cfg, dev_logits, x, wg, wu, wd, y, ws)
+    torch.cuda.synchronize()
+    # z rows of every assignment are written; finite rows match the oracle
+    assert torch.isfinite(views["z"]).all()
+    _, wt_ref = oracle.route(np.ascontiguousarray(logits[bad:]), k)
+    y_ref = oracle.forward_tokens(np.arange(T - bad), idx_ref, wt_ref,
+                                  inp.x[bad:], inp.Wg, inp.Wu, inp.Wd)
+    assert_close(y[bad:].cpu().numpy(), y_ref, "f32", "y of the finite rows")
