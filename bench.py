@@ -1,16 +1,19 @@
 #!/usr/bin/env python3
 """Throughput of the multi-round dropless MoE layer forward on one MI355X.
 
-A step is one moe_forward over the balanced bf16 workload (T=8192 tokens,
-d_model=2048, d_ff=1024, E=32 experts, top-4, C=ceil(T*k/E)=1024): routing,
-plan, the read of the round count, every round's dispatch + grouped
-gate/up + grouped down/collect, and the weighted combine. Inputs are seeded
-synthetic data already resident in HBM when timing starts.
+A step is one moe_forward: routing, plan, the read of the round count, every
+round's dispatch + grouped gate/up + grouped down/collect, and the weighted
+combine. The default workload is the largest single-GPU one, the hot-expert
+layer (T=32768 tokens, d_model=4096, d_ff=1536, E=64 experts, top-8,
+C=ceil(T*k/(2E))=2048, +10 logit bias on expert 0, so expert 0 takes every
+token over 16 rounds); the balanced layer (T=8192, d_model=2048, d_ff=1024,
+E=32, top-4, C=1024) is measured after it and reported under extra keys.
+Inputs are seeded synthetic data already resident in HBM when timing starts.
 
 Prints one JSON line with the whole-step throughput (tokens/s), the roofline
-of the dominant kernel (the grouped gate/up GEMM, timed with HIP events on
-the stream it runs on), per-kernel figures, and the CPU oracle timed on a
-bounded sample of the same workload.
+of the dominant kernel (the round-0 grouped gate/up GEMM, timed with HIP
+events on the stream it runs on), per-kernel figures, and the CPU oracle
+timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -39,7 +42,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=None,
-                    help="workload name (default: the balanced bf16 layer)")
+                    help="workload name (default: the hot-expert bf16 layer, "
+                         "then the balanced one under extra keys)")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="default run only: skip the balanced workload's extra "
+                         "figures")
     ap.add_argument("--kernel-steps", type=int, default=20,
                     help="steps of the per-kernel timing pass")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -71,41 +78,83 @@ def parse():
     return ap.parse_args()
 
 
+# above this many tokens the oracle's per-token loop runs on a sample
+CPU_FULL_T = 8192
+CPU_SAMPLE = 1024
+
+
+def cpu_sample_tokens(w, plan):
+    """Tokens for the oracle's per-token loop on a large workload: CPU_SAMPLE
+    tokens stratified over the rounds of the most-loaded expert (an equal
+    share from each round's part of its list, seeded), plus tokens 0 and
+    T-1."""
+    import numpy as np
+    rng = np.random.default_rng(1234)
+    e = int(np.argmax(plan.counts))
+    seg = plan.perm[plan.offsets[e]:plan.offsets[e + 1]].astype(np.int64)
+    ce = plan.C_eff
+    rounds = [seg[r * ce:(r + 1) * ce] for r in range(-(-seg.size // ce))]
+    per = -(-CPU_SAMPLE // len(rounds))
+    picks = [np.array([0, w.T - 1], dtype=np.int64)]
+    for part in rounds:
+        n = min(per, part.size)
+        picks.append(rng.choice(part, n, replace=False) // w.k)
+    return np.unique(np.concatenate(picks)), e, len(rounds)
+
+
 def cpu_baseline(w, inp, seconds: float) -> dict:
     """The fp64 oracle as it stands, on the host cores: route + plan over all
-    T tokens, then the per-token expert loop over seeded token batches until
-    about `seconds` of wall time."""
+    T tokens, then the per-token expert loop. Up to CPU_FULL_T tokens: over
+    seeded token batches until about `seconds` of wall time (all T if
+    sooner); above: over the round-stratified sample of cpu_sample_tokens.
+    Per-token work is the same for every token (k experts), so sampled
+    tokens over wall time is the rate."""
     import numpy as np
 
     import oracle
     t0 = time.perf_counter()
     idx, wt = oracle.route(inp.logits, w.k)
-    oracle.plan(idx, w.E, w.C)
+    plan = oracle.plan(idx, w.E, w.C)
     t_plan = time.perf_counter() - t0
-    rng = np.random.default_rng(1234)
-    order = rng.permutation(w.T)
-    done, t_ffn, batch = 0, 0.0, 64
-    while done < w.T and t_ffn < seconds:
-        toks = order[done:done + batch].astype(np.int64)
+    if w.T > CPU_FULL_T:
+        toks, e_hot, n_r = cpu_sample_tokens(w, plan)
         t1 = time.perf_counter()
         oracle.forward_tokens(toks, idx, wt, inp.x, inp.Wg, inp.Wu, inp.Wd)
-        dt = time.perf_counter() - t1
-        t_ffn += dt
-        done += toks.size
-        if dt < seconds / 8:
-            batch *= 2
+        t_ffn = time.perf_counter() - t1
+        done = toks.size
+        sample = (f"{done} tokens of {w.name} (T={w.T}): tokens 0 and T-1 plus "
+                  f"{CPU_SAMPLE} stratified over the {n_r} rounds of expert "
+                  f"{e_hot}, the most loaded (seeded), through the per-token "
+                  f"fp64 expert loop in {t_ffn:.1f} s, plus route+plan over "
+                  f"all {w.T} tokens in {t_plan:.2f} s")
+    else:
+        rng = np.random.default_rng(1234)
+        order = rng.permutation(w.T)
+        done, t_ffn, batch = 0, 0.0, 64
+        while done < w.T and t_ffn < seconds:
+            toks = order[done:done + batch].astype(np.int64)
+            t1 = time.perf_counter()
+            oracle.forward_tokens(toks, idx, wt, inp.x, inp.Wg, inp.Wu, inp.Wd)
+            dt = time.perf_counter() - t1
+            t_ffn += dt
+            done += toks.size
+            if dt < seconds / 8:
+                batch *= 2
+        sample = (f"{done} of {w.T} tokens of {w.name} (seeded order) "
+                  f"through the per-token fp64 expert loop in "
+                  f"{t_ffn:.1f} s, plus route+plan over all {w.T} tokens "
+                  f"in {t_plan:.2f} s")
     per_token = t_ffn / done + t_plan / w.T
     return {"value": 1.0 / per_token, "unit": "tokens/s",
-            "cores": oracle.max_threads(), "kind": "oracle",
-            "sample": f"{done} of {w.T} tokens of {w.name} (seeded order) "
-                      f"through the per-token fp64 expert loop in "
-                      f"{t_ffn:.1f} s, plus route+plan over all {w.T} tokens "
-                      f"in {t_plan:.2f} s"}
+            "cores": oracle.max_threads(), "kind": "oracle", "sample": sample}
 
 
 COPY_BYTES = 256 << 20  # bytes read and bytes written per calibration copy
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic_gate_up_balanced_bf16.md")
 GEMM_SOURCE = os.path.join(ROOT, "round_dropless_expert_amd", "csrc", "grouped_gemm.hip")
+
+
+def traffic_file(name: str) -> str:
+    return os.path.join(ROOT, "profiles", f"pmc_traffic_gate_up_{name}.md")
 
 
 def copy_calibration():
@@ -120,18 +169,18 @@ def copy_calibration():
 
 
 def measured_traffic(w, args):
-    """HBM bytes per launch of the round-0 gate/up kernel from the committed
-    counter summary, or None if the kernel source changed since then or the
-    run is not the launch the summary measured (the balanced bf16 workload
-    with tiled weights, one capacity group and one set of round buffers)."""
+    """HBM bytes per launch of the round-0 gate/up kernel from the workload's
+    committed counter summary, or None if there is none, the kernel source
+    changed since it was taken, or the run is not the launch it measured
+    (tiled weights, one capacity group, one set of round buffers)."""
     import hashlib
     import re
-    if (w.name != "balanced_bf16" or args.weights != "tiled" or args.group != 1
-            or args.round_buffers != 1):
+    if args.weights != "tiled" or args.group != 1 or args.round_buffers != 1:
         return None
-    if not os.path.exists(TRAFFIC_FILE):
+    path = traffic_file(w.name)
+    if not os.path.exists(path):
         return None
-    text = open(TRAFFIC_FILE).read()
+    text = open(path).read()
     m = re.search(r"^source_sha256: ([0-9a-f]{64})$", text, re.M)
     t = re.search(r"^traffic_bytes_per_launch: ([0-9.e+]+)$", text, re.M)
     if not m or not t:
@@ -213,7 +262,8 @@ def backward_bench(args):
     from round_dropless_expert_amd import binding as B
     from round_dropless_expert_amd import configs, synth
 
-    w = configs.WORKLOADS[args.workload] if args.workload else configs.BENCH_WORKLOAD
+    w = (configs.WORKLOADS[args.workload] if args.workload
+         else configs.BACKWARD_BENCH_WORKLOAD)
     B.load()
     B.check_runtime()
     dev = "cuda:0"
@@ -285,32 +335,15 @@ def backward_bench(args):
         "backward_workspace_bytes": B.backward_workspace_size(cfg)}), flush=True)
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py: this layer runs on one GPU; --gpus {args.gpus} is not "
-              "supported (multi-GPU expert parallelism is not built)",
-              file=sys.stderr, flush=True)
-        sys.exit(2)
-    if args.backward:
-        backward_bench(args)
-        return
-    if args.copy_calibration:
-        copy_calibration()
-        return
-    if args.capacity_curve:
-        capacity_curve(args)
-        return
-
+def measure(w, args, steps, warmup, kernel_steps, with_cpu):
+    """One workload: timed moe_forward steps, the per-launch pass, the
+    roofline of the round-0 gate/up launch and (with_cpu) the oracle."""
     import numpy as np
     import torch
 
     from round_dropless_expert_amd import binding as B
     from round_dropless_expert_amd import configs, synth
 
-    w = configs.WORKLOADS[args.workload] if args.workload else configs.BENCH_WORKLOAD
-    B.load()
-    B.check_runtime()
     dev = "cuda:0"
     torch.cuda.set_device(0)
     print(f"[bench] generating {w.name}", file=sys.stderr, flush=True)
@@ -340,26 +373,26 @@ def main():
     def step():
         B.moe_forward(cfg, logits, x, wg, wu, wd, y, ws, stream)
 
-    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
+    print(f"[bench] warmup {warmup}", file=sys.stderr, flush=True)
+    for _ in range(warmup):
         step()
     # an event after every step (they only mark the stream) gives the
     # per-step GPU times for the median and the minimum; the wall clock over
     # the whole bracket gives the value
-    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     marks[0].record(stream)
-    for i in range(args.steps):
+    for i in range(steps):
         step()
         marks[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
-    step_ms = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
-    tokens_per_s = w.T * args.steps / wall
+    ms_per_step = wall * 1e3 / steps
+    step_ms = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(steps))
+    tokens_per_s = w.T * steps / wall
     peak_bytes = torch.cuda.max_memory_allocated() - base_alloc
-    print(f"[bench] timed {args.steps} steps: {ms_per_step:.4f} ms/step",
+    print(f"[bench] timed {steps} steps: {ms_per_step:.4f} ms/step",
           file=sys.stderr, flush=True)
 
     # plan figures for the algorithmic bytes; the counts let the stage calls
@@ -380,7 +413,7 @@ def main():
     stages = ["plan"] + [f"{n}[{r}]" for r in range(R)
                          for n in ("dispatch", "gate_up", "down")] + ["combine"]
     tot = {n: 0.0 for n in stages}
-    for it in range(args.kernel_steps + 2):
+    for it in range(kernel_steps + 2):
         ev = {}
         torch.cuda._sleep(SPIN_CYCLES)
 
@@ -405,7 +438,7 @@ def main():
         if it >= 2:  # two untimed passes
             for n, (e0, e1) in ev.items():
                 tot[n] += e0.elapsed_time(e1) * 1e-3
-    ks = args.kernel_steps
+    ks = kernel_steps
     sec = {n: tot[n] / ks for n in stages}  # seconds per launch
 
     def stage_sum(name):
@@ -479,7 +512,7 @@ def main():
 
     out = {
         "metric": METRIC, "value": tokens_per_s, "unit": "tokens/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "n_gpus": 1, "steps": steps, "warmup": warmup,
         "ms_per_step": ms_per_step, "higher_is_better": True,
         "ms_per_step_median": float(np.median(step_ms)),
         "ms_per_step_min": step_ms[0],
@@ -494,16 +527,56 @@ def main():
                    "rows_per_round": A.tolist()},
         "grouped_gemm_mfma_util_pct": 100.0 * gemm_util,
         "dispatch_GBps": sum(disp_bytes) / t_disp / 1e9,
+        "dispatch_round0_GBps": kernels["dispatch[0]"]["GB/s"],
         "combine_GBps": kernels["combine"]["GB/s"],
         "device_copy_GBps": copy_gbps,
         "workspace_bytes": ws_bytes, "peak_allocated_bytes": peak_bytes,
         "roofline": roofline, "layer_bound": layer_bound, "kernels": kernels,
     }
-    if not args.no_cpu_baseline:
+    if with_cpu:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
-    print(json.dumps(out), flush=True)
+    return out
 
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this layer runs on one GPU; --gpus {args.gpus} is not "
+              "supported (multi-GPU expert parallelism is not built)",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
+    if args.backward:
+        backward_bench(args)
+        return
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    if args.capacity_curve:
+        capacity_curve(args)
+        return
+
+    from round_dropless_expert_amd import binding as B
+    from round_dropless_expert_amd import configs
+
+    B.load()
+    B.check_runtime()
+    w = configs.WORKLOADS[args.workload] if args.workload else configs.BENCH_WORKLOAD
+    out = measure(w, args, args.steps, args.warmup, args.kernel_steps,
+                  not args.no_cpu_baseline)
+    if args.workload is None and not args.no_extra:
+        # the balanced layer beside the headline: its step and launch figures
+        import torch
+        torch.cuda.empty_cache()
+        xb = measure(configs.BALANCED_BF16, args, args.steps, args.warmup,
+                     args.kernel_steps, False)
+        out["extra_workloads"] = {xb["config"]["workload"]: {
+            k: xb[k] for k in ("value", "unit", "ms_per_step", "ms_per_step_median",
+                               "ms_per_step_min", "config", "roofline",
+                               "grouped_gemm_mfma_util_pct", "dispatch_GBps",
+                               "dispatch_round0_GBps", "combine_GBps",
+                               "peak_allocated_bytes", "layer_bound", "kernels")}}
+    print(json.dumps(out), flush=True)
 
 if __name__ == "__main__":
     main()

@@ -167,3 +167,19 @@ def untile(mat_bytes: torch.Tensor, rows: int, cols: int, dtype) -> torch.Tensor
     es = torch.empty(0, dtype=dtype).element_size()
     idx = torch.from_numpy(tiled_index(rows, cols * es)).to(mat_bytes.device)
     return mat_bytes[idx.reshape(-1)].view(rows, cols * es).view(dtype)
+
+
+def tiled_rows(buf: torch.Tensor, rows: np.ndarray, cols: int, dtype) -> torch.Tensor:
+    """Rows `rows` (row indices of one tiled matrix whose rows hold `cols`
+    elements of `dtype`, stored in the byte tensor `buf`) as a row-major
+    [len(rows), cols] tensor."""
+    es = torch.empty(0, dtype=dtype).element_size()
+    rb = cols * es
+    r = np.asarray(rows, dtype=np.int64)[:, None]
+    b = np.arange(rb, dtype=np.int64)[None, :]
+    blk = (r >> 6) * (rb >> 6) + (b >> 6)
+    rr = r & 63
+    bb = b & 63
+    off = blk * 4096 + rr * 64 + (((bb >> 4) ^ ((rr >> 2) & 3)) << 4) + (bb & 15)
+    idx = torch.from_numpy(off.reshape(-1)).to(buf.device)
+    return buf[idx].view(len(rows), rb).view(dtype)

@@ -1,12 +1,15 @@
 """End-to-end parity of moe_forward with the oracle on the five workloads,
-run-to-run and capacity-sweep bit-identity, and fixed memory under skew."""
+stage-level parity at the full sizes of the large ones, run-to-run and
+capacity-sweep bit-identity, and fixed memory under skew."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
 
 import oracle
 from gpu_util import (Case, assert_close, assert_plan_equal, note,
-                      sample_tokens, to_np)
+                      sample_tokens, tiled_rows, to_np)
 from round_dropless_expert_amd import binding as B
 from round_dropless_expert_amd import configs
 
@@ -15,11 +18,18 @@ pytestmark = pytest.mark.gpu
 _cache = {}
 
 
+# the balanced layer's shapes with the hot-expert bias (+10 on expert 0):
+# expert 0 takes every token, 8 rounds at C = 1024
+BALANCED_HOT = dataclasses.replace(configs.BALANCED_BF16, name="balanced_hot_bf16",
+                                   skew=("hot", 0, 10.0))
+
+
 def get_case(name):
     if name not in _cache:
         _cache.clear()
         torch.cuda.empty_cache()
-        _cache[name] = Case(configs.WORKLOADS[name])
+        w = BALANCED_HOT if name == BALANCED_HOT.name else configs.WORKLOADS[name]
+        _cache[name] = Case(w)
     return _cache[name]
 
 
@@ -101,6 +111,66 @@ def test_hot_expert_capacity_sweep_is_bit_identical():
         assert torch.equal(first, yv), f"C={C} differs from C={w.sweep_C[0]}"
 
 
+# sampled slots per round for the gathered rows, assignments for z
+XR_PER_ROUND = 48
+Z_TOTAL = 256
+
+
+@pytest.mark.parametrize("name", ["hot_expert_bf16", "frontier_share_bf16"])
+def test_full_size_stages_on_sampled_slots(name):
+    """The large workloads stage by stage, in moe_forward's launch
+    configuration (each round's tile shape and grid fitted from the plan's
+    counts): the plan bit-exact, gathered rows bit-exact for sampled slots of
+    every round (an expert's first and last slot among them), and the expert
+    outputs z within tolerance for sampled assignments spread over every
+    round, including the one-expert rounds."""
+    case = get_case(name)
+    w = case.w
+    cfg = case.cfg()
+    wg, wu, wd = case.weights()
+    ws = case.workspace(cfg)
+    note(f"{name}: moe_plan (full size)")
+    R, counts = B.moe_plan(cfg, case.logits, ws, return_counts=True)
+    views = B.workspace_views(cfg, ws)
+    p = oracle.plan(case.idx, w.E, w.C)
+    assert_plan_equal(views, p, case.idx)
+    geo = B.buffer_geometry(cfg)
+    rng = np.random.default_rng(11)
+    per_round_z = max(4, Z_TOTAL // R)
+    z_assign = []
+    for r in range(R):
+        note(f"{name}: moe_dispatch round {r} of {R}")
+        B.moe_dispatch(cfg, r, case.x, ws)
+        torch.cuda.synchronize()
+        m = p.rows_in_round(r)
+        first = p.first_in_round(r)
+        slots = [(e, c) for e in range(w.E) if m[e] > 0 for c in range(int(m[e]))]
+        pick = rng.choice(len(slots), min(XR_PER_ROUND, len(slots)), replace=False)
+        busiest = int(np.argmax(m))
+        chosen = {slots[i] for i in pick} | {(busiest, 0), (busiest, int(m[busiest]) - 1)}
+        chosen = sorted(chosen)
+        a = np.array([p.perm[p.offsets[e] + first[e] + c] for e, c in chosen])
+        # G = 1: expert e's matrix of the round starts at buffer row e * P
+        brow = np.array([e * geo["Q"] + c for e, c in chosen])
+        got = tiled_rows(views["xr"], brow, w.d_model, torch.bfloat16)
+        want = case.x[torch.from_numpy(a // w.k).to(case.dev)]
+        assert torch.equal(got.view(torch.int16), want.view(torch.int16)), f"xr round {r}"
+        note(f"{name}: moe_expert_ffn round {r} of {R} (fitted launch shape)")
+        B.moe_expert_ffn(cfg, r, wg, wu, wd, ws, counts_host=counts)
+        in_round = np.nonzero(p.round_of == r)[0]
+        z_assign.append(rng.choice(in_round, min(per_round_z, in_round.size),
+                                   replace=False))
+    torch.cuda.synchronize()
+    a_z = np.concatenate(z_assign)
+    _, o_ref = oracle.assignment_outputs(a_z, case.idx, case.inp.x, case.inp.Wg,
+                                         case.inp.Wu, case.inp.Wd)
+    for r, part in enumerate(z_assign):
+        lo = sum(x.size for x in z_assign[:r])
+        rows = torch.from_numpy(p.pos[part]).to(case.dev).long()
+        assert_close(to_np(views["z"][rows]), o_ref[lo:lo + part.size], w.dtype,
+                     f"z of {name} round {r}")
+
+
 def test_capacity_sweep_small_every_C():
     """Every capacity from 1 to T on the tiny workload gives the same bits."""
     case = get_case("tiny_f32")
@@ -163,22 +233,37 @@ def test_two_round_buffer_sets_are_bit_identical(name):
         torch.cuda.empty_cache()
 
 
-def _peak_for(name):
+def _memory_of(name):
+    """torch's peak over one moe_forward (workspace and y allocated inside
+    the bracket), the workspace size, and the change of the device's free
+    memory (hipMemGetInfo) across a second forward call."""
     case = get_case(name)
     torch.cuda.synchronize()
     torch.cuda.reset_peak_memory_stats()
     base = torch.cuda.memory_allocated()
     cfg, ws, y = forward(case, poison=False)
     peak = torch.cuda.max_memory_allocated() - base
+    free0, _ = torch.cuda.mem_get_info()
+    note(f"{name}: moe_forward again")
+    B.moe_forward(cfg, case.logits, case.x, *case.weights(), y, ws)
+    torch.cuda.synchronize()
+    free1, _ = torch.cuda.mem_get_info()
+    R = int(B.workspace_views(cfg, ws)["n_rounds"].item())
     del ws, y
-    return peak, B.workspace_size(cfg)
+    return peak, B.workspace_size(cfg), free0 - free1, R
 
 
 def test_memory_is_flat_under_skew():
-    p2, ws2 = _peak_for("balanced_bf16")
-    p3, ws3 = _peak_for("skewed_bf16")
-    assert ws2 == ws3
-    assert p2 == p3, f"peak bytes differ: {p2} vs {p3}"
+    """Balanced routing (2 rounds), Zipf skew (8 rounds) and one expert taking
+    every token (8 rounds) on the same shapes: the same workspace and the same
+    peak to the byte, and no device memory taken during the forward itself."""
+    p2, ws2, d2, r2 = _memory_of("balanced_bf16")
+    p3, ws3, d3, r3 = _memory_of("skewed_bf16")
+    ph, wsh, dh, rh = _memory_of(BALANCED_HOT.name)
+    assert (r2, r3, rh) == (2, 8, 8)
+    assert ws2 == ws3 == wsh
+    assert p2 == p3 == ph, f"peak bytes differ: {p2}, {p3}, {ph}"
+    assert d2 == d3 == dh == 0, f"device memory taken by a forward: {d2}, {d3}, {dh}"
 
 
 @pytest.mark.parametrize("name,G", [("skewed_bf16", 1), ("skewed_bf16", 4),

@@ -37,7 +37,9 @@ def test_every_capacity_is_bit_identical_tiny(tiny):
 
 
 def test_capacities_on_balanced_shapes_slice():
-    w = configs.BALANCED_BF16.with_T(256)
+    """A 2048-token slice of the balanced layer's shapes (d = 2048, f = 1024,
+    E = 32, k = 4): capacities 1, 7, ceil(T*k/E) and T give the same bits."""
+    w = configs.BALANCED_BF16.with_T(2048)
     inp = synth.generate(w)
     idx, wt = oracle.route(inp.logits, w.k)
     y = oracle.forward_tokens(np.arange(w.T), idx, wt, inp.x, inp.Wg, inp.Wu,
