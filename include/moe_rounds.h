@@ -327,6 +327,32 @@ moe_status_t moe_forward(const moe_config_t *cfg, const float *logits,
                          const void *w_down, void *y, void *ws,
                          size_t ws_bytes, void *stream);
 
+/* Bytes of the static workspace moe_forward_static uses: a device array
+ * inside the library, one per GPU the library runs on, held until the
+ * process ends. */
+#define MOE_STATIC_WORKSPACE_BYTES ((size_t)64 << 20)
+
+/* moe_forward for callers that cannot allocate memory: serving loops and
+ * harnesses that must not call hipMalloc or create streams and events. The
+ * same layer, kernels and launch shapes as moe_forward, with bit-identical
+ * y, but the workspace is the library's static device array of
+ * MOE_STATIC_WORKSPACE_BYTES on the current device instead of a caller
+ * buffer, and the call creates and allocates nothing (no device or pinned
+ * memory, no stream, no event). The caller passes the inputs and y as for
+ * moe_forward. The plan's counts and R are read into the call's own host
+ * frame with one wait on `stream`; every round then runs on `stream` in
+ * order (with round_buffers = 2 the two buffer sets alternate, without
+ * overlap). A config whose moe_workspace_size exceeds
+ * MOE_STATIC_WORKSPACE_BYTES returns MOE_ERR_WORKSPACE_TOO_SMALL before any
+ * HIP call. All calls on one GPU share its array and it keeps the last
+ * call's contents: calls that overlap in time on one GPU (on different
+ * streams or from different threads) race and give wrong results; calls
+ * queued on one stream do not overlap. */
+moe_status_t moe_forward_static(const moe_config_t *cfg, const float *logits,
+                                const void *x, const void *w_gate,
+                                const void *w_up, const void *w_down, void *y,
+                                void *stream);
+
 /* ------------------------------------------------------------------------
  * Backward (bf16 only). The gradient of a loss through y = layer(x, logits,
  * W), given dy = dL/dy [T][d], with respect to x, the router logits and the

@@ -35,7 +35,7 @@ EXPORTS = ("moe_status_string", "moe_last_error", "moe_hip_runtime_version",
            "moe_expert_down", "moe_pack_weights", "moe_combine", "moe_forward",
            "moe_capacity_curve", "moe_capacity_for_rounds",
            "moe_backward_workspace_size", "moe_backward_layout",
-           "moe_pack_backward_weights", "moe_backward")
+           "moe_pack_backward_weights", "moe_backward", "moe_forward_static")
 
 
 class MoeConfig(ctypes.Structure):
@@ -104,6 +104,7 @@ def load() -> ctypes.CDLL:
     L.moe_pack_weights.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp]
     L.moe_combine.argtypes = [cfgp, vp, sz, vp, vp]
     L.moe_forward.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_forward_static.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp]
     i64, i64p = ctypes.c_int64, ctypes.POINTER(ctypes.c_int64)
     L.moe_capacity_curve.argtypes = [cfgp, i32p, i64, i64p, i32, i32p,
                                      ctypes.POINTER(ctypes.c_size_t)]
@@ -119,7 +120,8 @@ def load() -> ctypes.CDLL:
               "moe_expert_gate_up", "moe_expert_down", "moe_pack_weights",
               "moe_combine", "moe_forward", "moe_capacity_curve",
               "moe_capacity_for_rounds", "moe_backward_workspace_size",
-              "moe_backward_layout", "moe_pack_backward_weights", "moe_backward"):
+              "moe_backward_layout", "moe_pack_backward_weights", "moe_backward",
+              "moe_forward_static"):
         getattr(L, n).restype = ctypes.c_int
     _lib = L
     return L
@@ -321,6 +323,21 @@ def moe_forward(cfg, logits, x, w_gate, w_up, w_down, y, ws, stream=None):
                               _arg(w_up, "w_up", el, nw), _arg(w_down, "w_down", el, nw),
                               _arg(y, "y", el, nx), _arg(ws, "ws"), _nbytes(ws),
                               _stream(stream)))
+
+
+# bytes of the library's static workspace (MOE_STATIC_WORKSPACE_BYTES)
+STATIC_WORKSPACE_BYTES = 64 << 20
+
+
+def moe_forward_static(cfg, logits, x, w_gate, w_up, w_down, y, stream=None):
+    """moe_forward on the library's static device workspace: the call
+    allocates nothing (see moe_forward_static in the header)."""
+    nw, el, nx = cfg.E * cfg.d_model * cfg.d_ff, _el(cfg), cfg.T * cfg.d_model
+    _check(load().moe_forward_static(
+        ctypes.byref(cfg), _arg(logits, "logits", torch.float32, cfg.T * cfg.E),
+        _arg(x, "x", el, nx), _arg(w_gate, "w_gate", el, nw),
+        _arg(w_up, "w_up", el, nw), _arg(w_down, "w_down", el, nw),
+        _arg(y, "y", el, nx), _stream(stream)))
 
 
 def backward_workspace_size(cfg: MoeConfig) -> int:

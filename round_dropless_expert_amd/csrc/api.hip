@@ -12,6 +12,7 @@
 // size each round's launches.
 #include <atomic>
 #include <cstdio>
+#include <mutex>
 #include <algorithm>
 #include <cmath>
 #include <cstring>
@@ -366,6 +367,33 @@ moe_status_t check_bwd_cfg(const moe_config_t* c) {
   return MOE_OK;
 }
 
+
+// Workspace of moe_forward_static: one static device array, which every GPU
+// the library runs on holds, at its own address, until the process ends.
+// Host code never uses the array's name for its memory (on the host the name
+// is only a stand-in): it uses the device address hipGetSymbolAddress returns
+// for the current device, fetched once per device.
+static __device__ __align__(256) char scratch[MOE_STATIC_WORKSPACE_BYTES];
+
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[64];
+
+moe_status_t static_workspace(char** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= 64) return fail(MOE_ERR_UNSUPPORTED, "device id >= 64");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress of the static workspace");
+    if (!ptr) return fail(MOE_ERR_HIP, "hipGetSymbolAddress returned NULL");
+    g_scratch_ptr[dev] = static_cast<char*>(ptr);
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
 
 }  // namespace
 
@@ -781,6 +809,61 @@ moe_status_t moe_forward(const moe_config_t* cfg, const float* logits,
   if (two) {  // the combine reads z rows of every round
     MOE_HIP(hipEventRecord(rb->joined, rb->side), "hipEventRecord");
     MOE_HIP(hipStreamWaitEvent(s, rb->joined, 0), "hipStreamWaitEvent");
+  }
+  MOE_HIP(moe::launch_combine(b.s, b.ws + b.L.z, b.pb.weight, b.pb.pos, y, cus, s),
+          "combine launch");
+  return MOE_OK;
+}
+
+moe_status_t moe_forward_static(const moe_config_t* cfg, const float* logits,
+                                const void* x, const void* w_gate, const void* w_up,
+                                const void* w_down, void* y, void* stream) {
+  moe_status_t st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  moe_workspace_layout_t L;
+  layout_of(cfg, &L);
+  if (L.total > (size_t)MOE_STATIC_WORKSPACE_BYTES) {
+    std::snprintf(g_err, sizeof g_err,
+                  "the config needs a workspace of %zu bytes; the static workspace "
+                  "holds %zu",
+                  L.total, (size_t)MOE_STATIC_WORKSPACE_BYTES);
+    return MOE_ERR_WORKSPACE_TOO_SMALL;
+  }
+  const void* ptrs[] = {logits, x, w_gate, w_up, w_down, y};
+  const char* names[] = {"logits", "x", "w_gate", "w_up", "w_down", "y"};
+  for (int i = 0; i < 6; ++i)
+    if ((st = check_ptr(ptrs[i], names[i])) != MOE_OK) return st;
+  char* ws = nullptr;
+  if ((st = static_workspace(&ws)) != MOE_OK) return st;
+  Bound b;
+  if ((st = bind(cfg, ws, (size_t)MOE_STATIC_WORKSPACE_BYTES, &b)) != MOE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int cus = 0;
+  if ((st = num_cus(&cus)) != MOE_OK) return st;
+  // Nothing in the workspace has to start at zero: the plan writes every
+  // entry it later reads, and the rows of a round buffer past an expert's
+  // rows only feed outputs that are never stored.
+  if ((st = run_plan(b, logits, s)) != MOE_OK) return st;
+  MOE_HIP(moe::launch_dispatch(b.s, 0, x, b.pb, b.xr(0), cus, s), "dispatch launch");
+  // counts and R into host memory of this frame, then one wait
+  int32_t counts_r[kMaxExperts + 1];
+  MOE_HIP(hipMemcpyAsync(counts_r, b.pb.counts, (b.s.E + 1) * sizeof(int32_t),
+                         hipMemcpyDeviceToHost, s),
+          "read of counts and R");
+  MOE_HIP(hipStreamSynchronize(s), "stream sync");
+  const int32_t R = counts_r[b.s.E];
+  const int64_t max_rounds = (b.s.T + b.s.ce - 1) / b.s.ce;
+  if (R < 1 || R > max_rounds)
+    return fail(MOE_ERR_HIP, "device plan reported an impossible round count");
+  int64_t rem[kMaxExperts];
+  for (int e = 0; e < b.s.E; ++e) rem[e] = counts_r[e];
+  int32_t rows[kMaxExperts];
+  // every round on the caller's stream, in order (round r in set r % S)
+  for (int r = 0; r < R; ++r) {
+    if (r > 0)
+      MOE_HIP(moe::launch_dispatch(b.s, r, x, b.pb, b.xr(r), cus, s), "dispatch launch");
+    moe::host_next_round(b.s, rem, rows);
+    if ((st = run_ffn(b, r, w_gate, w_up, w_down, rows, cus, s)) != MOE_OK) return st;
   }
   MOE_HIP(moe::launch_combine(b.s, b.ws + b.L.z, b.pb.weight, b.pb.pos, y, cus, s),
           "combine launch");

@@ -178,6 +178,29 @@ def test_pointer_and_workspace_checks_before_any_hip_call(B):
     assert L.moe_status_string(3) == b"MOE_ERR_WORKSPACE_TOO_SMALL"
 
 
+def test_static_forward_checks_before_any_hip_call(B):
+    """moe_forward_static rejects a config whose workspace exceeds the
+    static one, and bad pointers, before any HIP call."""
+    L = B.load()
+    m = re.search(r"#define MOE_STATIC_WORKSPACE_BYTES \(\(size_t\)(\d+) << (\d+)\)",
+                  open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == B.STATIC_WORKSPACE_BYTES
+    p = 1 << 20
+    big = B.config(8192, 32, 4, 2048, 1024, 1024, "bf16")
+    assert B.workspace_size(big) > B.STATIC_WORKSPACE_BYTES
+    assert L.moe_forward_static(ctypes.byref(big), p, p, p, p, p, p, None) == \
+        B.MOE_ERR_WORKSPACE_TOO_SMALL
+    assert b"static workspace" in L.moe_last_error()
+    small = B.config(512, 8, 2, 64, 128, 64, "f32")
+    c = ctypes.byref(small)
+    assert L.moe_forward_static(c, p, p, p, p, p, None, None) == \
+        B.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_forward_static(c, p, p + 4, p, p, p, p, None) == \
+        B.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_forward_static(None, p, p, p, p, p, p, None) == \
+        B.MOE_ERR_INVALID_ARGUMENT
+
+
 def expected_backward_total(T, E, k, d, f, C, G=1):
     al = lambda v: (v + 255) // 256 * 256
     ce = min(C, T)
