@@ -396,21 +396,26 @@ def measure(w, args, steps, warmup, kernel_steps, with_cpu):
           file=sys.stderr, flush=True)
 
     # plan figures for the algorithmic bytes; the counts let the stage calls
-    # below pick the same launch shapes as moe_forward
+    # below make the launches moe_forward makes (one dispatch and one launch
+    # of each GEMM per launch batch of rounds, with the same launch shapes)
     R, counts = B.moe_plan(cfg, logits, ws, stream=stream, return_counts=True)
+    batches = B.launch_batches(cfg, counts)
     views = B.workspace_views(cfg, ws)
     round_of = views["round_of"].cpu().numpy()
     A = np.bincount(round_of, minlength=R)[:R].astype(np.int64)
-    U = np.array([np.unique(np.nonzero(round_of == r)[0] // w.k).size
-                  for r in range(R)], dtype=np.int64)
     es = 2 if w.dtype == "bf16" else 4
     TK = w.T * w.k
+    # per batch: its label (its rounds), assignments and distinct tokens
+    labels = [f"{r0}" if n == 1 else f"{r0}-{r0 + n - 1}" for r0, n in batches]
+    A_b = [int(A[r0:r0 + n].sum()) for r0, n in batches]
+    U_b = [int(np.unique(np.nonzero((round_of >= r0) & (round_of < r0 + n))[0]
+                         // w.k).size) for r0, n in batches]
 
     # per-kernel pass: HIP events on the same stream around each launch. A
     # spin kernel of about a millisecond goes first, so that the host has
     # queued the whole pass before the GPU reaches it: each event pair then
     # brackets its launch's execution and not the host's time to issue it.
-    stages = ["plan"] + [f"{n}[{r}]" for r in range(R)
+    stages = ["plan"] + [f"{n}[{lb}]" for lb in labels
                          for n in ("dispatch", "gate_up", "down")] + ["combine"]
     tot = {n: 0.0 for n in stages}
     for it in range(kernel_steps + 2):
@@ -427,12 +432,13 @@ def measure(w, args, steps, warmup, kernel_steps, with_cpu):
 
         timed("plan", lambda: B.moe_plan(cfg, logits, ws, read_rounds=False,
                                          stream=stream))
-        for r in range(R):
-            timed(f"dispatch[{r}]", lambda: B.moe_dispatch(cfg, r, x, ws, stream))
-            timed(f"gate_up[{r}]", lambda: B.moe_expert_gate_up(
-                cfg, r, wg, wu, ws, stream, counts_host=counts))
-            timed(f"down[{r}]", lambda: B.moe_expert_down(
-                cfg, r, wd, ws, stream, counts_host=counts))
+        for lb, (r0, n) in zip(labels, batches):
+            timed(f"dispatch[{lb}]",
+                  lambda r0=r0, n=n: B.moe_dispatch(cfg, r0, x, ws, stream, n_rounds=n))
+            timed(f"gate_up[{lb}]", lambda r0=r0, n=n: B.moe_expert_gate_up(
+                cfg, r0, wg, wu, ws, stream, counts_host=counts, n_rounds=n))
+            timed(f"down[{lb}]", lambda r0=r0, n=n: B.moe_expert_down(
+                cfg, r0, wd, ws, stream, counts_host=counts, n_rounds=n))
         timed("combine", lambda: B.moe_combine(cfg, ws, y, stream))
         torch.cuda.synchronize()
         if it >= 2:  # two untimed passes
@@ -442,25 +448,25 @@ def measure(w, args, steps, warmup, kernel_steps, with_cpu):
     sec = {n: tot[n] / ks for n in stages}  # seconds per launch
 
     def stage_sum(name):
-        return sum(sec[f"{name}[{r}]"] for r in range(R))
+        return sum(sec[f"{name}[{lb}]"] for lb in labels)
 
     peak_tf = PEAK_TFLOPS[w.dtype]
     df = float(w.d_model) * w.d_ff
-    disp_bytes = [float(U[r] * w.d_model * es + A[r] * w.d_model * es + 4 * A[r])
-                  for r in range(R)]
+    disp_bytes = [float(U_b[i] * w.d_model * es + A_b[i] * w.d_model * es + 4 * A_b[i])
+                  for i in range(len(batches))]
     comb_bytes = float(TK * w.d_model * es + w.T * w.d_model * es + 8 * TK)
     per_launch = {"plan": {"us": sec["plan"] * 1e6}}
-    for r in range(R):
-        t_d, t_g, t_n = (sec[f"{n}[{r}]"] for n in ("dispatch", "gate_up", "down"))
-        per_launch[f"dispatch[{r}]"] = {
-            "us": t_d * 1e6, "rows": int(A[r]), "GB/s": disp_bytes[r] / t_d / 1e9,
-            "algorithmic_bytes": disp_bytes[r]}
-        per_launch[f"gate_up[{r}]"] = {
-            "us": t_g * 1e6, "rows": int(A[r]),
-            "TFLOP/s": 4.0 * A[r] * df / t_g / 1e12}
-        per_launch[f"down[{r}]"] = {
-            "us": t_n * 1e6, "rows": int(A[r]),
-            "TFLOP/s": 2.0 * A[r] * df / t_n / 1e12}
+    for i, lb in enumerate(labels):
+        t_d, t_g, t_n = (sec[f"{n}[{lb}]"] for n in ("dispatch", "gate_up", "down"))
+        per_launch[f"dispatch[{lb}]"] = {
+            "us": t_d * 1e6, "rows": A_b[i], "GB/s": disp_bytes[i] / t_d / 1e9,
+            "algorithmic_bytes": disp_bytes[i]}
+        per_launch[f"gate_up[{lb}]"] = {
+            "us": t_g * 1e6, "rows": A_b[i],
+            "TFLOP/s": 4.0 * A_b[i] * df / t_g / 1e12}
+        per_launch[f"down[{lb}]"] = {
+            "us": t_n * 1e6, "rows": A_b[i],
+            "TFLOP/s": 2.0 * A_b[i] * df / t_n / 1e12}
     per_launch["combine"] = {"us": sec["combine"] * 1e6,
                              "GB/s": comb_bytes / sec["combine"] / 1e9,
                              "algorithmic_bytes": comb_bytes}
@@ -484,28 +490,31 @@ def measure(w, args, steps, warmup, kernel_steps, with_cpu):
     copy_gbps = 2 * COPY_BYTES * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
     del csrc, cdst
 
-    # dominant kernel: the round-0 grouped gate/up launch (the largest round)
-    flops_g0 = 4.0 * float(A[0]) * df
-    achieved = flops_g0 / sec["gate_up[0]"] / 1e12
-    roofline = {"bound": "mfma", "kernel": "grouped gate/up GEMM + SwiGLU, round 0",
+    # dominant kernel: the grouped gate/up launch of the first batch (round 0,
+    # the largest round)
+    flops_g0 = 4.0 * float(A_b[0]) * df
+    t_g0 = sec[f"gate_up[{labels[0]}]"]
+    achieved = flops_g0 / t_g0 / 1e12
+    roofline = {"bound": "mfma",
+                "kernel": f"grouped gate/up GEMM + SwiGLU, rounds {labels[0]}",
                 "achieved": achieved, "peak": peak_tf, "unit": "TFLOP/s",
                 "frac": achieved / peak_tf, "traffic": measured_traffic(w, args),
-                "flops_per_launch": flops_g0,
-                "avg_launch_us": sec["gate_up[0]"] * 1e6}
+                "flops_per_launch": flops_g0, "avg_launch_us": t_g0 * 1e6}
     kernels = per_launch
 
-    # the layer's attainable time with no overlap: per round the larger of
-    # its GEMM FLOPs at the bf16 peak and the bytes it must stream at 8 TB/s
-    # (active experts' three weight matrices, the round's rows in and out),
-    # plus dispatch and combine bytes at 8 TB/s
+    # the layer's attainable time with no overlap: per launch batch the larger
+    # of its GEMM FLOPs at the bf16 peak and the bytes it must stream at
+    # 8 TB/s (the three weight matrices of each expert with rows in the
+    # batch, the batch's rows in and out), plus dispatch and combine bytes
+    # at 8 TB/s
     views_r = views["rounds"].cpu().numpy()
     hbm = 8.0e12
     bound_s = 0.0
-    for r in range(R):
-        active = int((views_r[0, r] > 0).sum())
-        f_r = 6.0 * A[r] * df
-        b_r = (active * 3.0 * df * es + A[r] * (2 * w.d_model + 2 * w.d_ff) * es)
-        bound_s += max(f_r / (peak_tf * 1e12), b_r / hbm)
+    for i, (r0, n) in enumerate(batches):
+        active = int((views_r[0, r0:r0 + n] > 0).any(axis=0).sum())
+        f_b = 6.0 * A_b[i] * df
+        b_b = (active * 3.0 * df * es + A_b[i] * (2 * w.d_model + 2 * w.d_ff) * es)
+        bound_s += max(f_b / (peak_tf * 1e12), b_b / hbm)
     bound_s += (sum(disp_bytes) + comb_bytes) / hbm
     layer_bound = {"us": bound_s * 1e6, "tokens_per_s": w.T / bound_s,
                    "frac": tokens_per_s * bound_s / w.T}
@@ -524,10 +533,11 @@ def measure(w, args, steps, warmup, kernel_steps, with_cpu):
                    "weight_layout": layout, "group": args.group,
                    "round_buffers": args.round_buffers,
                    "skew": list(w.skew), "rounds": R,
-                   "rows_per_round": A.tolist()},
+                   "rows_per_round": A.tolist(),
+                   "launch_batches": [list(b) for b in batches]},
         "grouped_gemm_mfma_util_pct": 100.0 * gemm_util,
         "dispatch_GBps": sum(disp_bytes) / t_disp / 1e9,
-        "dispatch_round0_GBps": kernels["dispatch[0]"]["GB/s"],
+        "dispatch_round0_GBps": kernels[f"dispatch[{labels[0]}]"]["GB/s"],
         "combine_GBps": kernels["combine"]["GB/s"],
         "device_copy_GBps": copy_gbps,
         "workspace_bytes": ws_bytes, "peak_allocated_bytes": peak_bytes,

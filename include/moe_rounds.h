@@ -138,21 +138,27 @@ typedef struct {
  *                            c (for G = 1: e*C' + i % C'), i = pos[a] -
  *                            offsets[e] its index in expert e's list, c
  *                            its index among e's entries of the round
- *   rounds   int32 [4][M][E] per round r < M = ceil(T/C') and expert e:
- *                            m(r,e); the index in e's list of its first
- *                            entry of round r; the rows of the lower
- *                            experts of e's group in round r; the same
- *                            with each expert's rows rounded up to 64
- *                            (rows r >= R are unused)
+ *   rounds   int32 [9][M][E] + [2][M], M = ceil(T/C'): per round r and
+ *                            expert e, m(r,e); the index in e's list of
+ *                            its first entry of round r; the rows of the
+ *                            lower experts of e's group in round r; the
+ *                            same with each expert's rows rounded up to
+ *                            64; brow(r,e), the buffer row where e's
+ *                            matrix of round r starts (see "Launch
+ *                            batches"). Then the pair tables, indexed by
+ *                            b*E + v: expert, rows, buffer row and first
+ *                            row of z of pair v of launch batch b. Then
+ *                            rbeg[M], rend[M]: the pair indices of round
+ *                            r's first pair and one past its last.
+ *                            Entries of rounds r >= R are unused.
  *   xr       elem [S][E/G][Q][d] round buffers of gathered token rows (set
  *                            r % S for round r): Q = P
  *                            (G = 1) or G*(P+64) rows per group, P = C'
  *                            rounded up to a multiple of 64. In round r
- *                            expert e's rows start at row (padded rounds
- *                            table entry) of its group's block, as an
- *                            m(r,e) x d matrix in the tiled layout (its
- *                            slot c is row c; rows up to the next multiple
- *                            of 64 hold stale data)
+ *                            expert e's rows start at row brow(r,e) of the
+ *                            set, as an m(r,e) x d matrix in the tiled
+ *                            layout (its slot c is row c; rows up to the
+ *                            next multiple of 64 hold stale data)
  *   h        elem [S][E/G][Q][f] SwiGLU activations of the round, same layout
  *   z        elem [T*k][d]   unweighted expert output of every assignment,
  *                            in expert-sorted order: row i holds the output
@@ -161,6 +167,21 @@ typedef struct {
  *   scratch  int32 [...]     plan-internal partial counts
  * The layout, and so the size, is a pure function of the config.
  */
+/* Launch batches. The forward does not need one dispatch and one launch of
+ * each grouped GEMM per round: with G = 1 and one set of round buffers, a
+ * round's experts with rows (its "pairs") fill only some of the E expert
+ * regions of the round buffer, so consecutive rounds run together while
+ * their pairs fit in the E regions (a per-execution schedule of the same
+ * plan: rounds, slots and results are unchanged, memory stays the same
+ * buffer). Rounds are taken in order; a round joins the current batch if
+ * its pairs still fit, else it opens the next one. Pair v of a batch
+ * (numbered round by round, experts ascending inside a round) uses region
+ * v: its matrix starts at buffer row brow(r,e) = v * P. With G > 1 or two
+ * sets of round buffers every round is a batch of its own and brow(r,e) is
+ * the expert's place in its group's block, (e / G) * Q + (padded rows of
+ * the group's lower experts). moe_launch_batches lists the batches from a
+ * step's counts. */
+
 typedef struct {
   size_t idx, weight, counts, offsets, n_rounds, perm, pos, round_of, row_of,
       rounds, scratch, xr, h, z;
@@ -241,51 +262,68 @@ moe_status_t moe_capacity_for_rounds(const moe_config_t *cfg,
 moe_status_t moe_plan(const moe_config_t *cfg, const float *logits, void *ws,
                       size_t ws_bytes, int32_t *plan_host, void *stream);
 
-/* Dispatch of round r, the first of a round's dispatch, compute and collect
- * steps ("Frontier Pre-training at Microsoft AI (MAI-Base-2)", section "Key
- * claims", item on multi-round dropless MoE: each round moves at most the
- * fixed capacity of tokens to every expert): for every
- * expert e and slot c < m(r,e), copies x[perm[offsets[e] + s + c] / k]
- * (s = the index of e's first entry of round r) into row c of expert e's
- * matrix of the round buffer (tiled layout). Other rows are left
- * untouched.
- * 0 <= round < ceil(T / C'); a round >= R moves nothing. Asynchronous. */
-moe_status_t moe_dispatch(const moe_config_t *cfg, int32_t round,
-                          const void *x, void *ws, size_t ws_bytes,
-                          void *stream);
+/* The launch batches of a step (see "Launch batches") from its counts
+ * (host, E int32 as moe_plan stores them; each in [0, T] and summing to
+ * T*k): batch i covers rounds [first_round[i], first_round[i] +
+ * n_rounds[i]). Writes at most max_batches entries and their number to
+ * *n_batches (MOE_ERR_INVALID_ARGUMENT if there are more). Pure host
+ * function, no HIP call. */
+moe_status_t moe_launch_batches(const moe_config_t *cfg, const int32_t *counts_host,
+                                int32_t max_batches, int32_t *first_round,
+                                int32_t *n_rounds, int32_t *n_batches);
 
-/* Expert compute and collect of round r: for every expert e with
- * m(r,e) > 0, h = silu(xr_e . w_gate[e]^T) * (xr_e . w_up[e]^T) on the
- * first m(r,e) rows of expert e's matrix, then o = h . w_down[e]^T, and
- * row c of o is stored at z[offsets[e] + s + c], the row of assignment
- * perm[offsets[e] + s + c] (s as for moe_dispatch; the combine collects
- * these rows back to token order). Each product is one grouped GEMM launch
- * over all active experts (one GEMM per expert group rather than per
- * expert: "Frontier Pre-training at Microsoft AI (MAI-Base-2)", section
- * "Key claims", summarizing the post's "Reducing per-expert overhead").
+/* Dispatch of rounds r = round .. round + n_rounds - 1, the first of a
+ * round's dispatch, compute and collect steps ("Frontier Pre-training at
+ * Microsoft AI (MAI-Base-2)", section "Key claims", item on multi-round
+ * dropless MoE: each round moves at most the fixed capacity of tokens to
+ * every expert): for every expert e and slot c < m(r,e), copies
+ * x[perm[offsets[e] + s + c] / k] (s = the index of e's first entry of
+ * round r) into row c of the matrix of (r, e), at buffer row brow(r,e) of
+ * set round % S (tiled layout). Other rows are left untouched. The rounds
+ * must lie in one launch batch (n_rounds = 1 always does); rounds >= R move
+ * nothing. 0 <= round, 1 <= n_rounds, round + n_rounds <= ceil(T / C').
+ * Asynchronous. */
+moe_status_t moe_dispatch(const moe_config_t *cfg, int32_t round,
+                          int32_t n_rounds, const void *x, void *ws,
+                          size_t ws_bytes, void *stream);
+
+/* Expert compute and collect of rounds r = round .. round + n_rounds - 1
+ * (one launch batch): for every pair (r, e) with m(r,e) > 0, h =
+ * silu(xr_re . w_gate[e]^T) * (xr_re . w_up[e]^T) on the first m(r,e) rows
+ * of the matrix of (r, e), then o = h . w_down[e]^T, and row c of o is
+ * stored at z[offsets[e] + s + c], the row of assignment perm[offsets[e] +
+ * s + c] (s as for moe_dispatch; the combine collects these rows back to
+ * token order). Each product is one grouped GEMM launch over all the
+ * pairs (one GEMM per expert group rather than per expert: "Frontier
+ * Pre-training at Microsoft AI (MAI-Base-2)", section "Key claims",
+ * summarizing the post's "Reducing per-expert overhead").
  * counts_host: NULL, or a host copy of the E counts n_e (the first E values
- * moe_plan stores in plan_host). With it the launch shape fits the round:
- * the output tile (256 x 256, 256 x 128 or 128 x 64) with the least
- * estimated time for the round's rows, and no more workgroups than tiles
- * (what moe_forward does); without it the 256 x 256 tile and one workgroup
- * per CU are used. The results are bit-identical either way.
- * 0 <= round < ceil(T / C'); a round >= R computes nothing. Asynchronous. */
+ * moe_plan stores in plan_host). With it the launch shape fits the pairs'
+ * rows: the output tile (256 x 256, 256 x 128 or 128 x 64) with the least
+ * estimated time, and no more workgroups than tiles (what moe_forward
+ * does), and rounds that are not in one launch batch are refused
+ * (MOE_ERR_INVALID_ARGUMENT); without it the 256 x 256 tile and one
+ * workgroup per CU are used, and such rounds compute nothing. The results
+ * are bit-identical either way. Rounds >= R compute nothing. 0 <= round,
+ * 1 <= n_rounds, round + n_rounds <= ceil(T / C'). Asynchronous. */
 moe_status_t moe_expert_ffn(const moe_config_t *cfg, int32_t round,
-                            const void *w_gate, const void *w_up,
-                            const void *w_down, const int32_t *counts_host,
-                            void *ws, size_t ws_bytes, void *stream);
+                            int32_t n_rounds, const void *w_gate,
+                            const void *w_up, const void *w_down,
+                            const int32_t *counts_host, void *ws,
+                            size_t ws_bytes, void *stream);
 
 /* The two halves of moe_expert_ffn, for callers that time or schedule them
  * separately: gate/up writes h for round r (first m(r,e) rows of each
  * expert's region), down reads h and writes the round's rows of z. Same
  * arguments, layouts and asynchrony as moe_expert_ffn. */
 moe_status_t moe_expert_gate_up(const moe_config_t *cfg, int32_t round,
-                                const void *w_gate, const void *w_up,
-                                const int32_t *counts_host, void *ws,
-                                size_t ws_bytes, void *stream);
+                                int32_t n_rounds, const void *w_gate,
+                                const void *w_up, const int32_t *counts_host,
+                                void *ws, size_t ws_bytes, void *stream);
 moe_status_t moe_expert_down(const moe_config_t *cfg, int32_t round,
-                             const void *w_down, const int32_t *counts_host,
-                             void *ws, size_t ws_bytes, void *stream);
+                             int32_t n_rounds, const void *w_down,
+                             const int32_t *counts_host, void *ws,
+                             size_t ws_bytes, void *stream);
 
 /* Repack expert weights from the row-major layout into the tiled layout
  * (MOE_WEIGHTS_TILED): gate and up are [E][f][d], down is [E][d][f]; each
@@ -307,10 +345,11 @@ moe_status_t moe_pack_weights(const moe_config_t *cfg, const void *w_gate,
 moe_status_t moe_combine(const moe_config_t *cfg, const void *ws,
                          size_t ws_bytes, void *y, void *stream);
 
-/* The whole layer: plan, one wait to learn the counts and R, then R rounds
- * of dispatch and expert compute (launch shapes fitted to each round as
- * with counts_host above), then the collect and weighted combine. y is
- * written in full.
+/* The whole layer: plan, one wait to learn the counts and R, then the R
+ * rounds of dispatch and expert compute, one dispatch and one launch of
+ * each grouped GEMM per launch batch (see "Launch batches"; launch shapes
+ * fitted to each batch as with counts_host above), then the collect and
+ * weighted combine. y is written in full.
  * Returns after enqueueing the combine (the plan's wait is the only host
  * synchronisation; round 0's dispatch is queued before it). For that read
  * the library keeps, per calling thread and device, a pinned host buffer of
@@ -340,9 +379,9 @@ moe_status_t moe_forward(const moe_config_t *cfg, const float *logits,
  * buffer, and the call creates and allocates nothing (no device or pinned
  * memory, no stream, no event). The caller passes the inputs and y as for
  * moe_forward. The plan's counts and R are read into the call's own host
- * frame with one wait on `stream`; every round then runs on `stream` in
- * order (with round_buffers = 2 the two buffer sets alternate, without
- * overlap). A config whose moe_workspace_size exceeds
+ * frame with one wait on `stream`; every launch batch then runs on
+ * `stream` in order (with round_buffers = 2 the two buffer sets alternate,
+ * without overlap). A config whose moe_workspace_size exceeds
  * MOE_STATIC_WORKSPACE_BYTES returns MOE_ERR_WORKSPACE_TOO_SMALL before any
  * HIP call. All calls on one GPU share its array and it keeps the last
  * call's contents: calls that overlap in time on one GPU (on different

@@ -31,7 +31,8 @@ MOE_WEIGHTS_TILED = 1
 
 EXPORTS = ("moe_status_string", "moe_last_error", "moe_hip_runtime_version",
            "moe_check_config", "moe_workspace_size", "moe_workspace_layout",
-           "moe_plan", "moe_dispatch", "moe_expert_ffn", "moe_expert_gate_up",
+           "moe_plan", "moe_launch_batches", "moe_dispatch", "moe_expert_ffn",
+           "moe_expert_gate_up",
            "moe_expert_down", "moe_pack_weights", "moe_combine", "moe_forward",
            "moe_capacity_curve", "moe_capacity_for_rounds",
            "moe_backward_workspace_size", "moe_backward_layout",
@@ -97,10 +98,11 @@ def load() -> ctypes.CDLL:
     L.moe_workspace_size.argtypes = [cfgp, ctypes.POINTER(ctypes.c_size_t)]
     L.moe_workspace_layout.argtypes = [cfgp, ctypes.POINTER(MoeLayout)]
     L.moe_plan.argtypes = [cfgp, vp, vp, sz, i32p, vp]
-    L.moe_dispatch.argtypes = [cfgp, i32, vp, vp, sz, vp]
-    L.moe_expert_ffn.argtypes = [cfgp, i32, vp, vp, vp, i32p, vp, sz, vp]
-    L.moe_expert_gate_up.argtypes = [cfgp, i32, vp, vp, i32p, vp, sz, vp]
-    L.moe_expert_down.argtypes = [cfgp, i32, vp, i32p, vp, sz, vp]
+    L.moe_launch_batches.argtypes = [cfgp, i32p, i32, i32p, i32p, i32p]
+    L.moe_dispatch.argtypes = [cfgp, i32, i32, vp, vp, sz, vp]
+    L.moe_expert_ffn.argtypes = [cfgp, i32, i32, vp, vp, vp, i32p, vp, sz, vp]
+    L.moe_expert_gate_up.argtypes = [cfgp, i32, i32, vp, vp, i32p, vp, sz, vp]
+    L.moe_expert_down.argtypes = [cfgp, i32, i32, vp, i32p, vp, sz, vp]
     L.moe_pack_weights.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp]
     L.moe_combine.argtypes = [cfgp, vp, sz, vp, vp]
     L.moe_forward.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -116,7 +118,7 @@ def load() -> ctypes.CDLL:
     L.moe_backward.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                vp, sz, vp, sz, vp]
     for n in ("moe_check_config", "moe_workspace_size", "moe_workspace_layout",
-              "moe_plan", "moe_dispatch", "moe_expert_ffn",
+              "moe_plan", "moe_launch_batches", "moe_dispatch", "moe_expert_ffn",
               "moe_expert_gate_up", "moe_expert_down", "moe_pack_weights",
               "moe_combine", "moe_forward", "moe_capacity_curve",
               "moe_capacity_for_rounds", "moe_backward_workspace_size",
@@ -261,17 +263,31 @@ def _counts(counts_host):
     return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), a
 
 
-def moe_dispatch(cfg, round_, x, ws, stream=None):
-    _check(load().moe_dispatch(ctypes.byref(cfg), int(round_),
+def launch_batches(cfg, counts_host):
+    """The forward's launch batches for a step's counts: a list of
+    (first_round, n_rounds)."""
+    a = np.ascontiguousarray(counts_host, dtype=np.int32)
+    n_max = max(1, -(-cfg.T // max(1, min(cfg.C, cfg.T))))
+    first = np.zeros(n_max, dtype=np.int32)
+    nr = np.zeros(n_max, dtype=np.int32)
+    n = ctypes.c_int32(0)
+    p32 = lambda v: v.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    _check(load().moe_launch_batches(ctypes.byref(cfg), p32(a), n_max, p32(first),
+                                     p32(nr), ctypes.byref(n)))
+    return [(int(first[i]), int(nr[i])) for i in range(n.value)]
+
+
+def moe_dispatch(cfg, round_, x, ws, stream=None, n_rounds=1):
+    _check(load().moe_dispatch(ctypes.byref(cfg), int(round_), int(n_rounds),
                                _arg(x, "x", _el(cfg), cfg.T * cfg.d_model),
                                _arg(ws, "ws"), _nbytes(ws), _stream(stream)))
 
 
 def moe_expert_ffn(cfg, round_, w_gate, w_up, w_down, ws, stream=None,
-                   counts_host=None):
+                   counts_host=None, n_rounds=1):
     c = _counts(counts_host)
     nw = cfg.E * cfg.d_model * cfg.d_ff
-    _check(load().moe_expert_ffn(ctypes.byref(cfg), int(round_),
+    _check(load().moe_expert_ffn(ctypes.byref(cfg), int(round_), int(n_rounds),
                                  _arg(w_gate, "w_gate", _el(cfg), nw),
                                  _arg(w_up, "w_up", _el(cfg), nw),
                                  _arg(w_down, "w_down", _el(cfg), nw), c and c[0],
@@ -279,18 +295,19 @@ def moe_expert_ffn(cfg, round_, w_gate, w_up, w_down, ws, stream=None,
 
 
 def moe_expert_gate_up(cfg, round_, w_gate, w_up, ws, stream=None,
-                       counts_host=None):
+                       counts_host=None, n_rounds=1):
     c = _counts(counts_host)
     nw = cfg.E * cfg.d_model * cfg.d_ff
-    _check(load().moe_expert_gate_up(ctypes.byref(cfg), int(round_),
+    _check(load().moe_expert_gate_up(ctypes.byref(cfg), int(round_), int(n_rounds),
                                      _arg(w_gate, "w_gate", _el(cfg), nw),
                                      _arg(w_up, "w_up", _el(cfg), nw), c and c[0],
                                      _arg(ws, "ws"), _nbytes(ws), _stream(stream)))
 
 
-def moe_expert_down(cfg, round_, w_down, ws, stream=None, counts_host=None):
+def moe_expert_down(cfg, round_, w_down, ws, stream=None, counts_host=None,
+                    n_rounds=1):
     c = _counts(counts_host)
-    _check(load().moe_expert_down(ctypes.byref(cfg), int(round_),
+    _check(load().moe_expert_down(ctypes.byref(cfg), int(round_), int(n_rounds),
                                   _arg(w_down, "w_down", _el(cfg),
                                        cfg.E * cfg.d_model * cfg.d_ff),
                                   c and c[0], _arg(ws, "ws"),
@@ -420,8 +437,10 @@ def workspace_views(cfg: MoeConfig, ws: torch.Tensor) -> dict:
     """torch views of the internal buffers of a uint8 workspace tensor.
     xr and h are returned as raw bytes of all sets of the round buffer (rows
     of d (f) elements in the tiled layout, see buffer_geometry); rounds is
-    [4, M, E]: rows, first index, rows of the group's lower experts, and
-    the same padded to 64."""
+    [9, M, E]: per (round, expert) rows, first index, rows of the group's
+    lower experts, the same padded to 64, and the buffer row brow; then the
+    pair tables indexed [b, v] (expert, rows, buffer row, first z row);
+    round_pairs is [2, M]: rbeg and rend of every round."""
     L = workspace_layout(cfg)
     T, E, k = cfg.T, cfg.E, cfg.k
     geo = buffer_geometry(cfg)
@@ -443,7 +462,9 @@ def workspace_views(cfg: MoeConfig, ws: torch.Tensor) -> dict:
         "pos": view("pos", T * k, i32, 4),
         "round_of": view("round_of", T * k, i32, 4),
         "row_of": view("row_of", T * k, i32, 4),
-        "rounds": view("rounds", 4 * M * E, i32, 4).view(4, M, E),
+        "rounds": view("rounds", 9 * M * E, i32, 4).view(9, M, E),
+        "round_pairs": ws[L["rounds"] + 36 * M * E:L["rounds"] + 36 * M * E + 8 * M]
+        .view(i32).view(2, M),
         "xr": view("xr", rows * cfg.d_model * es, torch.uint8, 1),
         "h": view("h", rows * cfg.d_ff * es, torch.uint8, 1),
         "z": view("z", T * k * cfg.d_model, el, es).view(T * k, cfg.d_model),

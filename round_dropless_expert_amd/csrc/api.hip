@@ -55,7 +55,7 @@ int sets_of(const moe_config_t* c) {
 moe::Shape shape_of(const moe_config_t* c) {
   return moe::Shape{c->T,       c->E, c->k, c->d_model, c->d_ff, (int)eff_capacity(c),
                     c->dtype == MOE_BF16, c->weight_layout == MOE_WEIGHTS_TILED,
-                    group_of(c)};
+                    group_of(c), group_of(c) == 1 && sets_of(c) == 1};
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
@@ -119,7 +119,7 @@ void layout_of(const moe_config_t* c, moe_workspace_layout_t* L) {
   L->pos = take(TK * 4);
   L->round_of = take(TK * 4);
   L->row_of = take(TK * 4);
-  L->rounds = take(4 * (size_t)s.max_rounds() * E * 4);
+  L->rounds = take((size_t)moe::round_table_ints(s) * 4);
   L->scratch = take((size_t)moe::plan_scratch_ints(s) * 4);
   const size_t sets = (size_t)sets_of(c);
   L->xr = take(sets * (size_t)s.buf_rows() * (size_t)c->d_model * es);
@@ -174,10 +174,13 @@ moe_status_t check_ptr(const void* p, const char* name) {
   return MOE_OK;
 }
 
-moe_status_t check_round(const Bound& b, int32_t round) {
+moe_status_t check_round(const Bound& b, int32_t round, int32_t n_rounds = 1) {
   const int64_t max_rounds = (b.s.T + b.s.ce - 1) / b.s.ce;
   if (round < 0 || round >= max_rounds)
     return fail(MOE_ERR_INVALID_ARGUMENT, "round out of range [0, ceil(T/C'))");
+  if (n_rounds < 1 || (int64_t)round + n_rounds > max_rounds)
+    return fail(MOE_ERR_INVALID_ARGUMENT,
+                "n_rounds must be >= 1 with round + n_rounds <= ceil(T/C')");
   return MOE_OK;
 }
 
@@ -273,26 +276,51 @@ moe_status_t read_plan(const Bound& b, int32_t* out, hipStream_t st) {
   return MOE_OK;
 }
 
-moe_status_t run_ffn(const Bound& b, int r, const void* wg, const void* wu,
-                     const void* wd, const int32_t* rows_host, int cus,
+// The grouped GEMMs of the rounds [r0, r0 + nr) (one launch batch; its
+// buffer set is round r0's), with the rows of its nv pairs on the host.
+moe_status_t run_ffn(const Bound& b, int r0, int nr, const void* wg, const void* wu,
+                     const void* wd, const int32_t* pair_rows, int nv, int cus,
                      hipStream_t st) {
-  MOE_HIP(moe::launch_gate_up(b.s, r, b.xr(r), wg, wu, b.pb, rows_host, b.h(r),
-                              cus, st),
+  MOE_HIP(moe::launch_gate_up(b.s, r0, nr, b.xr(r0), wg, wu, b.pb, pair_rows, nv,
+                              b.h(r0), cus, st),
           "gate/up launch");
-  MOE_HIP(moe::launch_down(b.s, r, b.h(r), wd, b.pb, rows_host,
+  MOE_HIP(moe::launch_down(b.s, r0, nr, b.h(r0), wd, b.pb, pair_rows, nv,
                            b.ws + b.L.z, cus, st),
           "down launch");
   return MOE_OK;
 }
 
-// Rows of every expert in round r from host counts (NULL if counts is NULL).
-const int32_t* rows_from_counts(const moe::Shape& s, const int32_t* counts, int r,
-                                int32_t* rows) {
-  if (!counts) return nullptr;
-  int64_t rem[kMaxExperts];
-  for (int e = 0; e < s.E; ++e) rem[e] = counts[e];
-  for (int rr = 0; rr <= r; ++rr) moe::host_next_round(s, rem, rows);
-  return rows;
+// The rows of the pairs of rounds [r0, r0 + nr) (experts with rows, round
+// by round, in expert order) from host counts, in *pairs; NULL if counts is
+// NULL. The rounds must lie in one launch batch of the forward (else
+// MOE_ERR_INVALID_ARGUMENT): their pairs are then at most E.
+moe_status_t pairs_from_counts(const moe::Shape& s, const int32_t* counts, int r0, int nr,
+                               int32_t* pair_rows, const int32_t** pairs, int* nv) {
+  *nv = 0;
+  *pairs = nullptr;
+  if (!counts) return MOE_OK;
+  for (int e = 0; e < s.E; ++e)
+    if (counts[e] < 0 || counts[e] > s.T)
+      return fail(MOE_ERR_INVALID_ARGUMENT, "counts_host: a count is outside [0, T]");
+  moe::BatchWalker walk(s, counts);
+  moe::LaunchBatch lb;
+  while (walk.next(&lb)) {
+    if (r0 >= lb.r0 + lb.nr) continue;  // a later batch holds r0
+    if (r0 + nr > lb.r0 + lb.nr)
+      return fail(MOE_ERR_INVALID_ARGUMENT,
+                  "rounds [round, round + n_rounds) are not in one launch batch");
+    int64_t rem[kMaxExperts];
+    int32_t rows[kMaxExperts];
+    for (int e = 0; e < s.E; ++e) rem[e] = counts[e];
+    for (int r = 0; r < r0 + nr; ++r) {
+      moe::host_next_round(s, rem, rows);
+      if (r >= r0) *nv += moe::round_pairs(s.E, rows, pair_rows + *nv);
+    }
+    break;
+  }
+  // (rounds past the counts' last round have no pairs)
+  *pairs = pair_rows;
+  return MOE_OK;
 }
 
 // Observed counts must be a plan's: every n_e in [0, T] and their sum T*k.
@@ -392,6 +420,42 @@ moe_status_t static_workspace(char** out) {
     g_scratch_ptr[dev] = static_cast<char*>(ptr);
   }
   *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+// The grouped GEMM launches of a stage call over rounds [round, round +
+// n_rounds): the pairs' rows from the counts (if given) size the launch.
+enum StageGemm { kStageBoth = 0, kStageGateUp = 1, kStageDown = 2 };
+
+moe_status_t stage_gemm(const moe_config_t* cfg, int32_t round, int32_t n_rounds,
+                        const void* w_gate, const void* w_up, const void* w_down,
+                        const int32_t* counts_host, void* ws, size_t ws_bytes,
+                        void* stream, StageGemm which) {
+  Bound b;
+  moe_status_t st = bind(cfg, ws, ws_bytes, &b);
+  if (st != MOE_OK) return st;
+  if (which != kStageDown) {
+    if ((st = check_ptr(w_gate, "w_gate")) != MOE_OK) return st;
+    if ((st = check_ptr(w_up, "w_up")) != MOE_OK) return st;
+  }
+  if (which != kStageGateUp && (st = check_ptr(w_down, "w_down")) != MOE_OK) return st;
+  if ((st = check_round(b, round, n_rounds)) != MOE_OK) return st;
+  int32_t rows[kMaxExperts];
+  const int32_t* pr = nullptr;
+  int nv = 0;
+  if ((st = pairs_from_counts(b.s, counts_host, round, n_rounds, rows, &pr, &nv)) != MOE_OK)
+    return st;
+  int cus = 0;
+  if ((st = num_cus(&cus)) != MOE_OK) return st;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (which != kStageDown)
+    MOE_HIP(moe::launch_gate_up(b.s, round, n_rounds, b.xr(round), w_gate, w_up, b.pb, pr,
+                                nv, b.h(round), cus, hs),
+            "gate/up launch");
+  if (which != kStageGateUp)
+    MOE_HIP(moe::launch_down(b.s, round, n_rounds, b.h(round), w_down, b.pb, pr, nv,
+                             b.ws + b.L.z, cus, hs),
+            "down launch");
   return MOE_OK;
 }
 
@@ -511,76 +575,65 @@ moe_status_t moe_plan(const moe_config_t* cfg, const float* logits, void* ws,
   return MOE_OK;
 }
 
-moe_status_t moe_dispatch(const moe_config_t* cfg, int32_t round, const void* x,
-                          void* ws, size_t ws_bytes, void* stream) {
+moe_status_t moe_launch_batches(const moe_config_t* cfg, const int32_t* counts_host,
+                                int32_t max_batches, int32_t* first_round,
+                                int32_t* n_rounds, int32_t* n_batches) {
+  moe_status_t st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if ((st = check_counts(cfg, counts_host, 1)) != MOE_OK) return st;
+  if (!first_round || !n_rounds || !n_batches || max_batches < 1)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "outputs missing or max_batches < 1");
+  const moe::Shape s = shape_of(cfg);
+  moe::BatchWalker walk(s, counts_host);
+  moe::LaunchBatch lb;
+  int32_t n = 0;
+  while (walk.next(&lb)) {
+    if (n == max_batches)
+      return fail(MOE_ERR_INVALID_ARGUMENT, "more batches than max_batches");
+    first_round[n] = lb.r0;
+    n_rounds[n] = lb.nr;
+    ++n;
+  }
+  *n_batches = n;
+  return MOE_OK;
+}
+
+moe_status_t moe_dispatch(const moe_config_t* cfg, int32_t round, int32_t n_rounds,
+                          const void* x, void* ws, size_t ws_bytes, void* stream) {
   Bound b;
   moe_status_t st = bind(cfg, ws, ws_bytes, &b);
   if (st != MOE_OK) return st;
   if ((st = check_ptr(x, "x")) != MOE_OK) return st;
-  if ((st = check_round(b, round)) != MOE_OK) return st;
+  if ((st = check_round(b, round, n_rounds)) != MOE_OK) return st;
   int cus = 0;
   if ((st = num_cus(&cus)) != MOE_OK) return st;
-  MOE_HIP(moe::launch_dispatch(b.s, round, x, b.pb, b.xr(round), cus,
+  MOE_HIP(moe::launch_dispatch(b.s, round, n_rounds, x, b.pb, b.xr(round), cus,
                                static_cast<hipStream_t>(stream)),
           "dispatch launch");
   return MOE_OK;
 }
 
-moe_status_t moe_expert_ffn(const moe_config_t* cfg, int32_t round,
+moe_status_t moe_expert_ffn(const moe_config_t* cfg, int32_t round, int32_t n_rounds,
                             const void* w_gate, const void* w_up,
                             const void* w_down, const int32_t* counts_host,
                             void* ws, size_t ws_bytes, void* stream) {
-  Bound b;
-  moe_status_t st = bind(cfg, ws, ws_bytes, &b);
-  if (st != MOE_OK) return st;
-  if ((st = check_ptr(w_gate, "w_gate")) != MOE_OK) return st;
-  if ((st = check_ptr(w_up, "w_up")) != MOE_OK) return st;
-  if ((st = check_ptr(w_down, "w_down")) != MOE_OK) return st;
-  if ((st = check_round(b, round)) != MOE_OK) return st;
-  int cus = 0;
-  if ((st = num_cus(&cus)) != MOE_OK) return st;
-  int32_t rows[kMaxExperts];
-  return run_ffn(b, round, w_gate, w_up, w_down,
-                 rows_from_counts(b.s, counts_host, round, rows), cus,
-                 static_cast<hipStream_t>(stream));
+  return stage_gemm(cfg, round, n_rounds, w_gate, w_up, w_down, counts_host, ws,
+                    ws_bytes, stream, kStageBoth);
 }
 
-moe_status_t moe_expert_gate_up(const moe_config_t* cfg, int32_t round,
+moe_status_t moe_expert_gate_up(const moe_config_t* cfg, int32_t round, int32_t n_rounds,
                                 const void* w_gate, const void* w_up,
                                 const int32_t* counts_host, void* ws,
                                 size_t ws_bytes, void* stream) {
-  Bound b;
-  moe_status_t st = bind(cfg, ws, ws_bytes, &b);
-  if (st != MOE_OK) return st;
-  if ((st = check_ptr(w_gate, "w_gate")) != MOE_OK) return st;
-  if ((st = check_ptr(w_up, "w_up")) != MOE_OK) return st;
-  if ((st = check_round(b, round)) != MOE_OK) return st;
-  int cus = 0;
-  if ((st = num_cus(&cus)) != MOE_OK) return st;
-  int32_t rows[kMaxExperts];
-  MOE_HIP(moe::launch_gate_up(b.s, round, b.xr(round), w_gate, w_up, b.pb,
-                              rows_from_counts(b.s, counts_host, round, rows),
-                              b.h(round), cus, static_cast<hipStream_t>(stream)),
-          "gate/up launch");
-  return MOE_OK;
+  return stage_gemm(cfg, round, n_rounds, w_gate, w_up, nullptr, counts_host, ws,
+                    ws_bytes, stream, kStageGateUp);
 }
 
-moe_status_t moe_expert_down(const moe_config_t* cfg, int32_t round,
+moe_status_t moe_expert_down(const moe_config_t* cfg, int32_t round, int32_t n_rounds,
                              const void* w_down, const int32_t* counts_host,
                              void* ws, size_t ws_bytes, void* stream) {
-  Bound b;
-  moe_status_t st = bind(cfg, ws, ws_bytes, &b);
-  if (st != MOE_OK) return st;
-  if ((st = check_ptr(w_down, "w_down")) != MOE_OK) return st;
-  if ((st = check_round(b, round)) != MOE_OK) return st;
-  int cus = 0;
-  if ((st = num_cus(&cus)) != MOE_OK) return st;
-  int32_t rows[kMaxExperts];
-  MOE_HIP(moe::launch_down(b.s, round, b.h(round), w_down, b.pb,
-                           rows_from_counts(b.s, counts_host, round, rows),
-                           b.ws + b.L.z, cus, static_cast<hipStream_t>(stream)),
-          "down launch");
-  return MOE_OK;
+  return stage_gemm(cfg, round, n_rounds, nullptr, nullptr, w_down, counts_host, ws,
+                    ws_bytes, stream, kStageDown);
 }
 
 moe_status_t moe_pack_weights(const moe_config_t* cfg, const void* w_gate,
@@ -697,6 +750,7 @@ moe_status_t moe_backward(const moe_config_t* cfg, const void* x, const void* w_
   int64_t rem[kMaxExperts];
   for (int e = 0; e < b.s.E; ++e) rem[e] = counts_r[e];
   int32_t rows[2][kMaxExperts];
+  int32_t prow[kMaxExperts];
   const int d = b.s.d, f = b.s.f;
   const size_t set = (size_t)b.s.buf_rows() * 2;  // bytes per feature of a set
   char* xr[2] = {w + L.xr, w + L.xr + set * d};
@@ -711,15 +765,16 @@ moe_status_t moe_backward(const moe_config_t* cfg, const void* x, const void* w_
     for (int q = 0; q < nr; ++q) {
       const int rr = r + q;
       moe::host_next_round(b.s, rem, rows[q]);
-      MOE_HIP(moe::launch_dispatch(b.s, rr, x, b.pb, xr[q], cus, s), "dispatch launch");
-      MOE_HIP(moe::launch_dispatch(b.s, rr, dy, b.pb, dyr[q], cus, s), "dispatch launch");
-      MOE_HIP(moe::launch_recompute(b.s, rr, xr[q], w_gate, w_up, b.pb, rows[q], gu, hw[q],
-                                    cus, s),
+      const int nv = moe::round_pairs(b.s.E, rows[q], prow);
+      MOE_HIP(moe::launch_dispatch(b.s, rr, 1, x, b.pb, xr[q], cus, s), "dispatch launch");
+      MOE_HIP(moe::launch_dispatch(b.s, rr, 1, dy, b.pb, dyr[q], cus, s), "dispatch launch");
+      MOE_HIP(moe::launch_recompute(b.s, rr, xr[q], w_gate, w_up, b.pb, prow, nv, gu,
+                                    hw[q], cus, s),
               "recompute launch");
-      MOE_HIP(moe::launch_dgate(b.s, rr, dyr[q], w_down_t, b.pb, rows[q], gu, dgu[q], cus,
-                                s),
+      MOE_HIP(moe::launch_dgate(b.s, rr, dyr[q], w_down_t, b.pb, prow, nv, gu, dgu[q],
+                                cus, s),
               "dgate launch");
-      MOE_HIP(moe::launch_dx(b.s, rr, dgu[q], w_gate_up_t, b.pb, rows[q], dz, cus, s),
+      MOE_HIP(moe::launch_dx(b.s, rr, dgu[q], w_gate_up_t, b.pb, prow, nv, dz, cus, s),
               "dx launch");
     }
     MOE_HIP(moe::launch_wgrad(b.s, r, nr, dyr[0], hw[0], dyr[1], hw[1], d, d, f, dw_down,
@@ -776,7 +831,7 @@ moe_status_t moe_forward(const moe_config_t* cfg, const float* logits,
                          hipMemcpyDeviceToHost, rb->side),
           "read of counts and R");
   MOE_HIP(hipEventRecord(rb->done, rb->side), "hipEventRecord");
-  MOE_HIP(moe::launch_dispatch(b.s, 0, x, b.pb, b.xr(0), cus, s), "dispatch launch");
+  MOE_HIP(moe::launch_dispatch(b.s, 0, 1, x, b.pb, b.xr(0), cus, s), "dispatch launch");
   // With two sets of round buffers the odd rounds run on the side stream
   // (set 1) and the even rounds on the caller's (set 0): consecutive rounds
   // use different buffers, so the dispatch of round r + 1 and the expert
@@ -786,7 +841,7 @@ moe_status_t moe_forward(const moe_config_t* cfg, const float* logits,
   const int64_t max_rounds = (b.s.T + b.s.ce - 1) / b.s.ce;
   const bool two = b.sets == 2 && max_rounds >= 2;
   if (two)
-    MOE_HIP(moe::launch_dispatch(b.s, 1, x, b.pb, b.xr(1), cus, rb->side),
+    MOE_HIP(moe::launch_dispatch(b.s, 1, 1, x, b.pb, b.xr(1), cus, rb->side),
             "dispatch launch");
   MOE_HIP(hipEventSynchronize(rb->done), "wait for the plan");
   int32_t counts_r[kMaxExperts + 1];
@@ -794,16 +849,21 @@ moe_status_t moe_forward(const moe_config_t* cfg, const float* logits,
   const int32_t R = counts_r[b.s.E];
   if (R < 1 || R > max_rounds)
     return fail(MOE_ERR_HIP, "device plan reported an impossible round count");
-  int64_t rem[kMaxExperts];
-  for (int e = 0; e < b.s.E; ++e) rem[e] = counts_r[e];
-  int32_t rows[kMaxExperts];
-  for (int r = 0; r < R; ++r) {
-    hipStream_t sr = two && (r & 1) ? rb->side : s;
-    if (r > (two ? 1 : 0))
-      MOE_HIP(moe::launch_dispatch(b.s, r, x, b.pb, b.xr(r), cus, sr),
+  // The launch batches (one round each with two sets): the rest of each
+  // batch's dispatch (rounds not queued before the wait), then one launch
+  // of each grouped GEMM over the batch's pairs.
+  const int queued = two ? 2 : 1;
+  moe::BatchWalker walk(b.s, counts_r);
+  moe::LaunchBatch lb;
+  while (walk.next(&lb)) {
+    hipStream_t sr = two && (lb.r0 & 1) ? rb->side : s;
+    const int d0 = lb.r0 < queued ? queued : lb.r0;
+    if (lb.r0 + lb.nr > d0)
+      MOE_HIP(moe::launch_dispatch(b.s, d0, lb.r0 + lb.nr - d0, x, b.pb, b.xr(lb.r0),
+                                   cus, sr),
               "dispatch launch");
-    moe::host_next_round(b.s, rem, rows);
-    if ((st = run_ffn(b, r, w_gate, w_up, w_down, rows, cus, sr)) != MOE_OK)
+    if ((st = run_ffn(b, lb.r0, lb.nr, w_gate, w_up, w_down, lb.rows, lb.nv, cus, sr)) !=
+        MOE_OK)
       return st;
   }
   if (two) {  // the combine reads z rows of every round
@@ -844,7 +904,7 @@ moe_status_t moe_forward_static(const moe_config_t* cfg, const float* logits,
   // entry it later reads, and the rows of a round buffer past an expert's
   // rows only feed outputs that are never stored.
   if ((st = run_plan(b, logits, s)) != MOE_OK) return st;
-  MOE_HIP(moe::launch_dispatch(b.s, 0, x, b.pb, b.xr(0), cus, s), "dispatch launch");
+  MOE_HIP(moe::launch_dispatch(b.s, 0, 1, x, b.pb, b.xr(0), cus, s), "dispatch launch");
   // counts and R into host memory of this frame, then one wait
   int32_t counts_r[kMaxExperts + 1];
   MOE_HIP(hipMemcpyAsync(counts_r, b.pb.counts, (b.s.E + 1) * sizeof(int32_t),
@@ -855,15 +915,19 @@ moe_status_t moe_forward_static(const moe_config_t* cfg, const float* logits,
   const int64_t max_rounds = (b.s.T + b.s.ce - 1) / b.s.ce;
   if (R < 1 || R > max_rounds)
     return fail(MOE_ERR_HIP, "device plan reported an impossible round count");
-  int64_t rem[kMaxExperts];
-  for (int e = 0; e < b.s.E; ++e) rem[e] = counts_r[e];
-  int32_t rows[kMaxExperts];
-  // every round on the caller's stream, in order (round r in set r % S)
-  for (int r = 0; r < R; ++r) {
-    if (r > 0)
-      MOE_HIP(moe::launch_dispatch(b.s, r, x, b.pb, b.xr(r), cus, s), "dispatch launch");
-    moe::host_next_round(b.s, rem, rows);
-    if ((st = run_ffn(b, r, w_gate, w_up, w_down, rows, cus, s)) != MOE_OK) return st;
+  // every launch batch on the caller's stream, in order (as moe_forward;
+  // with two sets one round per batch, round r in set r % S)
+  moe::BatchWalker walk(b.s, counts_r);
+  moe::LaunchBatch lb;
+  while (walk.next(&lb)) {
+    const int d0 = lb.r0 < 1 ? 1 : lb.r0;
+    if (lb.r0 + lb.nr > d0)
+      MOE_HIP(moe::launch_dispatch(b.s, d0, lb.r0 + lb.nr - d0, x, b.pb, b.xr(lb.r0),
+                                   cus, s),
+              "dispatch launch");
+    if ((st = run_ffn(b, lb.r0, lb.nr, w_gate, w_up, w_down, lb.rows, lb.nv, cus, s)) !=
+        MOE_OK)
+      return st;
   }
   MOE_HIP(moe::launch_combine(b.s, b.ws + b.L.z, b.pb.weight, b.pb.pos, y, cus, s),
           "combine launch");

@@ -11,22 +11,22 @@
 
 namespace moe {
 
-// Round r, token-major: one wavefront per token reads the token's row of x
-// once and writes it to every slot the token holds in round r. The token's
-// k assignments a = t*k + j carry their expert idx[a], round round_of[a]
-// and slot row_of[a] = g*G*C' + ubase(r,e) + c (g = e / G); assignment j
-// goes to slot c of expert e's matrix if round_of[a] == r. That matrix
-// starts at buffer row g*Q + pbase(r,e) (Q rows per group), a multiple of
-// 64, so the whole buffer is one tiled matrix: each lane moves 16-byte
-// chunks q = lane + 64 i of the row, and chunk q of buffer row p lands in
-// 4 KiB block q / 4 of p's 64-row band, at row p % 64 and chunk position
-// (q % 4) ^ ((p / 4) % 4).
+// Rounds [r0, r0 + nr), token-major: one wavefront per token reads the
+// token's row of x once and writes it to every slot the token holds in those
+// rounds. The token's k assignments a = t*k + j carry their expert idx[a],
+// round r = round_of[a] and slot row_of[a] = g*G*C' + ubase(r,e) + c (g =
+// e / G, c the assignment's index among e's entries of round r); assignment
+// j goes to row c of the matrix of (r, e), which starts at buffer row
+// brow(r,e), a multiple of 64, so the whole buffer is one tiled matrix:
+// each lane moves 16-byte chunks q = lane + 64 i of the row, and chunk q of
+// buffer row p lands in 4 KiB block q / 4 of p's 64-row band, at row p % 64
+// and chunk position (q % 4) ^ ((p / 4) % 4).
 template <int kChunks>  // 16-byte chunks per lane held in registers
 __global__ __launch_bounds__(256) void dispatch_kernel(
     const char* __restrict__ x, int64_t T, int row_bytes, int E, int k, int ce,
-    int G, int64_t pool_rows, int r, const int32_t* __restrict__ idx,
+    int G, int r0, int nr, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ round_of, const int32_t* __restrict__ row_of,
-    const int32_t* __restrict__ ubase, const int32_t* __restrict__ pbase,
+    const int32_t* __restrict__ ubase, const int32_t* __restrict__ brow,
     char* __restrict__ xr) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kWave;
@@ -38,12 +38,13 @@ __global__ __launch_bounds__(256) void dispatch_kernel(
     bool mine = false;
     if (lane < k) {
       const int64_t a = t * k + lane;
-      mine = round_of[a] == r;
+      const int r = round_of[a];
+      mine = r >= r0 && r - r0 < nr;
       if (mine) {
         const int e = idx[a];
-        const int g = e / G;
-        const int c = row_of[a] - g * G * ce - ubase[(int64_t)r * E + e];
-        prow = (int64_t)g * pool_rows + pbase[(int64_t)r * E + e] + c;
+        const int64_t at = (int64_t)r * E + e;
+        const int c = row_of[a] - (e / G) * G * ce - ubase[at];
+        prow = (int64_t)brow[at] + c;
       }
     }
     uint64_t todo = __builtin_amdgcn_ballot_w64(mine);
@@ -73,7 +74,7 @@ __global__ __launch_bounds__(256) void dispatch_kernel(
   }
 }
 
-hipError_t launch_dispatch(const Shape& s, int r, const void* x,
+hipError_t launch_dispatch(const Shape& s, int r0, int nr, const void* x,
                            const PlanBuffers& b, void* xr, int num_cus,
                            hipStream_t st) {
   const int row_bytes = s.d * (s.bf16 ? 2 : 4);
@@ -84,8 +85,8 @@ hipError_t launch_dispatch(const Shape& s, int r, const void* x,
   const int64_t tbl = s.max_rounds() * s.E;
   hipLaunchKernelGGL(dispatch_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, st,
                      static_cast<const char*>(x), s.T, row_bytes, s.E, s.k, s.ce,
-                     s.G, s.pool_rows(), r, b.idx, b.round_of, b.row_of,
-                     b.rounds + kUbase * tbl, b.rounds + kPbase * tbl,
+                     s.G, r0, nr, b.idx, b.round_of, b.row_of,
+                     b.rounds + kUbase * tbl, b.rounds + kBrow * tbl,
                      static_cast<char*>(xr));
   return hipGetLastError();
 }

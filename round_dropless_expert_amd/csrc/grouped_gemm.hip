@@ -103,13 +103,11 @@ struct GemmParams {
   const Elem* aux;   // gu [rows][2N] (dgate only)
   const float* weight;     // routing weights [T*k] (recompute, dgate)
   const int32_t* perm;     // the plan's permutation (recompute, dgate)
-  const int32_t* rounds;   // the plan's round tables [4][max_rounds][E]
-  const int32_t* offsets;  // [E+1]
-  const int32_t* n_rounds; // R: a round r >= R has no rows (its tables are unset)
-  int E, r, K, N;      // N = output features: f (gate/up) or d (down)
+  const int32_t* rounds;   // the plan's round tables (RoundTable)
+  const int32_t* n_rounds; // R: rounds >= R have no pairs (their tables are unset)
+  int E, r0, nr, K, N; // rounds [r0, r0 + nr) of one batch; N = output
+                       // features: f (gate/up) or d (down)
   int max_rounds;      // rows of each round table
-  int G;               // experts per capacity group
-  int pool_rows;       // round-buffer rows per group (multiple of 64)
   int tiled_w;         // weights in the tiled layout (else row-major)
 };
 
@@ -300,21 +298,27 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
   const int half = lane / 32;
   const int l32 = lane & 31;
 
-  // Every wavefront keeps the round's tile table in registers: lane e holds
-  // expert e's rows m_e, the inclusive prefix of the tile counts, the first
-  // buffer row of e's matrix (its group's block plus the padded rows of the
-  // group's lower experts) and, for down, e's first row of z in the round
-  // (offsets[e] + the index of its first entry of the round).
+  // Every wavefront keeps the launch's tile table in registers: lane v holds
+  // pair v of the launch (a round's expert with rows; the pairs of rounds
+  // [r0, r0 + nr) are [rbeg[r0], rend[r0 + nr - 1]) of the plan's pair
+  // tables): its expert, its rows m_v, the inclusive prefix of the tile
+  // counts, the first buffer row of its matrix and, past gate/up, its first
+  // row of z (offsets[e] + the index of its first entry of the round). A
+  // launch reaching past R has no pairs.
   const int nt = (p.N + NF - 1) / NF;
   const int64_t tbl = (int64_t)p.max_rounds * p.E;
-  const int64_t at = (int64_t)p.r * p.E + lane;
-  const bool lv = lane < p.E && p.r < *p.n_rounds;
-  const int lane_m = lv ? p.rounds[kAlloc * tbl + at] : 0;
+  const int32_t* rb = p.rounds + kTables * tbl;
+  const int g0 = rb[p.r0];
+  const int g1 = rb[p.max_rounds + p.r0 + p.nr - 1];
+  const int nv = p.r0 + p.nr <= *p.n_rounds ? g1 - g0 : 0;
+  const bool lv = lane < nv;
+  const int64_t gi = (int64_t)g0 + lane;
+  const int lane_e = lv ? p.rounds[kPairE * tbl + gi] : 0;
+  const int lane_m = lv ? p.rounds[kPairM * tbl + gi] : 0;
   const int lane_incl = wave_inclusive_scan(((lane_m + BM - 1) / BM) * nt);
   const int total = __builtin_amdgcn_readlane(lane_incl, kWave - 1);
-  const int lane_row = lv ? (lane / p.G) * p.pool_rows + p.rounds[kPbase * tbl + at] : 0;
-  const int lane_off =
-      kMode != kModeGateUp && lv ? p.offsets[lane] + p.rounds[kCum * tbl + at] : 0;
+  const int lane_row = lv ? p.rounds[kPairRow * tbl + gi] : 0;
+  const int lane_off = kMode != kModeGateUp && lv ? p.rounds[kPairZ * tbl + gi] : 0;
 
   // XCD-contiguous walk: workgroup b runs on XCD b % 8.
   const int G = gridDim.x;
@@ -340,14 +344,15 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
   const uint32_t vo_w = p.tiled_w ? (uint32_t)tid * 16 : (uint32_t)r0 * kbytes + chunk * 16;
   const uint32_t vo_t = (uint32_t)tid * 16;
 
-  // Tile t: expert, feature block and token block, and its operand sources.
+  // Tile t: pair (te, below), feature block and token block, and its operand
+  // sources.
   // Weight rows at or past N and token bands past the expert's m rows fall
   // outside the descriptors' ranges, so they read as zeros; they only feed
   // outputs that are never stored. Offsets stay below 2^32: the matrices'
   // bytes are below 2^31 and a tile reaches at most three bands past them.
   int e = 0, m = 0, n0 = 0, m0 = 0;
   auto locate = [&](int t, int& te, int& tm, int& tn0, int& tm0) {
-    // expert of the tile: the number of experts whose tiles all come first
+    // pair of the tile: the number of pairs whose tiles all come first
     te = __builtin_popcountll(__builtin_amdgcn_ballot_w64(lane_incl <= t));
     tm = __builtin_amdgcn_readlane(lane_m, te);
     const int mt = (tm + BM - 1) / BM;
@@ -358,12 +363,12 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
   auto sources = [&](int te, int tm, int tn0, int tm0, bool exists) {
     src_t S;
     const uint32_t wb = exists ? wbytes : 0u;  // no next tile: all out of range
+    const int64_t ex = __builtin_amdgcn_readlane(lane_e, te);  // the pair's expert
     S.rw0 = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(p.w0 + (int64_t)te * p.N * p.K), 0, (int)wb, kRsrcWord3);
+        (void*)(p.w0 + ex * p.N * p.K), 0, (int)wb, kRsrcWord3);
     S.rw1 = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(kGateUp ? p.w1 + (int64_t)te * p.N * p.K : p.w0), 0, (int)wb,
-        kRsrcWord3);
-    // expert te's matrix: its m rows padded to 64, from its first row
+        (void*)(kGateUp ? p.w1 + ex * p.N * p.K : p.w0), 0, (int)wb, kRsrcWord3);
+    // pair te's matrix: its m rows padded to 64, from its first row
     S.ra = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(p.act + (int64_t)__builtin_amdgcn_readlane(lane_row, te) * p.K), 0,
         exists ? (int)((uint32_t)((tm + 63) & ~63) * kbytes) : 0, kRsrcWord3);
@@ -777,13 +782,12 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
 // Tiles one round needs under configuration Cfg (host side, from the rows
 // of every expert in the round).
 template <typename Cfg>
-static int64_t round_tiles(const Shape& s, const int32_t* rows, int N,
-                           bool gate_up) {
+static int64_t round_tiles(const int32_t* rows, int nv, int N, bool gate_up) {
   const int BM = 64 * Cfg::WJ;
   const int NF = gate_up ? 32 * Cfg::WI : 64 * Cfg::WI;
   const int64_t nt = (N + NF - 1) / NF;
   int64_t tiles = 0;
-  for (int e = 0; e < s.E; ++e) tiles += ((int64_t)rows[e] + BM - 1) / BM * nt;
+  for (int v = 0; v < nv; ++v) tiles += ((int64_t)rows[v] + BM - 1) / BM * nt;
   return tiles;
 }
 
@@ -812,24 +816,25 @@ static hipError_t launch_gemm_cfg(const GemmParams<Elem>& p, int grid,
   return hipGetLastError();
 }
 
-// rows_host (nullable): rows of every expert in this round, on the host.
-// With them the round's tile shape and grid are chosen from its tile counts;
+// rows_host (nullable): rows of the launch's nv pairs, on the host. With
+// them the launch's tile shape and grid are chosen from its tile counts;
 // without them the large tile and one workgroup per CU are used. Every shape
 // runs the same MFMA sequence over K for every output, so results are
 // identical. p.N is the number of output features.
 template <typename Elem, int kMode>
 static hipError_t launch_gemm(const Shape& s, const GemmParams<Elem>& p,
-                              const int32_t* rows_host, int num_cus,
+                              const int32_t* rows_host, int nv, int num_cus,
                               hipStream_t st) {
   constexpr bool kDual = kMode == kModeGateUp || kMode == kModeRecompute;
   const int N = p.N;
+  (void)s;
   if (rows_host) {
     int64_t mmax = 0;
-    for (int e = 0; e < s.E; ++e) mmax = rows_host[e] > mmax ? rows_host[e] : mmax;
-    if (mmax == 0) return hipSuccess;  // nothing in this round
-    const int64_t tb = round_tiles<TileBig>(s, rows_host, N, kDual);
-    const int64_t tm = round_tiles<TileMedium>(s, rows_host, N, kDual);
-    const int64_t ts = round_tiles<TileSmall>(s, rows_host, N, kDual);
+    for (int v = 0; v < nv; ++v) mmax = rows_host[v] > mmax ? rows_host[v] : mmax;
+    if (mmax == 0) return hipSuccess;  // nothing in this launch
+    const int64_t tb = round_tiles<TileBig>(rows_host, nv, N, kDual);
+    const int64_t tm = round_tiles<TileMedium>(rows_host, nv, N, kDual);
+    const int64_t ts = round_tiles<TileSmall>(rows_host, nv, N, kDual);
     const float cb = est_cost<TileBig>(tb, num_cus);
     const float cm = est_cost<TileMedium>(tm, num_cus);
     const float cs = est_cost<TileSmall>(ts, num_cus);
@@ -845,7 +850,7 @@ static hipError_t launch_gemm(const Shape& s, const GemmParams<Elem>& p,
 // Parameters of a launch over round r: activations act [rows][K], weights
 // w0 (and w1) [E][N][K], output out; K and N as given.
 template <typename Elem>
-static GemmParams<Elem> params(const Shape& s, int r, const void* act,
+static GemmParams<Elem> params(const Shape& s, int r0, int nr, const void* act,
                                const void* w0, const void* w1, void* out,
                                const PlanBuffers& b, int K, int N, bool tiled_w) {
   GemmParams<Elem> p{};
@@ -856,67 +861,65 @@ static GemmParams<Elem> params(const Shape& s, int r, const void* act,
   p.weight = b.weight;
   p.perm = b.perm;
   p.rounds = b.rounds;
-  p.offsets = b.offsets;
   p.n_rounds = b.n_rounds;
   p.E = s.E;
-  p.r = r;
+  p.r0 = r0;
+  p.nr = nr;
   p.K = K;
   p.N = N;
   p.max_rounds = (int)s.max_rounds();
-  p.G = s.G;
-  p.pool_rows = (int)s.pool_rows();
   p.tiled_w = tiled_w ? 1 : 0;
   return p;
 }
 
-hipError_t launch_gate_up(const Shape& s, int r, const void* xr,
+hipError_t launch_gate_up(const Shape& s, int r0, int nr, const void* xr,
                           const void* wg, const void* wu, const PlanBuffers& b,
-                          const int32_t* rows_host, void* h, int num_cus,
+                          const int32_t* rows_host, int nv, void* h, int num_cus,
                           hipStream_t st) {
   if (s.bf16)
     return launch_gemm<bf16, kModeGateUp>(
-        s, params<bf16>(s, r, xr, wg, wu, h, b, s.d, s.f, s.tiled_w), rows_host,
-        num_cus, st);
+        s, params<bf16>(s, r0, nr, xr, wg, wu, h, b, s.d, s.f, s.tiled_w), rows_host,
+        nv, num_cus, st);
   return launch_gemm<float, kModeGateUp>(
-      s, params<float>(s, r, xr, wg, wu, h, b, s.d, s.f, s.tiled_w), rows_host,
-      num_cus, st);
+      s, params<float>(s, r0, nr, xr, wg, wu, h, b, s.d, s.f, s.tiled_w), rows_host,
+      nv, num_cus, st);
 }
 
-hipError_t launch_down(const Shape& s, int r, const void* h, const void* wd,
-                       const PlanBuffers& b, const int32_t* rows_host, void* z,
-                       int num_cus, hipStream_t st) {
+hipError_t launch_down(const Shape& s, int r0, int nr, const void* h, const void* wd,
+                       const PlanBuffers& b, const int32_t* rows_host, int nv,
+                       void* z, int num_cus, hipStream_t st) {
   if (s.bf16)
     return launch_gemm<bf16, kModeDown>(
-        s, params<bf16>(s, r, h, wd, nullptr, z, b, s.f, s.d, s.tiled_w), rows_host,
-        num_cus, st);
+        s, params<bf16>(s, r0, nr, h, wd, nullptr, z, b, s.f, s.d, s.tiled_w),
+        rows_host, nv, num_cus, st);
   return launch_gemm<float, kModeDown>(
-      s, params<float>(s, r, h, wd, nullptr, z, b, s.f, s.d, s.tiled_w), rows_host,
-      num_cus, st);
+      s, params<float>(s, r0, nr, h, wd, nullptr, z, b, s.f, s.d, s.tiled_w),
+      rows_host, nv, num_cus, st);
 }
 
 hipError_t launch_recompute(const Shape& s, int r, const void* xr, const void* wg,
                             const void* wu, const PlanBuffers& b,
-                            const int32_t* rows_host, void* gu, void* hw,
+                            const int32_t* rows_host, int nv, void* gu, void* hw,
                             int num_cus, hipStream_t st) {
-  GemmParams<bf16> p = params<bf16>(s, r, xr, wg, wu, gu, b, s.d, s.f, s.tiled_w);
+  GemmParams<bf16> p = params<bf16>(s, r, 1, xr, wg, wu, gu, b, s.d, s.f, s.tiled_w);
   p.out2 = static_cast<bf16*>(hw);
-  return launch_gemm<bf16, kModeRecompute>(s, p, rows_host, num_cus, st);
+  return launch_gemm<bf16, kModeRecompute>(s, p, rows_host, nv, num_cus, st);
 }
 
 hipError_t launch_dgate(const Shape& s, int r, const void* dyr, const void* wd_t,
-                        const PlanBuffers& b, const int32_t* rows_host,
+                        const PlanBuffers& b, const int32_t* rows_host, int nv,
                         const void* gu, void* dgu, int num_cus, hipStream_t st) {
-  GemmParams<bf16> p = params<bf16>(s, r, dyr, wd_t, nullptr, dgu, b, s.d, s.f, true);
+  GemmParams<bf16> p = params<bf16>(s, r, 1, dyr, wd_t, nullptr, dgu, b, s.d, s.f, true);
   p.aux = static_cast<const bf16*>(gu);
-  return launch_gemm<bf16, kModeDgate>(s, p, rows_host, num_cus, st);
+  return launch_gemm<bf16, kModeDgate>(s, p, rows_host, nv, num_cus, st);
 }
 
 hipError_t launch_dx(const Shape& s, int r, const void* dgu, const void* wgu_t,
-                     const PlanBuffers& b, const int32_t* rows_host, void* dz,
-                     int num_cus, hipStream_t st) {
+                     const PlanBuffers& b, const int32_t* rows_host, int nv,
+                     void* dz, int num_cus, hipStream_t st) {
   return launch_gemm<bf16, kModeDown>(
-      s, params<bf16>(s, r, dgu, wgu_t, nullptr, dz, b, 2 * s.f, s.d, true),
-      rows_host, num_cus, st);
+      s, params<bf16>(s, r, 1, dgu, wgu_t, nullptr, dz, b, 2 * s.f, s.d, true),
+      rows_host, nv, num_cus, st);
 }
 
 }  // namespace moe

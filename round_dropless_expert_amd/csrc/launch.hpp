@@ -15,6 +15,10 @@ struct Shape {
   bool bf16;     // element type of x, weights, y and the round buffers
   bool tiled_w;  // weights in the tiled layout of moe_pack_weights
   int G;         // experts per capacity group
+  // consecutive rounds share launches while their (round, expert) pairs fit
+  // the round buffer's E expert regions (G = 1 with one set of round
+  // buffers); otherwise every round is launched on its own
+  bool pack;
   int ce_pad() const { return (ce + 63) / 64 * 64; }
   // round-buffer rows per group: each expert's rows of a round start at a
   // multiple of 64, so a group of G > 1 needs up to 64 more per expert
@@ -57,31 +61,61 @@ struct PlanBuffers {
   int32_t* round_of;
   int32_t* row_of;
   int32_t* scratch;  // hist [hist_rows][E], chunk sums [rank_blocks][E]
-  // [4][max_rounds][E]: rows m(r,e), first list index cum(r,e), rows of the
-  // lower experts of the group ubase(r,e), the same padded to 64 pbase(r,e)
+  // the round tables, see RoundTable
   int32_t* rounds;
 };
 
-// Tables of PlanBuffers::rounds.
-enum RoundTable { kAlloc = 0, kCum = 1, kUbase = 2, kPbase = 3 };
+// Tables of PlanBuffers::rounds: kTables tables of [max_rounds][E] int32,
+// then rbeg and rend, [max_rounds] each.
+//
+// Launch batches: the forward runs consecutive rounds in one dispatch and
+// one launch of each grouped GEMM while their (round, expert) pairs with
+// rows fit the E expert regions of the round buffer (Shape::pack; the
+// results are identical, each output keeps its fixed K order). Batch b's
+// pairs are numbered v = 0, 1, ... round by round, experts ascending inside
+// a round; pair v's matrix starts at buffer row v * P. Without packing every
+// round is a batch of its own and expert e's matrix of round r starts at
+// its group's block plus pbase(r,e). The pair tables are indexed by the
+// global pair index b * E + v; rbeg[r] and rend[r] are the global indices
+// of round r's first pair and one past its last, so a launch over rounds
+// [r0, r1] of one batch covers the pairs [rbeg[r0], rend[r1]).
+enum RoundTable {
+  kAlloc = 0,    // [r][e] rows m(r,e)
+  kCum = 1,      // [r][e] index in e's list of its first entry of round r
+  kUbase = 2,    // [r][e] rows of the lower experts of e's group in round r
+  kPbase = 3,    // [r][e] the same with each expert's rows rounded up to 64
+  kBrow = 4,     // [r][e] first buffer row (inside a set) of e's matrix of round r
+  kPairE = 5,    // [b*E + v] expert of pair v of batch b
+  kPairM = 6,    // its rows
+  kPairRow = 7,  // its first buffer row
+  kPairZ = 8,    // its first row of z: offsets[e] + cum(r,e)
+  kTables = 9
+};
+inline int64_t round_table_ints(const Shape& s) {
+  return (int64_t)kTables * s.max_rounds() * s.E + 2 * s.max_rounds();
+}
 
 hipError_t launch_route(const Shape& s, const float* logits, PlanBuffers b,
                         hipStream_t st);
 hipError_t launch_plan(const Shape& s, PlanBuffers b, hipStream_t st);
-hipError_t launch_dispatch(const Shape& s, int r, const void* x,
+// Dispatch of the rounds [r0, r0 + nr): every assignment of those rounds
+// to its slot of the round buffer.
+hipError_t launch_dispatch(const Shape& s, int r0, int nr, const void* x,
                            const PlanBuffers& b, void* xr, int num_cus,
                            hipStream_t st);
-// rows_host: the round's rows m(r,e) of every expert on the host, or NULL.
-// With them the round gets the tile shape and grid that fit it (results are
+// Grouped GEMMs over the rounds [r0, r0 + nr), which lie in one launch
+// batch (nothing runs unless r0 + nr <= R). rows_host: the rows of the
+// launch's pairs on the host (nv of them, in pair order), or NULL. With
+// them the launch gets the tile shape and grid that fit it (results are
 // identical either way); without them the large tile and one workgroup per
 // CU are used.
-hipError_t launch_gate_up(const Shape& s, int r, const void* xr,
+hipError_t launch_gate_up(const Shape& s, int r0, int nr, const void* xr,
                           const void* wg, const void* wu, const PlanBuffers& b,
-                          const int32_t* rows_host, void* h, int num_cus,
+                          const int32_t* rows_host, int nv, void* h, int num_cus,
                           hipStream_t st);
-hipError_t launch_down(const Shape& s, int r, const void* h, const void* wd,
-                       const PlanBuffers& b, const int32_t* rows_host, void* z,
-                       int num_cus, hipStream_t st);
+hipError_t launch_down(const Shape& s, int r0, int nr, const void* h, const void* wd,
+                       const PlanBuffers& b, const int32_t* rows_host, int nv,
+                       void* z, int num_cus, hipStream_t st);
 
 // Backward GEMMs of round r (bf16; weights of the dgrad launches packed by
 // launch_pack_backward): the recompute of g and u into gu [rows][2f] and of
@@ -90,14 +124,14 @@ hipError_t launch_down(const Shape& s, int r, const void* h, const void* wd,
 // assignments' expert-sorted rows, like z.
 hipError_t launch_recompute(const Shape& s, int r, const void* xr, const void* wg,
                             const void* wu, const PlanBuffers& b,
-                            const int32_t* rows_host, void* gu, void* hw,
+                            const int32_t* rows_host, int nv, void* gu, void* hw,
                             int num_cus, hipStream_t st);
 hipError_t launch_dgate(const Shape& s, int r, const void* dyr, const void* wd_t,
-                        const PlanBuffers& b, const int32_t* rows_host,
+                        const PlanBuffers& b, const int32_t* rows_host, int nv,
                         const void* gu, void* dgu, int num_cus, hipStream_t st);
 hipError_t launch_dx(const Shape& s, int r, const void* dgu, const void* wgu_t,
-                     const PlanBuffers& b, const int32_t* rows_host, void* dz,
-                     int num_cus, hipStream_t st);
+                     const PlanBuffers& b, const int32_t* rows_host, int nv,
+                     void* dz, int num_cus, hipStream_t st);
 
 // Weight gradients of rounds r .. r + nr - 1 (nr = 1 or 2; round r's
 // buffers U, V, round r + 1's U1, V1): out_e[a][b] (+)= sum over expert e's
@@ -126,6 +160,34 @@ hipError_t launch_fill(float* p, int64_t n, float value, int num_cus, hipStream_
 // Host copy of the plan's fill rule: from the entries each expert has left
 // (rem[E], updated), the rows m(r,e) of every expert in the next round.
 void host_next_round(const Shape& s, int64_t* rem, int32_t* rows_out);
+
+// One launch batch (see RoundTable): rounds [r0, r0 + nr) and the rows of
+// its nv pairs in pair order.
+struct LaunchBatch {
+  int r0, nr, nv;
+  int32_t rows[64];
+};
+
+// Host copy of the plan's launch batches, walked in order from the counts
+// (no heap memory: the forward that allocates nothing uses it too).
+class BatchWalker {
+ public:
+  BatchWalker(const Shape& s, const int32_t* counts);
+  // the next batch; false after the last
+  bool next(LaunchBatch* out);
+
+ private:
+  Shape s_;
+  int64_t rem_[64];
+  int64_t left_;
+  int r_;
+  int32_t pending_[64];  // rows of round r_, computed but not yet placed
+  bool have_pending_;
+};
+
+// The rows of the experts with rows (the pairs of one round), in expert
+// order; returns how many.
+int round_pairs(int E, const int32_t* rows, int32_t* out);
 hipError_t launch_pack_weights(const Shape& s, const void* src, void* dst,
                                int rows, int cols, int num_cus, hipStream_t st);
 hipError_t launch_combine(const Shape& s, const void* z, const float* weight,

@@ -138,6 +138,49 @@ __global__ __launch_bounds__(256) void plan_chunk_sum_kernel(
         part[3][threadIdx.x];
 }
 
+// Launch batches (see RoundTable), one wavefront, lane = expert e. The
+// cursor is wavefront-uniform: the current batch and the pairs it holds.
+struct BatchCursor {
+  int b = 0, used = 0;
+};
+
+// Places round r: lane e (on: e < E) has m rows in it, the first of which is
+// entry `cum` of its list; off_e = offsets[e]; nobrow is where e's matrix
+// of the round starts without packing. Round r joins the current batch if
+// packing is on and its pairs still fit the E regions, else it opens the
+// next batch. Writes kBrow, the pair tables and rbeg/rend of round r.
+__device__ __forceinline__ void place_round(int r, int lane, bool on, int m, int cum,
+                                            int off_e, int nobrow, int E, int P,
+                                            bool pack, int64_t max_rounds,
+                                            int32_t* __restrict__ rounds,
+                                            BatchCursor& cur) {
+  const int64_t tbl = max_rounds * E;
+  const bool act = on && m > 0;
+  const uint64_t bal = __ballot(act);
+  const int a = __popcll(bal);
+  if (r > 0 && (!pack || cur.used + a > E)) {
+    ++cur.b;
+    cur.used = 0;
+  }
+  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (kWave - lane));
+  const int v = cur.used + __popcll(bal & below);
+  const int brow = pack ? v * P : nobrow;
+  if (on) rounds[kBrow * tbl + (int64_t)r * E + lane] = act ? brow : nobrow;
+  if (act) {
+    const int64_t g = (int64_t)cur.b * E + v;
+    rounds[kPairE * tbl + g] = lane;
+    rounds[kPairM * tbl + g] = m;
+    rounds[kPairRow * tbl + g] = brow;
+    rounds[kPairZ * tbl + g] = off_e + cum;
+  }
+  if (lane == 0) {
+    int32_t* rb = rounds + kTables * tbl;
+    rb[r] = cur.b * E + cur.used;
+    rb[max_rounds + r] = cur.b * E + cur.used + a;
+  }
+  cur.used += a;
+}
+
 // Phase 2 (one workgroup): counts n_e = sum_b sums[b][e], exclusive offsets
 // over e, the rounds and their tables, and, when there are more than
 // kSelfScanMaxChunks chunks, every chunk's first position of expert e's
@@ -155,7 +198,8 @@ __global__ __launch_bounds__(256) void plan_chunk_sum_kernel(
 // R is the number of rounds until nothing is left.
 __global__ __launch_bounds__(1024) void plan_scan_kernel(
     int32_t* __restrict__ sums, int64_t nchunks, int E, int ce, int G,
-    bool write_starts, int64_t max_rounds, int32_t* __restrict__ counts,
+    bool write_starts, int64_t max_rounds, bool pack, int pool_rows,
+    int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ n_rounds,
     int32_t* __restrict__ rounds) {
   constexpr int kWaves = 16;
@@ -198,6 +242,8 @@ __global__ __launch_bounds__(1024) void plan_scan_kernel(
       return last - (g0 > 0 ? before : 0);
     };
     const int64_t tbl = max_rounds * E;
+    const int P = (ce + 63) & ~63;
+    BatchCursor cur;
     int rem = tot;
     int r = 0;
     while (__ballot(rem > 0) != 0ull) {
@@ -216,6 +262,9 @@ __global__ __launch_bounds__(1024) void plan_scan_kernel(
         rounds[kUbase * tbl + at] = ub;
         rounds[kPbase * tbl + at] = pb;
       }
+      if (r < max_rounds)
+        place_round(r, lane, on, m, tot - rem, excl, (lane / G) * pool_rows + pb, E, P,
+                    pack, max_rounds, rounds, cur);
       rem -= m;
       ++r;
     }
@@ -271,8 +320,9 @@ __global__ __launch_bounds__(256) void plan_rank_kernel(
     int64_t nchunks, const int32_t* __restrict__ sums,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ n_rounds, int32_t* __restrict__ rounds,
-    int64_t max_rounds, int32_t* __restrict__ perm, int32_t* __restrict__ pos,
-    int32_t* __restrict__ round_of, int32_t* __restrict__ row_of) {
+    int64_t max_rounds, bool pack, int32_t* __restrict__ perm,
+    int32_t* __restrict__ pos, int32_t* __restrict__ round_of,
+    int32_t* __restrict__ row_of) {
   __shared__ int running[kWave];
   __shared__ int offs[kWave];
   __shared__ int cnt[4][kWave];
@@ -337,6 +387,20 @@ __global__ __launch_bounds__(256) void plan_rank_kernel(
         rounds[kCum * tbl + c] = (int)(first < n ? first : n);
         rounds[kUbase * tbl + c] = 0;
         rounds[kPbase * tbl + c] = 0;
+      }
+      // the launch batches, round by round on wavefront 0
+      if (wv == 0) {
+        const int P = (ce + 63) & ~63;
+        const bool on = lane < E;
+        const int64_t n = on ? tots[lane] : 0;
+        BatchCursor cur;
+        for (int r = 0; r < rmax_sh; ++r) {
+          const int64_t first = (int64_t)r * ce;
+          const int64_t left = n - first;
+          const int m = (int)(left <= 0 ? 0 : (left < ce ? left : ce));
+          place_round(r, lane, on, m, (int)(first < n ? first : n), on ? offs[lane] : 0,
+                      lane * P, E, P, pack, max_rounds, rounds, cur);
+        }
       }
     }
     cnt[wv][lane] = pre;
@@ -437,24 +501,24 @@ hipError_t launch_plan(const Shape& s, PlanBuffers b, hipStream_t st) {
   if (self && s.G == 1) {  // one pass: no phase 2
     hipLaunchKernelGGL(plan_rank_kernel<kSelfAll>, dim3((unsigned)nb), dim3(256), 0,
                        st, b.idx, TK, s.E, s.k, s.ce, s.G, nb, sums, b.counts,
-                       b.offsets, b.n_rounds, b.rounds, mr, b.perm, b.pos,
+                       b.offsets, b.n_rounds, b.rounds, mr, s.pack, b.perm, b.pos,
                        b.round_of, b.row_of);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(plan_scan_kernel, dim3(1), dim3(1024), 0, st, sums, nb, s.E,
-                     s.ce, s.G, !self, mr, b.counts, b.offsets, b.n_rounds,
-                     b.rounds);
+                     s.ce, s.G, !self, mr, s.pack, (int)s.pool_rows(), b.counts,
+                     b.offsets, b.n_rounds, b.rounds);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (self)
     hipLaunchKernelGGL(plan_rank_kernel<kSelfPrefix>, dim3((unsigned)nb), dim3(256),
                        0, st, b.idx, TK, s.E, s.k, s.ce, s.G, nb, sums, b.counts,
-                       b.offsets, b.n_rounds, b.rounds, mr, b.perm, b.pos,
+                       b.offsets, b.n_rounds, b.rounds, mr, s.pack, b.perm, b.pos,
                        b.round_of, b.row_of);
   else
     hipLaunchKernelGGL(plan_rank_kernel<kStartsGiven>, dim3((unsigned)nb), dim3(256),
                        0, st, b.idx, TK, s.E, s.k, s.ce, s.G, nb, sums, b.counts,
-                       b.offsets, b.n_rounds, b.rounds, mr, b.perm, b.pos,
+                       b.offsets, b.n_rounds, b.rounds, mr, s.pack, b.perm, b.pos,
                        b.round_of, b.row_of);
   return hipGetLastError();
 }
@@ -477,6 +541,46 @@ void host_next_round(const Shape& s, int64_t* rem, int32_t* rows_out) {
     }
     for (int e = g0; e < g0 + s.G; ++e) rem[e] -= rows_out[e];
   }
+}
+
+// The batches of place_round on the host: rounds in order, each joining
+// the current batch while its pairs fit the E regions (packing), else
+// opening the next.
+BatchWalker::BatchWalker(const Shape& s, const int32_t* counts)
+    : s_(s), left_(0), r_(0), have_pending_(false) {
+  for (int e = 0; e < s.E; ++e) {
+    rem_[e] = counts[e];
+    left_ += counts[e];
+  }
+}
+
+bool BatchWalker::next(LaunchBatch* out) {
+  out->r0 = r_;
+  out->nr = 0;
+  out->nv = 0;
+  while (true) {
+    if (!have_pending_) {
+      if (left_ <= 0) break;
+      host_next_round(s_, rem_, pending_);
+      for (int e = 0; e < s_.E; ++e) left_ -= pending_[e];
+      have_pending_ = true;
+    }
+    int a = 0;
+    for (int e = 0; e < s_.E; ++e) a += pending_[e] > 0;
+    if (out->nr > 0 && (!s_.pack || out->nv + a > s_.E)) break;
+    out->nv += round_pairs(s_.E, pending_, out->rows + out->nv);
+    ++out->nr;
+    ++r_;
+    have_pending_ = false;
+  }
+  return out->nr > 0;
+}
+
+int round_pairs(int E, const int32_t* rows, int32_t* out) {
+  int n = 0;
+  for (int e = 0; e < E; ++e)
+    if (rows[e] > 0) out[n++] = rows[e];
+  return n;
 }
 
 }  // namespace moe

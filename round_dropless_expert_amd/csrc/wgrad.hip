@@ -106,7 +106,7 @@ struct WgradParams {
   float* out1;     // [E][A - A0][B] (NULL when A0 == A)
   const int32_t* rounds;
   const int32_t* n_rounds;
-  int E, r, A, A0, B, G, max_rounds, pool_rows;
+  int E, r, A, A0, B, max_rounds;
   int nr;           // rounds contracted by this launch: r, or r and r + 1
   int tiles;        // tiles of the launch (the grid is this rounded up to 8)
   int all_experts;  // tiles of every expert (round 0: experts without rows get zeros)
@@ -156,9 +156,8 @@ __global__ __launch_bounds__(256, 1) void wgrad_kernel(WgradParams p) {
   const int64_t at0 = (int64_t)p.r * p.E + e, at1 = at0 + p.E;
   const int m0 = __builtin_amdgcn_readfirstlane(p.rounds[kAlloc * tbl + at0]);
   const int m1 = two ? __builtin_amdgcn_readfirstlane(p.rounds[kAlloc * tbl + at1]) : 0;
-  const int64_t gbase = (int64_t)(e / p.G) * p.pool_rows;
-  const int64_t row00 = gbase + p.rounds[kPbase * tbl + at0];
-  const int64_t row01 = two ? gbase + p.rounds[kPbase * tbl + at1] : 0;
+  const int64_t row00 = p.rounds[kBrow * tbl + at0];
+  const int64_t row01 = two ? p.rounds[kBrow * tbl + at1] : 0;
   const int a0 = (local / tb) * kTile, b0 = (local % tb) * kTile;
 
   const uint32_t ubytes = (uint32_t)p.A * 2, vbytes = (uint32_t)p.B * 2;
@@ -368,8 +367,8 @@ hipError_t launch_wgrad(const Shape& s, int r, int nr, const void* U, const void
   const int tiles = n * per;
   WgradParams p{static_cast<const bf16*>(U), static_cast<const bf16*>(V),
                 static_cast<const bf16*>(U1), static_cast<const bf16*>(V1), out0, out1,
-                b.rounds, b.n_rounds, s.E, r, A, A0, B, s.G, (int)s.max_rounds(),
-                (int)s.pool_rows(), nr, tiles, all ? 1 : 0, r == 0 ? 0 : 1};
+                b.rounds, b.n_rounds, s.E, r, A, A0, B, (int)s.max_rounds(),
+                nr, tiles, all ? 1 : 0, r == 0 ? 0 : 1};
   hipLaunchKernelGGL(wgrad_kernel, dim3((unsigned)((tiles + 7) / 8 * 8)), dim3(256), 0,
                      st, p);
   return hipGetLastError();

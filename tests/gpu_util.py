@@ -98,7 +98,43 @@ def to_np(t: torch.Tensor) -> np.ndarray:
         else t.detach().cpu().numpy()
 
 
-def assert_plan_equal(views: dict, p: oracle.Plan, idx: np.ndarray):
+def reference_placement(p: oracle.Plan, E: int, cfg):
+    """The launch batches of a plan and where every (round, expert) matrix
+    starts in the round buffer: with one capacity group per expert and one
+    set of round buffers, consecutive rounds share a batch while their pairs
+    (experts with rows) number at most E, and pair v of a batch starts at
+    row v * P; otherwise each round is a batch and expert e's matrix starts
+    at its group's block plus the padded rows of the group's lower experts.
+    Returns (brow [R, E], pairs: list per batch of (r, e, m, brow, z row),
+    rbeg [R], rend [R])."""
+    geo = B.buffer_geometry(cfg)
+    G, P, Q = geo["G"], geo["pad"], geo["Q"]
+    pack = G == 1 and geo["S"] == 1
+    brow = np.zeros((p.R, E), dtype=np.int64)
+    batches, rbeg, rend = [], np.zeros(p.R, np.int64), np.zeros(p.R, np.int64)
+    for r in range(p.R):
+        m = p.rows_in_round(r)
+        first = p.first_in_round(r)
+        act = [e for e in range(E) if m[e] > 0]
+        if not batches or not pack or len(batches[-1]) + len(act) > E:
+            batches.append([])
+        cur = batches[-1]
+        b = len(batches) - 1
+        rbeg[r] = b * E + len(cur)
+        mp = (m + 63) // 64 * 64
+        for e in range(E):
+            g0 = e - e % G
+            brow[r, e] = (e // G) * Q + mp[g0:e].sum()
+        for e in act:
+            if pack:
+                brow[r, e] = len(cur) * P
+            cur.append((r, e, int(m[e]), int(brow[r, e]),
+                        int(p.offsets[e] + first[e])))
+        rend[r] = b * E + len(cur)
+    return brow, batches, rbeg, rend
+
+
+def assert_plan_equal(views: dict, p: oracle.Plan, idx: np.ndarray, cfg=None):
     np.testing.assert_array_equal(views["idx"].cpu().numpy(), idx)
     np.testing.assert_array_equal(views["counts"].cpu().numpy(), p.counts)
     np.testing.assert_array_equal(views["offsets"].cpu().numpy(), p.offsets)
@@ -122,18 +158,34 @@ def assert_plan_equal(views: dict, p: oracle.Plan, idx: np.ndarray):
                 g0 = e - e % p.G
                 ex[e] = v[g0:e].sum()
             np.testing.assert_array_equal(row, ex, err_msg=f"{name} round {r}")
+    if cfg is None:
+        return
+    # launch batches: buffer rows of every active (round, expert), the pair
+    # tables and each round's range of pairs
+    brow, batches, rbeg, rend = reference_placement(p, E, cfg)
+    full = views["rounds"].cpu().numpy().astype(np.int64)
+    for r in range(p.R):
+        act = p.rows_in_round(r) > 0
+        np.testing.assert_array_equal(full[4, r][act], brow[r][act],
+                                      err_msg=f"brow round {r}")
+    rp = views["round_pairs"].cpu().numpy()[:, :p.R].astype(np.int64)
+    np.testing.assert_array_equal(rp[0], rbeg, err_msg="rbeg")
+    np.testing.assert_array_equal(rp[1], rend, err_msg="rend")
+    flat = full[5:9].reshape(4, -1)
+    for b, pairs in enumerate(batches):
+        for v, (r, e, m, row, z) in enumerate(pairs):
+            np.testing.assert_array_equal(flat[:, b * E + v], [e, m, row, z],
+                                          err_msg=f"pair {v} of batch {b}")
 
 
 def expert_rows(views: dict, cfg, r: int, e: int, m: int, cols: int, dtype,
                 buf: str = "xr") -> torch.Tensor:
     """Rows 0..m-1 of expert e's matrix of round r in the xr (or h) round
-    buffer: in set r % S it starts at row (e // G) * Q + pbase(r, e), padded
-    to 64."""
+    buffer: in set r % S it starts at row brow(r, e), padded to 64."""
     geo = B.buffer_geometry(cfg)
     es = torch.empty(0, dtype=dtype).element_size()
     rb = cols * es
-    start = (r % geo["S"]) * geo["rows"] + (e // geo["G"]) * geo["Q"] + \
-        int(views["rounds"][3, r, e].item())
+    start = (r % geo["S"]) * geo["rows"] + int(views["rounds"][4, r, e].item())
     rows = (m + 63) // 64 * 64
     seg = views[buf][start * rb:(start + rows) * rb]
     return untile(seg, rows, cols, dtype)[:m]

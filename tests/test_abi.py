@@ -61,7 +61,8 @@ def expected_total(T, E, k, d, f, C, es, G=1, S=1):
     nb = ceil_div(T, 8) + ceil_div(T, 256)  # plan histogram rows, chunk sums
     # counts and R share one block: [E counts][R]
     parts = [TK * 4, TK * 4, (E + 1) * 4, (E + 1) * 4, TK * 4, TK * 4, TK * 4,
-             TK * 4, 4 * M * E * 4, nb * E * 4, S * rows * d * es, S * rows * f * es,
+             TK * 4, (9 * M * E + 2 * M) * 4, nb * E * 4, S * rows * d * es,
+             S * rows * f * es,
              TK * d * es]
     return sum(al(p) for p in parts)
 
@@ -164,13 +165,18 @@ def test_pointer_and_workspace_checks_before_any_hip_call(B):
     assert L.moe_plan(c, None, p, need, None, None) == B.MOE_ERR_INVALID_ARGUMENT
     assert L.moe_plan(c, p, p + 8, need, None, None) == B.MOE_ERR_INVALID_ARGUMENT
     # round range: ceil(T / C') rounds at most
-    assert L.moe_dispatch(c, -1, p, p, need, None) == B.MOE_ERR_INVALID_ARGUMENT
-    assert L.moe_dispatch(c, 8, p, p, need, None) == B.MOE_ERR_INVALID_ARGUMENT
-    assert L.moe_expert_ffn(c, 8, p, p, p, None, p, need, None) == \
+    assert L.moe_dispatch(c, -1, 1, p, p, need, None) == B.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_dispatch(c, 8, 1, p, p, need, None) == B.MOE_ERR_INVALID_ARGUMENT
+    # a round range: n_rounds >= 1 and round + n_rounds <= ceil(T / C')
+    assert L.moe_dispatch(c, 0, 0, p, p, need, None) == B.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_dispatch(c, 5, 4, p, p, need, None) == B.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_expert_ffn(c, 8, 1, p, p, p, None, p, need, None) == \
         B.MOE_ERR_INVALID_ARGUMENT
-    assert L.moe_expert_gate_up(c, 0, p, None, None, p, need, None) == \
+    assert L.moe_expert_ffn(c, 7, 2, p, p, p, None, p, need, None) == \
         B.MOE_ERR_INVALID_ARGUMENT
-    assert L.moe_expert_down(c, -1, p, None, p, need, None) == \
+    assert L.moe_expert_gate_up(c, 0, 1, p, None, None, p, need, None) == \
+        B.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_expert_down(c, -1, 1, p, None, p, need, None) == \
         B.MOE_ERR_INVALID_ARGUMENT
     assert L.moe_combine(c, p, need, None, None) == B.MOE_ERR_INVALID_ARGUMENT
     assert L.moe_pack_weights(c, p, p, None, p, p, p, None) == \

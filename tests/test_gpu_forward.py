@@ -57,7 +57,7 @@ def test_forward_matches_oracle(name):
     cfg, ws, y = forward(case)
     views = B.workspace_views(cfg, ws)
     p = oracle.plan(case.idx, w.E, w.C)
-    assert_plan_equal(views, p, case.idx)
+    assert_plan_equal(views, p, case.idx, cfg)
     n = SAMPLE[name]
     tokens = np.arange(w.T) if n is None else sample_tokens(w.T, p, w.k, n)
     y_ref = case.oracle_y(tokens)
@@ -133,8 +133,7 @@ def test_full_size_stages_on_sampled_slots(name):
     R, counts = B.moe_plan(cfg, case.logits, ws, return_counts=True)
     views = B.workspace_views(cfg, ws)
     p = oracle.plan(case.idx, w.E, w.C)
-    assert_plan_equal(views, p, case.idx)
-    geo = B.buffer_geometry(cfg)
+    assert_plan_equal(views, p, case.idx, cfg)
     rng = np.random.default_rng(11)
     per_round_z = max(4, Z_TOTAL // R)
     z_assign = []
@@ -150,8 +149,9 @@ def test_full_size_stages_on_sampled_slots(name):
         chosen = {slots[i] for i in pick} | {(busiest, 0), (busiest, int(m[busiest]) - 1)}
         chosen = sorted(chosen)
         a = np.array([p.perm[p.offsets[e] + first[e] + c] for e, c in chosen])
-        # G = 1: expert e's matrix of the round starts at buffer row e * P
-        brow = np.array([e * geo["Q"] + c for e, c in chosen])
+        # the matrix of (r, e) starts at buffer row brow(r, e)
+        br = views["rounds"][4, r].cpu().numpy()
+        brow = np.array([int(br[e]) + c for e, c in chosen])
         got = tiled_rows(views["xr"], brow, w.d_model, torch.bfloat16)
         want = case.x[torch.from_numpy(a // w.k).to(case.dev)]
         assert torch.equal(got.view(torch.int16), want.view(torch.int16)), f"xr round {r}"
@@ -199,7 +199,7 @@ def test_capacity_groups_match_oracle_and_are_bit_identical(name, groups):
     for G in groups:
         cfg, ws, y = forward(case, group=G)
         p = oracle.plan_groups(case.idx, w.E, w.C, G)
-        assert_plan_equal(B.workspace_views(cfg, ws), p, case.idx)
+        assert_plan_equal(B.workspace_views(cfg, ws), p, case.idx, cfg)
         assert torch.equal(ref, y.view(ib)), f"G={G} differs from G=1"
         assert torch.isfinite(B.workspace_views(cfg, ws)["z"].float()).all()
         del ws, y
@@ -222,7 +222,7 @@ def test_two_round_buffer_sets_are_bit_identical(name):
         cfg, ws, y = forward(case, group=G, sets=2)
         assert torch.equal(ref, y.view(ib)), f"S=2 G={G} differs from S=1"
         p = oracle.plan_groups(case.idx, w.E, w.C, G)
-        assert_plan_equal(B.workspace_views(cfg, ws), p, case.idx)
+        assert_plan_equal(B.workspace_views(cfg, ws), p, case.idx, cfg)
         assert torch.isfinite(B.workspace_views(cfg, ws)["z"].float()).all()
         y.fill_(float("nan"))
         note(f"{name}: moe_forward S=2 G={G} again")

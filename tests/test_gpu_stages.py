@@ -70,7 +70,7 @@ def test_stages_match_oracle(w, G, S, layout):
     # tiled weights: launch shapes fitted to each round (as moe_forward);
     # row-major: the default shape
     counts_host = counts if layout == "tiled" else None
-    assert_plan_equal(views, p, case.idx)
+    assert_plan_equal(views, p, case.idx, cfg)
     wt = views["weight"].cpu().numpy().astype(np.float64)
     assert np.all(np.abs(wt - case.wt) <= 1e-6 * case.wt), "routing weights"
 
@@ -109,6 +109,7 @@ def test_stages_match_oracle(w, G, S, layout):
         # a round past R computes nothing, whatever its (unset) tables hold
         note(f"{w.name}/G{G}/S{S}/{layout}: round {R} of {M} (past R)")
         views["rounds"][:, R:] = 1 << 29
+        views["round_pairs"][:, R:] = 1 << 29
         before = [views[n].view(torch.uint8).clone() for n in ("xr", "h", "z")]
         B.moe_dispatch(cfg, R, case.x, ws)
         B.moe_expert_ffn(cfg, R, wg, wu, wd, ws)
@@ -168,7 +169,7 @@ def test_plan_with_more_chunks_than_the_self_scan_limit(G):
                            return_counts=True)
     assert R == p.R
     np.testing.assert_array_equal(counts, p.counts)
-    assert_plan_equal(B.workspace_views(cfg, ws), p, idx)
+    assert_plan_equal(B.workspace_views(cfg, ws), p, idx, cfg)
 
 
 EDGE_CASES = [
@@ -196,7 +197,7 @@ def test_degenerate_shapes_forward(w):
     torch.cuda.synchronize()
     views = B.workspace_views(cfg, ws)
     p = oracle.plan(case.idx, w.E, w.C)
-    assert_plan_equal(views, p, case.idx)
+    assert_plan_equal(views, p, case.idx, cfg)
     assert_close(to_np(y), case.oracle_y(np.arange(w.T)), w.dtype, "y")
     assert torch.isfinite(views["z"].float()).all()
 
@@ -242,7 +243,7 @@ def test_nonfinite_logits_give_an_in_range_plan(E, k):
     # the plan of the whole batch is the oracle's plan of these picks
     p = oracle.plan(idx, E, w.C)
     assert R == p.R
-    assert_plan_equal(views, p, idx)
+    assert_plan_equal(views, p, idx, cfg)
 
     x, wg, wu, wd = (torch.from_numpy(a).cuda() for a in (inp.x, inp.Wg, inp.Wu, inp.Wd))
     y = torch.full((T, d), float("nan"), device="cuda:0")
@@ -255,3 +256,85 @@ def test_nonfinite_logits_give_an_in_range_plan(E, k):
     y_ref = oracle.forward_tokens(np.arange(T - bad), idx_ref, wt_ref,
                                   inp.x[bad:], inp.Wg, inp.Wu, inp.Wd)
     assert_close(y[bad:].cpu().numpy(), y_ref, "f32", "y of the finite rows")
+
+
+# cases whose plans have launch batches of several rounds (seed 0):
+# batched_bf16 (0)(1-2)(3-6)(7-13)(14-23), skewed_slice (0)(1-7),
+# batched_f32 (0)(1)(2-3)(4-6)(7-12)
+BATCH_CASES = [
+    W("batched_bf16", T=2000, d_model=256, d_ff=384, E=16, k=2, C=64, dtype="bf16",
+      skew=("zipf", 1.2)),
+    dataclasses.replace(configs.SKEWED_BF16, name="skewed_slice", T=2048, C=256),
+    W("batched_f32", T=600, d_model=128, d_ff=192, E=8, k=2, C=40, dtype="f32",
+      skew=("zipf", 1.5)),
+]
+
+
+@pytest.mark.parametrize("w", BATCH_CASES, ids=lambda w: w.name)
+def test_batched_stages_match_oracle(w):
+    """Stage calls over whole launch batches, as moe_forward makes them: one
+    dispatch over the batch's rounds puts every row at its pair's region
+    (bit-exact), one launch of each GEMM over the batch's pairs gives h and
+    z within tolerance, and the layer's y matches the oracle; the same
+    batches without counts (the default launch shape) give the same bits,
+    and so does moe_forward."""
+    case = Case(w)
+    cfg = case.cfg()
+    wg, wu, wd = case.weights()
+    ws = case.workspace(cfg)
+    note(f"{w.name}: moe_plan")
+    R, counts = B.moe_plan(cfg, case.logits, ws, return_counts=True)
+    views = B.workspace_views(cfg, ws)
+    p = oracle.plan(case.idx, w.E, w.C)
+    assert R == p.R
+    assert_plan_equal(views, p, case.idx, cfg)
+    batches = B.launch_batches(cfg, counts)
+    assert any(n > 1 for _, n in batches)
+    dt = el_dtype(w)
+    ibits = torch.int16 if w.dtype == "bf16" else torch.int32
+    for r0, n in batches:
+        note(f"{w.name}: moe_dispatch rounds {r0}..{r0 + n - 1}")
+        B.moe_dispatch(cfg, r0, case.x, ws, n_rounds=n)
+        torch.cuda.synchronize()
+        pairs, assigns = [], []
+        for r in range(r0, r0 + n):
+            m = p.rows_in_round(r)
+            first = p.first_in_round(r)
+            for e in range(w.E):
+                if m[e] > 0:
+                    a = [int(p.perm[p.offsets[e] + first[e] + c]) for c in range(int(m[e]))]
+                    pairs.append((r, e, int(m[e])))
+                    assigns += a
+        xr = torch.cat([expert_rows(views, cfg, r, e, m, w.d_model, dt) for r, e, m in pairs])
+        a_t = torch.tensor(assigns, device=case.dev, dtype=torch.long)
+        assert torch.equal(xr.view(ibits), case.x[a_t // w.k].view(ibits)), \
+            f"xr of rounds {r0}..{r0 + n - 1}"
+        note(f"{w.name}: moe_expert_ffn rounds {r0}..{r0 + n - 1}")
+        B.moe_expert_ffn(cfg, r0, wg, wu, wd, ws, counts_host=counts, n_rounds=n)
+        torch.cuda.synchronize()
+        h_ref, o_ref = oracle.assignment_outputs(
+            np.array(assigns), case.idx, case.inp.x, case.inp.Wg, case.inp.Wu,
+            case.inp.Wd, want_h=True)
+        h = torch.cat([expert_rows(views, cfg, r, e, m, w.d_ff, dt, "h") for r, e, m in pairs])
+        assert_close(to_np(h), h_ref, w.dtype, f"h of rounds {r0}..{r0 + n - 1}")
+        rows = torch.from_numpy(p.pos[np.array(assigns)]).to(case.dev).long()
+        assert_close(to_np(views["z"][rows]), o_ref, w.dtype,
+                     f"z of rounds {r0}..{r0 + n - 1}")
+    y = case.new_y()
+    B.moe_combine(cfg, ws, y)
+    torch.cuda.synchronize()
+    assert_close(to_np(y), case.oracle_y(np.arange(w.T)), w.dtype, "y")
+    # default launch shape over the same batches, and moe_forward: same bits
+    ws2 = case.workspace(cfg)
+    B.moe_plan(cfg, case.logits, ws2)
+    for r0, n in batches:
+        B.moe_dispatch(cfg, r0, case.x, ws2, n_rounds=n)
+        B.moe_expert_ffn(cfg, r0, wg, wu, wd, ws2, n_rounds=n)
+    y2 = case.new_y()
+    B.moe_combine(cfg, ws2, y2)
+    y3 = case.new_y()
+    note(f"{w.name}: moe_forward")
+    B.moe_forward(cfg, case.logits, case.x, wg, wu, wd, y3, ws2)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(ibits), y2.view(ibits)), "launch shapes disagree"
+    assert torch.equal(y.view(ibits), y3.view(ibits)), "moe_forward disagrees"
