@@ -43,9 +43,10 @@
  *
  * Ownership: the caller allocates every buffer, including the workspace of
  * moe_workspace_size() bytes. The library allocates no device memory; its
- * only state is, per calling thread and device, the small pinned host
- * buffer, side stream and events moe_forward and moe_backward use to read
- * the plan's counts (see moe_forward). All work is enqueued on the caller's
+ * only state is, per device, a pool of the small pinned host buffer, side
+ * stream and events with which moe_forward and moe_backward read the
+ * plan's counts (see moe_forward), and the static workspace of
+ * moe_forward_static. All work is enqueued on the caller's
  * HIP stream (`stream` is a hipStream_t; NULL means the null stream). Calls
  * on one workspace must not overlap in time. Device pointers must be
  * 16-byte aligned and point to memory of the current device: the library
@@ -352,9 +353,12 @@ moe_status_t moe_combine(const moe_config_t *cfg, const void *ws,
  * weighted combine. y is written in full.
  * Returns after enqueueing the combine (the plan's wait is the only host
  * synchronisation; round 0's dispatch is queued before it). For that read
- * the library keeps, per calling thread and device, a pinned host buffer of
- * 65 int32, a side stream of default priority that does the copy, and three
- * events, created on first use. With S = 2 the rounds overlap as the method
+ * the call takes from a pool of the current device a set of a pinned host
+ * buffer of 65 int32, a side stream of default priority that does the copy
+ * and three events, and returns it when it returns: sets are created when
+ * no idle one is left, so a device never holds more than the most calls in
+ * flight on it at once (from any number of threads), and are kept until the
+ * process ends. With S = 2 the rounds overlap as the method
  * overlaps dispatch with compute ("Frontier Pre-training at Microsoft AI
  * (MAI-Base-2)", section "Key claims"): odd rounds run on the side stream with buffer set 1, even rounds
  * on the caller's stream with set 0 (round 1's dispatch is also queued

@@ -207,13 +207,18 @@ moe_status_t num_cus(int* out) {
   return MOE_OK;
 }
 
-// Per thread and device: a small pinned host buffer that receives the
-// plan's counts and R, a side stream (default priority) that copies them,
-// and two events: "planned" on the caller's stream behind the plan, "done"
-// on the side stream behind the copy. moe_forward queues round 0's dispatch
-// on the caller's stream while the side stream copies, so neither the copy
-// nor the host's wake-up delays the GPU. Created on first use and kept for
-// the life of the thread.
+// The forward's and backward's read of the plan: a small pinned host buffer
+// that receives the counts and R, a side stream (default priority) that
+// copies them, and events: "planned" on the caller's stream behind the
+// plan, "done" on the side stream behind the copy, "joined" behind the side
+// stream's rounds. moe_forward queues round 0's dispatch on the caller's
+// stream while the side stream copies, so neither the copy nor the host's
+// wake-up delays the GPU. The sets live in a pool per device: a call takes
+// one for its duration and returns it, so there are never more sets than
+// calls that were in flight at once on that device, whatever the number of
+// calling threads; they are kept until the process ends. A returned set may
+// still have the previous call's side-stream rounds queued; the next call's
+// work on it queues behind them.
 struct PlanReadback {
   int32_t* host = nullptr;  // kMaxExperts + 1 int32, hipHostMalloc
   hipStream_t side = nullptr;
@@ -221,39 +226,72 @@ struct PlanReadback {
   hipEvent_t done = nullptr;
   hipEvent_t joined = nullptr;  // the side stream's rounds are done
 };
-thread_local PlanReadback g_readback[64];
 
-moe_status_t plan_readback(PlanReadback** out) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-  if (dev < 0 || dev >= 64) return fail(MOE_ERR_UNSUPPORTED, "device id >= 64");
-  PlanReadback& r = g_readback[dev];
-  if (!r.host) {
-    void* h = nullptr;
-    e = hipHostMalloc(&h, (kMaxExperts + 1) * sizeof(int32_t), hipHostMallocDefault);
-    if (e != hipSuccess) return hip_fail(e, "hipHostMalloc of the plan readback");
-    r.host = static_cast<int32_t*>(h);
-  }
-  if (!r.side) {
-    e = hipStreamCreateWithFlags(&r.side, hipStreamNonBlocking);
-    if (e != hipSuccess) return hip_fail(e, "hipStreamCreateWithFlags");
-  }
-  if (!r.planned) {
-    e = hipEventCreateWithFlags(&r.planned, hipEventDisableTiming);
+struct ReadbackPool {
+  std::mutex mu;
+  std::vector<PlanReadback*> idle;
+};
+ReadbackPool g_readback_pool[64];
+
+moe_status_t make_readback(PlanReadback* r) {
+  void* h = nullptr;
+  hipError_t e = hipHostMalloc(&h, (kMaxExperts + 1) * sizeof(int32_t), hipHostMallocDefault);
+  if (e != hipSuccess) return hip_fail(e, "hipHostMalloc of the plan readback");
+  r->host = static_cast<int32_t*>(h);
+  e = hipStreamCreateWithFlags(&r->side, hipStreamNonBlocking);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamCreateWithFlags");
+  hipEvent_t* evs[3] = {&r->planned, &r->done, &r->joined};
+  for (hipEvent_t* ev : evs) {
+    e = hipEventCreateWithFlags(ev, hipEventDisableTiming);
     if (e != hipSuccess) return hip_fail(e, "hipEventCreateWithFlags");
   }
-  if (!r.done) {
-    e = hipEventCreateWithFlags(&r.done, hipEventDisableTiming);
-    if (e != hipSuccess) return hip_fail(e, "hipEventCreateWithFlags");
-  }
-  if (!r.joined) {
-    e = hipEventCreateWithFlags(&r.joined, hipEventDisableTiming);
-    if (e != hipSuccess) return hip_fail(e, "hipEventCreateWithFlags");
-  }
-  *out = &r;
   return MOE_OK;
 }
+
+// A readback set of the current device for the duration of one call.
+class ReadbackLease {
+ public:
+  ~ReadbackLease() {
+    if (set_) {
+      ReadbackPool& pool = g_readback_pool[dev_];
+      std::lock_guard<std::mutex> lock(pool.mu);
+      pool.idle.push_back(set_);
+    }
+  }
+  moe_status_t acquire(PlanReadback** out) {
+    hipError_t e = hipGetDevice(&dev_);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev_ < 0 || dev_ >= 64) return fail(MOE_ERR_UNSUPPORTED, "device id >= 64");
+    ReadbackPool& pool = g_readback_pool[dev_];
+    {
+      std::lock_guard<std::mutex> lock(pool.mu);
+      if (!pool.idle.empty()) {
+        set_ = pool.idle.back();
+        pool.idle.pop_back();
+      }
+    }
+    if (!set_) {
+      PlanReadback* r = new PlanReadback();
+      moe_status_t st = make_readback(r);
+      if (st != MOE_OK) {  // release what was made; the error text stays
+        if (r->host) (void)hipHostFree(r->host);
+        if (r->side) (void)hipStreamDestroy(r->side);
+        if (r->planned) (void)hipEventDestroy(r->planned);
+        if (r->done) (void)hipEventDestroy(r->done);
+        if (r->joined) (void)hipEventDestroy(r->joined);
+        delete r;
+        return st;
+      }
+      set_ = r;
+    }
+    *out = set_;
+    return MOE_OK;
+  }
+
+ private:
+  int dev_ = 0;
+  PlanReadback* set_ = nullptr;
+};
 
 #define MOE_HIP(call, where)                         \
   do {                                               \
@@ -727,8 +765,9 @@ moe_status_t moe_backward(const moe_config_t* cfg, const void* x, const void* w_
   int cus = 0;
   if ((st = num_cus(&cus)) != MOE_OK) return st;
   // the forward's counts and R, read once (as in moe_forward)
+  ReadbackLease lease;
   PlanReadback* rb = nullptr;
-  if ((st = plan_readback(&rb)) != MOE_OK) return st;
+  if ((st = lease.acquire(&rb)) != MOE_OK) return st;
   MOE_HIP(hipEventRecord(rb->planned, s), "hipEventRecord");
   MOE_HIP(hipStreamWaitEvent(rb->side, rb->planned, 0), "hipStreamWaitEvent");
   MOE_HIP(hipMemcpyAsync(rb->host, b.pb.counts, (b.s.E + 1) * sizeof(int32_t),
@@ -823,8 +862,9 @@ moe_status_t moe_forward(const moe_config_t* cfg, const float* logits,
   // on the side stream behind the plan. Round 0 always exists and its
   // dispatch needs nothing from the host, so it is queued on the caller's
   // stream before the wait: the GPU gathers while the counts travel.
+  ReadbackLease lease;
   PlanReadback* rb = nullptr;
-  if ((st = plan_readback(&rb)) != MOE_OK) return st;
+  if ((st = lease.acquire(&rb)) != MOE_OK) return st;
   MOE_HIP(hipEventRecord(rb->planned, s), "hipEventRecord");
   MOE_HIP(hipStreamWaitEvent(rb->side, rb->planned, 0), "hipStreamWaitEvent");
   MOE_HIP(hipMemcpyAsync(rb->host, b.pb.counts, (b.s.E + 1) * sizeof(int32_t),

@@ -293,3 +293,57 @@ def test_capacity_helper_matches_the_device_plan(name, G):
             assert R <= 1 + picks.index(C)
         del ws
         torch.cuda.empty_cache()
+
+
+def test_forward_from_many_threads():
+    """The plan readback sets are pooled per device: forwards from threads
+    running at once, each on its own stream and workspace, give the
+    single-thread bits; later forwards from new threads reuse the pooled sets
+    and take no more device memory."""
+    import threading
+
+    case = get_case("tiny_f32")
+    w = case.w
+    cfg = case.cfg(C=100)
+    wg, wu, wd = case.weights()
+    _, _, y_ref = forward(case, C=100, poison=False)
+    n = 4
+    wss = [case.workspace(cfg, poison=False) for _ in range(n)]
+    ys = [case.new_y() for _ in range(n)]
+    streams = [torch.cuda.Stream() for _ in range(n)]
+    errors = []
+
+    def run(i, reps):
+        try:
+            torch.cuda.set_device(0)
+            with torch.cuda.stream(streams[i]):
+                for _ in range(reps):
+                    B.moe_forward(cfg, case.logits, case.x, wg, wu, wd, ys[i], wss[i],
+                                  streams[i])
+            streams[i].synchronize()
+        except Exception as exc:  # reported below
+            errors.append(exc)
+
+    note("tiny_f32: moe_forward from 4 threads at once")
+    torch.cuda.synchronize()
+    threads = [threading.Thread(target=run, args=(i, 5)) for i in range(n)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    for i in range(n):
+        assert torch.equal(ys[i].view(torch.int32), y_ref.view(torch.int32)), f"thread {i}"
+    # the pool now holds at least n sets: n more threads, one at a time,
+    # take no new ones
+    torch.cuda.synchronize()
+    free0, _ = torch.cuda.mem_get_info()
+    note("tiny_f32: moe_forward from 8 new threads, one after another")
+    for k in range(8):
+        t = threading.Thread(target=run, args=(k % n, 1))
+        t.start()
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    free1, _ = torch.cuda.mem_get_info()
+    assert free0 == free1, f"device memory changed by {free0 - free1} bytes"
