@@ -253,9 +253,9 @@ def capacity_curve(args):
 
 
 def backward_bench(args):
-    """Forward + backward of the layer per step (the backward weights packed
-    once per step, as after a weight update), plus per-launch times of one
-    backward from a kernel trace of HIP events."""
+    """Forward + backward of the layer per step. Both read the same tiled
+    weights, packed once before timing (the backward's input-gradient GEMMs
+    read them transposed, so there is no per-step weight repack)."""
     import numpy as np
     import torch
 
@@ -278,8 +278,6 @@ def backward_bench(args):
                    args.group, args.round_buffers)
     wts = [torch.empty_like(t) for t in rm]
     B.moe_pack_weights(cfg, *rm, *wts)
-    wdt = torch.empty(w.E, w.d_ff, w.d_model, dtype=torch.bfloat16, device=dev)
-    wgut = torch.empty(w.E, w.d_model, 2 * w.d_ff, dtype=torch.bfloat16, device=dev)
     ws = torch.empty(B.workspace_size(cfg), dtype=torch.uint8, device=dev)
     bws = torch.empty(B.backward_workspace_size(cfg), dtype=torch.uint8, device=dev)
     y = torch.empty(w.T, w.d_model, dtype=torch.bfloat16, device=dev)
@@ -296,8 +294,7 @@ def backward_bench(args):
         B.moe_forward(cfg, logits, x, *wts, y, ws, stream)
 
     def bwd():
-        B.moe_pack_backward_weights(cfg, *rm, wdt, wgut, stream)
-        B.moe_backward(cfg, x, wts[0], wts[1], wdt, wgut, dy, dx, dl, dWg, dWu, dWd,
+        B.moe_backward(cfg, x, *wts, dy, dx, dl, dWg, dWu, dWd,
                        ws, bws, stream)
 
     for _ in range(args.warmup):

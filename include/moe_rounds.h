@@ -438,21 +438,12 @@ moe_status_t moe_backward_workspace_size(const moe_config_t *cfg, size_t *bytes)
 moe_status_t moe_backward_layout(const moe_config_t *cfg,
                                  moe_backward_layout_t *out);
 
-/* The weights the backward's input-gradient GEMMs read, from the row-major
- * forward weights (w_gate, w_up [E][f][d], w_down [E][d][f], bf16):
- * out_down_t = w_down transposed to [E][f][d] and out_gate_up_t = [w_gate;
- * w_up] transposed to [E][d][2f], both in the tiled layout. Call again
- * whenever the weights change. Asynchronous. */
-moe_status_t moe_pack_backward_weights(const moe_config_t *cfg,
-                                       const void *w_gate, const void *w_up,
-                                       const void *w_down, void *out_down_t,
-                                       void *out_gate_up_t, void *stream);
-
 /* The backward of the layer. ws: the forward's workspace after moe_forward
  * with the same cfg, logits and x (its plan and z are read, nothing in it
- * is written). x, w_gate and w_up as given to moe_forward (w_gate/w_up in
- * cfg->weight_layout); w_down_t and w_gate_up_t from
- * moe_pack_backward_weights. dy [T][d] bf16. Outputs (written in full): dx
+ * is written). x, w_gate, w_up and w_down as given to moe_forward (in
+ * cfg->weight_layout; the input-gradient GEMMs read the same matrices
+ * transposed, so no second copy of the weights exists). dy [T][d] bf16.
+ * Outputs (written in full): dx
  * [T][d] bf16, dlogits [T][E] float, dw_gate, dw_up [E][f][d] and dw_down
  * [E][d][f] float. bws: moe_backward_workspace_size bytes. Waits once for
  * the forward's counts and R (as moe_forward), then asynchronous on stream.
@@ -460,8 +451,8 @@ moe_status_t moe_pack_backward_weights(const moe_config_t *cfg,
  * order follows the rounds. */
 moe_status_t moe_backward(const moe_config_t *cfg, const void *x,
                           const void *w_gate, const void *w_up,
-                          const void *w_down_t, const void *w_gate_up_t,
-                          const void *dy, void *dx, float *dlogits,
+                          const void *w_down, const void *dy, void *dx,
+                          float *dlogits,
                           float *dw_gate, float *dw_up, float *dw_down,
                           const void *ws, size_t ws_bytes, void *bws,
                           size_t bws_bytes, void *stream);

@@ -36,7 +36,7 @@ EXPORTS = ("moe_status_string", "moe_last_error", "moe_hip_runtime_version",
            "moe_expert_down", "moe_pack_weights", "moe_combine", "moe_forward",
            "moe_capacity_curve", "moe_capacity_for_rounds",
            "moe_backward_workspace_size", "moe_backward_layout",
-           "moe_pack_backward_weights", "moe_backward", "moe_forward_static")
+           "moe_backward", "moe_forward_static")
 
 
 class MoeConfig(ctypes.Structure):
@@ -114,15 +114,14 @@ def load() -> ctypes.CDLL:
                                           i64p]
     L.moe_backward_workspace_size.argtypes = [cfgp, ctypes.POINTER(ctypes.c_size_t)]
     L.moe_backward_layout.argtypes = [cfgp, ctypes.POINTER(MoeBackwardLayout)]
-    L.moe_pack_backward_weights.argtypes = [cfgp, vp, vp, vp, vp, vp, vp]
-    L.moe_backward.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+    L.moe_backward.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                vp, sz, vp, sz, vp]
     for n in ("moe_check_config", "moe_workspace_size", "moe_workspace_layout",
               "moe_plan", "moe_launch_batches", "moe_dispatch", "moe_expert_ffn",
               "moe_expert_gate_up", "moe_expert_down", "moe_pack_weights",
               "moe_combine", "moe_forward", "moe_capacity_curve",
               "moe_capacity_for_rounds", "moe_backward_workspace_size",
-              "moe_backward_layout", "moe_pack_backward_weights", "moe_backward",
+              "moe_backward_layout", "moe_backward",
               "moe_forward_static"):
         getattr(L, n).restype = ctypes.c_int
     _lib = L
@@ -369,26 +368,16 @@ def backward_layout(cfg: MoeConfig) -> dict:
     return {n: getattr(L, n) for n in BWD_LAYOUT_FIELDS + ("total",)}
 
 
-def moe_pack_backward_weights(cfg, w_gate, w_up, w_down, out_down_t,
-                              out_gate_up_t, stream=None):
-    """Row-major forward weights -> the backward's transposed tiled weights
-    (out_down_t [E][f][d], out_gate_up_t [E][d][2f])."""
-    nw, el = cfg.E * cfg.d_model * cfg.d_ff, _el(cfg)
-    _check(load().moe_pack_backward_weights(
-        ctypes.byref(cfg), _arg(w_gate, "w_gate", el, nw), _arg(w_up, "w_up", el, nw),
-        _arg(w_down, "w_down", el, nw), _arg(out_down_t, "out_down_t", el, nw),
-        _arg(out_gate_up_t, "out_gate_up_t", el, 2 * nw), _stream(stream)))
-
-
-def moe_backward(cfg, x, w_gate, w_up, w_down_t, w_gate_up_t, dy, dx, dlogits,
+def moe_backward(cfg, x, w_gate, w_up, w_down, dy, dx, dlogits,
                  dw_gate, dw_up, dw_down, ws, bws, stream=None):
-    """The layer's backward after moe_forward (ws: its workspace)."""
+    """The layer's backward after moe_forward (ws: its workspace; the
+    weights as given to moe_forward)."""
     nw, el, nx = cfg.E * cfg.d_model * cfg.d_ff, _el(cfg), cfg.T * cfg.d_model
     f32 = torch.float32
     _check(load().moe_backward(
         ctypes.byref(cfg), _arg(x, "x", el, nx), _arg(w_gate, "w_gate", el, nw),
-        _arg(w_up, "w_up", el, nw), _arg(w_down_t, "w_down_t", el, nw),
-        _arg(w_gate_up_t, "w_gate_up_t", el, 2 * nw), _arg(dy, "dy", el, nx),
+        _arg(w_up, "w_up", el, nw), _arg(w_down, "w_down", el, nw),
+        _arg(dy, "dy", el, nx),
         _arg(dx, "dx", el, nx), _arg(dlogits, "dlogits", f32, cfg.T * cfg.E),
         _arg(dw_gate, "dw_gate", f32, nw), _arg(dw_up, "dw_up", f32, nw),
         _arg(dw_down, "dw_down", f32, nw), _arg(ws, "ws"), _nbytes(ws),

@@ -721,28 +721,8 @@ moe_status_t moe_backward_layout(const moe_config_t* cfg, moe_backward_layout_t*
   return MOE_OK;
 }
 
-moe_status_t moe_pack_backward_weights(const moe_config_t* cfg, const void* w_gate,
-                                       const void* w_up, const void* w_down,
-                                       void* out_down_t, void* out_gate_up_t,
-                                       void* stream) {
-  moe_status_t st = check_bwd_cfg(cfg);
-  if (st != MOE_OK) return st;
-  if ((st = check_ptr(w_gate, "w_gate")) != MOE_OK) return st;
-  if ((st = check_ptr(w_up, "w_up")) != MOE_OK) return st;
-  if ((st = check_ptr(w_down, "w_down")) != MOE_OK) return st;
-  if ((st = check_ptr(out_down_t, "out_down_t")) != MOE_OK) return st;
-  if ((st = check_ptr(out_gate_up_t, "out_gate_up_t")) != MOE_OK) return st;
-  int cus = 0;
-  if ((st = num_cus(&cus)) != MOE_OK) return st;
-  MOE_HIP(moe::launch_pack_backward(shape_of(cfg), w_gate, w_up, w_down, out_down_t,
-                                    out_gate_up_t, cus, static_cast<hipStream_t>(stream)),
-          "backward pack launch");
-  return MOE_OK;
-}
-
 moe_status_t moe_backward(const moe_config_t* cfg, const void* x, const void* w_gate,
-                          const void* w_up, const void* w_down_t,
-                          const void* w_gate_up_t, const void* dy, void* dx,
+                          const void* w_up, const void* w_down, const void* dy, void* dx,
                           float* dlogits, float* dw_gate, float* dw_up, float* dw_down,
                           const void* ws, size_t ws_bytes, void* bws, size_t bws_bytes,
                           void* stream) {
@@ -750,11 +730,11 @@ moe_status_t moe_backward(const moe_config_t* cfg, const void* x, const void* w_
   if (st != MOE_OK) return st;
   Bound b;
   if ((st = bind(cfg, const_cast<void*>(ws), ws_bytes, &b)) != MOE_OK) return st;
-  const void* ptrs[] = {x, w_gate, w_up, w_down_t, w_gate_up_t, dy, dx, dlogits,
+  const void* ptrs[] = {x, w_gate, w_up, w_down, dy, dx, dlogits,
                         dw_gate, dw_up, dw_down, bws};
-  const char* names[] = {"x", "w_gate", "w_up", "w_down_t", "w_gate_up_t", "dy", "dx",
+  const char* names[] = {"x", "w_gate", "w_up", "w_down", "dy", "dx",
                          "dlogits", "dw_gate", "dw_up", "dw_down", "bws"};
-  for (int i = 0; i < 12; ++i)
+  for (int i = 0; i < 11; ++i)
     if ((st = check_ptr(ptrs[i], names[i])) != MOE_OK) return st;
   moe_backward_layout_t L;
   bwd_layout_of(cfg, &L);
@@ -810,10 +790,10 @@ moe_status_t moe_backward(const moe_config_t* cfg, const void* x, const void* w_
       MOE_HIP(moe::launch_recompute(b.s, rr, xr[q], w_gate, w_up, b.pb, prow, nv, gu,
                                     hw[q], cus, s),
               "recompute launch");
-      MOE_HIP(moe::launch_dgate(b.s, rr, dyr[q], w_down_t, b.pb, prow, nv, gu, dgu[q],
+      MOE_HIP(moe::launch_dgate(b.s, rr, dyr[q], w_down, b.pb, prow, nv, gu, dgu[q],
                                 cus, s),
               "dgate launch");
-      MOE_HIP(moe::launch_dx(b.s, rr, dgu[q], w_gate_up_t, b.pb, prow, nv, dz, cus, s),
+      MOE_HIP(moe::launch_dx(b.s, rr, dgu[q], w_gate, w_up, b.pb, prow, nv, dz, cus, s),
               "dx launch");
     }
     MOE_HIP(moe::launch_wgrad(b.s, r, nr, dyr[0], hw[0], dyr[1], hw[1], d, d, f, dw_down,

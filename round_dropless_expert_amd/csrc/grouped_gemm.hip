@@ -84,20 +84,30 @@ struct MmaOp<float> {
 
 // What a launch computes (the operand passes and the epilogue):
 //   kModeGateUp    forward: h = silu(xr Wg^T) * (xr Wu^T) into h
-//   kModeDown      forward: o = h Wd^T into z rows (also the backward's
-//                  dx rows: dgu [Wg | Wu], weights packed as [d][2f])
+//   kModeDown      forward: o = h Wd^T into z rows
 //   kModeRecompute backward: g = xr Wg^T and u = xr Wu^T into gu
 //                  ([rows][2f]: g, then u) and w * silu(g) u into hw
-//   kModeDgate     backward: dh = dyr Wd (weights packed as [f][d]), then
-//                  dg = w dh u silu'(g) and du = w dh silu(g) into dgu
-//                  ([rows][2f]), with g, u read from gu
-enum GemmMode { kModeGateUp = 0, kModeDown = 1, kModeRecompute = 2, kModeDgate = 3 };
+//   kModeDgate     backward: dh = dyr Wd, then dg = w dh u silu'(g) and
+//                  du = w dh silu(g) into dgu ([rows][2f]), with g, u read
+//                  from gu
+//   kModeDx        backward: dx rows = dgu [Wg; Wu] into dz rows (as z)
+// The last two contract over the weights' rows (Wd [d][f] over d, Wg and
+// Wu [f][d] over f): they read the forward's weight matrices transposed
+// (below), so the backward needs no second copy of the weights.
+enum GemmMode {
+  kModeGateUp = 0,
+  kModeDown = 1,
+  kModeRecompute = 2,
+  kModeDgate = 3,
+  kModeDx = 4
+};
 
 template <typename Elem>
 struct GemmParams {
   const Elem* act;   // round buffer [rows][K]: xr (gate/up) or h (down)
-  const Elem* w0;    // [E][*][K]: gate (gate/up) or down weights
-  const Elem* w1;    // [E][N][K]: up weights (gate/up only)
+  const Elem* w0;    // [E][N][K]: gate (gate/up) or down weights; dgate:
+                     // down weights [E][K][N]; dx: gate weights [E][K/2][N]
+  const Elem* w1;    // [E][N][K]: up weights (gate/up); dx: up [E][K/2][N]
   Elem* out;         // h [rows][N] (gate/up) or z [T*k][N] (down)
   Elem* out2;        // hw [rows][N] (recompute only)
   const Elem* aux;   // gu [rows][2N] (dgate only)
@@ -134,6 +144,9 @@ __device__ __forceinline__ float acc_read(float a) {
 constexpr int kRsrcWord3 = 0x00020000;
 
 typedef __attribute__((address_space(3))) char lds_char;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 // Buffer-to-LDS loads (LDS-direct): lane i reads `bytes` at voff + soff
 // of the buffer and writes them to LDS at m0 + bytes * i. Written as asm:
@@ -250,8 +263,11 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
   // two weight matrices per tile (gate rows, then up rows of the same
   // features)
   constexpr bool kGateUp = kMode == kModeGateUp || kMode == kModeRecompute;
+  // weights read transposed: K runs along the matrices' rows
+  constexpr bool kTransW = kMode == kModeDgate || kMode == kModeDx;
   typedef Frags<Elem, WI, WJ> frags_t;
   constexpr int kEs = sizeof(Elem);
+  static_assert(!kTransW || kEs == 2, "transposed weights: bf16 only");
   constexpr int kStageK = kRowBytes / kEs;       // k elements per stage
   constexpr int BN = 64 * WI;                    // weight rows per tile
   constexpr int BM = 64 * WJ;                    // token rows per tile
@@ -327,8 +343,14 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
 
   const uint32_t kbytes = (uint32_t)p.K * kEs;    // bytes of one row
   const uint32_t band_bytes = kbytes * kTileRows;  // one 64-row band, tiled
-  const uint32_t wbytes = (uint32_t)p.N * kbytes;  // one expert's matrix
+  // one expert's weight matrix (dx: each of its two), elements and bytes
+  const int64_t wmat = (int64_t)p.N * (kMode == kModeDx ? p.K / 2 : p.K);
+  const uint32_t wbytes = (uint32_t)(wmat * kEs);
   const uint32_t wstride = p.tiled_w ? (uint32_t)kTileBytes : (uint32_t)kRowBytes;
+  // transposed weights: one matrix row holds N features; a tiled 64-row
+  // band of the matrix is N / 32 blocks of 4 KiB
+  const uint32_t nbytes = (uint32_t)p.N * kEs;
+  const uint32_t band_bytes_t = nbytes * kTileRows;
 
   // Row order inside a stage: weight rows, then token rows. For gate/up the
   // weight rows are all gate rows (features n0 .. n0+NF-1), then all up
@@ -339,9 +361,27 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
   // lane's part of the source offset is the same for every pass: a tiled
   // band is one contiguous 4 KiB block per stage; a row-major band gives
   // row r0 of the band, logical chunk `chunk`.
+  //
+  // Transposed weights: a stage is 32 K rows of the matrix, and pass i holds
+  // the tile's output features 64 i .. 64 i + 63 as two 2 KiB half blocks,
+  // one per 32 features: 32 rows (K) of 64 bytes (32 features), with the
+  // tiled layout's chunk swizzle by row. From a tiled matrix each half block
+  // is the upper or lower half of one 4 KiB block (rows k0 % 64 ..), copied
+  // as it lies: lane tid moves bytes [16 (tid % 128), + 16) of half block
+  // tid / 128. From a row-major matrix the lane gathers the 16 bytes that
+  // belong at that place: row rt = (tid % 128) / 4, logical chunk
+  // (tid % 4) ^ ((rt >> 2) & 3).
   const int r0 = tid >> 2;
   const int chunk = (tid & 3) ^ ((r0 >> 2) & 3);
-  const uint32_t vo_w = p.tiled_w ? (uint32_t)tid * 16 : (uint32_t)r0 * kbytes + chunk * 16;
+  uint32_t vo_w;
+  if constexpr (kTransW) {
+    const int hb = tid >> 7, rt = (tid & 127) >> 2;
+    const int lc = (tid & 3) ^ ((rt >> 2) & 3);
+    vo_w = p.tiled_w ? (uint32_t)hb * kTileBytes + (uint32_t)(tid & 127) * 16
+                     : (uint32_t)rt * nbytes + (uint32_t)(32 * hb + 8 * lc) * kEs;
+  } else {
+    vo_w = p.tiled_w ? (uint32_t)tid * 16 : (uint32_t)r0 * kbytes + chunk * 16;
+  }
   const uint32_t vo_t = (uint32_t)tid * 16;
 
   // Tile t: pair (te, below), feature block and token block, and its operand
@@ -365,9 +405,10 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
     const uint32_t wb = exists ? wbytes : 0u;  // no next tile: all out of range
     const int64_t ex = __builtin_amdgcn_readlane(lane_e, te);  // the pair's expert
     S.rw0 = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(p.w0 + ex * p.N * p.K), 0, (int)wb, kRsrcWord3);
+        (void*)(p.w0 + ex * wmat), 0, (int)wb, kRsrcWord3);
     S.rw1 = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(kGateUp ? p.w1 + ex * p.N * p.K : p.w0), 0, (int)wb, kRsrcWord3);
+        (void*)(kGateUp || kMode == kModeDx ? p.w1 + ex * wmat : p.w0), 0, (int)wb,
+        kRsrcWord3);
     // pair te's matrix: its m rows padded to 64, from its first row
     S.ra = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(p.act + (int64_t)__builtin_amdgcn_readlane(lane_row, te) * p.K), 0,
@@ -376,8 +417,13 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
     for (int i = 0; i < kWPasses; ++i) {
       int feat0 = tn0 + 64 * i;
       if (kGateUp && 64 * i >= BN / 2) feat0 -= BN / 2;  // an up-row pass
-      S.wbase[i] = p.tiled_w ? (uint32_t)(feat0 / 64) * band_bytes
-                             : (uint32_t)feat0 * kbytes;
+      if constexpr (kTransW)  // the pass's first column (features past N: zeros)
+        S.wbase[i] = feat0 >= p.N ? kOutOfRange
+                     : p.tiled_w ? (uint32_t)(feat0 / 32) * kTileBytes
+                                 : (uint32_t)feat0 * kEs;
+      else
+        S.wbase[i] = p.tiled_w ? (uint32_t)(feat0 / 64) * band_bytes
+                               : (uint32_t)feat0 * kbytes;
     }
 #pragma unroll
     for (int j = 0; j < kTPasses; ++j)
@@ -398,8 +444,12 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
   // per-load scalar work is then one add: with one wavefront per SIMD every
   // instruction takes an issue slot the MFMA stream could use.
   const uint32_t lds_wave = (uint32_t)wave_id * 1024;
+  // Transposed weights: stage g is rows 32 g' .. 32 g' + 31 of the matrix
+  // (g' = g, or for dx g - KT / 2 of the up matrix once g reaches the
+  // second half of K): half of a tiled band, or 32 row-major rows.
   struct StageOff {
     uint32_t w[SPB], t[SPB];
+    bool up[SPB];  // dx: the stage's rows are up-matrix rows
   };
   auto stage_off = [&](int ks) {
     StageOff o;
@@ -407,7 +457,17 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
     for (int sub = 0; sub < SPB; ++sub) {
       const int g = ks * SPB + sub;
       const bool in = g < KT;
-      o.w[sub] = in ? (uint32_t)g * wstride : kOutOfRange;
+      if constexpr (kTransW) {
+        o.up[sub] = kMode == kModeDx && g >= KT / 2;
+        const int gh = o.up[sub] ? g - KT / 2 : g;
+        o.w[sub] = !in ? kOutOfRange
+                   : p.tiled_w ? (uint32_t)(gh >> 1) * band_bytes_t +
+                                     (uint32_t)(gh & 1) * (kTileBytes / 2)
+                               : (uint32_t)gh * 32u * nbytes;
+      } else {
+        o.up[sub] = false;
+        o.w[sub] = in ? (uint32_t)g * wstride : kOutOfRange;
+      }
       o.t[sub] = in ? (uint32_t)g * (uint32_t)kTileBytes : kOutOfRange;
     }
     return o;
@@ -415,8 +475,8 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
   auto fetch_one = [&](char* slot_mem, const StageOff& o, const src_t& S, int x) {
     const int sub = x / kPasses, i = x % kPasses;
     const bool w = i < kWPasses;
-    const __amdgpu_buffer_rsrc_t rs =
-        !w ? S.ra : ((kGateUp && 64 * i >= BN / 2) ? S.rw1 : S.rw0);
+    const bool use_w1 = kTransW ? o.up[sub] : (kGateUp && 64 * i >= BN / 2);
+    const __amdgpu_buffer_rsrc_t rs = !w ? S.ra : (use_w1 ? S.rw1 : S.rw0);
     const uint32_t soff = w ? S.wbase[i] + o.w[sub] : S.tbase[i - kWPasses] + o.t[sub];
     const uint32_t lds = (uint32_t)(uintptr_t)(lds_char*)slot_mem +
                          sub * kStageBytes + i * 4096 + lds_wave;
@@ -429,14 +489,40 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
     return wn * (BN / 2) + ib * 32 + l32;
   };
   const int trow = BN + wm * (BM / 2) + l32;
+  // Transposed weight fragments come from gfx950's transposing LDS read
+  // (ds_read_b64_tr_b16): in each group of 16 lanes, lane i receives 16-bit
+  // element i % 4 of the 8 bytes addressed by lanes 4 j + i / 4, j = 0..3.
+  // Lanes 4 j + q of group g address K row 8 (g / 2) + j (+ 4 for the second
+  // read) of the step and features 16 (g % 2) + 4 q .. + 3 of the half
+  // block, so lane l receives feature l % 32 at K rows 8 (l / 32) .. + 7 of
+  // the step: the MFMA operand of that feature. The swizzle repeats every 16
+  // rows, so the per-lane offsets do not depend on the step.
+  const int tgrp = lane >> 4, tgq = lane & 3;
+  const int t_row = 8 * (tgrp >> 1) + ((lane >> 2) & 3);
+  const int t_chunk = 2 * (tgrp & 1) + (tgq >> 1);
+  const int t_lo = t_row * 64 + ((t_chunk ^ ((t_row >> 2) & 3)) << 4) + (tgq & 1) * 8;
+  const int t_hi =
+      (t_row + 4) * 64 + ((t_chunk ^ (((t_row + 4) >> 2) & 3)) << 4) + (tgq & 1) * 8;
+  auto wfrag_t = [&](const char* stage, int hb, int s) {
+    const char* blk = stage + hb * (kTileBytes / 2) + s * 16 * kRowBytes;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4*)(lds_char*)(blk + t_lo));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4*)(lds_char*)(blk + t_hi));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
   frags_t f0, f1;
   // fragment r of step s of the stage at `stage`: weight blocks, then token
   // blocks
   auto read_one = [&](frags_t& f, const char* stage, int s, int r) {
-    if (r < WI)
-      f.a[r] = MmaOp<Elem>::load(stage, wrow_of(r), s, half);
-    else
+    if (r < WI) {
+      if constexpr (kTransW)  // half block of the wavefront's features
+        f.a[r] = wfrag_t(stage, wn * (BN / 64) + r, s);
+      else
+        f.a[r] = MmaOp<Elem>::load(stage, wrow_of(r), s, half);
+    } else {
       f.b[r - WI] = MmaOp<Elem>::load(stage, trow + 32 * (r - WI), s, half);
+    }
   };
 
   // prologue of the workgroup's first tile: super-stages 0 .. 2 in flight;
@@ -906,19 +992,20 @@ hipError_t launch_recompute(const Shape& s, int r, const void* xr, const void* w
   return launch_gemm<bf16, kModeRecompute>(s, p, rows_host, nv, num_cus, st);
 }
 
-hipError_t launch_dgate(const Shape& s, int r, const void* dyr, const void* wd_t,
+hipError_t launch_dgate(const Shape& s, int r, const void* dyr, const void* wd,
                         const PlanBuffers& b, const int32_t* rows_host, int nv,
                         const void* gu, void* dgu, int num_cus, hipStream_t st) {
-  GemmParams<bf16> p = params<bf16>(s, r, 1, dyr, wd_t, nullptr, dgu, b, s.d, s.f, true);
+  GemmParams<bf16> p =
+      params<bf16>(s, r, 1, dyr, wd, nullptr, dgu, b, s.d, s.f, s.tiled_w);
   p.aux = static_cast<const bf16*>(gu);
   return launch_gemm<bf16, kModeDgate>(s, p, rows_host, nv, num_cus, st);
 }
 
-hipError_t launch_dx(const Shape& s, int r, const void* dgu, const void* wgu_t,
-                     const PlanBuffers& b, const int32_t* rows_host, int nv,
-                     void* dz, int num_cus, hipStream_t st) {
-  return launch_gemm<bf16, kModeDown>(
-      s, params<bf16>(s, r, 1, dgu, wgu_t, nullptr, dz, b, 2 * s.f, s.d, true),
+hipError_t launch_dx(const Shape& s, int r, const void* dgu, const void* wg,
+                     const void* wu, const PlanBuffers& b, const int32_t* rows_host,
+                     int nv, void* dz, int num_cus, hipStream_t st) {
+  return launch_gemm<bf16, kModeDx>(
+      s, params<bf16>(s, r, 1, dgu, wg, wu, dz, b, 2 * s.f, s.d, s.tiled_w),
       rows_host, nv, num_cus, st);
 }
 

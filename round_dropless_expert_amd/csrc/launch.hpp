@@ -117,21 +117,22 @@ hipError_t launch_down(const Shape& s, int r0, int nr, const void* h, const void
                        const PlanBuffers& b, const int32_t* rows_host, int nv,
                        void* z, int num_cus, hipStream_t st);
 
-// Backward GEMMs of round r (bf16; weights of the dgrad launches packed by
-// launch_pack_backward): the recompute of g and u into gu [rows][2f] and of
-// w * h into hw [rows][f]; dh = dyr Wd turned into dg and du (with gu) in
-// dgu [rows][2f]; and dx rows = dgu [Wg | Wu] into dz [T*k][d] at the
-// assignments' expert-sorted rows, like z.
+// Backward GEMMs of round r (bf16; the forward's weights, in the shape's
+// weight layout): the recompute of g and u into gu [rows][2f] and of w * h
+// into hw [rows][f]; dh = dyr Wd turned into dg and du (with gu) in dgu
+// [rows][2f]; and dx rows = dgu [Wg; Wu] into dz [T*k][d] at the
+// assignments' expert-sorted rows, like z. The last two read Wd, Wg and Wu
+// transposed.
 hipError_t launch_recompute(const Shape& s, int r, const void* xr, const void* wg,
                             const void* wu, const PlanBuffers& b,
                             const int32_t* rows_host, int nv, void* gu, void* hw,
                             int num_cus, hipStream_t st);
-hipError_t launch_dgate(const Shape& s, int r, const void* dyr, const void* wd_t,
+hipError_t launch_dgate(const Shape& s, int r, const void* dyr, const void* wd,
                         const PlanBuffers& b, const int32_t* rows_host, int nv,
                         const void* gu, void* dgu, int num_cus, hipStream_t st);
-hipError_t launch_dx(const Shape& s, int r, const void* dgu, const void* wgu_t,
-                     const PlanBuffers& b, const int32_t* rows_host, int nv,
-                     void* dz, int num_cus, hipStream_t st);
+hipError_t launch_dx(const Shape& s, int r, const void* dgu, const void* wg,
+                     const void* wu, const PlanBuffers& b, const int32_t* rows_host,
+                     int nv, void* dz, int num_cus, hipStream_t st);
 
 // Weight gradients of rounds r .. r + nr - 1 (nr = 1 or 2; round r's
 // buffers U, V, round r + 1's U1, V1): out_e[a][b] (+)= sum over expert e's
@@ -149,12 +150,6 @@ hipError_t launch_wgrad(const Shape& s, int r, int nr, const void* U, const void
 hipError_t launch_router_backward(const Shape& s, const void* z, const void* dy,
                                   const PlanBuffers& b, float* dlogits, int num_cus,
                                   hipStream_t st);
-// The dgrad GEMMs' weights from row-major Wg, Wu [E][f][d] and Wd [E][d][f]
-// (bf16): Wd transposed to [E][f][d] and [Wg; Wu] transposed to
-// [E][d][2f], both tiled.
-hipError_t launch_pack_backward(const Shape& s, const void* w_gate, const void* w_up,
-                                const void* w_down, void* out_down_t, void* out_gu_t,
-                                int num_cus, hipStream_t st);
 hipError_t launch_fill(float* p, int64_t n, float value, int num_cus, hipStream_t st);
 
 // Host copy of the plan's fill rule: from the entries each expert has left

@@ -25,14 +25,20 @@
 // (checked on the device). Lanes 4 j + p of a group address tokens t0 + j,
 // features c0 + 4 p .. + 3, so lane i gets feature c0 + i at tokens t0 ..
 // t0 + 3: two such reads make one 8-token fragment, and the four rows a
-// group touches cover different banks. A workgroup computes a 256 (b) x
-// 256 (a) tile with 2 x 2 wavefronts of 128 x 128 (4 x 4 blocks of
-// v_mfma_f32_32x32x16_bf16, 256 accumulators); the output block is [b][a],
-// so a lane holds four consecutive b of one a: one 16-byte fp32 store.
-// Four LDS slots form a ring with three stages in flight; the kernel waits
-// on its own loads with exact vmcnt counts, as the grouped GEMM does. The
-// fragments of one K step are read while the previous step's MFMAs run
-// (two register sets), interleaved with the MFMAs at fixed points.
+// group touches cover different banks. A workgroup computes a 256 (a) x
+// 256 (b) tile with 2 x 2 wavefronts of 128 x 128 (4 x 4 blocks of
+// v_mfma_f32_32x32x16_bf16, 256 accumulators). The MFMA's row operand is
+// the a fragment and its column operand the b fragment, so the 32 lanes of
+// a half wavefront hold 32 consecutive b of one a: each fp32 store writes
+// two whole 128-byte row pieces (row-major out), rather than 32-byte
+// pieces of 32 rows. Four LDS slots form a ring with three stages in
+// flight; the kernel waits on its own loads with exact vmcnt counts, as the
+// grouped GEMM does. The fragments of one K step are read while the
+// previous step's MFMAs run (two register sets), interleaved with the
+// MFMAs at fixed points, and the stage loop is unrolled over the four ring
+// slots, so that every LDS address is a per-lane base plus an immediate
+// offset (one wavefront per SIMD: each address instruction would take an
+// issue slot from the matrix core).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -55,21 +61,24 @@ constexpr int kRsrcWord3 = 0x00020000;
 
 typedef __attribute__((address_space(3))) char lds_char;
 
-// Buffer-to-LDS load (LDS-direct): lane i reads 16 bytes at voff + soff of
-// the buffer and writes them to LDS at m0 + 16 i. Asm, so that the compiler
-// neither moves nor waits on it: every wait on these loads is the kernel's
-// own, exact vmcnt count. M0 is declared clobbered (the compiler restores
-// it where it needs it); one wait state separates its write from the load.
+// Buffer-to-LDS loads (LDS-direct) of two 1 KiB pieces: lane i reads 16
+// bytes at v0 + soff of the buffer into LDS at m0 + 16 i, and 16 bytes at
+// v1 + soff + 1024 into LDS at m0 + 1024 + 16 i (the immediate offset
+// advances both addresses). Asm, so that the compiler neither moves nor
+// waits on them: every wait on these loads is the kernel's own, exact vmcnt
+// count. M0 is declared clobbered (the compiler restores it where it needs
+// it); one wait state separates its write from the loads.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff,
-                                           uint32_t soff, uint32_t lds) {
+__device__ __forceinline__ void lds_load_pair(__amdgpu_buffer_rsrc_t rsrc, uint32_t v0,
+                                              uint32_t v1, uint32_t soff, uint32_t lds) {
   asm volatile(
       "s_mov_b32 m0, %0\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %1, %2, %3 offen lds"
+      "buffer_load_dwordx4 %1, %3, %4 offen lds\n\t"
+      "buffer_load_dwordx4 %2, %3, %4 offen offset:1024 lds"
       :
-      : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+      : "s"(lds), "v"(v0), "v"(v1), "s"(rsrc), "s"(soff)
       : "m0");
 }
 #pragma clang diagnostic pop
@@ -172,11 +181,14 @@ __global__ __launch_bounds__(256, 1) void wgrad_kernel(WgradParams p) {
       (void*)(two ? p.V1 + row01 * p.B : p.V), 0, (int)(mpad1 * vbytes), kRsrcWord3);
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char*)&lds[0][0];
 
-  // Loads of a stage: wavefronts 0-1 fetch U, 2-3 fetch V; load x of a
-  // wavefront moves 1 KiB = part x % 2 of the 32-feature half block
-  // h = 4 (wave % 2) + x / 2; lane i moves 16 bytes, of token
-  // k0 + 16 (x % 2) + i / 4 of the stage's segment (zeros past its m, and
-  // past A or B). Stages 0 .. S0-1 are segment 0's, then segment 1's.
+  // Loads of a stage: wavefronts 0-1 fetch U, 2-3 fetch V. A wavefront
+  // moves four 32-feature half blocks h = 0..3 (features fbase + 32 h of
+  // the operand, LDS half block 4 (wave % 2) + h), each as two 1 KiB parts:
+  // lane i moves 16 bytes, of token k0 + 16 part + i / 4 of the stage's
+  // segment (zeros past its m, and past A or B). One M0 value serves both
+  // parts of a half block, whose LDS and buffer addresses both advance by
+  // the load's 1 KiB immediate offset. Stages 0 .. S0-1 are segment 0's,
+  // then segment 1's.
   const int op = wave >> 1;
   const __amdgpu_buffer_rsrc_t rsrc0 = op == 0 ? ru0 : rv0;
   const __amdgpu_buffer_rsrc_t rsrc1 = op == 0 ? ru1 : rv1;
@@ -185,22 +197,21 @@ __global__ __launch_bounds__(256, 1) void wgrad_kernel(WgradParams p) {
   const int fbase = (op == 0 ? a0 : b0) + 128 * (wave & 1);
   const int flim = op == 0 ? p.A : p.B;
   const uint32_t dst0 = lds0 + (uint32_t)(op * kOpBytes + 4 * (wave & 1) * kHalfBlock);
-  // per tile: the buffer offset of load x's 1 KiB inside a stage's 64-row
-  // band (out of range for feature blocks at or past A or B)
-  uint32_t xoff[kLoads];
+  // per tile: this lane's offset of half block h inside a stage's 64-row
+  // band (out of range for feature blocks at or past A or B; the range
+  // check then zero-fills whatever the stage's offset is)
+  uint32_t vh[4];
 #pragma unroll
-  for (int x = 0; x < kLoads; ++x) {
-    const int h = x >> 1, part = x & 1;
-    xoff[x] = fbase + 32 * h < flim
-                  ? (uint32_t)((fbase >> 5) + h) * 4096u + (uint32_t)part * 1024u
-                  : kOutOfRange;
-  }
-  // Per stage: the segment's descriptor, the stage's offset and, per part,
-  // this lane's offset (out of range for tokens past the segment's m).
+  for (int h = 0; h < 4; ++h)
+    vh[h] = fbase + 32 * h < flim ? (uint32_t)((fbase >> 5) + h) * 4096u + (uint32_t)lane * 16u
+                                  : kOutOfRange;
+  // Per stage: the segment's descriptor, the stage's band offset and, per
+  // half block and part, this lane's offset (out of range for tokens past
+  // the segment's m).
   struct StageLd {
     __amdgpu_buffer_rsrc_t rs;
     uint32_t koff;
-    uint32_t vo[2];
+    uint32_t vo[4][2];
   };
   auto stage_ld = [&](int s) {
     StageLd L;
@@ -210,39 +221,57 @@ __global__ __launch_bounds__(256, 1) void wgrad_kernel(WgradParams p) {
     L.rs = seg1 ? rsrc1 : rsrc0;
     L.koff = (uint32_t)(k0 >> 6) * (rb >> 6) * 4096u + (uint32_t)((k0 >> 5) & 1) * kHalfBlock;
 #pragma unroll
-    for (int part = 0; part < 2; ++part)
-      L.vo[part] = k0 + part * 16 + (lane >> 2) < m ? (uint32_t)lane * 16u : kOutOfRange;
+    for (int part = 0; part < 2; ++part) {
+      const bool in = k0 + part * 16 + (lane >> 2) < m;
+#pragma unroll
+      for (int h = 0; h < 4; ++h) L.vo[h][part] = in ? vh[h] : kOutOfRange;
+    }
     return L;
   };
-  auto fetch = [&](const StageLd& L, int s, int x) {
-    const int h = x >> 1, part = x & 1;
-    const uint32_t dst =
-        dst0 + (uint32_t)((s & 3) * kSlotBytes + h * kHalfBlock + part * 1024);
-    lds_load16(L.rs, L.vo[part], L.koff + xoff[x], dst);
+  // half block h of a stage into ring slot `slot`
+  auto fetch = [&](const StageLd& L, int slot, int h) {
+    lds_load_pair(L.rs, L.vo[h][0], L.vo[h][1], L.koff,
+                  dst0 + (uint32_t)(slot * kSlotBytes + h * kHalfBlock));
   };
 
   // this lane's part of a transposed read: group g = lane / 16, position
   // 4 j + q in it -> token 8 (g / 2) + j (+ 4 for the second read) and
   // features 16 (g % 2) + 4 q of a 32-feature block: 16-byte chunk
-  // 2 (g % 2) + q / 2, 8-byte half q % 2, swizzled by the row
+  // 2 (g % 2) + q / 2, 8-byte half q % 2, swizzled by the row (the swizzle
+  // repeats every 16 rows, so it does not depend on the K step). The
+  // fragment reads of a slot, block and K step then differ only by
+  // immediate offsets from eight per-lane bases: operand a or b, first or
+  // second read, slots 0-1 or 2-3 (the offset field holds 16 bits).
   const int grp = lane >> 4, gj = (lane >> 2) & 3, gq = lane & 3;
   const int tr_row = 8 * (grp >> 1) + gj;
   const int tr_chunk = 2 * (grp & 1) + (gq >> 1);
   const int tr_half = (gq & 1) * 8;
-  auto frag = [&](const char* op_base, int feat0, int tok0) {
-    const char* blk = op_base + (feat0 >> 5) * kHalfBlock;
-    const int r0 = tok0 + tr_row, r1 = r0 + 4;
-    const char* p0 = blk + r0 * 64 + ((tr_chunk ^ ((r0 >> 2) & 3)) << 4) + tr_half;
-    const char* p1 = blk + r1 * 64 + ((tr_chunk ^ ((r1 >> 2) & 3)) << 4) + tr_half;
+  const int tr_lo = tr_row * 64 + ((tr_chunk ^ ((tr_row >> 2) & 3)) << 4) + tr_half;
+  const int tr_hi = (tr_row + 4) * 64 + ((tr_chunk ^ (((tr_row + 4) >> 2) & 3)) << 4) + tr_half;
+  const lds_char* ldsb = (const lds_char*)&lds[0][0];
+  const lds_char* base_a = ldsb + wa * 4 * kHalfBlock;
+  const lds_char* base_b = ldsb + kOpBytes + wb * 4 * kHalfBlock;
+  const lds_char* rd[2][2][2];  // [a, b][first, second read][slots 0-1, 2-3]
+#pragma unroll
+  for (int sp = 0; sp < 2; ++sp) {
+    rd[0][0][sp] = base_a + tr_lo + sp * 2 * kSlotBytes;
+    rd[0][1][sp] = base_a + tr_hi + sp * 2 * kSlotBytes;
+    rd[1][0][sp] = base_b + tr_lo + sp * 2 * kSlotBytes;
+    rd[1][1][sp] = base_b + tr_hi + sp * 2 * kSlotBytes;
+  }
+  // fragment of operand o (0: a, 1: b), this wavefront's 32-feature block
+  // blk (0..3), K step ks of the stage in ring slot `slot`
+  auto frag = [&](int o, int slot, int blk, int ks) {
+    const int off = (slot & 1) * kSlotBytes + blk * kHalfBlock + ks * 1024;
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_s16x4*)(lds_char*)p0);
+        (lds_s16x4*)(rd[o][0][slot >> 1] + off));
     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_s16x4*)(lds_char*)p1);
+        (lds_s16x4*)(rd[o][1][slot >> 1] + off));
     const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     return __builtin_bit_cast(bf16x8, v);
   };
 
-  f32x16 acc[4][4];  // [b block][a block]
+  f32x16 acc[4][4];  // [b block][a block]: rows a, columns b
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -255,27 +284,23 @@ __global__ __launch_bounds__(256, 1) void wgrad_kernel(WgradParams p) {
   bf16x8 fb0[4], fa0[4], fb1[4], fa1[4];
   // fragment x of a K step, in the order the MFMAs first use them: b
   // block 0, a blocks 0 .. 3, b blocks 1 .. 3
-  auto read_one = [&](bf16x8 (&fb)[4], bf16x8 (&fa)[4], const char* stage, int ks, int x) {
+  auto read_one = [&](bf16x8 (&fb)[4], bf16x8 (&fa)[4], int slot, int ks, int x) {
     if (x == 0)
-      fb[0] = frag(stage + kOpBytes, wb * 128, ks * 16);
+      fb[0] = frag(1, slot, 0, ks);
     else if (x <= 4)
-      fa[x - 1] = frag(stage, wa * 128 + (x - 1) * 32, ks * 16);
+      fa[x - 1] = frag(0, slot, x - 1, ks);
     else
-      fb[x - 4] = frag(stage + kOpBytes, wb * 128 + (x - 4) * 32, ks * 16);
-  };
-  auto read_step = [&](bf16x8 (&fb)[4], bf16x8 (&fa)[4], const char* stage, int ks) {
-#pragma unroll
-    for (int x = 0; x < 8; ++x) read_one(fb, fa, stage, ks, x);
+      fb[x - 4] = frag(1, slot, x - 4, ks);
   };
   // One K step's 16 MFMAs with kOps other operations spread over them in a
   // fixed order (op(x) after MFMA i for x in [i kOps / 16, (i + 1) kOps /
   // 16)), each group fenced so that the compiler keeps the order.
-  constexpr int kOps = 8 + kLoads / 2;
+  constexpr int kOps = 10;  // 8 fragment reads, 2 half-block fetches
   auto mma_step = [&](const bf16x8 (&fb)[4], const bf16x8 (&fa)[4], auto op) {
 #pragma unroll
     for (int n = 0; n < 16; ++n) {
       const int i = n / 4, j = n % 4;
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[i], fa[j], acc[i][j], 0, 0, 0);
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[j], fb[i], acc[i][j], 0, 0, 0);
 #pragma unroll
       for (int x = n * kOps / 16; x < (n + 1) * kOps / 16; ++x) op(x);
       __builtin_amdgcn_sched_barrier(0);
@@ -287,66 +312,70 @@ __global__ __launch_bounds__(256, 1) void wgrad_kernel(WgradParams p) {
   for (int st = 0; st < 3; ++st) {
     const StageLd L = stage_ld(st);
 #pragma unroll
-    for (int x = 0; x < kLoads; ++x) fetch(L, st, x);
+    for (int h = 0; h < 4; ++h) fetch(L, st, h);
   }
   wait_vmem_barrier<2 * kLoads>();
-  read_step(fb0, fa0, &lds[0][0], 0);
-  // Stage s: the first K step's MFMAs run while the second step's fragments
-  // are read and half of stage s + 3 is fetched into the slot of s - 1 (every
-  // wavefront's reads of it finished before the previous barrier); then the
-  // barrier waits for stage s + 1 (s + 2 and the first half of s + 3 stay in
-  // flight), and the second step's MFMAs run while stage s + 1's first
-  // fragments are read and the rest of s + 3 is fetched.
-  for (int s = 0; s < stages; ++s) {
-    const char* cur = &lds[s & 3][0];
-    const char* nxt = &lds[(s + 1) & 3][0];
+#pragma unroll
+  for (int x = 0; x < 8; ++x) read_one(fb0, fa0, 0, 0, x);
+  // Stage s (in slot u = s % 4): the first K step's MFMAs run while the
+  // second step's fragments are read and half blocks 0-1 of stage s + 3 are
+  // fetched into the slot of s - 1 (every wavefront's reads of it finished
+  // before the previous barrier); then the barrier waits for stage s + 1
+  // (s + 2 and the first half of s + 3 stay in flight), and the second
+  // step's MFMAs run while stage s + 1's first fragments are read and half
+  // blocks 2-3 of s + 3 are fetched. The loop is unrolled over the four
+  // slots so that every LDS address is an immediate offset.
+  auto stage = [&](int s, int u) {
     const StageLd L = stage_ld(s + 3);
     mma_step(fb0, fa0, [&](int x) {
       if (x < 8)
-        read_one(fb1, fa1, cur, 1, x);
+        read_one(fb1, fa1, u, 1, x);
       else
-        fetch(L, s + 3, x - 8);
+        fetch(L, (u + 3) & 3, x - 8);
     });
     wait_vmem_barrier<kLoads + kLoads / 2>();
     mma_step(fb1, fa1, [&](int x) {
       if (x < 8)
-        read_one(fb0, fa0, nxt, 0, x);
+        read_one(fb0, fa0, (u + 1) & 3, 0, x);
       else
-        fetch(L, s + 3, kLoads / 2 + x - 8);
+        fetch(L, (u + 3) & 3, x - 6);
     });
+  };
+  for (int s = 0; s < stages; s += 4) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (s + u < stages) stage(s + u, u);
   }
   // the loads that ran past the last stage read nothing but still write
   // LDS: let them land before the workgroup ends
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  // lane: a = column l32 of the block, b = rows 8 g4 + 4 half + q. (The
+  // lane: b = column l32 of the block, a = rows 8 (v / 4) + 4 half + v % 4
+  // for its values v: every store writes two 128-byte row pieces. (The
   // accumulators are read by asm: give the last MFMAs the wait states a
   // VALU read of their results needs, which the compiler cannot see.)
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  const uint32_t rowb = (uint32_t)p.B * 4u;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int j = 0; j < 4; ++j) {
+    const int ab = a0 + wa * 128 + j * 32;
+    if (ab >= p.A) continue;
+    float* base = ab < p.A0 ? p.out0 + ((int64_t)e * p.A0 + ab) * p.B
+                            : p.out1 + ((int64_t)e * (p.A - p.A0) + (ab - p.A0)) * p.B;
+    const __amdgpu_buffer_rsrc_t ro =
+        __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)(32u * rowb), kRsrcWord3);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int a = a0 + wa * 128 + j * 32 + l32;
-      if (a >= p.A) continue;
-      float* row = a < p.A0 ? p.out0 + ((int64_t)e * p.A0 + a) * p.B
-                            : p.out1 + ((int64_t)e * (p.A - p.A0) + (a - p.A0)) * p.B;
+    for (int i = 0; i < 4; ++i) {
+      const int bb = b0 + wb * 128 + i * 32;
+      if (bb >= p.B) continue;
+      const uint32_t vo = (uint32_t)(4 * half) * rowb + (uint32_t)(bb + l32) * 4u;
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int b = b0 + wb * 128 + i * 32 + 8 * g4 + 4 * half;
-        if (b >= p.B) continue;
-        float4 v = make_float4(acc_get(acc[i][j][4 * g4]), acc_get(acc[i][j][4 * g4 + 1]),
-                               acc_get(acc[i][j][4 * g4 + 2]),
-                               acc_get(acc[i][j][4 * g4 + 3]));
-        float4* dst = reinterpret_cast<float4*>(row + b);
-        if (p.accumulate) {
-          const float4 o = *dst;
-          v.x += o.x;
-          v.y += o.y;
-          v.z += o.z;
-          v.w += o.w;
-        }
-        *dst = v;
+      for (int v = 0; v < 16; ++v) {
+        const uint32_t so = (uint32_t)(8 * (v / 4) + v % 4) * rowb;
+        float x = acc_get(acc[i][j][v]);
+        if (p.accumulate)
+          x += __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ro, (int)vo, (int)so, 0));
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), ro, (int)vo, (int)so, 0);
       }
     }
   }

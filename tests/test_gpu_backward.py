@@ -44,11 +44,6 @@ def run_backward(case, C=None, G=1, layout="tiled", seed=7, S=1):
     B.moe_forward(cfg, case.logits, case.x, wg, wu, wd, y, ws)
     gen = torch.Generator().manual_seed(seed)
     dy = torch.randn(w.T, w.d_model, generator=gen).to(torch.bfloat16).to(case.dev)
-    wdt = torch.empty(w.E, w.d_ff, w.d_model, dtype=torch.bfloat16, device=case.dev)
-    wgut = torch.empty(w.E, w.d_model, 2 * w.d_ff, dtype=torch.bfloat16,
-                       device=case.dev)
-    note(f"{w.name}: moe_pack_backward_weights")
-    B.moe_pack_backward_weights(cfg, case.wg, case.wu, case.wd, wdt, wgut)
     bws = torch.full((B.backward_workspace_size(cfg),), 0xFF, dtype=torch.uint8,
                      device=case.dev)
     nan = float("nan")
@@ -58,7 +53,7 @@ def run_backward(case, C=None, G=1, layout="tiled", seed=7, S=1):
     dWu = torch.full_like(dWg, nan)
     dWd = torch.full((w.E, w.d_model, w.d_ff), nan, device=case.dev)
     note(f"{w.name}: moe_backward C={cfg.C} G={G}")
-    B.moe_backward(cfg, case.x, wg, wu, wdt, wgut, dy, dx, dl, dWg, dWu, dWd, ws, bws)
+    B.moe_backward(cfg, case.x, wg, wu, wd, dy, dx, dl, dWg, dWu, dWd, ws, bws)
     torch.cuda.synchronize()
     return dict(dy=dy, dx=dx, dl=dl, dWg=dWg, dWu=dWu, dWd=dWd)
 
