@@ -797,10 +797,10 @@ moe_status_t moe_backward(const moe_config_t* cfg, const void* x, const void* w_
               "dx launch");
     }
     MOE_HIP(moe::launch_wgrad(b.s, r, nr, dyr[0], hw[0], dyr[1], hw[1], d, d, f, dw_down,
-                              nullptr, b.pb, rows[0], rows[1], s),
+                              nullptr, b.pb, rows[0], rows[1], cus, s),
             "wgrad launch");
     MOE_HIP(moe::launch_wgrad(b.s, r, nr, dgu[0], xr[0], dgu[1], xr[1], 2 * f, f, d,
-                              dw_gate, dw_up, b.pb, rows[0], rows[1], s),
+                              dw_gate, dw_up, b.pb, rows[0], rows[1], cus, s),
             "wgrad launch");
   }
   MOE_HIP(moe::launch_combine(b.s, dz, ones, b.pb.pos, dx, cus, s), "combine launch");

@@ -144,7 +144,8 @@ hipError_t launch_dx(const Shape& s, int r, const void* dgu, const void* wg,
 hipError_t launch_wgrad(const Shape& s, int r, int nr, const void* U, const void* V,
                         const void* U1, const void* V1, int A, int A0, int B,
                         float* out0, float* out1, const PlanBuffers& b,
-                        const int32_t* rows0, const int32_t* rows1, hipStream_t st);
+                        const int32_t* rows0, const int32_t* rows1, int num_cus,
+                        hipStream_t st);
 
 // Router-weight gradient dlogits [T][E] (fp32) from z and dy (bf16).
 hipError_t launch_router_backward(const Shape& s, const void* z, const void* dy,

@@ -117,11 +117,19 @@ struct WgradParams {
   const int32_t* n_rounds;
   int E, r, A, A0, B, max_rounds;
   int nr;           // rounds contracted by this launch: r, or r and r + 1
-  int tiles;        // tiles of the launch (the grid is this rounded up to 8)
+  int tiles;        // tiles of the launch
   int all_experts;  // tiles of every expert (round 0: experts without rows get zeros)
   int accumulate;   // add to out (else store)
 };
 
+// Persistent: each workgroup walks a list of tiles. XCD x (workgroups b
+// with b % 8 == x) takes the tiles [x n8, (x + 1) n8), n8 = ceil(tiles / 8),
+// and its Q workgroups take every Q-th of them, so that at any time an
+// XCD's workgroups work on consecutive tiles of one expert, which share its
+// operand panels in that XCD's L2. The LDS ring runs on across the tiles of
+// a workgroup: the fetches three stages ahead of the MFMAs reach into the
+// next tile, whose first stages then land while the current tile's
+// epilogue stores its results.
 __global__ __launch_bounds__(256, 1) void wgrad_kernel(WgradParams p) {
   __shared__ __attribute__((aligned(1024))) char lds[kSlots][kSlotBytes];
   const int tid = threadIdx.x;
@@ -133,53 +141,51 @@ __global__ __launch_bounds__(256, 1) void wgrad_kernel(WgradParams p) {
   if (p.r >= R) return;
   const bool two = p.nr == 2 && p.r + 1 < R;
 
-  // tile -> expert: expert-major, tiles_a x tiles_b per expert
+  const int Q = (int)gridDim.x / 8;
+  const int xcd = (int)(blockIdx.x % 8), q = (int)(blockIdx.x / 8);
+  const int n8 = (p.tiles + 7) / 8;
+  const int t_first = xcd * n8 + q;
+  const int t_end = (xcd + 1) * n8 < p.tiles ? (xcd + 1) * n8 : p.tiles;
+  if (t_first >= t_end) return;
+
+  // The launch's expert table, in every wavefront's registers: lane e < E
+  // holds expert e's rows in round r (segment 0) and r + 1 (segment 1, the
+  // second buffer set) and the first buffer row of each of its matrices;
+  // lrank: the number of experts with rows below lane e.
+  const int64_t tbl = (int64_t)p.max_rounds * p.E;
+  const bool le = lane < p.E;
+  const int64_t at = (int64_t)p.r * p.E + lane;
+  const int lm0 = le ? p.rounds[kAlloc * tbl + at] : 0;
+  const int lm1 = le && two ? p.rounds[kAlloc * tbl + at + p.E] : 0;
+  const int lrow0 = le ? p.rounds[kBrow * tbl + at] : 0;
+  const int lrow1 = le && two ? p.rounds[kBrow * tbl + at + p.E] : 0;
+  const bool lact = lm0 > 0 || lm1 > 0;
+  const int lrank =
+      __builtin_popcountll(__builtin_amdgcn_ballot_w64(lact) & ((1ull << lane) - 1));
+
+  // tile t -> expert (expert-major: ta x tb tiles each; without all_experts,
+  // the (t / per)-th expert with rows) and its a, b origin
   const int ta = (p.A + kTile - 1) / kTile, tb = (p.B + kTile - 1) / kTile;
   const int per = ta * tb;
-  const int64_t tbl = (int64_t)p.max_rounds * p.E;
-  // XCD-contiguous walk: workgroup b runs on XCD b % 8, so XCD x takes
-  // tiles [x n / 8, (x + 1) n / 8): an expert's tiles, which share its
-  // operand panels, stay on one XCD's L2
-  const int per_xcd = (int)gridDim.x / 8;
-  const int tile = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
-  if (tile >= p.tiles) return;
-  const int slot = tile / per;
-  const int local = tile % per;
-  int e;
-  if (p.all_experts) {
-    e = slot;
-  } else {  // the slot-th expert with rows in these rounds
-    const bool act =
-        lane < p.E && (p.rounds[kAlloc * tbl + (int64_t)p.r * p.E + lane] > 0 ||
-                       (two && p.rounds[kAlloc * tbl + (int64_t)(p.r + 1) * p.E + lane] > 0));
-    const uint64_t mask = __builtin_amdgcn_ballot_w64(act);
-    const uint64_t below = lane == 0 ? 0ull : (mask & (~0ull >> (64 - lane)));
-    const bool hit = act && __builtin_popcountll(below) == slot;
-    const uint64_t h = __builtin_amdgcn_ballot_w64(hit);
-    if (h == 0) return;
-    e = __builtin_ctzll(h);
-  }
-  if (e >= p.E) return;
-  // the expert's rows in round r (segment 0) and, with two rounds, in round
-  // r + 1 (segment 1, the second buffer set): m rows padded to 64 each
-  const int64_t at0 = (int64_t)p.r * p.E + e, at1 = at0 + p.E;
-  const int m0 = __builtin_amdgcn_readfirstlane(p.rounds[kAlloc * tbl + at0]);
-  const int m1 = two ? __builtin_amdgcn_readfirstlane(p.rounds[kAlloc * tbl + at1]) : 0;
-  const int64_t row00 = p.rounds[kBrow * tbl + at0];
-  const int64_t row01 = two ? p.rounds[kBrow * tbl + at1] : 0;
-  const int a0 = (local / tb) * kTile, b0 = (local % tb) * kTile;
-
-  const uint32_t ubytes = (uint32_t)p.A * 2, vbytes = (uint32_t)p.B * 2;
-  const uint32_t mpad0 = (uint32_t)((m0 + 63) & ~63), mpad1 = (uint32_t)((m1 + 63) & ~63);
-  const __amdgpu_buffer_rsrc_t ru0 = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(p.U + row00 * p.A), 0, (int)(mpad0 * ubytes), kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t rv0 = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(p.V + row00 * p.B), 0, (int)(mpad0 * vbytes), kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t ru1 = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(two ? p.U1 + row01 * p.A : p.U), 0, (int)(mpad1 * ubytes), kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t rv1 = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(two ? p.V1 + row01 * p.B : p.V), 0, (int)(mpad1 * vbytes), kRsrcWord3);
-  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char*)&lds[0][0];
+  struct Tile {
+    int e, a0, b0, m0, m1, stages;
+    int64_t row0, row1;
+  };
+  auto tile_at = [&](int t) {
+    Tile T;
+    const int slot = t / per, local = t % per;
+    T.e = p.all_experts ? slot
+                        : (int)__builtin_ctzll(
+                              __builtin_amdgcn_ballot_w64(lact && lrank == slot));
+    T.m0 = __builtin_amdgcn_readlane(lm0, T.e);
+    T.m1 = __builtin_amdgcn_readlane(lm1, T.e);
+    T.row0 = __builtin_amdgcn_readlane(lrow0, T.e);
+    T.row1 = __builtin_amdgcn_readlane(lrow1, T.e);
+    T.a0 = (local / tb) * kTile;
+    T.b0 = (local % tb) * kTile;
+    T.stages = (T.m0 + kStageTok - 1) / kStageTok + (T.m1 + kStageTok - 1) / kStageTok;
+    return T;
+  };
 
   // Loads of a stage: wavefronts 0-1 fetch U, 2-3 fetch V. A wavefront
   // moves four 32-feature half blocks h = 0..3 (features fbase + 32 h of
@@ -187,44 +193,63 @@ __global__ __launch_bounds__(256, 1) void wgrad_kernel(WgradParams p) {
   // lane i moves 16 bytes, of token k0 + 16 part + i / 4 of the stage's
   // segment (zeros past its m, and past A or B). One M0 value serves both
   // parts of a half block, whose LDS and buffer addresses both advance by
-  // the load's 1 KiB immediate offset. Stages 0 .. S0-1 are segment 0's,
+  // the load's 1 KiB immediate offset. A tile's stages are segment 0's,
   // then segment 1's.
   const int op = wave >> 1;
-  const __amdgpu_buffer_rsrc_t rsrc0 = op == 0 ? ru0 : rv0;
-  const __amdgpu_buffer_rsrc_t rsrc1 = op == 0 ? ru1 : rv1;
-  const int S0 = (m0 + kStageTok - 1) / kStageTok;
-  const uint32_t rb = op == 0 ? ubytes : vbytes;
-  const int fbase = (op == 0 ? a0 : b0) + 128 * (wave & 1);
+  const uint32_t rb = op == 0 ? (uint32_t)p.A * 2 : (uint32_t)p.B * 2;  // row bytes
   const int flim = op == 0 ? p.A : p.B;
+  const bf16* src0 = op == 0 ? p.U : p.V;
+  const bf16* src1 = two ? (op == 0 ? p.U1 : p.V1) : src0;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char*)&lds[0][0];
   const uint32_t dst0 = lds0 + (uint32_t)(op * kOpBytes + 4 * (wave & 1) * kHalfBlock);
-  // per tile: this lane's offset of half block h inside a stage's 64-row
-  // band (out of range for feature blocks at or past A or B; the range
-  // check then zero-fills whatever the stage's offset is)
-  uint32_t vh[4];
+  // what this wavefront fetches of a tile: its operand's two segments and,
+  // per half block, this lane's offset inside a stage's 64-row band (out of
+  // range for feature blocks at or past A or B: the range check then
+  // zero-fills whatever the stage's offset is)
+  struct FetchTile {
+    __amdgpu_buffer_rsrc_t rs0, rs1;
+    int S0, stages, m0, m1;
+    uint32_t vh[4];
+  };
+  auto fetch_tile = [&](const Tile& T) {
+    FetchTile F;
+    const int64_t row = (int64_t)(rb / 2);  // elements per buffer row
+    F.rs0 = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(src0 + T.row0 * row), 0, (int)((uint32_t)((T.m0 + 63) & ~63) * rb), kRsrcWord3);
+    F.rs1 = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(src1 + T.row1 * row), 0, (int)((uint32_t)((T.m1 + 63) & ~63) * rb), kRsrcWord3);
+    F.S0 = (T.m0 + kStageTok - 1) / kStageTok;
+    F.stages = T.stages;
+    F.m0 = T.m0;
+    F.m1 = T.m1;
+    const int fbase = (op == 0 ? T.a0 : T.b0) + 128 * (wave & 1);
 #pragma unroll
-  for (int h = 0; h < 4; ++h)
-    vh[h] = fbase + 32 * h < flim ? (uint32_t)((fbase >> 5) + h) * 4096u + (uint32_t)lane * 16u
-                                  : kOutOfRange;
+    for (int h = 0; h < 4; ++h)
+      F.vh[h] = fbase + 32 * h < flim
+                    ? (uint32_t)((fbase >> 5) + h) * 4096u + (uint32_t)lane * 16u
+                    : kOutOfRange;
+    return F;
+  };
   // Per stage: the segment's descriptor, the stage's band offset and, per
   // half block and part, this lane's offset (out of range for tokens past
-  // the segment's m).
+  // the segment's m, and for every stage past the workgroup's last tile).
   struct StageLd {
     __amdgpu_buffer_rsrc_t rs;
     uint32_t koff;
     uint32_t vo[4][2];
   };
-  auto stage_ld = [&](int s) {
+  auto stage_ld = [&](const FetchTile& F, int s, bool valid) {
     StageLd L;
-    const bool seg1 = s >= S0;
-    const int k0 = (seg1 ? s - S0 : s) * kStageTok;
-    const int m = seg1 ? m1 : m0;
-    L.rs = seg1 ? rsrc1 : rsrc0;
+    const bool seg1 = s >= F.S0;
+    const int k0 = (seg1 ? s - F.S0 : s) * kStageTok;
+    const int m = valid ? (seg1 ? F.m1 : F.m0) : 0;
+    L.rs = seg1 ? F.rs1 : F.rs0;
     L.koff = (uint32_t)(k0 >> 6) * (rb >> 6) * 4096u + (uint32_t)((k0 >> 5) & 1) * kHalfBlock;
 #pragma unroll
     for (int part = 0; part < 2; ++part) {
       const bool in = k0 + part * 16 + (lane >> 2) < m;
 #pragma unroll
-      for (int h = 0; h < 4; ++h) L.vo[h][part] = in ? vh[h] : kOutOfRange;
+      for (int h = 0; h < 4; ++h) L.vo[h][part] = in ? F.vh[h] : kOutOfRange;
     }
     return L;
   };
@@ -233,15 +258,28 @@ __global__ __launch_bounds__(256, 1) void wgrad_kernel(WgradParams p) {
     lds_load_pair(L.rs, L.vo[h][0], L.vo[h][1], L.koff,
                   dst0 + (uint32_t)(slot * kSlotBytes + h * kHalfBlock));
   };
+  // The fetch cursor: tile ft of the workgroup's list, its stage fs. Each
+  // call hands out the next stage of the workgroup's sequence (tiles without
+  // rows have no stages and are passed over); past the last tile, stages
+  // that load nothing, so that every stage issues the same loads.
+  int ft = t_first, fs = 0;
+  FetchTile F = fetch_tile(tile_at(ft));
+  auto next_stage = [&]() {
+    while (ft < t_end && fs >= F.stages) {
+      ft += Q;
+      fs = 0;
+      if (ft < t_end) F = fetch_tile(tile_at(ft));
+    }
+    const StageLd L = stage_ld(F, fs, ft < t_end);
+    ++fs;
+    return L;
+  };
 
   // this lane's part of a transposed read: group g = lane / 16, position
   // 4 j + q in it -> token 8 (g / 2) + j (+ 4 for the second read) and
   // features 16 (g % 2) + 4 q of a 32-feature block: 16-byte chunk
   // 2 (g % 2) + q / 2, 8-byte half q % 2, swizzled by the row (the swizzle
-  // repeats every 16 rows, so it does not depend on the K step). The
-  // fragment reads of a slot, block and K step then differ only by
-  // immediate offsets from eight per-lane bases: operand a or b, first or
-  // second read, slots 0-1 or 2-3 (the offset field holds 16 bits).
+  // repeats every 16 rows, so it does not depend on the K step)
   const int grp = lane >> 4, gj = (lane >> 2) & 3, gq = lane & 3;
   const int tr_row = 8 * (grp >> 1) + gj;
   const int tr_chunk = 2 * (grp & 1) + (gq >> 1);
@@ -251,35 +289,27 @@ __global__ __launch_bounds__(256, 1) void wgrad_kernel(WgradParams p) {
   const lds_char* ldsb = (const lds_char*)&lds[0][0];
   const lds_char* base_a = ldsb + wa * 4 * kHalfBlock;
   const lds_char* base_b = ldsb + kOpBytes + wb * 4 * kHalfBlock;
-  const lds_char* rd[2][2][2];  // [a, b][first, second read][slots 0-1, 2-3]
-#pragma unroll
-  for (int sp = 0; sp < 2; ++sp) {
-    rd[0][0][sp] = base_a + tr_lo + sp * 2 * kSlotBytes;
-    rd[0][1][sp] = base_a + tr_hi + sp * 2 * kSlotBytes;
-    rd[1][0][sp] = base_b + tr_lo + sp * 2 * kSlotBytes;
-    rd[1][1][sp] = base_b + tr_hi + sp * 2 * kSlotBytes;
-  }
   // fragment of operand o (0: a, 1: b), this wavefront's 32-feature block
   // blk (0..3), K step ks of the stage in ring slot `slot`
   auto frag = [&](int o, int slot, int blk, int ks) {
-    const int off = (slot & 1) * kSlotBytes + blk * kHalfBlock + ks * 1024;
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_s16x4*)(rd[o][0][slot >> 1] + off));
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_s16x4*)(rd[o][1][slot >> 1] + off));
+    const lds_char* b = (o == 0 ? base_a : base_b) + slot * kSlotBytes + blk * kHalfBlock +
+                        ks * 1024;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(b + tr_lo));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(b + tr_hi));
     const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     return __builtin_bit_cast(bf16x8, v);
   };
 
   f32x16 acc[4][4];  // [b block][a block]: rows a, columns b
+  auto zero_acc = [&]() {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  };
 
-  const int stages = S0 + (m1 + kStageTok - 1) / kStageTok;
   // the fragments of one K step (16 tokens): b blocks, then a blocks
   bf16x8 fb0[4], fa0[4], fb1[4], fa1[4];
   // fragment x of a K step, in the order the MFMAs first use them: b
@@ -306,79 +336,99 @@ __global__ __launch_bounds__(256, 1) void wgrad_kernel(WgradParams p) {
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // prologue: stages 0, 1, 2 in flight, wait for stage 0, read its first
-  // step
+
+  // Epilogue of tile T. lane: b = column l32 of the block, a = rows
+  // 8 (v / 4) + 4 half + v % 4 for its values v: every store writes two
+  // 128-byte row pieces. (The accumulators are read by asm: give the last
+  // MFMAs the wait states a VALU read of their results needs, which the
+  // compiler cannot see.)
+  const uint32_t rowb = (uint32_t)p.B * 4u;
+  auto epilogue = [&](const Tile& T) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int ab = T.a0 + wa * 128 + j * 32;
+      if (ab >= p.A) continue;
+      float* base = ab < p.A0 ? p.out0 + ((int64_t)T.e * p.A0 + ab) * p.B
+                              : p.out1 + ((int64_t)T.e * (p.A - p.A0) + (ab - p.A0)) * p.B;
+      const __amdgpu_buffer_rsrc_t ro =
+          __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)(32u * rowb), kRsrcWord3);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int bb = T.b0 + wb * 128 + i * 32;
+        if (bb >= p.B) continue;
+        const uint32_t vo = (uint32_t)(4 * half) * rowb + (uint32_t)(bb + l32) * 4u;
+        auto so = [&](int v) { return (int)((uint32_t)(8 * (v / 4) + v % 4) * rowb); };
+        if (p.accumulate) {  // later launches: add to the stored sums
+          float o[16];
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            o[v] = __builtin_bit_cast(float,
+                                      __builtin_amdgcn_raw_buffer_load_b32(ro, (int)vo, so(v), 0));
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            __builtin_amdgcn_raw_buffer_store_b32(
+                __builtin_bit_cast(uint32_t, acc_get(acc[i][j][v]) + o[v]), ro, (int)vo, so(v), 0);
+        } else {
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, acc_get(acc[i][j][v])),
+                                                  ro, (int)vo, so(v), 0);
+        }
+      }
+    }
+  };
+
+  // prologue: the first three stages of the sequence in flight, wait for
+  // the first, read its first step
 #pragma unroll
   for (int st = 0; st < 3; ++st) {
-    const StageLd L = stage_ld(st);
+    const StageLd L = next_stage();
 #pragma unroll
     for (int h = 0; h < 4; ++h) fetch(L, st, h);
   }
   wait_vmem_barrier<2 * kLoads>();
 #pragma unroll
   for (int x = 0; x < 8; ++x) read_one(fb0, fa0, 0, 0, x);
-  // Stage s (in slot u = s % 4): the first K step's MFMAs run while the
-  // second step's fragments are read and half blocks 0-1 of stage s + 3 are
-  // fetched into the slot of s - 1 (every wavefront's reads of it finished
-  // before the previous barrier); then the barrier waits for stage s + 1
-  // (s + 2 and the first half of s + 3 stay in flight), and the second
-  // step's MFMAs run while stage s + 1's first fragments are read and half
-  // blocks 2-3 of s + 3 are fetched. The loop is unrolled over the four
-  // slots so that every LDS address is an immediate offset.
-  auto stage = [&](int s, int u) {
-    const StageLd L = stage_ld(s + 3);
-    mma_step(fb0, fa0, [&](int x) {
-      if (x < 8)
-        read_one(fb1, fa1, u, 1, x);
-      else
-        fetch(L, (u + 3) & 3, x - 8);
-    });
-    wait_vmem_barrier<kLoads + kLoads / 2>();
-    mma_step(fb1, fa1, [&](int x) {
-      if (x < 8)
-        read_one(fb0, fa0, (u + 1) & 3, 0, x);
-      else
-        fetch(L, (u + 3) & 3, x - 6);
-    });
-  };
-  for (int s = 0; s < stages; s += 4) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (s + u < stages) stage(s + u, u);
+
+  // Tiles of the workgroup in order; g counts its stages (ring slot g % 4).
+  // A tile without rows (an expert without rows in a launch over every
+  // expert) has no stages and is stored as zeros.
+  //
+  // Stage g: the first K step's MFMAs run while the second step's fragments
+  // are read and half blocks 0-1 of stage g + 3 are fetched into the slot
+  // of g - 1 (every wavefront's reads of it finished before the previous
+  // barrier); then the barrier waits for stage g + 1 (g + 2 and the first
+  // half of g + 3 stay in flight), and the second step's MFMAs run while
+  // stage g + 1's first fragments are read and half blocks 2-3 of g + 3
+  // are fetched. (After an epilogue the barrier's count also waits for
+  // most of its stores, which were issued after the loads of g + 1.)
+  int g = 0;
+  for (int ct = t_first; ct < t_end; ct += Q) {
+    const Tile CT = tile_at(ct);
+    zero_acc();
+    for (int cs = 0; cs < CT.stages; ++cs, ++g) {
+      const int u = g & 3;
+      const StageLd L = next_stage();
+      mma_step(fb0, fa0, [&](int x) {
+        if (x < 8)
+          read_one(fb1, fa1, u, 1, x);
+        else
+          fetch(L, (u + 3) & 3, x - 8);
+      });
+      wait_vmem_barrier<kLoads + kLoads / 2>();
+      mma_step(fb1, fa1, [&](int x) {
+        if (x < 8)
+          read_one(fb0, fa0, (u + 1) & 3, 0, x);
+        else
+          fetch(L, (u + 3) & 3, x - 6);
+      });
+    }
+    epilogue(CT);
   }
   // the loads that ran past the last stage read nothing but still write
   // LDS: let them land before the workgroup ends
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-
-  // lane: b = column l32 of the block, a = rows 8 (v / 4) + 4 half + v % 4
-  // for its values v: every store writes two 128-byte row pieces. (The
-  // accumulators are read by asm: give the last MFMAs the wait states a
-  // VALU read of their results needs, which the compiler cannot see.)
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-  const uint32_t rowb = (uint32_t)p.B * 4u;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int ab = a0 + wa * 128 + j * 32;
-    if (ab >= p.A) continue;
-    float* base = ab < p.A0 ? p.out0 + ((int64_t)e * p.A0 + ab) * p.B
-                            : p.out1 + ((int64_t)e * (p.A - p.A0) + (ab - p.A0)) * p.B;
-    const __amdgpu_buffer_rsrc_t ro =
-        __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)(32u * rowb), kRsrcWord3);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int bb = b0 + wb * 128 + i * 32;
-      if (bb >= p.B) continue;
-      const uint32_t vo = (uint32_t)(4 * half) * rowb + (uint32_t)(bb + l32) * 4u;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const uint32_t so = (uint32_t)(8 * (v / 4) + v % 4) * rowb;
-        float x = acc_get(acc[i][j][v]);
-        if (p.accumulate)
-          x += __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ro, (int)vo, (int)so, 0));
-        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), ro, (int)vo, (int)so, 0);
-      }
-    }
-  }
 }
 
 }  // namespace
@@ -386,7 +436,8 @@ __global__ __launch_bounds__(256, 1) void wgrad_kernel(WgradParams p) {
 hipError_t launch_wgrad(const Shape& s, int r, int nr, const void* U, const void* V,
                         const void* U1, const void* V1, int A, int A0, int B,
                         float* out0, float* out1, const PlanBuffers& b,
-                        const int32_t* rows0, const int32_t* rows1, hipStream_t st) {
+                        const int32_t* rows0, const int32_t* rows1, int num_cus,
+                        hipStream_t st) {
   int active = 0;
   for (int e = 0; e < s.E; ++e) active += rows0[e] > 0 || (nr == 2 && rows1[e] > 0);
   const bool all = r == 0;
@@ -394,12 +445,14 @@ hipError_t launch_wgrad(const Shape& s, int r, int nr, const void* U, const void
   if (n == 0) return hipSuccess;
   const int per = ((A + kTile - 1) / kTile) * ((B + kTile - 1) / kTile);
   const int tiles = n * per;
+  // one workgroup per CU (or per tile), a multiple of 8 for the XCD walk
+  int grid = tiles < num_cus ? tiles : num_cus;
+  grid = (grid + 7) / 8 * 8;
   WgradParams p{static_cast<const bf16*>(U), static_cast<const bf16*>(V),
                 static_cast<const bf16*>(U1), static_cast<const bf16*>(V1), out0, out1,
                 b.rounds, b.n_rounds, s.E, r, A, A0, B, (int)s.max_rounds(),
                 nr, tiles, all ? 1 : 0, r == 0 ? 0 : 1};
-  hipLaunchKernelGGL(wgrad_kernel, dim3((unsigned)((tiles + 7) / 8 * 8)), dim3(256), 0,
-                     st, p);
+  hipLaunchKernelGGL(wgrad_kernel, dim3((unsigned)grid), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
