@@ -332,6 +332,49 @@ def backward_bench(args):
         "backward_workspace_bytes": B.backward_workspace_size(cfg)}), flush=True)
 
 
+def mfma_ceiling(grid: int = 1024, iters: int = 8000, reps: int = 3) -> dict:
+    """The bf16 matrix-core rate this chip sustains: the calibration kernel
+    (libmoe_calibrate.so) runs back-to-back independent 32x32x16 bf16 MFMAs
+    on random operands, no memory traffic, 4 wavefronts per CU. The
+    published 2.5 PFLOP/s assumes 2.4 GHz; under sustained matrix load the
+    clock drops, so this is the practical ceiling a GEMM can approach."""
+    import ctypes
+
+    import torch
+
+    from round_dropless_expert_amd.csrc import build as hip_build
+
+    if not os.path.exists(hip_build.CALIB_LIB):
+        raise RuntimeError(f"{hip_build.CALIB_LIB} is not built (run build())")
+    L = ctypes.CDLL(hip_build.CALIB_LIB)
+    L.moe_calibrate_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                          ctypes.c_int, ctypes.c_void_p]
+    L.moe_calibrate_mfma_bf16.restype = ctypes.c_int
+    gen = torch.Generator().manual_seed(3)
+    ops = torch.randn(8192, generator=gen).to(torch.bfloat16).to("cuda:0")
+    out = torch.empty(grid * 256, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    times = []
+    for r in range(reps + 1):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        rc = L.moe_calibrate_mfma_bf16(ops.data_ptr(), out.data_ptr(), grid, iters,
+                                       ctypes.c_void_p(stream.cuda_stream))
+        e1.record(stream)
+        if rc != 0:
+            raise RuntimeError(f"calibration launch failed (hipError {rc})")
+        torch.cuda.synchronize()
+        if r:
+            times.append(e0.elapsed_time(e1) * 1e-3)
+    flop = float(grid) * 4 * iters * 16 * 32768
+    return {"TFLOPs": flop / min(times) / 1e12,
+            "TFLOPs_median": flop / sorted(times)[len(times) // 2] / 1e12,
+            "kernel": "back-to-back independent v_mfma_f32_32x32x16_bf16, random bf16 "
+                      "operands, 16 accumulators per wavefront, no memory traffic",
+            "grid": grid, "iters": iters}
+
+
 def measure(w, args, steps, warmup, kernel_steps, with_cpu):
     """One workload: timed moe_forward steps, the per-launch pass, the
     roofline of the round-0 gate/up launch and (with_cpu) the oracle."""
@@ -583,6 +626,15 @@ def main():
                                "grouped_gemm_mfma_util_pct", "dispatch_GBps",
                                "dispatch_round0_GBps", "combine_GBps",
                                "peak_allocated_bytes", "layer_bound", "kernels")}}
+    if w.dtype == "bf16":
+        # the rooflines' achieved rates against the rate the matrix cores
+        # sustain on this chip (beside the published peak)
+        cal = mfma_ceiling()
+        out["mfma_ceiling"] = cal
+        rooflines = [out["roofline"]] + [x["roofline"] for x in
+                                         out.get("extra_workloads", {}).values()]
+        for rf in rooflines:
+            rf["frac_of_mfma_ceiling"] = rf["achieved"] / cal["TFLOPs"]
     print(json.dumps(out), flush=True)
 
 if __name__ == "__main__":

@@ -1,4 +1,5 @@
-"""Build libmoe_rounds.so (gfx950) in-tree with hipcc.
+"""Build libmoe_rounds.so (gfx950) in-tree with hipcc, and the benchmark's
+matrix-core calibration library libmoe_calibrate.so.
 
 Every source is compiled for gfx950 only. Packed fp32 instructions are
 disabled on the device side (-packed-fp32-ops); the host pass warns that it
@@ -16,6 +17,8 @@ PKG = os.path.dirname(HERE)
 ROOT = os.path.dirname(PKG)
 OUT_DIR = os.path.join(PKG, "lib")
 LIB = os.path.join(OUT_DIR, "libmoe_rounds.so")
+CALIB_LIB = os.path.join(OUT_DIR, "libmoe_calibrate.so")
+CALIB_SOURCE = "calibrate.hip"
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["route_plan.hip", "dispatch_combine.hip", "grouped_gemm.hip",
@@ -64,6 +67,14 @@ def build(verbose: bool = False) -> str:
     if missing:
         raise RuntimeError(f"{tmp}: undefined kernel symbols {missing}")
     os.replace(tmp, LIB)
+    # the calibration kernel: a library of its own, outside the layer's ABI
+    cobj = _compile(CALIB_SOURCE, verbose)
+    ctmp = CALIB_LIB + ".tmp"
+    cmd = [HIPCC, "-shared", f"--offload-arch={ARCH}", "-o", ctmp, cobj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(ctmp, CALIB_LIB)
     return LIB
 
 

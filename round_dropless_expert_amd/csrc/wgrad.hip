@@ -35,10 +35,7 @@
 // flight; the kernel waits on its own loads with exact vmcnt counts, as the
 // grouped GEMM does. The fragments of one K step are read while the
 // previous step's MFMAs run (two register sets), interleaved with the
-// MFMAs at fixed points, and the stage loop is unrolled over the four ring
-// slots, so that every LDS address is a per-lane base plus an immediate
-// offset (one wavefront per SIMD: each address instruction would take an
-// issue slot from the matrix core).
+// MFMAs at fixed points. The launch is persistent (below).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>

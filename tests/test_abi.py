@@ -291,3 +291,21 @@ def test_binding_rejects_host_tensors_before_the_library(B):
         B.moe_pack_weights(cfg, w, w, wd, w, w, wd)
     with pytest.raises(TypeError):
         B.moe_forward(cfg, logits.numpy(), x, w, w, wd, y, ws)
+
+
+def test_calibration_library_loads_and_checks_arguments():
+    """The benchmark's matrix-core calibration kernel lives in a library of
+    its own (not the layer's ABI); it loads without a GPU and refuses bad
+    arguments before any HIP call."""
+    from round_dropless_expert_amd.csrc import build as hip_build
+    L = ctypes.CDLL(hip_build.CALIB_LIB)
+    f = L.moe_calibrate_mfma_bf16
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                  ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    p = 1 << 20
+    hip_error_invalid_value = 1
+    assert f(None, p, 8, 1, None) == hip_error_invalid_value
+    assert f(p, None, 8, 1, None) == hip_error_invalid_value
+    assert f(p, p, 0, 1, None) == hip_error_invalid_value
+    assert f(p, p, 8, 0, None) == hip_error_invalid_value
