@@ -734,8 +734,60 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
           }
         }
       }
+    } else if constexpr (kMode == kModeGateUp && kEs == 2) {
+      // h: expert e's tiled matrix of the round. A 32-token x 32-feature
+      // block of the accumulators is one contiguous 2 KiB half of a 4 KiB
+      // tiled block (rows c0 % 64 .. + 31 of the band, 64 bytes each), but
+      // the lane layout spreads it over 32 rows, 8 bytes a store. Each
+      // wavefront writes the block into 2 KiB of its 4 KiB share of slot3
+      // (free as in the z epilogue below) in the tiled order, swizzle
+      // included, and copies it out as two whole 1 KiB stores. Rows past m
+      // (up to the 64-row padding the descriptor covers) receive values
+      // computed from the padding rows of the operand; no kernel reads them
+      // for a stored output.
+      const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(p.out + (int64_t)__builtin_amdgcn_readlane(lane_row, e) * p.N), 0,
+          (int)((uint32_t)((m + 63) & ~63) * p.N * kEs), kRsrcWord3);
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+      char* const stg0 = slot3 + wave_id * 4096;
+      const int put_off = l32 * 64 + half * 8;  // this lane's row of the block
+      const int put_swz = (l32 >> 2) & 3;
+#pragma unroll
+      for (int jb = 0; jb < WJ; ++jb) {
+        const int c0 = m0 + wm * (BM / 2) + jb * 32;
+#pragma unroll
+        for (int ib = 0; ib < WI / 2; ++ib) {
+          const int f0 = n0 + wn * (BN / 4) + ib * 32;
+          char* stg = stg0 + ((jb * (WI / 2) + ib) & 1) * 2048;
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            vec4_t o;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              o[q] = from_f32<Elem>(silu_mul(acc_read(acc[ib][jb][4 * g4 + q]),
+                                             acc_read(acc[ib + WI / 2][jb][4 * g4 + q])));
+            *reinterpret_cast<u32x2*>(stg + put_off + ((g4 ^ put_swz) << 4)) =
+                __builtin_bit_cast(u32x2, o);
+          }
+          const uint32_t off =
+              f0 < p.N ? (uint32_t)tiled_offset(c0, (int64_t)f0 * kEs, (int64_t)p.N * kEs)
+                       : kOutOfRange;
+#pragma unroll
+          for (int hk = 0; hk < 2; ++hk)
+            __builtin_amdgcn_raw_buffer_store_b128(
+                *reinterpret_cast<const u32x4*>(stg + hk * 1024 + lane * 16), rh,
+                off + (uint32_t)(hk * 1024 + lane * 16), 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      // every wavefront's staging reads are done before the next tile's ring
+      // writes slot3
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
     } else if constexpr (kMode == kModeGateUp) {
-      // h: expert e's tiled matrix of the round, row c
+      // h (fp32): row c, four features per 16-byte store
       const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(
           (void*)(p.out + (int64_t)__builtin_amdgcn_readlane(lane_row, e) * p.N), 0,
           (int)((uint32_t)((m + 63) & ~63) * p.N * kEs), kRsrcWord3);
