@@ -3,7 +3,8 @@
 Each case draws (from a fixed seed, so every run covers the same cases) the
 shape (T, E, k, d_model, d_ff), the capacity C, the capacity group G, one
 or two sets of round buffers, the weight layout, the element type and the
-routing skew. The forward's plan must match the oracle's bit for bit and y
+routing skew; four fixed cases add the extremes of the routing (k = E = 64,
+one token over 64 experts, a single expert, k = 8). The forward's plan must match the oracle's bit for bit and y
 must be within the dtype's tolerance on every token; for bf16 the backward
 (dx, dlogits on every token, the three weight gradients of two experts)
 must match the oracle's fp64 backward as well."""
@@ -39,7 +40,20 @@ def draw(i: int):
     return w, G, S, layout
 
 
-CASES = [draw(i) for i in range(16)]
+CASES = [draw(i) for i in range(16)] + [
+    # extremes of the routing: every token to every one of 64 experts (k = E,
+    # the router's widest selection; fp32, so the backward is not run), one
+    # token spread over 64 experts, a single expert, and k = 8 (the backward's
+    # largest k) over 16 experts in capacity groups of 4
+    (configs.Workload("edge_k64", T=300, d_model=64, d_ff=64, E=64, k=64, C=37,
+                      dtype="f32", seed=201), 1, 1, "tiled"),
+    (configs.Workload("edge_one_token", T=1, d_model=128, d_ff=64, E=64, k=8, C=1,
+                      dtype="bf16", seed=202), 8, 2, "row_major"),
+    (configs.Workload("edge_one_expert", T=333, d_model=64, d_ff=128, E=1, k=1, C=100,
+                      dtype="bf16", skew=("hot", 0, 5.0), seed=203), 1, 2, "tiled"),
+    (configs.Workload("edge_k8", T=400, d_model=128, d_ff=192, E=16, k=8, C=90,
+                      dtype="bf16", skew=("zipf", 1.0), seed=204), 4, 1, "tiled"),
+]
 
 
 def case_id(c):
