@@ -839,19 +839,28 @@ moe_status_t moe_forward(const moe_config_t* cfg, const float* logits,
   if ((st = num_cus(&cus)) != MOE_OK) return st;
   if ((st = run_plan(b, logits, s)) != MOE_OK) return st;
   // One read of the E per-expert counts followed by R into pinned memory,
-  // on the side stream behind the plan. Round 0 always exists and its
-  // dispatch needs nothing from the host, so it is queued on the caller's
-  // stream before the wait: the GPU gathers while the counts travel.
+  // on the side stream behind the plan. Round 0 always exists, and neither
+  // its dispatch nor its grouped GEMMs need anything from the host (they
+  // read their pairs from the plan's tables; without host counts the GEMMs
+  // take the 256 x 256 tile and one workgroup per CU, the shape a full
+  // round gets, and every shape gives the same results), so they are queued
+  // on the caller's stream first: the GPU gathers and computes round 0
+  // while the counts travel and the host waits for them.
   ReadbackLease lease;
   PlanReadback* rb = nullptr;
   if ((st = lease.acquire(&rb)) != MOE_OK) return st;
   MOE_HIP(hipEventRecord(rb->planned, s), "hipEventRecord");
+  MOE_HIP(moe::launch_dispatch(b.s, 0, 1, x, b.pb, b.xr(0), cus, s), "dispatch launch");
+  // (only where a full round 0 fills the chip with 256 x 256 tiles; a small
+  // layer's round 0 keeps the shape its counts choose)
+  const bool early = (int64_t)b.s.E * ((b.s.ce + 255) / 256) * ((b.s.f + 127) / 128) >= cus;
+  if (early && (st = run_ffn(b, 0, 1, w_gate, w_up, w_down, nullptr, 0, cus, s)) != MOE_OK)
+    return st;
   MOE_HIP(hipStreamWaitEvent(rb->side, rb->planned, 0), "hipStreamWaitEvent");
   MOE_HIP(hipMemcpyAsync(rb->host, b.pb.counts, (b.s.E + 1) * sizeof(int32_t),
                          hipMemcpyDeviceToHost, rb->side),
           "read of counts and R");
   MOE_HIP(hipEventRecord(rb->done, rb->side), "hipEventRecord");
-  MOE_HIP(moe::launch_dispatch(b.s, 0, 1, x, b.pb, b.xr(0), cus, s), "dispatch launch");
   // With two sets of round buffers the odd rounds run on the side stream
   // (set 1) and the even rounds on the caller's (set 0): consecutive rounds
   // use different buffers, so the dispatch of round r + 1 and the expert
@@ -871,8 +880,19 @@ moe_status_t moe_forward(const moe_config_t* cfg, const float* logits,
     return fail(MOE_ERR_HIP, "device plan reported an impossible round count");
   // The launch batches (one round each with two sets): the rest of each
   // batch's dispatch (rounds not queued before the wait), then one launch
-  // of each grouped GEMM over the batch's pairs.
+  // of each grouped GEMM over the batch's pairs not yet computed. If round
+  // 0's GEMMs ran above and the first batch holds later rounds as well,
+  // those are one launch over rounds 1 .. of that batch (its pairs after
+  // round 0's).
   const int queued = two ? 2 : 1;
+  int round0_pairs = 0;
+  {
+    int64_t rem[kMaxExperts];
+    int32_t rows0[kMaxExperts];
+    for (int e = 0; e < b.s.E; ++e) rem[e] = counts_r[e];
+    moe::host_next_round(b.s, rem, rows0);
+    for (int e = 0; e < b.s.E; ++e) round0_pairs += rows0[e] > 0;
+  }
   moe::BatchWalker walk(b.s, counts_r);
   moe::LaunchBatch lb;
   while (walk.next(&lb)) {
@@ -882,8 +902,11 @@ moe_status_t moe_forward(const moe_config_t* cfg, const float* logits,
       MOE_HIP(moe::launch_dispatch(b.s, d0, lb.r0 + lb.nr - d0, x, b.pb, b.xr(lb.r0),
                                    cus, sr),
               "dispatch launch");
-    if ((st = run_ffn(b, lb.r0, lb.nr, w_gate, w_up, w_down, lb.rows, lb.nv, cus, sr)) !=
-        MOE_OK)
+    const int skip = early && lb.r0 == 0 ? 1 : 0;  // round 0 is computed
+    if (lb.nr > skip &&
+        (st = run_ffn(b, lb.r0 + skip, lb.nr - skip, w_gate, w_up, w_down,
+                      lb.rows + (skip ? round0_pairs : 0), lb.nv - (skip ? round0_pairs : 0),
+                      cus, sr)) != MOE_OK)
       return st;
   }
   if (two) {  // the combine reads z rows of every round
