@@ -759,6 +759,30 @@ moe_status_t moe_backward(const moe_config_t* cfg, const void* x, const void* w_
           "router backward launch");
   float* ones = reinterpret_cast<float*>(w + L.ones);
   MOE_HIP(moe::launch_fill(ones, b.s.T * (int64_t)b.s.k, 1.0f, cus, s), "fill launch");
+  const int d = b.s.d, f = b.s.f;
+  const size_t set = (size_t)b.s.buf_rows() * 2;  // bytes per feature of a set
+  char* xr[2] = {w + L.xr, w + L.xr + set * d};
+  char* dyr[2] = {w + L.dyr, w + L.dyr + set * d};
+  char* hw[2] = {w + L.hw, w + L.hw + set * f};
+  char* dgu[2] = {w + L.dgu, w + L.dgu + set * 2 * f};
+  char *gu = w + L.gu, *dz = w + L.dz;
+  // Round 0's gathers and its recompute and dgrad GEMMs need nothing from
+  // the host (as in moe_forward, where a full round 0 fills the chip with
+  // 256 x 256 tiles): queued before the wait for the counts.
+  const bool early = (int64_t)b.s.E * ((b.s.ce + 255) / 256) * ((b.s.f + 127) / 128) >= cus;
+  auto round_work = [&](int rr, int q, const int32_t* prow, int nv) -> moe_status_t {
+    MOE_HIP(moe::launch_dispatch(b.s, rr, 1, x, b.pb, xr[q], cus, s), "dispatch launch");
+    MOE_HIP(moe::launch_dispatch(b.s, rr, 1, dy, b.pb, dyr[q], cus, s), "dispatch launch");
+    MOE_HIP(moe::launch_recompute(b.s, rr, xr[q], w_gate, w_up, b.pb, prow, nv, gu, hw[q],
+                                  cus, s),
+            "recompute launch");
+    MOE_HIP(moe::launch_dgate(b.s, rr, dyr[q], w_down, b.pb, prow, nv, gu, dgu[q], cus, s),
+            "dgate launch");
+    MOE_HIP(moe::launch_dx(b.s, rr, dgu[q], w_gate, w_up, b.pb, prow, nv, dz, cus, s),
+            "dx launch");
+    return MOE_OK;
+  };
+  if (early && (st = round_work(0, 0, nullptr, 0)) != MOE_OK) return st;
   MOE_HIP(hipEventSynchronize(rb->done), "wait for the plan");
   int32_t counts_r[kMaxExperts + 1];
   std::memcpy(counts_r, rb->host, (b.s.E + 1) * sizeof(int32_t));
@@ -770,13 +794,6 @@ moe_status_t moe_backward(const moe_config_t* cfg, const void* x, const void* w_
   for (int e = 0; e < b.s.E; ++e) rem[e] = counts_r[e];
   int32_t rows[2][kMaxExperts];
   int32_t prow[kMaxExperts];
-  const int d = b.s.d, f = b.s.f;
-  const size_t set = (size_t)b.s.buf_rows() * 2;  // bytes per feature of a set
-  char* xr[2] = {w + L.xr, w + L.xr + set * d};
-  char* dyr[2] = {w + L.dyr, w + L.dyr + set * d};
-  char* hw[2] = {w + L.hw, w + L.hw + set * f};
-  char* dgu[2] = {w + L.dgu, w + L.dgu + set * 2 * f};
-  char *gu = w + L.gu, *dz = w + L.dz;
   // rounds in pairs: each round's gathers, recompute and dgrad GEMMs into
   // its set, then one weight-gradient contraction over both rounds
   for (int r = 0; r < R; r += 2) {
@@ -784,17 +801,9 @@ moe_status_t moe_backward(const moe_config_t* cfg, const void* x, const void* w_
     for (int q = 0; q < nr; ++q) {
       const int rr = r + q;
       moe::host_next_round(b.s, rem, rows[q]);
+      if (early && rr == 0) continue;  // queued before the wait
       const int nv = moe::round_pairs(b.s.E, rows[q], prow);
-      MOE_HIP(moe::launch_dispatch(b.s, rr, 1, x, b.pb, xr[q], cus, s), "dispatch launch");
-      MOE_HIP(moe::launch_dispatch(b.s, rr, 1, dy, b.pb, dyr[q], cus, s), "dispatch launch");
-      MOE_HIP(moe::launch_recompute(b.s, rr, xr[q], w_gate, w_up, b.pb, prow, nv, gu,
-                                    hw[q], cus, s),
-              "recompute launch");
-      MOE_HIP(moe::launch_dgate(b.s, rr, dyr[q], w_down, b.pb, prow, nv, gu, dgu[q],
-                                cus, s),
-              "dgate launch");
-      MOE_HIP(moe::launch_dx(b.s, rr, dgu[q], w_gate, w_up, b.pb, prow, nv, dz, cus, s),
-              "dx launch");
+      if ((st = round_work(rr, q, prow, nv)) != MOE_OK) return st;
     }
     MOE_HIP(moe::launch_wgrad(b.s, r, nr, dyr[0], hw[0], dyr[1], hw[1], d, d, f, dw_down,
                               nullptr, b.pb, rows[0], rows[1], cus, s),
