@@ -436,8 +436,10 @@ def measure(w, args, steps, warmup, kernel_steps, with_cpu):
           file=sys.stderr, flush=True)
 
     # plan figures for the algorithmic bytes; the counts let the stage calls
-    # below make the launches moe_forward makes (one dispatch and one launch
-    # of each GEMM per launch batch of rounds, with the same launch shapes)
+    # below make the launches moe_forward makes (per launch batch of rounds
+    # one launch of each GEMM, with the same launch shapes; the gate/up launch
+    # gathers its rows from x, or, for an x of more than 2^30 bytes, a
+    # dispatch launch fills the round buffer first)
     R, counts = B.moe_plan(cfg, logits, ws, stream=stream, return_counts=True)
     batches = B.launch_batches(cfg, counts)
     views = B.workspace_views(cfg, ws)
@@ -445,6 +447,7 @@ def measure(w, args, steps, warmup, kernel_steps, with_cpu):
     A = np.bincount(round_of, minlength=R)[:R].astype(np.int64)
     es = 2 if w.dtype == "bf16" else 4
     TK = w.T * w.k
+    fused = w.T * w.d_model * es <= 1 << 30
     # per batch: its label (its rounds), assignments and distinct tokens
     labels = [f"{r0}" if n == 1 else f"{r0}-{r0 + n - 1}" for r0, n in batches]
     A_b = [int(A[r0:r0 + n].sum()) for r0, n in batches]
@@ -455,6 +458,9 @@ def measure(w, args, steps, warmup, kernel_steps, with_cpu):
     # spin kernel of about a millisecond goes first, so that the host has
     # queued the whole pass before the GPU reaches it: each event pair then
     # brackets its launch's execution and not the host's time to issue it.
+    # With the gathering gate/up the forward has no dispatch launch; the
+    # dispatch kernel (the backward's gather) is then timed after the
+    # combine, on its own.
     stages = ["plan"] + [f"{n}[{lb}]" for lb in labels
                          for n in ("dispatch", "gate_up", "down")] + ["combine"]
     tot = {n: 0.0 for n in stages}
@@ -473,13 +479,21 @@ def measure(w, args, steps, warmup, kernel_steps, with_cpu):
         timed("plan", lambda: B.moe_plan(cfg, logits, ws, read_rounds=False,
                                          stream=stream))
         for lb, (r0, n) in zip(labels, batches):
-            timed(f"dispatch[{lb}]",
-                  lambda r0=r0, n=n: B.moe_dispatch(cfg, r0, x, ws, stream, n_rounds=n))
-            timed(f"gate_up[{lb}]", lambda r0=r0, n=n: B.moe_expert_gate_up(
-                cfg, r0, wg, wu, ws, stream, counts_host=counts, n_rounds=n))
+            if fused:
+                timed(f"gate_up[{lb}]", lambda r0=r0, n=n: B.moe_dispatch_gate_up(
+                    cfg, r0, x, wg, wu, ws, stream, counts_host=counts, n_rounds=n))
+            else:
+                timed(f"dispatch[{lb}]", lambda r0=r0, n=n: B.moe_dispatch(
+                    cfg, r0, x, ws, stream, n_rounds=n))
+                timed(f"gate_up[{lb}]", lambda r0=r0, n=n: B.moe_expert_gate_up(
+                    cfg, r0, wg, wu, ws, stream, counts_host=counts, n_rounds=n))
             timed(f"down[{lb}]", lambda r0=r0, n=n: B.moe_expert_down(
                 cfg, r0, wd, ws, stream, counts_host=counts, n_rounds=n))
         timed("combine", lambda: B.moe_combine(cfg, ws, y, stream))
+        if fused:
+            for lb, (r0, n) in zip(labels, batches):
+                timed(f"dispatch[{lb}]", lambda r0=r0, n=n: B.moe_dispatch(
+                    cfg, r0, x, ws, stream, n_rounds=n))
         torch.cuda.synchronize()
         if it >= 2:  # two untimed passes
             for n, (e0, e1) in ev.items():
@@ -501,6 +515,8 @@ def measure(w, args, steps, warmup, kernel_steps, with_cpu):
         per_launch[f"dispatch[{lb}]"] = {
             "us": t_d * 1e6, "rows": A_b[i], "GB/s": disp_bytes[i] / t_d / 1e9,
             "algorithmic_bytes": disp_bytes[i]}
+        if fused:
+            per_launch[f"dispatch[{lb}]"]["in_forward"] = False
         per_launch[f"gate_up[{lb}]"] = {
             "us": t_g * 1e6, "rows": A_b[i],
             "TFLOP/s": 4.0 * A_b[i] * df / t_g / 1e12}
@@ -536,7 +552,9 @@ def measure(w, args, steps, warmup, kernel_steps, with_cpu):
     t_g0 = sec[f"gate_up[{labels[0]}]"]
     achieved = flops_g0 / t_g0 / 1e12
     roofline = {"bound": "mfma",
-                "kernel": f"grouped gate/up GEMM + SwiGLU, rounds {labels[0]}",
+                "kernel": ("grouped gate/up GEMM + SwiGLU" +
+                           (" gathering its rows from x" if fused else "") +
+                           f", rounds {labels[0]}"),
                 "achieved": achieved, "peak": peak_tf, "unit": "TFLOP/s",
                 "frac": achieved / peak_tf, "traffic": measured_traffic(w, args),
                 "flops_per_launch": flops_g0, "avg_launch_us": t_g0 * 1e6}
@@ -545,8 +563,8 @@ def measure(w, args, steps, warmup, kernel_steps, with_cpu):
     # the layer's attainable time with no overlap: per launch batch the larger
     # of its GEMM FLOPs at the bf16 peak and the bytes it must stream at
     # 8 TB/s (the three weight matrices of each expert with rows in the
-    # batch, the batch's rows in and out), plus dispatch and combine bytes
-    # at 8 TB/s
+    # batch, the batch's rows in and out), plus the combine's bytes (and a
+    # dispatch launch's, where the forward has one) at 8 TB/s
     views_r = views["rounds"].cpu().numpy()
     hbm = 8.0e12
     bound_s = 0.0
@@ -555,7 +573,7 @@ def measure(w, args, steps, warmup, kernel_steps, with_cpu):
         f_b = 6.0 * A_b[i] * df
         b_b = (active * 3.0 * df * es + A_b[i] * (2 * w.d_model + 2 * w.d_ff) * es)
         bound_s += max(f_b / (peak_tf * 1e12), b_b / hbm)
-    bound_s += (sum(disp_bytes) + comb_bytes) / hbm
+    bound_s += ((0.0 if fused else sum(disp_bytes)) + comb_bytes) / hbm
     layer_bound = {"us": bound_s * 1e6, "tokens_per_s": w.T / bound_s,
                    "frac": tokens_per_s * bound_s / w.T}
 
@@ -578,6 +596,10 @@ def measure(w, args, steps, warmup, kernel_steps, with_cpu):
         "grouped_gemm_mfma_util_pct": 100.0 * gemm_util,
         "dispatch_GBps": sum(disp_bytes) / t_disp / 1e9,
         "dispatch_round0_GBps": kernels[f"dispatch[{labels[0]}]"]["GB/s"],
+        "forward_dispatch": ("fused: the gate/up launch gathers the rows from x "
+                             "(moe_dispatch_gate_up); dispatch_GBps is the "
+                             "dispatch kernel on its own (the backward's gather)"
+                             if fused else "dispatch launch per batch"),
         "combine_GBps": kernels["combine"]["GB/s"],
         "device_copy_GBps": copy_gbps,
         "workspace_bytes": ws_bytes, "peak_allocated_bytes": peak_bytes,

@@ -326,6 +326,25 @@ moe_status_t moe_expert_down(const moe_config_t *cfg, int32_t round,
                              const int32_t *counts_host, void *ws,
                              size_t ws_bytes, void *stream);
 
+/* Dispatch and gate/up of rounds round .. round + n_rounds - 1 in one
+ * grouped GEMM launch: h exactly as moe_dispatch followed by
+ * moe_expert_gate_up computes it (bit for bit), but each slot's token row is
+ * read from x (row-major [T][d]) through the plan's permutation while the
+ * GEMM fetches its operands, so the round buffer xr is neither written nor
+ * read. This is the dispatch step of the rounds ("Frontier Pre-training at
+ * Microsoft AI (MAI-Base-2)", section "Key claims": dispatch, compute,
+ * collect) on one GPU, where the dispatch moves rows within one device
+ * memory and a separate copy into xr would only add a write and a read of
+ * every assignment's row; moe_forward takes this path. x must hold at most
+ * 2^30 bytes (T * d * sizeof(elem)), else MOE_ERR_UNSUPPORTED (use
+ * moe_dispatch and moe_expert_gate_up). Other arguments, checks and
+ * asynchrony as moe_expert_gate_up. */
+moe_status_t moe_dispatch_gate_up(const moe_config_t *cfg, int32_t round,
+                                  int32_t n_rounds, const void *x,
+                                  const void *w_gate, const void *w_up,
+                                  const int32_t *counts_host, void *ws,
+                                  size_t ws_bytes, void *stream);
+
 /* Repack expert weights from the row-major layout into the tiled layout
  * (MOE_WEIGHTS_TILED): gate and up are [E][f][d], down is [E][d][f]; each
  * output array has the size of its input. cfg->weight_layout is ignored.
@@ -347,12 +366,16 @@ moe_status_t moe_combine(const moe_config_t *cfg, const void *ws,
                          size_t ws_bytes, void *y, void *stream);
 
 /* The whole layer: plan, one wait to learn the counts and R, then the R
- * rounds of dispatch and expert compute, one dispatch and one launch of
- * each grouped GEMM per launch batch (see "Launch batches"; launch shapes
- * fitted to each batch as with counts_host above), then the collect and
- * weighted combine. y is written in full.
+ * rounds of dispatch and expert compute, one launch of each grouped GEMM
+ * per launch batch (see "Launch batches"; launch shapes fitted to each
+ * batch as with counts_host above), then the collect and weighted combine.
+ * y is written in full. The dispatch is the gate/up launch's own fetch of
+ * the token rows from x (as moe_dispatch_gate_up) when x holds at most 2^30
+ * bytes, else one moe_dispatch launch per batch before its GEMMs; the
+ * results are the same bits either way.
  * Returns after enqueueing the combine (the plan's wait is the only host
- * synchronisation; round 0's dispatch is queued before it). For that read
+ * synchronisation; round 0's dispatch, and its GEMMs where a full round 0
+ * fills the GPU, are queued before it). For that read
  * the call takes from a pool of the current device a set of a pinned host
  * buffer of 65 int32, a side stream of default priority that does the copy
  * and three events, and returns it when it returns: sets are created when
@@ -361,8 +384,8 @@ moe_status_t moe_combine(const moe_config_t *cfg, const void *ws,
  * process ends. With S = 2 the rounds overlap as the method
  * overlaps dispatch with compute ("Frontier Pre-training at Microsoft AI
  * (MAI-Base-2)", section "Key claims"): odd rounds run on the side stream with buffer set 1, even rounds
- * on the caller's stream with set 0 (round 1's dispatch is also queued
- * before the wait), and the caller's stream waits for the side stream
+ * on the caller's stream with set 0 (round 1's dispatch, where it is a
+ * launch of its own, is also queued before the wait), and the caller's stream waits for the side stream
  * before the combine, so the caller still sees one stream's order. The
  * result does not depend on C, G or S. */
 moe_status_t moe_forward(const moe_config_t *cfg, const float *logits,

@@ -33,7 +33,7 @@ EXPORTS = ("moe_status_string", "moe_last_error", "moe_hip_runtime_version",
            "moe_check_config", "moe_workspace_size", "moe_workspace_layout",
            "moe_plan", "moe_launch_batches", "moe_dispatch", "moe_expert_ffn",
            "moe_expert_gate_up",
-           "moe_expert_down", "moe_pack_weights", "moe_combine", "moe_forward",
+           "moe_expert_down", "moe_dispatch_gate_up", "moe_pack_weights", "moe_combine", "moe_forward",
            "moe_capacity_curve", "moe_capacity_for_rounds",
            "moe_backward_workspace_size", "moe_backward_layout",
            "moe_backward", "moe_forward_static")
@@ -103,6 +103,7 @@ def load() -> ctypes.CDLL:
     L.moe_expert_ffn.argtypes = [cfgp, i32, i32, vp, vp, vp, i32p, vp, sz, vp]
     L.moe_expert_gate_up.argtypes = [cfgp, i32, i32, vp, vp, i32p, vp, sz, vp]
     L.moe_expert_down.argtypes = [cfgp, i32, i32, vp, i32p, vp, sz, vp]
+    L.moe_dispatch_gate_up.argtypes = [cfgp, i32, i32, vp, vp, vp, i32p, vp, sz, vp]
     L.moe_pack_weights.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp]
     L.moe_combine.argtypes = [cfgp, vp, sz, vp, vp]
     L.moe_forward.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -118,7 +119,8 @@ def load() -> ctypes.CDLL:
                                vp, sz, vp, sz, vp]
     for n in ("moe_check_config", "moe_workspace_size", "moe_workspace_layout",
               "moe_plan", "moe_launch_batches", "moe_dispatch", "moe_expert_ffn",
-              "moe_expert_gate_up", "moe_expert_down", "moe_pack_weights",
+              "moe_expert_gate_up", "moe_expert_down", "moe_dispatch_gate_up",
+              "moe_pack_weights",
               "moe_combine", "moe_forward", "moe_capacity_curve",
               "moe_capacity_for_rounds", "moe_backward_workspace_size",
               "moe_backward_layout", "moe_backward",
@@ -301,6 +303,17 @@ def moe_expert_gate_up(cfg, round_, w_gate, w_up, ws, stream=None,
                                      _arg(w_gate, "w_gate", _el(cfg), nw),
                                      _arg(w_up, "w_up", _el(cfg), nw), c and c[0],
                                      _arg(ws, "ws"), _nbytes(ws), _stream(stream)))
+
+
+def moe_dispatch_gate_up(cfg, round_, x, w_gate, w_up, ws, stream=None,
+                         counts_host=None, n_rounds=1):
+    c = _counts(counts_host)
+    nw = cfg.E * cfg.d_model * cfg.d_ff
+    _check(load().moe_dispatch_gate_up(ctypes.byref(cfg), int(round_), int(n_rounds),
+                                       _arg(x, "x", _el(cfg), cfg.T * cfg.d_model),
+                                       _arg(w_gate, "w_gate", _el(cfg), nw),
+                                       _arg(w_up, "w_up", _el(cfg), nw), c and c[0],
+                                       _arg(ws, "ws"), _nbytes(ws), _stream(stream)))
 
 
 def moe_expert_down(cfg, round_, w_down, ws, stream=None, counts_host=None,

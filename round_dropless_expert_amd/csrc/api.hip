@@ -318,9 +318,9 @@ moe_status_t read_plan(const Bound& b, int32_t* out, hipStream_t st) {
 // buffer set is round r0's), with the rows of its nv pairs on the host.
 moe_status_t run_ffn(const Bound& b, int r0, int nr, const void* wg, const void* wu,
                      const void* wd, const int32_t* pair_rows, int nv, int cus,
-                     hipStream_t st) {
+                     hipStream_t st, const void* x = nullptr) {
   MOE_HIP(moe::launch_gate_up(b.s, r0, nr, b.xr(r0), wg, wu, b.pb, pair_rows, nv,
-                              b.h(r0), cus, st),
+                              b.h(r0), cus, st, x),
           "gate/up launch");
   MOE_HIP(moe::launch_down(b.s, r0, nr, b.h(r0), wd, b.pb, pair_rows, nv,
                            b.ws + b.L.z, cus, st),
@@ -468,7 +468,7 @@ enum StageGemm { kStageBoth = 0, kStageGateUp = 1, kStageDown = 2 };
 moe_status_t stage_gemm(const moe_config_t* cfg, int32_t round, int32_t n_rounds,
                         const void* w_gate, const void* w_up, const void* w_down,
                         const int32_t* counts_host, void* ws, size_t ws_bytes,
-                        void* stream, StageGemm which) {
+                        void* stream, StageGemm which, const void* x = nullptr) {
   Bound b;
   moe_status_t st = bind(cfg, ws, ws_bytes, &b);
   if (st != MOE_OK) return st;
@@ -488,7 +488,7 @@ moe_status_t stage_gemm(const moe_config_t* cfg, int32_t round, int32_t n_rounds
   hipStream_t hs = static_cast<hipStream_t>(stream);
   if (which != kStageDown)
     MOE_HIP(moe::launch_gate_up(b.s, round, n_rounds, b.xr(round), w_gate, w_up, b.pb, pr,
-                                nv, b.h(round), cus, hs),
+                                nv, b.h(round), cus, hs, x),
             "gate/up launch");
   if (which != kStageGateUp)
     MOE_HIP(moe::launch_down(b.s, round, n_rounds, b.h(round), w_down, b.pb, pr, nv,
@@ -672,6 +672,21 @@ moe_status_t moe_expert_down(const moe_config_t* cfg, int32_t round, int32_t n_r
                              void* ws, size_t ws_bytes, void* stream) {
   return stage_gemm(cfg, round, n_rounds, nullptr, nullptr, w_down, counts_host, ws,
                     ws_bytes, stream, kStageDown);
+}
+
+moe_status_t moe_dispatch_gate_up(const moe_config_t* cfg, int32_t round,
+                                  int32_t n_rounds, const void* x, const void* w_gate,
+                                  const void* w_up, const int32_t* counts_host,
+                                  void* ws, size_t ws_bytes, void* stream) {
+  moe_status_t st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if ((st = check_ptr(x, "x")) != MOE_OK) return st;
+  if (!moe::gather_fits(shape_of(cfg)))
+    return fail(MOE_ERR_UNSUPPORTED,
+                "x holds more than 2^30 bytes: dispatch with moe_dispatch and run "
+                "moe_expert_gate_up");
+  return stage_gemm(cfg, round, n_rounds, w_gate, w_up, nullptr, counts_host, ws,
+                    ws_bytes, stream, kStageGateUp, x);
 }
 
 moe_status_t moe_pack_weights(const moe_config_t* cfg, const void* w_gate,
@@ -859,11 +874,17 @@ moe_status_t moe_forward(const moe_config_t* cfg, const float* logits,
   PlanReadback* rb = nullptr;
   if ((st = lease.acquire(&rb)) != MOE_OK) return st;
   MOE_HIP(hipEventRecord(rb->planned, s), "hipEventRecord");
-  MOE_HIP(moe::launch_dispatch(b.s, 0, 1, x, b.pb, b.xr(0), cus, s), "dispatch launch");
+  // The gate/up GEMM gathers each slot's token row from x through the plan
+  // (where x has at most 2^30 bytes), so no round is dispatched into xr;
+  // otherwise each launch batch's dispatch comes first.
+  const void* gx = moe::gather_fits(b.s) ? x : nullptr;
+  if (!gx)
+    MOE_HIP(moe::launch_dispatch(b.s, 0, 1, x, b.pb, b.xr(0), cus, s), "dispatch launch");
   // (only where a full round 0 fills the chip with 256 x 256 tiles; a small
   // layer's round 0 keeps the shape its counts choose)
   const bool early = (int64_t)b.s.E * ((b.s.ce + 255) / 256) * ((b.s.f + 127) / 128) >= cus;
-  if (early && (st = run_ffn(b, 0, 1, w_gate, w_up, w_down, nullptr, 0, cus, s)) != MOE_OK)
+  if (early &&
+      (st = run_ffn(b, 0, 1, w_gate, w_up, w_down, nullptr, 0, cus, s, gx)) != MOE_OK)
     return st;
   MOE_HIP(hipStreamWaitEvent(rb->side, rb->planned, 0), "hipStreamWaitEvent");
   MOE_HIP(hipMemcpyAsync(rb->host, b.pb.counts, (b.s.E + 1) * sizeof(int32_t),
@@ -878,7 +899,7 @@ moe_status_t moe_forward(const moe_config_t* cfg, const float* logits,
   // it finds no assignment of round 1 and moves nothing.
   const int64_t max_rounds = (b.s.T + b.s.ce - 1) / b.s.ce;
   const bool two = b.sets == 2 && max_rounds >= 2;
-  if (two)
+  if (two && !gx)
     MOE_HIP(moe::launch_dispatch(b.s, 1, 1, x, b.pb, b.xr(1), cus, rb->side),
             "dispatch launch");
   MOE_HIP(hipEventSynchronize(rb->done), "wait for the plan");
@@ -907,7 +928,7 @@ moe_status_t moe_forward(const moe_config_t* cfg, const float* logits,
   while (walk.next(&lb)) {
     hipStream_t sr = two && (lb.r0 & 1) ? rb->side : s;
     const int d0 = lb.r0 < queued ? queued : lb.r0;
-    if (lb.r0 + lb.nr > d0)
+    if (!gx && lb.r0 + lb.nr > d0)
       MOE_HIP(moe::launch_dispatch(b.s, d0, lb.r0 + lb.nr - d0, x, b.pb, b.xr(lb.r0),
                                    cus, sr),
               "dispatch launch");
@@ -915,7 +936,7 @@ moe_status_t moe_forward(const moe_config_t* cfg, const float* logits,
     if (lb.nr > skip &&
         (st = run_ffn(b, lb.r0 + skip, lb.nr - skip, w_gate, w_up, w_down,
                       lb.rows + (skip ? round0_pairs : 0), lb.nv - (skip ? round0_pairs : 0),
-                      cus, sr)) != MOE_OK)
+                      cus, sr, gx)) != MOE_OK)
       return st;
   }
   if (two) {  // the combine reads z rows of every round
@@ -956,7 +977,10 @@ moe_status_t moe_forward_static(const moe_config_t* cfg, const float* logits,
   // entry it later reads, and the rows of a round buffer past an expert's
   // rows only feed outputs that are never stored.
   if ((st = run_plan(b, logits, s)) != MOE_OK) return st;
-  MOE_HIP(moe::launch_dispatch(b.s, 0, 1, x, b.pb, b.xr(0), cus, s), "dispatch launch");
+  // gate/up gathers from x as in moe_forward, else round 0 is dispatched
+  const void* gx = moe::gather_fits(b.s) ? x : nullptr;
+  if (!gx)
+    MOE_HIP(moe::launch_dispatch(b.s, 0, 1, x, b.pb, b.xr(0), cus, s), "dispatch launch");
   // counts and R into host memory of this frame, then one wait
   int32_t counts_r[kMaxExperts + 1];
   MOE_HIP(hipMemcpyAsync(counts_r, b.pb.counts, (b.s.E + 1) * sizeof(int32_t),
@@ -973,12 +997,12 @@ moe_status_t moe_forward_static(const moe_config_t* cfg, const float* logits,
   moe::LaunchBatch lb;
   while (walk.next(&lb)) {
     const int d0 = lb.r0 < 1 ? 1 : lb.r0;
-    if (lb.r0 + lb.nr > d0)
+    if (!gx && lb.r0 + lb.nr > d0)
       MOE_HIP(moe::launch_dispatch(b.s, d0, lb.r0 + lb.nr - d0, x, b.pb, b.xr(lb.r0),
                                    cus, s),
               "dispatch launch");
-    if ((st = run_ffn(b, lb.r0, lb.nr, w_gate, w_up, w_down, lb.rows, lb.nv, cus, s)) !=
-        MOE_OK)
+    if ((st = run_ffn(b, lb.r0, lb.nr, w_gate, w_up, w_down, lb.rows, lb.nv, cus, s,
+                      gx)) != MOE_OK)
       return st;
   }
   MOE_HIP(moe::launch_combine(b.s, b.ws + b.L.z, b.pb.weight, b.pb.pos, y, cus, s),

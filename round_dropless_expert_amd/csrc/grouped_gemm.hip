@@ -83,7 +83,9 @@ struct MmaOp<float> {
 };
 
 // What a launch computes (the operand passes and the epilogue):
-//   kModeGateUp    forward: h = silu(xr Wg^T) * (xr Wu^T) into h
+//   kModeGateUp    forward: h = silu(xr Wg^T) * (xr Wu^T) into h; with
+//                  kGather the token rows are read from x through the plan
+//                  instead of from a dispatched round buffer xr (below)
 //   kModeDown      forward: o = h Wd^T into z rows
 //   kModeRecompute backward: g = xr Wg^T and u = xr Wu^T into gu
 //                  ([rows][2f]: g, then u) and w * silu(g) u into hw
@@ -105,6 +107,9 @@ enum GemmMode {
 template <typename Elem>
 struct GemmParams {
   const Elem* act;   // round buffer [rows][K]: xr (gate/up) or h (down)
+  const Elem* x;     // gathering gate/up: the layer's input x [T][K]
+  int x_bytes;       // its bytes (at most 2^30)
+  int topk;          // k: assignment a is token a / k's
   const Elem* w0;    // [E][N][K]: gate (gate/up) or down weights; dgate:
                      // down weights [E][K][N]; dx: gate weights [E][K/2][N]
   const Elem* w1;    // [E][N][K]: up weights (gate/up); dx: up [E][K/2][N]
@@ -255,11 +260,19 @@ struct TileSrc {
   __amdgpu_buffer_rsrc_t rw0, rw1, ra;
   uint32_t wbase[kWPasses];  // weight pass offsets
   uint32_t tbase[kTPasses];  // token pass offsets (past the rows: out of range)
+  uint32_t vt[kTPasses];     // gathering: this lane's token row offset in x
+                             // for each token pass (per lane, not uniform)
 };
 
-template <typename Elem, int WI, int WJ, int SPB, int kMode>
+// Offset of a gathered token row past the pair's m rows: beyond any x (at
+// most 2^30 bytes), and still below 2^32 with a stage offset added, even the
+// out-of-range one of a stage past the end of K.
+constexpr uint32_t kDeadRow = 0x40000000u;
+
+template <typename Elem, int WI, int WJ, int SPB, int kMode, bool kGather>
 __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
     GemmParams<Elem> p) {
+  static_assert(!kGather || kMode == kModeGateUp, "gathering: forward gate/up only");
   // two weight matrices per tile (gate rows, then up rows of the same
   // features)
   constexpr bool kGateUp = kMode == kModeGateUp || kMode == kModeRecompute;
@@ -334,7 +347,8 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
   const int lane_incl = wave_inclusive_scan(((lane_m + BM - 1) / BM) * nt);
   const int total = __builtin_amdgcn_readlane(lane_incl, kWave - 1);
   const int lane_row = lv ? p.rounds[kPairRow * tbl + gi] : 0;
-  const int lane_off = kMode != kModeGateUp && lv ? p.rounds[kPairZ * tbl + gi] : 0;
+  const int lane_off =
+      (kMode != kModeGateUp || kGather) && lv ? p.rounds[kPairZ * tbl + gi] : 0;
 
   // XCD-contiguous walk: workgroup b runs on XCD b % 8.
   const int G = gridDim.x;
@@ -410,9 +424,13 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
         (void*)(kGateUp || kMode == kModeDx ? p.w1 + ex * wmat : p.w0), 0, (int)wb,
         kRsrcWord3);
     // pair te's matrix: its m rows padded to 64, from its first row
-    S.ra = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(p.act + (int64_t)__builtin_amdgcn_readlane(lane_row, te) * p.K), 0,
-        exists ? (int)((uint32_t)((tm + 63) & ~63) * kbytes) : 0, kRsrcWord3);
+    // (gathering: all of x; each lane's row offsets select the rows)
+    if constexpr (kGather)
+      S.ra = __builtin_amdgcn_make_buffer_rsrc((void*)p.x, 0, p.x_bytes, kRsrcWord3);
+    else
+      S.ra = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(p.act + (int64_t)__builtin_amdgcn_readlane(lane_row, te) * p.K), 0,
+          exists ? (int)((uint32_t)((tm + 63) & ~63) * kbytes) : 0, kRsrcWord3);
 #pragma unroll
     for (int i = 0; i < kWPasses; ++i) {
       int feat0 = tn0 + 64 * i;
@@ -427,8 +445,31 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
     }
 #pragma unroll
     for (int j = 0; j < kTPasses; ++j)
-      S.tbase[j] = (uint32_t)(tm0 / 64 + j) * band_bytes;
+      S.tbase[j] = kGather ? 0u : (uint32_t)(tm0 / 64 + j) * band_bytes;
     return S;
+  };
+  // Gathering: token pass j of a tile holds the pair's rows tm0 + 64 j ..
+  // + 63, and this lane fetches row tm0 + 64 j + r0 of them, logical chunk
+  // `chunk` of each stage (as a row-major weight band), from x. Row c of
+  // pair te is the assignment perm[z0 + c] (z0: the pair's first entry in
+  // expert order), i.e. token perm[z0 + c] / k. perm_rows loads those
+  // assignments (-1: past the pair's rows, or no tile); token_offs turns
+  // them into the lane's byte offsets in x. The loads are the compiler's
+  // own (it waits for them where token_offs uses them): they are issued a
+  // whole tile before that use, so they have landed by then.
+  auto perm_rows = [&](int te, int tm, int tm0, bool exists, int32_t (&pa)[kTPasses]) {
+    const int64_t z0 = exists ? __builtin_amdgcn_readlane(lane_off, te) : 0;
+#pragma unroll
+    for (int j = 0; j < kTPasses; ++j) {
+      const int row = tm0 + 64 * j + r0;
+      pa[j] = exists && row < tm ? p.perm[z0 + row] : -1;
+    }
+  };
+  auto token_offs = [&](const int32_t (&pa)[kTPasses], src_t& S) {
+#pragma unroll
+    for (int j = 0; j < kTPasses; ++j)
+      S.vt[j] = pa[j] < 0 ? kDeadRow
+                          : (uint32_t)(pa[j] / p.topk) * kbytes + (uint32_t)chunk * 16;
   };
 
   const int KT = p.K / kStageK;            // 64-byte K stages
@@ -468,7 +509,8 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
         o.up[sub] = false;
         o.w[sub] = in ? (uint32_t)g * wstride : kOutOfRange;
       }
-      o.t[sub] = in ? (uint32_t)g * (uint32_t)kTileBytes : kOutOfRange;
+      o.t[sub] = in ? (uint32_t)g * (uint32_t)(kGather ? kRowBytes : kTileBytes)
+                    : kOutOfRange;
     }
     return o;
   };
@@ -480,7 +522,7 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
     const uint32_t soff = w ? S.wbase[i] + o.w[sub] : S.tbase[i - kWPasses] + o.t[sub];
     const uint32_t lds = (uint32_t)(uintptr_t)(lds_char*)slot_mem +
                          sub * kStageBytes + i * 4096 + lds_wave;
-    lds_load16(rs, w ? vo_w : vo_t, soff, lds);
+    lds_load16(rs, w ? vo_w : kGather ? S.vt[i - kWPasses] : vo_t, soff, lds);
   };
   // fragment rows of this lane: weight block ib, token block 0
   auto wrow_of = [&](int ib) {
@@ -529,6 +571,17 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
   // wait for the first
   locate(tile, e, m, n0, m0);
   src_t cur = sources(e, m, n0, m0, true);
+  // gathering: pa holds the assignments of the tile after the one being
+  // computed, loaded one tile ahead of their use
+  int32_t pa[kTPasses];
+  if constexpr (kGather) {
+    perm_rows(e, m, m0, true, pa);
+    token_offs(pa, cur);
+    const int t1 = tile + (int)gridDim.x;
+    int e1 = 0, m1 = 0, n01 = 0, m01 = 0;
+    if (t1 < total) locate(t1, e1, m1, n01, m01);
+    perm_rows(e1, m1, m01, t1 < total, pa);
+  }
   {
     const StageOff o0 = stage_off(0), o1 = stage_off(1), o2 = stage_off(2);
 #pragma unroll
@@ -551,7 +604,14 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
     const bool has_next = tile_n < total;
     int e_n = 0, m_n = 0, n0_n = 0, m0_n = 0;
     if (has_next) locate(tile_n, e_n, m_n, n0_n, m0_n);
-    const src_t nxt = sources(e_n, m_n, n0_n, m0_n, has_next);
+    src_t nxt = sources(e_n, m_n, n0_n, m0_n, has_next);
+    if constexpr (kGather) {
+      token_offs(pa, nxt);
+      const int tile_nn = tile_n + G;
+      int e2 = 0, m2 = 0, n02 = 0, m02 = 0;
+      if (tile_nn < total) locate(tile_nn, e2, m2, n02, m02);
+      perm_rows(e2, m2, m02, tile_nn < total, pa);
+    }
 
 #pragma unroll
     for (int ib = 0; ib < WI; ++ib)
@@ -945,11 +1005,11 @@ static int grid_for(int64_t tiles, int num_cus) {
   return (int)(g < 8 ? 8 : g);
 }
 
-template <typename Elem, typename Cfg, int kMode>
+template <typename Elem, typename Cfg, int kMode, bool kGather>
 static hipError_t launch_gemm_cfg(const GemmParams<Elem>& p, int grid,
                                   hipStream_t st) {
   hipLaunchKernelGGL(
-      (grouped_ffn_gemm_kernel<Elem, Cfg::WI, Cfg::WJ, Cfg::SPB, kMode>),
+      (grouped_ffn_gemm_kernel<Elem, Cfg::WI, Cfg::WJ, Cfg::SPB, kMode, kGather>),
       dim3(grid), dim3(256), 0, st, p);
   return hipGetLastError();
 }
@@ -959,7 +1019,7 @@ static hipError_t launch_gemm_cfg(const GemmParams<Elem>& p, int grid,
 // without them the large tile and one workgroup per CU are used. Every shape
 // runs the same MFMA sequence over K for every output, so results are
 // identical. p.N is the number of output features.
-template <typename Elem, int kMode>
+template <typename Elem, int kMode, bool kGather = false>
 static hipError_t launch_gemm(const Shape& s, const GemmParams<Elem>& p,
                               const int32_t* rows_host, int nv, int num_cus,
                               hipStream_t st) {
@@ -977,12 +1037,13 @@ static hipError_t launch_gemm(const Shape& s, const GemmParams<Elem>& p,
     const float cm = est_cost<TileMedium>(tm, num_cus);
     const float cs = est_cost<TileSmall>(ts, num_cus);
     if (cb <= cm && cb <= cs)
-      return launch_gemm_cfg<Elem, TileBig, kMode>(p, grid_for(tb, num_cus), st);
+      return launch_gemm_cfg<Elem, TileBig, kMode, kGather>(p, grid_for(tb, num_cus), st);
     if (cm <= cs)
-      return launch_gemm_cfg<Elem, TileMedium, kMode>(p, grid_for(tm, num_cus), st);
-    return launch_gemm_cfg<Elem, TileSmall, kMode>(p, grid_for(ts, num_cus), st);
+      return launch_gemm_cfg<Elem, TileMedium, kMode, kGather>(p, grid_for(tm, num_cus),
+                                                               st);
+    return launch_gemm_cfg<Elem, TileSmall, kMode, kGather>(p, grid_for(ts, num_cus), st);
   }
-  return launch_gemm_cfg<Elem, TileBig, kMode>(p, grid_for(num_cus, num_cus), st);
+  return launch_gemm_cfg<Elem, TileBig, kMode, kGather>(p, grid_for(num_cus, num_cus), st);
 }
 
 // Parameters of a launch over round r: activations act [rows][K], weights
@@ -1010,17 +1071,30 @@ static GemmParams<Elem> params(const Shape& s, int r0, int nr, const void* act,
   return p;
 }
 
+bool gather_fits(const Shape& s) {
+  return s.T * s.d * (s.bf16 ? 2 : 4) <= ((int64_t)1 << 30);
+}
+
+template <typename Elem>
+static hipError_t gate_up(const Shape& s, int r0, int nr, const void* xr,
+                          const void* x, const void* wg, const void* wu,
+                          const PlanBuffers& b, const int32_t* rows_host, int nv,
+                          void* h, int num_cus, hipStream_t st) {
+  GemmParams<Elem> p = params<Elem>(s, r0, nr, xr, wg, wu, h, b, s.d, s.f, s.tiled_w);
+  if (!x) return launch_gemm<Elem, kModeGateUp>(s, p, rows_host, nv, num_cus, st);
+  if (!gather_fits(s)) return hipErrorInvalidValue;
+  p.x = static_cast<const Elem*>(x);
+  p.x_bytes = (int)(s.T * s.d * (int64_t)sizeof(Elem));
+  p.topk = s.k;
+  return launch_gemm<Elem, kModeGateUp, true>(s, p, rows_host, nv, num_cus, st);
+}
+
 hipError_t launch_gate_up(const Shape& s, int r0, int nr, const void* xr,
                           const void* wg, const void* wu, const PlanBuffers& b,
                           const int32_t* rows_host, int nv, void* h, int num_cus,
-                          hipStream_t st) {
-  if (s.bf16)
-    return launch_gemm<bf16, kModeGateUp>(
-        s, params<bf16>(s, r0, nr, xr, wg, wu, h, b, s.d, s.f, s.tiled_w), rows_host,
-        nv, num_cus, st);
-  return launch_gemm<float, kModeGateUp>(
-      s, params<float>(s, r0, nr, xr, wg, wu, h, b, s.d, s.f, s.tiled_w), rows_host,
-      nv, num_cus, st);
+                          hipStream_t st, const void* x) {
+  if (s.bf16) return gate_up<bf16>(s, r0, nr, xr, x, wg, wu, b, rows_host, nv, h, num_cus, st);
+  return gate_up<float>(s, r0, nr, xr, x, wg, wu, b, rows_host, nv, h, num_cus, st);
 }
 
 hipError_t launch_down(const Shape& s, int r0, int nr, const void* h, const void* wd,

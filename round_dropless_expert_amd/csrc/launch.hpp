@@ -108,11 +108,15 @@ hipError_t launch_dispatch(const Shape& s, int r0, int nr, const void* x,
 // launch's pairs on the host (nv of them, in pair order), or NULL. With
 // them the launch gets the tile shape and grid that fit it (results are
 // identical either way); without them the large tile and one workgroup per
-// CU are used.
+// CU are used. x: NULL, or the layer's input, from which the launch then
+// gathers each pair's token rows through the plan (the dispatch fused into
+// the GEMM's operand fetch; xr is not read); only where gather_fits(s).
 hipError_t launch_gate_up(const Shape& s, int r0, int nr, const void* xr,
                           const void* wg, const void* wu, const PlanBuffers& b,
                           const int32_t* rows_host, int nv, void* h, int num_cus,
-                          hipStream_t st);
+                          hipStream_t st, const void* x = nullptr);
+// x small enough for the gathering gate/up (at most 2^30 bytes)
+bool gather_fits(const Shape& s);
 hipError_t launch_down(const Shape& s, int r0, int nr, const void* h, const void* wd,
                        const PlanBuffers& b, const int32_t* rows_host, int nv,
                        void* z, int num_cus, hipStream_t st);

@@ -178,6 +178,19 @@ def test_pointer_and_workspace_checks_before_any_hip_call(B):
         B.MOE_ERR_INVALID_ARGUMENT
     assert L.moe_expert_down(c, -1, 1, p, None, p, need, None) == \
         B.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_dispatch_gate_up(c, 0, 1, None, p, p, None, p, need, None) == \
+        B.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_dispatch_gate_up(c, 8, 1, p, p, p, None, p, need, None) == \
+        B.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_dispatch_gate_up(c, 0, 1, p, p, p, None, p, need - 1, None) == \
+        B.MOE_ERR_WORKSPACE_TOO_SMALL
+    # x of more than 2^30 bytes: the gathering launch is refused (the forward
+    # dispatches such an x into the round buffer instead)
+    huge = B.config(1 << 19, 8, 2, 2048, 128, 1 << 16, "bf16")
+    assert huge.T * huge.d_model * 2 > 1 << 30
+    assert L.moe_dispatch_gate_up(ctypes.byref(huge), 0, 1, p, p, p, None, p,
+                                  B.workspace_size(huge), None) == B.MOE_ERR_UNSUPPORTED
+    assert b"2^30" in L.moe_last_error()
     assert L.moe_combine(c, p, need, None, None) == B.MOE_ERR_INVALID_ARGUMENT
     assert L.moe_pack_weights(c, p, p, None, p, p, p, None) == \
         B.MOE_ERR_INVALID_ARGUMENT

@@ -123,7 +123,8 @@ def test_full_size_stages_on_sampled_slots(name):
     counts): the plan bit-exact, gathered rows bit-exact for sampled slots of
     every round (an expert's first and last slot among them), and the expert
     outputs z within tolerance for sampled assignments spread over every
-    round, including the one-expert rounds."""
+    round, including the one-expert rounds; the gate/up launch that gathers
+    its rows from x writes the same h bits as dispatch + gate/up."""
     case = get_case(name)
     w = case.w
     cfg = case.cfg()
@@ -139,6 +140,11 @@ def test_full_size_stages_on_sampled_slots(name):
     z_assign = []
     for r in range(R):
         note(f"{name}: moe_dispatch round {r} of {R}")
+        # (xr's rows past an expert's m then read as the zeros the gathering
+        # launch reads there, so all of h can be compared below: the epilogue
+        # also stores the rows up to the next multiple of 32, which only feed
+        # outputs that are never stored)
+        views["xr"].zero_()
         B.moe_dispatch(cfg, r, case.x, ws)
         torch.cuda.synchronize()
         m = p.rows_in_round(r)
@@ -156,7 +162,18 @@ def test_full_size_stages_on_sampled_slots(name):
         want = case.x[torch.from_numpy(a // w.k).to(case.dev)]
         assert torch.equal(got.view(torch.int16), want.view(torch.int16)), f"xr round {r}"
         note(f"{name}: moe_expert_ffn round {r} of {R} (fitted launch shape)")
+        views["h"].fill_(0xFF)
         B.moe_expert_ffn(cfg, r, wg, wu, wd, ws, counts_host=counts)
+        # the dispatch fused into gate/up (what moe_forward runs): every byte
+        # of h the same, from the same poisoned start, with xr poisoned
+        h1 = views["h"].clone()
+        note(f"{name}: moe_dispatch_gate_up round {r} of {R}")
+        views["xr"].fill_(0xFF)
+        views["h"].fill_(0xFF)
+        B.moe_dispatch_gate_up(cfg, r, case.x, wg, wu, ws, counts_host=counts)
+        torch.cuda.synchronize()
+        assert torch.equal(views["h"], h1), f"fused h of {name} round {r}"
+        del h1
         in_round = np.nonzero(p.round_of == r)[0]
         z_assign.append(rng.choice(in_round, min(per_round_z, in_round.size),
                                    replace=False))
@@ -347,3 +364,51 @@ def test_forward_from_many_threads():
     assert not errors, errors
     free1, _ = torch.cuda.mem_get_info()
     assert free0 == free1, f"device memory changed by {free0 - free1} bytes"
+
+
+def test_forward_with_an_x_over_2_30_bytes_dispatches_into_the_round_buffer():
+    """x of more than 2^30 bytes (T = 2^19, d = 1088, bf16): the gate/up
+    launch that gathers rows from x is refused, and moe_forward dispatches
+    each launch batch into the round buffer instead. Its y has the bits of
+    the stage calls (moe_dispatch + moe_expert_ffn per batch, moe_combine)
+    and matches the oracle on sampled tokens. Inputs: seeded N(0, 1) logits
+    and x, N(0, 1/fan_in) weights, drawn on the device."""
+    T, E, k, d, f, C = 1 << 19, 8, 1, 1088, 64, 1 << 16
+    assert T * d * 2 > 1 << 30
+    dev = "cuda:0"
+    _cache.clear()
+    torch.cuda.empty_cache()
+    gen = torch.Generator(device=dev).manual_seed(7)
+    logits = torch.randn(T, E, device=dev, generator=gen)
+    x = torch.randn(T, d, device=dev, generator=gen).to(torch.bfloat16)
+    wg = (torch.randn(E, f, d, device=dev, generator=gen) * d ** -0.5).to(torch.bfloat16)
+    wu = (torch.randn(E, f, d, device=dev, generator=gen) * d ** -0.5).to(torch.bfloat16)
+    wd = (torch.randn(E, d, f, device=dev, generator=gen) * f ** -0.5).to(torch.bfloat16)
+    cfg = B.config(T, E, k, d, f, C, "bf16", "row_major")
+    ws = torch.empty(B.workspace_size(cfg), dtype=torch.uint8, device=dev)
+    note("big x: moe_forward")
+    y1 = torch.empty(T, d, dtype=torch.bfloat16, device=dev)
+    B.moe_forward(cfg, logits, x, wg, wu, wd, y1, ws)
+    torch.cuda.synchronize()
+    with pytest.raises(B.MoeError) as err:
+        B.moe_dispatch_gate_up(cfg, 0, x, wg, wu, ws)
+    assert err.value.status == B.MOE_ERR_UNSUPPORTED
+    note("big x: stage calls")
+    R, counts = B.moe_plan(cfg, logits, ws, return_counts=True)
+    assert R >= 2
+    for r0, n in B.launch_batches(cfg, counts):
+        B.moe_dispatch(cfg, r0, x, ws, n_rounds=n)
+        B.moe_expert_ffn(cfg, r0, wg, wu, wd, ws, counts_host=counts, n_rounds=n)
+    y2 = torch.empty_like(y1)
+    B.moe_combine(cfg, ws, y2)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    del ws, y2
+    note("big x: oracle on sampled tokens")
+    idx, wt = oracle.route(logits.cpu().numpy(), k)
+    tok = np.unique(np.concatenate(
+        [[0, T - 1], np.random.default_rng(3).choice(T, 62, replace=False)]))
+    t_dev = torch.from_numpy(tok).to(dev)
+    y_ref = oracle.forward_tokens(np.arange(tok.size), idx[tok], wt[tok],
+                                  to_np(x[t_dev]), to_np(wg), to_np(wu), to_np(wd))
+    assert_close(to_np(y1[t_dev]), y_ref, "bf16", "y (x over 2^30 bytes)")

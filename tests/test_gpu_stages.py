@@ -53,6 +53,12 @@ def _case_id(v):
     return v.name if hasattr(v, "name") else str(v)
 
 
+def _poison(views, *names):
+    """Fill workspace buffers with NaN bits (all ones)."""
+    for n in names:
+        views[n].view(torch.uint8).fill_(0xFF)
+
+
 @pytest.mark.parametrize("layout", ["tiled", "row_major"])
 @pytest.mark.parametrize("w,G,S", GROUP_CASES, ids=_case_id)
 def test_stages_match_oracle(w, G, S, layout):
@@ -103,6 +109,16 @@ def test_stages_match_oracle(w, G, S, layout):
         # z is in expert-sorted order: assignment a's row is pos[a]
         rows = torch.from_numpy(p.pos[np.array(assigns)]).to(case.dev).long()
         assert_close(to_np(views["z"][rows]), o_ref, w.dtype, f"z round {r}")
+
+        # the dispatch fused into gate/up: the same h bits with xr and h
+        # poisoned first (so xr is not read and every row of h is written)
+        note(f"{w.name}/G{G}/S{S}/{layout}: moe_dispatch_gate_up round {r}")
+        _poison(views, "xr", "h")
+        B.moe_dispatch_gate_up(cfg, r, case.x, wg, wu, ws, counts_host=counts_host)
+        torch.cuda.synchronize()
+        h2 = torch.cat([expert_rows(views, cfg, r, e, int(m[e]), w.d_ff, dt, "h")
+                        for e in experts])
+        assert torch.equal(h2.view(ibits), h.view(ibits)), f"fused h round {r}"
 
     M = B.buffer_geometry(cfg)["M"]
     if R < M:
@@ -320,6 +336,15 @@ def test_batched_stages_match_oracle(w):
         rows = torch.from_numpy(p.pos[np.array(assigns)]).to(case.dev).long()
         assert_close(to_np(views["z"][rows]), o_ref, w.dtype,
                      f"z of rounds {r0}..{r0 + n - 1}")
+        note(f"{w.name}: moe_dispatch_gate_up rounds {r0}..{r0 + n - 1}")
+        _poison(views, "xr", "h")
+        B.moe_dispatch_gate_up(cfg, r0, case.x, wg, wu, ws, counts_host=counts,
+                               n_rounds=n)
+        torch.cuda.synchronize()
+        h2 = torch.cat([expert_rows(views, cfg, r, e, m, w.d_ff, dt, "h")
+                        for r, e, m in pairs])
+        assert torch.equal(h2.view(ibits), h.view(ibits)), \
+            f"fused h of rounds {r0}..{r0 + n - 1}"
     y = case.new_y()
     B.moe_combine(cfg, ws, y)
     torch.cuda.synchronize()
