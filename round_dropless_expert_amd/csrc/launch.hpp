@@ -29,9 +29,10 @@ struct Shape {
   int64_t max_rounds() const { return (T + ce - 1) / ce; }
 };
 
-// Plan-internal granularity: the router counts an expert histogram for
-// every 8 consecutive tokens (one workgroup each); a reduction sums them per
-// chunk of 256 tokens, and the ranking kernel takes one chunk per workgroup.
+// Plan-internal granularity: the ranking kernel takes one chunk of 256
+// tokens per workgroup and needs each chunk's expert counts. The wavefront
+// router (k > 8) counts an expert histogram for every 8 consecutive tokens
+// (one workgroup each) and a reduction sums them per chunk.
 constexpr int kHistTokens = 8;
 constexpr int kRankTokens = 256;
 
@@ -41,6 +42,10 @@ inline int64_t hist_rows(const Shape& s) {
 inline int64_t rank_blocks(const Shape& s) {
   return (s.T + kRankTokens - 1) / kRankTokens;
 }
+// The router for k <= 8 (one token per lane, one ranking chunk per
+// workgroup) writes the chunk sums itself; for larger k the wavefront
+// router writes the 8-token histogram and a reduction sums it per chunk.
+inline bool route_sums_chunks(const Shape& s) { return s.k <= 8; }
 // plan scratch: hist [hist_rows][E], then chunk sums [rank_blocks][E]
 inline int64_t plan_scratch_ints(const Shape& s) {
   return (hist_rows(s) + rank_blocks(s)) * s.E;

@@ -17,6 +17,7 @@
 namespace moe {
 
 // ---------------------------------------------------------------- router
+// Wavefront router (k > 8; topk_lane_kernel below serves k <= 8).
 // Workgroup b routes the tokens [kHistTokens*b, kHistTokens*(b+1)): one
 // wavefront serves 64/EP rows at a time, lane e of a row segment holding
 // logit e. The k picks are k butterfly arg-max reductions over the segment,
@@ -92,6 +93,124 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(
   if (threadIdx.x < E) hist[(int64_t)blockIdx.x * E + threadIdx.x] = h[threadIdx.x];
 }
 
+// Router for k <= 8: lanes 4 t .. 4 t + 3 of workgroup b route token
+// kRankTokens * b + t. Lane q of the four holds experts q M .. q M + M - 1
+// (M = EP / 4) and keeps its K best (value, expert) pairs (K: k rounded up
+// to a power of two) in registers, sorted by the same strict total order
+// (logit descending, expert ascending): each insertion carries the losing
+// pair down the list, and placeholders (-inf, 64 + i) lose to every real
+// expert, -inf included. Two exchange rounds with the lanes at xor distance
+// 1 and 2 then merge the four lists: the pairwise better of a[i] and the
+// partner's b[K-1-i] are the K best of both lists in bitonic order, which
+// K/2 log2 K compare-exchanges sort (both lanes of a pair end with the same
+// list). The workgroup's 256 tokens are exactly one ranking chunk, so it
+// writes that chunk's expert counts (plan phase 1 summed per chunk)
+// directly. kVec: the logits rows are 16-byte aligned and each lane's M
+// logits are read four at a time.
+struct Pick {
+  float v;
+  int e;
+};
+
+__device__ __forceinline__ bool pick_better(float v1, int e1, float v2, int e2) {
+  // bitwise, not short-circuit: no branch per comparison
+  return (v1 > v2) | ((v1 == v2) & (e1 < e2));
+}
+
+template <int EP, int K, bool kVec>
+__global__ __launch_bounds__(1024) void topk_lane_kernel(
+    const float* __restrict__ logits, int64_t T, int E, int k,
+    int32_t* __restrict__ idx, float* __restrict__ weight,
+    int32_t* __restrict__ sums) {
+  constexpr int L = 4, M = EP / L;
+  static_assert(K <= 8 && EP <= kWave && EP >= L, "lane router: k <= 8, E <= 64");
+  static_assert(!kVec || M % 4 == 0, "four logits per load");
+  __shared__ int h[kWave];
+  if (threadIdx.x < kWave) h[threadIdx.x] = 0;
+  __syncthreads();
+  const int q = threadIdx.x & (L - 1);
+  const int64_t row = (int64_t)blockIdx.x * kRankTokens + threadIdx.x / L;
+  const bool live = row < T;
+  const int e0 = q * M;
+  const float* lr = logits + (live ? row : 0) * E + e0;
+  float lv[M];
+  if constexpr (kVec) {
+#pragma unroll
+    for (int c = 0; c < M / 4; ++c) {
+      const float4 f = live && e0 + 4 * c < E ? reinterpret_cast<const float4*>(lr)[c]
+                                              : make_float4(0.f, 0.f, 0.f, 0.f);
+      lv[4 * c] = f.x;
+      lv[4 * c + 1] = f.y;
+      lv[4 * c + 2] = f.z;
+      lv[4 * c + 3] = f.w;
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < M; ++m) lv[m] = live && e0 + m < E ? lr[m] : 0.f;
+  }
+  Pick t[K];
+#pragma unroll
+  for (int i = 0; i < K; ++i) t[i] = {-INFINITY, kWave + i};
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    if (e0 + m < E) {
+      // NaN as -inf, as in the wavefront router: it ranks below every
+      // number and above no real expert's place
+      Pick c = {lv[m] == lv[m] ? lv[m] : -INFINITY, e0 + m};
+#pragma unroll
+      for (int i = 0; i < K; ++i) {
+        const bool win = pick_better(c.v, c.e, t[i].v, t[i].e);
+        const Pick d = win ? t[i] : c;
+        t[i] = win ? c : t[i];
+        c = d;
+      }
+    }
+  }
+  // merge with the lanes at xor distance 1, then 2 (all lanes take part)
+#pragma unroll
+  for (int x = 1; x < L; x <<= 1) {
+    Pick b[K];
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      b[i].v = __shfl_xor(t[i].v, x);
+      b[i].e = __shfl_xor(t[i].e, x);
+    }
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      const Pick o = b[K - 1 - i];
+      t[i] = pick_better(t[i].v, t[i].e, o.v, o.e) ? t[i] : o;
+    }
+#pragma unroll
+    for (int st = K / 2; st > 0; st >>= 1)
+#pragma unroll
+      for (int i = 0; i < K; ++i)
+        if ((i & st) == 0) {
+          const Pick a = t[i], c = t[i + st];
+          const bool keep = pick_better(a.v, a.e, c.v, c.e);
+          t[i] = keep ? a : c;
+          t[i + st] = keep ? c : a;
+        }
+  }
+  if (live && q == 0) {
+    // softmax over the k picks
+    float ex[K], sum = 0.f;
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      ex[j] = j < k ? expf(t[j].v - t[0].v) : 0.f;
+      sum += ex[j];
+    }
+#pragma unroll
+    for (int j = 0; j < K; ++j)
+      if (j < k) {
+        idx[row * k + j] = t[j].e;
+        weight[row * k + j] = ex[j] / sum;
+        atomicAdd(&h[t[j].e], 1);
+      }
+  }
+  __syncthreads();
+  if (threadIdx.x < E) sums[(int64_t)blockIdx.x * E + threadIdx.x] = h[threadIdx.x];
+}
+
 template <int EP>
 static hipError_t route_ep(const Shape& s, const float* logits, PlanBuffers b,
                            hipStream_t st) {
@@ -101,8 +220,40 @@ static hipError_t route_ep(const Shape& s, const float* logits, PlanBuffers b,
   return hipGetLastError();
 }
 
+template <int EP, int K>
+static hipError_t route_lane(const Shape& s, const float* logits, PlanBuffers b,
+                             hipStream_t st) {
+  static_assert(kRankTokens * 4 == 1024, "one ranking chunk per workgroup, 4 lanes a token");
+  int32_t* sums = b.scratch + hist_rows(s) * s.E;
+  constexpr bool kCanVec = EP >= 16;  // four logits or more per lane
+  const bool vec = kCanVec && s.E % 4 == 0 && ((uintptr_t)logits & 15) == 0;
+  if (vec)
+    hipLaunchKernelGGL((topk_lane_kernel<EP, K, kCanVec>), dim3((unsigned)rank_blocks(s)),
+                       dim3(1024), 0, st, logits, s.T, s.E, s.k, b.idx, b.weight, sums);
+  else
+    hipLaunchKernelGGL((topk_lane_kernel<EP, K, false>), dim3((unsigned)rank_blocks(s)),
+                       dim3(1024), 0, st, logits, s.T, s.E, s.k, b.idx, b.weight, sums);
+  return hipGetLastError();
+}
+
+template <int EP>
+static hipError_t route_lane_k(const Shape& s, const float* logits, PlanBuffers b,
+                               hipStream_t st) {
+  if (s.k <= 1) return route_lane<EP, 1>(s, logits, b, st);
+  if (s.k <= 2) return route_lane<EP, 2>(s, logits, b, st);
+  if (s.k <= 4) return route_lane<EP, 4>(s, logits, b, st);
+  return route_lane<EP, 8>(s, logits, b, st);
+}
+
 hipError_t launch_route(const Shape& s, const float* logits, PlanBuffers b,
                         hipStream_t st) {
+  if (route_sums_chunks(s)) {
+    if (s.E <= 4) return route_lane_k<4>(s, logits, b, st);
+    if (s.E <= 8) return route_lane_k<8>(s, logits, b, st);
+    if (s.E <= 16) return route_lane_k<16>(s, logits, b, st);
+    if (s.E <= 32) return route_lane_k<32>(s, logits, b, st);
+    return route_lane_k<64>(s, logits, b, st);
+  }
   if (s.E <= 1) return route_ep<1>(s, logits, b, st);
   if (s.E <= 2) return route_ep<2>(s, logits, b, st);
   if (s.E <= 4) return route_ep<4>(s, logits, b, st);
@@ -492,10 +643,13 @@ hipError_t launch_plan(const Shape& s, PlanBuffers b, hipStream_t st) {
   const int64_t nrows = hist_rows(s);
   const int64_t nb = rank_blocks(s);
   int32_t* sums = b.scratch + nrows * s.E;
-  hipLaunchKernelGGL(plan_chunk_sum_kernel, dim3((unsigned)nb), dim3(256), 0, st,
-                     b.scratch, nrows, s.E, sums);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  hipError_t err = hipSuccess;
+  if (!route_sums_chunks(s)) {  // else the router wrote the chunk sums
+    hipLaunchKernelGGL(plan_chunk_sum_kernel, dim3((unsigned)nb), dim3(256), 0, st,
+                       b.scratch, nrows, s.E, sums);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
   const bool self = nb <= kSelfScanMaxChunks;
   const int64_t mr = s.max_rounds();
   if (self && s.G == 1) {  // one pass: no phase 2

@@ -218,7 +218,7 @@ def test_degenerate_shapes_forward(w):
     assert torch.isfinite(views["z"].float()).all()
 
 
-@pytest.mark.parametrize("E,k", [(8, 2), (5, 5), (64, 8)])
+@pytest.mark.parametrize("E,k", [(8, 2), (5, 5), (64, 8), (16, 12)])
 def test_nonfinite_logits_give_an_in_range_plan(E, k):
     """NaN and infinite logits: the routing of such a row is unspecified, but
     its k picks are distinct experts in [0, E), so the plan stays a valid

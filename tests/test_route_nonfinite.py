@@ -1,6 +1,6 @@
 """Router selection with non-finite logits (CPU).
 
-The router kernel picks a token's k experts with k butterfly arg-max
+For k > 8 the router kernel picks a token's k experts with k butterfly arg-max
 reductions across the lanes of a row segment (EP lanes, lane e holding
 logit e; lanes e >= E are padding). Each lane carries a key: e for a live
 lane, 64 + e for padding, 128 + e once its expert has been picked. Pairs are
@@ -11,6 +11,15 @@ a padding or retired key, i.e. an expert index >= E. The kernel maps NaN to
 and checks that every pick is k distinct experts in [0, E) for all-NaN,
 mixed NaN/inf and all -inf rows, and that finite rows keep the documented
 order (largest logit first, ties to the lower expert).
+
+For k <= 8 four lanes hold one token: lane q keeps the K (k rounded up to a
+power of two) best (value, expert) pairs of its quarter of the experts in a
+sorted list, inserting them in expert order (an insertion carries the
+losing pair down the list; the list starts with placeholders (-inf, 64 + i),
+which lose to every real expert), and two exchange rounds (xor distance 1,
+then 2) merge the four lists: the pairwise better of a[i] and the partner's
+b[K-1-i], sorted by a bitonic network. The same checks run on a replay of
+that.
 """
 import math
 
@@ -113,3 +122,83 @@ def test_random_finite_rows_match_the_reference_order():
         k = int(rng.integers(1, E + 1))
         logits = rng.integers(-2, 3, size=E).astype(np.float32).tolist()
         assert emulate_row(logits, k, segment_width(E)) == reference_order(logits, k)
+
+
+def _lane_better(a, b):
+    return a[0] > b[0] or (a[0] == b[0] and a[1] < b[1])
+
+
+def emulate_lane(logits, k):
+    """The lane router's k picks for one row (list of experts)."""
+    E = len(logits)
+    K = 1
+    while K < k:
+        K *= 2
+    EP = 4
+    while EP < E:
+        EP *= 2
+    M = EP // 4
+    lists = []
+    for q in range(4):
+        t = [(-math.inf, WAVE + i) for i in range(K)]
+        for e in range(q * M, q * M + M):
+            if e >= E:
+                continue
+            v = float(np.float32(logits[e]))
+            c = (v if v == v else -math.inf, e)
+            for i in range(K):
+                if _lane_better(c, t[i]):
+                    t[i], c = c, t[i]
+        lists.append(t)
+    for x in (1, 2):
+        new = []
+        for q in range(4):
+            a, b = lists[q], lists[q ^ x]
+            t = [a[i] if _lane_better(a[i], b[K - 1 - i]) else b[K - 1 - i]
+                 for i in range(K)]
+            st = K // 2
+            while st > 0:
+                for i in range(K):
+                    if i & st == 0 and not _lane_better(t[i], t[i + st]):
+                        t[i], t[i + st] = t[i + st], t[i]
+                st //= 2
+            new.append(t)
+        # the two lanes of a pair agree
+        for q in range(4):
+            assert new[q] == new[q ^ x] or K == 0
+        lists = new
+    return [e for _, e in lists[0][:k]]
+
+
+@pytest.mark.parametrize("E", [1, 2, 5, 8, 13, 32, 64])
+@pytest.mark.parametrize("row", list(ROWS))
+def test_lane_router_picks_are_distinct_in_range_experts(E, row):
+    logits = ROWS[row](E)
+    for k in sorted({1, min(2, E), min(3, E), min(4, E), min(8, E)}):
+        picks = emulate_lane(logits, k)
+        assert len(set(picks)) == k, (row, E, k, picks)
+        assert all(0 <= p < E for p in picks), (row, E, k, picks)
+        assert picks == reference_order(logits, k), (row, E, k, picks)
+
+
+def test_lane_router_placeholders_must_lose_ties():
+    """The failure the placeholder keys prevent: compared by value alone, an
+    all -inf row would keep the placeholders (-inf) and pick no real
+    expert."""
+    K, tv, te = 2, [-math.inf] * 2, [WAVE, WAVE + 1]
+    for e in range(4):
+        v, ce = -math.inf, e
+        for i in range(K):
+            if v > tv[i]:  # value only
+                tv[i], te[i], v, ce = v, ce, tv[i], te[i]
+    assert te == [WAVE, WAVE + 1]
+    assert emulate_lane([-INF] * 4, 2) == [0, 1]
+
+
+def test_lane_router_random_rows_match_the_reference_order():
+    rng = np.random.default_rng(6)
+    for _ in range(300):
+        E = int(rng.integers(1, 65))
+        k = int(rng.integers(1, min(E, 8) + 1))
+        logits = rng.integers(-2, 3, size=E).astype(np.float32).tolist()
+        assert emulate_lane(logits, k) == reference_order(logits, k)
