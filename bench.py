@@ -396,10 +396,10 @@ def measure(w, args, steps, warmup, kernel_steps, with_cpu):
     cfg = B.config(w.T, w.E, w.k, w.d_model, w.d_ff, w.C, w.dtype, layout,
                    args.group, args.round_buffers)
     if layout == "tiled":
-        # one-time repack at load time, outside the timed region
+        # one-time repack at load time, outside the timed region (the
+        # row-major copies stay for the repack's own timing below)
         wg, wu, wd = (torch.empty_like(t) for t in (wg_rm, wu_rm, wd_rm))
         B.moe_pack_weights(cfg, wg_rm, wu_rm, wd_rm, wg, wu, wd)
-        del wg_rm, wu_rm, wd_rm
     else:
         wg, wu, wd = wg_rm, wu_rm, wd_rm
     ws_bytes = B.workspace_size(cfg)
@@ -546,6 +546,34 @@ def measure(w, args, steps, warmup, kernel_steps, with_cpu):
     copy_gbps = 2 * COPY_BYTES * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
     del csrc, cdst
 
+    # the tiled layout's price, for callers that update the weights every
+    # step: the repack's time (three launches' worth, events on the stream),
+    # and the layer with the row-major weights as given (no repack)
+    weights = {"layout": layout}
+    if layout == "tiled":
+        p0 = torch.cuda.Event(enable_timing=True)
+        p1 = torch.cuda.Event(enable_timing=True)
+        B.moe_pack_weights(cfg, wg_rm, wu_rm, wd_rm, wg, wu, wd, stream)
+        p0.record(stream)
+        for _ in range(3):
+            B.moe_pack_weights(cfg, wg_rm, wu_rm, wd_rm, wg, wu, wd, stream)
+        p1.record(stream)
+        torch.cuda.synchronize()
+        weights["pack_us"] = p0.elapsed_time(p1) * 1e3 / 3
+        weights["pack_GBps"] = 2 * 3 * w.E * df * es / (weights["pack_us"] * 1e-6) / 1e9
+        cfg_rm = B.config(w.T, w.E, w.k, w.d_model, w.d_ff, w.C, w.dtype, "row_major",
+                          args.group, args.round_buffers)
+        n_rm = 10
+        for _ in range(2):
+            B.moe_forward(cfg_rm, logits, x, wg_rm, wu_rm, wd_rm, y, ws, stream)
+        torch.cuda.synchronize()
+        t_rm = time.perf_counter()
+        for _ in range(n_rm):
+            B.moe_forward(cfg_rm, logits, x, wg_rm, wu_rm, wd_rm, y, ws, stream)
+        torch.cuda.synchronize()
+        weights["row_major_ms_per_step"] = (time.perf_counter() - t_rm) * 1e3 / n_rm
+        del wg_rm, wu_rm, wd_rm
+
     # dominant kernel: the grouped gate/up launch of the first batch (round 0,
     # the largest round)
     flops_g0 = 4.0 * float(A_b[0]) * df
@@ -604,6 +632,7 @@ def measure(w, args, steps, warmup, kernel_steps, with_cpu):
         "device_copy_GBps": copy_gbps,
         "workspace_bytes": ws_bytes, "peak_allocated_bytes": peak_bytes,
         "roofline": roofline, "layer_bound": layer_bound, "kernels": kernels,
+        "weights": weights,
     }
     if with_cpu:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
@@ -647,7 +676,8 @@ def main():
                                "ms_per_step_min", "config", "roofline",
                                "grouped_gemm_mfma_util_pct", "dispatch_GBps",
                                "dispatch_round0_GBps", "combine_GBps",
-                               "peak_allocated_bytes", "layer_bound", "kernels")}}
+                               "peak_allocated_bytes", "layer_bound", "kernels",
+                               "weights")}}
     if w.dtype == "bf16":
         # the rooflines' achieved rates against the rate the matrix cores
         # sustain on this chip (beside the published peak)
