@@ -91,35 +91,46 @@ hipError_t launch_dispatch(const Shape& s, int r0, int nr, const void* x,
   return hipGetLastError();
 }
 
-// Row-major [E][rows][cols] -> tiled per expert (moe_pack_weights): one
-// thread per 16-byte chunk, reads coalesced.
+// Row-major [E][rows][cols] -> tiled per expert (moe_pack_weights). rows
+// and the row bytes are multiples of 64, and the experts' matrices follow
+// each other, so the input is E * rows / 64 whole bands of 64 rows, each
+// the same bytes of the output. Workgroup b packs band b: for each 4 KiB
+// output block of the band (64 rows x 64 bytes), thread t writes its bytes
+// [16 t, 16 t + 16): physical row t / 4, chunk t % 4, which holds logical
+// chunk (t % 4) ^ ((t / 16) % 4) of that row. Four blocks per step, so
+// each thread has four loads in flight; stores are whole 1 KiB pieces per
+// wavefront.
 __global__ __launch_bounds__(256) void pack_tiled_kernel(
-    const char* __restrict__ src, char* __restrict__ dst, int64_t chunks,
-    int rows, int64_t row_bytes) {
-  const int64_t cpr = row_bytes / 16;
-  const int64_t per_mat = (int64_t)rows * cpr;
-  for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < chunks;
-       g += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t e = g / per_mat;
-    const int64_t w = g - e * per_mat;
-    const int64_t row = w / cpr;
-    const int64_t q = w - row * cpr;
-    const int64_t base = e * per_mat * 16;
-    *reinterpret_cast<u32x4*>(dst + base + tiled_offset(row, q * 16, row_bytes)) =
-        *reinterpret_cast<const u32x4*>(src + g * 16);
+    const char* __restrict__ src, char* __restrict__ dst, int64_t row_bytes) {
+  const int t = threadIdx.x;
+  const int r = t >> 2;
+  const int lc = (t & 3) ^ ((r >> 2) & 3);
+  const int64_t band = (int64_t)blockIdx.x * kTileRows * row_bytes;
+  const char* s = src + band + r * row_bytes + lc * 16;
+  char* d = dst + band + t * 16;
+  const int nblk = (int)(row_bytes / kTileRowBytes);
+  int b = 0;
+  for (; b + 4 <= nblk; b += 4) {
+    u32x4 v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      v[i] = *reinterpret_cast<const u32x4*>(s + (int64_t)(b + i) * kTileRowBytes);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<u32x4*>(d + (int64_t)(b + i) * kTileBytes) = v[i];
   }
+  for (; b < nblk; ++b)
+    *reinterpret_cast<u32x4*>(d + (int64_t)b * kTileBytes) =
+        *reinterpret_cast<const u32x4*>(s + (int64_t)b * kTileRowBytes);
 }
 
 hipError_t launch_pack_weights(const Shape& s, const void* src, void* dst,
                                int rows, int cols, int num_cus, hipStream_t st) {
+  (void)num_cus;
   const int64_t row_bytes = (int64_t)cols * (s.bf16 ? 2 : 4);
-  const int64_t chunks = (int64_t)s.E * rows * (row_bytes / 16);
-  int64_t blocks = (chunks + 255) / 256;
-  const int64_t cap = (int64_t)num_cus * 16;
-  if (blocks > cap) blocks = cap;
-  hipLaunchKernelGGL(pack_tiled_kernel, dim3((unsigned)blocks), dim3(256), 0, st,
-                     static_cast<const char*>(src), static_cast<char*>(dst), chunks,
-                     rows, row_bytes);
+  const int64_t bands = (int64_t)s.E * rows / kTileRows;  // rows % 64 == 0
+  hipLaunchKernelGGL(pack_tiled_kernel, dim3((unsigned)bands), dim3(256), 0, st,
+                     static_cast<const char*>(src), static_cast<char*>(dst), row_bytes);
   return hipGetLastError();
 }
 
