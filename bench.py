@@ -416,19 +416,24 @@ def measure(w, args, steps, warmup, kernel_steps, with_cpu):
     print(f"[bench] warmup {warmup}", file=sys.stderr, flush=True)
     for _ in range(warmup):
         step()
-    # an event after every step (they only mark the stream) gives the
-    # per-step GPU times for the median and the minimum; the wall clock over
-    # the whole bracket gives the value
-    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    # the value: the wall clock over the bracket of the timed steps, which
+    # run back to back with nothing else on the stream
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for i in range(steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / steps
+    # per-step GPU times for the median and the minimum, from a second pass
+    # with an event after every step (an event record takes a few
+    # microseconds of the stream, so it stays out of the timed pass)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     marks[0].record(stream)
     for i in range(steps):
         step()
         marks[i + 1].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / steps
     step_ms = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(steps))
     tokens_per_s = w.T * steps / wall
     peak_bytes = torch.cuda.max_memory_allocated() - base_alloc
