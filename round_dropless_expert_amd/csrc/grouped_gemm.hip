@@ -455,8 +455,11 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
   // expert order), i.e. token perm[z0 + c] / k. perm_rows loads those
   // assignments (-1: past the pair's rows, or no tile); token_offs turns
   // them into the lane's byte offsets in x. The loads are the compiler's
-  // own (it waits for them where token_offs uses them): they are issued a
-  // whole tile before that use, so they have landed by then.
+  // own, issued a whole tile before token_offs uses them: the compiler,
+  // which does not see the LDS-direct loads, waits there for the whole
+  // vector-memory counter, at the top of a tile, where the ring's first
+  // barrier waits for nearly all of it anyway (a build of the kernel that
+  // reads xr with that full wait added ran at the same speed).
   auto perm_rows = [&](int te, int tm, int tm0, bool exists, int32_t (&pa)[kTPasses]) {
     const int64_t z0 = exists ? __builtin_amdgcn_readlane(lane_off, te) : 0;
 #pragma unroll
