@@ -635,7 +635,12 @@ def measure(w, args, steps, warmup, kernel_steps, with_cpu):
                              if fused else "dispatch launch per batch"),
         "combine_GBps": kernels["combine"]["GB/s"],
         "device_copy_GBps": copy_gbps,
-        "workspace_bytes": ws_bytes, "peak_allocated_bytes": peak_bytes,
+        "workspace_bytes": ws_bytes,
+        # what moe_forward itself needs (the workspace before the round
+        # buffer xr, which the gathering forward never touches); the bench
+        # allocates all of it for the dispatch kernel's stand-alone timing
+        "forward_workspace_bytes": B.forward_workspace_size(cfg),
+        "peak_allocated_bytes": peak_bytes,
         "roofline": roofline, "layer_bound": layer_bound, "kernels": kernels,
         "weights": weights,
     }

@@ -42,7 +42,8 @@
  * row once, and y once after an fp32 weighted sum.
  *
  * Ownership: the caller allocates every buffer, including the workspace of
- * moe_workspace_size() bytes. The library allocates no device memory; its
+ * moe_workspace_size() bytes (moe_forward_workspace_size() bytes suffice for
+ * moe_forward and moe_backward). The library allocates no device memory; its
  * only state is, per device, a pool of the small pinned host buffer, side
  * stream and events with which moe_forward and moe_backward read the
  * plan's counts (see moe_forward), and the static workspace of
@@ -152,21 +153,24 @@ typedef struct {
  *                            rbeg[M], rend[M]: the pair indices of round
  *                            r's first pair and one past its last.
  *                            Entries of rounds r >= R are unused.
- *   xr       elem [S][E/G][Q][d] round buffers of gathered token rows (set
- *                            r % S for round r): Q = P
+ *   scratch  int32 [...]     plan-internal partial counts
+ *   h        elem [S][E/G][Q][f] SwiGLU activations of the round (set r % S
+ *                            for round r): Q = P
  *                            (G = 1) or G*(P+64) rows per group, P = C'
  *                            rounded up to a multiple of 64. In round r
  *                            expert e's rows start at row brow(r,e) of the
- *                            set, as an m(r,e) x d matrix in the tiled
+ *                            set, as an m(r,e) x f matrix in the tiled
  *                            layout (its slot c is row c; rows up to the
  *                            next multiple of 64 hold stale data)
- *   h        elem [S][E/G][Q][f] SwiGLU activations of the round, same layout
  *   z        elem [T*k][d]   unweighted expert output of every assignment,
  *                            in expert-sorted order: row i holds the output
  *                            of assignment perm[i] (so assignment a's row
  *                            is pos[a])
- *   scratch  int32 [...]     plan-internal partial counts
- * The layout, and so the size, is a pure function of the config.
+ *   xr       elem [S][E/G][Q][d] round buffers of gathered token rows, same
+ *                            layout as h with d columns (written by
+ *                            moe_dispatch); laid out last
+ * The offsets follow this order. The layout, and so the size, is a pure
+ * function of the config.
  */
 /* Launch batches. The forward does not need one dispatch and one launch of
  * each grouped GEMM per round: with G = 1 and one set of round buffers, a
@@ -207,6 +211,15 @@ moe_status_t moe_check_config(const moe_config_t *cfg);
  * memory of the method ("Expert groups keep memory fixed when tokens pile
  * up"). */
 moe_status_t moe_workspace_size(const moe_config_t *cfg, size_t *bytes);
+
+/* Workspace bytes that moe_forward and moe_backward need (also a pure host
+ * function of the config): the workspace up to the round buffer xr, which
+ * is laid out last, when the forward's gate/up launches read their token
+ * rows from x (x of at most 2^30 bytes, see moe_dispatch_gate_up), else
+ * moe_workspace_size's. These two calls accept a workspace of this size
+ * (its offsets are moe_workspace_layout's); every other call that takes a
+ * workspace needs moe_workspace_size bytes. */
+moe_status_t moe_forward_workspace_size(const moe_config_t *cfg, size_t *bytes);
 
 /* Offsets of every internal buffer (pure host function). */
 moe_status_t moe_workspace_layout(const moe_config_t *cfg,
@@ -372,7 +385,9 @@ moe_status_t moe_combine(const moe_config_t *cfg, const void *ws,
  * y is written in full. The dispatch is the gate/up launch's own fetch of
  * the token rows from x (as moe_dispatch_gate_up) when x holds at most 2^30
  * bytes, else one moe_dispatch launch per batch before its GEMMs; the
- * results are the same bits either way.
+ * results are the same bits either way. ws_bytes: at least
+ * moe_forward_workspace_size (with the gathering launches the round buffer
+ * xr is neither read nor written).
  * Returns after enqueueing the combine (the plan's wait is the only host
  * synchronisation; round 0's dispatch, and its GEMMs where a full round 0
  * fills the GPU, are queued before it). For that read
@@ -408,7 +423,7 @@ moe_status_t moe_forward(const moe_config_t *cfg, const float *logits,
  * moe_forward. The plan's counts and R are read into the call's own host
  * frame with one wait on `stream`; every launch batch then runs on
  * `stream` in order (with round_buffers = 2 the two buffer sets alternate,
- * without overlap). A config whose moe_workspace_size exceeds
+ * without overlap). A config whose moe_forward_workspace_size exceeds
  * MOE_STATIC_WORKSPACE_BYTES returns MOE_ERR_WORKSPACE_TOO_SMALL before any
  * HIP call. All calls on one GPU share its array and it keeps the last
  * call's contents: calls that overlap in time on one GPU (on different
@@ -468,7 +483,8 @@ moe_status_t moe_backward_layout(const moe_config_t *cfg,
  * transposed, so no second copy of the weights exists). dy [T][d] bf16.
  * Outputs (written in full): dx
  * [T][d] bf16, dlogits [T][E] float, dw_gate, dw_up [E][f][d] and dw_down
- * [E][d][f] float. bws: moe_backward_workspace_size bytes. Waits once for
+ * [E][d][f] float. ws_bytes: at least moe_forward_workspace_size (the
+ * forward's xr is not used). bws: moe_backward_workspace_size bytes. Waits once for
  * the forward's counts and R (as moe_forward), then asynchronous on stream.
  * dx and dlogits do not depend on C or G; the weight gradients' summation
  * order follows the rounds. */

@@ -30,7 +30,8 @@ MOE_WEIGHTS_ROW_MAJOR = 0
 MOE_WEIGHTS_TILED = 1
 
 EXPORTS = ("moe_status_string", "moe_last_error", "moe_hip_runtime_version",
-           "moe_check_config", "moe_workspace_size", "moe_workspace_layout",
+           "moe_check_config", "moe_workspace_size", "moe_forward_workspace_size",
+           "moe_workspace_layout",
            "moe_plan", "moe_launch_batches", "moe_dispatch", "moe_expert_ffn",
            "moe_expert_gate_up",
            "moe_expert_down", "moe_dispatch_gate_up", "moe_pack_weights", "moe_combine", "moe_forward",
@@ -96,6 +97,7 @@ def load() -> ctypes.CDLL:
     L.moe_hip_runtime_version.restype = ctypes.c_int32
     L.moe_check_config.argtypes = [cfgp]
     L.moe_workspace_size.argtypes = [cfgp, ctypes.POINTER(ctypes.c_size_t)]
+    L.moe_forward_workspace_size.argtypes = [cfgp, ctypes.POINTER(ctypes.c_size_t)]
     L.moe_workspace_layout.argtypes = [cfgp, ctypes.POINTER(MoeLayout)]
     L.moe_plan.argtypes = [cfgp, vp, vp, sz, i32p, vp]
     L.moe_launch_batches.argtypes = [cfgp, i32p, i32, i32p, i32p, i32p]
@@ -117,7 +119,8 @@ def load() -> ctypes.CDLL:
     L.moe_backward_layout.argtypes = [cfgp, ctypes.POINTER(MoeBackwardLayout)]
     L.moe_backward.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                vp, sz, vp, sz, vp]
-    for n in ("moe_check_config", "moe_workspace_size", "moe_workspace_layout",
+    for n in ("moe_check_config", "moe_workspace_size", "moe_forward_workspace_size",
+              "moe_workspace_layout",
               "moe_plan", "moe_launch_batches", "moe_dispatch", "moe_expert_ffn",
               "moe_expert_gate_up", "moe_expert_down", "moe_dispatch_gate_up",
               "moe_pack_weights",
@@ -186,6 +189,14 @@ def check_config(cfg: MoeConfig) -> int:
 def workspace_size(cfg: MoeConfig) -> int:
     n = ctypes.c_size_t(0)
     _check(load().moe_workspace_size(ctypes.byref(cfg), ctypes.byref(n)))
+    return n.value
+
+
+def forward_workspace_size(cfg: MoeConfig) -> int:
+    """Bytes moe_forward and moe_backward need (the workspace up to xr when
+    the forward gathers its rows from x)."""
+    n = ctypes.c_size_t(0)
+    _check(load().moe_forward_workspace_size(ctypes.byref(cfg), ctypes.byref(n)))
     return n.value
 
 

@@ -122,10 +122,18 @@ void layout_of(const moe_config_t* c, moe_workspace_layout_t* L) {
   L->rounds = take((size_t)moe::round_table_ints(s) * 4);
   L->scratch = take((size_t)moe::plan_scratch_ints(s) * 4);
   const size_t sets = (size_t)sets_of(c);
-  L->xr = take(sets * (size_t)s.buf_rows() * (size_t)c->d_model * es);
   L->h = take(sets * (size_t)s.buf_rows() * (size_t)c->d_ff * es);
   L->z = take(TK * (size_t)c->d_model * es);
+  // last, so that callers that never dispatch into it (the forward when
+  // its gate/up launches gather from x, and the backward) can leave it out
+  L->xr = take(sets * (size_t)s.buf_rows() * (size_t)c->d_model * es);
   L->total = off;
+}
+
+// Bytes moe_forward and moe_backward need: everything before xr when the
+// forward's gate/up launches gather their rows from x, else all of it.
+size_t forward_bytes(const moe_config_t* c, const moe_workspace_layout_t& L) {
+  return moe::gather_fits(shape_of(c)) ? L.xr : L.total;
 }
 
 struct Bound {
@@ -143,14 +151,17 @@ struct Bound {
   }
 };
 
-moe_status_t bind(const moe_config_t* c, void* ws, size_t ws_bytes, Bound* b) {
+// forward: the call is moe_forward, moe_forward_static or moe_backward,
+// which need only forward_bytes of the workspace.
+moe_status_t bind(const moe_config_t* c, void* ws, size_t ws_bytes, Bound* b,
+                  bool forward = false) {
   moe_status_t st = check_cfg(c);
   if (st != MOE_OK) return st;
   if (!ws) return fail(MOE_ERR_INVALID_ARGUMENT, "workspace is NULL");
   if (!aligned16(ws))
     return fail(MOE_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
   layout_of(c, &b->L);
-  if (ws_bytes < b->L.total)
+  if (ws_bytes < (forward ? forward_bytes(c, b->L) : b->L.total))
     return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace too small");
   b->s = shape_of(c);
   b->sets = sets_of(c);
@@ -532,6 +543,16 @@ moe_status_t moe_workspace_size(const moe_config_t* cfg, size_t* bytes) {
   return MOE_OK;
 }
 
+moe_status_t moe_forward_workspace_size(const moe_config_t* cfg, size_t* bytes) {
+  moe_status_t st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if (!bytes) return fail(MOE_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  moe_workspace_layout_t L;
+  layout_of(cfg, &L);
+  *bytes = forward_bytes(cfg, L);
+  return MOE_OK;
+}
+
 moe_status_t moe_capacity_curve(const moe_config_t* cfg, const int32_t* counts,
                                 int64_t n_steps, const int64_t* capacities,
                                 int32_t n_capacities, int32_t* rounds,
@@ -744,7 +765,7 @@ moe_status_t moe_backward(const moe_config_t* cfg, const void* x, const void* w_
   moe_status_t st = check_bwd_cfg(cfg);
   if (st != MOE_OK) return st;
   Bound b;
-  if ((st = bind(cfg, const_cast<void*>(ws), ws_bytes, &b)) != MOE_OK) return st;
+  if ((st = bind(cfg, const_cast<void*>(ws), ws_bytes, &b, true)) != MOE_OK) return st;
   const void* ptrs[] = {x, w_gate, w_up, w_down, dy, dx, dlogits,
                         dw_gate, dw_up, dw_down, bws};
   const char* names[] = {"x", "w_gate", "w_up", "w_down", "dy", "dx",
@@ -850,7 +871,7 @@ moe_status_t moe_forward(const moe_config_t* cfg, const float* logits,
                          const void* w_down, void* y, void* ws, size_t ws_bytes,
                          void* stream) {
   Bound b;
-  moe_status_t st = bind(cfg, ws, ws_bytes, &b);
+  moe_status_t st = bind(cfg, ws, ws_bytes, &b, true);
   if (st != MOE_OK) return st;
   if ((st = check_ptr(logits, "logits")) != MOE_OK) return st;
   if ((st = check_ptr(x, "x")) != MOE_OK) return st;
@@ -955,11 +976,12 @@ moe_status_t moe_forward_static(const moe_config_t* cfg, const float* logits,
   if (st != MOE_OK) return st;
   moe_workspace_layout_t L;
   layout_of(cfg, &L);
-  if (L.total > (size_t)MOE_STATIC_WORKSPACE_BYTES) {
+  const size_t need = forward_bytes(cfg, L);
+  if (need > (size_t)MOE_STATIC_WORKSPACE_BYTES) {
     std::snprintf(g_err, sizeof g_err,
                   "the config needs a workspace of %zu bytes; the static workspace "
                   "holds %zu",
-                  L.total, (size_t)MOE_STATIC_WORKSPACE_BYTES);
+                  need, (size_t)MOE_STATIC_WORKSPACE_BYTES);
     return MOE_ERR_WORKSPACE_TOO_SMALL;
   }
   const void* ptrs[] = {logits, x, w_gate, w_up, w_down, y};
@@ -969,7 +991,8 @@ moe_status_t moe_forward_static(const moe_config_t* cfg, const float* logits,
   char* ws = nullptr;
   if ((st = static_workspace(&ws)) != MOE_OK) return st;
   Bound b;
-  if ((st = bind(cfg, ws, (size_t)MOE_STATIC_WORKSPACE_BYTES, &b)) != MOE_OK) return st;
+  if ((st = bind(cfg, ws, (size_t)MOE_STATIC_WORKSPACE_BYTES, &b, true)) != MOE_OK)
+    return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   int cus = 0;
   if ((st = num_cus(&cus)) != MOE_OK) return st;

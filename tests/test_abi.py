@@ -77,9 +77,16 @@ def test_workspace_is_a_function_of_the_config_only(B):
         assert n == expected_total(w.T, w.E, w.k, w.d_model, w.d_ff, w.C, es)
         lay = B.workspace_layout(cfg)
         assert lay["n_rounds"] == lay["counts"] + 4 * w.E
-        offs = [lay[f] for f in B.LAYOUT_FIELDS if f != "n_rounds"]
+        # the documented order, the round buffer xr last
+        order = ("idx", "weight", "counts", "offsets", "perm", "pos", "round_of",
+                 "row_of", "rounds", "scratch", "h", "z", "xr")
+        offs = [lay[f] for f in order]
         assert all(o % 256 == 0 for o in offs)
         assert offs == sorted(offs) and lay["total"] == n
+        # the forward gathers its rows from x (at most 2^30 bytes here), so
+        # it and the backward need only the workspace before xr
+        assert w.T * w.d_model * es <= 1 << 30
+        assert B.forward_workspace_size(cfg) == lay["xr"]
         sizes[name] = n
     # skewed routing needs exactly the balanced workload's memory
     assert sizes["skewed_bf16"] == sizes["balanced_bf16"]
@@ -154,8 +161,8 @@ def test_pointer_and_workspace_checks_before_any_hip_call(B):
     need = B.workspace_size(cfg)
     p = 1 << 20  # aligned fake device address, never dereferenced
     c = ctypes.byref(cfg)
-    assert L.moe_forward(c, p, p, p, p, p, p, p, need - 1, None) == \
-        B.MOE_ERR_WORKSPACE_TOO_SMALL
+    assert L.moe_forward(c, p, p, p, p, p, p, p, B.forward_workspace_size(cfg) - 1,
+                         None) == B.MOE_ERR_WORKSPACE_TOO_SMALL
     assert L.moe_forward(c, p, p, p, p, p, p, None, need, None) == \
         B.MOE_ERR_INVALID_ARGUMENT
     assert L.moe_forward(c, p + 4, p, p, p, p, p, p, need, None) == \
@@ -185,12 +192,26 @@ def test_pointer_and_workspace_checks_before_any_hip_call(B):
     assert L.moe_dispatch_gate_up(c, 0, 1, p, p, p, None, p, need - 1, None) == \
         B.MOE_ERR_WORKSPACE_TOO_SMALL
     # x of more than 2^30 bytes: the gathering launch is refused (the forward
-    # dispatches such an x into the round buffer instead)
+    # dispatches such an x into the round buffer instead, so it needs all of
+    # the workspace)
     huge = B.config(1 << 19, 8, 2, 2048, 128, 1 << 16, "bf16")
     assert huge.T * huge.d_model * 2 > 1 << 30
     assert L.moe_dispatch_gate_up(ctypes.byref(huge), 0, 1, p, p, p, None, p,
                                   B.workspace_size(huge), None) == B.MOE_ERR_UNSUPPORTED
     assert b"2^30" in L.moe_last_error()
+    assert B.forward_workspace_size(huge) == B.workspace_size(huge)
+    # the forward and the backward accept the workspace before xr; the stage
+    # calls need all of it
+    fwd = B.forward_workspace_size(cfg)
+    assert fwd == B.workspace_layout(cfg)["xr"] < need
+    assert L.moe_forward(c, p, p, p, p, p, p, p, fwd - 1, None) == \
+        B.MOE_ERR_WORKSPACE_TOO_SMALL
+    assert L.moe_forward(c, p, p, p, p, None, p, p, fwd, None) == \
+        B.MOE_ERR_INVALID_ARGUMENT  # past the size check: a NULL pointer
+    assert L.moe_dispatch(c, 0, 1, p, p, fwd, None) == B.MOE_ERR_WORKSPACE_TOO_SMALL
+    assert L.moe_expert_ffn(c, 0, 1, p, p, p, None, p, fwd, None) == \
+        B.MOE_ERR_WORKSPACE_TOO_SMALL
+    assert L.moe_forward_workspace_size(c, None) == B.MOE_ERR_INVALID_ARGUMENT
     assert L.moe_combine(c, p, need, None, None) == B.MOE_ERR_INVALID_ARGUMENT
     assert L.moe_pack_weights(c, p, p, None, p, p, p, None) == \
         B.MOE_ERR_INVALID_ARGUMENT
@@ -206,7 +227,7 @@ def test_static_forward_checks_before_any_hip_call(B):
     assert m and int(m.group(1)) << int(m.group(2)) == B.STATIC_WORKSPACE_BYTES
     p = 1 << 20
     big = B.config(8192, 32, 4, 2048, 1024, 1024, "bf16")
-    assert B.workspace_size(big) > B.STATIC_WORKSPACE_BYTES
+    assert B.forward_workspace_size(big) > B.STATIC_WORKSPACE_BYTES
     assert L.moe_forward_static(ctypes.byref(big), p, p, p, p, p, p, None) == \
         B.MOE_ERR_WORKSPACE_TOO_SMALL
     assert b"static workspace" in L.moe_last_error()
@@ -261,8 +282,9 @@ def test_backward_argument_checks_before_any_hip_call(B):
     ptrs = [p] * 10  # x, w_gate, w_up, w_down, dy, dx, dlogits, dw_gate/up/down
     assert L.moe_backward(c, *ptrs, p, need, p, bneed - 1, None) == \
         B.MOE_ERR_WORKSPACE_TOO_SMALL
-    assert L.moe_backward(c, *ptrs, p, need - 1, p, bneed, None) == \
-        B.MOE_ERR_WORKSPACE_TOO_SMALL
+    # the forward's workspace up to xr is enough
+    assert L.moe_backward(c, *ptrs, p, B.forward_workspace_size(cfg) - 1, p, bneed,
+                          None) == B.MOE_ERR_WORKSPACE_TOO_SMALL
     for i in range(10):
         bad = list(ptrs)
         bad[i] = None

@@ -34,11 +34,13 @@ CASES = [
 ]
 
 
-def run_backward(case, C=None, G=1, layout="tiled", seed=7, S=1):
+def run_backward(case, C=None, G=1, layout="tiled", seed=7, S=1, forward_ws=False):
     w = case.w
     cfg = case.cfg(C, weight_layout=layout, group=G, round_buffers=S)
     wg, wu, wd = case.weights(layout)
     ws = case.workspace(cfg)
+    if forward_ws:  # only the part moe_forward and moe_backward need
+        ws = ws[:B.forward_workspace_size(cfg)].clone()
     y = case.new_y()
     note(f"{w.name}: moe_forward C={cfg.C} G={G} S={S} ({layout})")
     B.moe_forward(cfg, case.logits, case.x, wg, wu, wd, y, ws)
@@ -55,7 +57,7 @@ def run_backward(case, C=None, G=1, layout="tiled", seed=7, S=1):
     note(f"{w.name}: moe_backward C={cfg.C} G={G}")
     B.moe_backward(cfg, case.x, wg, wu, wd, dy, dx, dl, dWg, dWu, dWd, ws, bws)
     torch.cuda.synchronize()
-    return dict(dy=dy, dx=dx, dl=dl, dWg=dWg, dWu=dWu, dWd=dWd)
+    return dict(dy=dy, dx=dx, dl=dl, dWg=dWg, dWu=dWu, dWd=dWd, y=y)
 
 
 @pytest.mark.parametrize("w,G", CASES, ids=lambda v: getattr(v, "name", f"G{v}"))
@@ -176,4 +178,21 @@ def test_backward_after_a_two_buffer_forward_is_identical(G):
     a = run_backward(case, G=G, S=1)
     b = run_backward(case, G=G, S=2)
     for name in ("dx", "dl", "dWg", "dWu", "dWd"):
+        assert torch.equal(a[name], b[name]), name
+
+
+@pytest.mark.parametrize("G,S", [(1, 1), (3, 1), (1, 2)])
+def test_forward_and_backward_run_on_the_forward_workspace(G, S):
+    """moe_forward and moe_backward on a workspace of exactly
+    moe_forward_workspace_size bytes (everything before the round buffer xr,
+    which the gathering forward never touches): the same bits as with the
+    whole workspace."""
+    w = CASES[3][0] if G == 3 else CASES[0][0]
+    case = Case(w)
+    cfg = case.cfg(group=G, round_buffers=S)
+    assert B.forward_workspace_size(cfg) == B.workspace_layout(cfg)["xr"]
+    assert B.forward_workspace_size(cfg) < B.workspace_size(cfg)
+    a = run_backward(case, G=G, S=S)
+    b = run_backward(case, G=G, S=S, forward_ws=True)
+    for name in ("y", "dx", "dl", "dWg", "dWu", "dWd"):
         assert torch.equal(a[name], b[name]), name

@@ -35,7 +35,7 @@ def test_static_forward_matches_moe_forward_twice():
     for i, (w, G, S) in enumerate(CALLS):
         case = Case(w)
         cfg = case.cfg(group=G, round_buffers=S)
-        assert B.workspace_size(cfg) <= B.STATIC_WORKSPACE_BYTES
+        assert B.forward_workspace_size(cfg) <= B.STATIC_WORKSPACE_BYTES
         wg, wu, wd = case.weights()
         ws = case.workspace(cfg)
         y_ref = case.new_y()
@@ -59,14 +59,15 @@ def test_static_forward_matches_moe_forward_twice():
         # and against the oracle on every token (the bar moe_forward meets)
         assert_close(to_np(y), case.oracle_y(np.arange(w.T)), w.dtype, f"y of {w.name}")
         if ref_bytes is not None:
-            assert B.workspace_size(cfg) < ref_bytes, "each call smaller than the last"
-        ref_bytes = B.workspace_size(cfg)
+            assert B.forward_workspace_size(cfg) < ref_bytes, \
+                "each call smaller than the last"
+        ref_bytes = B.forward_workspace_size(cfg)
 
 
 def test_static_forward_rejects_a_config_beyond_the_static_workspace():
     w = configs.BALANCED_BF16
     cfg = B.config(w.T, w.E, w.k, w.d_model, w.d_ff, w.C, w.dtype, "tiled")
-    assert B.workspace_size(cfg) > B.STATIC_WORKSPACE_BYTES
+    assert B.forward_workspace_size(cfg) > B.STATIC_WORKSPACE_BYTES
     dev = "cuda:0"
     logits = torch.zeros(w.T, w.E, device=dev)
     x = torch.zeros(w.T, w.d_model, dtype=torch.bfloat16, device=dev)
