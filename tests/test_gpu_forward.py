@@ -412,3 +412,44 @@ def test_forward_with_an_x_over_2_30_bytes_dispatches_into_the_round_buffer():
     y_ref = oracle.forward_tokens(np.arange(tok.size), idx[tok], wt[tok],
                                   to_np(x[t_dev]), to_np(wg), to_np(wu), to_np(wd))
     assert_close(to_np(y1[t_dev]), y_ref, "bf16", "y (x over 2^30 bytes)")
+
+
+def test_fp32_forward_with_several_tiles_per_workgroup():
+    """fp32 with more grouped-GEMM tiles than CUs (T = 8192, d = f = 1024,
+    E = 16, k = 2: 32 tiles per expert in round 0), so that each workgroup
+    of the gathering gate/up launch walks several tiles and prefetches the
+    next tiles' rows: its h is bit-identical to dispatch + gate/up, and y
+    matches the oracle on sampled tokens."""
+    w = configs.Workload("f32_multi_tile", T=8192, d_model=1024, d_ff=1024, E=16, k=2,
+                         C=600, dtype="f32", skew=("zipf", 0.5))
+    _cache.clear()
+    torch.cuda.empty_cache()
+    case = Case(w)
+    cfg = case.cfg()
+    wg, wu, wd = case.weights()
+    ws = case.workspace(cfg)
+    note(f"{w.name}: moe_plan")
+    R, counts = B.moe_plan(cfg, case.logits, ws, return_counts=True)
+    views = B.workspace_views(cfg, ws)
+    assert R >= 2
+    for r0, n in B.launch_batches(cfg, counts):
+        note(f"{w.name}: rounds {r0}..{r0 + n - 1}: dispatch + gate/up, then fused")
+        views["xr"].zero_()
+        views["h"].fill_(0xFF)
+        B.moe_dispatch(cfg, r0, case.x, ws, n_rounds=n)
+        B.moe_expert_gate_up(cfg, r0, wg, wu, ws, counts_host=counts, n_rounds=n)
+        torch.cuda.synchronize()
+        h1 = views["h"].clone()
+        views["xr"].fill_(0xFF)
+        views["h"].fill_(0xFF)
+        B.moe_dispatch_gate_up(cfg, r0, case.x, wg, wu, ws, counts_host=counts,
+                               n_rounds=n)
+        torch.cuda.synchronize()
+        assert torch.equal(views["h"], h1), f"fused h of rounds {r0}..{r0 + n - 1}"
+    note(f"{w.name}: moe_forward")
+    y = case.new_y()
+    B.moe_forward(cfg, case.logits, case.x, wg, wu, wd, y, ws)
+    torch.cuda.synchronize()
+    p = oracle.plan(case.idx, w.E, w.C)
+    tok = sample_tokens(w.T, p, w.k, 96)
+    assert_close(to_np(y)[tok], case.oracle_y(tok), "f32", "y")
