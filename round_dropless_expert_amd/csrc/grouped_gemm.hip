@@ -474,6 +474,26 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
       S.vt[j] = pa[j] < 0 ? kDeadRow
                           : (uint32_t)(pa[j] / p.topk) * kbytes + (uint32_t)chunk * 16;
   };
+  // Recompute and dgate: the epilogue scales row c of token block jb (c =
+  // m0 + wm BM/2 + 32 jb + l32) by its assignment's routing weight,
+  // weight[perm[z0 + c]]. Both loads are issued ahead (the assignments two
+  // tiles, the weights one tile before the epilogue that uses them), so
+  // that the compiler's waits for them fall at the top of a tile, like the
+  // gathered rows' above, instead of two dependent loads with a wait each
+  // in every epilogue block.
+  constexpr bool kRowWeight = kMode == kModeRecompute || kMode == kModeDgate;
+  auto epi_perm = [&](int te, int tm, int tm0, bool exists, int32_t (&pw)[WJ]) {
+    const int64_t z0 = exists ? __builtin_amdgcn_readlane(lane_off, te) : 0;
+#pragma unroll
+    for (int jb = 0; jb < WJ; ++jb) {
+      const int c = tm0 + wm * (BM / 2) + jb * 32 + l32;
+      pw[jb] = exists && c < tm ? p.perm[z0 + c] : -1;
+    }
+  };
+  auto epi_weight = [&](const int32_t (&pw)[WJ], float (&w)[WJ]) {
+#pragma unroll
+    for (int jb = 0; jb < WJ; ++jb) w[jb] = pw[jb] < 0 ? 0.f : p.weight[pw[jb]];
+  };
 
   const int KT = p.K / kStageK;            // 64-byte K stages
   const int KS = (KT + SPB - 1) / SPB;     // super-stages of one tile
@@ -585,6 +605,19 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
     if (t1 < total) locate(t1, e1, m1, n01, m01);
     perm_rows(e1, m1, m01, t1 < total, pa);
   }
+  // row weights: w_pend holds the tile's (the top of the loop moves them to
+  // w_cur), pw the next tile's assignments
+  int32_t pw[WJ];
+  float w_pend[WJ], w_cur[WJ];
+  if constexpr (kRowWeight) {
+    int32_t p0[WJ];
+    epi_perm(e, m, m0, true, p0);
+    epi_weight(p0, w_pend);
+    const int t1 = tile + (int)gridDim.x;
+    int e1 = 0, m1 = 0, n01 = 0, m01 = 0;
+    if (t1 < total) locate(t1, e1, m1, n01, m01);
+    epi_perm(e1, m1, m01, t1 < total, pw);
+  }
   {
     const StageOff o0 = stage_off(0), o1 = stage_off(1), o2 = stage_off(2);
 #pragma unroll
@@ -614,6 +647,19 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
       int e2 = 0, m2 = 0, n02 = 0, m02 = 0;
       if (tile_nn < total) locate(tile_nn, e2, m2, n02, m02);
       perm_rows(e2, m2, m02, tile_nn < total, pa);
+    }
+    if constexpr (kRowWeight) {
+#pragma unroll
+      for (int jb = 0; jb < WJ; ++jb) {
+        w_cur[jb] = w_pend[jb];
+        // in a register here, so the wait for its load is at this point
+        asm volatile("" : "+v"(w_cur[jb]));
+      }
+      epi_weight(pw, w_pend);
+      const int tile_nn = tile_n + G;
+      int e2 = 0, m2 = 0, n02 = 0, m02 = 0;
+      if (tile_nn < total) locate(tile_nn, e2, m2, n02, m02);
+      epi_perm(e2, m2, m02, tile_nn < total, pw);
     }
 
 #pragma unroll
@@ -694,9 +740,8 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
     if constexpr (kMode == kModeRecompute) {
       // gu (g in columns [0, N), u in [N, 2N)) and hw = w * silu(g) u: rows
       // c of expert e's tiled matrices of the round; w is the routing
-      // weight of the row's assignment perm[i0 + c]
+      // weight of the row's assignment (w_cur, loaded ahead)
       const int rowb = __builtin_amdgcn_readlane(lane_row, e);
-      const int64_t i0 = (int64_t)__builtin_amdgcn_readlane(lane_off, e);
       const uint32_t mrows = (uint32_t)((m + 63) & ~63);
       const __amdgpu_buffer_rsrc_t rgu = __builtin_amdgcn_make_buffer_rsrc(
           (void*)(p.out + (int64_t)rowb * 2 * p.N), 0,
@@ -707,7 +752,7 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
 #pragma unroll
       for (int jb = 0; jb < WJ; ++jb) {
         const int c = m0 + wm * (BM / 2) + jb * 32 + l32;
-        const float wc = c < m ? p.weight[p.perm[i0 + c]] : 0.f;
+        const float wc = w_cur[jb];
 #pragma unroll
         for (int ib = 0; ib < WI / 2; ++ib) {
 #pragma unroll
@@ -741,7 +786,6 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
       // silu'(g) = dh u s (1 + g (1 - s)), s = sigmoid(g); into dgu (dg in
       // columns [0, N), du in [N, 2N)), rows c of expert e's tiled matrix
       const int rowb = __builtin_amdgcn_readlane(lane_row, e);
-      const int64_t i0 = (int64_t)__builtin_amdgcn_readlane(lane_off, e);
       const uint32_t range =
           (uint32_t)((m + 63) & ~63) * 2 * (uint32_t)p.N * kEs;
       const __amdgpu_buffer_rsrc_t rin = __builtin_amdgcn_make_buffer_rsrc(
@@ -753,7 +797,7 @@ __global__ __launch_bounds__(256, 1) void grouped_ffn_gemm_kernel(
 #pragma unroll
       for (int jb = 0; jb < WJ; ++jb) {
         const int c = m0 + wm * (BM / 2) + jb * 32 + l32;
-        const float wc = c < m ? p.weight[p.perm[i0 + c]] : 0.f;
+        const float wc = w_cur[jb];  // routing weight (loaded ahead)
         // this token's g and u for every output of the block, loaded first
         u32x2 gv[WI][4], uv[WI][4];
 #pragma unroll
