@@ -142,7 +142,10 @@ hipError_t launch_pack_weights(const Shape& s, const void* src, void* dst,
 // row and loads them from up to kMaxK rows before it adds (up to
 // kMaxK * kVecs loads in flight; with k <= 4 a lane covers a 2048-element
 // bf16 row in one pass). z is read exactly once, so its loads are
-// non-temporal (a tenth faster on the balanced layer, same result).
+// non-temporal (a tenth faster on the balanced layer, same result). For
+// bf16 with k up to 8, four vectors per lane (32 loads in flight, two
+// wavefronts per SIMD) read faster than two (four wavefronts per SIMD):
+// on the hot-expert layer's 2.4 GB, 430 against 440 us.
 template <typename Elem, int kVecs, int kMaxK>
 __global__ __launch_bounds__(256) void combine_kernel(
     const Elem* __restrict__ z, const float* __restrict__ weight,
@@ -213,7 +216,7 @@ hipError_t launch_combine(const Shape& s, const void* z, const float* weight,
                        0, st, static_cast<const bf16*>(z), weight, pos, s.T, s.k,
                        s.d, static_cast<bf16*>(y));
   else if (s.bf16)
-    hipLaunchKernelGGL((combine_kernel<bf16, 2, 8>), dim3((unsigned)blocks), dim3(256),
+    hipLaunchKernelGGL((combine_kernel<bf16, 4, 8>), dim3((unsigned)blocks), dim3(256),
                        0, st, static_cast<const bf16*>(z), weight, pos, s.T, s.k,
                        s.d, static_cast<bf16*>(y));
   else
